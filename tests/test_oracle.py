@@ -1,0 +1,262 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each check uses something other than the oracle's own formulas: original
+fp32 weights and the quantiser's error bound, exact integer arithmetic,
+library routines in fp64 (numpy matmul, scipy softmax, stable sorts),
+closed forms, and the pages' invariants (layer-major equals token-major;
+swapping gate and up breaks the result).
+"""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+import oracle
+import synth
+from synth import configs
+
+
+def bf16_to_f32(h):
+    return (np.asarray(h).astype(np.uint32) << 16).view(np.float32)
+
+
+def unpack(w):
+    shifts = np.arange(8, dtype=np.uint32) * 4
+    return ((w[..., None] >> shifts) & 0xF).reshape(*w.shape[:-1], w.shape[-1] * 8)
+
+
+def pack(q):
+    q = np.asarray(q, np.uint32)
+    w = np.zeros(q.shape[:-1] + (q.shape[-1] // 8,), np.uint32)
+    for i in range(8):
+        w |= q[..., i::8] << (4 * i)
+    return w
+
+
+def rel_l2(a, ref):
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(a - ref) / np.linalg.norm(ref))
+
+
+# ----------------------------------------------------------------- dequant
+def test_dequant_recovers_original_weights_within_quantiser_bound():
+    rng = np.random.default_rng(7)
+    W = (rng.standard_normal((40, 320)) * 0.02).astype(np.float32)
+    w, s, b = synth.quantize_matrix(W)
+    D = oracle.dequant(w, s, b).astype(np.float64)
+    S = np.repeat(bf16_to_f32(s), 64, axis=1).astype(np.float64)
+    Bv = np.repeat(bf16_to_f32(b), 64, axis=1).astype(np.float64)
+    bound = 0.5 * S + 15 * S * 2.0**-8 + np.abs(Bv) * 2.0**-8 + 1e-9
+    assert np.all(np.abs(D - W) <= bound)
+    # a wrong nibble order or group index would break the bound badly
+    assert rel_l2(D, W) < 0.15
+
+
+def test_dequant_integer_codes_exact():
+    rng = np.random.default_rng(3)
+    q = rng.integers(0, 16, size=(8, 128))
+    s = np.full((8, 2), 0x3F80, np.uint16)          # bf16 1.0
+    b = np.full((8, 2), 0xC100, np.uint16)          # bf16 -8.0
+    D = oracle.dequant(pack(q), s, b)
+    assert np.array_equal(D, (q - 8).astype(np.float32))
+
+
+# ------------------------------------------------------------- routing
+def test_router_logits_match_fp64_matmul():
+    cfg = configs.TINY
+    Wr = synth.router(0, 0, cfg.num_experts, cfg.d_model, cfg.router_sigma, False)
+    x = synth.hidden(0, 0, 0, cfg.batch, cfg.d_model)
+    lg = oracle.router_logits(Wr, x)
+    ref = x.astype(np.float64) @ Wr.astype(np.float64).T
+    assert np.max(np.abs(lg - ref)) < 1e-5 * np.max(np.abs(ref)) * 10
+    # bf16 gates are widened exactly
+    Wb = synth.router(0, 0, 32, 512, 1 / math.sqrt(512), True)
+    xb = synth.hidden(0, 0, 1, 4, 512)
+    ref_b = xb.astype(np.float64) @ bf16_to_f32(Wb).astype(np.float64).T
+    assert np.max(np.abs(oracle.router_logits(Wb, xb) - ref_b)) < 1e-5
+
+
+def test_topk_order_ties_and_weights():
+    rng = np.random.default_rng(0)
+    lg = rng.standard_normal((50, 40)).astype(np.float32)
+    lg[0, [3, 9, 17]] = 5.0                          # three-way tie at the top
+    lg[1, [30, 2]] = lg[1].max() + 1.0               # tie, higher index listed first
+    for norm in (True, False):
+        idx, w = oracle.topk_softmax(lg, 6, norm)
+        for t in range(lg.shape[0]):
+            order = np.lexsort((np.arange(40), -lg[t].astype(np.float64)))
+            assert np.array_equal(idx[t], order[:6])
+            p = softmax(lg[t].astype(np.float64))
+            ref = p[order[:6]] / p[order[:6]].sum() if norm else p[order[:6]]
+            assert np.allclose(w[t], ref, rtol=2e-6, atol=0)
+        if norm:
+            assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    idx, _ = oracle.topk_softmax(lg, 6, True)
+    assert list(idx[0, :3]) == [3, 9, 17] and list(idx[1, :2]) == [2, 30]
+
+
+def test_topk_all_experts_is_full_softmax():
+    rng = np.random.default_rng(1)
+    lg = (rng.standard_normal((7, 16)) * 3).astype(np.float32)
+    idx, w = oracle.topk_softmax(lg, 16, True)
+    for t in range(7):
+        p = softmax(lg[t].astype(np.float64))
+        assert np.allclose(w[t], p[idx[t]], rtol=2e-6)
+        assert sorted(idx[t]) == list(range(16))
+
+
+# --------------------------------------------------------------- union
+def brute_union(idx, E):
+    flat = idx.reshape(-1)
+    ue = np.unique(flat)
+    lists = [np.flatnonzero(flat == e) for e in ue]
+    return ue, lists
+
+
+@pytest.mark.parametrize("B,K,E", [(1, 8, 128), (8, 4, 16), (64, 8, 128), (37, 8, 256),
+                                   (64, 16, 16), (5, 1, 3)])
+def test_union_matches_filter(B, K, E):
+    rng = np.random.default_rng(B * 1000 + K)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(B)]).astype(np.int32)
+    n, ue, off, pl, pp = oracle.build_union(idx, E)
+    bu, lists = brute_union(idx, E)
+    assert n == len(bu) and np.array_equal(ue, bu)
+    assert off[0] == 0 and off[-1] == B * K
+    for u in range(n):
+        assert np.array_equal(pl[off[u]:off[u + 1]], lists[u])
+    assert np.array_equal(pl[pp], np.arange(B * K))
+    if B == 1:
+        assert n == K
+
+
+def test_union_rejects_bad_expert():
+    with pytest.raises(ValueError):
+        oracle.build_union(np.array([[0, 16]], np.int32), 16)
+
+
+def test_expected_union_closed_form_monte_carlo():
+    for (E, K, B) in [(128, 8, 64), (256, 8, 64), (16, 4, 8)]:
+        rng = np.random.default_rng(E + B)
+        sizes = []
+        for _ in range(300):
+            idx = np.stack([rng.choice(E, K, replace=False) for _ in range(B)]).astype(np.int32)
+            sizes.append(oracle.build_union(idx, E)[0])
+        sizes = np.asarray(sizes, np.float64)
+        mu = configs.expected_union(E, K, B)
+        assert abs(sizes.mean() - mu) < 3 * sizes.std(ddof=1) / math.sqrt(len(sizes)) + 1e-9
+    assert abs(configs.expected_union(128, 8, 64) - 125.94) < 0.01
+    assert abs(configs.expected_union(256, 8, 64) - 222.44) < 0.01
+
+
+# ---------------------------------------------------------- expert FFN
+def test_integer_ffn_closed_form():
+    """s=1, b=0 codes and small integer inputs: every pre-activation is an
+    exact integer, compared with int64 arithmetic."""
+    rng = np.random.default_rng(11)
+    d, f = 256, 128
+    qg = rng.integers(0, 16, (f, d))
+    qu = rng.integers(0, 16, (f, d))
+    qd = rng.integers(0, 16, (d, f))
+    x = rng.integers(-3, 4, d).astype(np.float32)
+    one = lambda r, c: np.full((r, c // 64), 0x3F80, np.uint16)
+    zero = lambda r, c: np.zeros((r, c // 64), np.uint16)
+    Wg = oracle.dequant(pack(qg), one(f, d), zero(f, d))
+    Wu = oracle.dequant(pack(qu), one(f, d), zero(f, d))
+    Wd = oracle.dequant(pack(qd), one(d, f), zero(d, f))
+    g, u, h, y = oracle.expert_ffn(Wg, Wu, Wd, x)
+    xi = x.astype(np.int64)
+    assert np.array_equal(g.astype(np.int64), qg @ xi)
+    assert np.array_equal(u.astype(np.int64), qu @ xi)
+    # silu against the logistic function in fp64
+    g64, u64 = (qg @ xi).astype(np.float64), (qu @ xi).astype(np.float64)
+    h_ref = g64 / (1 + np.exp(-g64)) * u64
+    assert np.allclose(h, h_ref, rtol=1e-6, atol=1e-6 * np.abs(h_ref).max())
+    assert rel_l2(y, qd.astype(np.float64) @ h.astype(np.float64)) < 1e-6
+
+
+def brute_force_layer(L, x, K, norm=True, swap_gate_up=False, residual=None):
+    """Dense fp64 layer: every expert on every token, masked by top-k."""
+    gw, gs, gb = L["gate"]
+    uw, us, ub = L["up"]
+    dw, ds, db = L["down"]
+    if swap_gate_up:
+        (gw, gs, gb), (uw, us, ub) = (uw, us, ub), (gw, gs, gb)
+
+    def deq(w, s, b):
+        q = unpack(w).astype(np.float64)
+        return q * np.repeat(bf16_to_f32(s), 64, -1) + np.repeat(bf16_to_f32(b), 64, -1)
+
+    Wr = L["router"]
+    Wr64 = bf16_to_f32(Wr).astype(np.float64) if Wr.dtype == np.uint16 else Wr.astype(np.float64)
+    x64 = x.astype(np.float64)
+    logits = x64 @ Wr64.T
+    E = Wr.shape[0]
+    out = np.zeros_like(x64) if residual is None else residual.astype(np.float64).copy()
+    for t in range(x.shape[0]):
+        order = np.lexsort((np.arange(E), -logits[t]))[:K]
+        p = softmax(logits[t])
+        wk = p[order] / p[order].sum() if norm else p[order]
+        for k, e in enumerate(order):
+            g = deq(gw[e], gs[e], gb[e]) @ x64[t]
+            u = deq(uw[e], us[e], ub[e]) @ x64[t]
+            h = g / (1 + np.exp(-g)) * u
+            out[t] += wk[k] * (deq(dw[e], ds[e], db[e]) @ h)
+    return out
+
+
+def test_layer_matches_dense_fp64_brute_force_tiny():
+    cfg = configs.TINY
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 0, cfg.batch, cfg.d_model)
+    _, idx, w = oracle.route(L["router"], x, cfg.top_k)
+    out = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w)
+    ref = brute_force_layer(L, x, cfg.top_k)
+    assert rel_l2(out, ref) < 1e-5
+    # negative control from the pages: a gate/up reorder must fail by a wide
+    # margin.  With these small pre-activations silu(g)*u ~ g*u/2 is nearly
+    # symmetric in g and u, so the swap costs ~37% here rather than the ~100%
+    # the pages saw on a trained model; still >100x the 3e-3 tolerance.
+    swapped = brute_force_layer(L, x, cfg.top_k, swap_gate_up=True)
+    assert rel_l2(swapped, ref) > 0.3
+
+
+def test_layer_major_equals_token_major_bitwise():
+    cfg = configs.LayerConfig("mid", 512, 24, 6, 192, 13, router_bf16=True)
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 0, cfg.batch, cfg.d_model)
+    res = synth.hidden(cfg.seed, 0, 9, cfg.batch, cfg.d_model, tensor=synth.T_RESIDUAL)
+    _, idx, w = oracle.route(L["router"], x, cfg.top_k)
+    a, ya = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res, return_pairs=True)
+    b, yb = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res, layer_major=True,
+                       return_pairs=True)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    ref = brute_force_layer(L, x, cfg.top_k, residual=res)
+    assert rel_l2(a - res, ref - res) < 1e-5
+
+
+def test_combine_order_and_residual():
+    """out = residual + (w0*y0 + w1*y1 + ...), k ascending, checked on a case
+    where the fp32 sum order matters."""
+    cfg = configs.TINY
+    L = synth.make_layer(cfg)
+    x = synth.hidden(0, 0, 0, 2, cfg.d_model)
+    idx = np.array([[1, 2, 3, 4], [5, 6, 7, 8]], np.int32)
+    w = np.array([[1e8, 1.0, -1e8, 0.5], [0.25, 0.25, 0.25, 0.25]], np.float32)
+    out, yp = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, return_pairs=True)
+    y = yp.reshape(2, 4, -1)
+    for t in range(2):
+        acc = np.zeros(cfg.d_model, np.float32)
+        for k in range(4):
+            acc = (acc + np.float32(w[t, k]) * y[t, k]).astype(np.float32)
+        assert np.array_equal(out[t], acc)
+
+
+def test_rmsnorm_closed_form():
+    v = np.full((2, 64), 3.0, np.float32)
+    v[1] = -2.0
+    out = oracle.rmsnorm(v, eps=1e-6)
+    assert np.allclose(out[0], 3.0 / math.sqrt(9 + 1e-6), rtol=1e-7)
+    assert np.allclose(out[1], -2.0 / math.sqrt(4 + 1e-6), rtol=1e-7)
