@@ -1,0 +1,233 @@
+"""Benchmark: one routed MoE layer (exact routing -> union -> fused 4-bit
+SwiGLU experts -> combine) on one MI355X.
+
+A step is one call of the whole layer (router gate matvec, softmax/top-k,
+union and pair lists, gate_up, down, combine) on one fresh batch.  Steps
+rotate over a stack of distinct layers resident in HBM (16 by default) so
+that the weights stream from HBM, not from the 256 MB Infinity Cache.
+
+Prints one JSON line:
+  value       tokens/s of the decode layer (d=4096, 128 experts, top-8,
+              ffn 1536, B=1), whole job, inputs resident in HBM;
+  effective_gbps / hbm_frac   bytes of the distinct routed experts per step
+              (packed words + bf16 scales + biases) / step time, vs 8 TB/s;
+  secondary   the same layer as a 64-token prefill chunk;
+  roofline    the dominant kernel (gate_up) timed with HIP events on its
+              launch stream: algorithmic bytes per launch / mean duration;
+  cpu_baseline  the CPU oracle on a bounded sample of the decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MoE-layer tokens/s and effective expert-weight GB/s (% HBM peak), B=1 and B=64"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000, help="timed decode steps")
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--prefill-steps", type=int, default=200)
+    p.add_argument("--layers", type=int, default=16, help="distinct layers rotated through")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    return p.parse_args()
+
+
+class Stack:
+    """n distinct layers of one shape in device memory plus shared buffers."""
+
+    def __init__(self, smoe, cfg, n_layers, max_batch):
+        import torch
+
+        import synth.gpu as sg
+        self.cfg, self.smoe = cfg, smoe
+        self.desc = smoe.make_desc(cfg.d_model, cfg.ffn_dim, cfg.num_experts, cfg.top_k,
+                                   cfg.norm_topk_prob, cfg.router_bf16)
+        self.layers = []
+        for l in range(n_layers):
+            W = sg.make_layer(cfg, layer=l)
+            ex = smoe.Experts(smoe.qmat(*W["gate"]), smoe.qmat(*W["up"]), smoe.qmat(*W["down"]))
+            self.layers.append((W, ex))
+        dev = torch.device("cuda:0")
+        self.ws = torch.zeros(smoe.workspace_size(self.desc, max_batch), dtype=torch.uint8,
+                              device=dev)
+        smoe.workspace_init(self.ws)
+        self.un = smoe.UnionBuffers.alloc(cfg.num_experts, max_batch * cfg.top_k, dev)
+        self.idx = torch.zeros(max_batch, cfg.top_k, dtype=torch.int32, device=dev)
+        self.w = torch.zeros(max_batch, cfg.top_k, dtype=torch.float32, device=dev)
+        self.out = torch.zeros(max_batch, cfg.d_model, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def call(self, l, x):
+        W, ex = self.layers[l]
+        B = x.shape[0]
+        self.smoe.moe_layer(self.desc, W["router"], ex, x, self.out[:B], self.idx[:B],
+                            self.w[:B], self.un, self.ws)
+
+    def stage(self, st, l, x):
+        W, ex = self.layers[l]
+        B = x.shape[0]
+        self.smoe.moe_layer_stage(st, self.desc, W["router"], ex, x, self.out[:B], self.idx[:B],
+                                  self.w[:B], self.un, self.ws)
+
+
+def x_pool(cfg, B, n):
+    import synth.gpu as sg
+    return [sg.hidden(cfg.seed, 0, 1000 + i, B, cfg.d_model) for i in range(n)]
+
+
+def time_layer(stack, xs, steps, warmup):
+    """Seconds for `steps` whole-layer calls, rotating layers and inputs."""
+    import torch
+    nl = len(stack.layers)
+    for s in range(warmup):
+        stack.call(s % nl, xs[s % len(xs)])
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for s in range(steps):
+        stack.call(s % nl, xs[s % len(xs)])
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / 1e3
+
+
+def time_gate_up(stack, xs, steps):
+    """Mean gate_up duration (s) measured with events on the launch stream,
+    with the whole layer still run stage by stage around it."""
+    import torch
+    smoe = stack.smoe
+    nl = len(stack.layers)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s in range(steps):
+        l, x = s % nl, xs[s % len(xs)]
+        stack.stage(smoe.SMOE_STAGE_ROUTE, l, x)
+        evs[s][0].record()
+        stack.stage(smoe.SMOE_STAGE_GATE_UP, l, x)
+        evs[s][1].record()
+        stack.stage(smoe.SMOE_STAGE_DOWN, l, x)
+        stack.stage(smoe.SMOE_STAGE_COMBINE, l, x)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps / 1e3
+
+
+def union_sizes(stack, xs, steps):
+    """|U| of every timed step (the routing is deterministic; re-run untimed)."""
+    import torch
+    nl = len(stack.layers)
+    sizes = []
+    for s in range(steps):
+        stack.stage(stack.smoe.SMOE_STAGE_ROUTE, s % nl, xs[s % len(xs)])
+        sizes.append(stack.un.n_union.clone())
+    torch.cuda.synchronize()
+    return [int(t.item()) for t in sizes]
+
+
+def cpu_baseline(cfg, seconds):
+    """The oracle (as it stands) on a bounded sample of the decode workload:
+    route + layer-major MoE of single tokens through layer 0, repeated until
+    `seconds` of CPU time have elapsed.  Weight generation is not timed."""
+    import numpy as np
+
+    import oracle
+    import synth
+    Wr = synth.router(cfg.seed, 0, cfg.num_experts, cfg.d_model, cfg.router_sigma, cfg.router_bf16)
+    tokens = [synth.hidden(cfg.seed, 0, 1000 + i, 1, cfg.d_model) for i in range(4)]
+    routed = set()
+    for x in tokens:
+        _, idx, _ = oracle.route(Wr, x, cfg.top_k, cfg.norm_topk_prob)
+        routed.update(int(e) for e in idx.reshape(-1))
+    L = synth.make_layer(cfg, layer=0, experts=sorted(routed))
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        x = tokens[done % len(tokens)]
+        _, idx, w = oracle.route(Wr, x, cfg.top_k, cfg.norm_topk_prob)
+        oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, layer_major=True)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": done * cfg.batch / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} single-token decode calls of layer 0 ({len(tokens)} distinct tokens, "
+                      f"{len(routed)} experts generated beforehand), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(this build runs the layer on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import exact_routing_bit_amd as smoe
+    from synth import configs
+    torch.cuda.set_device(0)
+
+    dec = configs.DECODE
+    stack = Stack(smoe, dec, args.layers, max_batch=64)
+    xs1 = x_pool(dec, 1, 257)
+    t = time_layer(stack, xs1, args.steps, args.warmup)
+    eb = dec.expert_bytes()
+    sizes1 = union_sizes(stack, xs1, min(args.steps, 512))
+    u1 = sum(sizes1) / len(sizes1)
+    step_s = t / args.steps
+    gbps = u1 * eb / step_s / 1e9
+    # roofline: gate_up (two thirds of the expert bytes) timed on its own
+    gu_s = time_gate_up(stack, xs1, min(args.steps, 1000))
+    gu_bytes = u1 * (2 * dec.ffn_dim * dec.d_model // 2 + 2 * 2 * 2 * dec.ffn_dim * dec.d_model // 64)
+    gu_gbps = gu_bytes / gu_s / 1e9
+
+    result = {
+        "metric": METRIC, "value": round(dec.batch * args.steps / t, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{dec.name}: one routed MoE layer, d=4096, 128 experts, top-8 "
+                               "norm_topk_prob, ffn 1536, 4-bit g64 experts, B=1 decode",
+                   "layers_rotated": args.layers, "mean_union": u1,
+                   "effective_bytes_per_step": int(u1 * eb)},
+        "effective_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_expert_ffn<gate_up>",
+                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(gu_bytes), "mean_launch_us": round(gu_s * 1e6, 3)},
+    }
+    if not args.no_prefill:
+        pre = configs.PREFILL
+        xs64 = x_pool(pre, 64, 17)
+        tp = time_layer(stack, xs64, args.prefill_steps, 5)
+        sz = union_sizes(stack, xs64, args.prefill_steps)
+        up_ = sum(sz) / len(sz)
+        sp = tp / args.prefill_steps
+        g64 = up_ * eb / sp / 1e9
+        result["secondary"] = {"workload": f"{pre.name}: same layer, 64-token prefill chunk",
+                               "tokens_per_s": round(64 * args.prefill_steps / tp, 1),
+                               "ms_per_step": round(sp * 1e3, 5), "mean_union": up_,
+                               "effective_gbps": round(g64, 1),
+                               "hbm_frac": round(g64 / HBM_PEAK_GBPS, 4),
+                               "steps": args.prefill_steps}
+    del stack
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

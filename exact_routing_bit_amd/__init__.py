@@ -1,0 +1,280 @@
+"""Python binding of libsmoe: one routed mixture-of-experts layer on MI355X.
+
+Argument marshalling only.  Every step of the layer runs in the HIP kernels
+of ``libsmoe.so`` (declared in ``include/smoe.h``); PyTorch provides device
+memory and the current stream.  There is no CPU fallback: importing this
+module fails when the library is missing.
+
+Entry points (same names as the C-ABI, without the ``smoe_`` prefix):
+``workspace_size``, ``workspace_init``, ``route``, ``build_union``,
+``moe_forward``, ``moe_layer``, ``read_status``.  ``Layer`` bundles the
+device tensors and descriptors of one layer.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmoe.so")
+
+SMOE_OK, SMOE_EINVAL, SMOE_EUNSUPPORTED, SMOE_EWORKSPACE, SMOE_EHIP = 0, -1, -2, -3, -4
+SMOE_F32, SMOE_BF16 = 0, 1
+SMOE_ROUTE_LOGITS_IN = 0x1
+SMOE_STATUS_BAD_EXPERT = 0x1
+MAX_BATCH = 64
+
+SMOE_STAGE_ROUTE, SMOE_STAGE_GATE_UP, SMOE_STAGE_DOWN, SMOE_STAGE_COMBINE = 0, 1, 2, 3
+
+EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_build_union",
+            "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_read_status",
+            "smoe_strerror")
+
+
+class SmoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("ffn_dim", ctypes.c_int32),
+                ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
+                ("router_dtype", ctypes.c_int32)]
+
+
+class QMat(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("s", ctypes.c_void_p), ("b", ctypes.c_void_p),
+                ("expert_stride_w", ctypes.c_int64), ("expert_stride_sb", ctypes.c_int64)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+
+
+class Union(ctypes.Structure):
+    _fields_ = [("n_union", ctypes.c_void_p), ("union_experts", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("pair_list", ctypes.c_void_p),
+                ("pair_pos", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+    dp = ctypes.POINTER(LayerDesc)
+    L.smoe_workspace_size.argtypes = [dp, i32]
+    L.smoe_workspace_size.restype = sz
+    L.smoe_workspace_init.argtypes = [vp, sz, vp]
+    L.smoe_route.argtypes = [dp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
+    L.smoe_build_union.argtypes = [dp, vp, i32, ctypes.POINTER(Union), vp, sz, vp]
+    L.smoe_moe_forward.argtypes = [dp, ctypes.POINTER(Experts), vp, vp, vp, ctypes.POINTER(Union),
+                                   i32, vp, vp, vp, sz, vp]
+    L.smoe_moe_layer.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp, vp,
+                                 ctypes.POINTER(Union), vp, sz, vp]
+    L.smoe_moe_layer_stage.argtypes = [ctypes.c_int, dp, vp, ctypes.POINTER(Experts), vp, i32, vp,
+                                       vp, vp, vp, vp, ctypes.POINTER(Union), vp, sz, vp]
+    L.smoe_read_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
+    L.smoe_strerror.argtypes = [ctypes.c_int]
+    L.smoe_strerror.restype = ctypes.c_char_p
+    for name in EXPORTED:
+        if name != "smoe_workspace_size" and name != "smoe_strerror":
+            getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def strerror(code: int) -> str:
+    return lib.smoe_strerror(code).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != SMOE_OK:
+        raise SmoeError(rc, what)
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous CUDA tensor (or None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def make_desc(d_model, ffn_dim, num_experts, top_k, norm_topk_prob=True, router_bf16=True):
+    return LayerDesc(d_model, ffn_dim, num_experts, top_k, 64, int(bool(norm_topk_prob)),
+                     SMOE_BF16 if router_bf16 else SMOE_F32)
+
+
+def workspace_size(desc: LayerDesc, max_batch: int) -> int:
+    return int(lib.smoe_workspace_size(ctypes.byref(desc), max_batch))
+
+
+def workspace_init(ws: torch.Tensor, stream=None):
+    _check(lib.smoe_workspace_init(_ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+           "smoe_workspace_init")
+
+
+def qmat(w: torch.Tensor, s: torch.Tensor, b: torch.Tensor, expert_stride_w=None,
+         expert_stride_sb=None) -> QMat:
+    """Descriptor of a quantised projection with a leading expert axis.
+    w: int32/uint32 [E, rows, cols/8]; s, b: int16/uint16 bf16 bits [E, rows, cols/64].
+    Strides default to the tensors' expert strides (so views into a fused
+    gate_up tensor work)."""
+    sw = w.stride(0) if expert_stride_w is None else expert_stride_w
+    ssb = s.stride(0) if expert_stride_sb is None else expert_stride_sb
+    for t, nm in ((w, "w"), (s, "s"), (b, "b")):
+        if not t.is_cuda:
+            raise TypeError(f"{nm} must be a CUDA tensor")
+        if t.dim() == 3 and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
+            raise ValueError(f"{nm}: rows must be contiguous")
+    return QMat(w.data_ptr(), s.data_ptr(), b.data_ptr(), sw, ssb)
+
+
+@dataclass
+class UnionBuffers:
+    n_union: torch.Tensor
+    union_experts: torch.Tensor
+    expert_offsets: torch.Tensor
+    pair_list: torch.Tensor
+    pair_pos: torch.Tensor
+
+    @staticmethod
+    def alloc(num_experts: int, max_pairs: int, device="cuda") -> "UnionBuffers":
+        m = max(1, min(num_experts, max_pairs))
+        i32 = dict(dtype=torch.int32, device=device)
+        return UnionBuffers(torch.zeros(1, **i32), torch.zeros(m, **i32), torch.zeros(m + 1, **i32),
+                            torch.zeros(max(1, max_pairs), **i32),
+                            torch.zeros(max(1, max_pairs), **i32))
+
+    def c(self) -> Union:
+        return Union(self.n_union.data_ptr(), self.union_experts.data_ptr(),
+                     self.expert_offsets.data_ptr(), self.pair_list.data_ptr(),
+                     self.pair_pos.data_ptr())
+
+
+def route(desc, router_w, x, topk_idx, topk_w, ws, logits=None, logits_in=False, stream=None):
+    B = logits.shape[0] if logits_in else x.shape[0]
+    flags = SMOE_ROUTE_LOGITS_IN if logits_in else 0
+    _check(lib.smoe_route(ctypes.byref(desc), _ptr(router_w, None, "router_w"),
+                          _ptr(x, torch.float32, "x"), B, _ptr(logits, torch.float32, "logits"),
+                          _ptr(topk_idx, torch.int32, "topk_idx"),
+                          _ptr(topk_w, torch.float32, "topk_w"), flags,
+                          _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "smoe_route")
+
+
+def build_union(desc, topk_idx, un: UnionBuffers, ws, stream=None):
+    cu = un.c()
+    _check(lib.smoe_build_union(ctypes.byref(desc), _ptr(topk_idx, torch.int32, "topk_idx"),
+                                topk_idx.shape[0], ctypes.byref(cu), _ptr(ws, torch.uint8, "ws"),
+                                ws.numel(), _stream(stream)), "smoe_build_union")
+
+
+def moe_forward(desc, experts: Experts, x, topk_idx, topk_w, un: UnionBuffers, out, ws,
+                residual=None, stream=None):
+    cu = un.c()
+    _check(lib.smoe_moe_forward(ctypes.byref(desc), ctypes.byref(experts),
+                                _ptr(x, torch.float32, "x"), _ptr(topk_idx, torch.int32, "topk_idx"),
+                                _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu), x.shape[0],
+                                _ptr(residual, torch.float32, "residual"),
+                                _ptr(out, torch.float32, "out"), _ptr(ws, torch.uint8, "ws"),
+                                ws.numel(), _stream(stream)), "smoe_moe_forward")
+
+
+def moe_layer(desc, router_w, experts: Experts, x, out, topk_idx, topk_w, un: UnionBuffers, ws,
+              residual=None, logits=None, stream=None):
+    cu = un.c()
+    _check(lib.smoe_moe_layer(ctypes.byref(desc), _ptr(router_w, None, "router_w"),
+                              ctypes.byref(experts), _ptr(x, torch.float32, "x"), x.shape[0],
+                              _ptr(residual, torch.float32, "residual"),
+                              _ptr(out, torch.float32, "out"),
+                              _ptr(logits, torch.float32, "logits"),
+                              _ptr(topk_idx, torch.int32, "topk_idx"),
+                              _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu),
+                              _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+           "smoe_moe_layer")
+
+
+def moe_layer_stage(stage, desc, router_w, experts: Experts, x, out, topk_idx, topk_w,
+                    un: UnionBuffers, ws, residual=None, logits=None, stream=None):
+    cu = un.c()
+    _check(lib.smoe_moe_layer_stage(stage, ctypes.byref(desc), _ptr(router_w, None, "router_w"),
+                                    ctypes.byref(experts), _ptr(x, torch.float32, "x"), x.shape[0],
+                                    _ptr(residual, torch.float32, "residual"),
+                                    _ptr(out, torch.float32, "out"),
+                                    _ptr(logits, torch.float32, "logits"),
+                                    _ptr(topk_idx, torch.int32, "topk_idx"),
+                                    _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu),
+                                    _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+           "smoe_moe_layer_stage")
+
+
+def read_status(ws, stream=None) -> int:
+    v = ctypes.c_uint32(0)
+    _check(lib.smoe_read_status(_ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream),
+                                ctypes.byref(v)), "smoe_read_status")
+    return int(v.value)
+
+
+class Layer:
+    """Device tensors and descriptors of one layer, plus its scratch buffers.
+
+    ``weights`` maps 'router' and 'gate'/'up'/'down' (each a (w, s, b) triple
+    of CUDA tensors with a leading expert axis) or 'gate_up' (fused, gate rows
+    on top) + 'down'.
+    """
+
+    def __init__(self, desc: LayerDesc, weights: dict, max_batch: int = MAX_BATCH,
+                 device="cuda"):
+        self.desc = desc
+        self.w = weights
+        self.router_w = weights["router"]
+        f, d = desc.ffn_dim, desc.d_model
+        if "gate_up" in weights:
+            gw, gs, gb = weights["gate_up"]
+            gate = qmat(gw[:, :f], gs[:, :f], gb[:, :f], gw.stride(0), gs.stride(0))
+            up = qmat(gw[:, f:], gs[:, f:], gb[:, f:], gw.stride(0), gs.stride(0))
+        else:
+            gate = qmat(*weights["gate"])
+            up = qmat(*weights["up"])
+        down = qmat(*weights["down"])
+        self.experts = Experts(gate, up, down)
+        self.max_batch = max_batch
+        nbytes = workspace_size(desc, max_batch)
+        if nbytes == 0:
+            raise SmoeError(SMOE_EUNSUPPORTED, "smoe_workspace_size")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        workspace_init(self.ws)
+        P = max_batch * desc.top_k
+        self.union = UnionBuffers.alloc(desc.num_experts, P, device)
+        i = dict(device=device)
+        self.topk_idx = torch.zeros(max_batch, desc.top_k, dtype=torch.int32, **i)
+        self.topk_w = torch.zeros(max_batch, desc.top_k, dtype=torch.float32, **i)
+        self.logits = torch.zeros(max_batch, desc.num_experts, dtype=torch.float32, **i)
+
+    def forward(self, x, out=None, residual=None, want_logits=False, stream=None):
+        B = x.shape[0]
+        if out is None:
+            out = torch.empty(B, self.desc.d_model, dtype=torch.float32, device=x.device)
+        moe_layer(self.desc, self.router_w, self.experts, x, out, self.topk_idx[:B],
+                  self.topk_w[:B], self.union, self.ws, residual=residual,
+                  logits=self.logits[:B] if want_logits else None, stream=stream)
+        return out

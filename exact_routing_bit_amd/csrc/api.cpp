@@ -1,0 +1,311 @@
+// api.cpp - the C-ABI entry points of libsmoe (declared in include/smoe.h).
+//
+// Every entry point validates all arguments on the host before launching
+// anything, then enqueues kernels on the caller's stream and returns without
+// synchronising (smoe_read_status excepted).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "smoe_internal.hpp"
+
+#define SMOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using smoe::WsLayout;
+
+constexpr int kMaxDim = 8192;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_desc(const smoe_layer_desc* L) {
+  if (L == nullptr) return SMOE_EINVAL;
+  if (L->group_size != SMOE_GROUP) return SMOE_EUNSUPPORTED;
+  if (L->d_model < 64 || L->d_model > kMaxDim || L->d_model % 64 != 0) return SMOE_EUNSUPPORTED;
+  if (L->ffn_dim < 64 || L->ffn_dim > kMaxDim || L->ffn_dim % 64 != 0) return SMOE_EUNSUPPORTED;
+  if (L->num_experts < 1 || L->num_experts > SMOE_MAX_EXPERTS) return SMOE_EUNSUPPORTED;
+  if (L->top_k < 1 || L->top_k > SMOE_MAX_TOPK || L->top_k > L->num_experts)
+    return SMOE_EUNSUPPORTED;
+  if (L->norm_topk_prob != 0 && L->norm_topk_prob != 1) return SMOE_EINVAL;
+  if (L->router_dtype != SMOE_F32 && L->router_dtype != SMOE_BF16) return SMOE_EUNSUPPORTED;
+  return SMOE_OK;
+}
+
+int check_batch(int32_t B) {
+  if (B < 0) return SMOE_EINVAL;
+  if (B > SMOE_MAX_BATCH) return SMOE_EUNSUPPORTED;
+  return SMOE_OK;
+}
+
+int check_ws(const smoe_layer_desc* L, int32_t B, const void* ws, size_t ws_bytes) {
+  if (ws == nullptr || !aligned(ws, 256)) return SMOE_EINVAL;
+  if (ws_bytes < smoe::ws_layout(*L, B).total) return SMOE_EWORKSPACE;
+  return SMOE_OK;
+}
+
+int check_union(const smoe_union* un) {
+  if (un == nullptr || un->n_union == nullptr || un->union_experts == nullptr ||
+      un->expert_offsets == nullptr || un->pair_list == nullptr || un->pair_pos == nullptr)
+    return SMOE_EINVAL;
+  return SMOE_OK;
+}
+
+int check_qmat(const smoe_qmat& m, int rows, int cols) {
+  if (m.w == nullptr || m.s == nullptr || m.b == nullptr) return SMOE_EINVAL;
+  if (!aligned(m.w, 16) || !aligned(m.s, 2) || !aligned(m.b, 2)) return SMOE_EINVAL;
+  // every expert's matrix must start 16-byte aligned and not overlap the next
+  if (m.expert_stride_w < (int64_t)rows * cols / 8 || (m.expert_stride_w * 4) % 16 != 0)
+    return SMOE_EINVAL;
+  if (m.expert_stride_sb < (int64_t)rows * cols / 64) return SMOE_EINVAL;
+  return SMOE_OK;
+}
+
+int check_experts(const smoe_layer_desc* L, const smoe_experts* ex) {
+  if (ex == nullptr) return SMOE_EINVAL;
+  int rc = check_qmat(ex->gate, L->ffn_dim, L->d_model);
+  if (rc == SMOE_OK) rc = check_qmat(ex->up, L->ffn_dim, L->d_model);
+  if (rc == SMOE_OK) rc = check_qmat(ex->down, L->d_model, L->ffn_dim);
+  return rc;
+}
+
+template <class T>
+T* ws_at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+smoe::QMat to_q(const smoe_qmat& m) {
+  return smoe::QMat{m.w, m.s, m.b, m.expert_stride_w, m.expert_stride_sb};
+}
+
+smoe::FfnArgs ffn_args(const smoe_layer_desc* L, const smoe_experts* ex, const smoe_union* un,
+                       const float* topk_w, int32_t B, const float* residual, float* out, void* ws,
+                       const WsLayout& lay) {
+  smoe::FfnArgs a{};
+  a.gate = to_q(ex->gate);
+  a.up = to_q(ex->up);
+  a.down = to_q(ex->down);
+  a.B = B;
+  a.d = L->d_model;
+  a.f = L->ffn_dim;
+  a.E = L->num_experts;
+  a.K = L->top_k;
+  a.n_union = un->n_union;
+  a.union_experts = un->union_experts;
+  a.expert_offsets = un->expert_offsets;
+  a.pair_list = un->pair_list;
+  a.pair_pos = un->pair_pos;
+  a.topk_w = topk_w;
+  a.residual = residual;
+  a.out = out;
+  a.xp = ws_at<uint16_t>(ws, lay.xp);
+  a.xs = ws_at<float2>(ws, lay.xs);
+  a.hp = ws_at<uint16_t>(ws, lay.hp);
+  a.hs = ws_at<float2>(ws, lay.hs);
+  a.y = ws_at<float>(ws, lay.y);
+  return a;
+}
+
+int hip_rc(hipError_t e) { return e == hipSuccess ? SMOE_OK : SMOE_EHIP; }
+
+}  // namespace
+
+SMOE_API size_t smoe_workspace_size(const smoe_layer_desc* desc, int32_t max_batch) {
+  if (check_desc(desc) != SMOE_OK || max_batch < 1 || max_batch > SMOE_MAX_BATCH) return 0;
+  return smoe::ws_layout(*desc, max_batch).total;
+}
+
+SMOE_API int smoe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < 256) return SMOE_EINVAL;
+  return hip_rc(smoe::launch_fill_u32(static_cast<uint32_t*>(ws), 0u, 64,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+SMOE_API int smoe_route(const smoe_layer_desc* desc, const void* router_w, const float* x,
+                        int32_t B, float* logits, int32_t* topk_idx, float* topk_w,
+                        uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc == SMOE_OK) rc = check_batch(B);
+  if (rc != SMOE_OK) return rc;
+  if ((flags & ~SMOE_ROUTE_LOGITS_IN) != 0) return SMOE_EINVAL;
+  if (B == 0) return SMOE_OK;
+  const bool logits_in = (flags & SMOE_ROUTE_LOGITS_IN) != 0;
+  if (topk_idx == nullptr || topk_w == nullptr) return SMOE_EINVAL;
+  if (logits_in && logits == nullptr) return SMOE_EINVAL;
+  if (!logits_in) {
+    if (router_w == nullptr || x == nullptr || !aligned(router_w, 16) || !aligned(x, 16))
+      return SMOE_EINVAL;
+  }
+  rc = check_ws(desc, B, ws, ws_bytes);
+  if (rc != SMOE_OK) return rc;
+  const WsLayout lay = smoe::ws_layout(*desc, B);
+  smoe::RouteArgs a{};
+  a.router_w = router_w;
+  a.router_bf16 = desc->router_dtype == SMOE_BF16;
+  a.x = x;
+  a.B = B;
+  a.d = desc->d_model;
+  a.E = desc->num_experts;
+  a.K = desc->top_k;
+  a.norm = desc->norm_topk_prob;
+  a.logits = logits ? logits : ws_at<float>(ws, lay.logits);
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.status = ws_at<uint32_t>(ws, lay.status);
+  return hip_rc(smoe::launch_router(a, logits_in, true, false, static_cast<hipStream_t>(stream)));
+}
+
+SMOE_API int smoe_build_union(const smoe_layer_desc* desc, const int32_t* topk_idx, int32_t B,
+                              const smoe_union* un, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc == SMOE_OK) rc = check_batch(B);
+  if (rc == SMOE_OK) rc = check_union(un);
+  if (rc != SMOE_OK) return rc;
+  if (topk_idx == nullptr && B > 0) return SMOE_EINVAL;
+  rc = check_ws(desc, B, ws, ws_bytes);
+  if (rc != SMOE_OK) return rc;
+  const WsLayout lay = smoe::ws_layout(*desc, B);
+  smoe::RouteArgs a{};
+  a.B = B;
+  a.d = desc->d_model;
+  a.E = desc->num_experts;
+  a.K = desc->top_k;
+  a.topk_idx = const_cast<int32_t*>(topk_idx);  // read-only in union-only mode
+  a.status = ws_at<uint32_t>(ws, lay.status);
+  a.n_union = un->n_union;
+  a.union_experts = un->union_experts;
+  a.expert_offsets = un->expert_offsets;
+  a.pair_list = un->pair_list;
+  a.pair_pos = un->pair_pos;
+  // B == 0 still writes n_union = 0 so that a later forward is a no-op
+  return hip_rc(smoe::launch_router(a, true, false, true, static_cast<hipStream_t>(stream)));
+}
+
+SMOE_API int smoe_moe_forward(const smoe_layer_desc* desc, const smoe_experts* experts,
+                              const float* x, const int32_t* topk_idx, const float* topk_w,
+                              const smoe_union* un, int32_t B, const float* residual, float* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc == SMOE_OK) rc = check_batch(B);
+  if (rc == SMOE_OK) rc = check_union(un);
+  if (rc == SMOE_OK) rc = check_experts(desc, experts);
+  if (rc != SMOE_OK) return rc;
+  if (B == 0) return SMOE_OK;
+  if (x == nullptr || topk_idx == nullptr || topk_w == nullptr || out == nullptr ||
+      !aligned(x, 16) || !aligned(out, 16) || (residual != nullptr && !aligned(residual, 16)))
+    return SMOE_EINVAL;
+  rc = check_ws(desc, B, ws, ws_bytes);
+  if (rc != SMOE_OK) return rc;
+  const WsLayout lay = smoe::ws_layout(*desc, B);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  smoe::FfnArgs a = ffn_args(desc, experts, un, topk_w, B, residual, out, ws, lay);
+  hipError_t err = smoe::launch_prep(x, B, desc->d_model, ws_at<uint16_t>(ws, lay.xp),
+                                     ws_at<float2>(ws, lay.xs), s);
+  if (err != hipSuccess) return SMOE_EHIP;
+  return hip_rc(smoe::launch_ffn(a, s));
+}
+
+namespace {
+
+// Validation and argument set-up shared by smoe_moe_layer and its stages.
+int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_experts* experts,
+                const float* x, int32_t B, const float* residual, float* out, float* logits,
+                int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
+                smoe::RouteArgs* r, smoe::FfnArgs* a) {
+  int rc = check_desc(desc);
+  if (rc == SMOE_OK) rc = check_batch(B);
+  if (rc == SMOE_OK) rc = check_union(un);
+  if (rc == SMOE_OK) rc = check_experts(desc, experts);
+  if (rc != SMOE_OK) return rc;
+  if (B == 0) return SMOE_OK;
+  if (router_w == nullptr || x == nullptr || out == nullptr || topk_idx == nullptr ||
+      topk_w == nullptr || !aligned(router_w, 16) || !aligned(x, 16) || !aligned(out, 16) ||
+      (residual != nullptr && !aligned(residual, 16)))
+    return SMOE_EINVAL;
+  rc = check_ws(desc, B, ws, ws_bytes);
+  if (rc != SMOE_OK) return rc;
+  const WsLayout lay = smoe::ws_layout(*desc, B);
+  *r = smoe::RouteArgs{};
+  r->router_w = router_w;
+  r->router_bf16 = desc->router_dtype == SMOE_BF16;
+  r->x = x;
+  r->B = B;
+  r->d = desc->d_model;
+  r->E = desc->num_experts;
+  r->K = desc->top_k;
+  r->norm = desc->norm_topk_prob;
+  r->logits = logits ? logits : ws_at<float>(ws, lay.logits);
+  r->topk_idx = topk_idx;
+  r->topk_w = topk_w;
+  r->status = ws_at<uint32_t>(ws, lay.status);
+  r->xp = ws_at<uint16_t>(ws, lay.xp);
+  r->xs = ws_at<float2>(ws, lay.xs);
+  r->n_union = un->n_union;
+  r->union_experts = un->union_experts;
+  r->expert_offsets = un->expert_offsets;
+  r->pair_list = un->pair_list;
+  r->pair_pos = un->pair_pos;
+  *a = ffn_args(desc, experts, un, topk_w, B, residual, out, ws, lay);
+  return SMOE_OK;
+}
+
+}  // namespace
+
+SMOE_API int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w,
+                            const smoe_experts* experts, const float* x, int32_t B,
+                            const float* residual, float* out, float* logits, int32_t* topk_idx,
+                            float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
+                            void* stream) {
+  smoe::RouteArgs r;
+  smoe::FfnArgs a;
+  const int rc = layer_setup(desc, router_w, experts, x, B, residual, out, logits, topk_idx,
+                             topk_w, un, ws, ws_bytes, &r, &a);
+  if (rc != SMOE_OK || B == 0) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = smoe::launch_router(r, false, true, true, s);
+  if (err == hipSuccess) err = smoe::launch_ffn(a, s);
+  return hip_rc(err);
+}
+
+SMOE_API int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* router_w,
+                                  const smoe_experts* experts, const float* x, int32_t B,
+                                  const float* residual, float* out, float* logits,
+                                  int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  if (stage < SMOE_STAGE_ROUTE || stage > SMOE_STAGE_COMBINE) return SMOE_EINVAL;
+  smoe::RouteArgs r;
+  smoe::FfnArgs a;
+  const int rc = layer_setup(desc, router_w, experts, x, B, residual, out, logits, topk_idx,
+                             topk_w, un, ws, ws_bytes, &r, &a);
+  if (rc != SMOE_OK || B == 0) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (stage) {
+    case SMOE_STAGE_ROUTE: return hip_rc(smoe::launch_router(r, false, true, true, s));
+    case SMOE_STAGE_GATE_UP: return hip_rc(smoe::launch_gate_up(a, s));
+    case SMOE_STAGE_DOWN: return hip_rc(smoe::launch_down(a, s));
+    default: return hip_rc(smoe::launch_combine(a, s));
+  }
+}
+
+SMOE_API int smoe_read_status(const void* ws, size_t ws_bytes, void* stream,
+                              uint32_t* status_out) {
+  if (ws == nullptr || ws_bytes < 256 || status_out == nullptr) return SMOE_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return SMOE_EHIP;
+  uint32_t v = 0;
+  if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return SMOE_EHIP;
+  *status_out = v;
+  return SMOE_OK;
+}
+
+SMOE_API const char* smoe_strerror(int code) {
+  switch (code) {
+    case SMOE_OK: return "success";
+    case SMOE_EINVAL: return "invalid argument (null or misaligned pointer, bad flag or batch)";
+    case SMOE_EUNSUPPORTED: return "unsupported shape or dtype";
+    case SMOE_EWORKSPACE: return "workspace too small";
+    case SMOE_EHIP: return "HIP runtime or kernel launch error";
+    default: return "unknown error code";
+  }
+}

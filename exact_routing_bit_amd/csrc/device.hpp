@@ -1,0 +1,111 @@
+// device.hpp - device-side helpers of libsmoe (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smoe {
+
+typedef _Float16 half_t;
+typedef half_t half2_t __attribute__((ext_vector_type(2)));
+typedef half_t half8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming loads of weight words: marked nontemporal so that the expert
+// bytes, read once, do not evict the activations from the caches.
+__device__ __forceinline__ uint4 ld_stream4(const uint32_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream2(const uint32_t* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+__device__ __forceinline__ uint16_t f16_bits(half_t h) { return __builtin_bit_cast(uint16_t, h); }
+__device__ __forceinline__ half_t bits_f16(uint16_t u) { return __builtin_bit_cast(half_t, u); }
+
+// Four fp16 pairs from one packed word of eight 4-bit codes q0..q7
+// (q_i at bits 4i..4i+3).  OR-ing a code into the mantissa of 1024.0h
+// (0x6400) gives 1024 + code exactly (the magic-number conversion of Kim et
+// al., "Who Says Elephants Can't Run", 2022).  Codes at bit offset 4 inside
+// a half land at mantissa bits 4..7 and read as 1024 + 16*code, so the
+// activation paired with them is pre-divided by 16:
+//   p0 = (1024+q0, 1024+q4)        p1 = (1024+16 q1, 1024+16 q5)
+//   p2 = (1024+q2, 1024+q6)        p3 = (1024+16 q3, 1024+16 q7)
+// Five integer ops per word.
+__device__ __forceinline__ void dequant_word(uint32_t w, uint32_t p[4]) {
+  constexpr uint32_t kMagic = 0x64006400u;
+  p[0] = (w & 0x000F000Fu) | kMagic;
+  p[1] = (w & 0x00F000F0u) | kMagic;
+  const uint32_t w8 = w >> 8;
+  p[2] = (w8 & 0x000F000Fu) | kMagic;
+  p[3] = (w8 & 0x00F000F0u) | kMagic;
+}
+
+// acc + sum over the word's 8 inputs of (1024 + m*q) * stored, where the
+// prepped activation chunk xc holds the matching stored halves.
+__device__ __forceinline__ float dot_word(uint32_t w, const uint4& xc, float acc) {
+  uint32_t p[4];
+  dequant_word(w, p);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, p[0]), __builtin_bit_cast(half2_t, xc.x),
+                               acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, p[1]), __builtin_bit_cast(half2_t, xc.y),
+                               acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, p[2]), __builtin_bit_cast(half2_t, xc.z),
+                               acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, p[3]), __builtin_bit_cast(half2_t, xc.w),
+                               acc, false);
+  return acc;
+}
+
+// The MFMA operand (8 halves) of one packed word, in the same slot order.
+__device__ __forceinline__ half8_t word_operand(uint32_t w) {
+  uint32_t p[4];
+  dequant_word(w, p);
+  uint4 v = make_uint4(p[0], p[1], p[2], p[3]);
+  return __builtin_bit_cast(half8_t, v);
+}
+
+// Sum over aligned segments of `width` lanes (power of two <= 64); every lane
+// of a segment gets the segment total.  Fixed butterfly order.
+__device__ __forceinline__ float segment_sum(float v, int width) {
+  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return segment_sum(v, 64); }
+
+// The stored halves of 8 consecutive inputs (one packed word's worth) in the
+// prepped order, plus their contributions to the group sums X and C/1024.
+__device__ __forceinline__ uint4 prep_chunk(const float v[8], float* X, float* S) {
+  uint16_t hsv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const half_t xi = (half_t)v[i];                       // round to nearest even
+    const half_t st = (i & 1) ? (half_t)((float)xi * 0.0625f) : xi;
+    hsv[i] = f16_bits(st);
+    const float stf = (float)st;
+    *S += stf;
+    *X += (i & 1) ? stf * 16.0f : stf;
+  }
+  // slot order: (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+  uint4 c;
+  c.x = (uint32_t)hsv[0] | ((uint32_t)hsv[4] << 16);
+  c.y = (uint32_t)hsv[1] | ((uint32_t)hsv[5] << 16);
+  c.z = (uint32_t)hsv[2] | ((uint32_t)hsv[6] << 16);
+  c.w = (uint32_t)hsv[3] | ((uint32_t)hsv[7] << 16);
+  return c;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+}  // namespace smoe

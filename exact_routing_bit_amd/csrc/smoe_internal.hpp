@@ -1,0 +1,132 @@
+// smoe_internal.hpp - shared declarations of libsmoe's kernels and host code.
+//
+// Data layouts in device memory (all row-major):
+//   quantised weights  u32 [rows, cols/8], element c at bits 4*(c%8) of word
+//                      c/8; bf16 scale/bias [rows, cols/64]
+//                      ("SSD Streaming Expert Layers", "Quantized Layout").
+//   prepped activations fp16 [rows, K]: for every 8 consecutive inputs
+//                      x0..x7 (one packed weight word) the 8 halves are
+//                      (x0, x4), (x1/16, x5/16), (x2, x6), (x3/16, x7/16),
+//                      the pairing that the nibble-to-fp16 conversion of a
+//                      word produces (see dequant_word).  Per 64-input group:
+//                      X = sum of the fp16 inputs, C = 1024 * sum of the
+//                      stored halves (float2 per group).
+//   h (gate/up output) is stored in the same prepped layout, with its group
+//                      sums as two 32-column partials per group.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/smoe.h"
+
+namespace smoe {
+
+// ------------------------------------------------------------ constants
+constexpr int kMaxBatch = SMOE_MAX_BATCH;
+constexpr int kMaxExperts = SMOE_MAX_EXPERTS;
+constexpr int kMaxTopK = SMOE_MAX_TOPK;
+constexpr int kMaxPairs = kMaxBatch * kMaxTopK;
+
+// An expert whose pair count is at most this takes the VALU dot-product path;
+// above it the dequantised tile feeds MFMA.
+constexpr int kValuMaxPairs = 2;
+
+// Expert-FFN blocks: 256 threads, four 16-row weight tiles.
+constexpr int kFfnThreads = 256;
+constexpr int kGateUpCols = 32;   // h columns per gate_up block (32 gate + 32 up rows)
+constexpr int kDownRows = 64;     // output rows per down block
+
+// ------------------------------------------------------------ workspace
+struct WsLayout {
+  size_t status;   // uint32 status word (+ padding)
+  size_t logits;   // [B, E] f32
+  size_t xp;       // [B, d] f16 prepped activations
+  size_t xs;       // [B, d/64] float2 group sums of xp
+  size_t hp;       // [P, f] f16 prepped h
+  size_t hs;       // [P, f/64, 2] float2 half-group sums of hp
+  size_t y;        // [P, d] f32 per-pair expert outputs
+  size_t total;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline WsLayout ws_layout(const smoe_layer_desc& L, int B) {
+  WsLayout w{};
+  const size_t P = (size_t)B * L.top_k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  w.status = take(256);
+  w.logits = take((size_t)B * L.num_experts * 4);
+  w.xp = take((size_t)B * L.d_model * 2);
+  w.xs = take((size_t)B * (L.d_model / 64) * 8);
+  w.hp = take(P * L.ffn_dim * 2);
+  w.hs = take(P * (L.ffn_dim / 64) * 2 * 8);
+  w.y = take(P * L.d_model * 4);
+  w.total = off;
+  return w;
+}
+
+// ------------------------------------------------------- kernel arguments
+struct QMat {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  int64_t stride_w;
+  int64_t stride_sb;
+};
+
+struct RouteArgs {
+  const void* router_w;
+  int router_bf16;
+  const float* x;
+  int B, d, E, K, norm;
+  float* logits;       // read (logits_in) or written
+  int32_t* topk_idx;
+  float* topk_w;
+  uint32_t* status;
+  // prepped activations (written by the router kernel when non-null)
+  uint16_t* xp;
+  float2* xs;
+  // union outputs (built after top-k when non-null)
+  int32_t* n_union;
+  int32_t* union_experts;
+  int32_t* expert_offsets;
+  int32_t* pair_list;
+  int32_t* pair_pos;
+};
+
+struct FfnArgs {
+  QMat gate, up, down;
+  int B, d, f, E, K;
+  const int32_t* n_union;
+  const int32_t* union_experts;
+  const int32_t* expert_offsets;
+  const int32_t* pair_list;
+  const int32_t* pair_pos;
+  const float* topk_w;
+  const float* residual;
+  float* out;
+  const uint16_t* xp;
+  const float2* xs;
+  uint16_t* hp;
+  float2* hs;
+  float* y;
+};
+
+// ------------------------------------------------------------- launchers
+// All return hipSuccess or the launch error.
+hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
+                         hipStream_t s);
+hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, hipStream_t s);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
+hipError_t launch_down(const FfnArgs& a, hipStream_t s);
+hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s);
+
+}  // namespace smoe

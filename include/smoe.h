@@ -1,0 +1,206 @@
+/*
+ * smoe.h - C-ABI of libsmoe: one routed mixture-of-experts layer on an
+ * AMD Instinct MI355X (gfx950), every expert resident in device memory.
+ *
+ * The layer (the pages it follows are named in brackets):
+ *   [LMP] "Layer-Major Batched Prefill" (S-MoE internals docs)
+ *   [DF]  "Data Flow" (S-MoE architecture docs)
+ *   [SSD] "SSD Streaming Expert Layers" (edge0 streaming.md)
+ *   [SC]  "Surface Scout" (S-MoE architecture docs)
+ *
+ *   1. exact routing: router gate matvec on the true hidden state, softmax,
+ *      top-k, norm_topk_prob renormalisation ([DF] serial step "EXACT
+ *      ROUTING"; [LMP] "Choreography Per Chunk" step 5; [SC] model config);
+ *   2. the layer-major inversion: the batch's experts deduplicated into a
+ *      union, each with the list of (token, rank) pairs routed to it
+ *      ([LMP] "The Inversion");
+ *   3. the token-batch fused SwiGLU expert FFN down(silu(gate x) * up x) over
+ *      4-bit affine weights, each union expert's bytes streamed once for all
+ *      of its pairs ([LMP] step 6; [SSD] "Math Contract", "Quantized Layout");
+ *   4. the weighted combine into the residual, in fixed rank order
+ *      ([DF] "gather GPU outputs x routing weights", "residual += ...").
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless a comment says "host".  The
+ *     descriptor structs themselves are host memory, read during the call.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronise, except smoe_read_status.
+ *   - The caller owns every buffer: weights, activations, outputs, union
+ *     lists and the workspace.  The library allocates nothing, keeps no
+ *     state between calls and never frees caller memory.
+ *   - Return 0 on success or a negative SMOE_E* code.  Every argument check
+ *     happens before anything is launched, so a failed call has no effect.
+ *   - Pair p = t*top_k + k is token t's rank-k expert.
+ *   - Calls sharing one workspace must be ordered on one stream.
+ */
+#ifndef SMOE_H
+#define SMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----------------------------------------------------------- error codes */
+#define SMOE_OK 0
+#define SMOE_EINVAL -1        /* null or misaligned pointer, B < 0, bad flag */
+#define SMOE_EUNSUPPORTED -2  /* shape outside the supported range (below) */
+#define SMOE_EWORKSPACE -3    /* workspace too small */
+#define SMOE_EHIP -4          /* a HIP runtime call or kernel launch failed */
+
+/* ------------------------------------------------------------ constants */
+#define SMOE_F32 0            /* router gate element type: fp32 */
+#define SMOE_BF16 1           /* router gate element type: bf16 bit patterns */
+#define SMOE_MAX_BATCH 64     /* tokens per call (a prefill chunk, [DF] Regime 1) */
+#define SMOE_MAX_EXPERTS 256
+#define SMOE_MAX_TOPK 16
+#define SMOE_GROUP 64         /* quantisation group size along the input axis */
+
+/* smoe_route flags */
+#define SMOE_ROUTE_LOGITS_IN 0x1u /* read logits from `logits` instead of computing them */
+
+/* Device status bits, accumulated in the workspace until cleared. */
+#define SMOE_STATUS_BAD_EXPERT 0x1u /* an expert id outside [0, E) was given; its pair is skipped */
+
+/* ----------------------------------------------------------- descriptors */
+/* Supported: d_model and ffn_dim multiples of 64 in [64, 8192];
+ * 1 <= num_experts <= 256; 1 <= top_k <= min(num_experts, 16);
+ * group_size == 64; router_dtype SMOE_F32 or SMOE_BF16. */
+typedef struct smoe_layer_desc {
+  int32_t d_model;
+  int32_t ffn_dim;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t group_size;     /* must be 64 */
+  int32_t norm_topk_prob; /* 1: top-k weights renormalised to sum 1; 0: raw softmax */
+  int32_t router_dtype;   /* SMOE_F32 or SMOE_BF16 */
+} smoe_layer_desc;
+
+/* One quantised projection of every expert ([SSD] "Quantized Layout"):
+ * expert e's matrix [rows, cols] is w + e*expert_stride_w (u32 words,
+ * row-major [rows, cols/8]; element c of a row is bits 4*(c%8)..+3 of word
+ * c/8) with per-group bf16 scale s and bias b at s/b + e*expert_stride_sb
+ * ([rows, cols/64]); the weight is s*q + b.  Strides are in elements.
+ * w, s and b must be 16-byte aligned; with 4 KiB alignment or better, rows
+ * keep their 16-byte alignment for every supported shape. */
+typedef struct smoe_qmat {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+  int64_t expert_stride_w;
+  int64_t expert_stride_sb;
+} smoe_qmat;
+
+/* gate and up are [ffn_dim, d_model] per expert, down is [d_model, ffn_dim].
+ * The fused gate_up layout of [SSD] ("gate rows on top, up rows below",
+ * [E, 2*ffn_dim, d_model/8]) is expressed as gate.w = gu,
+ * up.w = gu + ffn_dim*d_model/8, both with expert_stride_w = 2*ffn_dim*d_model/8
+ * (and likewise for s and b). */
+typedef struct smoe_experts {
+  smoe_qmat gate;
+  smoe_qmat up;
+  smoe_qmat down;
+} smoe_experts;
+
+/* The layer-major inversion ([LMP] "The Inversion"), all int32 device arrays:
+ *   n_union[1]                 number of distinct experts routed to;
+ *   union_experts[min(E,B*K)]  those experts, ascending;
+ *   expert_offsets[min(E,B*K)+1]  union expert u owns
+ *                              pair_list[expert_offsets[u] .. expert_offsets[u+1]);
+ *   pair_list[B*K]             pairs grouped by union expert, ascending within;
+ *   pair_pos[B*K]              position of pair p in pair_list (-1: skipped). */
+typedef struct smoe_union {
+  int32_t* n_union;
+  int32_t* union_experts;
+  int32_t* expert_offsets;
+  int32_t* pair_list;
+  int32_t* pair_pos;
+} smoe_union;
+
+/* ------------------------------------------------------------ workspace */
+/* Bytes of device workspace needed for calls with up to max_batch tokens
+ * (1..64).  0 when the descriptor is unsupported.  Host only. */
+size_t smoe_workspace_size(const smoe_layer_desc* desc, int32_t max_batch);
+
+/* Clears the workspace's status word.  Call once after allocating a
+ * workspace; afterwards the library keeps it consistent.  Async on stream. */
+int smoe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- routing */
+/* Exact routing of B tokens ([DF] "EXACT ROUTING: gate matvec on
+ * heavy_normed -> ranked top-k", "norm_topk_prob weights"):
+ *   logits[t,e] = sum_i Wr[e,i] * x[t,i]     (fp32 accumulation)
+ *   topk_idx[t,:] = the top_k experts by (logit descending, index ascending)
+ *   topk_w[t,k]   = softmax weight of topk_idx[t,k], renormalised over the
+ *                   top_k when norm_topk_prob.
+ * router_w: [E, d] fp32 or bf16 per desc->router_dtype.  x: [B, d] fp32.
+ * logits: [B, E] fp32; nullable unless SMOE_ROUTE_LOGITS_IN; when given
+ * without the flag it receives the logits.  With SMOE_ROUTE_LOGITS_IN the
+ * logits are read from it and router_w/x may be NULL (top-k stage only).
+ * topk_idx [B, top_k] int32, topk_w [B, top_k] fp32: outputs, rank order.
+ * B == 0 is a no-op. */
+int smoe_route(const smoe_layer_desc* desc, const void* router_w, const float* x, int32_t B,
+               float* logits, int32_t* topk_idx, float* topk_w, uint32_t flags, void* ws,
+               size_t ws_bytes, void* stream);
+
+/* Builds the union and the pair lists from topk_idx [B, top_k] on the
+ * device, with no host synchronisation ([LMP] "dedupe -> expert UNION").
+ * Ids outside [0, E) set SMOE_STATUS_BAD_EXPERT and their pairs are left
+ * out (pair_pos = -1). */
+int smoe_build_union(const smoe_layer_desc* desc, const int32_t* topk_idx, int32_t B,
+                     const smoe_union* un, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------- expert FFN */
+/* The token-batch fused expert FFN and the combine ([LMP] step 6; [SSD]
+ * "Math Contract"; [DF] "residual += shared_out + routed_out"):
+ *   for every union expert e and every pair p = (t, k) in its list:
+ *     h_p = silu(Wg_e x_t) * (Wu_e x_t),   y_p = Wd_e h_p
+ *   out[t] = residual[t] + (w[t,0] y_(t,0) + w[t,1] y_(t,1) + ...), k ascending.
+ * Each union expert's weights are read once for all of its pairs.
+ * x: [B, d] fp32; topk_idx/topk_w as produced by smoe_route (or injected);
+ * un: as produced by smoe_build_union for the same topk_idx;
+ * residual: [B, d] fp32 or NULL (zero); out: [B, d] fp32, may alias residual.
+ * Activations enter the dot products as fp16 and the gate/up output h is kept
+ * as fp16; every sum and the scale/bias arithmetic are fp32. */
+int smoe_moe_forward(const smoe_layer_desc* desc, const smoe_experts* experts, const float* x,
+                     const int32_t* topk_idx, const float* topk_w, const smoe_union* un,
+                     int32_t B, const float* residual, float* out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* The whole layer in one call: smoe_route + smoe_build_union +
+ * smoe_moe_forward with shared launches.  topk_idx, topk_w and un are
+ * written as by those calls; logits (nullable) receives the logits. */
+int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w, const smoe_experts* experts,
+                   const float* x, int32_t B, const float* residual, float* out, float* logits,
+                   int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Diagnostic: enqueue one stage of smoe_moe_layer, so that a caller can put
+ * events between stages and time each one.  Same arguments as
+ * smoe_moe_layer.  Enqueuing SMOE_STAGE_ROUTE, _GATE_UP, _DOWN and _COMBINE
+ * in this order on one stream launches exactly the kernels of one
+ * smoe_moe_layer call, in the same order. */
+#define SMOE_STAGE_ROUTE 0    /* logits + activation prep, top-k + union */
+#define SMOE_STAGE_GATE_UP 1  /* gate/up projections and SwiGLU for every union expert */
+#define SMOE_STAGE_DOWN 2     /* down projection for every union expert */
+#define SMOE_STAGE_COMBINE 3  /* weighted combine into the residual */
+int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* router_w,
+                         const smoe_experts* experts, const float* x, int32_t B,
+                         const float* residual, float* out, float* logits, int32_t* topk_idx,
+                         float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* ------------------------------------------------------------ utilities */
+/* Synchronises `stream`, then copies the workspace status bits into
+ * *status_out (host).  For tests and diagnostics, not for the hot path. */
+int smoe_read_status(const void* ws, size_t ws_bytes, void* stream, uint32_t* status_out);
+
+/* A static, human-readable name for an SMOE_* return code. */
+const char* smoe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMOE_H */

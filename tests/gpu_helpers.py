@@ -1,0 +1,72 @@
+"""Helpers shared by the GPU tests: host<->device marshalling and comparisons.
+Oracle inputs always come from the CPU generator; GPU results are only ever
+compared, never fed to the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from synth import configs
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def up(a) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint32:
+        a = a.view(np.int32)
+    elif a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(dev())
+
+
+def down(t: torch.Tensor) -> np.ndarray:
+    a = t.detach().cpu().numpy()
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    return a
+
+
+def rel_l2(a, ref) -> float:
+    a = np.asarray(a, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(a - ref) / np.linalg.norm(ref))
+
+
+def desc_for(smoe, cfg):
+    return smoe.make_desc(cfg.d_model, cfg.ffn_dim, cfg.num_experts, cfg.top_k,
+                          cfg.norm_topk_prob, cfg.router_bf16)
+
+
+def device_weights(L: dict) -> dict:
+    W = {"router": up(L["router"])}
+    for k in ("gate", "up", "down", "gate_up"):
+        if k in L:
+            W[k] = tuple(up(a) for a in L[k])
+    if "gate_up" in W:
+        del W["gate"], W["up"]
+    return W
+
+
+def small_config(name, d, E, K, f, B, bf16=True, fused=False, norm=True):
+    return configs.LayerConfig(name, d, E, K, f, B, router_bf16=bf16, fused=fused,
+                               norm_topk_prob=norm)
+
+
+def near_tie(logits_row: np.ndarray, K: int) -> bool:
+    """True when the oracle's K-th and (K+1)-th logits are within fp32
+    rounding noise, so two correct implementations may pick either."""
+    s = np.sort(logits_row.astype(np.float64))[::-1]
+    if K >= len(s):
+        return False
+    return (s[K - 1] - s[K]) <= 1e-5 * max(1.0, np.abs(s).max())
+
+
+def oracle_layer(L, x, cfg, residual=None, idx=None, w=None):
+    if idx is None:
+        _, idx, w = oracle.route(L["router"], x, cfg.top_k, cfg.norm_topk_prob)
+    return oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=residual), idx, w

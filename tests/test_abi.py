@@ -1,0 +1,138 @@
+"""The C-ABI library on the host: it loads, exports every declared entry point,
+and rejects bad arguments before launching anything (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smoe.h")
+
+
+def _lib_path():
+    return os.path.join(ROOT, "exact_routing_bit_amd", "libsmoe.so")
+
+
+@pytest.fixture(scope="module")
+def smoe():
+    if not os.path.exists(_lib_path()):
+        from exact_routing_bit_amd import build as b
+        b.build()
+    import exact_routing_bit_amd as m
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smoe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("smoe_route", "smoe_build_union", "smoe_moe_forward", "smoe_moe_layer",
+              "smoe_workspace_size", "smoe_workspace_init", "smoe_read_status", "smoe_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(smoe):
+    lib = ctypes.CDLL(_lib_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(smoe.EXPORTED) <= set(declared_functions())
+
+
+def desc_of(smoe, **kw):
+    base = dict(d_model=4096, ffn_dim=1536, num_experts=128, top_k=8, norm_topk_prob=True,
+                router_bf16=True)
+    base.update(kw)
+    return smoe.make_desc(**base)
+
+
+def test_workspace_size(smoe):
+    d = desc_of(smoe)
+    n1, n64 = smoe.workspace_size(d, 1), smoe.workspace_size(d, 64)
+    assert 0 < n1 < n64
+    # per-pair y [P, d] fp32 dominates at B=64: 512 * 4096 * 4 bytes
+    assert n64 >= 512 * 4096 * 4
+    assert smoe.workspace_size(d, 0) == 0 and smoe.workspace_size(d, 65) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d_model=100), -2), (dict(ffn_dim=96), -2), (dict(d_model=16384), -2),
+    (dict(num_experts=257), -2), (dict(top_k=17, num_experts=32), -2),
+    (dict(top_k=9, num_experts=8), -2), (dict(num_experts=0), -2),
+])
+def test_descriptor_rejected(smoe, kw, code):
+    d = desc_of(smoe, **kw)
+    assert smoe.workspace_size(d, 8) == 0
+    fake = ctypes.c_void_p(4096)
+    rc = smoe.lib.smoe_route(ctypes.byref(d), fake, fake, 1, None, fake, fake, 0, fake, 1 << 30,
+                             None)
+    assert rc == code
+
+
+def test_group_size_and_flags_rejected(smoe):
+    d = desc_of(smoe)
+    d.group_size = 32
+    fake = ctypes.c_void_p(4096)
+    assert smoe.lib.smoe_route(ctypes.byref(d), fake, fake, 1, None, fake, fake, 0, fake, 1 << 30,
+                               None) == smoe.SMOE_EUNSUPPORTED
+    d = desc_of(smoe)
+    assert smoe.lib.smoe_route(ctypes.byref(d), fake, fake, 1, None, fake, fake, 0x10, fake,
+                               1 << 30, None) == smoe.SMOE_EINVAL
+
+
+def test_route_argument_errors(smoe):
+    d = desc_of(smoe)
+    f = ctypes.c_void_p(4096)
+    r = smoe.lib.smoe_route
+    big = 1 << 30
+    assert r(ctypes.byref(d), f, f, -1, None, f, f, 0, f, big, None) == smoe.SMOE_EINVAL
+    assert r(ctypes.byref(d), f, f, 65, None, f, f, 0, f, big, None) == smoe.SMOE_EUNSUPPORTED
+    assert r(ctypes.byref(d), None, f, 1, None, f, f, 0, f, big, None) == smoe.SMOE_EINVAL
+    assert r(ctypes.byref(d), ctypes.c_void_p(4097), f, 1, None, f, f, 0, f, big,
+             None) == smoe.SMOE_EINVAL                                  # misaligned gate
+    assert r(ctypes.byref(d), f, f, 1, None, None, f, 0, f, big, None) == smoe.SMOE_EINVAL
+    assert r(ctypes.byref(d), f, f, 1, None, f, f, smoe.SMOE_ROUTE_LOGITS_IN, f, big,
+             None) == smoe.SMOE_EINVAL                                  # logits_in needs logits
+    assert r(ctypes.byref(d), f, f, 8, None, f, f, 0, f, 1024, None) == smoe.SMOE_EWORKSPACE
+    assert r(ctypes.byref(d), f, f, 8, None, f, f, 0, ctypes.c_void_p(4096 + 16), big,
+             None) == smoe.SMOE_EINVAL                                  # misaligned workspace
+
+
+def test_forward_argument_errors(smoe):
+    d = desc_of(smoe)
+    f = 4096
+    q = smoe.QMat(f, f, f, 1536 * 512, 1536 * 64)
+    qd = smoe.QMat(f, f, f, 4096 * 192, 4096 * 24)
+    ex = smoe.Experts(q, q, qd)
+    un = smoe.Union(f, f, f, f, f)
+    fw = smoe.lib.smoe_moe_forward
+    big = 1 << 30
+    args = lambda **o: dict(dict(desc=ctypes.byref(d), ex=ctypes.byref(ex), x=f, idx=f, w=f,
+                                 un=ctypes.byref(un), B=8, res=None, out=f, ws=f, n=big), **o)
+
+    def call(**o):
+        a = args(**o)
+        return fw(a["desc"], a["ex"], a["x"], a["idx"], a["w"], a["un"], a["B"], a["res"], a["out"],
+                  a["ws"], a["n"], None)
+
+    assert call(ex=None) == smoe.SMOE_EINVAL
+    assert call(un=None) == smoe.SMOE_EINVAL
+    assert call(x=None) == smoe.SMOE_EINVAL
+    assert call(out=f + 4) == smoe.SMOE_EINVAL
+    assert call(res=f + 8) == smoe.SMOE_EINVAL
+    bad_stride = smoe.Experts(smoe.QMat(f, f, f, 1536 * 512 - 4, 1536 * 64), q, qd)
+    assert call(ex=ctypes.byref(bad_stride)) == smoe.SMOE_EINVAL
+    bad_align = smoe.Experts(smoe.QMat(f + 4, f, f, 1536 * 512, 1536 * 64), q, qd)
+    assert call(ex=ctypes.byref(bad_align)) == smoe.SMOE_EINVAL
+    assert call(n=4096) == smoe.SMOE_EWORKSPACE
+    assert call(B=-3) == smoe.SMOE_EINVAL
+
+
+def test_strerror(smoe):
+    for c in (0, -1, -2, -3, -4):
+        assert smoe.strerror(c)
+    assert "unknown" in smoe.strerror(-99)

@@ -1,0 +1,268 @@
+"""Parity of the HIP path (through the C-ABI) with the CPU oracle.
+
+Bars: integer/index outputs bit-exact; routing indices bit-exact when both
+top-k stages see the same logits; layer outputs within relative L2 3e-3
+(expected ~5e-4: activations and h enter the dot products as fp16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import configs
+
+from gpu_helpers import (desc_for, dev, device_weights, down, near_tie, oracle_layer, rel_l2,
+                         small_config, up)
+
+pytestmark = pytest.mark.gpu
+TOL = 3e-3
+
+
+@pytest.fixture(scope="module")
+def smoe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_routing_bit_amd as m
+    return m
+
+
+def new_ws(smoe, desc, B):
+    ws = torch.zeros(smoe.workspace_size(desc, max(1, B)), dtype=torch.uint8, device=dev())
+    smoe.workspace_init(ws)
+    return ws
+
+
+# ------------------------------------------------------------------ generator
+def test_gpu_generator_matches_cpu_generator():
+    import synth.gpu as sg
+    cfg = small_config("gen", 512, 6, 2, 192, 4, fused=True)
+    Lc = synth.make_layer(cfg, layer=3)
+    Lg = sg.make_layer(cfg, layer=3)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(Lg["router"]), Lc["router"])
+    for k in ("gate_up", "down"):
+        for a, b in zip(Lg[k], Lc[k]):
+            assert np.array_equal(down(a).view(b.dtype), b), k
+    xg = sg.hidden(0, 0, 5, 7, 512)
+    assert np.array_equal(down(xg).view(np.uint32), synth.hidden(0, 0, 5, 7, 512).view(np.uint32))
+
+
+# -------------------------------------------------------------------- routing
+ROUTE_CASES = [(configs.TINY, 8), (configs.TINY, 1), (configs.DECODE, 1), (configs.DECODE, 37),
+               (configs.DECODE, 64), (configs.FUSED_B64, 64),
+               (small_config("k16", 256, 16, 16, 64, 5, bf16=False), 5),
+               (small_config("nonorm", 512, 40, 6, 64, 9, norm=False), 9)]
+
+
+@pytest.mark.parametrize("cfg,B", ROUTE_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_route_parity(smoe, cfg, B):
+    desc = desc_for(smoe, cfg)
+    Wr = synth.router(cfg.seed, 0, cfg.num_experts, cfg.d_model, cfg.router_sigma, cfg.router_bf16)
+    x = synth.hidden(cfg.seed, 0, 11, B, cfg.d_model)
+    lg_ref, idx_ref, w_ref = oracle.route(Wr, x, cfg.top_k, cfg.norm_topk_prob)
+    ws = new_ws(smoe, desc, B)
+    lg = torch.zeros(B, cfg.num_experts, dtype=torch.float32, device=dev())
+    idx = torch.zeros(B, cfg.top_k, dtype=torch.int32, device=dev())
+    w = torch.zeros(B, cfg.top_k, dtype=torch.float32, device=dev())
+    smoe.route(desc, up(Wr), up(x), idx, w, ws, logits=lg)
+    lg_g = down(lg)
+    # both fp32 sums sit within a summation-error bound of the exact logits:
+    # |err| <= c * sqrt(d) * 2^-24 * sum_i |w_i x_i| (random-walk growth, c = 8)
+    W64 = (Wr.astype(np.uint32) << 16).view(np.float32).astype(np.float64) if cfg.router_bf16 \
+        else Wr.astype(np.float64)
+    exact = x.astype(np.float64) @ W64.T
+    mag = np.abs(x.astype(np.float64)) @ np.abs(W64).T
+    bound = 8 * np.sqrt(cfg.d_model) * 2.0**-24 * mag + 1e-12
+    assert np.all(np.abs(lg_g - exact) <= bound)
+    assert np.all(np.abs(lg_ref - exact) <= bound)
+    # the GPU's own top-k is exact on the logits it computed
+    idx_own, w_own = oracle.topk_softmax(lg_g, cfg.top_k, cfg.norm_topk_prob)
+    assert np.array_equal(down(idx), idx_own)
+    assert np.allclose(down(w), w_own, rtol=1e-6, atol=1e-7)
+    # fed the oracle's logits, indices are bit-exact and weights match
+    smoe.route(desc, None, None, idx, w, ws, logits=up(lg_ref), logits_in=True)
+    assert np.array_equal(down(idx), idx_ref)
+    assert np.allclose(down(w), w_ref, rtol=1e-6, atol=1e-7)
+    if cfg.norm_topk_prob:
+        assert np.allclose(down(w).sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_topk_ties_lower_index_wins(smoe):
+    cfg = small_config("ties", 64, 40, 6, 64, 3)
+    desc = desc_for(smoe, cfg)
+    lg = np.zeros((3, 40), np.float32)
+    lg[0] = 1.0                                    # all tied
+    lg[1, [39, 7, 20, 3]] = 2.5                   # tie above a flat floor
+    lg[2] = np.arange(40, dtype=np.float32) % 5   # repeated values
+    idx_ref, w_ref = oracle.topk_softmax(lg, 6, True)
+    ws = new_ws(smoe, desc, 3)
+    idx = torch.zeros(3, 6, dtype=torch.int32, device=dev())
+    w = torch.zeros(3, 6, dtype=torch.float32, device=dev())
+    smoe.route(desc, None, None, idx, w, ws, logits=up(lg), logits_in=True)
+    assert np.array_equal(down(idx), idx_ref)
+    assert list(down(idx)[0]) == [0, 1, 2, 3, 4, 5]
+    assert np.allclose(down(w), w_ref, rtol=1e-6)
+
+
+# ---------------------------------------------------------------------- union
+@pytest.mark.parametrize("B,K,E,mode", [(1, 8, 128, "rand"), (8, 4, 16, "rand"),
+                                        (64, 8, 128, "rand"), (37, 8, 256, "rand"),
+                                        (64, 16, 256, "rand"), (64, 8, 128, "same"),
+                                        (3, 1, 1, "rand"), (64, 16, 16, "rand")])
+def test_union_parity(smoe, B, K, E, mode):
+    cfg = small_config("u", 64, E, K, 64, B)
+    desc = desc_for(smoe, cfg)
+    rng = np.random.default_rng(B * 7 + K)
+    if mode == "same":
+        idx = np.tile(np.arange(K, dtype=np.int32), (B, 1))
+    else:
+        idx = np.stack([rng.choice(E, K, replace=False) for _ in range(B)]).astype(np.int32)
+    n, ue, off, pl, pp = oracle.build_union(idx, E)
+    ws = new_ws(smoe, desc, B)
+    un = smoe.UnionBuffers.alloc(E, B * K, dev())
+    smoe.build_union(desc, up(idx), un, ws)
+    assert int(down(un.n_union)[0]) == n
+    assert np.array_equal(down(un.union_experts)[:n], ue)
+    assert np.array_equal(down(un.expert_offsets)[:n + 1], off)
+    assert np.array_equal(down(un.pair_list)[:B * K], pl)
+    assert np.array_equal(down(un.pair_pos)[:B * K], pp)
+    assert smoe.read_status(ws) == 0
+
+
+# -------------------------------------------------------------- expert FFN
+FWD_CASES = [
+    (configs.TINY, 8, False),
+    (configs.TINY, 1, True),
+    (small_config("odd_groups", 512, 24, 6, 192, 13), 13, True),     # f/64 = 3 groups
+    (small_config("ragged", 768, 12, 4, 320, 37), 37, False),        # 12 and 5 groups
+    (small_config("hot", 1024, 8, 4, 256, 64), 64, True),            # up to 4 token tiles
+    (small_config("fused", 512, 32, 8, 128, 64, fused=True), 64, False),
+    (small_config("wide", 2048, 16, 2, 128, 3, bf16=False), 3, True),
+]
+
+
+@pytest.mark.parametrize("cfg,B,with_res", FWD_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_forward_parity_injected_routing(smoe, cfg, B, with_res):
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 1, B, cfg.d_model)
+    res = synth.hidden(cfg.seed, 0, 2, B, cfg.d_model, tensor=synth.T_RESIDUAL) if with_res else None
+    _, idx, w = oracle.route(L["router"], x, cfg.top_k, cfg.norm_topk_prob)
+    ref = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res)
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=B, device=dev())
+    smoe.build_union(desc, up(idx), layer.union, layer.ws)
+    out = torch.empty(B, cfg.d_model, dtype=torch.float32, device=dev())
+    smoe.moe_forward(desc, layer.experts, up(x), up(idx), up(w), layer.union, out, layer.ws,
+                     residual=up(res) if with_res else None)
+    got = down(out)
+    if with_res:
+        err = rel_l2(got - res, ref - res)
+    else:
+        err = rel_l2(got, ref)
+    assert err <= TOL, err
+    assert err <= 1.5e-3, f"precision regression: {err}"
+
+
+@pytest.mark.parametrize("cfg,B", [(configs.TINY, 8), (small_config("l", 1024, 64, 8, 256, 64), 64),
+                                   (small_config("l1", 1024, 64, 8, 256, 1), 1)],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_parity(smoe, cfg, B):
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 3, B, cfg.d_model)
+    ref, idx_ref, w_ref = oracle_layer(L, x, cfg)
+    lg_ref = oracle.router_logits(L["router"], x)
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=B, device=dev())
+    out = down(layer.forward(up(x), want_logits=True))
+    idx = down(layer.topk_idx[:B])
+    bad = [t for t in range(B) if not np.array_equal(idx[t], idx_ref[t])]
+    for t in bad:
+        assert near_tie(lg_ref[t], cfg.top_k), f"routing differs for token {t}"
+    if bad:
+        ref, _, _ = oracle_layer(L, x, cfg, idx=idx, w=down(layer.topk_w[:B]))
+    assert rel_l2(out, ref) <= TOL
+
+
+def test_deterministic_bitwise(smoe):
+    cfg = small_config("det", 1024, 32, 8, 256, 64)
+    L = synth.make_layer(cfg)
+    x = up(synth.hidden(0, 0, 4, 64, 1024))
+    layer = smoe.Layer(desc_for(smoe, cfg), device_weights(L), max_batch=64, device=dev())
+    a = down(layer.forward(x))
+    b = down(layer.forward(x))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_integer_case_bit_exact(smoe):
+    """s=1 and small integer biases, one-hot inputs, unit routing weights: every
+    value on both paths is an exact integer, so GPU and oracle agree bit for
+    bit.  Pins nibble order, row order, group indexing and the pair mapping."""
+    d, f, E, K, B = 512, 256, 8, 2, 6
+    rng = np.random.default_rng(5)
+
+    def quant(rows, cols, lo, hi, bias):
+        q = rng.integers(lo, hi + 1, (E, rows, cols)).astype(np.uint32)
+        w = np.zeros((E, rows, cols // 8), np.uint32)
+        for i in range(8):
+            w |= q[..., i::8] << (4 * i)
+        s = np.full((E, rows, cols // 64), 0x3F80, np.uint16)               # 1.0
+        b = np.full((E, rows, cols // 64), np.float32(bias).view(np.uint32) >> 16, np.uint16)
+        return w, s, b
+
+    gate = quant(f, d, 0, 15, 20.0)     # g in [20, 35]: silu(g) == g in fp32
+    upp = quant(f, d, 4, 11, -8.0)      # u in [-4, 3]
+    dn = quant(d, f, 0, 15, 0.0)
+    x = np.zeros((B, d), np.float32)
+    for t in range(B):
+        x[t, rng.integers(0, d)] = 1.0
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(B)]).astype(np.int32)
+    w = np.ones((B, K), np.float32)
+    ref = oracle.moe(gate, upp, dn, x, idx, w)
+    assert np.all(ref == np.round(ref))
+    cfg = small_config("int", d, E, K, f, B)
+    desc = desc_for(smoe, cfg)
+    W = {"router": up(np.zeros((E, d), np.uint16)), "gate": tuple(map(up, gate)),
+         "up": tuple(map(up, upp)), "down": tuple(map(up, dn))}
+    layer = smoe.Layer(desc, W, max_batch=B, device=dev())
+    smoe.build_union(desc, up(idx), layer.union, layer.ws)
+    out = torch.empty(B, d, dtype=torch.float32, device=dev())
+    smoe.moe_forward(desc, layer.experts, up(x), up(idx), up(w), layer.union, out, layer.ws)
+    assert np.array_equal(down(out), ref)
+
+
+def test_bad_expert_sets_status_and_skips_pair(smoe):
+    cfg = small_config("bad", 256, 16, 4, 128, 4)
+    L = synth.make_layer(cfg)
+    x = synth.hidden(0, 0, 6, 4, 256)
+    _, idx, w = oracle.route(L["router"], x, 4)
+    idx_bad = idx.copy()
+    idx_bad[2, 1] = 999
+    idx_bad[0, 3] = -1
+    w_ref = w.copy()
+    w_ref[2, 1] = 0.0
+    w_ref[0, 3] = 0.0
+    ref = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w_ref)
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=4, device=dev())
+    assert smoe.read_status(layer.ws) == 0
+    smoe.build_union(desc, up(idx_bad), layer.union, layer.ws)
+    pp = down(layer.union.pair_pos)[:16]
+    assert pp[2 * 4 + 1] == -1 and pp[0 * 4 + 3] == -1
+    out = torch.empty(4, 256, dtype=torch.float32, device=dev())
+    smoe.moe_forward(desc, layer.experts, up(x), up(idx_bad), up(w), layer.union, out, layer.ws)
+    assert smoe.read_status(layer.ws) & smoe.SMOE_STATUS_BAD_EXPERT
+    assert rel_l2(down(out), ref) <= TOL
+
+
+def test_empty_batch_is_noop(smoe):
+    cfg = configs.TINY
+    L = synth.make_layer(cfg)
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=8, device=dev())
+    x = torch.zeros(0, cfg.d_model, dtype=torch.float32, device=dev())
+    out = layer.forward(x)
+    assert out.shape == (0, cfg.d_model)
+    smoe.build_union(desc, torch.zeros(0, cfg.top_k, dtype=torch.int32, device=dev()), layer.union,
+                     layer.ws)
+    assert int(down(layer.union.n_union)[0]) == 0
