@@ -204,7 +204,7 @@ def main():
                    "layers_rotated": args.layers, "mean_union": u1,
                    "effective_bytes_per_step": int(u1 * eb)},
         "effective_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "k_expert_ffn<gate_up>",
+        "roofline": {"bound": "hbm", "kernel": "k_gate_up_gemv<1>",
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                      "bytes_per_launch": int(gu_bytes), "mean_launch_us": round(gu_s * 1e6, 3)},

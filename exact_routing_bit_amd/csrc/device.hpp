@@ -73,14 +73,71 @@ __device__ __forceinline__ half8_t word_operand(uint32_t w) {
   return __builtin_bit_cast(half8_t, v);
 }
 
-// Sum over aligned segments of `width` lanes (power of two <= 64); every lane
-// of a segment gets the segment total.  Fixed butterfly order.
-__device__ __forceinline__ float segment_sum(float v, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+// ----------------------------------------------------- cross-lane reductions
+// DPP lane moves (VALU, a few cycles each) instead of ds_bpermute shuffles.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF,
+                                                            0xF, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
+
+__device__ __forceinline__ float readlane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+// Sum over aligned segments of `width` lanes (1, 2, 4, 8 or 16); every lane of
+// a segment gets the segment total (each lane in a fixed order).
+__device__ __forceinline__ float segment_sum16(float v, int width) {
+  if (width >= 2) v += dpp<kDppXor1>(v);
+  if (width >= 4) v += dpp<kDppXor2>(v);
+  if (width >= 8) v += dpp<kDppHalfMirror>(v);
+  if (width >= 16) v += dpp<kDppMirror>(v);
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return segment_sum(v, 64); }
+// Wave-wide sum, the same value in every lane: 16-lane DPP sums, then the
+// four row totals added in lane order 0, 16, 32, 48.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = segment_sum16(v, 16);
+  return ((readlane(v, 0) + readlane(v, 16)) + readlane(v, 32)) + readlane(v, 48);
+}
+
+// Sum over aligned segments of `width` lanes (power of two <= 64).  For width
+// <= 16 every lane of a segment gets the total; for 32 and 64 the total is
+// returned to every lane of the segment through readlane.
+__device__ __forceinline__ float segment_sum(float v, int width) {
+  if (width <= 16) return segment_sum16(v, width);
+  v = segment_sum16(v, 16);
+  if (width == 64) return ((readlane(v, 0) + readlane(v, 16)) + readlane(v, 32)) + readlane(v, 48);
+  const float lo = readlane(v, 0) + readlane(v, 16);
+  const float hi = readlane(v, 32) + readlane(v, 48);
+  return (__lane_id() < 32) ? lo : hi;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp<kDppMirror>(v));
+  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kDppXor1>(v));
+  v = min(v, dpp_i<kDppXor2>(v));
+  v = min(v, dpp_i<kDppHalfMirror>(v));
+  v = min(v, dpp_i<kDppMirror>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
 
 // The stored halves of 8 consecutive inputs (one packed word's worth) in the
 // prepped order, plus their contributions to the group sums X and C/1024.

@@ -1,14 +1,17 @@
 // router.hip - exact routing and the layer-major inversion on the device.
 //
-//  k_logits_prep : logits[t,e] = sum_i Wr[e,i] x[t,i] (fp32), one wave per
-//                  (expert, 8-token tile); the same launch converts x to the
-//                  prepped fp16 activation layout the expert kernels read.
-//  k_topk_union  : one workgroup.  Top-k per token by (logit desc, index asc)
-//                  with softmax / norm_topk_prob weights ("Data Flow", serial
-//                  step "EXACT ROUTING"; "Surface Scout", model config), then
-//                  the union of the batch's experts and the per-expert pair
-//                  lists ("Layer-Major Batched Prefill", "The Inversion"),
-//                  all from LDS, with no host synchronisation.
+// One launch does the whole routing step ("Data Flow", serial step "EXACT
+// ROUTING: gate matvec on heavy_normed -> ranked top-k", "norm_topk_prob
+// weights"; "Layer-Major Batched Prefill", "The Inversion"):
+//   1. every block computes logits[t,e] = sum_i Wr[e,i] x[t,i] (fp32) for a
+//      tile of experts x tokens, and converts a share of x into the prepped
+//      fp16 activation layout the expert kernels read;
+//   2. the last block to finish (an integer ticket; grids stay <= 64 blocks so
+//      the tickets do not queue up) ranks every token's experts by (logit
+//      descending, index ascending), forms the softmax / norm_topk_prob
+//      weights, and builds the union of the batch's experts with the sorted
+//      per-expert pair lists, all from LDS.
+// No host synchronisation; downstream grids read n_union on the device.
 #include <float.h>
 #include <limits.h>
 
@@ -18,8 +21,10 @@
 namespace smoe {
 namespace {
 
-constexpr int kLogitTokens = 8;   // tokens per logits block
-constexpr int kLogitWaves = 4;    // experts per logits block (one per wave)
+constexpr int kRouteThreads = 256;              // 4 waves: 4 experts per block
+constexpr int kTokensPerWave = 2;
+constexpr int kTailThreads = 1024;              // stand-alone top-k / union block
+constexpr int kMaxTicketBlocks = 64;            // larger grids hand the tail to its own kernel
 
 // Prepped activations of one (token, 64-input group): 8 chunks + group sums.
 __device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, float2* xs) {
@@ -35,163 +40,94 @@ __device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, fl
   xs[(int64_t)t * (d / 64) + g] = make_float2(X, 1024.0f * S);
 }
 
-template <bool kBf16>
-__global__ __launch_bounds__(256) void k_logits_prep(RouteArgs a, int do_logits) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (do_logits) {
-    const int e = blockIdx.x * kLogitWaves + wave;
-    const int t0 = blockIdx.y * kLogitTokens;
-    const int nt = min(kLogitTokens, a.B - t0);
-    if (e < a.E && nt > 0) {
-      float acc[kLogitTokens];
-#pragma unroll
-      for (int j = 0; j < kLogitTokens; ++j) acc[j] = 0.f;
-      for (int i = lane * 8; i < a.d; i += 512) {
-        float wv[8];
-        if (kBf16) {
-          const uint4 raw =
-              *reinterpret_cast<const uint4*>((const uint16_t*)a.router_w + (int64_t)e * a.d + i);
-          const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            wv[2 * q] = __uint_as_float(r4[q] << 16);
-            wv[2 * q + 1] = __uint_as_float(r4[q] & 0xFFFF0000u);
-          }
-        } else {
-          const float4* wp = reinterpret_cast<const float4*>((const float*)a.router_w +
-                                                             (int64_t)e * a.d + i);
-          const float4 lo = wp[0], hi = wp[1];
-          wv[0] = lo.x; wv[1] = lo.y; wv[2] = lo.z; wv[3] = lo.w;
-          wv[4] = hi.x; wv[5] = hi.y; wv[6] = hi.z; wv[7] = hi.w;
-        }
-#pragma unroll
-        for (int j = 0; j < kLogitTokens; ++j) {
-          if (j < nt) {
-            const float4* xp4 = reinterpret_cast<const float4*>(a.x + (int64_t)(t0 + j) * a.d + i);
-            const float4 lo = xp4[0], hi = xp4[1];
-            acc[j] += wv[0] * lo.x + wv[1] * lo.y + wv[2] * lo.z + wv[3] * lo.w + wv[4] * hi.x +
-                      wv[5] * hi.y + wv[6] * hi.z + wv[7] * hi.w;
-          }
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kLogitTokens; ++j) {
-        const float tot = wave_sum(acc[j]);
-        if (j < nt && lane == 0) a.logits[(int64_t)(t0 + j) * a.E + e] = tot;
-      }
-    }
-  }
-  if (a.xp != nullptr) {
-    const int G = a.d / 64;
-    const int units = a.B * G;
-    const int nthreads = gridDim.x * gridDim.y * blockDim.x;
-    const int gid = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-    for (int u = gid; u < units; u += nthreads) prep_group(a.x, a.d, u / G, u % G, a.xp, a.xs);
-  }
-}
-
-__global__ __launch_bounds__(256) void k_prep(const float* x, int B, int d, uint16_t* xp,
-                                              float2* xs) {
-  const int G = d / 64;
-  const int u = blockIdx.x * blockDim.x + threadIdx.x;
-  if (u < B * G) prep_group(x, d, u / G, u % G, xp, xs);
-}
-
 // (v, e) ranks above (bv, be): larger logit, or equal logit and lower index.
 __device__ __forceinline__ bool ranks_above(float v, int e, float bv, int be) {
   return v > bv || (v == bv && e < be);
 }
 
-constexpr int kTopkThreads = 512;
-
-__global__ __launch_bounds__(kTopkThreads) void k_topk_union(RouteArgs a, int do_topk,
-                                                             int do_union) {
-  __shared__ int32_t s_idx[kMaxPairs];
-  __shared__ int32_t s_hist[kMaxExperts];
-  __shared__ int32_t s_pos[kMaxExperts];
-  __shared__ uint32_t s_mask[kMaxExperts * (kMaxPairs / 32)];
-
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nwaves = kTopkThreads / 64;
-  const int E = a.E, K = a.K, B = a.B, P = B * K;
-
-  if (do_topk) {
-    for (int t = wave; t < B; t += nwaves) {
-      float v[4];
-      bool taken[4];
+// Top-k of one token's E <= 256 logits by one full wave; writes indices and
+// weights (rank order) to global memory and the indices to s_idx.
+__device__ void topk_token(const RouteArgs& a, int t, int32_t* s_idx) {
+  const int lane = __lane_id();
+  const int E = a.E, K = a.K;
+  float v[4];
+  bool live[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = lane + 64 * j;
-        v[j] = e < E ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
-        taken[j] = e >= E;
-      }
-      float my_v = 0.f;
-      int my_e = 0;
-      for (int k = 0; k < K; ++k) {
-        float bv = -INFINITY;
-        int be = INT_MAX;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = lane + 64 * j;
-          if (!taken[j] && ranks_above(v[j], e, bv, be)) { bv = v[j]; be = e; }
-        }
-        for (int off = 32; off > 0; off >>= 1) {
-          const float ov = __shfl_xor(bv, off, 64);
-          const int oe = __shfl_xor(be, off, 64);
-          if (ranks_above(ov, oe, bv, be)) { bv = ov; be = oe; }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (be == lane + 64 * j) taken[j] = true;
-        if (lane == k) { my_v = bv; my_e = be; }
-      }
-      // weights: p_k = exp(l_k - max); divide by the top-k sum (norm_topk_prob)
-      // or by the full softmax denominator.
-      const float m = __shfl(my_v, 0, 64);
-      const float p = lane < K ? expf(my_v - m) : 0.f;
-      float den;
-      if (a.norm) {
-        den = wave_sum(p);
-      } else {
-        float z = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (lane + 64 * j < E) z += expf(v[j] - m);
-        den = wave_sum(z);
-      }
-      if (lane < K) {
-        a.topk_idx[t * K + lane] = my_e;
-        a.topk_w[t * K + lane] = p / den;
-        s_idx[t * K + lane] = my_e;
-      }
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    live[j] = e < E;
+    v[j] = live[j] ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
   }
-  if (!do_union) return;
-  __syncthreads();
-  if (!do_topk)
-    for (int p = threadIdx.x; p < P; p += kTopkThreads) s_idx[p] = a.topk_idx[p];
+  float my_v = 0.f;
+  int my_e = 0;
+  for (int k = 0; k < K; ++k) {
+    // this lane's best live candidate (ascending j keeps the lower index on ties)
+    float bv = -INFINITY;
+    int be = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (live[j] && ranks_above(v[j], lane + 64 * j, bv, be)) { bv = v[j]; be = lane + 64 * j; }
+    const float m = wave_max(bv);
+    const int win = wave_min_i(bv == m ? be : INT_MAX);   // lowest index among the maxima
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (win == lane + 64 * j) live[j] = false;
+    if (lane == k) { my_v = m; my_e = win; }
+  }
+  const float top = readlane(my_v, 0);
+  const float p = lane < K ? expf(my_v - top) : 0.f;
+  float den;
+  if (a.norm) {
+    den = wave_sum(p);
+  } else {
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < E) z += expf(v[j] - top);
+    den = wave_sum(z);
+  }
+  if (lane < K) {
+    a.topk_idx[t * K + lane] = my_e;
+    a.topk_w[t * K + lane] = p / den;
+    s_idx[t * K + lane] = my_e;
+  }
+}
+
+struct UnionSmem {
+  int32_t idx[kMaxPairs];
+  int32_t hist[kMaxExperts];
+  int32_t pos[kMaxExperts];
+  uint32_t mask[kMaxExperts * (kMaxPairs / 32)];
+};
+
+// Union of the batch's experts and the per-expert pair lists, by one block
+// (any size that is a multiple of 64) from us->idx[0..P).
+__device__ void build_union(const RouteArgs& a, UnionSmem* us) {
+  const int nthr = blockDim.x, tid = threadIdx.x;
+  const int E = a.E, P = a.B * a.K;
   const int W = (P + 31) / 32;
-  for (int i = threadIdx.x; i < E; i += kTopkThreads) s_hist[i] = 0;
-  for (int i = threadIdx.x; i < E * W; i += kTopkThreads) s_mask[i] = 0u;
+  for (int i = tid; i < E; i += nthr) us->hist[i] = 0;
+  for (int i = tid; i < E * W; i += nthr) us->mask[i] = 0u;
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += kTopkThreads) {
-    const int e = s_idx[p];
+  for (int p = tid; p < P; p += nthr) {
+    const int e = us->idx[p];
     if (e >= 0 && e < E) {
-      atomicAdd(&s_hist[e], 1);
-      atomicOr(&s_mask[e * W + (p >> 5)], 1u << (p & 31));
+      atomicAdd(&us->hist[e], 1);
+      atomicOr(&us->mask[e * W + (p >> 5)], 1u << (p & 31));
     } else {
       atomicOr(a.status, (uint32_t)SMOE_STATUS_BAD_EXPERT);
       a.pair_pos[p] = -1;
     }
   }
   __syncthreads();
-  if (wave == 0) {
-    // exclusive scans of counts and of non-empty experts; lane l owns experts 4l..4l+3
+  if (tid < 64) {
+    // exclusive scans of pair counts and of non-empty experts; lane l owns experts 4l..4l+3
+    const int lane = tid;
     int c[4], cnt = 0, nz = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
-      c[j] = e < E ? s_hist[e] : 0;
+      c[j] = e < E ? us->hist[e] : 0;
       cnt += c[j];
       nz += c[j] > 0;
     }
@@ -204,7 +140,7 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_union(RouteArgs a, int do
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = 4 * lane + j;
-      if (e < E) s_pos[e] = pos;
+      if (e < E) us->pos[e] = pos;
       if (c[j] > 0) {
         a.union_experts[uid] = e;
         a.expert_offsets[uid] = pos;
@@ -218,16 +154,132 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_union(RouteArgs a, int do
     }
   }
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += kTopkThreads) {
-    const int e = s_idx[p];
+  for (int p = tid; p < P; p += nthr) {
+    const int e = us->idx[p];
     if (e < 0 || e >= E) continue;
-    const uint32_t* m = s_mask + e * W;
+    const uint32_t* m = us->mask + e * W;
     int rank = __popc(m[p >> 5] & ((1u << (p & 31)) - 1u));
     for (int i = 0; i < (p >> 5); ++i) rank += __popc(m[i]);
-    const int q = s_pos[e] + rank;
+    const int q = us->pos[e] + rank;
     a.pair_list[q] = p;
     a.pair_pos[p] = q;
   }
+}
+
+// Top-k of every token, then (optionally) the union, by the calling block.
+__device__ void route_tail(const RouteArgs& a, bool do_topk, bool do_union, UnionSmem* us) {
+  const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  if (do_topk)
+    for (int t = wave; t < a.B; t += nwaves) topk_token(a, t, us->idx);
+  if (!do_union) return;
+  __syncthreads();
+  if (!do_topk)
+    for (int p = threadIdx.x; p < a.B * a.K; p += blockDim.x) us->idx[p] = a.topk_idx[p];
+  build_union(a, us);
+}
+
+// Logits of expert e for tokens t0, t0+1 (one wave).  Lanes stride the input
+// 8 elements at a time; within each 4096-element chunk every gate and input
+// load is issued before the products.
+template <bool kBf16>
+__device__ void logits_wave(const RouteArgs& a, int e, int t0, int nt) {
+  const int lane = __lane_id();
+  const int d = a.d;
+  float acc[kTokensPerWave] = {};
+  for (int c0 = 0; c0 < d; c0 += 4096) {
+    float wv[8][8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int i = c0 + lane * 8 + 512 * m;
+      const bool ok = i < d;
+      const int64_t at = (int64_t)e * d + (ok ? i : 0);
+      if (kBf16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>((const uint16_t*)a.router_w + at);
+        const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+          wv[m][2 * z] = ok ? __uint_as_float(r4[z] << 16) : 0.f;
+          wv[m][2 * z + 1] = ok ? __uint_as_float(r4[z] & 0xFFFF0000u) : 0.f;
+        }
+      } else {
+        const float4* wp = reinterpret_cast<const float4*>((const float*)a.router_w + at);
+        const float4 lo = wp[0], hi = wp[1];
+        const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int z = 0; z < 8; ++z) wv[m][z] = ok ? v8[z] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kTokensPerWave; ++j) {
+      const int t = t0 + min(j, nt - 1);
+      float part = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int i = c0 + lane * 8 + 512 * m;
+        const float4* xp4 =
+            reinterpret_cast<const float4*>(a.x + (int64_t)t * d + (i < d ? i : 0));
+        const float4 lo = xp4[0], hi = xp4[1];
+        part += wv[m][0] * lo.x + wv[m][1] * lo.y + wv[m][2] * lo.z + wv[m][3] * lo.w +
+                wv[m][4] * hi.x + wv[m][5] * hi.y + wv[m][6] * hi.z + wv[m][7] * hi.w;
+      }
+      acc[j] += part;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kTokensPerWave; ++j) {
+    const float tot = wave_sum(acc[j]);
+    if (lane == 0 && j < nt) a.logits[(int64_t)(t0 + j) * a.E + e] = tot;
+  }
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tail,
+                                                         uint32_t* ticket) {
+  __shared__ UnionSmem us;
+  __shared__ int is_last;
+  {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int e = blockIdx.x * (kRouteThreads / 64) + wave;
+    const int t0 = blockIdx.y * kTokensPerWave;
+    if (e < a.E) logits_wave<kBf16>(a, e, t0, min(kTokensPerWave, a.B - t0));
+  }
+  if (a.xp != nullptr) {
+    const int G = a.d / 64;
+    const int units = a.B * G;
+    const int nthreads = gridDim.x * gridDim.y * blockDim.x;
+    const int gid = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int u = gid; u < units; u += nthreads) prep_group(a.x, a.d, u / G, u % G, a.xp, a.xs);
+  }
+  if (!do_tail) return;
+  // last block: every other block's logits are visible after its release and our acquire
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const uint32_t n = gridDim.x * gridDim.y;
+    const uint32_t t = atomicAdd(ticket, 1u);
+    is_last = (t == n - 1);
+    if (is_last) {
+      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __threadfence();
+    }
+  }
+  __syncthreads();
+  if (!is_last) return;
+  route_tail(a, true, a.n_union != nullptr, &us);
+}
+
+// Top-k only (logits given) and/or union only (indices given): one block.
+__global__ __launch_bounds__(kTailThreads) void k_topk_union(RouteArgs a, int do_topk,
+                                                             int do_union) {
+  __shared__ UnionSmem us;
+  route_tail(a, do_topk != 0, do_union != 0, &us);
+}
+
+__global__ __launch_bounds__(256) void k_prep(const float* x, int B, int d, uint16_t* xp,
+                                              float2* xs) {
+  const int G = d / 64;
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u < B * G) prep_group(x, d, u / G, u % G, xp, xs);
 }
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
@@ -239,19 +291,24 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
 
 hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
                          hipStream_t s) {
-  const bool do_logits = !logits_in;
-  if (do_logits || a.xp != nullptr) {
-    const dim3 grid((a.E + kLogitWaves - 1) / kLogitWaves,
-                    (a.B + kLogitTokens - 1) / kLogitTokens);
+  RouteArgs r = a;
+  if (!do_union) r.n_union = nullptr;
+  bool tail_done = false;
+  if (!logits_in) {
+    // logits (+ activation prep); small grids finish top-k/union in their last block
+    const dim3 grid((a.E + 3) / 4, (a.B + kTokensPerWave - 1) / kTokensPerWave);
+    const bool fused = (do_topk || do_union) && (int)(grid.x * grid.y) <= kMaxTicketBlocks;
+    uint32_t* ticket = a.status + 1;
     if (a.router_bf16)
-      hipLaunchKernelGGL(k_logits_prep<true>, grid, dim3(256), 0, s, a, (int)do_logits);
+      hipLaunchKernelGGL(k_route<true>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
     else
-      hipLaunchKernelGGL(k_logits_prep<false>, grid, dim3(256), 0, s, a, (int)do_logits);
+      hipLaunchKernelGGL(k_route<false>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    tail_done = fused;
   }
-  if (do_topk || do_union) {
-    hipLaunchKernelGGL(k_topk_union, dim3(1), dim3(kTopkThreads), 0, s, a, (int)do_topk,
+  if (!tail_done && (do_topk || do_union)) {
+    hipLaunchKernelGGL(k_topk_union, dim3(1), dim3(kTailThreads), 0, s, r, (int)do_topk,
                        (int)do_union);
     return hipGetLastError();
   }

@@ -28,15 +28,6 @@ constexpr int kMaxExperts = SMOE_MAX_EXPERTS;
 constexpr int kMaxTopK = SMOE_MAX_TOPK;
 constexpr int kMaxPairs = kMaxBatch * kMaxTopK;
 
-// An expert whose pair count is at most this takes the VALU dot-product path;
-// above it the dequantised tile feeds MFMA.
-constexpr int kValuMaxPairs = 2;
-
-// Expert-FFN blocks: 256 threads, four 16-row weight tiles.
-constexpr int kFfnThreads = 256;
-constexpr int kGateUpCols = 32;   // h columns per gate_up block (32 gate + 32 up rows)
-constexpr int kDownRows = 64;     // output rows per down block
-
 // ------------------------------------------------------------ workspace
 struct WsLayout {
   size_t status;   // uint32 status word (+ padding)
@@ -128,5 +119,10 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s);
+// small-batch (B <= 2) matrix-vector kernels
+bool gemv_path_ok(const FfnArgs& a);
+hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up);
+// prefill-chunk MFMA kernels
+hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up);
 
 }  // namespace smoe

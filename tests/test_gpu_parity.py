@@ -139,6 +139,9 @@ FWD_CASES = [
     (small_config("hot", 1024, 8, 4, 256, 64), 64, True),            # up to 4 token tiles
     (small_config("fused", 512, 32, 8, 128, 64, fused=True), 64, False),
     (small_config("wide", 2048, 16, 2, 128, 3, bf16=False), 3, True),
+    (small_config("gemv_b2", 1024, 32, 8, 1536, 2), 2, True),           # small-batch path, 3 groups/lane
+    (small_config("gemv_b1", 4096, 64, 8, 1536, 1), 1, False),
+    (small_config("gemv_k16", 2048, 64, 16, 512, 1), 1, True),
 ]
 
 
