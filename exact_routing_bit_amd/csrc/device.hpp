@@ -24,6 +24,41 @@ __device__ __forceinline__ uint2 ld_stream2(const uint32_t* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Direct global -> LDS copies (no VGPRs held while in flight).  Each active
+// lane copies n bytes from its own source address to lds_base + n * lane;
+// lds_base must be wave-uniform (it goes to M0).  The copies count in vmcnt
+// and are complete in LDS once the issuing wave's vmcnt has dropped past
+// them.  They are written as inline assembly so that the compiler neither
+// tracks them nor inserts its own (whole-queue) waits for them: callers wait
+// with wait_vmcnt<N>() themselves.  M0 is written here; the kernels that use
+// these copies make no other use of M0 (no dynamic register indexing).  The
+// s_nop is the one wait state required between an M0 write and an LDS copy.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void dma16_to_lds(const void* src, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src),
+               "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_to_lds(const void* src, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src),
+               "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wait until at most N vector-memory operations of this wave are in flight.
+// The memory clobber keeps the compiler from moving LDS reads above it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the implied wait for all outstanding memory
+// operations (the LDS copies of later stages stay in flight).
+__device__ __forceinline__ void barrier_no_wait() { asm volatile("s_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
@@ -40,13 +75,28 @@ __device__ __forceinline__ half_t bits_f16(uint16_t u) { return __builtin_bit_ca
 //   p0 = (1024+q0, 1024+q4)        p1 = (1024+16 q1, 1024+16 q5)
 //   p2 = (1024+q2, 1024+q6)        p3 = (1024+16 q3, 1024+16 q7)
 // Five integer ops per word.
+// The masks live in registers: gfx9 VOP3 instructions take no literal
+// operands, so with the masks as literals the compiler splits every
+// (w & mask) | magic into a v_and and a v_or.  Produced by (pure, hence
+// hoisted and shared) inline assembly, they stay opaque and each half pair is
+// one v_and_or_b32.
+struct NibbleMasks {
+  uint32_t lo, hi, magic;
+};
+__device__ __forceinline__ NibbleMasks nibble_masks() {
+  NibbleMasks m;
+  asm("v_mov_b32 %0, 0x000f000f" : "=v"(m.lo));
+  asm("v_mov_b32 %0, 0x00f000f0" : "=v"(m.hi));
+  asm("s_mov_b32 %0, 0x64006400" : "=s"(m.magic));
+  return m;
+}
 __device__ __forceinline__ void dequant_word(uint32_t w, uint32_t p[4]) {
-  constexpr uint32_t kMagic = 0x64006400u;
-  p[0] = (w & 0x000F000Fu) | kMagic;
-  p[1] = (w & 0x00F000F0u) | kMagic;
+  const NibbleMasks m = nibble_masks();
+  p[0] = (w & m.lo) | m.magic;
+  p[1] = (w & m.hi) | m.magic;
   const uint32_t w8 = w >> 8;
-  p[2] = (w8 & 0x000F000Fu) | kMagic;
-  p[3] = (w8 & 0x00F000F0u) | kMagic;
+  p[2] = (w8 & m.lo) | m.magic;
+  p[3] = (w8 & m.hi) | m.magic;
 }
 
 // acc + sum over the word's 8 inputs of (1024 + m*q) * stored, where the

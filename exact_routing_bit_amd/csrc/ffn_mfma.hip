@@ -2,31 +2,36 @@
 //
 // "Layer-Major Batched Prefill", step 6: every union expert is applied to all
 // of its routed pairs in one pass over its weights (gate_up, then down).
-// Each wave owns one unit = (union expert, 64 weight rows) and streams the
-// unit's rows over the whole input dimension, so the expert's bytes are read
-// once per layer for up to 16 pairs (an expert that serves more pairs is
-// streamed once per 16-pair tile, which keeps a single small register body).
+// A workgroup serves one union expert and one 16-pair token tile; each of its
+// four waves owns a unit of 64 weight rows and streams them over the whole
+// input dimension, so an expert's bytes are read once per layer for up to 16
+// pairs (an expert that serves more is streamed once per 16-pair tile).
 //
 //   gate_up unit: gate rows j0..j0+31 and up rows j0..j0+31 (four 16-row
 //     tiles) -> h[pair, j0..j0+31] = silu(g) * u (prepped fp16) and the
 //     half-group sums of h that the down pass needs;
 //   down unit: down rows r0..r0+63 -> y[pair, r0..r0+63] (fp32).
 //
-// Per 64-input group g, the dequantised words of each 16-row tile are the B
-// operand of two v_mfma_f32_16x16x32_f16 (one per 32-input half), the pairs'
-// prepped activations the A operand; the group's scale and bias are applied
-// in fp32 right after ("SSD Streaming Expert Layers", "Quantized Layout":
-// w = s*q + b):
+// Arithmetic.  Per 64-input group g and 16-row tile, the dequantised words
+// are the B operand of two v_mfma_f32_16x16x32_f16 (one per 32-input half),
+// the pairs' prepped activations the A operand, and the group's scale and
+// bias are applied in fp32 right after ("SSD Streaming Expert Layers",
+// "Quantized Layout": w = s*q + b):
 //     acc += s * (D - C) + b * X,   D = sum_k (1024 + m q_k) stored_k,
-// with the accumulator seeded by -C so D - C comes straight out of the MFMA.
-// Every union expert of a prefill chunk takes this tile: per weight word the
-// VALU work is the 5-op dequantisation plus ~4 ops of epilogue whether the
-// expert serves one pair or sixteen, so the kernel stays uniform.
+// with the MFMA accumulator seeded by -C so that D - C comes straight out.
 //
-// Memory: weights arrive with 8-byte loads per lane (16 rows x 32 contiguous
-// bytes per instruction and tile), software-pipelined two stages of
-// kGroupsPerStage groups deep, so compute of one stage overlaps the loads of
-// the next.  Activations come from L2, group sums from LDS.
+// Memory.  Everything a stage of two groups needs - the wave's 64 rows x 64
+// bytes of packed words, their scales and biases, the tile's activations and
+// group sums - is copied global -> LDS by the DMA path (global_load_lds, 16
+// bytes a lane for the words and activations), three stages deep.  The copies
+// hold no registers while in flight, so each wave keeps two stages (8 KB of
+// weights) in the air while it computes on the third, and the words arrive
+// as whole 64-byte row segments however the MFMA wants them laid out.  The
+// activations and sums of a stage are shared by the four waves (one copy
+// instruction each) behind one workgroup barrier per stage.  Scales and
+// biases come 16 bytes (8 groups) a row per copy, once every four stages,
+// when the group count and the strides allow it (kFastSB); otherwise one
+// aligned dword per row and group each stage.
 #include "device.hpp"
 #include "smoe_internal.hpp"
 
@@ -35,224 +40,345 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerUnit = 64;
-constexpr int kMaxExpertPairs = 64;                // pairs per expert (B <= 64)
+constexpr int kTiles = 4;                          // 16-row tiles per wave (64 rows)
+constexpr int kPairTile = 16;                      // pairs per token tile (MFMA M)
+constexpr int kGps = 2;                            // groups per pipeline stage
+constexpr int kRing = 3;                           // stages resident in LDS
+constexpr int kSuper = 4;                          // stages per scale/bias copy (kFastSB)
 
-template <int GPS>
-struct Stage {
-  uint2 w[GPS][4];                                 // 2 words per tile and group
-  uint32_t sb[GPS][4];                             // bf16 scale | bf16 bias << 16
-  uint4 a[GPS][2];                                 // A operand (this lane's pair)
+// One ring slot (one stage).  Layouts, 16-byte entries unless noted:
+//   W  [wave][tile][chunk 4][row 16]    chunk c = group c/2, words 4(c%2)..+3
+//   A  [word 16][pair 16]               prepped activations of one word
+//   XS [group 2][half 2][X|C][pair 16]               f32 (gate_up: half 0 only)
+//   SB [wave][s|b][group 2][col 16][tile 4]          u32, the aligned dword
+//                                        holding that row's bf16 s (or b)
+//                                        (only without kFastSB)
+// kFastSB keeps scales and biases outside the ring, double-buffered per four
+// stages: [buffer 2][wave][s|b][tile 4][col 16] x 16 bytes = groups 8j..8j+7.
+constexpr int kWBytes = kWaves * kTiles * 1024;
+constexpr int kABytes = 16 * kPairTile * 16;
+constexpr int kXSBytes = kGps * 2 * 2 * kPairTile * 4;
+constexpr int kSBSlotBytes = kWaves * 2 * kGps * 256;
+constexpr int kOffA = kWBytes;
+constexpr int kOffXS = kOffA + kABytes;
+constexpr int kOffSB = kOffXS + kXSBytes;
+constexpr int slot_bytes(bool fast_sb) { return kOffSB + (fast_sb ? 0 : kSBSlotBytes); }
+constexpr int kSBFastBytes = 2 * kWaves * 2 * kTiles * 16 * 16;
+// copy instructions per wave and stage: words (one per tile), activations,
+// sums, and the scale/bias copies (kFastSB: two on every fourth stage)
+constexpr int kCopiesBase = kTiles + 1 + 1;
+
+template <bool kFastSB>
+constexpr int copies_of_stage(bool superstage_start) {
+  return kCopiesBase + (kFastSB ? (superstage_start ? 2 : 0) : 2 * kGps);
+}
+
+// Per-lane copy sources that stay fixed over the K loop.
+struct Sources {
+  const uint32_t* w[kTiles];   // row (tile T, lane%16), chunk half (lane/16)%2
+  const uint16_t* s;           // scales of this lane's copy row (group 0)
+  const uint16_t* b;           // biases of the same row
+  const uint4* act;            // activation row of pair lane%16, word 4(wave%2) + lane/16
+  const float* sums;           // group sums of the same pair
 };
 
-struct UnitPtrs {
-  const uint32_t* w[4];
-  const uint16_t* s[4];
-  const uint16_t* b[4];
-};
-
-template <bool kNT>
-__device__ __forceinline__ uint2 ld_w2(const uint32_t* p) {
-  if (kNT) return ld_stream2(p);
-  return *reinterpret_cast<const uint2*>(p);
+__device__ __forceinline__ const void* align4(const uint16_t* p) {
+  return reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)3);
 }
 
-// Loads of groups g0 .. g0 + GPS - 1, clamped to the last group (the compute
-// step gives the copies zero weight).
-template <int GPS, bool kNT>
-__device__ __forceinline__ void load_stage(const UnitPtrs& P, const uint4* arow, bool avalid,
-                                           int g0, int G, int lg, Stage<GPS>& st) {
+// Copies of stage k (groups gA = 2k and gB = min(2k+1, G-1)) into `slot`.
+template <bool kGateUp, bool kFastSB>
+__device__ __forceinline__ void issue_stage(const Sources& S, char* slot, char* sbfast, int k, int G,
+                                            bool superstage_start, int wave, int lane) {
+  const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
+  // packed words: lanes 0-31 copy group gA, lanes 32-63 group gB
+  const int gw = (lane >> 5) ? gB : gA;
 #pragma unroll
-  for (int gg = 0; gg < GPS; ++gg) {
-    const int g = min(g0 + gg, G - 1);
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      st.w[gg][T] = ld_w2<kNT>(P.w[T] + 8 * g + 2 * lg);
-      st.sb[gg][T] = (uint32_t)P.s[T][g] | ((uint32_t)P.b[T][g] << 16);
-    }
-    const uint4 a0 = arow[8 * g + 2 * lg], a1 = arow[8 * g + 2 * lg + 1];
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    st.a[gg][0] = avalid ? a0 : z;
-    st.a[gg][1] = avalid ? a1 : z;
-  }
-}
-
-// acc += s (D - C) + b X for the groups of one stage; groups past the end
-// (clamped copies) get s = b = 0.
-template <int GPS>
-__device__ __forceinline__ void compute_stage(const Stage<GPS>& cur, int g0, int G, const float2* ls,
-                                              int ne, int m0, int lg, floatx4 (&acc)[4]) {
-#pragma unroll
-  for (int gg = 0; gg < GPS; ++gg) {
-    const int g = g0 + gg;
-    const bool live = g < G;
-    const int gc = min(g, G - 1);
-    const half8_t A0 = __builtin_bit_cast(half8_t, cur.a[gg][0]);
-    const half8_t A1 = __builtin_bit_cast(half8_t, cur.a[gg][1]);
-    float2 xsum[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 4 * lg + i;
-      const float2 v = ls[min(m, ne - 1) * G + gc];
-      xsum[i] = m < ne ? v : make_float2(0.f, 0.f);
-    }
-    const floatx4 seed = floatx4{-xsum[0].y, -xsum[1].y, -xsum[2].y, -xsum[3].y};
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const uint32_t sbv = live ? cur.sb[gg][T] : 0u;
-      const float sc = __uint_as_float(sbv << 16);
-      const float bi = __uint_as_float(sbv & 0xFFFF0000u);
-      floatx4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, word_operand(cur.w[gg][T].x), seed, 0,
-                                                         0, 0);
-      D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, word_operand(cur.w[gg][T].y), D, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[T][i] += sc * D[i] + bi * xsum[i].x;
-    }
-  }
-}
-
-// One 16-pair token tile (the expert's pairs m0 .. m0+15) of this wave's unit.
-template <bool kGateUp, int GPS, bool kNT>
-__device__ __forceinline__ void unit_tile(const FfnArgs& a, const UnitPtrs& P, const int (&rows0)[4],
-                                          const int* lpair, const float2* ls, int ne, int m0,
-                                          int unit, int G) {
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 15, lg = lane >> 4;
-  const int ma = m0 + col;                         // this lane's pair in the A operand
-  const bool avalid = ma < ne;
-  const int pa = lpair[avalid ? ma : m0];
-  const uint4* arow = kGateUp ? reinterpret_cast<const uint4*>(a.xp + (int64_t)(pa / a.K) * a.d)
-                              : reinterpret_cast<const uint4*>(a.hp + (int64_t)pa * a.f);
-
-  floatx4 acc[4];
-#pragma unroll
-  for (int T = 0; T < 4; ++T) acc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  Stage<GPS> st0, st1;
-  load_stage<GPS, kNT>(P, arow, avalid, 0, G, lg, st0);
-  load_stage<GPS, kNT>(P, arow, avalid, GPS, G, lg, st1);
-  for (int g0 = 0; g0 < G; g0 += 2 * GPS) {
-    compute_stage<GPS>(st0, g0, G, ls, ne, m0, lg, acc);
-    load_stage<GPS, kNT>(P, arow, avalid, g0 + 2 * GPS, G, lg, st0);
-    compute_stage<GPS>(st1, g0 + GPS, G, ls, ne, m0, lg, acc);
-    load_stage<GPS, kNT>(P, arow, avalid, g0 + 3 * GPS, G, lg, st1);
-  }
-
-  // epilogue: lane holds (pair slot m0 + 4 lg + i, row rows0[T] + col)
+  for (int T = 0; T < kTiles; ++T) dma16_to_lds(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
+  // activations: waves 0,1 copy the words of group gA, waves 2,3 those of gB
+  const int ga = wave < 2 ? gA : gB;
+  dma16_to_lds(S.act + ga * 8, slot + kOffA + wave * 1024);
+  // group sums: wave = 2 * group + (gate_up: X|C, down: half)
   if (kGateUp) {
-    // h for columns j = unit*32 + Th*16 + col, from gate tile Th and up tile Th+2
-    float X[4] = {0.f, 0.f, 0.f, 0.f}, S[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int Th = 0; Th < 2; ++Th) {
-      const int j = unit * 32 + Th * 16 + col;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 4 * lg + i;
-        const float h = silu_mul(acc[Th][i], acc[Th + 2][i]);
-        const half_t xi = (half_t)h;
-        const half_t stv = (j & 1) ? (half_t)((float)xi * 0.0625f) : xi;
-        const float stf = (float)stv;
-        S[i] += stf;
-        X[i] += (j & 1) ? stf * 16.0f : stf;
-        if (m < ne) {
-          const int n = j & 7;
-          a.hp[(int64_t)lpair[m] * a.f + (j & ~7) + 2 * (n & 3) + (n >> 2)] = f16_bits(stv);
-        }
-      }
-    }
-    // sums over the unit's 32 columns: the 16 lanes of a row segment
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float Xt = segment_sum16(X[i], 16), St = segment_sum16(S[i], 16);
-      const int m = m0 + 4 * lg + i;
-      if (col == 0 && m < ne) {
-        const int j0 = unit * 32;
-        a.hs[((int64_t)lpair[m] * (a.f / 64) + j0 / 64) * 2 + (j0 % 64) / 32] =
-            make_float2(Xt, 1024.0f * St);
-      }
+    if (lane < 16) dma4_to_lds(S.sums + ga * 2, slot + kOffXS + wave * 64);
+  } else {
+    if (lane < 32) dma4_to_lds(S.sums + ga * 4, slot + kOffXS + wave * 128);
+  }
+  if (kFastSB) {
+    if (superstage_start) {                        // groups 8j .. 8j+7, j = k / 4
+      const int j = k / kSuper;
+      char* dst = sbfast + ((j & 1) * kWaves + wave) * (2 * kTiles * 256);
+      dma16_to_lds(S.s + 8 * j, dst);
+      dma16_to_lds(S.b + 8 * j, dst + kTiles * 256);
     }
   } else {
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 4 * lg + i;
-        if (m < ne) a.y[(int64_t)lpair[m] * a.d + rows0[T] + col] = acc[T][i];
-      }
+    // one dword a lane, the aligned one that holds the value
+    char* sb = slot + kOffSB + wave * (2 * kGps * 256);
+    dma4_to_lds(align4(S.s + gA), sb);
+    dma4_to_lds(align4(S.s + gB), sb + 256);
+    dma4_to_lds(align4(S.b + gA), sb + 512);
+    dma4_to_lds(align4(S.b + gB), sb + 768);
   }
 }
 
-template <bool kGateUp, int GPS, bool kNT>
+// bf16 in the upper (hi) or lower half of a dword, as fp32
+__device__ __forceinline__ float bf16_half(uint32_t w, bool hi) {
+  return __uint_as_float(hi ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+// Scales and biases of this lane's rows, kFastSB: 8 groups of tile T in
+// sbw[T] (u16 pairs), biases in bbw[T].
+struct SBRegs {
+  uint4 s[kTiles], b[kTiles];
+};
+
+// acc[T] += s (D - C) + b X over the two groups of stage k.
+//   kFastSB: scales/biases from `regs` (groups 8j.. of the current four stages,
+//            kk = k % 4 static);
+//   else:    from the slot, with `parity` bit T (scales) and 4 + T (biases) =
+//            the u16 address parity of group 0 of this lane's row in tile T.
+template <bool kGateUp, bool kFastSB, int kk>
+__device__ __forceinline__ void compute_stage(const char* slot, int k, int G, int wave, int col,
+                                              int lg, const SBRegs& regs, uint32_t parity,
+                                              floatx4 (&acc)[kTiles]) {
+#pragma unroll
+  for (int gl = 0; gl < kGps; ++gl) {
+    const bool live = kFastSB || 2 * k + gl < G;   // uniform; a clamped copy otherwise
+    const half8_t A0 =
+        *reinterpret_cast<const half8_t*>(slot + kOffA + ((gl * 8 + 2 * lg) * 16 + col) * 16);
+    const half8_t A1 =
+        *reinterpret_cast<const half8_t*>(slot + kOffA + ((gl * 8 + 2 * lg + 1) * 16 + col) * 16);
+    floatx4 X, Cs;
+    if (kGateUp) {
+      X = *reinterpret_cast<const floatx4*>(slot + kOffXS + (gl * 2 + 0) * 64 + 16 * lg);
+      Cs = *reinterpret_cast<const floatx4*>(slot + kOffXS + (gl * 2 + 1) * 64 + 16 * lg);
+    } else {
+      const char* xs = slot + kOffXS + gl * 256 + 16 * lg;
+      X = *reinterpret_cast<const floatx4*>(xs) + *reinterpret_cast<const floatx4*>(xs + 128);
+      Cs = *reinterpret_cast<const floatx4*>(xs + 64) + *reinterpret_cast<const floatx4*>(xs + 192);
+    }
+    const floatx4 seed = -Cs;
+    uint32_t sw[kTiles], bw[kTiles];
+    if (kFastSB) {
+#pragma unroll
+      for (int T = 0; T < kTiles; ++T) {
+        const uint32_t sv[4] = {regs.s[T].x, regs.s[T].y, regs.s[T].z, regs.s[T].w};
+        const uint32_t bv[4] = {regs.b[T].x, regs.b[T].y, regs.b[T].z, regs.b[T].w};
+        sw[T] = sv[kk];                            // groups 2kk, 2kk+1 of the eight
+        bw[T] = bv[kk];
+      }
+    } else {
+      const char* sb = slot + kOffSB + wave * (2 * kGps * 256) + gl * 256 + col * 16;
+      const uint4 s4 = *reinterpret_cast<const uint4*>(sb);
+      const uint4 b4 = *reinterpret_cast<const uint4*>(sb + 512);
+      sw[0] = s4.x; sw[1] = s4.y; sw[2] = s4.z; sw[3] = s4.w;
+      bw[0] = b4.x; bw[1] = b4.y; bw[2] = b4.z; bw[3] = b4.w;
+    }
+    const char* wrow =
+        slot + (wave * kTiles) * 1024 + ((2 * gl + (lg >> 1)) * 16 + col) * 16 + (lg & 1) * 8;
+#pragma unroll
+    for (int T = 0; T < kTiles; ++T) {
+      const uint2 w2 = *reinterpret_cast<const uint2*>(wrow + T * 1024);
+      const bool shi = kFastSB ? gl == 1 : (((parity >> T) & 1) ^ gl) != 0;
+      const bool bhi = kFastSB ? gl == 1 : (((parity >> (4 + T)) & 1) ^ gl) != 0;
+      const float sc = live ? bf16_half(sw[T], shi) : 0.f;
+      const float bi = live ? bf16_half(bw[T], bhi) : 0.f;
+      floatx4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, word_operand(w2.x), seed, 0, 0, 0);
+      D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, word_operand(w2.y), D, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[T][i] = __builtin_fmaf(sc, D[i], acc[T][i]);
+        acc[T][i] = __builtin_fmaf(bi, X[i], acc[T][i]);
+      }
+    }
+  }
+}
+
+template <bool kGateUp, bool kFastSB>
 __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
-  extern __shared__ __align__(16) char smem[];
+  constexpr int kSlot = slot_bytes(kFastSB);
+  __shared__ __align__(16) char ring[kRing * kSlot];
+  __shared__ __align__(16) char sbfast[kFastSB ? kSBFastBytes : 16];
+  __shared__ int lpair[kPairTile];                 // pair ids of the current token tile
   const int u = blockIdx.y;
   const int nU = *a.n_union;
   if (u >= nU) return;
   const int e = a.union_experts[u];
   const int pb = a.expert_offsets[u];
-  const int ne = a.expert_offsets[u + 1] - pb;     // 1 .. kMaxExpertPairs
+  const int ne = a.expert_offsets[u + 1] - pb;     // >= 1
   const int K = kGateUp ? a.d : a.f;
   const int G = K / 64, C = K / 8;
-
-  // pairs of this expert and their group sums in LDS: ls[m][g] = (X, C)
-  int* lpair = reinterpret_cast<int*>(smem);                                  // [kMaxExpertPairs]
-  float2* ls = reinterpret_cast<float2*>(smem + 4 * kMaxExpertPairs);              // [ne][G]
-  for (int i = threadIdx.x; i < ne; i += kThreads) lpair[i] = a.pair_list[pb + i];
-  __syncthreads();
-  for (int i = threadIdx.x; i < ne * G; i += kThreads) {
-    const int m = i / G, g = i - m * G;
-    const int p = lpair[m];
-    float2 v;
-    if (kGateUp) {
-      v = a.xs[(int64_t)(p / a.K) * G + g];
-    } else {
-      const float2* hs = a.hs + ((int64_t)p * G + g) * 2;
-      const float2 lo = hs[0], hi = hs[1];
-      v = make_float2(lo.x + hi.x, lo.y + hi.y);
-    }
-    ls[i] = v;
-  }
-  __syncthreads();
-
-  // this wave's unit: four 16-row tiles (waves past the last unit stop here;
-  // no block barrier follows)
+  const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kWaves + wave;
-  const int units = kGateUp ? a.f / 32 : a.d / kRowsPerUnit;
-  if (unit >= units) return;
-  const int col = threadIdx.x & 15;
-  UnitPtrs P;
-  int rows0[4];
+  const int col = lane & 15, lg = lane >> 4;
+
+  // this wave's unit; waves past the last unit run along on a copy of the
+  // last one (they take part in the shared copies and barriers) and write nothing
+  const int units = kGateUp ? a.f / 32 : a.d / 64;
+  const bool has_unit = (int)blockIdx.x * kWaves + wave < units;
+  const int unit = min((int)blockIdx.x * kWaves + wave, units - 1);
+  int rows0[kTiles];
 #pragma unroll
-  for (int T = 0; T < 4; ++T) {
+  for (int T = 0; T < kTiles; ++T) rows0[T] = kGateUp ? unit * 32 + (T & 1) * 16 : unit * 64 + T * 16;
+
+  Sources S;
+#pragma unroll
+  for (int T = 0; T < kTiles; ++T) {
     const QMat& m = kGateUp ? (T < 2 ? a.gate : a.up) : a.down;   // T is a constant here
-    rows0[T] = kGateUp ? unit * 32 + (T & 1) * 16 : unit * kRowsPerUnit + T * 16;
-    const int64_t row = rows0[T] + col;
-    P.w[T] = m.w + e * m.stride_w + row * C;
-    P.s[T] = m.s + e * m.stride_sb + row * G;
-    P.b[T] = m.b + e * m.stride_sb + row * G;
+    S.w[T] = m.w + e * m.stride_w + (int64_t)(rows0[T] + (lane & 15)) * C + ((lane >> 4) & 1) * 4;
   }
-  for (int m0 = 0; m0 < ne; m0 += 16) unit_tile<kGateUp, GPS, kNT>(a, P, rows0, lpair, ls, ne, m0, unit, G);
+  {
+    // scale/bias copy row of this lane: kFastSB (tile lane/16, col lane%16),
+    // else (tile lane%4, col lane/4)
+    const int T = kFastSB ? lane >> 4 : lane & 3;
+    const int r = kFastSB ? lane & 15 : lane >> 2;
+    const bool up = kGateUp && T >= 2;
+    const uint16_t* s0 = kGateUp ? a.gate.s : a.down.s;
+    const uint16_t* b0 = kGateUp ? a.gate.b : a.down.b;
+    const int64_t st0 = kGateUp ? a.gate.stride_sb : a.down.stride_sb;
+    const uint16_t* sp = up ? a.up.s : s0;
+    const uint16_t* bp = up ? a.up.b : b0;
+    const int64_t stride = up ? a.up.stride_sb : st0;
+    const int row = (kGateUp ? unit * 32 + (T & 1) * 16 : unit * 64 + T * 16) + r;
+    S.s = sp + e * stride + (int64_t)row * G;
+    S.b = bp + e * stride + (int64_t)row * G;
+  }
+  uint32_t parity = 0;                             // see compute_stage
+  if (!kFastSB) {
+#pragma unroll
+    for (int T = 0; T < kTiles; ++T) {
+      const QMat& m = kGateUp ? (T < 2 ? a.gate : a.up) : a.down;
+      const int64_t first = e * m.stride_sb + (int64_t)(rows0[T] + col) * G;
+      parity |= (uint32_t)((reinterpret_cast<uintptr_t>(m.s + first) >> 1) & 1) << T;
+      parity |= (uint32_t)((reinterpret_cast<uintptr_t>(m.b + first) >> 1) & 1) << (4 + T);
+    }
+  }
+  const int nst = (G + kGps - 1) / kGps;
+
+  for (int m0 = 0; m0 < ne; m0 += kPairTile) {
+    __syncthreads();                               // the previous tile is done with lpair
+    if (threadIdx.x < kPairTile) lpair[threadIdx.x] = a.pair_list[pb + min(m0 + (int)threadIdx.x, ne - 1)];
+    __syncthreads();
+    {
+      const int q = lpair[lane & 15];
+      const int word = 4 * (wave & 1) + (lane >> 4);
+      if (kGateUp) {
+        const int t = q / a.K;
+        S.act = reinterpret_cast<const uint4*>(a.xp + (int64_t)t * a.d) + word;
+        S.sums = reinterpret_cast<const float*>(a.xs) + (int64_t)t * G * 2 + (wave & 1);
+      } else {
+        S.act = reinterpret_cast<const uint4*>(a.hp + (int64_t)q * a.f) + word;
+        S.sums = reinterpret_cast<const float*>(a.hs) + (int64_t)q * G * 4 + (wave & 1) * 2 +
+                 ((lane >> 4) & 1);
+      }
+    }
+    floatx4 acc[kTiles];
+#pragma unroll
+    for (int T = 0; T < kTiles; ++T) acc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
+    SBRegs regs;
+
+    issue_stage<kGateUp, kFastSB>(S, ring, sbfast, 0, G, true, wave, lane);
+    if (nst > 1) issue_stage<kGateUp, kFastSB>(S, ring + kSlot, sbfast, 1, G, false, wave, lane);
+    // stages in fours so that the stage's place in its four is a constant
+    for (int ks = 0; ks < nst; ks += kSuper) {
+#define SMOE_MFMA_STAGE(kk)                                                                       \
+      if (ks + kk < nst) {                                                                        \
+        const int k = ks + kk;                                                                    \
+        if (k + 1 < nst)             /* this wave's copies of stage k landed */                   \
+          wait_vmcnt<copies_of_stage<kFastSB>((kk + 1) % kSuper == 0)>();                         \
+        else                                                                                      \
+          wait_vmcnt<0>();                                                                        \
+        barrier_no_wait();           /* ... and every wave's; slot k-1 is free */                 \
+        if (k + 2 < nst)                                                                          \
+          issue_stage<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, sbfast, k + 2, G,    \
+                                        (kk + 2) % kSuper == 0, wave, lane);                      \
+        if (kFastSB && kk == 0) {                                                                 \
+          const char* sbr = sbfast + (((k / kSuper) & 1) * kWaves + wave) * (2 * kTiles * 256);   \
+          _Pragma("unroll") for (int T = 0; T < kTiles; ++T) {                                   \
+            regs.s[T] = *reinterpret_cast<const uint4*>(sbr + (T * 16 + col) * 16);               \
+            regs.b[T] = *reinterpret_cast<const uint4*>(sbr + kTiles * 256 + (T * 16 + col) * 16); \
+          }                                                                                       \
+        }                                                                                         \
+        compute_stage<kGateUp, kFastSB, kk>(ring + (k % kRing) * kSlot, k, G, wave, col, lg,      \
+                                            regs, parity, acc);                                   \
+      }
+      SMOE_MFMA_STAGE(0)
+      SMOE_MFMA_STAGE(1)
+      SMOE_MFMA_STAGE(2)
+      SMOE_MFMA_STAGE(3)
+#undef SMOE_MFMA_STAGE
+    }
+    if (!has_unit) continue;
+
+    // epilogue: lane holds (pair slot m0 + 4 lg + i, row rows0[T] + col)
+    if (kGateUp) {
+      // h for columns j = unit*32 + Th*16 + col, from gate tile Th and up tile Th+2
+      float X[4] = {0.f, 0.f, 0.f, 0.f}, Sm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int Th = 0; Th < 2; ++Th) {
+        const int j = unit * 32 + Th * 16 + col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 4 * lg + i;
+          const float h = silu_mul(acc[Th][i], acc[Th + 2][i]);
+          const half_t xi = (half_t)h;
+          const half_t stv = (j & 1) ? (half_t)((float)xi * 0.0625f) : xi;
+          const float stf = (float)stv;
+          Sm[i] += stf;
+          X[i] += (j & 1) ? stf * 16.0f : stf;
+          if (m < ne) {
+            const int n = j & 7;
+            a.hp[(int64_t)lpair[m - m0] * a.f + (j & ~7) + 2 * (n & 3) + (n >> 2)] = f16_bits(stv);
+          }
+        }
+      }
+      // sums over the unit's 32 columns: the 16 lanes of a row segment
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float Xt = segment_sum16(X[i], 16), St = segment_sum16(Sm[i], 16);
+        const int m = m0 + 4 * lg + i;
+        if (col == 0 && m < ne) {
+          const int j0 = unit * 32;
+          a.hs[((int64_t)lpair[m - m0] * (a.f / 64) + j0 / 64) * 2 + (j0 % 64) / 32] =
+              make_float2(Xt, 1024.0f * St);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int T = 0; T < kTiles; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 4 * lg + i;
+          if (m < ne) a.y[(int64_t)lpair[m - m0] * a.d + rows0[T] + col] = acc[T][i];
+        }
+    }
+  }
+}
+
+// 16-byte scale/bias copies need 8 | G, 8 | stride and 16-byte aligned bases
+bool fast_sb_ok(const QMat& m, int G) {
+  return G % 8 == 0 && m.stride_sb % 8 == 0 && (reinterpret_cast<uintptr_t>(m.s) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(m.b) & 15) == 0;
 }
 
 }  // namespace
 
-size_t mfma_smem_bytes(const FfnArgs& a, bool gate_up) {
-  const int G = (gate_up ? a.d : a.f) / 64;
-  // an expert serves at most one pair per token
-  return 4 * kMaxExpertPairs + (size_t)a.B * G * sizeof(float2);
-}
-
 hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up) {
-  if (a.B > kMaxExpertPairs) return hipErrorInvalidValue;
   const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
-  const int units = gate_up ? a.f / 32 : a.d / kRowsPerUnit;
+  const int units = gate_up ? a.f / 32 : a.d / 64;
   const dim3 grid((units + kWaves - 1) / kWaves, max_union);
-  if (gate_up)
-    hipLaunchKernelGGL((k_ffn_mfma<true, 1, false>), grid, dim3(kThreads), mfma_smem_bytes(a, true), s, a);
-  else
-    hipLaunchKernelGGL((k_ffn_mfma<false, 1, false>), grid, dim3(kThreads), mfma_smem_bytes(a, false), s,
-                       a);
+  if (gate_up) {
+    const bool fast = fast_sb_ok(a.gate, a.d / 64) && fast_sb_ok(a.up, a.d / 64);
+    if (fast)
+      hipLaunchKernelGGL((k_ffn_mfma<true, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_ffn_mfma<true, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (fast_sb_ok(a.down, a.f / 64))
+      hipLaunchKernelGGL((k_ffn_mfma<false, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_ffn_mfma<false, false>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
