@@ -41,6 +41,11 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a device-to-device copy of COPY_BYTES (for the counter scale)")
+    p.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                            "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                   help="write the traffic summary from rocprofv3 --pmc counter CSVs and exit")
     return p.parse_args()
 
 
@@ -75,11 +80,11 @@ class Stack:
         self.smoe.moe_layer(self.desc, W["router"], ex, x, self.out[:B], self.idx[:B],
                             self.w[:B], self.un, self.ws)
 
-    def stage(self, st, l, x):
+    def stage(self, st, l, x, events=None):
         W, ex = self.layers[l]
         B = x.shape[0]
         self.smoe.moe_layer_stage(st, self.desc, W["router"], ex, x, self.out[:B], self.idx[:B],
-                                  self.w[:B], self.un, self.ws)
+                                  self.w[:B], self.un, self.ws, events=events)
 
 
 def x_pool(cfg, B, n):
@@ -104,25 +109,28 @@ def time_layer(stack, xs, steps, warmup):
     return t0.elapsed_time(t1) / 1e3
 
 
-def time_gate_up(stack, xs, steps):
-    """Mean gate_up duration (s) measured with events on the launch stream,
-    with the whole layer still run stage by stage around it."""
+def time_gate_up(stack, xs, launches):
+    """Mean gate_up kernel duration (s): HIP events on the launch stream around
+    `launches` back-to-back gate_up launches over the rotating layers, all
+    with the routing (|U| = 8 experts at B = 1) of one routed token.  Events
+    around each single launch would add the runtime's marker overhead
+    (about 3 us) to every sample; back to back, only the dispatch gaps
+    between consecutive kernels remain."""
     import torch
     smoe = stack.smoe
     nl = len(stack.layers)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    stack.stage(smoe.SMOE_STAGE_ROUTE, 0, xs[0])
+    for i in range(20):
+        stack.stage(smoe.SMOE_STAGE_GATE_UP, i % nl, xs[0])
     torch.cuda.synchronize()
-    for s in range(steps):
-        l, x = s % nl, xs[s % len(xs)]
-        stack.stage(smoe.SMOE_STAGE_ROUTE, l, x)
-        evs[s][0].record()
-        stack.stage(smoe.SMOE_STAGE_GATE_UP, l, x)
-        evs[s][1].record()
-        stack.stage(smoe.SMOE_STAGE_DOWN, l, x)
-        stack.stage(smoe.SMOE_STAGE_COMBINE, l, x)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(launches):
+        stack.stage(smoe.SMOE_STAGE_GATE_UP, i % nl, xs[0])
+    e1.record()
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / steps / 1e3
+    return e0.elapsed_time(e1) / launches / 1e3
 
 
 def union_sizes(stack, xs, steps):
@@ -168,13 +176,112 @@ def cpu_baseline(cfg, seconds):
                       f"{len(routed)} experts generated beforehand), {el:.1f} s"}
 
 
+# ------------------------------------------------------------------ traffic
+# HBM traffic of the roofline kernel comes from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) over a short run of this script,
+# each scaled by what the same counter reads for a plain device-to-device
+# copy of COPY_BYTES.  The summary records a hash of the kernel's sources;
+# once they change, the figure is stale and `traffic` is reported as null.
+COPY_BYTES = 1 << 30
+ROOFLINE_KERNEL = "k_gate_up_gemv<1>"
+ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/device.hpp",
+                    "exact_routing_bit_amd/csrc/smoe_internal.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_up_gemv_decode_b1_traffic.txt")
+
+
+def sources_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ROOFLINE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def copy_calibration():
+    import torch
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "repeats": 3}), flush=True)
+
+
+def _counter_rows(path, counter):
+    import csv
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r.get("Counter_Name") == counter:
+                yield r["Kernel_Name"], float(r["Counter_Value"])
+
+
+def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    def per_dispatch(path, counter, match):
+        vals = [v for k, v in _counter_rows(path, counter) if match(k)]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for the kernel in {path}")
+        return sum(vals) / len(vals), len(vals)
+
+    is_gu = lambda k: "k_gate_up_gemv<1>" in k
+    is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
+    f_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE", is_gu)
+    w_kib, nw = per_dispatch(write_csv, "WRITE_SIZE", is_gu)
+    cf = [v for k, v in _counter_rows(copy_fetch_csv, "FETCH_SIZE") if is_copy(k)]
+    cw = [v for k, v in _counter_rows(copy_write_csv, "WRITE_SIZE") if is_copy(k)]
+    if not cf or not cw:
+        raise SystemExit("no copy-kernel rows in the calibration CSVs")
+    # the copy's largest dispatch is the 1 GiB copy itself
+    cf_kib, cw_kib = max(cf), max(cw)
+    f_scale = COPY_BYTES / (cf_kib * 1024.0)
+    w_scale = COPY_BYTES / (cw_kib * 1024.0)
+    traffic = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
+    lines = [
+        f"# HBM traffic per launch of {ROOFLINE_KERNEL} on the decode layer (B=1)",
+        "# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (two passes) over",
+        "#   python3 bench.py --no-cpu --no-prefill --steps 200 --warmup 10",
+        "# scaled by the same counters for a 1 GiB device copy:",
+        "#   python3 bench.py --copy-calibration",
+        f"kernel: {ROOFLINE_KERNEL}",
+        f"kernel_sources_sha256: {sources_sha()}",
+        f"fetch_kib_per_dispatch: {f_kib:.1f}  (mean of {nf} dispatches)",
+        f"write_kib_per_dispatch: {w_kib:.1f}  (mean of {nw} dispatches)",
+        f"copy_fetch_kib: {cf_kib:.1f}  (copy of {COPY_BYTES} bytes; scale {f_scale:.4f})",
+        f"copy_write_kib: {cw_kib:.1f}  (scale {w_scale:.4f})",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+    ]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_per_launch():
+    """Bytes per launch from the committed counter summary, or None when it is
+    missing or was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(l.split(":", 1) for l in fh if ":" in l and not l.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("kernel_sources_sha256", "").strip() != sources_sha():
+        return None
+    return float(kv["traffic_bytes_per_launch"].split()[0])
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(this build runs the layer on a single MI355X).", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import exact_routing_bit_amd as smoe
     from synth import configs
@@ -190,7 +297,7 @@ def main():
     step_s = t / args.steps
     gbps = u1 * eb / step_s / 1e9
     # roofline: gate_up (two thirds of the expert bytes) timed on its own
-    gu_s = time_gate_up(stack, xs1, min(args.steps, 1000))
+    gu_s = time_gate_up(stack, xs1, min(args.steps, 2000))
     gu_bytes = u1 * (2 * dec.ffn_dim * dec.d_model // 2 + 2 * 2 * 2 * dec.ffn_dim * dec.d_model // 64)
     gu_gbps = gu_bytes / gu_s / 1e9
 
@@ -204,9 +311,9 @@ def main():
                    "layers_rotated": args.layers, "mean_union": u1,
                    "effective_bytes_per_step": int(u1 * eb)},
         "effective_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "k_gate_up_gemv<1>",
+        "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL,
                      "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_per_launch(),
                      "bytes_per_launch": int(gu_bytes), "mean_launch_us": round(gu_s * 1e6, 3)},
     }
     if not args.no_prefill:

@@ -78,7 +78,7 @@ def _load():
     L.smoe_moe_layer.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp, vp,
                                  ctypes.POINTER(Union), vp, sz, vp]
     L.smoe_moe_layer_stage.argtypes = [ctypes.c_int, dp, vp, ctypes.POINTER(Experts), vp, i32, vp,
-                                       vp, vp, vp, vp, ctypes.POINTER(Union), vp, sz, vp]
+                                       vp, vp, vp, vp, ctypes.POINTER(Union), vp, sz, vp, vp, vp]
     L.smoe_read_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.smoe_strerror.argtypes = [ctypes.c_int]
     L.smoe_strerror.restype = ctypes.c_char_p
@@ -214,8 +214,16 @@ def moe_layer(desc, router_w, experts: Experts, x, out, topk_idx, topk_w, un: Un
 
 
 def moe_layer_stage(stage, desc, router_w, experts: Experts, x, out, topk_idx, topk_w,
-                    un: UnionBuffers, ws, residual=None, logits=None, stream=None):
+                    un: UnionBuffers, ws, residual=None, logits=None, stream=None, events=None):
+    """One stage of moe_layer.  `events` = (start, stop) torch.cuda.Events
+    (timing enabled, already recorded once so that they exist): they are
+    submitted together with the stage's main kernel and bracket it."""
     cu = un.c()
+    ev0 = ev1 = None
+    if events is not None:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in events)
+        if not ev0.value or not ev1.value:
+            raise ValueError("moe_layer_stage: record the events once before passing them")
     _check(lib.smoe_moe_layer_stage(stage, ctypes.byref(desc), _ptr(router_w, None, "router_w"),
                                     ctypes.byref(experts), _ptr(x, torch.float32, "x"), x.shape[0],
                                     _ptr(residual, torch.float32, "residual"),
@@ -223,7 +231,8 @@ def moe_layer_stage(stage, desc, router_w, experts: Experts, x, out, topk_idx, t
                                     _ptr(logits, torch.float32, "logits"),
                                     _ptr(topk_idx, torch.int32, "topk_idx"),
                                     _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu),
-                                    _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+                                    _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream),
+                                    ev0, ev1),
            "smoe_moe_layer_stage")
 
 

@@ -272,19 +272,25 @@ SMOE_API int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const 
                                   const smoe_experts* experts, const float* x, int32_t B,
                                   const float* residual, float* out, float* logits,
                                   int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws,
-                                  size_t ws_bytes, void* stream) {
+                                  size_t ws_bytes, void* stream, void* start_event,
+                                  void* stop_event) {
   if (stage < SMOE_STAGE_ROUTE || stage > SMOE_STAGE_COMBINE) return SMOE_EINVAL;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return SMOE_EINVAL;
   smoe::RouteArgs r;
   smoe::FfnArgs a;
   const int rc = layer_setup(desc, router_w, experts, x, B, residual, out, logits, topk_idx,
                              topk_w, un, ws, ws_bytes, &r, &a);
   if (rc != SMOE_OK || B == 0) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  smoe::LaunchTiming timing;
+  timing.start = static_cast<hipEvent_t>(start_event);
+  timing.stop = static_cast<hipEvent_t>(stop_event);
+  const smoe::LaunchTiming* t = start_event != nullptr ? &timing : nullptr;
   switch (stage) {
-    case SMOE_STAGE_ROUTE: return hip_rc(smoe::launch_router(r, false, true, true, s));
-    case SMOE_STAGE_GATE_UP: return hip_rc(smoe::launch_gate_up(a, s));
-    case SMOE_STAGE_DOWN: return hip_rc(smoe::launch_down(a, s));
-    default: return hip_rc(smoe::launch_combine(a, s));
+    case SMOE_STAGE_ROUTE: return hip_rc(smoe::launch_router(r, false, true, true, s, t));
+    case SMOE_STAGE_GATE_UP: return hip_rc(smoe::launch_gate_up(a, s, t));
+    case SMOE_STAGE_DOWN: return hip_rc(smoe::launch_down(a, s, t));
+    default: return hip_rc(smoe::launch_combine(a, s, t));
   }
 }
 

@@ -41,21 +41,21 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
 
 }  // namespace
 
-hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s) {
-  if (gemv_path_ok(a)) return launch_gemv(a, s, true);
-  return launch_ffn_mfma(a, s, true);
+hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+  if (gemv_path_ok(a)) return launch_gemv(a, s, true, t);
+  return launch_ffn_mfma(a, s, true, t);
 }
 
 // For small batches the down kernel also does the combine.
-hipError_t launch_down(const FfnArgs& a, hipStream_t s) {
-  if (gemv_path_ok(a)) return launch_gemv(a, s, false);
-  return launch_ffn_mfma(a, s, false);
+hipError_t launch_down(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+  if (gemv_path_ok(a)) return launch_gemv(a, s, false, t);
+  return launch_ffn_mfma(a, s, false, t);
 }
 
-hipError_t launch_combine(const FfnArgs& a, hipStream_t s) {
+hipError_t launch_combine(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
   if (gemv_path_ok(a)) return hipSuccess;
   const int n4 = a.B * a.d / 4;
-  hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a);
+  SMOE_LAUNCH(t, k_combine, dim3((n4 + 255) / 256), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

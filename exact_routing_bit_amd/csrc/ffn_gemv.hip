@@ -286,8 +286,8 @@ size_t down_gemv_smem(const FfnArgs& a) {
 }
 
 template <int GPL>
-hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_down_combine_gemv<GPL>, dim3(a.d / kDownRowsGemv), dim3(kGemvThreads),
+hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+  SMOE_LAUNCH(t, k_down_combine_gemv<GPL>, dim3(a.d / kDownRowsGemv), dim3(kGemvThreads),
                      down_gemv_smem(a), s,
                      a);
   return hipGetLastError();
@@ -311,20 +311,20 @@ bool gemv_path_ok(const FfnArgs& a) {
   return down_gemv_smem(a) <= 64 * 1024;
 }
 
-hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up) {
+hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {
   if (gate_up) {
     const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
     const dim3 grid(a.f / (kJPerWave * (kGemvThreads / 64)), max_union);
     if (a.B == 1)
-      hipLaunchKernelGGL(k_gate_up_gemv<1>, grid, dim3(kGemvThreads), 0, s, a);
+      SMOE_LAUNCH(t, k_gate_up_gemv<1>, grid, dim3(kGemvThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(k_gate_up_gemv<2>, grid, dim3(kGemvThreads), 0, s, a);
+      SMOE_LAUNCH(t, k_gate_up_gemv<2>, grid, dim3(kGemvThreads), 0, s, a);
     return hipGetLastError();
   }
   switch (gpl_of(a.f / 64)) {
-    case 1: return launch_down_gemv<1>(a, s);
-    case 2: return launch_down_gemv<2>(a, s);
-    default: return launch_down_gemv<3>(a, s);
+    case 1: return launch_down_gemv<1>(a, s, t);
+    case 2: return launch_down_gemv<2>(a, s, t);
+    default: return launch_down_gemv<3>(a, s, t);
   }
 }
 

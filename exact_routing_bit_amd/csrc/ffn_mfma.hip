@@ -363,21 +363,21 @@ bool fast_sb_ok(const QMat& m, int G) {
 
 }  // namespace
 
-hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up) {
+hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {
   const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
   const int units = gate_up ? a.f / 32 : a.d / 64;
   const dim3 grid((units + kWaves - 1) / kWaves, max_union);
   if (gate_up) {
     const bool fast = fast_sb_ok(a.gate, a.d / 64) && fast_sb_ok(a.up, a.d / 64);
     if (fast)
-      hipLaunchKernelGGL((k_ffn_mfma<true, true>), grid, dim3(kThreads), 0, s, a);
+      SMOE_LAUNCH(t, (k_ffn_mfma<true, true>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((k_ffn_mfma<true, false>), grid, dim3(kThreads), 0, s, a);
+      SMOE_LAUNCH(t, (k_ffn_mfma<true, false>), grid, dim3(kThreads), 0, s, a);
   } else {
     if (fast_sb_ok(a.down, a.f / 64))
-      hipLaunchKernelGGL((k_ffn_mfma<false, true>), grid, dim3(kThreads), 0, s, a);
+      SMOE_LAUNCH(t, (k_ffn_mfma<false, true>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((k_ffn_mfma<false, false>), grid, dim3(kThreads), 0, s, a);
+      SMOE_LAUNCH(t, (k_ffn_mfma<false, false>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

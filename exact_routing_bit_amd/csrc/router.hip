@@ -290,7 +290,7 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
 }  // namespace
 
 hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
-                         hipStream_t s) {
+                         hipStream_t s, const LaunchTiming* t) {
   RouteArgs r = a;
   if (!do_union) r.n_union = nullptr;
   bool tail_done = false;
@@ -300,9 +300,9 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
     const bool fused = (do_topk || do_union) && (int)(grid.x * grid.y) <= kMaxTicketBlocks;
     uint32_t* ticket = a.status + 1;
     if (a.router_bf16)
-      hipLaunchKernelGGL(k_route<true>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
+      SMOE_LAUNCH(t, k_route<true>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
     else
-      hipLaunchKernelGGL(k_route<false>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
+      SMOE_LAUNCH(t, k_route<false>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tail_done = fused;

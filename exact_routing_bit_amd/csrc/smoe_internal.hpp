@@ -15,6 +15,7 @@
 //                      sums as two 32-column partials per group.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -110,19 +111,37 @@ struct FfnArgs {
 };
 
 // ------------------------------------------------------------- launchers
+// Optional timing events for a stage's main kernel: when `start` is set the
+// kernel is launched with hipExtLaunchKernelGGL, which submits the events
+// together with the dispatch (no host-side gap between them).
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+#define SMOE_LAUNCH(timing, kernel, grid, block, shmem, stream, ...)                              \
+  do {                                                                                           \
+    if ((timing) != nullptr && (timing)->start != nullptr)                                       \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, (timing)->start, (timing)->stop, \
+                            0, __VA_ARGS__);                                                     \
+    else                                                                                         \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                       \
+  } while (0)
+
 // All return hipSuccess or the launch error.
 hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
-                         hipStream_t s);
+                         hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
-hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s);
-hipError_t launch_down(const FfnArgs& a, hipStream_t s);
-hipError_t launch_combine(const FfnArgs& a, hipStream_t s);
+hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+hipError_t launch_down(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
+hipError_t launch_combine(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s);
 // small-batch (B <= 2) matrix-vector kernels
 bool gemv_path_ok(const FfnArgs& a);
-hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up);
+hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up,
+                       const LaunchTiming* t = nullptr);
 // prefill-chunk MFMA kernels
-hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up);
+hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up,
+                           const LaunchTiming* t = nullptr);
 
 }  // namespace smoe

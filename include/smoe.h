@@ -177,11 +177,17 @@ int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w, const smoe
                    int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws,
                    size_t ws_bytes, void* stream);
 
-/* Diagnostic: enqueue one stage of smoe_moe_layer, so that a caller can put
- * events between stages and time each one.  Same arguments as
- * smoe_moe_layer.  Enqueuing SMOE_STAGE_ROUTE, _GATE_UP, _DOWN and _COMBINE
- * in this order on one stream launches exactly the kernels of one
- * smoe_moe_layer call, in the same order. */
+/* Diagnostic: enqueue one stage of smoe_moe_layer, so that a caller can time
+ * each one.  Same arguments as smoe_moe_layer, plus two optional hipEvent_t
+ * handles (both NULL, or both created with timing enabled): when given, the
+ * stage's main kernel (k_route, the gate_up kernel, the down kernel or
+ * k_combine) is launched together with start_event and stop_event in one
+ * submission (hipExtLaunchKernelGGL), so no host-side gap falls between
+ * them; the pair still includes the runtime's own marker overhead of a few
+ * microseconds.  Enqueuing
+ * SMOE_STAGE_ROUTE, _GATE_UP, _DOWN and _COMBINE in this order on one stream
+ * launches exactly the kernels of one smoe_moe_layer call, in the same order.
+ * SMOE_EINVAL when only one event is given. */
 #define SMOE_STAGE_ROUTE 0    /* logits + activation prep, top-k + union */
 #define SMOE_STAGE_GATE_UP 1  /* gate/up projections and SwiGLU for every union expert */
 #define SMOE_STAGE_DOWN 2     /* down projection for every union expert */
@@ -190,7 +196,7 @@ int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* rou
                          const smoe_experts* experts, const float* x, int32_t B,
                          const float* residual, float* out, float* logits, int32_t* topk_idx,
                          float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
-                         void* stream);
+                         void* stream, void* start_event, void* stop_event);
 
 /* ------------------------------------------------------------ utilities */
 /* Synchronises `stream`, then copies the workspace status bits into

@@ -46,19 +46,27 @@ __global__ void k_normals(uint64_t seed, uint32_t layer, uint32_t tensor, uint32
 }
 
 // One thread per row: the row's sum of squares is a sequential fp64 sum, as on the CPU.
-__global__ void k_hidden(uint64_t seed, uint32_t layer, uint32_t tensor, uint32_t stream_id, int B,
-                         int d, double eps, float* out) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+// One block per token: the normals in parallel, then the sum of squares in
+// index order by one thread (fp64, the same order as the CPU generator, so
+// the rows are bit-identical), then the scaling in parallel.
+__global__ __launch_bounds__(256) void k_hidden(uint64_t seed, uint32_t layer, uint32_t tensor,
+                                                 uint32_t stream_id, int B, int d, double eps,
+                                                 float* out) {
+  __shared__ double inv_s;
+  const int t = blockIdx.x;
   if (t >= B) return;
   float* row = out + (int64_t)t * d;
-  double ss = 0.0;
-  for (int i = 0; i < d; ++i) {
-    const float z = (float)syn_normal(seed, layer, tensor, stream_id, (uint64_t)t * d + i);
-    row[i] = z;
-    ss = ss + (double)z * (double)z;
+  for (int i = threadIdx.x; i < d; i += blockDim.x)
+    row[i] = (float)syn_normal(seed, layer, tensor, stream_id, (uint64_t)t * d + i);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double ss = 0.0;
+    for (int i = 0; i < d; ++i) ss = ss + (double)row[i] * (double)row[i];
+    inv_s = 1.0 / sqrt(ss / (double)d + eps);
   }
-  const double inv = 1.0 / sqrt(ss / (double)d + eps);
-  for (int i = 0; i < d; ++i) row[i] = (float)((double)row[i] * inv);
+  __syncthreads();
+  const double inv = inv_s;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) row[i] = (float)((double)row[i] * inv);
 }
 
 __global__ void k_router(uint64_t seed, uint32_t layer, uint32_t tensor, int64_t n, double sigma,
@@ -105,7 +113,7 @@ SYN_API int synth_gpu_normals(uint64_t seed, uint32_t layer, uint32_t tensor, ui
 SYN_API int synth_gpu_hidden(uint64_t seed, uint32_t layer, uint32_t tensor, uint32_t stream_id,
                              int B, int d, double eps, float* out, void* stream) {
   if (B <= 0) return 0;
-  hipLaunchKernelGGL(k_hidden, dim3((B + 63) / 64), dim3(64), 0, (hipStream_t)stream, seed, layer,
+  hipLaunchKernelGGL(k_hidden, dim3(B), dim3(256), 0, (hipStream_t)stream, seed, layer,
                      tensor, stream_id, B, d, eps, out);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

@@ -132,6 +132,26 @@ def test_forward_argument_errors(smoe):
     assert call(B=-3) == smoe.SMOE_EINVAL
 
 
+def test_stage_argument_errors(smoe):
+    d = desc_of(smoe)
+    f = 4096
+    q = smoe.QMat(f, f, f, 1536 * 512, 1536 * 64)
+    qd = smoe.QMat(f, f, f, 4096 * 192, 4096 * 24)
+    ex = smoe.Experts(q, q, qd)
+    un = smoe.Union(f, f, f, f, f)
+    st = smoe.lib.smoe_moe_layer_stage
+
+    def call(stage=smoe.SMOE_STAGE_GATE_UP, n=1 << 30, ev=(None, None)):
+        return st(stage, ctypes.byref(d), f, ctypes.byref(ex), f, 8, None, f, None, f, f,
+                  ctypes.byref(un), f, n, None, ev[0], ev[1])
+
+    assert call(stage=-1) == smoe.SMOE_EINVAL
+    assert call(stage=4) == smoe.SMOE_EINVAL
+    assert call(ev=(f, None)) == smoe.SMOE_EINVAL       # events come in pairs
+    assert call(ev=(None, f)) == smoe.SMOE_EINVAL
+    assert call(n=4096) == smoe.SMOE_EWORKSPACE
+
+
 def test_strerror(smoe):
     for c in (0, -1, -2, -3, -4):
         assert smoe.strerror(c)

@@ -197,6 +197,32 @@ def test_deterministic_bitwise(smoe):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("B", [1, 2, 64])
+def test_stages_equal_layer_and_stamp_events(smoe, B):
+    """The four diagnostic stages in order launch exactly one layer call's
+    kernels (bitwise the same output), and the timing events given to a
+    stage are stamped with its kernel's own duration."""
+    import torch
+    cfg = small_config("stages", 1024, 32, 8, 256, B)
+    L = synth.make_layer(cfg)
+    x = up(synth.hidden(0, 0, 5, B, 1024))
+    layer = smoe.Layer(desc_for(smoe, cfg), device_weights(L), max_batch=B, device=dev())
+    ref = down(layer.forward(x))
+    out = torch.zeros(B, 1024, dtype=torch.float32, device=dev())
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev[0].record()
+    ev[1].record()
+    for st in (smoe.SMOE_STAGE_ROUTE, smoe.SMOE_STAGE_GATE_UP, smoe.SMOE_STAGE_DOWN,
+               smoe.SMOE_STAGE_COMBINE):
+        smoe.moe_layer_stage(st, layer.desc, layer.router_w, layer.experts, x, out,
+                             layer.topk_idx[:B], layer.topk_w[:B], layer.union, layer.ws,
+                             events=ev if st == smoe.SMOE_STAGE_GATE_UP else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(out).view(np.uint32), ref.view(np.uint32))
+    ms = ev[0].elapsed_time(ev[1])
+    assert 0.0 < ms < 50.0
+
+
 def test_integer_case_bit_exact(smoe):
     """s=1 and small integer biases, one-hot inputs, unit routing weights: every
     value on both paths is an exact integer, so GPU and oracle agree bit for
