@@ -183,7 +183,7 @@ def cpu_baseline(cfg, seconds):
 # copy of COPY_BYTES.  The summary records a hash of the kernel's sources;
 # once they change, the figure is stale and `traffic` is reported as null.
 COPY_BYTES = 1 << 30
-ROOFLINE_KERNEL = "k_gate_up_gemv<1>"
+ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64>"
 ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/device.hpp",
                     "exact_routing_bit_amd/csrc/smoe_internal.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_up_gemv_decode_b1_traffic.txt")
@@ -224,7 +224,7 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
             raise SystemExit(f"no {counter} rows for the kernel in {path}")
         return sum(vals) / len(vals), len(vals)
 
-    is_gu = lambda k: "k_gate_up_gemv<1>" in k
+    is_gu = lambda k: ROOFLINE_KERNEL in k
     is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
     f_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE", is_gu)
     w_kib, nw = per_dispatch(write_csv, "WRITE_SIZE", is_gu)

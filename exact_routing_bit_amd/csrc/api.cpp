@@ -104,6 +104,7 @@ smoe::FfnArgs ffn_args(const smoe_layer_desc* L, const smoe_experts* ex, const s
   a.hp = ws_at<uint16_t>(ws, lay.hp);
   a.hs = ws_at<float2>(ws, lay.hs);
   a.y = ws_at<float>(ws, lay.y);
+  a.status = ws_at<uint32_t>(ws, lay.status);
   return a;
 }
 

@@ -1,34 +1,50 @@
 // ffn_gemv.hip - the expert FFN when every union expert serves one or two
 // pairs (B <= 2 tokens, the decode regime of "Data Flow", Regime 2).
 //
-// Each union expert is a matrix-vector product ("Layer-Major Batched
+// Each union expert is then a matrix-vector product ("Layer-Major Batched
 // Prefill", step 6, with B = 1): the work is a pure stream of the expert
-// bytes, so both kernels are built to keep many 16-byte loads in flight:
+// bytes, done by two kernels so that the kernel boundary (one cache
+// writeback for the whole device) publishes h, instead of in-kernel
+// device-scope fences, which on a multi-XCD part write back an XCD's whole L2
+// each time:
 //
-//  k_gate_up_gemv: wave = (union expert, 4 consecutive j); it loads the 4 gate
-//    rows and 4 up rows before any arithmetic, holds the pairs' activations
-//    for its fixed groups in registers, reduces rows with DPP, and writes
-//    h_j = silu(g_j) * u_j ("SSD Streaming Expert Layers", "Math Contract")
-//    as prepped fp16.
-//  k_down_combine_gemv: block = 8 output rows for ALL union experts; its
-//    weight loads are issued first, h and its group sums are staged in LDS
-//    meanwhile, and the block finishes with the weighted combine of its rows
-//    in rank order ("Data Flow": routed_out, residual += ...), so y never
-//    leaves the chip.
+//  k_gate_up_gemv: one item per wave (union expert, two consecutive j: 2 gate
+//    rows + 2 up rows, 8 KB at d = 4096), all of its loads issued before any
+//    arithmetic; h_j = silu(g_j) * u_j ("SSD Streaming Expert Layers", "Math
+//    Contract") is written as prepped fp16.
+//  k_down_combine_gemv: a block owns 8 output rows for ALL union experts.  It
+//    issues those rows' weight loads first, copies h of all pairs into LDS
+//    meanwhile, and finishes with the weighted combine of its rows in rank
+//    order ("Data Flow": gather outputs x routing weights, residual += ...),
+//    so y never leaves the chip.
 //
-// Lane layout: a row of G groups (64 inputs each) is spread over TPR lanes
-// (the largest power of two dividing G, at most 64), each lane owning GPL =
-// G/TPR consecutive groups (32*GPL contiguous bytes of the row), so one wave
-// instruction covers 64/TPR rows.
+// Both kernels stage the call's routing metadata (at most 16 pairs) in LDS
+// first, so no dependent global load sits inside their loops.
+//
+// Lane layout: a row of G groups (64 inputs each) is spread over TPR lanes,
+// each lane owning GPL consecutive groups (32*GPL contiguous bytes of the
+// row), so one wave instruction covers 64/TPR rows.  gate_up rows have one
+// group per lane (TPR = d/64, 32 or 64); down rows GPL = 1..3.
+#include <algorithm>
+
 #include "device.hpp"
 #include "smoe_internal.hpp"
 
 namespace smoe {
 namespace {
 
-constexpr int kGemvThreads = 256;
-constexpr int kJPerWave = 4;          // gate_up: j-rows per wave
-constexpr int kDownRowsGemv = 8;      // down: output rows per block
+constexpr int kDecThreads = 256;
+constexpr int kDecWaves = kDecThreads / 64;
+constexpr int kJ = 2;                 // gate_up item: j0, j0+1
+constexpr int kGuRows = 2 * kJ;       // gate rows then up rows
+constexpr int kDnRows = 8;            // down: output rows per block item
+constexpr int kMaxDecPairs = 16;      // B * K <= 16 on this path
+// gate_up: one 4-wave block per compute unit, i.e. one streaming wave per SIMD:
+// the arithmetic (about 9 VALU ops per packed word) then hides under the next
+// item's loads instead of piling up once all of a burst has landed
+constexpr int kGuBlocksPerCU = 1;
+constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU, h staged once per block
+constexpr int kHRegs = 6;             // down: h chunks per thread loaded ahead of the weights
 // down: (expert, row step) items per wave per batch of loads
 template <int GPL>
 constexpr int items_per_wave() { return GPL >= 3 ? 2 : 4; }
@@ -62,116 +78,127 @@ __device__ __forceinline__ float lane_row_dot(const uint4 (&w)[GPL][2], const fl
   return part;
 }
 
-// ----------------------------------------------------------------- gate_up
-template <int NTOK>
-__global__ __launch_bounds__(kGemvThreads) void k_gate_up_gemv(FfnArgs a) {
-  constexpr int kRows = 2 * kJPerWave;            // gate rows then up rows
-  __shared__ float red[kGemvThreads / 64][kRows][NTOK];
-  const int u = blockIdx.y;                        // < min(E, B*K): index always in range
-  const int nU = *a.n_union;
-  const int e = a.union_experts[u];
-  const int pb = a.expert_offsets[u];
-  const int ne = a.expert_offsets[u + 1] - pb;     // 1 .. NTOK
-  if (u >= nU) return;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int d = a.d, G = d / 64, C = d / 8;
-  const int tpr = G, rps = 64 / tpr;               // one group per lane
-  const int li = lane % tpr, slot = lane / tpr;
-  const int j0 = (blockIdx.x * (kGemvThreads / 64) + wave) * kJPerWave;
-  // per-expert bases (uniform), selected per lane by pointer, never by struct index
+// Routing metadata of the call (at most 16 pairs), staged once in LDS.
+struct DecMeta {
+  int n_union;
+  int experts[kMaxDecPairs];
+  int offsets[kMaxDecPairs + 1];
+  int pairs[kMaxDecPairs];    // pair_list
+  int pos[kMaxDecPairs];      // pair_pos
+  float w[kMaxDecPairs];      // topk_w
+};
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// ------------------------------------------------------------ gate_up items
+// One item: union slot u, j0 = 2 * (item % (f/2)); rows (gate j0, gate j0+1,
+// up j0, up j0+1).  TPR lanes per row (one group each), 64/TPR rows per step.
+template <int TPR>
+struct GuBuf {
+  static constexpr int kSteps = kGuRows / (64 / TPR);
+  uint4 w[kSteps][2];
+  uint32_t s[kSteps], b[kSteps];
+};
+
+template <int TPR>
+__device__ __forceinline__ void gu_load(const FfnArgs& a, const DecMeta& m, int item, int lane,
+                                        GuBuf<TPR>& buf) {
+  constexpr int kRps = 64 / TPR;
+  const int per = a.f / kJ;
+  const int u = uniform(item / per);
+  const int j0 = (item - u * per) * kJ;
+  const int e = uniform(m.experts[u]);
+  const int G = a.d / 64, C = a.d / 8;
+  const int li = lane % TPR, slot = lane / TPR;
   const uint32_t* gw = a.gate.w + e * a.gate.stride_w;
   const uint16_t* gs = a.gate.s + e * a.gate.stride_sb;
   const uint16_t* gb = a.gate.b + e * a.gate.stride_sb;
   const uint32_t* uw = a.up.w + e * a.up.stride_w;
   const uint16_t* us = a.up.s + e * a.up.stride_sb;
   const uint16_t* ub = a.up.b + e * a.up.stride_sb;
+#pragma unroll
+  for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
+    const int rs = k * kRps + slot;                 // < kGuRows: kRps divides it
+    const bool is_up = rs >= kJ;
+    const int64_t row = j0 + (rs % kJ);
+    const uint32_t* wr = (is_up ? uw : gw) + row * C + li * 8;
+    buf.w[k][0] = ld_stream4(wr);
+    buf.w[k][1] = ld_stream4(wr + 4);
+    buf.s[k] = (is_up ? us : gs)[row * G + li];
+    buf.b[k] = (is_up ? ub : gb)[row * G + li];
+  }
+  // keep every load of the item here: left to itself the scheduler sinks the
+  // scale/bias loads to their first use, after the next item's loads, which
+  // exposes a full memory latency per item
+  __builtin_amdgcn_sched_barrier(0);
+}
 
-  // 1. every weight load of this wave, raw; steps past the wave's rows are
-  //    skipped uniformly, lanes past them load a valid row and get zero scale
-  const int nsteps = (kRows + rps - 1) / rps;
-  uint4 w[kRows][2];
-  uint32_t sraw[kRows], braw[kRows];
+// Computes one item and writes its h values.  xr/xs: the lane's group of the
+// prepped activations of token t (t < NTOK).
+template <int NTOK, int TPR>
+__device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, int item, int lane,
+                                           const GuBuf<TPR>& buf, const uint4 (&xr)[NTOK][8],
+                                           const float2 (&xs)[NTOK]) {
+  constexpr int kRps = 64 / TPR;
+  const int per = a.f / kJ;
+  const int u = uniform(item / per);
+  const int j0 = (item - u * per) * kJ;
+  const int pb = uniform(m.offsets[u]);
+  const int ne = uniform(m.offsets[u + 1]) - pb;   // 1 .. NTOK
+  const int li = lane % TPR, slot = lane / TPR;
+  // r[k][t]: row (k*kRps + slot) against token t
+  float r[GuBuf<TPR>::kSteps][NTOK];
 #pragma unroll
-  for (int k = 0; k < kRows; ++k) {
-    if (k < nsteps) {
-      const int rs = k * rps + slot;
-      const bool live = rs < kRows;
-      const int rsc = live ? rs : kRows - 1;
-      const bool is_up = rsc >= kJPerWave;
-      const int64_t row = j0 + (rsc & (kJPerWave - 1));
-      const uint32_t* wr = (is_up ? uw : gw) + row * C + li * 8;
-      const int64_t sidx = row * G + li;
-      w[k][0] = ld_stream4(wr);
-      w[k][1] = ld_stream4(wr + 4);
-      const uint32_t sv = (is_up ? us : gs)[sidx], bv = (is_up ? ub : gb)[sidx];
-      sraw[k] = live ? sv : 0u;
-      braw[k] = live ? bv : 0u;
-    }
+  for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
+    const float sc[1] = {bf16_to_f32((uint16_t)buf.s[k])};
+    const float bi[1] = {bf16_to_f32((uint16_t)buf.b[k])};
+    const uint4 wk[1][2] = {{buf.w[k][0], buf.w[k][1]}};
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t)
+      r[k][t] = segment_sum(lane_row_dot<1>(wk, sc, bi, xr[t], &xs[t]), TPR);
   }
-  // 2. the pairs' activations for this lane's group
-  uint4 xr[NTOK][8];
-  float2 xs[NTOK];
+  // gate row j0 + jj sits in step jj / kRps at slot jj % kRps, its up row in
+  // step (kJ + jj) / kRps at the same slot (kRps is 1 or 2 = kJ)
 #pragma unroll
-  for (int t = 0; t < NTOK; ++t) {
-    const int tok = NTOK == 1 && a.B == 1 ? 0 : a.pair_list[pb + min(t, ne - 1)] / a.K;
-    const uint4* src = reinterpret_cast<const uint4*>(a.xp + (int64_t)tok * d) + li * 8;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) xr[t][q] = src[q];
-    xs[t] = a.xs[(int64_t)tok * G + li];
-  }
-  const int pair0 = a.pair_list[pb];
-  const int pair1 = NTOK > 1 ? a.pair_list[pb + min(1, ne - 1)] : pair0;
-  // 3. dot products, row sums across the row's lanes
-#pragma unroll
-  for (int k = 0; k < kRows; ++k) {
-    if (k < nsteps) {   // uniform: every lane takes part in the reductions
-      const int rs = k * rps + slot;
-      const float sc[1] = {bf16_to_f32((uint16_t)sraw[k])};
-      const float bi[1] = {bf16_to_f32((uint16_t)braw[k])};
-      const uint4 wk[1][2] = {{w[k][0], w[k][1]}};
-#pragma unroll
-      for (int t = 0; t < NTOK; ++t) {
-        if (t < ne) {
-          float part = lane_row_dot<1>(wk, sc, bi, xr[t], &xs[t]);
-          part = segment_sum(part, tpr);
-          if (li == 0 && rs < kRows) red[wave][rs][t] = part;
-        }
+  for (int jj = 0; jj < kJ; ++jj) {
+    if (kRps == 1 || slot == jj % kRps) {
+      const int kg = jj / kRps, ku = (kJ + jj) / kRps;
+      const int j = j0 + jj;
+      for (int q = 0; q < ne; ++q) {
+        const int p = uniform(m.pairs[pb + q]);
+        const int t = NTOK == 1 ? 0 : p / a.K;
+        const float g = (NTOK == 1 || t == 0) ? r[kg][0] : r[kg][NTOK - 1];
+        const float up = (NTOK == 1 || t == 0) ? r[ku][0] : r[ku][NTOK - 1];
+        const float h = silu_mul(g, up);
+        const half_t hv = (j & 1) ? (half_t)((float)(half_t)h * 0.0625f) : (half_t)h;
+        if (li == 0) a.hp[(int64_t)p * a.f + prepped_pos(j)] = f16_bits(hv);
       }
     }
   }
-  __syncthreads();
-  // 4. h_j = silu(g_j) * u_j, stored prepped
-  if (lane < kJPerWave * ne) {
-    const int jj = lane % kJPerWave, t = lane / kJPerWave;
-    const int j = j0 + jj;
-    const float h = silu_mul(red[wave][jj][t], red[wave][kJPerWave + jj][t]);
-    const half_t hv = (j & 1) ? (half_t)((float)(half_t)h * 0.0625f) : (half_t)h;
-    a.hp[(int64_t)(t == 0 ? pair0 : pair1) * a.f + prepped_pos(j)] = f16_bits(hv);
-  }
 }
 
-// --------------------------------------------------------- down + combine
-// Issue the loads of (up to) IPW items starting at `first`.
+// ------------------------------------------------------------- down items
+// Issue the loads of (up to) IPW (expert, row step) items of row block r0,
+// starting at item `first` and dealt every 4th to this wave.  Dead items and
+// lanes load a valid duplicate row and get zero scale and bias.  No early
+// exit: a branch here would keep the caller's in-flight loads alive across it.
 template <int GPL, int IPW = items_per_wave<GPL>()>
 __device__ __forceinline__ void down_load_items(
-    const FfnArgs& a, int first, int items, int steps, int rps, int slot, int li, int r0, int C,
-    int G, uint4 (&w)[IPW][GPL][2], uint32_t (&sraw)[IPW][GPL],
-    uint32_t (&braw)[IPW][GPL], int (&pbs)[IPW],
-    int (&nes)[IPW]) {
+    const FfnArgs& a, const DecMeta& m, int first, int items, int steps, int rps, int slot, int li,
+    int r0, int C, int G, uint4 (&w)[IPW][GPL][2], uint32_t (&sraw)[IPW][GPL],
+    uint32_t (&braw)[IPW][GPL]) {
 #pragma unroll
   for (int q = 0; q < IPW; ++q) {
-    // dead items / lanes load a valid duplicate row and get zero scale and bias
-    const int it = first + q * 4;
+    const int it = first + q * kDecWaves;
     const bool live_item = it < items;
-    const int itc = live_item ? it : items - 1;
-    const int uu = itc / steps, st = itc % steps;
-    const int e = a.union_experts[uu];
-    pbs[q] = live_item ? a.expert_offsets[uu] : 0;
-    nes[q] = live_item ? a.expert_offsets[uu + 1] - a.expert_offsets[uu] : 0;
+    // an empty union (every routed id invalid) loads expert 0 and uses none of it
+    const int itc = live_item ? it : max(items - 1, 0);
+    const int uu = uniform(itc / steps), st = itc % steps;
+    const int e0 = uniform(m.experts[uu]);
+    const int e = (unsigned)e0 < (unsigned)a.E ? e0 : 0;
     const int rr = st * rps + slot;
-    const bool live = live_item && rr < kDownRowsGemv;
-    const int64_t row = r0 + min(rr, kDownRowsGemv - 1);
+    const bool live = live_item && rr < kDnRows;
+    const int64_t row = r0 + min(rr, kDnRows - 1);
     const uint32_t* wr = a.down.w + e * a.down.stride_w + row * C + li * GPL * 8;
     const uint16_t* sr = a.down.s + e * a.down.stride_sb + row * G + li * GPL;
     const uint16_t* br = a.down.b + e * a.down.stride_sb + row * G + li * GPL;
@@ -184,67 +211,96 @@ __device__ __forceinline__ void down_load_items(
       braw[q][gi] = live ? bv : 0u;
     }
   }
+  __builtin_amdgcn_sched_barrier(0);               // issue them here (see gu_load)
 }
 
-template <int GPL>
-__global__ __launch_bounds__(kGemvThreads) void k_down_combine_gemv(FfnArgs a) {
-  constexpr int IPW = items_per_wave<GPL>();
-  extern __shared__ __align__(16) char smem[];
-  const int f = a.f, G = f / 64, C = f / 8, K = a.K, B = a.B, P = B * K;
-  const int hx_chunks = (P * C + 63) / 64 * 64;                        // padded for the DMA tail
-  uint4* hx = reinterpret_cast<uint4*>(smem);                          // [P][C] prepped h
-  float2* hsum = reinterpret_cast<float2*>(hx + hx_chunks);            // [P][G] (X, C)
-  float* ylds = reinterpret_cast<float*>(hsum + (size_t)P * G);        // [P][kDownRowsGemv]
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// Shared memory of the down kernel: [P][C] prepped h, [P][G] (X, C) sums,
+// [P][kDnRows] per-pair outputs of the block's rows.
+size_t decode_smem(const FfnArgs& a) {
+  const size_t P = (size_t)a.B * a.K;
+  const size_t hx_chunks = (P * (a.f / 8) + 63) / 64 * 64;
+  return hx_chunks * 16 + P * (a.f / 64) * 8 + P * kDnRows * 4;
+}
+
+// Routing metadata -> LDS (union arrays hold min(E, P) experts).
+__device__ __forceinline__ void load_meta(const FfnArgs& a, DecMeta& m) {
+  const int P = a.B * a.K, maxU = min(a.E, P);
+  if (threadIdx.x == 0) m.n_union = *a.n_union;
+  if (threadIdx.x <= kMaxDecPairs) {
+    const int i = threadIdx.x;
+    if (i < maxU) m.experts[i] = a.union_experts[i];
+    if (i <= maxU) m.offsets[i] = a.expert_offsets[i];
+    if (i < P) {
+      m.pairs[i] = a.pair_list[i];
+      m.pos[i] = a.pair_pos[i];
+      m.w[i] = a.topk_w[i];
+    }
+  }
+  __syncthreads();
+}
+
+// grid: one 4-wave block per compute unit (at most one wave per item).  Wave
+// w takes items w, w + W, w + 2W, ...; the next item's loads go out before
+// the current one is computed, so each wave streams its share with one item
+// in flight while it computes.
+template <int NTOK, int TPR>
+__global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a) {
+  __shared__ DecMeta m;
+  const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int nU = *a.n_union;
-  const int tpr = G / GPL, rps = 64 / tpr;
-  const int li = lane % tpr, slot = lane / tpr;
-  const int steps = (kDownRowsGemv + rps - 1) / rps;   // row steps per expert
-  const int r0 = blockIdx.x * kDownRowsGemv;
-  const int items = nU * steps;
-
-  // this wave's items (expert slot, row step), dealt round-robin over the 4 waves;
-  // expert ids are read as scalars and every weight load is issued at once
-  uint4 w[IPW][GPL][2];
-  uint32_t sraw[IPW][GPL], braw[IPW][GPL];
-  int pbs[IPW], nes[IPW];
-  down_load_items<GPL>(a, wave, items, steps, rps, slot, li, r0, C, G, w, sraw, braw, pbs, nes);
-  // h of every pair (written by gate_up, L2-resident) goes straight to LDS:
-  // each wave copies 1 KB per instruction (lane i -> 16 bytes at base + 16 i)
-  {
-    const int nchunk = P * C;
-    const uint4* src = reinterpret_cast<const uint4*>(a.hp);
-    for (int cb = wave * 64; cb < nchunk; cb += kGemvThreads) {
-      const int i = min(cb + lane, nchunk - 1);
-      __builtin_amdgcn_global_load_lds(src + i, (__attribute__((address_space(3))) void*)(hx + cb),
-                                       16, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
+  load_meta(a, m);
+  const int nU = uniform(m.n_union);
+  const int n_items = nU * (a.f / kJ);
+  const int W = gridDim.x * kDecWaves;
+  const int wid = blockIdx.x * kDecWaves + wave;
+  if (wid >= n_items) return;                     // no barrier follows
+  GuBuf<TPR> b0, b1;
+  gu_load<TPR>(a, m, wid, lane, b0);
+  // this lane's group of every token's prepped activations
+  const int G = a.d / 64, li = lane % TPR;
+  uint4 xr[NTOK][8];
+  float2 xs[NTOK];
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) {
+    const int tt = min(t, a.B - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(a.xp + (int64_t)tt * a.d) + li * 8;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xr[t][q] = src[q];
+    xs[t] = a.xs[(int64_t)tt * G + li];
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < P * G; i += kGemvThreads) {
-    const uint16_t* hh = reinterpret_cast<const uint16_t*>(hx + (size_t)(i / G) * C + (i % G) * 8);
-    // halves of a chunk: (x0,x4) (x1/16,x5/16) (x2,x6) (x3/16,x7/16)
-    float X = 0.f, S = 0.f;
-#pragma unroll 8
-    for (int z = 0; z < 64; ++z) {
-      const float st = (float)bits_f16(hh[z]);
-      S += st;
-      X += (z & 2) ? 16.0f * st : st;
-    }
-    hsum[i] = make_float2(X, 1024.0f * S);
+  // two items in flight: item i computes while i + W loads (a wave past the
+  // end reloads its current item, which is then not computed again)
+  for (int i = wid; i < n_items; i += 2 * W) {
+    const int i1 = i + W < n_items ? i + W : i;
+    gu_load<TPR>(a, m, i1, lane, b1);
+    gu_compute<NTOK, TPR>(a, m, i, lane, b0, xr, xs);
+    if (i + W >= n_items) break;
+    const int i2 = i + 2 * W < n_items ? i + 2 * W : i1;
+    gu_load<TPR>(a, m, i2, lane, b0);
+    gu_compute<NTOK, TPR>(a, m, i + W, lane, b1, xr, xs);
   }
-  __syncthreads();
+}
 
-  for (int first = wave; first < items; first += 4 * IPW) {
+// One row block: every (expert, row step) item of rows r0..r0+7 against the
+// staged h, then the weighted combine of those rows.  `w`/`sraw`/`braw` hold
+// the first batch of items (loaded by the caller); larger unions reload.
+template <int GPL, int IPW = items_per_wave<GPL>()>
+__device__ __forceinline__ void down_row_block(const FfnArgs& a, const DecMeta& m, int r0, int wave,
+                                               int items, int steps, int rps, int slot, int li,
+                                               int tpr, int C, int G, const uint4* hx,
+                                               const float2* hsum, float* ylds,
+                                               uint4 (&w)[IPW][GPL][2],
+                                               uint32_t (&sraw)[IPW][GPL],
+                                               uint32_t (&braw)[IPW][GPL]) {
+  for (int first = wave; first < items; first += kDecWaves * IPW) {
     if (first != wave)
-      down_load_items<GPL>(a, first, items, steps, rps, slot, li, r0, C, G, w, sraw, braw, pbs, nes);
+      down_load_items<GPL>(a, m, first, items, steps, rps, slot, li, r0, C, G, w, sraw, braw);
 #pragma unroll
     for (int q = 0; q < IPW; ++q) {
-      const int it = first + q * 4;
+      const int it = first + q * kDecWaves;
       if (it < items) {   // uniform across the wave
-        const int st = it % steps;
+        const int uu = uniform(it / steps), st = it % steps;
+        const int pb = uniform(m.offsets[uu]), ne = uniform(m.offsets[uu + 1]) - pb;
         const int rr = st * rps + slot;
         float sc[GPL], bi[GPL];
 #pragma unroll
@@ -252,45 +308,116 @@ __global__ __launch_bounds__(kGemvThreads) void k_down_combine_gemv(FfnArgs a) {
           sc[gi] = bf16_to_f32((uint16_t)sraw[q][gi]);
           bi[gi] = bf16_to_f32((uint16_t)braw[q][gi]);
         }
-        for (int j = 0; j < nes[q]; ++j) {
-          const int p = a.pair_list[pbs[q] + j];
+        for (int j = 0; j < ne; ++j) {
+          const int p = uniform(m.pairs[pb + j]);
           const uint4* xc = hx + (size_t)p * C + li * GPL * 8;
           const float2* xsm = hsum + (size_t)p * G + li * GPL;
           float part = lane_row_dot<GPL>(w[q], sc, bi, xc, xsm);
           part = segment_sum(part, tpr);
-          if (li == 0 && rr < kDownRowsGemv) ylds[p * kDownRowsGemv + rr] = part;
+          if (li == 0 && rr < kDnRows) ylds[p * kDnRows + rr] = part;
         }
       }
     }
   }
   __syncthreads();
   // combine: out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k ascending
-  for (int i = threadIdx.x; i < B * kDownRowsGemv; i += kGemvThreads) {
-    const int t = i / kDownRowsGemv, rr = i % kDownRowsGemv;
+  const int K = a.K;
+  if (threadIdx.x < a.B * kDnRows) {
+    const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
     float acc = 0.f;
     for (int k = 0; k < K; ++k) {
       const int p = t * K + k;
-      if (a.pair_pos[p] < 0) continue;
-      acc += a.topk_w[p] * ylds[p * kDownRowsGemv + rr];
+      if (m.pos[p] < 0) continue;
+      acc += m.w[p] * ylds[p * kDnRows + rr];
     }
     const int64_t o = (int64_t)t * a.d + r0 + rr;
     const float res = a.residual ? a.residual[o] : 0.f;
     a.out[o] = res + acc;
   }
+  __syncthreads();                                 // ylds is free again
 }
 
-size_t down_gemv_smem(const FfnArgs& a) {
-  const size_t P = (size_t)a.B * a.K;
-  const size_t hx_chunks = (P * (a.f / 8) + 63) / 64 * 64;
-  return hx_chunks * 16 + P * (a.f / 64) * 8 + P * kDownRowsGemv * 4;
-}
-
+// grid: two 4-wave blocks per compute unit (at most one per row block);
+// block b takes row blocks b, b + grid, ... of 8 output rows x all union
+// experts.
 template <int GPL>
-hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
-  SMOE_LAUNCH(t, k_down_combine_gemv<GPL>, dim3(a.d / kDownRowsGemv), dim3(kGemvThreads),
-                     down_gemv_smem(a), s,
-                     a);
-  return hipGetLastError();
+__global__ __launch_bounds__(kDecThreads) void k_down_combine_gemv(FfnArgs a) {
+  constexpr int IPW = items_per_wave<GPL>();
+  __shared__ DecMeta m;
+  extern __shared__ __align__(16) char smem[];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int P = a.B * a.K;
+  load_meta(a, m);
+  const int nU = uniform(m.n_union);
+  const int f = a.f, G = f / 64, C = f / 8;
+  const int hx_chunks = (P * C + 63) / 64 * 64;
+  uint4* hx = reinterpret_cast<uint4*>(smem);                          // [P][C]
+  float2* hsum = reinterpret_cast<float2*>(hx + hx_chunks);            // [P][G]
+  float* ylds = reinterpret_cast<float*>(hsum + (size_t)P * G);        // [P][kDnRows]
+  const int tpr = G / GPL, rps = 64 / tpr;
+  const int li = lane % tpr, slot = lane / tpr;
+  const int steps = (kDnRows + rps - 1) / rps;
+  const int items = nU * steps;
+  const int n_rb = a.d / kDnRows;
+  const int stride = gridDim.x;
+
+  // h of every pair (written by gate_up, L2-resident) is requested first with
+  // ordinary loads, then the first row block's weights: the wait for h then
+  // leaves the weight loads in flight while the group sums are formed
+  uint4 w0[IPW][GPL][2];
+  uint32_t s0[IPW][GPL], b0[IPW][GPL];
+  const int nchunk = P * C;
+  const uint4* hsrc = reinterpret_cast<const uint4*>(a.hp);
+  // six chunks a thread held in named registers (an array here ends up in
+  // scratch), clamped to the last chunk past the end
+  const int hi0 = threadIdx.x;
+  const uint4 h0 = hsrc[min(hi0 + 0 * kDecThreads, nchunk - 1)];
+  const uint4 h1 = hsrc[min(hi0 + 1 * kDecThreads, nchunk - 1)];
+  const uint4 h2 = hsrc[min(hi0 + 2 * kDecThreads, nchunk - 1)];
+  const uint4 h3 = hsrc[min(hi0 + 3 * kDecThreads, nchunk - 1)];
+  const uint4 h4 = hsrc[min(hi0 + 4 * kDecThreads, nchunk - 1)];
+  const uint4 h5 = hsrc[min(hi0 + 5 * kDecThreads, nchunk - 1)];
+  __builtin_amdgcn_sched_barrier(0);
+  int rb = blockIdx.x;
+  down_load_items<GPL>(a, m, wave, items, steps, rps, slot, li, rb * kDnRows, C, G, w0, s0, b0);
+  // (threads past the end rewrite chunk nchunk-1 with the value it already has)
+  hx[min(hi0 + 0 * kDecThreads, nchunk - 1)] = h0;
+  hx[min(hi0 + 1 * kDecThreads, nchunk - 1)] = h1;
+  hx[min(hi0 + 2 * kDecThreads, nchunk - 1)] = h2;
+  hx[min(hi0 + 3 * kDecThreads, nchunk - 1)] = h3;
+  hx[min(hi0 + 4 * kDecThreads, nchunk - 1)] = h4;
+  hx[min(hi0 + 5 * kDecThreads, nchunk - 1)] = h5;
+  for (int i = threadIdx.x + kHRegs * kDecThreads; i < nchunk; i += kDecThreads) hx[i] = hsrc[i];
+  __syncthreads();
+  // group sums (X, C) of h: one (pair, group) per thread, 8 chunks of 8 halves
+  for (int i = threadIdx.x; i < P * G; i += kDecThreads) {
+    const uint4* hc = hx + (size_t)(i / G) * C + (i % G) * 8;
+    float X = 0.f, S = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint4 v = hc[c];
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        // slot z of the chunk holds (x_z, x_{z+4}); odd z are pre-divided by 16
+        const float lo = (float)bits_f16((uint16_t)(wv[z] & 0xFFFFu));
+        const float hi = (float)bits_f16((uint16_t)(wv[z] >> 16));
+        S += lo + hi;
+        X += (z & 1) ? 16.0f * (lo + hi) : (lo + hi);
+      }
+    }
+    hsum[i] = make_float2(X, 1024.0f * S);
+  }
+  __syncthreads();
+
+  for (; rb < n_rb; rb += stride) {
+    if (rb != (int)blockIdx.x)
+      down_load_items<GPL>(a, m, wave, items, steps, rps, slot, li, rb * kDnRows, C, G, w0, s0,
+                           b0);
+    down_row_block<GPL>(a, m, rb * kDnRows, wave, items, steps, rps, slot, li, tpr, C, G, hx,
+                        hsum, ylds, w0, s0, b0);
+  }
 }
 
 int gpl_of(int G) {
@@ -299,27 +426,58 @@ int gpl_of(int G) {
   return G / t;
 }
 
+// Compute units of the current device, cached per device (an attribute
+// lookup, not state of any call).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int NTOK, int TPR>
+hipError_t launch_gate_up_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+  const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
+  const int items = max_union * (a.f / kJ);
+  const int ncu = cu_count();
+  if (ncu <= 0) return hipErrorInvalidDevice;
+  const int grid = std::min((items + kDecWaves - 1) / kDecWaves, ncu * kGuBlocksPerCU);
+  SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR>), dim3(grid), dim3(kDecThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int GPL>
+hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+  const int ncu = cu_count();
+  if (ncu <= 0) return hipErrorInvalidDevice;
+  const int grid = std::min(a.d / kDnRows, ncu * kDnBlocksPerCU);
+  SMOE_LAUNCH(t, k_down_combine_gemv<GPL>, dim3(grid), dim3(kDecThreads), decode_smem(a), s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-// The small-batch path applies when every expert serves at most two pairs,
-// the staged h fits in LDS, and the lanes' group counts are supported
-// (gate_up: one group per lane; down: up to three).
+// The decode path applies to B <= 2 tokens (B*K <= 16) with d = 2048 or 4096
+// (one gate_up group per lane, 32 or 64 lanes a row), f/64 split into 1-3
+// groups per lane, and the staged h within 64 KB of LDS.
 bool gemv_path_ok(const FfnArgs& a) {
-  if (a.B > 2 || a.B * a.K > 16) return false;
-  if (gpl_of(a.d / 64) != 1 || gpl_of(a.f / 64) > 3) return false;
-  if (a.f % (kJPerWave * (kGemvThreads / 64)) != 0 || a.d % kDownRowsGemv != 0) return false;
-  return down_gemv_smem(a) <= 64 * 1024;
+  if (a.B < 1 || a.B > 2 || a.B * a.K > kMaxDecPairs) return false;
+  if (a.d != 2048 && a.d != 4096) return false;
+  if (gpl_of(a.f / 64) > 3 || a.f % kJ != 0 || a.d % kDnRows != 0) return false;
+  return decode_smem(a) <= 64 * 1024;
 }
 
 hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {
   if (gate_up) {
-    const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
-    const dim3 grid(a.f / (kJPerWave * (kGemvThreads / 64)), max_union);
     if (a.B == 1)
-      SMOE_LAUNCH(t, k_gate_up_gemv<1>, grid, dim3(kGemvThreads), 0, s, a);
-    else
-      SMOE_LAUNCH(t, k_gate_up_gemv<2>, grid, dim3(kGemvThreads), 0, s, a);
-    return hipGetLastError();
+      return a.d == 4096 ? launch_gate_up_gemv<1, 64>(a, s, t) : launch_gate_up_gemv<1, 32>(a, s, t);
+    return a.d == 4096 ? launch_gate_up_gemv<2, 64>(a, s, t) : launch_gate_up_gemv<2, 32>(a, s, t);
   }
   switch (gpl_of(a.f / 64)) {
     case 1: return launch_down_gemv<1>(a, s, t);

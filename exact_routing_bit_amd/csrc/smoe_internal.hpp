@@ -108,6 +108,7 @@ struct FfnArgs {
   uint16_t* hp;
   float2* hs;
   float* y;
+  uint32_t* status;  // workspace status area: status bits, tickets, sync counters
 };
 
 // ------------------------------------------------------------- launchers

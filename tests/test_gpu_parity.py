@@ -139,7 +139,11 @@ FWD_CASES = [
     (small_config("hot", 1024, 8, 4, 256, 64), 64, True),            # up to 4 token tiles
     (small_config("fused", 512, 32, 8, 128, 64, fused=True), 64, False),
     (small_config("wide", 2048, 16, 2, 128, 3, bf16=False), 3, True),
-    (small_config("gemv_b2", 1024, 32, 8, 1536, 2), 2, True),           # small-batch path, 3 groups/lane
+    (small_config("mfma_b2", 1024, 32, 8, 1536, 2), 2, True),           # B=2 off the decode path
+    (small_config("dec_b2", 2048, 32, 8, 1536, 2), 2, True),            # decode kernel, 32 lanes/row
+    (small_config("dec_b2_f512", 4096, 64, 8, 512, 2), 2, False),       # 1 down group per lane
+    (small_config("dec_b1_f192", 2048, 16, 4, 192, 1), 1, True),        # 3 groups, 1 lane per row
+    (small_config("dec_b2_e8", 2048, 8, 8, 512, 2), 2, False),          # every expert, E < B*K
     (small_config("gemv_b1", 4096, 64, 8, 1536, 1), 1, False),
     (small_config("gemv_k16", 2048, 64, 16, 512, 1), 1, True),
 ]
@@ -282,6 +286,27 @@ def test_bad_expert_sets_status_and_skips_pair(smoe):
     smoe.moe_forward(desc, layer.experts, up(x), up(idx_bad), up(w), layer.union, out, layer.ws)
     assert smoe.read_status(layer.ws) & smoe.SMOE_STATUS_BAD_EXPERT
     assert rel_l2(down(out), ref) <= TOL
+
+
+@pytest.mark.parametrize("B", [1, 2])
+def test_decode_all_experts_bad_gives_residual(smoe, B):
+    """Every routed id invalid: an empty union on the decode kernels.  Nothing
+    is loaded for it, the combine adds nothing and the residual comes back."""
+    cfg = small_config("allbad", 2048, 16, 4, 512, B)
+    L = synth.make_layer(cfg)
+    x = synth.hidden(0, 0, 7, B, 2048)
+    res = synth.hidden(0, 0, 8, B, 2048, tensor=synth.T_RESIDUAL)
+    idx = np.full((B, 4), 77, np.int32)
+    w = np.full((B, 4), 0.25, np.float32)
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=B, device=dev())
+    smoe.build_union(desc, up(idx), layer.union, layer.ws)
+    assert int(down(layer.union.n_union)[0]) == 0
+    out = torch.empty(B, 2048, dtype=torch.float32, device=dev())
+    smoe.moe_forward(desc, layer.experts, up(x), up(idx), up(w), layer.union, out, layer.ws,
+                     residual=up(res))
+    assert smoe.read_status(layer.ws) & smoe.SMOE_STATUS_BAD_EXPERT
+    assert np.array_equal(down(out), res)
 
 
 def test_empty_batch_is_noop(smoe):
