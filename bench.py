@@ -112,7 +112,8 @@ def time_layer(stack, xs, steps, warmup):
 def time_gate_up(stack, xs, launches):
     """Mean gate_up kernel duration (s): HIP events on the launch stream around
     `launches` back-to-back gate_up launches over the rotating layers, all
-    with the routing (|U| = 8 experts at B = 1) of one routed token.  Events
+    with the logits (|U| = 8 experts at B = 1) of one routed token; at B = 1
+    the kernel also ranks them and builds the union.  Events
     around each single launch would add the runtime's marker overhead
     (about 3 us) to every sample; back to back, only the dispatch gaps
     between consecutive kernels remain."""
@@ -139,7 +140,7 @@ def union_sizes(stack, xs, steps):
     nl = len(stack.layers)
     sizes = []
     for s in range(steps):
-        stack.stage(stack.smoe.SMOE_STAGE_ROUTE, s % nl, xs[s % len(xs)])
+        stack.call(s % nl, xs[s % len(xs)])
         sizes.append(stack.un.n_union.clone())
     torch.cuda.synchronize()
     return [int(t.item()) for t in sizes]
@@ -183,7 +184,7 @@ def cpu_baseline(cfg, seconds):
 # copy of COPY_BYTES.  The summary records a hash of the kernel's sources;
 # once they change, the figure is stale and `traffic` is reported as null.
 COPY_BYTES = 1 << 30
-ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64>"
+ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64, true>"
 ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/device.hpp",
                     "exact_routing_bit_amd/csrc/smoe_internal.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_up_gemv_decode_b1_traffic.txt")

@@ -253,6 +253,32 @@ int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_ex
 
 }  // namespace
 
+namespace {
+
+// Decode batches (B <= 2) on the matrix-vector path: the router kernel only
+// computes logits and preps the activations, the gate_up kernel ranks the
+// logits and builds the union itself (see ffn_gemv.hip), then down + combine.
+smoe::DecodeRoute decode_route(const smoe::RouteArgs& r) {
+  smoe::DecodeRoute d{};
+  d.logits = r.logits;
+  d.norm = r.norm;
+  d.topk_idx = r.topk_idx;
+  d.topk_w = r.topk_w;
+  d.n_union = r.n_union;
+  d.union_experts = r.union_experts;
+  d.expert_offsets = r.expert_offsets;
+  d.pair_list = r.pair_list;
+  d.pair_pos = r.pair_pos;
+  return d;
+}
+
+hipError_t launch_decode_logits(const smoe::RouteArgs& r, hipStream_t s,
+                                const smoe::LaunchTiming* t = nullptr) {
+  return smoe::launch_router(r, false, false, false, s, t);   // logits + activation prep
+}
+
+}  // namespace
+
 SMOE_API int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w,
                             const smoe_experts* experts, const float* x, int32_t B,
                             const float* residual, float* out, float* logits, int32_t* topk_idx,
@@ -264,7 +290,14 @@ SMOE_API int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w,
                              topk_w, un, ws, ws_bytes, &r, &a);
   if (rc != SMOE_OK || B == 0) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err = smoe::launch_router(r, false, true, true, s);
+  hipError_t err;
+  if (smoe::gemv_path_ok(a)) {
+    err = launch_decode_logits(r, s);
+    if (err == hipSuccess) err = smoe::launch_gate_up_routed(a, decode_route(r), s);
+    if (err == hipSuccess) err = smoe::launch_down(a, s);
+    return hip_rc(err);
+  }
+  err = smoe::launch_router(r, false, true, true, s);
   if (err == hipSuccess) err = smoe::launch_ffn(a, s);
   return hip_rc(err);
 }
@@ -287,9 +320,14 @@ SMOE_API int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const 
   timing.start = static_cast<hipEvent_t>(start_event);
   timing.stop = static_cast<hipEvent_t>(stop_event);
   const smoe::LaunchTiming* t = start_event != nullptr ? &timing : nullptr;
+  const bool decode = smoe::gemv_path_ok(a);
   switch (stage) {
-    case SMOE_STAGE_ROUTE: return hip_rc(smoe::launch_router(r, false, true, true, s, t));
-    case SMOE_STAGE_GATE_UP: return hip_rc(smoe::launch_gate_up(a, s, t));
+    case SMOE_STAGE_ROUTE:
+      return hip_rc(decode ? launch_decode_logits(r, s, t)
+                           : smoe::launch_router(r, false, true, true, s, t));
+    case SMOE_STAGE_GATE_UP:
+      return hip_rc(decode ? smoe::launch_gate_up_routed(a, decode_route(r), s, t)
+                           : smoe::launch_gate_up(a, s, t));
     case SMOE_STAGE_DOWN: return hip_rc(smoe::launch_down(a, s, t));
     default: return hip_rc(smoe::launch_combine(a, s, t));
   }

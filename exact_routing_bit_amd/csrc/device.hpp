@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 namespace smoe {
@@ -187,6 +188,63 @@ __device__ __forceinline__ int wave_min_i(int v) {
   v = min(v, dpp_i<kDppMirror>(v));
   return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Top-k of one row of E <= 256 logits by one full wave (v[j] = logit of expert
+// lane + 64 j, -FLT_MAX past E): after the call lane k < K holds the rank-k
+// logit and expert, ranked by logit descending and, on equal logits, expert
+// index ascending.  K rounds of a wave-wide arg-max (DPP max, then the lowest
+// index among the maxima).
+__device__ __forceinline__ void wave_topk(const float (&v)[4], int E, int K, float& my_v,
+                                          int& my_e) {
+  const int lane = __lane_id();
+  bool live[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) live[j] = lane + 64 * j < E;
+  my_v = 0.f;
+  my_e = 0;
+  for (int k = 0; k < K; ++k) {
+    // this lane's best live candidate (ascending j keeps the lower index on ties)
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      if (live[j] && (v[j] > bv || (v[j] == bv && e < be))) {
+        bv = v[j];
+        be = e;
+      }
+    }
+    const float m = wave_max(bv);
+    const int win = wave_min_i(bv == m ? be : 0x7FFFFFFF);   // lowest index among the maxima
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (win == lane + 64 * j) live[j] = false;
+    if (lane == k) {
+      my_v = m;
+      my_e = win;
+    }
+  }
+}
+
+// Routing weight of the lane's rank (lane < K) from wave_topk's results:
+// exp(l - max) over the top-k sum (norm_topk_prob) or over all E experts.
+__device__ __forceinline__ float topk_weight(const float (&v)[4], int E, int K, bool norm,
+                                             float my_v) {
+  const int lane = __lane_id();
+  const float top = readlane(my_v, 0);
+  const float p = lane < K ? expf(my_v - top) : 0.f;
+  float den;
+  if (norm) {
+    den = wave_sum(p);
+  } else {
+    float z = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < E) z += expf(v[j] - top);
+    den = wave_sum(z);
+  }
+  return p / den;
 }
 
 // The stored halves of 8 consecutive inputs (one packed word's worth) in the

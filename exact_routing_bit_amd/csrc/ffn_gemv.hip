@@ -43,7 +43,7 @@ constexpr int kMaxDecPairs = 16;      // B * K <= 16 on this path
 // the arithmetic (about 9 VALU ops per packed word) then hides under the next
 // item's loads instead of piling up once all of a burst has landed
 constexpr int kGuBlocksPerCU = 1;
-constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU, h staged once per block
+constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU (one row block each at d = 4096)
 constexpr int kHRegs = 6;             // down: h chunks per thread loaded ahead of the weights
 // down: (expert, row step) items per wave per batch of loads
 template <int GPL>
@@ -239,16 +239,103 @@ __device__ __forceinline__ void load_meta(const FfnArgs& a, DecMeta& m) {
   __syncthreads();
 }
 
+// The routing of the call, in LDS, from the logits (B <= 2 tokens, one wave
+// per token): top-k and weights exactly as the router's own tail computes
+// them ("Data Flow", serial step "EXACT ROUTING"), then the union and pair
+// lists ("Layer-Major Batched Prefill", "The Inversion") by wave 0 with
+// readlane counts over the P <= 16 pairs: pairs grouped by ascending expert,
+// ascending within.  Block 0 writes the same outputs smoe_route and
+// smoe_build_union would.
+__device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& r, DecMeta& m) {
+  __shared__ int s_e[kMaxDecPairs];
+  __shared__ float s_w[kMaxDecPairs];
+  const int wave = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int E = a.E, K = a.K, P = a.B * a.K;
+  if (wave < a.B) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = e < E ? r.logits[(int64_t)wave * E + e] : -FLT_MAX;
+    }
+    float my_v;
+    int my_e;
+    wave_topk(v, E, K, my_v, my_e);
+    const float w = topk_weight(v, E, K, r.norm != 0, my_v);
+    if (lane < K) {
+      s_e[wave * K + lane] = my_e;
+      s_w[wave * K + lane] = w;
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool in = lane < P;
+    const int e = in ? s_e[lane] : 0x7FFFFFFF;
+    int less = 0, same_before = 0;
+    bool first = in;
+    for (int q = 0; q < P; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      less += eq < e;
+      if (q < lane && eq == e) {
+        ++same_before;
+        first = false;
+      }
+    }
+    const uint64_t firsts = __ballot(first);
+    int distinct_less = 0;
+    for (int q = 0; q < P; ++q) {
+      const int eq = __builtin_amdgcn_readlane(e, q);
+      distinct_less += ((firsts >> q) & 1) && eq < e;
+    }
+    const int nU = __popcll(firsts);
+    const int qpos = less + same_before;          // place of this pair in pair_list
+    if (in) {
+      m.pairs[qpos] = lane;
+      m.pos[lane] = qpos;
+      m.w[lane] = s_w[lane];
+      if (first) {
+        m.experts[distinct_less] = e;
+        m.offsets[distinct_less] = less;
+      }
+    }
+    if (lane == 0) {
+      m.n_union = nU;
+      m.offsets[nU] = P;
+    }
+    if (blockIdx.x == 0) {
+      if (in) {
+        r.topk_idx[lane] = e;
+        r.topk_w[lane] = s_w[lane];
+        r.pair_list[qpos] = lane;
+        r.pair_pos[lane] = qpos;
+        if (first) {
+          r.union_experts[distinct_less] = e;
+          r.expert_offsets[distinct_less] = less;
+        }
+      }
+      if (lane == 0) {
+        *r.n_union = nU;
+        r.expert_offsets[nU] = P;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // grid: one 4-wave block per compute unit (at most one wave per item).  Wave
 // w takes items w, w + W, w + 2W, ...; the next item's loads go out before
 // the current one is computed, so each wave streams its share with one item
 // in flight while it computes.
-template <int NTOK, int TPR>
-__global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a) {
+template <int NTOK, int TPR, bool kRoute>
+__global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeRoute r) {
   __shared__ DecMeta m;
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  load_meta(a, m);
+  if (kRoute)
+    route_meta(a, r, m);
+  else
+    load_meta(a, m);
   const int nU = uniform(m.n_union);
   const int n_items = nU * (a.f / kJ);
   const int W = gridDim.x * kDecWaves;
@@ -441,15 +528,26 @@ int cu_count() {
   return cached[dev];
 }
 
-template <int NTOK, int TPR>
-hipError_t launch_gate_up_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+template <int NTOK, int TPR, bool kRoute>
+hipError_t launch_gate_up_gemv(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
+                               const LaunchTiming* t) {
   const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
   const int items = max_union * (a.f / kJ);
   const int ncu = cu_count();
   if (ncu <= 0) return hipErrorInvalidDevice;
   const int grid = std::min((items + kDecWaves - 1) / kDecWaves, ncu * kGuBlocksPerCU);
-  SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR>), dim3(grid), dim3(kDecThreads), 0, s, a);
+  SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, kRoute>), dim3(grid), dim3(kDecThreads), 0, s, a, r);
   return hipGetLastError();
+}
+
+template <bool kRoute>
+hipError_t launch_gate_up_any(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
+                              const LaunchTiming* t) {
+  if (a.B == 1)
+    return a.d == 4096 ? launch_gate_up_gemv<1, 64, kRoute>(a, r, s, t)
+                       : launch_gate_up_gemv<1, 32, kRoute>(a, r, s, t);
+  return a.d == 4096 ? launch_gate_up_gemv<2, 64, kRoute>(a, r, s, t)
+                     : launch_gate_up_gemv<2, 32, kRoute>(a, r, s, t);
 }
 
 template <int GPL>
@@ -474,16 +572,17 @@ bool gemv_path_ok(const FfnArgs& a) {
 }
 
 hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {
-  if (gate_up) {
-    if (a.B == 1)
-      return a.d == 4096 ? launch_gate_up_gemv<1, 64>(a, s, t) : launch_gate_up_gemv<1, 32>(a, s, t);
-    return a.d == 4096 ? launch_gate_up_gemv<2, 64>(a, s, t) : launch_gate_up_gemv<2, 32>(a, s, t);
-  }
+  if (gate_up) return launch_gate_up_any<false>(a, DecodeRoute{}, s, t);
   switch (gpl_of(a.f / 64)) {
     case 1: return launch_down_gemv<1>(a, s, t);
     case 2: return launch_down_gemv<2>(a, s, t);
     default: return launch_down_gemv<3>(a, s, t);
   }
+}
+
+hipError_t launch_gate_up_routed(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
+                                 const LaunchTiming* t) {
+  return launch_gate_up_any<true>(a, r, s, t);
 }
 
 }  // namespace smoe

@@ -40,55 +40,24 @@ __device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, fl
   xs[(int64_t)t * (d / 64) + g] = make_float2(X, 1024.0f * S);
 }
 
-// (v, e) ranks above (bv, be): larger logit, or equal logit and lower index.
-__device__ __forceinline__ bool ranks_above(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
-}
-
 // Top-k of one token's E <= 256 logits by one full wave; writes indices and
 // weights (rank order) to global memory and the indices to s_idx.
 __device__ void topk_token(const RouteArgs& a, int t, int32_t* s_idx) {
   const int lane = __lane_id();
   const int E = a.E, K = a.K;
   float v[4];
-  bool live[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = lane + 64 * j;
-    live[j] = e < E;
-    v[j] = live[j] ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
+    v[j] = e < E ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
   }
-  float my_v = 0.f;
-  int my_e = 0;
-  for (int k = 0; k < K; ++k) {
-    // this lane's best live candidate (ascending j keeps the lower index on ties)
-    float bv = -INFINITY;
-    int be = INT_MAX;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (live[j] && ranks_above(v[j], lane + 64 * j, bv, be)) { bv = v[j]; be = lane + 64 * j; }
-    const float m = wave_max(bv);
-    const int win = wave_min_i(bv == m ? be : INT_MAX);   // lowest index among the maxima
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (win == lane + 64 * j) live[j] = false;
-    if (lane == k) { my_v = m; my_e = win; }
-  }
-  const float top = readlane(my_v, 0);
-  const float p = lane < K ? expf(my_v - top) : 0.f;
-  float den;
-  if (a.norm) {
-    den = wave_sum(p);
-  } else {
-    float z = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (lane + 64 * j < E) z += expf(v[j] - top);
-    den = wave_sum(z);
-  }
+  float my_v;
+  int my_e;
+  wave_topk(v, E, K, my_v, my_e);
+  const float w = topk_weight(v, E, K, a.norm != 0, my_v);
   if (lane < K) {
     a.topk_idx[t * K + lane] = my_e;
-    a.topk_w[t * K + lane] = p / den;
+    a.topk_w[t * K + lane] = w;
     s_idx[t * K + lane] = my_e;
   }
 }
@@ -244,11 +213,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
     if (e < a.E) logits_wave<kBf16>(a, e, t0, min(kTokensPerWave, a.B - t0));
   }
   if (a.xp != nullptr) {
+    // (token, group) units dealt round-robin over the blocks first, so that
+    // every block preps a few and none holds up the launch's end
     const int G = a.d / 64;
     const int units = a.B * G;
-    const int nthreads = gridDim.x * gridDim.y * blockDim.x;
-    const int gid = (blockIdx.y * gridDim.x + blockIdx.x) * blockDim.x + threadIdx.x;
-    for (int u = gid; u < units; u += nthreads) prep_group(a.x, a.d, u / G, u % G, a.xp, a.xs);
+    const int nblocks = gridDim.x * gridDim.y;
+    const int bid = blockIdx.y * gridDim.x + blockIdx.x;
+    for (int u = bid + (int)threadIdx.x * nblocks; u < units; u += nblocks * blockDim.x)
+      prep_group(a.x, a.d, u / G, u % G, a.xp, a.xs);
   }
   if (!do_tail) return;
   // last block: every other block's logits are visible after its release and our acquire

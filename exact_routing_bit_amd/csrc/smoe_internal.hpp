@@ -111,6 +111,21 @@ struct FfnArgs {
   uint32_t* status;  // workspace status area: status bits, tickets, sync counters
 };
 
+// Routing done inside the decode gate_up kernel (smoe_moe_layer with B <= 2):
+// every block ranks the logits itself and builds the union in LDS; block 0
+// also writes the routing outputs.
+struct DecodeRoute {
+  const float* logits;     // [B, E] from the router kernel
+  int norm;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* n_union;
+  int32_t* union_experts;
+  int32_t* expert_offsets;
+  int32_t* pair_list;
+  int32_t* pair_pos;
+};
+
 // ------------------------------------------------------------- launchers
 // Optional timing events for a stage's main kernel: when `start` is set the
 // kernel is launched with hipExtLaunchKernelGGL, which submits the events
@@ -141,6 +156,10 @@ hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s);
 bool gemv_path_ok(const FfnArgs& a);
 hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up,
                        const LaunchTiming* t = nullptr);
+// gate_up with the routing tail (top-k, weights, union) folded in; the router
+// kernel then only computes logits and the prepped activations
+hipError_t launch_gate_up_routed(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
+                                 const LaunchTiming* t = nullptr);
 // prefill-chunk MFMA kernels
 hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up,
                            const LaunchTiming* t = nullptr);

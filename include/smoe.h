@@ -187,6 +187,9 @@ int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w, const smoe
  * microseconds.  Enqueuing
  * SMOE_STAGE_ROUTE, _GATE_UP, _DOWN and _COMBINE in this order on one stream
  * launches exactly the kernels of one smoe_moe_layer call, in the same order.
+ * For decode batches (B <= 2 on the matrix-vector path) the ROUTE stage only
+ * computes the logits; the ranking, weights, union and activation prep run
+ * at the start of the GATE_UP stage's kernel, and COMBINE is part of DOWN.
  * SMOE_EINVAL when only one event is given. */
 #define SMOE_STAGE_ROUTE 0    /* logits + activation prep, top-k + union */
 #define SMOE_STAGE_GATE_UP 1  /* gate/up projections and SwiGLU for every union expert */

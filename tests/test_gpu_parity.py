@@ -172,7 +172,10 @@ def test_forward_parity_injected_routing(smoe, cfg, B, with_res):
 
 
 @pytest.mark.parametrize("cfg,B", [(configs.TINY, 8), (small_config("l", 1024, 64, 8, 256, 64), 64),
-                                   (small_config("l1", 1024, 64, 8, 256, 1), 1)],
+                                   (small_config("l1", 1024, 64, 8, 256, 1), 1),
+                                   (small_config("l_dec1", 4096, 32, 8, 256, 1), 1),
+                                   (small_config("l_dec2", 2048, 64, 8, 512, 2), 2),
+                                   (small_config("l_dec2_nonorm", 2048, 40, 6, 192, 2, norm=False), 2)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_layer_parity(smoe, cfg, B):
     L = synth.make_layer(cfg)
@@ -189,6 +192,19 @@ def test_layer_parity(smoe, cfg, B):
     if bad:
         ref, _, _ = oracle_layer(L, x, cfg, idx=idx, w=down(layer.topk_w[:B]))
     assert rel_l2(out, ref) <= TOL
+    # the routing outputs (written by the router's tail, or for B <= 2 by the
+    # gate_up kernel's prologue) are exact on the logits the GPU computed
+    lg = down(layer.logits[:B])
+    idx_own, w_own = oracle.topk_softmax(lg, cfg.top_k, cfg.norm_topk_prob)
+    assert np.array_equal(idx, idx_own)
+    assert np.allclose(down(layer.topk_w[:B]), w_own, rtol=1e-6, atol=1e-7)
+    n, ue, off, pl, pp = oracle.build_union(idx, cfg.num_experts)
+    un = layer.union
+    assert int(down(un.n_union)[0]) == n
+    assert np.array_equal(down(un.union_experts)[:n], ue)
+    assert np.array_equal(down(un.expert_offsets)[:n + 1], off)
+    assert np.array_equal(down(un.pair_list)[:B * cfg.top_k], pl)
+    assert np.array_equal(down(un.pair_pos)[:B * cfg.top_k], pp)
 
 
 def test_deterministic_bitwise(smoe):
@@ -207,12 +223,12 @@ def test_stages_equal_layer_and_stamp_events(smoe, B):
     kernels (bitwise the same output), and the timing events given to a
     stage are stamped with its kernel's own duration."""
     import torch
-    cfg = small_config("stages", 1024, 32, 8, 256, B)
+    cfg = small_config("stages", 2048, 32, 8, 256, B)      # B <= 2: the decode kernels
     L = synth.make_layer(cfg)
-    x = up(synth.hidden(0, 0, 5, B, 1024))
+    x = up(synth.hidden(0, 0, 5, B, 2048))
     layer = smoe.Layer(desc_for(smoe, cfg), device_weights(L), max_batch=B, device=dev())
     ref = down(layer.forward(x))
-    out = torch.zeros(B, 1024, dtype=torch.float32, device=dev())
+    out = torch.zeros(B, 2048, dtype=torch.float32, device=dev())
     ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     ev[0].record()
     ev[1].record()
