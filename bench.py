@@ -41,6 +41,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--stack", action="store_true",
+                   help="run only the stacked harness (94 layers: prompt chunks, then decode)")
+    p.add_argument("--no-stack", action="store_true", help="leave the stacked harness out")
+    p.add_argument("--stack-layers", type=int, default=94)
+    p.add_argument("--stack-prompt", type=int, default=512)
+    p.add_argument("--stack-decode", type=int, default=128)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a device-to-device copy of COPY_BYTES (for the counter scale)")
     p.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -177,6 +183,131 @@ def cpu_baseline(cfg, seconds):
                       f"{len(routed)} experts generated beforehand), {el:.1f} s"}
 
 
+# ------------------------------------------------------------------ stack
+STACK_CHUNK = 64
+
+
+def stack_stats(idx_pre, nu_pre, idx_dec, E):
+    """Routing statistics of a stacked run (host arrays).
+
+    idx_pre [chunks, layers, tokens, K], nu_pre [chunks, layers]: prompt
+    chunks; idx_dec [steps, layers, 1, K]: decode steps.  Union size of a
+    (chunk, layer) = its distinct experts (checked against the device's
+    count); adjacent-step reuse of layer l at step n >= 1 = the share of
+    step n's K experts that step n-1 also used in layer l."""
+    import numpy as np
+    from synth import configs
+    C, L, T, K = idx_pre.shape
+    distinct = np.array([[len(np.unique(idx_pre[c, l])) for l in range(L)] for c in range(C)])
+    if not np.array_equal(distinct, nu_pre):
+        raise RuntimeError("device union sizes differ from the routing's distinct experts")
+    S = idx_dec.shape[0]
+    reuse = np.zeros((max(S - 1, 0), L))
+    for n in range(1, S):
+        for l in range(L):
+            reuse[n - 1, l] = len(np.intersect1d(idx_dec[n, l, 0], idx_dec[n - 1, l, 0])) / K
+    per_step = reuse.mean(axis=1) if S > 1 else np.zeros(0)
+    return {
+        "prefill_union_mean": float(distinct.mean()), "prefill_union_min": int(distinct.min()),
+        "prefill_union_max": int(distinct.max()),
+        "prefill_union_expected_uniform": round(configs.expected_union(E, K, T), 3),
+        "prefill_union_per_chunk": [round(float(v), 2) for v in distinct.mean(axis=1)],
+        "decode_reuse_mean": float(reuse.mean()) if S > 1 else None,
+        "decode_reuse_expected_uniform": K / E,
+        "decode_reuse_per_step": [round(float(v), 4) for v in per_step],
+        "decode_union_per_layer": K,
+    }
+
+
+def stack_harness(smoe, n_layers, prompt, steps):
+    """The stacked routed-expert path: n_layers layers of the decode shape
+    resident in HBM; a prompt of `prompt` tokens in chunks of 64, layer-major
+    (each chunk through every layer before the next chunk), then `steps`
+    single-token decode steps through every layer; h <- RMSNorm(h + MoE(h))
+    between layers, attention left out.  Inputs: RMS-normalised N(0, 1)
+    rows, prompt from one seeded stream, decode step n from its own."""
+    import numpy as np
+    import torch
+
+    import synth.gpu as sg
+    from synth import configs
+    cfg = configs.STACK
+    E, K, d = cfg.num_experts, cfg.top_k, cfg.d_model
+    if prompt % STACK_CHUNK:
+        raise ValueError("the prompt is a whole number of 64-token chunks")
+    chunks = prompt // STACK_CHUNK
+    t0 = time.perf_counter()
+    Ws = [sg.make_layer(cfg, layer=l) for l in range(n_layers)]
+    ex = [smoe.Experts(smoe.qmat(*W["gate"]), smoe.qmat(*W["up"]), smoe.qmat(*W["down"]))
+          for W in Ws]
+    torch.cuda.synchronize()
+    gen_s = time.perf_counter() - t0
+    args = smoe.StackArgs([W["router"] for W in Ws], ex)
+    desc = smoe.make_desc(d, cfg.ffn_dim, E, K, cfg.norm_topk_prob, cfg.router_bf16)
+    dev = torch.device("cuda:0")
+    ws = torch.zeros(smoe.workspace_size(desc, STACK_CHUNK), dtype=torch.uint8, device=dev)
+    smoe.workspace_init(ws)
+    un = smoe.UnionBuffers.alloc(E, STACK_CHUNK * K, dev)
+    tmp = torch.zeros(STACK_CHUNK, d, dtype=torch.float32, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    idx_pre = torch.zeros(chunks, n_layers, STACK_CHUNK, K, **i32)
+    w_pre = torch.zeros(chunks, n_layers, STACK_CHUNK, K, **f32)
+    nu_pre = torch.zeros(chunks, n_layers, **i32)
+    idx_dec = torch.zeros(steps, n_layers, 1, K, **i32)
+    w_dec = torch.zeros(steps, n_layers, 1, K, **f32)
+    nu_dec = torch.zeros(steps, n_layers, **i32)
+    h_pre = sg.hidden(cfg.seed, 0, 5000, prompt, d)
+    h_dec = [sg.hidden(cfg.seed, 0, 6000 + n, 1, d) for n in range(steps)]
+    # warm-up: one chunk and one decode step through the stack, on copies
+    warm = h_pre[:STACK_CHUNK].clone()
+    smoe.stack_forward(desc, args, warm, tmp, idx_pre[0], w_pre[0], un, ws, n_union=nu_pre[0])
+    warm = h_dec[0].clone()
+    smoe.stack_forward(desc, args, warm, tmp[:1], idx_dec[0], w_dec[0], un, ws,
+                       n_union=nu_dec[0])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record()
+    for c in range(chunks):
+        smoe.stack_forward(desc, args, h_pre[c * STACK_CHUNK:(c + 1) * STACK_CHUNK], tmp,
+                           idx_pre[c], w_pre[c], un, ws, n_union=nu_pre[c])
+    ev[1].record()
+    for n in range(steps):
+        smoe.stack_forward(desc, args, h_dec[n], tmp[:1], idx_dec[n], w_dec[n], un, ws,
+                           n_union=nu_dec[n])
+    ev[2].record()
+    torch.cuda.synchronize()
+    if smoe.read_status(ws) != 0:
+        raise RuntimeError("the stack reported a bad expert id")
+    pre_s = ev[0].elapsed_time(ev[1]) / 1e3
+    dec_s = ev[1].elapsed_time(ev[2]) / 1e3
+    st = stack_stats(idx_pre.cpu().numpy(), nu_pre.cpu().numpy(), idx_dec.cpu().numpy(), E)
+    if not np.all(nu_dec.cpu().numpy() == K):
+        raise RuntimeError("a decode step's union is not its K experts")
+    finite = bool(torch.isfinite(h_pre).all()) and all(bool(torch.isfinite(h).all()) for h in h_dec)
+    eb = cfg.expert_bytes()
+    pre_bytes = float(nu_pre.sum().item()) * eb
+    dec_bytes = steps * n_layers * K * eb
+    out = {
+        "workload": f"{cfg.name}: {n_layers} stacked routed layers (d=4096, 128 experts, top-8, "
+                    f"ffn 1536, 4-bit g64), h <- RMSNorm(h + MoE(h)); prompt {prompt} tokens "
+                    f"in chunks of {STACK_CHUNK}, layer-major; then {steps} decode steps at B=1",
+        "resident_expert_gb": round(n_layers * E * eb / 1e9, 2),
+        "weight_generation_s": round(gen_s, 2),
+        "prefill_s": round(pre_s, 5), "prefill_tokens_per_s": round(prompt / pre_s, 1),
+        "prefill_effective_gbps": round(pre_bytes / pre_s / 1e9, 1),
+        "decode_ms_per_token": round(dec_s / steps * 1e3, 4),
+        "decode_tokens_per_s": round(steps / dec_s, 2),
+        "decode_effective_gbps": round(dec_bytes / dec_s / 1e9, 1),
+        "decode_hbm_frac": round(dec_bytes / dec_s / 1e9 / HBM_PEAK_GBPS, 4),
+        "outputs_finite": finite,
+    }
+    out.update(st)
+    del Ws, ex, args
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ traffic
 # HBM traffic of the roofline kernel comes from two rocprofv3 --pmc passes
 # (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) over a short run of this script,
@@ -287,6 +418,14 @@ def main():
     import exact_routing_bit_amd as smoe
     from synth import configs
     torch.cuda.set_device(0)
+    if args.stack:
+        r = stack_harness(smoe, args.stack_layers, args.stack_prompt, args.stack_decode)
+        print(json.dumps({"metric": "stacked routed path: decode tokens/s (B=1 through every "
+                                    "layer) and prompt tokens/s",
+                          "value": r["decode_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                          "higher_is_better": True, "dtype": "f16", "data": "synthetic",
+                          "config": {"workload": r.pop("workload")}, "stack": r}), flush=True)
+        return
 
     dec = configs.DECODE
     stack = Stack(smoe, dec, args.layers, max_batch=64)
@@ -332,6 +471,10 @@ def main():
                                "hbm_frac": round(g64 / HBM_PEAK_GBPS, 4),
                                "steps": args.prefill_steps}
     del stack
+    torch.cuda.empty_cache()
+    if not args.no_stack:
+        result["stack"] = stack_harness(smoe, args.stack_layers, args.stack_prompt,
+                                        args.stack_decode)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -30,8 +30,8 @@ MAX_BATCH = 64
 SMOE_STAGE_ROUTE, SMOE_STAGE_GATE_UP, SMOE_STAGE_DOWN, SMOE_STAGE_COMBINE = 0, 1, 2, 3
 
 EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_build_union",
-            "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_read_status",
-            "smoe_strerror")
+            "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_rmsnorm",
+            "smoe_stack_forward", "smoe_read_status", "smoe_strerror")
 
 
 class SmoeError(RuntimeError):
@@ -79,6 +79,10 @@ def _load():
                                  ctypes.POINTER(Union), vp, sz, vp]
     L.smoe_moe_layer_stage.argtypes = [ctypes.c_int, dp, vp, ctypes.POINTER(Experts), vp, i32, vp,
                                        vp, vp, vp, vp, ctypes.POINTER(Union), vp, sz, vp, vp, vp]
+    L.smoe_rmsnorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
+    L.smoe_stack_forward.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_void_p),
+                                     ctypes.POINTER(Experts), vp, i32, ctypes.c_float, vp, vp, vp,
+                                     vp, ctypes.POINTER(Union), vp, sz, vp]
     L.smoe_read_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.smoe_strerror.argtypes = [ctypes.c_int]
     L.smoe_strerror.restype = ctypes.c_char_p
@@ -234,6 +238,48 @@ def moe_layer_stage(stage, desc, router_w, experts: Experts, x, out, topk_idx, t
                                     _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream),
                                     ev0, ev1),
            "smoe_moe_layer_stage")
+
+
+def rmsnorm(v, out=None, eps=1e-6, stream=None):
+    """out = v / sqrt(mean(v^2) + eps) per row (fp32 [B, d]); out may be v."""
+    if out is None:
+        out = torch.empty_like(v)
+    if v.dim() != 2 or out.shape != v.shape:
+        raise ValueError("rmsnorm takes matching [B, d] tensors")
+    _check(lib.smoe_rmsnorm(_ptr(v, torch.float32, "v"), v.shape[0], v.shape[1], eps,
+                            _ptr(out, torch.float32, "out"), _stream(stream)), "smoe_rmsnorm")
+    return out
+
+
+class StackArgs:
+    """Host arrays of a stack's per-layer router pointers and expert
+    descriptors, built once and passed to every stack_forward call."""
+
+    def __init__(self, router_ws, experts):
+        n = len(router_ws)
+        if len(experts) != n:
+            raise ValueError("one router matrix per layer of experts")
+        self.n = n
+        self.router = (ctypes.c_void_p * max(n, 1))(
+            *[_ptr(r, name="router_w") for r in router_ws])
+        self.experts = (Experts * max(n, 1))(*experts)
+        self._keep = list(router_ws)
+
+
+def stack_forward(desc, stack: StackArgs, h, tmp, topk_idx, topk_w, un: UnionBuffers, ws,
+                  n_union=None, eps=1e-6, stream=None):
+    """h <- RMSNorm(h + MoE_l(h)) for every layer l of the stack, in place.
+    topk_idx/topk_w: [n_layers, B, top_k]; n_union: [n_layers] int32 or None."""
+    B = h.shape[0]
+    _check(lib.smoe_stack_forward(ctypes.byref(desc), stack.n, stack.router,
+                                  stack.experts, _ptr(h, torch.float32, "h"), B, eps,
+                                  _ptr(tmp, torch.float32, "tmp"),
+                                  _ptr(topk_idx, torch.int32, "topk_idx"),
+                                  _ptr(topk_w, torch.float32, "topk_w"),
+                                  _ptr(n_union, torch.int32, "n_union"), ctypes.byref(un.c()),
+                                  _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+           "smoe_stack_forward")
+    return h
 
 
 def read_status(ws, stream=None) -> int:

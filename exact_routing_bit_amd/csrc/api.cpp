@@ -277,6 +277,20 @@ hipError_t launch_decode_logits(const smoe::RouteArgs& r, hipStream_t s,
   return smoe::launch_router(r, false, false, false, s, t);   // logits + activation prep
 }
 
+// The kernels of one whole layer, in stream order.
+hipError_t launch_layer(const smoe::RouteArgs& r, const smoe::FfnArgs& a, hipStream_t s) {
+  hipError_t err;
+  if (smoe::gemv_path_ok(a)) {
+    err = launch_decode_logits(r, s);
+    if (err == hipSuccess) err = smoe::launch_gate_up_routed(a, decode_route(r), s);
+    if (err == hipSuccess) err = smoe::launch_down(a, s);
+    return err;
+  }
+  err = smoe::launch_router(r, false, true, true, s);
+  if (err == hipSuccess) err = smoe::launch_ffn(a, s);
+  return err;
+}
+
 }  // namespace
 
 SMOE_API int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w,
@@ -289,17 +303,7 @@ SMOE_API int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w,
   const int rc = layer_setup(desc, router_w, experts, x, B, residual, out, logits, topk_idx,
                              topk_w, un, ws, ws_bytes, &r, &a);
   if (rc != SMOE_OK || B == 0) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err;
-  if (smoe::gemv_path_ok(a)) {
-    err = launch_decode_logits(r, s);
-    if (err == hipSuccess) err = smoe::launch_gate_up_routed(a, decode_route(r), s);
-    if (err == hipSuccess) err = smoe::launch_down(a, s);
-    return hip_rc(err);
-  }
-  err = smoe::launch_router(r, false, true, true, s);
-  if (err == hipSuccess) err = smoe::launch_ffn(a, s);
-  return hip_rc(err);
+  return hip_rc(launch_layer(r, a, static_cast<hipStream_t>(stream)));
 }
 
 SMOE_API int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* router_w,
@@ -331,6 +335,56 @@ SMOE_API int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const 
     case SMOE_STAGE_DOWN: return hip_rc(smoe::launch_down(a, s, t));
     default: return hip_rc(smoe::launch_combine(a, s, t));
   }
+}
+
+SMOE_API int smoe_rmsnorm(const float* v, int32_t B, int32_t d, float eps, float* out,
+                          void* stream) {
+  if (B < 0) return SMOE_EINVAL;
+  if (d < 64 || d > kMaxDim || d % 64 != 0) return SMOE_EUNSUPPORTED;
+  if (!(eps > 0.0f)) return SMOE_EINVAL;
+  if (B == 0) return SMOE_OK;
+  if (v == nullptr || out == nullptr || !aligned(v, 16) || !aligned(out, 16)) return SMOE_EINVAL;
+  return hip_rc(smoe::launch_rmsnorm(v, B, d, eps, out, static_cast<hipStream_t>(stream)));
+}
+
+SMOE_API int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers,
+                                const void* const* router_w, const smoe_experts* experts,
+                                float* h, int32_t B, float eps, float* tmp, int32_t* topk_idx,
+                                float* topk_w, int32_t* n_union, const smoe_union* un, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (n_layers < 0 || !(eps > 0.0f) || un == nullptr) return SMOE_EINVAL;
+  int rc = check_desc(desc);
+  if (rc == SMOE_OK) rc = check_batch(B);
+  if (rc != SMOE_OK) return rc;
+  if (n_layers == 0 || B == 0) return SMOE_OK;
+  if (router_w == nullptr || experts == nullptr || h == nullptr || tmp == nullptr || h == tmp ||
+      !aligned(h, 16) || !aligned(tmp, 16))
+    return SMOE_EINVAL;
+  const int64_t per_layer = (int64_t)B * desc->top_k;
+  // every layer is checked before the first launch, so a bad layer leaves h as it was
+  for (int l = 0; l < n_layers; ++l) {
+    smoe::RouteArgs r;
+    smoe::FfnArgs a;
+    smoe_union u = *un;
+    if (n_union != nullptr) u.n_union = n_union + l;
+    rc = layer_setup(desc, router_w[l], experts + l, h, B, h, tmp, nullptr,
+                     topk_idx ? topk_idx + l * per_layer : nullptr,
+                     topk_w ? topk_w + l * per_layer : nullptr, &u, ws, ws_bytes, &r, &a);
+    if (rc != SMOE_OK) return rc;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < n_layers; ++l) {
+    smoe::RouteArgs r;
+    smoe::FfnArgs a;
+    smoe_union u = *un;
+    if (n_union != nullptr) u.n_union = n_union + l;
+    layer_setup(desc, router_w[l], experts + l, h, B, h, tmp, nullptr, topk_idx + l * per_layer,
+                topk_w + l * per_layer, &u, ws, ws_bytes, &r, &a);
+    hipError_t err = launch_layer(r, a, s);
+    if (err == hipSuccess) err = smoe::launch_rmsnorm(tmp, B, desc->d_model, eps, h, s);
+    if (err != hipSuccess) return SMOE_EHIP;
+  }
+  return SMOE_OK;
 }
 
 SMOE_API int smoe_read_status(const void* ws, size_t ws_bytes, void* stream,

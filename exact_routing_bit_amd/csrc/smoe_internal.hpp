@@ -152,6 +152,7 @@ hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s, const LaunchTiming* t
 hipError_t launch_down(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_combine(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int n, hipStream_t s);
+hipError_t launch_rmsnorm(const float* v, int B, int d, float eps, float* out, hipStream_t s);
 // small-batch (B <= 2) matrix-vector kernels
 bool gemv_path_ok(const FfnArgs& a);
 hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up,

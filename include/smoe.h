@@ -201,6 +201,39 @@ int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* rou
                          float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
                          void* stream, void* start_event, void* stop_event);
 
+/* ----------------------------------------------------- between layers */
+/* The norm between stacked layers, h <- RMSNorm(h + MoE(h)): run
+ * smoe_moe_layer with residual = h, then this on its output.  The backbone
+ * keeps an RMS norm before attention and one before the FFN of every layer
+ * ([SC] weight inventory, "layer norms"); with attention left out the two
+ * meet between the MoE blocks.  Unit gain here:
+ *   out[t,:] = v[t,:] / sqrt(mean_i v[t,i]^2 + eps)     (fp32)
+ * v, out: [B, d] fp32, 16-byte aligned; out may equal v (in place).
+ * d: multiple of 64 in [64, 8192]; eps > 0; B >= 0 (0 is a no-op).
+ * Async on stream. */
+int smoe_rmsnorm(const float* v, int32_t B, int32_t d, float eps, float* out, void* stream);
+
+/* B tokens through a stack of n_layers routed layers of one shape, each
+ * followed by the norm (the per-layer loop of [DF]'s serial step trace with
+ * attention left out):
+ *   for l = 0 .. n_layers-1:   h <- RMSNorm(h + MoE_l(h))
+ * where MoE_l is smoe_moe_layer with router_w[l], experts[l] and
+ * residual = h.  h: [B, d] fp32, updated in place; tmp: [B, d] fp32
+ * scratch, distinct from h.  router_w, experts: HOST arrays of n_layers
+ * entries (device pointers inside, as for smoe_moe_layer).
+ * topk_idx [n_layers, B, top_k] int32 and topk_w [n_layers, B, top_k] fp32
+ * receive every layer's routing; n_union (nullable) [n_layers] int32
+ * receives every layer's union size (else un->n_union holds the last
+ * layer's); the other union arrays of un hold the last layer's lists.
+ * ws: one workspace sized for (desc, B), shared by the layers.
+ * All layers are validated before the first launch: on an error nothing is
+ * launched and h is unchanged.  n_layers == 0 or B == 0 is a no-op.
+ * Async on stream; eps > 0. */
+int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers, const void* const* router_w,
+                       const smoe_experts* experts, float* h, int32_t B, float eps, float* tmp,
+                       int32_t* topk_idx, float* topk_w, int32_t* n_union, const smoe_union* un,
+                       void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ utilities */
 /* Synchronises `stream`, then copies the workspace status bits into
  * *status_out (host).  For tests and diagnostics, not for the hot path. */

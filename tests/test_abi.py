@@ -17,7 +17,11 @@ def _lib_path():
 @pytest.fixture(scope="module")
 def smoe():
     if not os.path.exists(_lib_path()):
-        from exact_routing_bit_amd import build as b
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_smoe_build", os.path.join(ROOT, "exact_routing_bit_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     import exact_routing_bit_amd as m
     return m
@@ -150,6 +154,50 @@ def test_stage_argument_errors(smoe):
     assert call(ev=(f, None)) == smoe.SMOE_EINVAL       # events come in pairs
     assert call(ev=(None, f)) == smoe.SMOE_EINVAL
     assert call(n=4096) == smoe.SMOE_EWORKSPACE
+
+
+def test_rmsnorm_argument_errors(smoe):
+    f = ctypes.c_void_p(4096)
+    rn = smoe.lib.smoe_rmsnorm
+    assert rn(f, -1, 4096, 1e-6, f, None) == smoe.SMOE_EINVAL
+    assert rn(f, 1, 100, 1e-6, f, None) == smoe.SMOE_EUNSUPPORTED
+    assert rn(f, 1, 16384, 1e-6, f, None) == smoe.SMOE_EUNSUPPORTED
+    assert rn(f, 1, 4096, 0.0, f, None) == smoe.SMOE_EINVAL
+    assert rn(f, 1, 4096, float("nan"), f, None) == smoe.SMOE_EINVAL
+    assert rn(None, 1, 4096, 1e-6, f, None) == smoe.SMOE_EINVAL
+    assert rn(f, 1, 4096, 1e-6, ctypes.c_void_p(4100), None) == smoe.SMOE_EINVAL
+    assert rn(None, 0, 4096, 1e-6, None, None) == smoe.SMOE_OK      # empty batch: no-op
+
+
+def test_stack_argument_errors(smoe):
+    d = desc_of(smoe)
+    f = 4096
+    q = smoe.QMat(f, f, f, 1536 * 512, 1536 * 64)
+    qd = smoe.QMat(f, f, f, 4096 * 192, 4096 * 24)
+    good = smoe.Experts(q, q, qd)
+    bad = smoe.Experts(smoe.QMat(f, f, f, 1536 * 512 - 4, 1536 * 64), q, qd)
+    un = smoe.Union(f, f, f, f, f)
+    sf = smoe.lib.smoe_stack_forward
+    big = 1 << 30
+
+    def call(n=3, experts=(good, good, good), B=1, eps=1e-6, h=f, tmp=2 * f, un_=un, nbytes=big,
+             routers=(f, f, f)):
+        ra = (ctypes.c_void_p * 3)(*routers)
+        ea = (smoe.Experts * 3)(*experts)
+        return sf(ctypes.byref(d), n, ra, ea, h, B, eps, tmp, f, f, None,
+                  ctypes.byref(un_) if un_ is not None else None, f, nbytes, None)
+
+    assert call(n=-1) == smoe.SMOE_EINVAL
+    assert call(eps=0.0) == smoe.SMOE_EINVAL
+    assert call(un_=None) == smoe.SMOE_EINVAL
+    assert call(B=65) == smoe.SMOE_EUNSUPPORTED
+    assert call(tmp=f) == smoe.SMOE_EINVAL                       # tmp must not be h
+    assert call(h=f + 4) == smoe.SMOE_EINVAL
+    # a bad last layer is found before anything is launched
+    assert call(experts=(good, good, bad)) == smoe.SMOE_EINVAL
+    assert call(routers=(f, f, None)) == smoe.SMOE_EINVAL
+    assert call(nbytes=4096) == smoe.SMOE_EWORKSPACE
+    assert call(n=0) == smoe.SMOE_OK and call(B=0) == smoe.SMOE_OK
 
 
 def test_strerror(smoe):

@@ -1,0 +1,188 @@
+"""The stacked path: the between-layer norm and a stack of routed layers.
+
+h <- RMSNorm(h + MoE_l(h)) per layer l.  The GPU norm is checked against the
+oracle's fp32 definition; smoe_stack_forward is checked to launch exactly the
+chain of single-layer calls and norms (bitwise), and every layer of that
+chain is checked against the oracle on the GPU's own layer input (teacher
+forcing), so rounding differences do not compound down the stack.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import configs
+
+from gpu_helpers import desc_for, dev, device_weights, down, near_tie, rel_l2, small_config, up
+
+pytestmark = pytest.mark.gpu
+TOL = 3e-3
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def smoe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import exact_routing_bit_amd as m
+    return m
+
+
+def norm_tol(d):
+    """Per-element relative bound of GPU vs oracle RMSNorm: the oracle sums
+    the d positive squares one after another in fp32 (relative error at most
+    (d-1) u of the sum, u = 2^-24), the GPU by a short tree (at most ~32 u);
+    1/sqrt halves a relative error of its argument, and the scaling adds u."""
+    return (0.5 * (d + 32) + 4) * 2.0 ** -24
+
+
+@pytest.mark.parametrize("B,d", [(1, 64), (3, 1024), (64, 4096), (2, 8192)])
+def test_rmsnorm_parity(smoe, B, d):
+    rng = np.random.default_rng(B * 7919 + d)
+    v = (rng.standard_normal((B, d)) * rng.uniform(0.1, 30.0, (B, 1))).astype(np.float32)
+    ref = oracle.rmsnorm(v, eps=EPS)
+    g = up(v)
+    out = down(smoe.rmsnorm(g, eps=EPS))
+    err = np.abs(out.astype(np.float64) - ref) / np.maximum(np.abs(ref), 1e-30)
+    assert err.max() <= norm_tol(d), err.max()
+    # in place gives the same bits
+    smoe.rmsnorm(g, out=g, eps=EPS)
+    assert np.array_equal(down(g).view(np.uint32), out.view(np.uint32))
+
+
+def test_rmsnorm_zero_row_and_empty(smoe):
+    v = np.zeros((2, 256), np.float32)
+    v[1] = 3.0
+    out = down(smoe.rmsnorm(up(v), eps=EPS))
+    assert np.array_equal(out[0], np.zeros(256, np.float32))     # 0 / sqrt(eps)
+    assert np.allclose(out[1], 1.0, rtol=1e-6)
+    empty = torch.zeros(0, 256, dtype=torch.float32, device=dev())
+    smoe.rmsnorm(empty, out=empty)
+
+
+class GpuStack:
+    def __init__(self, smoe, cfg, n_layers, B, layers_w):
+        self.smoe, self.cfg, self.B = smoe, cfg, B
+        self.desc = desc_for(smoe, cfg)
+        self.W = layers_w
+        self.ex = [smoe.Experts(smoe.qmat(*W["gate"]), smoe.qmat(*W["up"]), smoe.qmat(*W["down"]))
+                   for W in layers_w]
+        self.args = smoe.StackArgs([W["router"] for W in layers_w], self.ex)
+        self.ws = torch.zeros(smoe.workspace_size(self.desc, B), dtype=torch.uint8, device=dev())
+        smoe.workspace_init(self.ws)
+        self.un = smoe.UnionBuffers.alloc(cfg.num_experts, B * cfg.top_k, dev())
+        K = cfg.top_k
+        i32 = dict(dtype=torch.int32, device=dev())
+        self.idx = torch.full((n_layers, B, K), -7, **i32)
+        self.w = torch.zeros(n_layers, B, K, dtype=torch.float32, device=dev())
+        self.nu = torch.full((n_layers,), -7, **i32)
+        self.tmp = torch.zeros(B, cfg.d_model, dtype=torch.float32, device=dev())
+
+    def forward(self, h):
+        self.smoe.stack_forward(self.desc, self.args, h, self.tmp, self.idx, self.w, self.un,
+                                self.ws, n_union=self.nu, eps=EPS)
+        return h
+
+    def chain(self, h0):
+        """The same stack as single-layer calls and norms; returns every
+        layer's input, pre-norm sum h + MoE(h), routing and union size."""
+        smoe, B, K = self.smoe, self.B, self.cfg.top_k
+        h = h0.clone()
+        ins, sums, idxs, ws_, nus = [], [], [], [], []
+        idx = torch.zeros(B, K, dtype=torch.int32, device=dev())
+        w = torch.zeros(B, K, dtype=torch.float32, device=dev())
+        for W, ex in zip(self.W, self.ex):
+            ins.append(down(h))
+            s = torch.zeros_like(h)
+            smoe.moe_layer(self.desc, W["router"], ex, h, s, idx, w, self.un, self.ws, residual=h)
+            sums.append(down(s))
+            idxs.append(down(idx))
+            ws_.append(down(w))
+            nus.append(int(down(self.un.n_union)[0]))
+            smoe.rmsnorm(s, out=h, eps=EPS)
+        return down(h), ins, sums, idxs, ws_, nus
+
+
+def check_layer_vs_oracle(L, cfg, x, s_gpu, idx_gpu, w_gpu, tokens=None):
+    """One layer of the chain against the oracle on the GPU's layer input x:
+    routing exact (or a near-tie), MoE(x) = s - x within relative L2, and the
+    norm of s within the norm's bound."""
+    tokens = list(range(x.shape[0])) if tokens is None else tokens
+    xs = np.ascontiguousarray(x[tokens])
+    lg, idx_ref, w_ref = oracle.route(L["router"], xs, cfg.top_k, cfg.norm_topk_prob)
+    idx_g = idx_gpu[tokens]
+    for i in range(len(tokens)):
+        if not np.array_equal(idx_g[i], idx_ref[i]):
+            assert near_tie(lg[i], cfg.top_k), f"token {tokens[i]}: routing differs"
+            idx_ref, w_ref = idx_g, w_gpu[tokens]          # inject the GPU's routing
+    moe_ref = oracle.moe(L["gate"], L["up"], L["down"], xs, idx_ref, w_ref)
+    moe_gpu = s_gpu[tokens].astype(np.float64) - xs.astype(np.float64)
+    assert rel_l2(moe_gpu, moe_ref) <= TOL
+
+
+@pytest.mark.parametrize("B", [1, 2, 5, 64])
+def test_stack_equals_chain_and_oracle(smoe, B):
+    cfg = small_config("stack", 1024, 32, 8, 256, B)
+    n_layers = 3
+    Ls = [synth.make_layer(cfg, layer=l) for l in range(n_layers)]
+    st = GpuStack(smoe, cfg, n_layers, B, [device_weights(L) for L in Ls])
+    h0 = up(synth.hidden(cfg.seed, 0, 2000 + B, B, cfg.d_model))
+    final, ins, sums, idxs, wts, nus = st.chain(h0)
+    h = st.forward(h0.clone())
+    torch.cuda.synchronize()
+    # the stack call launches exactly the chain
+    assert np.array_equal(down(h).view(np.uint32), final.view(np.uint32))
+    for l in range(n_layers):
+        assert np.array_equal(down(st.idx[l]), idxs[l])
+        assert np.array_equal(down(st.w[l]).view(np.uint32), wts[l].view(np.uint32))
+        assert int(down(st.nu[l])) == nus[l] == len(np.unique(idxs[l]))
+    # each layer against the oracle, teacher-forced on the GPU's layer input
+    for l in range(n_layers):
+        check_layer_vs_oracle(Ls[l], cfg, ins[l], sums[l], idxs[l], wts[l])
+        nxt = ins[l + 1] if l + 1 < n_layers else final
+        ref = oracle.rmsnorm(sums[l], eps=EPS)
+        assert np.all(np.abs(nxt - ref) <= norm_tol(cfg.d_model) * np.abs(ref) + 1e-30)
+
+
+def test_stack_bad_layer_leaves_h_unchanged(smoe):
+    cfg = small_config("stack_bad", 1024, 32, 8, 256, 1)
+    Ls = [synth.make_layer(cfg, layer=l) for l in range(2)]
+    st = GpuStack(smoe, cfg, 2, 1, [device_weights(L) for L in Ls])
+    q = st.ex[1].gate
+    st.ex[1] = smoe.Experts(smoe.QMat(q.w + 4, q.s, q.b, q.expert_stride_w, q.expert_stride_sb),
+                            st.ex[1].up, st.ex[1].down)            # misaligned: rejected
+    st.args = smoe.StackArgs([W["router"] for W in st.W], st.ex)
+    h = up(synth.hidden(0, 0, 9, 1, 1024))
+    before = down(h)
+    with pytest.raises(smoe.SmoeError):
+        st.forward(h)
+    torch.cuda.synchronize()
+    assert np.array_equal(down(h), before)
+    assert np.array_equal(down(st.idx), np.full((2, 1, 8), -7, np.int32))
+
+
+@pytest.mark.parametrize("cfg,sample", [(configs.DECODE, [0]), (configs.PREFILL, [0, 33, 63])],
+                         ids=lambda v: getattr(v, "name", str(v)))
+def test_full_size_stack(smoe, cfg, sample):
+    """Two stacked layers at the full decode / prefill-chunk shape, in the
+    launch configuration the stacked benchmark times: the stack call equals
+    the chain bitwise, and sampled tokens of every layer match the oracle
+    with the CPU generator's bytes of the experts they use."""
+    import synth.gpu as sg
+    n_layers, B = 2, cfg.batch
+    Wg = [sg.make_layer(cfg, layer=l) for l in range(n_layers)]
+    st = GpuStack(smoe, cfg, n_layers, B, Wg)
+    h0 = up(synth.hidden(cfg.seed, 0, 3000, B, cfg.d_model))
+    final, ins, sums, idxs, wts, nus = st.chain(h0)
+    h = st.forward(h0.clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(down(h).view(np.uint32), final.view(np.uint32))
+    for l in range(n_layers):
+        assert np.array_equal(down(st.idx[l]), idxs[l])
+        experts = sorted(set(int(e) for t in sample for e in idxs[l][t]))
+        Lc = synth.make_layer(cfg, layer=l, experts=experts)
+        check_layer_vs_oracle(Lc, cfg, ins[l], sums[l], idxs[l], wts[l], tokens=sample)
+        nxt = ins[l + 1] if l + 1 < n_layers else final
+        ref = oracle.rmsnorm(sums[l][sample], eps=EPS)
+        assert np.all(np.abs(nxt[sample] - ref) <= norm_tol(cfg.d_model) * np.abs(ref) + 1e-30)
