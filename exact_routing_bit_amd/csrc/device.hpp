@@ -25,6 +25,24 @@ __device__ __forceinline__ uint2 ld_stream2(const uint32_t* p) {
   return make_uint2(v.x, v.y);
 }
 
+// Raw buffer loads.  A load at an offset at or past the resource's byte
+// count returns zero and makes no memory access, so a pipelined loop can
+// prefetch past its end with straight-line code (no branch, whose merge
+// would make the compiler's wait counts conservative) and no wasted bytes.
+constexpr uint32_t kBufferDead = 0x80000000u;   // an offset past every resource
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  // dword 3 = 0x00020000: raw 32-bit data format, no swizzle (gfx9 family)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+// 16 bytes, nontemporal (streamed once, see ld_stream4)
+__device__ __forceinline__ uint4 buf_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+
 // Direct global -> LDS copies (no VGPRs held while in flight).  Each active
 // lane copies n bytes from its own source address to lds_base + n * lane;
 // lds_base must be wave-uniform (it goes to M0).  The copies count in vmcnt
@@ -190,41 +208,198 @@ __device__ __forceinline__ int wave_min_i(int v) {
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
-// Top-k of one row of E <= 256 logits by one full wave (v[j] = logit of expert
-// lane + 64 j, -FLT_MAX past E): after the call lane k < K holds the rank-k
-// logit and expert, ranked by logit descending and, on equal logits, expert
-// index ascending.  K rounds of a wave-wide arg-max (DPP max, then the lowest
-// index among the maxima).
-__device__ __forceinline__ void wave_topk(const float (&v)[4], int E, int K, float& my_v,
-                                          int& my_e) {
-  const int lane = __lane_id();
-  bool live[4];
+// Per-wave LDS scratch of wave_topk: the K selected entries in expert order.
+constexpr int kTopkMax = 16;
+struct TopkScratch {
+  uint32_t key[kTopkMax];
+  int e[kTopkMax];
+  float v[kTopkMax];
+};
+
+// Order-preserving map of a float to an unsigned key: x > y (as floats, no
+// NaN) exactly when key(x) > key(y).  -0 is first made +0 (x + 0 rounds it to
+// +0), so that the two zeros compare equal, as floats do.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Counts of the wave's keys at or above c1, c2 and c3 (NJ = 2 or 4 keys per
+// lane).  The compares are VOP3 v_cmp into SGPR pairs of their own, issued
+// together in one block: the compiler's ballots all go through VCC (or one
+// reused pair), which chains every compare behind the previous mask's count.
+// Every lane of the wave must be active (inactive lanes read as 0).
+template <int NJ>
+__device__ __forceinline__ void count_ge3(const uint32_t (&key)[4], uint32_t c1, uint32_t c2,
+                                          uint32_t c3, int& n1, int& n2, int& n3);
+template <>
+__device__ __forceinline__ void count_ge3<2>(const uint32_t (&key)[4], uint32_t c1, uint32_t c2,
+                                             uint32_t c3, int& n1, int& n2, int& n3) {
+  uint64_t a0, a1, b0, b1, d0, d1;
+  asm("v_cmp_ge_u32_e64 %0, %6, %8\n\t"
+      "v_cmp_ge_u32_e64 %1, %7, %8\n\t"
+      "v_cmp_ge_u32_e64 %2, %6, %9\n\t"
+      "v_cmp_ge_u32_e64 %3, %7, %9\n\t"
+      "v_cmp_ge_u32_e64 %4, %6, %10\n\t"
+      "v_cmp_ge_u32_e64 %5, %7, %10"
+      : "=&s"(a0), "=&s"(a1), "=&s"(b0), "=&s"(b1), "=&s"(d0), "=&s"(d1)
+      : "v"(key[0]), "v"(key[1]), "s"(c1), "s"(c2), "s"(c3));
+  n1 = __popcll(a0) + __popcll(a1);
+  n2 = __popcll(b0) + __popcll(b1);
+  n3 = __popcll(d0) + __popcll(d1);
+}
+template <>
+__device__ __forceinline__ void count_ge3<4>(const uint32_t (&key)[4], uint32_t c1, uint32_t c2,
+                                             uint32_t c3, int& n1, int& n2, int& n3) {
+  int x1, x2, x3, y1, y2, y3;
+  const uint32_t lo[4] = {key[0], key[1], 0u, 0u}, hi[4] = {key[2], key[3], 0u, 0u};
+  count_ge3<2>(lo, c1, c2, c3, x1, x2, x3);
+  count_ge3<2>(hi, c1, c2, c3, y1, y2, y3);
+  n1 = x1 + y1;
+  n2 = x2 + y2;
+  n3 = x3 + y3;
+}
+
+// A key threshold t with #{key > t} <= K <= #{key >= t} (so that the top K
+// are the keys above t plus the lowest-index keys equal to t): the K-th
+// largest key, built two bits per step from the top (the three candidate
+// counts of a step are independent), or earlier the first prefix that
+// exactly K keys reach.
+template <int NJ>
+__device__ __forceinline__ uint32_t topk_threshold(const uint32_t (&key)[4], int K) {
+  uint32_t t = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) live[j] = lane + 64 * j < E;
-  my_v = 0.f;
-  my_e = 0;
-  for (int k = 0; k < K; ++k) {
-    // this lane's best live candidate (ascending j keeps the lower index on ties)
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      if (live[j] && (v[j] > bv || (v[j] == bv && e < be))) {
-        bv = v[j];
-        be = e;
-      }
-    }
-    const float m = wave_max(bv);
-    const int win = wave_min_i(bv == m ? be : 0x7FFFFFFF);   // lowest index among the maxima
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (win == lane + 64 * j) live[j] = false;
-    if (lane == k) {
-      my_v = m;
-      my_e = win;
-    }
+  for (int sh = 30; sh >= 0; sh -= 2) {
+    const uint32_t c1 = t | (1u << sh), c2 = t | (2u << sh), c3 = t | (3u << sh);
+    int n1, n2, n3;
+    count_ge3<NJ>(key, c1, c2, c3, n1, n2, n3);
+    const int n = n3 >= K ? n3 : (n2 >= K ? n2 : n1);
+    t = n3 >= K ? c3 : (n2 >= K ? c2 : (n1 >= K ? c1 : t));
+    if (n == K) break;                            // exactly K keys at or above t
   }
+  return t;
+}
+
+// Wave masks of key[j] > t and key[j] == t (j < 2), each in an SGPR pair of
+// its own (see count_ge3); the trailing s_nop covers a following VALU read of
+// the masks.
+__device__ __forceinline__ void masks_gt_eq2(uint32_t k0, uint32_t k1, uint32_t t, uint64_t& gt0,
+                                             uint64_t& gt1, uint64_t& eq0, uint64_t& eq1) {
+  asm("v_cmp_gt_u32_e64 %0, %4, %6\n\t"
+      "v_cmp_gt_u32_e64 %1, %5, %6\n\t"
+      "v_cmp_eq_u32_e64 %2, %4, %6\n\t"
+      "v_cmp_eq_u32_e64 %3, %5, %6\n\t"
+      "s_nop 4"
+      : "=&s"(gt0), "=&s"(gt1), "=&s"(eq0), "=&s"(eq1)
+      : "v"(k0), "v"(k1), "s"(t));
+}
+__device__ __forceinline__ void masks_nz2(uint32_t a0, uint32_t a1, uint64_t& m0, uint64_t& m1) {
+  asm("v_cmp_ne_u32_e64 %0, 0, %2\n\t"
+      "v_cmp_ne_u32_e64 %1, 0, %3\n\t"
+      "s_nop 4"
+      : "=&s"(m0), "=&s"(m1)
+      : "v"(a0), "v"(a1));
+}
+// Set bits of m below this lane.
+__device__ __forceinline__ int bits_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Result of wave_topk_sel.  Lane q < K: se/sv = the q-th selected expert in
+// ascending expert order and its logit, srank = its rank.  Lane k < K:
+// my_e/my_v = the rank-k expert and logit.  Lanes >= K: zeros.
+struct TopkSel {
+  int se;
+  float sv;
+  int srank;
+  int my_e;
+  float my_v;
+};
+
+// Top-k of one row of E <= 64 * NJ logits by one full wave (v[j] = logit of
+// expert lane + 64 j; entries past E are ignored), K <= 16, ranked by logit
+// descending and, on equal logits, expert index ascending:
+//   1. a threshold t (topk_threshold: wave mask counts);
+//   2. the keys above t, plus the lowest-index keys equal to t up to K in all,
+//      are copied in expert order to the wave's scratch;
+//   3. each of the K ranks itself against the other K-1 and is sent to the
+//      lane of its rank (ds_permute).
+// Candidates past E get key 0, below every real key, so no step needs a
+// branch on E.  sc: this wave's scratch in LDS (no other wave may use it
+// meanwhile).  Every lane of the wave must be active.
+template <int NJ>
+__device__ __forceinline__ TopkSel wave_topk_sel(const float (&v)[4], int E, int K,
+                                                 TopkScratch* sc) {
+  const int lane = __lane_id();
+  uint32_t key[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) key[j] = (j < NJ && lane + 64 * j < E) ? order_key(v[j]) : 0u;
+  const uint32_t t = topk_threshold<NJ>(key, K);
+  uint64_t gt[4], eq[4];
+#pragma unroll
+  for (int j = 0; j < NJ; j += 2) masks_gt_eq2(key[j], key[j + 1], t, gt[j], gt[j + 1], eq[j], eq[j + 1]);
+  int n_gt = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) n_gt += __popcll(gt[j]);
+  const int need = K - n_gt;                      // keys equal to t to take (>= 0)
+  // selection and place in expert order (expert lane + 64 j: j, then lane)
+  uint32_t sel[4];
+  int ties = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const bool is_gt = (gt[j] >> lane) & 1, is_eq = (eq[j] >> lane) & 1;
+    sel[j] = (is_gt || (is_eq && ties + bits_below(eq[j]) < need)) ? 1u : 0u;
+    ties += __popcll(eq[j]);
+  }
+  uint64_t ms[4];
+#pragma unroll
+  for (int j = 0; j < NJ; j += 2) masks_nz2(sel[j], sel[j + 1], ms[j], ms[j + 1]);
+  int taken = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (sel[j]) {
+      const int p = taken + bits_below(ms[j]);
+      sc->key[p] = key[j];
+      sc->e[p] = lane + 64 * j;
+      sc->v[p] = v[j];
+    }
+    taken += __popcll(ms[j]);
+  }
+  // a wave's LDS accesses execute in order; keep the compiler from moving the
+  // reads above the writes
+  asm volatile("" ::: "memory");
+  const bool mine = lane < K;
+  const int ql = mine ? lane : 0;
+  const uint32_t qk = sc->key[ql];
+  const int qe = sc->e[ql];
+  const float qv = sc->v[ql];
+  int rank = 0;
+#pragma unroll
+  for (int r = 0; r < kTopkMax; ++r) {
+    const uint32_t kr = sc->key[r];               // past K: stale, masked below
+    const int er = sc->e[r];
+    rank += (r < K && (kr > qk || (kr == qk && er < qe))) ? 1 : 0;
+  }
+  asm volatile("" ::: "memory");                  // the scratch may be reused after this
+  const int dst = mine ? rank : lane;             // a permutation of the lanes
+  const float pv = __int_as_float(__builtin_amdgcn_ds_permute(dst << 2, __float_as_int(qv)));
+  const int pe = __builtin_amdgcn_ds_permute(dst << 2, qe);
+  TopkSel out;
+  out.se = mine ? qe : 0;
+  out.sv = mine ? qv : 0.f;
+  out.srank = mine ? rank : 0;
+  out.my_e = mine ? pe : 0;
+  out.my_v = mine ? pv : 0.f;
+  return out;
+}
+
+// Top-k of one row of E <= 256 logits (see wave_topk_sel): lane k < K gets
+// the rank-k logit and expert.
+__device__ __forceinline__ void wave_topk(const float (&v)[4], int E, int K, float& my_v,
+                                          int& my_e, TopkScratch* sc) {
+  const TopkSel t = E <= 128 ? wave_topk_sel<2>(v, E, K, sc) : wave_topk_sel<4>(v, E, K, sc);
+  my_v = t.my_v;
+  my_e = t.my_e;
 }
 
 // Routing weight of the lane's rank (lane < K) from wave_topk's results:

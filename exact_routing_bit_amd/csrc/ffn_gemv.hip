@@ -43,6 +43,8 @@ constexpr int kMaxDecPairs = 16;      // B * K <= 16 on this path
 // the arithmetic (about 9 VALU ops per packed word) then hides under the next
 // item's loads instead of piling up once all of a burst has landed
 constexpr int kGuBlocksPerCU = 1;
+constexpr int kGuDepth = 3;           // gate_up: items per wave in the load ring
+constexpr int kGuMaxItems = 64;       // gate_up: items per wave (h staged in LDS)
 constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU (one row block each at d = 4096)
 constexpr int kHRegs = 6;             // down: h chunks per thread loaded ahead of the weights
 // down: (expert, row step) items per wave per batch of loads
@@ -101,31 +103,38 @@ struct GuBuf {
 };
 
 template <int TPR>
-__device__ __forceinline__ void gu_load(const FfnArgs& a, const DecMeta& m, int item, int lane,
-                                        GuBuf<TPR>& buf) {
+__device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int item, int n_items,
+                                        int lane, GuBuf<TPR>& buf) {
   constexpr int kRps = 64 / TPR;
   const int per = a.f / kJ;
-  const int u = uniform(item / per);
-  const int j0 = (item - u * per) * kJ;
-  const int e = uniform(m.experts[u]);
+  // an item past the end keeps a valid expert and loads at a dead offset
+  const bool live = item < n_items;
+  const int itc = live ? item : n_items - 1;
+  const int u = uniform(itc / per);
+  const int j0 = (itc - u * per) * kJ;
+  // union slot u's expert, from lane u of a register (no LDS read, so no
+  // temporary register is written while the ring's loads are in flight)
+  const int e = __builtin_amdgcn_readlane(lane_expert, u);
   const int G = a.d / 64, C = a.d / 8;
   const int li = lane % TPR, slot = lane / TPR;
-  const uint32_t* gw = a.gate.w + e * a.gate.stride_w;
-  const uint16_t* gs = a.gate.s + e * a.gate.stride_sb;
-  const uint16_t* gb = a.gate.b + e * a.gate.stride_sb;
-  const uint32_t* uw = a.up.w + e * a.up.stride_w;
-  const uint16_t* us = a.up.s + e * a.up.stride_sb;
-  const uint16_t* ub = a.up.b + e * a.up.stride_sb;
+  const uint32_t wbytes = (uint32_t)a.f * C * 4, sbytes = (uint32_t)a.f * G * 2;
+  const auto gw = buffer_rsrc(a.gate.w + e * a.gate.stride_w, wbytes);
+  const auto gs = buffer_rsrc(a.gate.s + e * a.gate.stride_sb, sbytes);
+  const auto gb = buffer_rsrc(a.gate.b + e * a.gate.stride_sb, sbytes);
+  const auto uw = buffer_rsrc(a.up.w + e * a.up.stride_w, wbytes);
+  const auto us = buffer_rsrc(a.up.s + e * a.up.stride_sb, sbytes);
+  const auto ub = buffer_rsrc(a.up.b + e * a.up.stride_sb, sbytes);
 #pragma unroll
   for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
     const int rs = k * kRps + slot;                 // < kGuRows: kRps divides it
     const bool is_up = rs >= kJ;
-    const int64_t row = j0 + (rs % kJ);
-    const uint32_t* wr = (is_up ? uw : gw) + row * C + li * 8;
-    buf.w[k][0] = ld_stream4(wr);
-    buf.w[k][1] = ld_stream4(wr + 4);
-    buf.s[k] = (is_up ? us : gs)[row * G + li];
-    buf.b[k] = (is_up ? ub : gb)[row * G + li];
+    const uint32_t row = j0 + (rs % kJ);
+    const uint32_t wo = live ? (row * C + li * 8) * 4 : kBufferDead;
+    const uint32_t so = live ? (row * G + li) * 2 : kBufferDead;
+    buf.w[k][0] = buf_load4_nt(is_up ? uw : gw, wo);
+    buf.w[k][1] = buf_load4_nt(is_up ? uw : gw, wo + 16);
+    buf.s[k] = buf_load_u16(is_up ? us : gs, so);
+    buf.b[k] = buf_load_u16(is_up ? ub : gb, so);
   }
   // keep every load of the item here: left to itself the scheduler sinks the
   // scale/bias loads to their first use, after the next item's loads, which
@@ -133,12 +142,14 @@ __device__ __forceinline__ void gu_load(const FfnArgs& a, const DecMeta& m, int 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Computes one item and writes its h values.  xr/xs: the lane's group of the
+// Computes one item and stages its h values (fp16 bits, prepped scaling) in
+// the wave's LDS row st: st[jj * NTOK + q] = h of row j0 + jj for the union
+// expert's q-th pair (q < its pair count).  xr/xs: the lane's group of the
 // prepped activations of token t (t < NTOK).
 template <int NTOK, int TPR>
 __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, int item, int lane,
                                            const GuBuf<TPR>& buf, const uint4 (&xr)[NTOK][8],
-                                           const float2 (&xs)[NTOK]) {
+                                           const float2 (&xs)[NTOK], uint16_t* st) {
   constexpr int kRps = 64 / TPR;
   const int per = a.f / kJ;
   const int u = uniform(item / per);
@@ -164,14 +175,15 @@ __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, i
     if (kRps == 1 || slot == jj % kRps) {
       const int kg = jj / kRps, ku = (kJ + jj) / kRps;
       const int j = j0 + jj;
-      for (int q = 0; q < ne; ++q) {
-        const int p = uniform(m.pairs[pb + q]);
-        const int t = NTOK == 1 ? 0 : p / a.K;
+#pragma unroll
+      for (int q = 0; q < NTOK; ++q) {
+        if (q >= ne) break;
+        const int t = NTOK == 1 ? 0 : uniform(m.pairs[pb + q]) / a.K;
         const float g = (NTOK == 1 || t == 0) ? r[kg][0] : r[kg][NTOK - 1];
         const float up = (NTOK == 1 || t == 0) ? r[ku][0] : r[ku][NTOK - 1];
         const float h = silu_mul(g, up);
         const half_t hv = (j & 1) ? (half_t)((float)(half_t)h * 0.0625f) : (half_t)h;
-        if (li == 0) a.hp[(int64_t)p * a.f + prepped_pos(j)] = f16_bits(hv);
+        if (li == 0) st[jj * NTOK + q] = f16_bits(hv);
       }
     }
   }
@@ -246,12 +258,48 @@ __device__ __forceinline__ void load_meta(const FfnArgs& a, DecMeta& m) {
 // readlane counts over the P <= 16 pairs: pairs grouped by ascending expert,
 // ascending within.  Block 0 writes the same outputs smoe_route and
 // smoe_build_union would.
-__device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& r, DecMeta& m) {
+// What wave 0 keeps of a single token's routing until the kernel's end, when
+// block 0 writes the routing outputs (the next kernel is the first reader).
+struct RouteKeep {
+  float v[4];
+  TopkSel t;
+};
+
+template <int NTOK>
+__device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& r, DecMeta& m,
+                                           RouteKeep& keep) {
   __shared__ int s_e[kMaxDecPairs];
   __shared__ float s_w[kMaxDecPairs];
+  __shared__ TopkScratch tks[2];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.K, P = a.B * a.K;
+  if (NTOK == 1) {
+    // one token: its K experts are distinct, so the union is the selected set
+    // in ascending expert order (as wave_topk_sel leaves it) and union slot q
+    // holds the one pair of that expert, the pair of its rank
+    if (wave == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        keep.v[j] = e < E ? r.logits[e] : -FLT_MAX;
+      }
+      keep.t = E <= 128 ? wave_topk_sel<2>(keep.v, E, K, &tks[0])
+                        : wave_topk_sel<4>(keep.v, E, K, &tks[0]);
+      if (lane < K) {
+        m.experts[lane] = keep.t.se;
+        m.offsets[lane] = lane;
+        m.pairs[lane] = keep.t.srank;
+        m.pos[keep.t.srank] = lane;
+      }
+      if (lane == 0) {
+        m.n_union = K;
+        m.offsets[K] = K;
+      }
+    }
+    __syncthreads();
+    return;
+  }
   if (wave < a.B) {
     float v[4];
 #pragma unroll
@@ -261,7 +309,7 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
     }
     float my_v;
     int my_e;
-    wave_topk(v, E, K, my_v, my_e);
+    wave_topk(v, E, K, my_v, my_e, &tks[wave]);
     const float w = topk_weight(v, E, K, r.norm != 0, my_v);
     if (lane < K) {
       s_e[wave * K + lane] = my_e;
@@ -270,24 +318,24 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
   }
   __syncthreads();
   if (wave == 0) {
+    // every pair's expert by broadcast LDS reads (no readlane chains)
     const bool in = lane < P;
     const int e = in ? s_e[lane] : 0x7FFFFFFF;
+    int eq[kMaxDecPairs];
+#pragma unroll
+    for (int q = 0; q < kMaxDecPairs; ++q) eq[q] = q < P ? s_e[q] : 0x7FFFFFFF;
     int less = 0, same_before = 0;
-    bool first = in;
-    for (int q = 0; q < P; ++q) {
-      const int eq = __builtin_amdgcn_readlane(e, q);
-      less += eq < e;
-      if (q < lane && eq == e) {
-        ++same_before;
-        first = false;
-      }
+#pragma unroll
+    for (int q = 0; q < kMaxDecPairs; ++q) {
+      less += eq[q] < e ? 1 : 0;
+      same_before += (q < lane && eq[q] == e) ? 1 : 0;
     }
+    const bool first = in && same_before == 0;
     const uint64_t firsts = __ballot(first);
     int distinct_less = 0;
-    for (int q = 0; q < P; ++q) {
-      const int eq = __builtin_amdgcn_readlane(e, q);
-      distinct_less += ((firsts >> q) & 1) && eq < e;
-    }
+#pragma unroll
+    for (int q = 0; q < kMaxDecPairs; ++q)
+      distinct_less += (((firsts >> q) & 1) && eq[q] < e) ? 1 : 0;
     const int nU = __popcll(firsts);
     const int qpos = less + same_before;          // place of this pair in pair_list
     if (in) {
@@ -332,8 +380,9 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   __shared__ DecMeta m;
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  RouteKeep keep;
   if (kRoute)
-    route_meta(a, r, m);
+    route_meta<NTOK>(a, r, m, keep);
   else
     load_meta(a, m);
   const int nU = uniform(m.n_union);
@@ -341,9 +390,8 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   const int W = gridDim.x * kDecWaves;
   const int wid = blockIdx.x * kDecWaves + wave;
   if (wid >= n_items) return;                     // no barrier follows
-  GuBuf<TPR> b0, b1;
-  gu_load<TPR>(a, m, wid, lane, b0);
-  // this lane's group of every token's prepped activations
+  // this lane's group of every token's prepped activations, loaded first:
+  // they are few and cached, and the weight loads queue behind them
   const int G = a.d / 64, li = lane % TPR;
   uint4 xr[NTOK][8];
   float2 xs[NTOK];
@@ -355,16 +403,65 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
     for (int q = 0; q < 8; ++q) xr[t][q] = src[q];
     xs[t] = a.xs[(int64_t)tt * G + li];
   }
-  // two items in flight: item i computes while i + W loads (a wave past the
-  // end reloads its current item, which is then not computed again)
-  for (int i = wid; i < n_items; i += 2 * W) {
-    const int i1 = i + W < n_items ? i + W : i;
-    gu_load<TPR>(a, m, i1, lane, b1);
-    gu_compute<NTOK, TPR>(a, m, i, lane, b0, xr, xs);
-    if (i + W >= n_items) break;
-    const int i2 = i + 2 * W < n_items ? i + 2 * W : i1;
-    gu_load<TPR>(a, m, i2, lane, b0);
-    gu_compute<NTOK, TPR>(a, m, i + W, lane, b1, xr, xs);
+  // a ring of kGuDepth items: item i computes while the next kGuDepth - 1
+  // items of this wave (i + W, i + 2W, ...) are in flight.  Loads past the
+  // end go to a dead offset (no memory access), so every item's bytes are
+  // read once and the loop body stays straight-line.
+  const int lane_expert = m.experts[min(lane, kMaxDecPairs - 1)];
+  // h is staged in LDS and written out after the loop: a global store inside
+  // the loop would count in vmcnt behind the ring's loads, and the compiler
+  // waits for it (and so for every load before it) before reusing its data
+  // registers.  The grid gives every wave at most kGuMaxItems items.
+  __shared__ uint16_t hst[kDecWaves][kGuMaxItems][kJ * NTOK];
+  GuBuf<TPR> b[kGuDepth];
+#pragma unroll
+  for (int s = 0; s < kGuDepth - 1; ++s)
+    gu_load<TPR>(a, lane_expert, wid + s * W, n_items, lane, b[s]);
+  for (int i = wid, loc = 0;; i += kGuDepth * W) {
+#pragma unroll
+    for (int s = 0; s < kGuDepth; ++s, ++loc) {
+      const int it = i + s * W;
+      if (it >= n_items) goto flush;
+      gu_load<TPR>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, lane,
+                   b[(s + kGuDepth - 1) % kGuDepth]);
+      gu_compute<NTOK, TPR>(a, m, it, lane, b[s], xr, xs, hst[wave][loc]);
+    }
+  }
+flush:
+  {
+    // the wave's own LDS rows: no barrier, the wave's LDS accesses are ordered
+    const int n_mine = (n_items - wid + W - 1) / W;
+    const int per = a.f / kJ;
+    for (int q = lane; q < n_mine * kJ * NTOK; q += 64) {
+      const int loc = q / (kJ * NTOK), rr = q % (kJ * NTOK);
+      const int jj = rr / NTOK, k = rr % NTOK;
+      const int item = wid + loc * W;
+      const int u = item / per;
+      const int j = (item - u * per) * kJ + jj;
+      const int pb = m.offsets[u];
+      if (k < m.offsets[u + 1] - pb) {
+        const int p = m.pairs[pb + k];
+        a.hp[(int64_t)p * a.f + prepped_pos(j)] = hst[wave][loc][rr];
+      }
+    }
+  }
+  if (kRoute && NTOK == 1 && blockIdx.x == 0 && wave == 0) {
+    // the single token's routing outputs, as smoe_route and smoe_build_union
+    // would write them (pair k = rank k; union slot q = the q-th expert)
+    const int K = a.K;
+    const float w = topk_weight(keep.v, a.E, K, r.norm != 0, keep.t.my_v);
+    if (lane < K) {
+      r.topk_idx[lane] = keep.t.my_e;
+      r.topk_w[lane] = w;
+      r.union_experts[lane] = keep.t.se;
+      r.expert_offsets[lane] = lane;
+      r.pair_list[lane] = keep.t.srank;
+      r.pair_pos[keep.t.srank] = lane;
+    }
+    if (lane == 0) {
+      *r.n_union = K;
+      r.expert_offsets[K] = K;
+    }
   }
 }
 
@@ -535,7 +632,11 @@ hipError_t launch_gate_up_gemv(const FfnArgs& a, const DecodeRoute& r, hipStream
   const int items = max_union * (a.f / kJ);
   const int ncu = cu_count();
   if (ncu <= 0) return hipErrorInvalidDevice;
-  const int grid = std::min((items + kDecWaves - 1) / kDecWaves, ncu * kGuBlocksPerCU);
+  // one block per CU, but enough blocks that no wave has more than
+  // kGuMaxItems items (its LDS staging rows)
+  const int per_block = kDecWaves * kGuMaxItems;
+  const int grid = std::max(std::min((items + kDecWaves - 1) / kDecWaves, ncu * kGuBlocksPerCU),
+                            (items + per_block - 1) / per_block);
   SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, kRoute>), dim3(grid), dim3(kDecThreads), 0, s, a, r);
   return hipGetLastError();
 }

@@ -42,7 +42,7 @@ __device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, fl
 
 // Top-k of one token's E <= 256 logits by one full wave; writes indices and
 // weights (rank order) to global memory and the indices to s_idx.
-__device__ void topk_token(const RouteArgs& a, int t, int32_t* s_idx) {
+__device__ void topk_token(const RouteArgs& a, int t, int32_t* s_idx, TopkScratch* sc) {
   const int lane = __lane_id();
   const int E = a.E, K = a.K;
   float v[4];
@@ -53,7 +53,7 @@ __device__ void topk_token(const RouteArgs& a, int t, int32_t* s_idx) {
   }
   float my_v;
   int my_e;
-  wave_topk(v, E, K, my_v, my_e);
+  wave_topk(v, E, K, my_v, my_e, sc);
   const float w = topk_weight(v, E, K, a.norm != 0, my_v);
   if (lane < K) {
     a.topk_idx[t * K + lane] = my_e;
@@ -67,6 +67,7 @@ struct UnionSmem {
   int32_t hist[kMaxExperts];
   int32_t pos[kMaxExperts];
   uint32_t mask[kMaxExperts * (kMaxPairs / 32)];
+  TopkScratch topk[16];   // one per wave (blocks of up to 1024 threads)
 };
 
 // Union of the batch's experts and the per-expert pair lists, by one block
@@ -139,7 +140,7 @@ __device__ void build_union(const RouteArgs& a, UnionSmem* us) {
 __device__ void route_tail(const RouteArgs& a, bool do_topk, bool do_union, UnionSmem* us) {
   const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   if (do_topk)
-    for (int t = wave; t < a.B; t += nwaves) topk_token(a, t, us->idx);
+    for (int t = wave; t < a.B; t += nwaves) topk_token(a, t, us->idx, &us->topk[wave]);
   if (!do_union) return;
   __syncthreads();
   if (!do_topk)
