@@ -22,9 +22,10 @@
 // first, so no dependent global load sits inside their loops.
 //
 // Lane layout: a row of G groups (64 inputs each) is spread over TPR lanes,
-// each lane owning GPL consecutive groups (32*GPL contiguous bytes of the
-// row), so one wave instruction covers 64/TPR rows.  gate_up rows have one
-// group per lane (TPR = d/64, 32 or 64); down rows GPL = 1..3.
+// lane li owning the GPL groups li, li + TPR, li + 2 TPR (so that one load
+// instruction reads adjacent group halves), and one wave instruction covers
+// 64/TPR rows.  gate_up rows have one group per lane (TPR = d/64, 32 or 64);
+// down rows GPL = 1..3.
 #include <algorithm>
 
 #include "device.hpp"
@@ -58,24 +59,27 @@ __device__ __forceinline__ int prepped_pos(int c) {
 }
 
 // Dot of one lane's GPL groups (8 words each) against prepped activations,
-// with the fp32 group epilogue: sum_g s_g (D_g - C_g) + b_g X_g.
+// with the fp32 group epilogue: sum_g s_g (D_g - C_g) + b_g X_g.  Group gi's
+// activations are xc[gi * gstride * 8 ...] and its sums xsum[gi * gstride].
 template <int GPL>
 __device__ __forceinline__ float lane_row_dot(const uint4 (&w)[GPL][2], const float (&sc)[GPL],
                                               const float (&bi)[GPL], const uint4* xc,
-                                              const float2* xsum) {
+                                              const float2* xsum, int gstride = 1) {
   float part = 0.f;
 #pragma unroll
   for (int gi = 0; gi < GPL; ++gi) {
+    const uint4* xg = xc + gi * gstride * 8;
     float acc = 0.f;
-    acc = dot_word(w[gi][0].x, xc[gi * 8 + 0], acc);
-    acc = dot_word(w[gi][0].y, xc[gi * 8 + 1], acc);
-    acc = dot_word(w[gi][0].z, xc[gi * 8 + 2], acc);
-    acc = dot_word(w[gi][0].w, xc[gi * 8 + 3], acc);
-    acc = dot_word(w[gi][1].x, xc[gi * 8 + 4], acc);
-    acc = dot_word(w[gi][1].y, xc[gi * 8 + 5], acc);
-    acc = dot_word(w[gi][1].z, xc[gi * 8 + 6], acc);
-    acc = dot_word(w[gi][1].w, xc[gi * 8 + 7], acc);
-    part += sc[gi] * (acc - xsum[gi].y) + bi[gi] * xsum[gi].x;
+    acc = dot_word(w[gi][0].x, xg[0], acc);
+    acc = dot_word(w[gi][0].y, xg[1], acc);
+    acc = dot_word(w[gi][0].z, xg[2], acc);
+    acc = dot_word(w[gi][0].w, xg[3], acc);
+    acc = dot_word(w[gi][1].x, xg[4], acc);
+    acc = dot_word(w[gi][1].y, xg[5], acc);
+    acc = dot_word(w[gi][1].z, xg[6], acc);
+    acc = dot_word(w[gi][1].w, xg[7], acc);
+    const float2 xsg = xsum[gi * gstride];
+    part += sc[gi] * (acc - xsg.y) + bi[gi] * xsg.x;
   }
   return part;
 }
@@ -211,14 +215,18 @@ __device__ __forceinline__ void down_load_items(
     const int rr = st * rps + slot;
     const bool live = live_item && rr < kDnRows;
     const int64_t row = r0 + min(rr, kDnRows - 1);
-    const uint32_t* wr = a.down.w + e * a.down.stride_w + row * C + li * GPL * 8;
-    const uint16_t* sr = a.down.s + e * a.down.stride_sb + row * G + li * GPL;
-    const uint16_t* br = a.down.b + e * a.down.stride_sb + row * G + li * GPL;
+    // lane li owns groups li, li + tpr, ...: one load instruction then reads
+    // adjacent 16-byte halves of the row's groups (two lines per row), not
+    // pieces of six lines
+    const int tpr = G / GPL;
+    const uint32_t* wr = a.down.w + e * a.down.stride_w + row * C + li * 8;
+    const uint16_t* sr = a.down.s + e * a.down.stride_sb + row * G + li;
+    const uint16_t* br = a.down.b + e * a.down.stride_sb + row * G + li;
 #pragma unroll
     for (int gi = 0; gi < GPL; ++gi) {
-      w[q][gi][0] = ld_stream4(wr + gi * 8);
-      w[q][gi][1] = ld_stream4(wr + gi * 8 + 4);
-      const uint32_t sv = sr[gi], bv = br[gi];
+      w[q][gi][0] = ld_stream4(wr + gi * tpr * 8);
+      w[q][gi][1] = ld_stream4(wr + gi * tpr * 8 + 4);
+      const uint32_t sv = sr[gi * tpr], bv = br[gi * tpr];
       sraw[q][gi] = live ? sv : 0u;
       braw[q][gi] = live ? bv : 0u;
     }
@@ -475,7 +483,8 @@ __device__ __forceinline__ void down_row_block(const FfnArgs& a, const DecMeta& 
                                                const float2* hsum, float* ylds,
                                                uint4 (&w)[IPW][GPL][2],
                                                uint32_t (&sraw)[IPW][GPL],
-                                               uint32_t (&braw)[IPW][GPL]) {
+                                               uint32_t (&braw)[IPW][GPL], bool have_res,
+                                               float res_pref) {
   for (int first = wave; first < items; first += kDecWaves * IPW) {
     if (first != wave)
       down_load_items<GPL>(a, m, first, items, steps, rps, slot, li, r0, C, G, w, sraw, braw);
@@ -494,9 +503,9 @@ __device__ __forceinline__ void down_row_block(const FfnArgs& a, const DecMeta& 
         }
         for (int j = 0; j < ne; ++j) {
           const int p = uniform(m.pairs[pb + j]);
-          const uint4* xc = hx + (size_t)p * C + li * GPL * 8;
-          const float2* xsm = hsum + (size_t)p * G + li * GPL;
-          float part = lane_row_dot<GPL>(w[q], sc, bi, xc, xsm);
+          const uint4* xc = hx + (size_t)p * C + li * 8;
+          const float2* xsm = hsum + (size_t)p * G + li;
+          float part = lane_row_dot<GPL>(w[q], sc, bi, xc, xsm, tpr);
           part = segment_sum(part, tpr);
           if (li == 0 && rr < kDnRows) ylds[p * kDnRows + rr] = part;
         }
@@ -515,7 +524,7 @@ __device__ __forceinline__ void down_row_block(const FfnArgs& a, const DecMeta& 
       acc += m.w[p] * ylds[p * kDnRows + rr];
     }
     const int64_t o = (int64_t)t * a.d + r0 + rr;
-    const float res = a.residual ? a.residual[o] : 0.f;
+    const float res = have_res ? res_pref : (a.residual ? a.residual[o] : 0.f);
     a.out[o] = res + acc;
   }
   __syncthreads();                                 // ylds is free again
@@ -532,6 +541,11 @@ __global__ __launch_bounds__(kDecThreads) void k_down_combine_gemv(FfnArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int P = a.B * a.K;
+  // the first row block's residual, fetched before anything waits
+  float res_pref = 0.f;
+  if (a.residual != nullptr && threadIdx.x < a.B * kDnRows)
+    res_pref = a.residual[(int64_t)(threadIdx.x / kDnRows) * a.d + blockIdx.x * kDnRows +
+                          threadIdx.x % kDnRows];
   load_meta(a, m);
   const int nU = uniform(m.n_union);
   const int f = a.f, G = f / 64, C = f / 8;
@@ -600,7 +614,7 @@ __global__ __launch_bounds__(kDecThreads) void k_down_combine_gemv(FfnArgs a) {
       down_load_items<GPL>(a, m, wave, items, steps, rps, slot, li, rb * kDnRows, C, G, w0, s0,
                            b0);
     down_row_block<GPL>(a, m, rb * kDnRows, wave, items, steps, rps, slot, li, tpr, C, G, hx,
-                        hsum, ylds, w0, s0, b0);
+                        hsum, ylds, w0, s0, b0, rb == (int)blockIdx.x, res_pref);
   }
 }
 
