@@ -44,7 +44,7 @@ constexpr int kMaxDecPairs = 16;      // B * K <= 16 on this path
 // the arithmetic (about 9 VALU ops per packed word) then hides under the next
 // item's loads instead of piling up once all of a burst has landed
 constexpr int kGuBlocksPerCU = 1;
-constexpr int kGuDepth = 3;           // gate_up: items per wave in the load ring
+constexpr int kGuDepth = 2;           // gate_up: items per wave in the load ring
 constexpr int kGuMaxItems = 64;       // gate_up: items per wave (h staged in LDS)
 constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU (one row block each at d = 4096)
 constexpr int kHRegs = 6;             // down: h chunks per thread loaded ahead of the weights

@@ -27,16 +27,24 @@ constexpr int kTailThreads = 1024;              // stand-alone top-k / union blo
 constexpr int kMaxTicketBlocks = 64;            // larger grids hand the tail to its own kernel
 
 // Prepped activations of one (token, 64-input group): 8 chunks + group sums.
+// All 16 loads are issued before the first store (a store between them would
+// keep the compiler from hoisting the next loads above it).
 __device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, float2* xs) {
   const float4* src = reinterpret_cast<const float4*>(x + (int64_t)t * d + g * 64);
   uint4* dst = reinterpret_cast<uint4*>(xp + (int64_t)t * d + g * 64);
+  float4 v4[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) v4[c] = src[c];
   float X = 0.f, S = 0.f;
-#pragma unroll 2
+  uint4 out[8];
+#pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const float4 lo = src[2 * c], hi = src[2 * c + 1];
+    const float4 lo = v4[2 * c], hi = v4[2 * c + 1];
     const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    dst[c] = prep_chunk(v, &X, &S);
+    out[c] = prep_chunk(v, &X, &S);
   }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) dst[c] = out[c];
   xs[(int64_t)t * (d / 64) + g] = make_float2(X, 1024.0f * S);
 }
 
@@ -207,21 +215,19 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
                                                          uint32_t* ticket) {
   __shared__ UnionSmem us;
   __shared__ int is_last;
-  {
+  // blocks [0, E/4) compute logits (4 experts each, kTokensPerWave tokens per
+  // grid row); the blocks after them prep the activations, one (token, group)
+  // unit per thread, in grid row 0, alongside the logits
+  const int n_logit_blocks = (a.E + 3) / 4;
+  if ((int)blockIdx.x < n_logit_blocks) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int e = blockIdx.x * (kRouteThreads / 64) + wave;
     const int t0 = blockIdx.y * kTokensPerWave;
     if (e < a.E) logits_wave<kBf16>(a, e, t0, min(kTokensPerWave, a.B - t0));
-  }
-  if (a.xp != nullptr) {
-    // (token, group) units dealt round-robin over the blocks first, so that
-    // every block preps a few and none holds up the launch's end
+  } else if (a.xp != nullptr && blockIdx.y == 0) {
     const int G = a.d / 64;
-    const int units = a.B * G;
-    const int nblocks = gridDim.x * gridDim.y;
-    const int bid = blockIdx.y * gridDim.x + blockIdx.x;
-    for (int u = bid + (int)threadIdx.x * nblocks; u < units; u += nblocks * blockDim.x)
-      prep_group(a.x, a.d, u / G, u % G, a.xp, a.xs);
+    const int u = (blockIdx.x - n_logit_blocks) * kRouteThreads + threadIdx.x;
+    if (u < a.B * G) prep_group(a.x, a.d, u / G, u % G, a.xp, a.xs);
   }
   if (!do_tail) return;
   // last block: every other block's logits are visible after its release and our acquire
@@ -269,7 +275,8 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
   bool tail_done = false;
   if (!logits_in) {
     // logits (+ activation prep); small grids finish top-k/union in their last block
-    const dim3 grid((a.E + 3) / 4, (a.B + kTokensPerWave - 1) / kTokensPerWave);
+    const int prep_blocks = a.xp != nullptr ? (a.B * (a.d / 64) + kRouteThreads - 1) / kRouteThreads : 0;
+    const dim3 grid((a.E + 3) / 4 + prep_blocks, (a.B + kTokensPerWave - 1) / kTokensPerWave);
     const bool fused = (do_topk || do_union) && (int)(grid.x * grid.y) <= kMaxTicketBlocks;
     uint32_t* ticket = a.status + 1;
     if (a.router_bf16)
