@@ -47,10 +47,12 @@ constexpr int kGuBlocksPerCU = 1;
 constexpr int kGuDepth = 2;           // gate_up: items per wave in the load ring
 constexpr int kGuMaxItems = 64;       // gate_up: items per wave (h staged in LDS)
 constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU (one row block each at d = 4096)
-constexpr int kHRegs = 6;             // down: h chunks per thread loaded ahead of the weights
+constexpr int kDnThreads = 512;       // down: 8 waves a block, one item each at d = 4096
+constexpr int kDnWaves = kDnThreads / 64;
+constexpr int kHRegs = 3;             // down: h chunks per thread loaded ahead of the weights
 // down: (expert, row step) items per wave per batch of loads
 template <int GPL>
-constexpr int items_per_wave() { return GPL >= 3 ? 2 : 4; }
+constexpr int items_per_wave() { return GPL >= 3 ? 1 : 2; }
 
 // Prepped position (half index within the row) of column c.
 __device__ __forceinline__ int prepped_pos(int c) {
@@ -205,7 +207,7 @@ __device__ __forceinline__ void down_load_items(
     uint32_t (&braw)[IPW][GPL]) {
 #pragma unroll
   for (int q = 0; q < IPW; ++q) {
-    const int it = first + q * kDecWaves;
+    const int it = first + q * kDnWaves;
     const bool live_item = it < items;
     // an empty union (every routed id invalid) loads expert 0 and uses none of it
     const int itc = live_item ? it : max(items - 1, 0);
@@ -485,12 +487,12 @@ __device__ __forceinline__ void down_row_block(const FfnArgs& a, const DecMeta& 
                                                uint32_t (&sraw)[IPW][GPL],
                                                uint32_t (&braw)[IPW][GPL], bool have_res,
                                                float res_pref) {
-  for (int first = wave; first < items; first += kDecWaves * IPW) {
+  for (int first = wave; first < items; first += kDnWaves * IPW) {
     if (first != wave)
       down_load_items<GPL>(a, m, first, items, steps, rps, slot, li, r0, C, G, w, sraw, braw);
 #pragma unroll
     for (int q = 0; q < IPW; ++q) {
-      const int it = first + q * kDecWaves;
+      const int it = first + q * kDnWaves;
       if (it < items) {   // uniform across the wave
         const int uu = uniform(it / steps), st = it % steps;
         const int pb = uniform(m.offsets[uu]), ne = uniform(m.offsets[uu + 1]) - pb;
@@ -534,7 +536,7 @@ __device__ __forceinline__ void down_row_block(const FfnArgs& a, const DecMeta& 
 // block b takes row blocks b, b + grid, ... of 8 output rows x all union
 // experts.
 template <int GPL>
-__global__ __launch_bounds__(kDecThreads) void k_down_combine_gemv(FfnArgs a) {
+__global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   constexpr int IPW = items_per_wave<GPL>();
   __shared__ DecMeta m;
   extern __shared__ __align__(16) char smem[];
@@ -567,29 +569,23 @@ __global__ __launch_bounds__(kDecThreads) void k_down_combine_gemv(FfnArgs a) {
   uint32_t s0[IPW][GPL], b0[IPW][GPL];
   const int nchunk = P * C;
   const uint4* hsrc = reinterpret_cast<const uint4*>(a.hp);
-  // six chunks a thread held in named registers (an array here ends up in
+  // three chunks a thread held in named registers (an array here ends up in
   // scratch), clamped to the last chunk past the end
   const int hi0 = threadIdx.x;
-  const uint4 h0 = hsrc[min(hi0 + 0 * kDecThreads, nchunk - 1)];
-  const uint4 h1 = hsrc[min(hi0 + 1 * kDecThreads, nchunk - 1)];
-  const uint4 h2 = hsrc[min(hi0 + 2 * kDecThreads, nchunk - 1)];
-  const uint4 h3 = hsrc[min(hi0 + 3 * kDecThreads, nchunk - 1)];
-  const uint4 h4 = hsrc[min(hi0 + 4 * kDecThreads, nchunk - 1)];
-  const uint4 h5 = hsrc[min(hi0 + 5 * kDecThreads, nchunk - 1)];
+  const uint4 h0 = hsrc[min(hi0 + 0 * kDnThreads, nchunk - 1)];
+  const uint4 h1 = hsrc[min(hi0 + 1 * kDnThreads, nchunk - 1)];
+  const uint4 h2 = hsrc[min(hi0 + 2 * kDnThreads, nchunk - 1)];
   __builtin_amdgcn_sched_barrier(0);
   int rb = blockIdx.x;
   down_load_items<GPL>(a, m, wave, items, steps, rps, slot, li, rb * kDnRows, C, G, w0, s0, b0);
   // (threads past the end rewrite chunk nchunk-1 with the value it already has)
-  hx[min(hi0 + 0 * kDecThreads, nchunk - 1)] = h0;
-  hx[min(hi0 + 1 * kDecThreads, nchunk - 1)] = h1;
-  hx[min(hi0 + 2 * kDecThreads, nchunk - 1)] = h2;
-  hx[min(hi0 + 3 * kDecThreads, nchunk - 1)] = h3;
-  hx[min(hi0 + 4 * kDecThreads, nchunk - 1)] = h4;
-  hx[min(hi0 + 5 * kDecThreads, nchunk - 1)] = h5;
-  for (int i = threadIdx.x + kHRegs * kDecThreads; i < nchunk; i += kDecThreads) hx[i] = hsrc[i];
+  hx[min(hi0 + 0 * kDnThreads, nchunk - 1)] = h0;
+  hx[min(hi0 + 1 * kDnThreads, nchunk - 1)] = h1;
+  hx[min(hi0 + 2 * kDnThreads, nchunk - 1)] = h2;
+  for (int i = threadIdx.x + kHRegs * kDnThreads; i < nchunk; i += kDnThreads) hx[i] = hsrc[i];
   __syncthreads();
   // group sums (X, C) of h: one (pair, group) per thread, 8 chunks of 8 halves
-  for (int i = threadIdx.x; i < P * G; i += kDecThreads) {
+  for (int i = threadIdx.x; i < P * G; i += kDnThreads) {
     const uint4* hc = hx + (size_t)(i / G) * C + (i % G) * 8;
     float X = 0.f, S = 0.f;
 #pragma unroll
@@ -670,7 +666,7 @@ hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming*
   const int ncu = cu_count();
   if (ncu <= 0) return hipErrorInvalidDevice;
   const int grid = std::min(a.d / kDnRows, ncu * kDnBlocksPerCU);
-  SMOE_LAUNCH(t, k_down_combine_gemv<GPL>, dim3(grid), dim3(kDecThreads), decode_smem(a), s, a);
+  SMOE_LAUNCH(t, k_down_combine_gemv<GPL>, dim3(grid), dim3(kDnThreads), decode_smem(a), s, a);
   return hipGetLastError();
 }
 
