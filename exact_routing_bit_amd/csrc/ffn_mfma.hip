@@ -29,9 +29,12 @@
 // as whole 64-byte row segments however the MFMA wants them laid out.  The
 // activations and sums of a stage are shared by the four waves (one copy
 // instruction each) behind one workgroup barrier per stage.  Scales and
-// biases come 16 bytes (8 groups) a row per copy, once every four stages,
-// when the group count and the strides allow it (kFastSB); otherwise one
-// aligned dword per row and group each stage.
+// biases (kFastSB: up to 64 groups, 16-byte aligned rows) are read once per
+// workgroup into registers, four lanes per row reading its run of bytes in
+// one piece, and handed to the lanes that use them with ds_bpermute every
+// four stages; reading them 16 bytes a row every four stages instead made
+// scattered small requests that cost more than the packed words.  Otherwise
+// one aligned dword per row and group is copied each stage.
 #include "device.hpp"
 #include "smoe_internal.hpp"
 
@@ -44,7 +47,7 @@ constexpr int kTiles = 4;                          // 16-row tiles per wave (64 
 constexpr int kPairTile = 16;                      // pairs per token tile (MFMA M)
 constexpr int kGps = 2;                            // groups per pipeline stage
 constexpr int kRing = 3;                           // stages resident in LDS
-constexpr int kSuper = 4;                          // stages per scale/bias copy (kFastSB)
+constexpr int kSuper = 4;                          // stages per scale/bias handout (kFastSB)
 
 // One ring slot (one stage).  Layouts, 16-byte entries unless noted:
 //   W  [wave][tile][chunk 4][row 16]    chunk c = group c/2, words 4(c%2)..+3
@@ -53,8 +56,7 @@ constexpr int kSuper = 4;                          // stages per scale/bias copy
 //   SB [wave][s|b][group 2][col 16][tile 4]          u32, the aligned dword
 //                                        holding that row's bf16 s (or b)
 //                                        (only without kFastSB)
-// kFastSB keeps scales and biases outside the ring, double-buffered per four
-// stages: [buffer 2][wave][s|b][tile 4][col 16] x 16 bytes = groups 8j..8j+7.
+// kFastSB keeps scales and biases in registers (see the kernel).
 constexpr int kWBytes = kWaves * kTiles * 1024;
 constexpr int kABytes = 16 * kPairTile * 16;
 constexpr int kXSBytes = kGps * 2 * 2 * kPairTile * 4;
@@ -63,14 +65,13 @@ constexpr int kOffA = kWBytes;
 constexpr int kOffXS = kOffA + kABytes;
 constexpr int kOffSB = kOffXS + kXSBytes;
 constexpr int slot_bytes(bool fast_sb) { return kOffSB + (fast_sb ? 0 : kSBSlotBytes); }
-constexpr int kSBFastBytes = 2 * kWaves * 2 * kTiles * 16 * 16;
 // copy instructions per wave and stage: words (one per tile), activations,
-// sums, and the scale/bias copies (kFastSB: two on every fourth stage)
+// sums, and (without kFastSB) the scale/bias dwords
 constexpr int kCopiesBase = kTiles + 1 + 1;
 
 template <bool kFastSB>
 constexpr int copies_of_stage(bool superstage_start) {
-  return kCopiesBase + (kFastSB ? (superstage_start ? 2 : 0) : 2 * kGps);
+  return kCopiesBase + (kFastSB ? 0 : 2 * kGps);
 }
 
 // Per-lane copy sources that stay fixed over the K loop.
@@ -88,8 +89,8 @@ __device__ __forceinline__ const void* align4(const uint16_t* p) {
 
 // Copies of stage k (groups gA = 2k and gB = min(2k+1, G-1)) into `slot`.
 template <bool kGateUp, bool kFastSB>
-__device__ __forceinline__ void issue_stage(const Sources& S, char* slot, char* sbfast, int k, int G,
-                                            bool superstage_start, int wave, int lane) {
+__device__ __forceinline__ void issue_stage(const Sources& S, char* slot, int k, int G, int wave,
+                                            int lane) {
   const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
   // packed words: lanes 0-31 copy group gA, lanes 32-63 group gB
   const int gw = (lane >> 5) ? gB : gA;
@@ -104,14 +105,7 @@ __device__ __forceinline__ void issue_stage(const Sources& S, char* slot, char* 
   } else {
     if (lane < 32) dma4_to_lds(S.sums + ga * 4, slot + kOffXS + wave * 128);
   }
-  if (kFastSB) {
-    if (superstage_start) {                        // groups 8j .. 8j+7, j = k / 4
-      const int j = k / kSuper;
-      char* dst = sbfast + ((j & 1) * kWaves + wave) * (2 * kTiles * 256);
-      dma16_to_lds(S.s + 8 * j, dst);
-      dma16_to_lds(S.b + 8 * j, dst + kTiles * 256);
-    }
-  } else {
+  if (!kFastSB) {
     // one dword a lane, the aligned one that holds the value
     char* sb = slot + kOffSB + wave * (2 * kGps * 256);
     dma4_to_lds(align4(S.s + gA), sb);
@@ -119,6 +113,14 @@ __device__ __forceinline__ void issue_stage(const Sources& S, char* slot, char* 
     dma4_to_lds(align4(S.b + gA), sb + 512);
     dma4_to_lds(align4(S.b + gB), sb + 768);
   }
+}
+
+// The uint4 that lane src/4 holds in v.
+__device__ __forceinline__ uint4 bpermute4(int src, const uint4& v) {
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.z),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.w));
 }
 
 // bf16 in the upper (hi) or lower half of a dword, as fp32
@@ -198,7 +200,6 @@ template <bool kGateUp, bool kFastSB>
 __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   constexpr int kSlot = slot_bytes(kFastSB);
   __shared__ __align__(16) char ring[kRing * kSlot];
-  __shared__ __align__(16) char sbfast[kFastSB ? kSBFastBytes : 16];
   __shared__ int lpair[kPairTile];                 // pair ids of the current token tile
   const int u = blockIdx.y;
   const int nU = *a.n_union;
@@ -254,6 +255,27 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     }
   }
   const int nst = (G + kGps - 1) / kGps;
+  // kFastSB: this wave's scales and biases for the whole K loop, read once as
+  // contiguous runs (lane l: row rows0[T] + l/4, 16-byte piece 4h + l%4 of the
+  // row's G/8), not as 16-byte pieces of 64 rows per four stages; each group
+  // of four stages hands every lane its rows' piece with ds_bpermute
+  uint4 sbs[kTiles][2], sbb[kTiles][2];
+  if (kFastSB) {
+    const int P = G / 8;                           // <= 8 pieces a row (G <= 64)
+#pragma unroll
+    for (int T = 0; T < kTiles; ++T) {
+      const QMat& m = kGateUp ? (T < 2 ? a.gate : a.up) : a.down;
+      const int64_t row = rows0[T] + (lane >> 2);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int piece = 4 * h + (lane & 3);
+        const int pc = piece < P ? piece : 0;      // a valid address; the value is unused
+        const int64_t at = e * m.stride_sb + row * G + pc * 8;
+        sbs[T][h] = *reinterpret_cast<const uint4*>(m.s + at);
+        sbb[T][h] = *reinterpret_cast<const uint4*>(m.b + at);
+      }
+    }
+  }
 
   for (int m0 = 0; m0 < ne; m0 += kPairTile) {
     __syncthreads();                               // the previous tile is done with lpair
@@ -277,8 +299,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     for (int T = 0; T < kTiles; ++T) acc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
     SBRegs regs;
 
-    issue_stage<kGateUp, kFastSB>(S, ring, sbfast, 0, G, true, wave, lane);
-    if (nst > 1) issue_stage<kGateUp, kFastSB>(S, ring + kSlot, sbfast, 1, G, false, wave, lane);
+    issue_stage<kGateUp, kFastSB>(S, ring, 0, G, wave, lane);
+    if (nst > 1) issue_stage<kGateUp, kFastSB>(S, ring + kSlot, 1, G, wave, lane);
     // stages in fours so that the stage's place in its four is a constant
     for (int ks = 0; ks < nst; ks += kSuper) {
 #define SMOE_MFMA_STAGE(kk)                                                                       \
@@ -290,13 +312,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
           wait_vmcnt<0>();                                                                        \
         barrier_no_wait();           /* ... and every wave's; slot k-1 is free */                 \
         if (k + 2 < nst)                                                                          \
-          issue_stage<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, sbfast, k + 2, G,    \
-                                        (kk + 2) % kSuper == 0, wave, lane);                      \
+          issue_stage<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave,       \
+                                        lane);                                                    \
         if (kFastSB && kk == 0) {                                                                 \
-          const char* sbr = sbfast + (((k / kSuper) & 1) * kWaves + wave) * (2 * kTiles * 256);   \
+          const int j = k / kSuper;                  /* groups 8j .. 8j+7: piece j */             \
+          const int src = (col * 4 + (j & 3)) * 4;   /* lane holding this row's piece j */        \
           _Pragma("unroll") for (int T = 0; T < kTiles; ++T) {                                   \
-            regs.s[T] = *reinterpret_cast<const uint4*>(sbr + (T * 16 + col) * 16);               \
-            regs.b[T] = *reinterpret_cast<const uint4*>(sbr + kTiles * 256 + (T * 16 + col) * 16); \
+            regs.s[T] = bpermute4(src, j < 4 ? sbs[T][0] : sbs[T][1]);                            \
+            regs.b[T] = bpermute4(src, j < 4 ? sbb[T][0] : sbb[T][1]);                            \
           }                                                                                       \
         }                                                                                         \
         compute_stage<kGateUp, kFastSB, kk>(ring + (k % kRing) * kSlot, k, G, wave, col, lg,      \
@@ -357,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
 
 // 16-byte scale/bias copies need 8 | G, 8 | stride and 16-byte aligned bases
 bool fast_sb_ok(const QMat& m, int G) {
-  return G % 8 == 0 && m.stride_sb % 8 == 0 && (reinterpret_cast<uintptr_t>(m.s) & 15) == 0 &&
+  return G % 8 == 0 && G <= 64 && m.stride_sb % 8 == 0 && (reinterpret_cast<uintptr_t>(m.s) & 15) == 0 &&
          (reinterpret_cast<uintptr_t>(m.b) & 15) == 0;
 }
 
