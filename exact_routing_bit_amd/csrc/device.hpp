@@ -316,25 +316,19 @@ struct TopkSel {
   float my_v;
 };
 
-// Top-k of one row of E <= 64 * NJ logits by one full wave (v[j] = logit of
-// expert lane + 64 j; entries past E are ignored), K <= 16, ranked by logit
-// descending and, on equal logits, expert index ascending:
-//   1. a threshold t (topk_threshold: wave mask counts);
-//   2. the keys above t, plus the lowest-index keys equal to t up to K in all,
-//      are copied in expert order to the wave's scratch;
-//   3. each of the K ranks itself against the other K-1 and is sent to the
-//      lane of its rank (ds_permute).
-// Candidates past E get key 0, below every real key, so no step needs a
-// branch on E.  sc: this wave's scratch in LDS (no other wave may use it
-// meanwhile).  Every lane of the wave must be active.
+// Order keys of the lane's candidates (expert lane + 64 j); 0 past E.
 template <int NJ>
-__device__ __forceinline__ TopkSel wave_topk_sel(const float (&v)[4], int E, int K,
-                                                 TopkScratch* sc) {
+__device__ __forceinline__ void topk_keys(const float (&v)[4], int E, uint32_t (&key)[4]) {
   const int lane = __lane_id();
-  uint32_t key[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) key[j] = (j < NJ && lane + 64 * j < E) ? order_key(v[j]) : 0u;
-  const uint32_t t = topk_threshold<NJ>(key, K);
+}
+
+// Steps 2 and 3 of wave_topk_sel for one row, given its threshold t.
+template <int NJ>
+__device__ __forceinline__ TopkSel topk_finish(const float (&v)[4], const uint32_t (&key)[4],
+                                               uint32_t t, int K, TopkScratch* sc) {
+  const int lane = __lane_id();
   uint64_t gt[4], eq[4];
 #pragma unroll
   for (int j = 0; j < NJ; j += 2) masks_gt_eq2(key[j], key[j + 1], t, gt[j], gt[j + 1], eq[j], eq[j + 1]);
@@ -391,6 +385,25 @@ __device__ __forceinline__ TopkSel wave_topk_sel(const float (&v)[4], int E, int
   out.my_e = mine ? pe : 0;
   out.my_v = mine ? pv : 0.f;
   return out;
+}
+
+// Top-k of one row of E <= 64 * NJ logits by one full wave (v[j] = logit of
+// expert lane + 64 j; entries past E are ignored), K <= 16, ranked by logit
+// descending and, on equal logits, expert index ascending:
+//   1. a threshold t (topk_threshold: wave mask counts);
+//   2. the keys above t, plus the lowest-index keys equal to t up to K in all,
+//      are copied in expert order to the wave's scratch;
+//   3. each of the K ranks itself against the other K-1 and is sent to the
+//      lane of its rank (ds_permute).
+// Candidates past E get key 0, below every real key, so no step needs a
+// branch on E.  sc: this wave's scratch in LDS (no other wave may use it
+// meanwhile).  Every lane of the wave must be active.
+template <int NJ>
+__device__ __forceinline__ TopkSel wave_topk_sel(const float (&v)[4], int E, int K,
+                                                 TopkScratch* sc) {
+  uint32_t key[4];
+  topk_keys<NJ>(v, E, key);
+  return topk_finish<NJ>(v, key, topk_threshold<NJ>(key, K), K, sc);
 }
 
 // Top-k of one row of E <= 256 logits (see wave_topk_sel): lane k < K gets

@@ -18,19 +18,35 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
   const int per_row = a.d / 4;
   if (i >= a.B * per_row) return;
   const int t = i / per_row, r4 = i - t * per_row;
+  // every load first (pair rows are always valid memory; a dropped pair's row
+  // is loaded and not used), so that they overlap instead of each waiting on
+  // the previous pair's position
+  float4 y[kMaxTopK];
+  float w[kMaxTopK];
+  int pos[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k < a.K) {
+      const int p = t * a.K + k;
+      pos[k] = a.pair_pos[p];
+      w[k] = a.topk_w[p];
+      y[k] = reinterpret_cast<const float4*>(a.y + (int64_t)p * a.d)[r4];
+    }
+  }
+  const float4 res = a.residual ? reinterpret_cast<const float4*>(a.residual + (int64_t)t * a.d)[r4]
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+  // k ascending, fp32, then the residual
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k = 0; k < a.K; ++k) {
-    const int p = t * a.K + k;
-    if (a.pair_pos[p] < 0) continue;
-    const float w = a.topk_w[p];
-    const float4 y = reinterpret_cast<const float4*>(a.y + (int64_t)p * a.d)[r4];
-    acc.x += w * y.x;
-    acc.y += w * y.y;
-    acc.z += w * y.z;
-    acc.w += w * y.w;
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) {
+    if (k < a.K && pos[k] >= 0) {
+      acc.x += w[k] * y[k].x;
+      acc.y += w[k] * y[k].y;
+      acc.z += w[k] * y[k].z;
+      acc.w += w[k] * y[k].w;
+    }
   }
   if (a.residual) {
-    const float4 res = reinterpret_cast<const float4*>(a.residual + (int64_t)t * a.d)[r4];
     acc.x = res.x + acc.x;
     acc.y = res.y + acc.y;
     acc.z = res.z + acc.z;

@@ -50,7 +50,8 @@ __device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, fl
 
 // Top-k of one token's E <= 256 logits by one full wave; writes indices and
 // weights (rank order) to global memory and the indices to s_idx.
-__device__ void topk_token(const RouteArgs& a, int t, int32_t* s_idx, TopkScratch* sc) {
+__device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int32_t* s_idx,
+                                           TopkScratch* sc) {
   const int lane = __lane_id();
   const int E = a.E, K = a.K;
   float v[4];
@@ -80,7 +81,7 @@ struct UnionSmem {
 
 // Union of the batch's experts and the per-expert pair lists, by one block
 // (any size that is a multiple of 64) from us->idx[0..P).
-__device__ void build_union(const RouteArgs& a, UnionSmem* us) {
+__device__ __forceinline__ void build_union(const RouteArgs& a, UnionSmem* us) {
   const int nthr = blockDim.x, tid = threadIdx.x;
   const int E = a.E, P = a.B * a.K;
   const int W = (P + 31) / 32;
@@ -145,8 +146,9 @@ __device__ void build_union(const RouteArgs& a, UnionSmem* us) {
 }
 
 // Top-k of every token, then (optionally) the union, by the calling block.
-__device__ void route_tail(const RouteArgs& a, bool do_topk, bool do_union, UnionSmem* us) {
-  const int wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+__device__ __forceinline__ void route_tail(const RouteArgs& a, bool do_topk, bool do_union,
+                                           UnionSmem* us) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), nwaves = blockDim.x >> 6;
   if (do_topk)
     for (int t = wave; t < a.B; t += nwaves) topk_token(a, t, us->idx, &us->topk[wave]);
   if (!do_union) return;
