@@ -372,7 +372,7 @@ def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     lines = [
         f"# HBM traffic per launch of {ROOFLINE_KERNEL} on the decode layer (B=1)",
         "# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (two passes) over",
-        "#   python3 bench.py --no-cpu --no-prefill --steps 200 --warmup 10",
+        "#   python3 bench.py --no-cpu --no-stack --no-prefill --steps 200 --warmup 10",
         "# scaled by the same counters for a 1 GiB device copy:",
         "#   python3 bench.py --copy-calibration",
         f"kernel: {ROOFLINE_KERNEL}",
