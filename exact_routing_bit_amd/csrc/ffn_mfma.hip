@@ -67,11 +67,14 @@ constexpr int kOffSB = kOffXS + kXSBytes;
 constexpr int slot_bytes(bool fast_sb) { return kOffSB + (fast_sb ? 0 : kSBSlotBytes); }
 // copy instructions per wave and stage: words (one per tile), activations,
 // sums, and (without kFastSB) the scale/bias dwords
-constexpr int kCopiesBase = kTiles + 1 + 1;
 
 template <bool kFastSB>
-constexpr int copies_of_stage(bool superstage_start) {
-  return kCopiesBase + (kFastSB ? 0 : 2 * kGps);
+constexpr int copies_of_rest() {
+  return 2 + (kFastSB ? 0 : 2 * kGps);
+}
+template <bool kFastSB>
+constexpr int copies_of_stage() {
+  return kTiles + copies_of_rest<kFastSB>();
 }
 
 // Per-lane copy sources that stay fixed over the K loop.
@@ -87,15 +90,22 @@ __device__ __forceinline__ const void* align4(const uint16_t* p) {
   return reinterpret_cast<const void*>(reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)3);
 }
 
-// Copies of stage k (groups gA = 2k and gB = min(2k+1, G-1)) into `slot`.
-template <bool kGateUp, bool kFastSB>
-__device__ __forceinline__ void issue_stage(const Sources& S, char* slot, int k, int G, int wave,
+// Copies of stage k (groups gA = 2k and gB = min(2k+1, G-1)) into `slot`:
+// the packed words (issue_words, kTiles copies) and the rest (issue_rest:
+// activations, sums and, without kFastSB, the scale/bias dwords).
+template <bool kGateUp>
+__device__ __forceinline__ void issue_words(const Sources& S, char* slot, int k, int G, int wave,
                                             int lane) {
   const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
   // packed words: lanes 0-31 copy group gA, lanes 32-63 group gB
   const int gw = (lane >> 5) ? gB : gA;
 #pragma unroll
   for (int T = 0; T < kTiles; ++T) dma16_to_lds(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
+}
+template <bool kGateUp, bool kFastSB>
+__device__ __forceinline__ void issue_rest(const Sources& S, char* slot, int k, int G, int wave,
+                                           int lane) {
+  const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
   // activations: waves 0,1 copy the words of group gA, waves 2,3 those of gB
   const int ga = wave < 2 ? gA : gB;
   dma16_to_lds(S.act + ga * 8, slot + kOffA + wave * 1024);
@@ -113,6 +123,12 @@ __device__ __forceinline__ void issue_stage(const Sources& S, char* slot, int k,
     dma4_to_lds(align4(S.b + gA), sb + 512);
     dma4_to_lds(align4(S.b + gB), sb + 768);
   }
+}
+template <bool kGateUp, bool kFastSB>
+__device__ __forceinline__ void issue_stage(const Sources& S, char* slot, int k, int G, int wave,
+                                            int lane) {
+  issue_words<kGateUp>(S, slot, k, G, wave, lane);
+  issue_rest<kGateUp, kFastSB>(S, slot, k, G, wave, lane);
 }
 
 // The uint4 that lane src/4 holds in v.
@@ -200,13 +216,18 @@ template <bool kGateUp, bool kFastSB>
 __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   constexpr int kSlot = slot_bytes(kFastSB);
   __shared__ __align__(16) char ring[kRing * kSlot];
-  __shared__ int lpair[kPairTile];                 // pair ids of the current token tile
+  __shared__ int lpair_w[kWaves][kPairTile];       // each wave's copy of the tile's pair ids
   const int u = blockIdx.y;
+  // the union's size and this slot's expert and offsets in one round trip (slot
+  // u < the largest union is always inside the union arrays)
   const int nU = *a.n_union;
+  const int e_ld = a.union_experts[u];
+  const int pb_ld = a.expert_offsets[u];
+  const int pe_ld = a.expert_offsets[u + 1];
   if (u >= nU) return;
-  const int e = a.union_experts[u];
-  const int pb = a.expert_offsets[u];
-  const int ne = a.expert_offsets[u + 1] - pb;     // >= 1
+  const int e = e_ld;
+  const int pb = pb_ld;
+  const int ne = pe_ld - pb;                       // >= 1
   const int K = kGateUp ? a.d : a.f;
   const int G = K / 64, C = K / 8;
   const int lane = threadIdx.x & 63;
@@ -275,12 +296,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
         sbb[T][h] = *reinterpret_cast<const uint4*>(m.b + at);
       }
     }
+    // wait for them here, before any copy is in flight: the compiler does not
+    // count the copies (inline assembly), so its wait at their first use
+    // would otherwise be vmcnt(0) behind three stages of copies
+#pragma unroll
+    for (int T = 0; T < kTiles; ++T)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        asm volatile("" ::"v"(sbs[T][h].x), "v"(sbs[T][h].y), "v"(sbs[T][h].z), "v"(sbs[T][h].w));
+        asm volatile("" ::"v"(sbb[T][h].x), "v"(sbb[T][h].y), "v"(sbb[T][h].z), "v"(sbb[T][h].w));
+      }
   }
 
   for (int m0 = 0; m0 < ne; m0 += kPairTile) {
-    __syncthreads();                               // the previous tile is done with lpair
-    if (threadIdx.x < kPairTile) lpair[threadIdx.x] = a.pair_list[pb + min(m0 + (int)threadIdx.x, ne - 1)];
-    __syncthreads();
+    __syncthreads();                               // the previous tile is done with the ring
+    int* lpair = lpair_w[wave];
+    // the tile's pair ids (copied like the rest, so that no compiler-counted
+    // load sits behind the copies), then the first two stages' words, which
+    // need only the expert; the wait covers the ids alone
+    if (lane < kPairTile) dma4_to_lds(a.pair_list + pb + min(m0 + lane, ne - 1), lpair);
+    issue_words<kGateUp>(S, ring, 0, G, wave, lane);
+    if (nst > 1) {
+      issue_words<kGateUp>(S, ring + kSlot, 1, G, wave, lane);
+      wait_vmcnt<2 * kTiles>();
+    } else {
+      wait_vmcnt<kTiles>();
+    }
     {
       const int q = lpair[lane & 15];
       const int word = 4 * (wave & 1) + (lane >> 4);
@@ -299,17 +340,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     for (int T = 0; T < kTiles; ++T) acc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
     SBRegs regs;
 
-    issue_stage<kGateUp, kFastSB>(S, ring, 0, G, wave, lane);
-    if (nst > 1) issue_stage<kGateUp, kFastSB>(S, ring + kSlot, 1, G, wave, lane);
+    issue_rest<kGateUp, kFastSB>(S, ring, 0, G, wave, lane);
+    if (nst > 1) issue_rest<kGateUp, kFastSB>(S, ring + kSlot, 1, G, wave, lane);
     // stages in fours so that the stage's place in its four is a constant
     for (int ks = 0; ks < nst; ks += kSuper) {
 #define SMOE_MFMA_STAGE(kk)                                                                       \
       if (ks + kk < nst) {                                                                        \
         const int k = ks + kk;                                                                    \
-        if (k + 1 < nst)             /* this wave's copies of stage k landed */                   \
-          wait_vmcnt<copies_of_stage<kFastSB>((kk + 1) % kSuper == 0)>();                         \
-        else                                                                                      \
+        if (k + 1 >= nst)            /* this wave's copies of stage k landed: */                  \
           wait_vmcnt<0>();                                                                        \
+        else if (kk == 0 && ks == 0) /* stage 1's words went out before stage 0's rest */         \
+          wait_vmcnt<copies_of_rest<kFastSB>()>();                                                \
+        else                                                                                      \
+          wait_vmcnt<copies_of_stage<kFastSB>()>();                                               \
         barrier_no_wait();           /* ... and every wave's; slot k-1 is free */                 \
         if (k + 2 < nst)                                                                          \
           issue_stage<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave,       \
