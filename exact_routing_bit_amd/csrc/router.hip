@@ -24,6 +24,7 @@ namespace {
 constexpr int kRouteThreads = 256;              // 4 waves: 4 experts per block
 constexpr int kTokensPerWave = 2;
 constexpr int kTailThreads = 1024;              // stand-alone top-k / union block
+constexpr int kTopkThreads = 256;               // top-k grid: one token per wave
 constexpr int kMaxTicketBlocks = 64;            // larger grids hand the tail to its own kernel
 
 // Prepped activations of one (token, 64-input group): 8 chunks + group sums.
@@ -249,6 +250,55 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
   route_tail(a, true, a.n_union != nullptr, &us);
 }
 
+// Top-k with the logits given, one token per wave over a grid, and then (do_union)
+// the union by the last block to finish.  The top-k indices are stored and,
+// in the last block, loaded with agent-scope accesses, which are coherent
+// across the XCDs' L2s; the last block is found with an integer ticket
+// (status[2]) that it resets for the next call.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_union,
+                                                           uint32_t* ticket) {
+  __shared__ UnionSmem us;
+  __shared__ int is_last;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kTopkThreads / 64) + wave;
+  const int E = a.E, K = a.K;
+  if (t < a.B) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = e < E ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
+    }
+    float my_v;
+    int my_e;
+    wave_topk(v, E, K, my_v, my_e, &us.topk[wave]);
+    const float w = topk_weight(v, E, K, a.norm != 0, my_v);
+    if (lane < K) {
+      __hip_atomic_store(&a.topk_idx[t * K + lane], my_e, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      a.topk_w[t * K + lane] = w;
+    }
+  }
+  if (!do_union) return;
+  __builtin_amdgcn_s_waitcnt(0);                   // this wave's stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t n = gridDim.x;
+    const uint32_t tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (tk == n - 1);
+    if (is_last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  const int P = a.B * K;
+  for (int p = threadIdx.x; p < P; p += blockDim.x)
+    us.idx[p] = __hip_atomic_load(&a.topk_idx[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  build_union(a, &us);
+}
+
 // Top-k only (logits given) and/or union only (indices given): one block.
 __global__ __launch_bounds__(kTailThreads) void k_topk_union(RouteArgs a, int do_topk,
                                                              int do_union) {
@@ -289,9 +339,14 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
     if (err != hipSuccess) return err;
     tail_done = fused;
   }
-  if (!tail_done && (do_topk || do_union)) {
-    hipLaunchKernelGGL(k_topk_union, dim3(1), dim3(kTailThreads), 0, s, r, (int)do_topk,
-                       (int)do_union);
+  if (!tail_done && do_topk) {
+    const int blocks = (a.B + kTopkThreads / 64 - 1) / (kTopkThreads / 64);
+    hipLaunchKernelGGL(k_topk_grid, dim3(blocks), dim3(kTopkThreads), 0, s, r, (int)do_union,
+                       a.status + 2);
+    return hipGetLastError();
+  }
+  if (!tail_done && do_union) {
+    hipLaunchKernelGGL(k_topk_union, dim3(1), dim3(kTailThreads), 0, s, r, 0, 1);
     return hipGetLastError();
   }
   return hipSuccess;
