@@ -157,6 +157,7 @@ constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i within 8
 constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i within 16
+constexpr int kDppRowRor8 = 0x128;     // lane i <- lane i^8 within 16 (rotate by 8)
 
 __device__ __forceinline__ float readlane(float v, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));

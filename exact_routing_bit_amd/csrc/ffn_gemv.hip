@@ -49,10 +49,7 @@ constexpr int kGuMaxItems = 64;       // gate_up: items per wave (h staged in LD
 constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU (one row block each at d = 4096)
 constexpr int kDnThreads = 512;       // down: 8 waves a block, one item each at d = 4096
 constexpr int kDnWaves = kDnThreads / 64;
-constexpr int kHRegs = 3;             // down: h chunks per thread loaded ahead of the weights
-// down: (expert, row step) items per wave per batch of loads
-template <int GPL>
-constexpr int items_per_wave() { return GPL >= 3 ? 1 : 2; }
+constexpr int kDnMaxF = 2048;         // down: f/32 <= 64 lanes of 4 words a row
 
 // Prepped position (half index within the row) of column c.
 __device__ __forceinline__ int prepped_pos(int c) {
@@ -196,52 +193,138 @@ __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, i
 }
 
 // ------------------------------------------------------------- down items
-// Issue the loads of (up to) IPW (expert, row step) items of row block r0,
-// starting at item `first` and dealt every 4th to this wave.  Dead items and
-// lanes load a valid duplicate row and get zero scale and bias.  No early
-// exit: a branch here would keep the caller's in-flight loads alive across it.
-template <int GPL, int IPW = items_per_wave<GPL>()>
-__device__ __forceinline__ void down_load_items(
-    const FfnArgs& a, const DecMeta& m, int first, int items, int steps, int rps, int slot, int li,
-    int r0, int C, int G, uint4 (&w)[IPW][GPL][2], uint32_t (&sraw)[IPW][GPL],
-    uint32_t (&braw)[IPW][GPL]) {
+// Lane layout of the down kernel: lane L < NL = f/32 owns words 4L .. 4L+3 of
+// every row (32 inputs, half of group L/2) and the matching four chunks of h,
+// read once per item and kept in registers for all kDnRows rows of the item.
+// Lanes from NL on repeat lane NL-1's addresses with zero scale and bias.
+template <int NTOK>
+struct DnItem {
+  uint4 w[kDnRows];
+  uint32_t s[kDnRows], b[kDnRows];
+  uint4 h[NTOK][4];
+};
+
+// Issue the loads of item (union slot u, rows r0 .. r0+7): h of the slot's
+// pairs first (the compute needs it first), then the rows' words, scales and
+// biases.  No branch: dead pair slots repeat the last live pair.
+template <int NTOK>
+__device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, int u, int r0, int L,
+                                          bool lane_live, int C, int G, DnItem<NTOK>& it) {
+  // an empty union (every routed id invalid) has no items; an invalid id in a
+  // live slot cannot occur, but would read expert 0
+  const int e0 = uniform(m.experts[u]);
+  const int e = (unsigned)e0 < (unsigned)a.E ? e0 : 0;
+  const int pb = uniform(m.offsets[u]), ne = uniform(m.offsets[u + 1]) - pb;
+  // h of pair p: C chunks of 8 prepped halves; chunk c goes with word c of a row
+  const uint4* hsrc = reinterpret_cast<const uint4*>(a.hp);
 #pragma unroll
-  for (int q = 0; q < IPW; ++q) {
-    const int it = first + q * kDnWaves;
-    const bool live_item = it < items;
-    // an empty union (every routed id invalid) loads expert 0 and uses none of it
-    const int itc = live_item ? it : max(items - 1, 0);
-    const int uu = uniform(itc / steps), st = itc % steps;
-    const int e0 = uniform(m.experts[uu]);
-    const int e = (unsigned)e0 < (unsigned)a.E ? e0 : 0;
-    const int rr = st * rps + slot;
-    const bool live = live_item && rr < kDnRows;
-    const int64_t row = r0 + min(rr, kDnRows - 1);
-    // lane li owns groups li, li + tpr, ...: one load instruction then reads
-    // adjacent 16-byte halves of the row's groups (two lines per row), not
-    // pieces of six lines
-    const int tpr = G / GPL;
-    const uint32_t* wr = a.down.w + e * a.down.stride_w + row * C + li * 8;
-    const uint16_t* sr = a.down.s + e * a.down.stride_sb + row * G + li;
-    const uint16_t* br = a.down.b + e * a.down.stride_sb + row * G + li;
+  for (int q = 0; q < NTOK; ++q) {
+    const int p = uniform(m.pairs[pb + max(min(q, ne - 1), 0)]);
 #pragma unroll
-    for (int gi = 0; gi < GPL; ++gi) {
-      w[q][gi][0] = ld_stream4(wr + gi * tpr * 8);
-      w[q][gi][1] = ld_stream4(wr + gi * tpr * 8 + 4);
-      const uint32_t sv = sr[gi * tpr], bv = br[gi * tpr];
-      sraw[q][gi] = live ? sv : 0u;
-      braw[q][gi] = live ? bv : 0u;
-    }
+    for (int k = 0; k < 4; ++k) it.h[q][k] = hsrc[(int64_t)p * C + L * 4 + k];
+  }
+  const uint32_t* wr = a.down.w + e * a.down.stride_w + (int64_t)r0 * C + L * 4;
+#pragma unroll
+  for (int r = 0; r < kDnRows; ++r) it.w[r] = ld_stream4(wr + (int64_t)r * C);
+  const int64_t sb = e * a.down.stride_sb + (int64_t)r0 * G + (L >> 1);
+#pragma unroll
+  for (int r = 0; r < kDnRows; ++r) {
+    const uint32_t sv = a.down.s[sb + (int64_t)r * G], bv = a.down.b[sb + (int64_t)r * G];
+    it.s[r] = lane_live ? sv : 0u;
+    it.b[r] = lane_live ? bv : 0u;
   }
   __builtin_amdgcn_sched_barrier(0);               // issue them here (see gu_load)
 }
 
-// Shared memory of the down kernel: [P][C] prepped h, [P][G] (X, C) sums,
-// [P][kDnRows] per-pair outputs of the block's rows.
-size_t decode_smem(const FfnArgs& a) {
-  const size_t P = (size_t)a.B * a.K;
-  const size_t hx_chunks = (P * (a.f / 8) + 63) / 64 * 64;
-  return hx_chunks * 16 + P * (a.f / 64) * 8 + P * kDnRows * 4;
+// v_permlane32_swap / v_permlane16_swap through inline assembly: with the
+// compiler's builtins, the second register of the swapped pair was dropped
+// (both sums read the first).  The s_nop pairs cover the VALU-write ->
+// permlane-read and permlane-write -> VALU-read hazards, which the compiler
+// does not see through an asm statement.
+__device__ __forceinline__ void permlane32_swap(float& x, float& y) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void permlane16_swap(float& x, float& y) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+
+// Sum over the wave of eight per-lane row partials v[0..7]: afterwards every
+// lane of 8L' .. 8L'+7 holds the total of row L' (= lane / 8).  Bit 5 of the
+// lane is folded by permlane32 swaps (lanes 32-63 of the first register
+// trade places with lanes 0-31 of the second, so lanes 0-31 keep rows 0-3 and
+// lanes 32-63 rows 4-7), bit 4 by permlane16 swaps (odd 16-lane rows of the
+// first with even rows of the second), bit 3 by a DPP exchange, and bits 0-2
+// by DPP adds: about 20 VALU operations for eight rows.
+__device__ __forceinline__ float rows8_wave_sum(const float (&v)[8]) {
+  float a4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float x = v[j], y = v[j + 4];
+    permlane32_swap(x, y);
+    a4[j] = x + y;                                 // row j + 4 bit5
+  }
+  float c2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float x = a4[j], y = a4[j + 2];
+    permlane16_swap(x, y);
+    c2[j] = x + y;                                 // row j + 2 bit4 + 4 bit5
+  }
+  // lane bit 3 picks which of the two it keeps; the partner lane^8 sends the other
+  const bool b3 = (__lane_id() & 8) != 0;
+  const float keep = b3 ? c2[1] : c2[0];
+  const float send = b3 ? c2[0] : c2[1];
+  const float t = keep + dpp<kDppRowRor8>(send);
+  return segment_sum16(t, 8);
+}
+
+// One item: the group sums of its pairs' h slices, the eight row dots, the
+// wave sums, and the rows' outputs into ylds[pair][row] (live pairs only).
+template <int NTOK>
+__device__ __forceinline__ void down_compute(const FfnArgs& a, const DecMeta& m, int u, int lane,
+                                             const DnItem<NTOK>& it, float* ylds) {
+  const int pb = uniform(m.offsets[u]), ne = uniform(m.offsets[u + 1]) - pb;
+  float sc[kDnRows], bi[kDnRows];
+#pragma unroll
+  for (int r = 0; r < kDnRows; ++r) {
+    sc[r] = bf16_to_f32((uint16_t)it.s[r]);
+    bi[r] = bf16_to_f32((uint16_t)it.b[r]);
+  }
+  const half2_t one = {(half_t)1.0f, (half_t)1.0f};
+  const half2_t sixteen = {(half_t)16.0f, (half_t)16.0f};
+#pragma unroll
+  for (int q = 0; q < NTOK; ++q) {
+    // slot z of a chunk holds (x_z, x_{z+4}), odd z pre-divided by 16: S sums
+    // the stored halves (the 1024 offsets of the dequantised nibbles), X the
+    // true values (the bias term)
+    float S = 0.f, X = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t hw[4] = {it.h[q][k].x, it.h[q][k].y, it.h[q][k].z, it.h[q][k].w};
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        const half2_t hv = __builtin_bit_cast(half2_t, hw[z]);
+        S = __builtin_amdgcn_fdot2(hv, one, S, false);
+        X = __builtin_amdgcn_fdot2(hv, (z & 1) ? sixteen : one, X, false);
+      }
+    }
+    const float S1024 = 1024.0f * S;
+    float part[kDnRows];
+#pragma unroll
+    for (int r = 0; r < kDnRows; ++r) {
+      float acc = 0.f;
+      acc = dot_word(it.w[r].x, it.h[q][0], acc);
+      acc = dot_word(it.w[r].y, it.h[q][1], acc);
+      acc = dot_word(it.w[r].z, it.h[q][2], acc);
+      acc = dot_word(it.w[r].w, it.h[q][3], acc);
+      part[r] = sc[r] * (acc - S1024) + bi[r] * X;
+    }
+    const float y = rows8_wave_sum(part);
+    if (q < ne && (lane & 7) == 0) {
+      const int p = uniform(m.pairs[pb + q]);
+      ylds[p * kDnRows + (lane >> 3)] = y;
+    }
+  }
 }
 
 // Routing metadata -> LDS (union arrays hold min(E, P) experts).
@@ -475,74 +558,16 @@ flush:
   }
 }
 
-// One row block: every (expert, row step) item of rows r0..r0+7 against the
-// staged h, then the weighted combine of those rows.  `w`/`sraw`/`braw` hold
-// the first batch of items (loaded by the caller); larger unions reload.
-template <int GPL, int IPW = items_per_wave<GPL>()>
-__device__ __forceinline__ void down_row_block(const FfnArgs& a, const DecMeta& m, int r0, int wave,
-                                               int items, int steps, int rps, int slot, int li,
-                                               int tpr, int C, int G, const uint4* hx,
-                                               const float2* hsum, float* ylds,
-                                               uint4 (&w)[IPW][GPL][2],
-                                               uint32_t (&sraw)[IPW][GPL],
-                                               uint32_t (&braw)[IPW][GPL], bool have_res,
-                                               float res_pref) {
-  for (int first = wave; first < items; first += kDnWaves * IPW) {
-    if (first != wave)
-      down_load_items<GPL>(a, m, first, items, steps, rps, slot, li, r0, C, G, w, sraw, braw);
-#pragma unroll
-    for (int q = 0; q < IPW; ++q) {
-      const int it = first + q * kDnWaves;
-      if (it < items) {   // uniform across the wave
-        const int uu = uniform(it / steps), st = it % steps;
-        const int pb = uniform(m.offsets[uu]), ne = uniform(m.offsets[uu + 1]) - pb;
-        const int rr = st * rps + slot;
-        float sc[GPL], bi[GPL];
-#pragma unroll
-        for (int gi = 0; gi < GPL; ++gi) {
-          sc[gi] = bf16_to_f32((uint16_t)sraw[q][gi]);
-          bi[gi] = bf16_to_f32((uint16_t)braw[q][gi]);
-        }
-        for (int j = 0; j < ne; ++j) {
-          const int p = uniform(m.pairs[pb + j]);
-          const uint4* xc = hx + (size_t)p * C + li * 8;
-          const float2* xsm = hsum + (size_t)p * G + li;
-          float part = lane_row_dot<GPL>(w[q], sc, bi, xc, xsm, tpr);
-          part = segment_sum(part, tpr);
-          if (li == 0 && rr < kDnRows) ylds[p * kDnRows + rr] = part;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  // combine: out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k ascending
-  const int K = a.K;
-  if (threadIdx.x < a.B * kDnRows) {
-    const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
-    float acc = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int p = t * K + k;
-      if (m.pos[p] < 0) continue;
-      acc += m.w[p] * ylds[p * kDnRows + rr];
-    }
-    const int64_t o = (int64_t)t * a.d + r0 + rr;
-    const float res = have_res ? res_pref : (a.residual ? a.residual[o] : 0.f);
-    a.out[o] = res + acc;
-  }
-  __syncthreads();                                 // ylds is free again
-}
-
-// grid: two 4-wave blocks per compute unit (at most one per row block);
+// grid: two 8-wave blocks per compute unit (at most one per row block);
 // block b takes row blocks b, b + grid, ... of 8 output rows x all union
-// experts.
-template <int GPL>
+// experts, one (union slot, row block) item per wave, and ends each row block
+// with the weighted combine of its rows in rank order.
+template <int NTOK>
 __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
-  constexpr int IPW = items_per_wave<GPL>();
   __shared__ DecMeta m;
-  extern __shared__ __align__(16) char smem[];
+  __shared__ float ylds[kMaxDecPairs * kDnRows];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int P = a.B * a.K;
   // the first row block's residual, fetched before anything waits
   float res_pref = 0.f;
   if (a.residual != nullptr && threadIdx.x < a.B * kDnRows)
@@ -550,75 +575,46 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
                           threadIdx.x % kDnRows];
   load_meta(a, m);
   const int nU = uniform(m.n_union);
-  const int f = a.f, G = f / 64, C = f / 8;
-  const int hx_chunks = (P * C + 63) / 64 * 64;
-  uint4* hx = reinterpret_cast<uint4*>(smem);                          // [P][C]
-  float2* hsum = reinterpret_cast<float2*>(hx + hx_chunks);            // [P][G]
-  float* ylds = reinterpret_cast<float*>(hsum + (size_t)P * G);        // [P][kDnRows]
-  const int tpr = G / GPL, rps = 64 / tpr;
-  const int li = lane % tpr, slot = lane / tpr;
-  const int steps = (kDnRows + rps - 1) / rps;
-  const int items = nU * steps;
+  const int C = a.f / 8, G = a.f / 64, NL = C / 4;
+  const bool lane_live = lane < NL;
+  const int L = lane_live ? lane : NL - 1;
   const int n_rb = a.d / kDnRows;
-  const int stride = gridDim.x;
-
-  // h of every pair (written by gate_up, L2-resident) is requested first with
-  // ordinary loads, then the first row block's weights: the wait for h then
-  // leaves the weight loads in flight while the group sums are formed
-  uint4 w0[IPW][GPL][2];
-  uint32_t s0[IPW][GPL], b0[IPW][GPL];
-  const int nchunk = P * C;
-  const uint4* hsrc = reinterpret_cast<const uint4*>(a.hp);
-  // three chunks a thread held in named registers (an array here ends up in
-  // scratch), clamped to the last chunk past the end
-  const int hi0 = threadIdx.x;
-  const uint4 h0 = hsrc[min(hi0 + 0 * kDnThreads, nchunk - 1)];
-  const uint4 h1 = hsrc[min(hi0 + 1 * kDnThreads, nchunk - 1)];
-  const uint4 h2 = hsrc[min(hi0 + 2 * kDnThreads, nchunk - 1)];
-  __builtin_amdgcn_sched_barrier(0);
-  int rb = blockIdx.x;
-  down_load_items<GPL>(a, m, wave, items, steps, rps, slot, li, rb * kDnRows, C, G, w0, s0, b0);
-  // (threads past the end rewrite chunk nchunk-1 with the value it already has)
-  hx[min(hi0 + 0 * kDnThreads, nchunk - 1)] = h0;
-  hx[min(hi0 + 1 * kDnThreads, nchunk - 1)] = h1;
-  hx[min(hi0 + 2 * kDnThreads, nchunk - 1)] = h2;
-  for (int i = threadIdx.x + kHRegs * kDnThreads; i < nchunk; i += kDnThreads) hx[i] = hsrc[i];
-  __syncthreads();
-  // group sums (X, C) of h: one (pair, group) per thread, 8 chunks of 8 halves
-  for (int i = threadIdx.x; i < P * G; i += kDnThreads) {
-    const uint4* hc = hx + (size_t)(i / G) * C + (i % G) * 8;
-    float X = 0.f, S = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 v = hc[c];
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        // slot z of the chunk holds (x_z, x_{z+4}); odd z are pre-divided by 16
-        const float lo = (float)bits_f16((uint16_t)(wv[z] & 0xFFFFu));
-        const float hi = (float)bits_f16((uint16_t)(wv[z] >> 16));
-        S += lo + hi;
-        X += (z & 1) ? 16.0f * (lo + hi) : (lo + hi);
-      }
+  const int K = a.K;
+  for (int rb = blockIdx.x; rb < n_rb; rb += gridDim.x) {
+    const int r0 = rb * kDnRows;
+    for (int u = wave; u < nU; u += kDnWaves) {
+      DnItem<NTOK> it;
+      down_load<NTOK>(a, m, u, r0, L, lane_live, C, G, it);
+      down_compute<NTOK>(a, m, u, lane, it, ylds);
     }
-    hsum[i] = make_float2(X, 1024.0f * S);
-  }
-  __syncthreads();
-
-  for (; rb < n_rb; rb += stride) {
-    if (rb != (int)blockIdx.x)
-      down_load_items<GPL>(a, m, wave, items, steps, rps, slot, li, rb * kDnRows, C, G, w0, s0,
-                           b0);
-    down_row_block<GPL>(a, m, rb * kDnRows, wave, items, steps, rps, slot, li, tpr, C, G, hx,
-                        hsum, ylds, w0, s0, b0, rb == (int)blockIdx.x, res_pref);
+    __syncthreads();
+    // combine: out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k
+    // ascending; a batch of eight pairs' values is read before it is summed
+    if (threadIdx.x < a.B * kDnRows) {
+      const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
+      float acc = 0.f;
+      for (int k0 = 0; k0 < K; k0 += 8) {
+        float yv[8], wv[8];
+        int pv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = t * K + min(k0 + j, K - 1);
+          pv[j] = m.pos[p];
+          wv[j] = m.w[p];
+          yv[j] = ylds[p * kDnRows + rr];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (k0 + j < K && pv[j] >= 0) acc += wv[j] * yv[j];
+      }
+      const int64_t o = (int64_t)t * a.d + r0 + rr;
+      const float res = rb == (int)blockIdx.x ? res_pref : (a.residual ? a.residual[o] : 0.f);
+      a.out[o] = res + acc;
+    }
+    __syncthreads();                               // ylds is free again
   }
 }
 
-int gpl_of(int G) {
-  int t = 1;
-  while (t < 64 && G % (2 * t) == 0) t *= 2;
-  return G / t;
-}
 
 // Compute units of the current device, cached per device (an attribute
 // lookup, not state of any call).
@@ -661,34 +657,29 @@ hipError_t launch_gate_up_any(const FfnArgs& a, const DecodeRoute& r, hipStream_
                      : launch_gate_up_gemv<2, 32, kRoute>(a, r, s, t);
 }
 
-template <int GPL>
+template <int NTOK>
 hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
   const int ncu = cu_count();
   if (ncu <= 0) return hipErrorInvalidDevice;
   const int grid = std::min(a.d / kDnRows, ncu * kDnBlocksPerCU);
-  SMOE_LAUNCH(t, k_down_combine_gemv<GPL>, dim3(grid), dim3(kDnThreads), decode_smem(a), s, a);
+  SMOE_LAUNCH(t, k_down_combine_gemv<NTOK>, dim3(grid), dim3(kDnThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 // The decode path applies to B <= 2 tokens (B*K <= 16) with d = 2048 or 4096
-// (one gate_up group per lane, 32 or 64 lanes a row), f/64 split into 1-3
-// groups per lane, and the staged h within 64 KB of LDS.
+// (one gate_up group per lane, 32 or 64 lanes a row) and f <= 2048 (a down
+// row's words spread over at most 64 lanes, four a lane).
 bool gemv_path_ok(const FfnArgs& a) {
   if (a.B < 1 || a.B > 2 || a.B * a.K > kMaxDecPairs) return false;
   if (a.d != 2048 && a.d != 4096) return false;
-  if (gpl_of(a.f / 64) > 3 || a.f % kJ != 0 || a.d % kDnRows != 0) return false;
-  return decode_smem(a) <= 64 * 1024;
+  return a.f % 64 == 0 && a.f <= kDnMaxF && a.f % kJ == 0 && a.d % kDnRows == 0;
 }
 
 hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {
   if (gate_up) return launch_gate_up_any<false>(a, DecodeRoute{}, s, t);
-  switch (gpl_of(a.f / 64)) {
-    case 1: return launch_down_gemv<1>(a, s, t);
-    case 2: return launch_down_gemv<2>(a, s, t);
-    default: return launch_down_gemv<3>(a, s, t);
-  }
+  return a.B == 1 ? launch_down_gemv<1>(a, s, t) : launch_down_gemv<2>(a, s, t);
 }
 
 hipError_t launch_gate_up_routed(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
