@@ -9,23 +9,23 @@
 // each time:
 //
 //  k_gate_up_gemv: one item per wave (union expert, two consecutive j: 2 gate
-//    rows + 2 up rows, 8 KB at d = 4096), all of its loads issued before any
-//    arithmetic; h_j = silu(g_j) * u_j ("SSD Streaming Expert Layers", "Math
-//    Contract") is written as prepped fp16.
-//  k_down_combine_gemv: a block owns 8 output rows for ALL union experts.  It
-//    issues those rows' weight loads first, copies h of all pairs into LDS
-//    meanwhile, and finishes with the weighted combine of its rows in rank
-//    order ("Data Flow": gather outputs x routing weights, residual += ...),
-//    so y never leaves the chip.
+//    rows + 2 up rows, 8 KB at d = 4096), streamed through a two-item ring;
+//    h_j = silu(g_j) * u_j ("SSD Streaming Expert Layers", "Math Contract")
+//    is written as prepped fp16.
+//  k_down_combine_gemv: a block owns 8 output rows for ALL union experts, one
+//    (union expert, 8 rows) item per wave, and finishes with the weighted
+//    combine of its rows in rank order ("Data Flow": gather outputs x routing
+//    weights, residual += ...), so y never leaves the chip.
 //
 // Both kernels stage the call's routing metadata (at most 16 pairs) in LDS
 // first, so no dependent global load sits inside their loops.
 //
-// Lane layout: a row of G groups (64 inputs each) is spread over TPR lanes,
-// lane li owning the GPL groups li, li + TPR, li + 2 TPR (so that one load
-// instruction reads adjacent group halves), and one wave instruction covers
-// 64/TPR rows.  gate_up rows have one group per lane (TPR = d/64, 32 or 64);
-// down rows GPL = 1..3.
+// Lane layouts.  gate_up: a row's d/64 groups (64 inputs each) over TPR =
+// d/64 lanes (32 or 64), one group a lane, 64/TPR rows per wave instruction.
+// down: lane L owns words 4L .. 4L+3 (32 inputs) of every row and the
+// matching slice of h, so that a lane reads its h once per item and uses it
+// for all 8 rows; the row sums then come from one transpose-reduce over the
+// wave.
 #include <algorithm>
 
 #include "device.hpp"
