@@ -325,10 +325,13 @@ __device__ __forceinline__ void topk_keys(const float (&v)[4], int E, uint32_t (
   for (int j = 0; j < 4; ++j) key[j] = (j < NJ && lane + 64 * j < E) ? order_key(v[j]) : 0u;
 }
 
-// Steps 2 and 3 of wave_topk_sel for one row, given its threshold t.
+// Step 2 of wave_topk_sel for one row, given its threshold t: the keys above
+// t, plus the lowest-index keys equal to t up to K in all, are copied in
+// expert order to the wave's scratch (and, when `order` is not null, their
+// experts to order[0 .. K-1]).
 template <int NJ>
-__device__ __forceinline__ TopkSel topk_finish(const float (&v)[4], const uint32_t (&key)[4],
-                                               uint32_t t, int K, TopkScratch* sc) {
+__device__ __forceinline__ void topk_compact(const float (&v)[4], const uint32_t (&key)[4],
+                                             uint32_t t, int K, TopkScratch* sc, int* order) {
   const int lane = __lane_id();
   uint64_t gt[4], eq[4];
 #pragma unroll
@@ -357,9 +360,17 @@ __device__ __forceinline__ TopkSel topk_finish(const float (&v)[4], const uint32
       sc->key[p] = key[j];
       sc->e[p] = lane + 64 * j;
       sc->v[p] = v[j];
+      if (order != nullptr) order[p] = lane + 64 * j;
     }
     taken += __popcll(ms[j]);
   }
+}
+
+// Step 3 of wave_topk_sel: each of the K selected entries in the wave's
+// scratch (written by topk_compact of this wave) ranks itself against the
+// other K-1 and is sent to the lane of its rank (ds_permute).
+__device__ __forceinline__ TopkSel topk_rank(int K, TopkScratch* sc) {
+  const int lane = __lane_id();
   // a wave's LDS accesses execute in order; keep the compiler from moving the
   // reads above the writes
   asm volatile("" ::: "memory");
@@ -386,6 +397,14 @@ __device__ __forceinline__ TopkSel topk_finish(const float (&v)[4], const uint32
   out.my_e = mine ? pe : 0;
   out.my_v = mine ? pv : 0.f;
   return out;
+}
+
+// Steps 2 and 3 of wave_topk_sel for one row, given its threshold t.
+template <int NJ>
+__device__ __forceinline__ TopkSel topk_finish(const float (&v)[4], const uint32_t (&key)[4],
+                                               uint32_t t, int K, TopkScratch* sc) {
+  topk_compact<NJ>(v, key, t, K, sc, nullptr);
+  return topk_rank(K, sc);
 }
 
 // Top-k of one row of E <= 64 * NJ logits by one full wave (v[j] = logit of

@@ -105,12 +105,39 @@ struct GuBuf {
   uint32_t s[kSteps], b[kSteps];
 };
 
+// Per-lane byte offsets of a gate_up item's loads, the same for every item:
+// step k covers rows rs = k kRps + slot (gate j0 + rs, or up j0 + rs - kJ).
+template <int TPR>
+struct GuLane {
+  uint32_t w[GuBuf<TPR>::kSteps];   // packed words, first 16 bytes
+  uint32_t s[GuBuf<TPR>::kSteps];   // scale and bias (bf16)
+};
+template <int TPR>
+__device__ __forceinline__ GuLane<TPR> gu_lane(const FfnArgs& a, int lane) {
+  constexpr int kRps = 64 / TPR;
+  const int G = a.d / 64, C = a.d / 8;
+  const int li = lane % TPR, slot = lane / TPR;
+  GuLane<TPR> o;
+#pragma unroll
+  for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
+    const int r = (k * kRps + slot) % kJ;           // row within the item's kJ
+    o.w[k] = (uint32_t)(r * C + li * 8) * 4;
+    o.s[k] = (uint32_t)(r * G + li) * 2;
+  }
+  return o;
+}
+
+// Issue the loads of one item.  Everything that changes from item to item
+// (expert, rows, past-the-end) lives in the buffer resources, which are
+// scalar: the loop writes no vector register before these loads, so the
+// compiler has no reason to wait for the previous item's loads first.  An
+// item past the end gets empty resources: its loads return zeros and touch
+// no memory.
 template <int TPR>
 __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int item, int n_items,
-                                        int lane, GuBuf<TPR>& buf) {
+                                        const GuLane<TPR>& lo, GuBuf<TPR>& buf) {
   constexpr int kRps = 64 / TPR;
   const int per = a.f / kJ;
-  // an item past the end keeps a valid expert and loads at a dead offset
   const bool live = item < n_items;
   const int itc = live ? item : n_items - 1;
   const int u = uniform(itc / per);
@@ -119,25 +146,22 @@ __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int i
   // temporary register is written while the ring's loads are in flight)
   const int e = __builtin_amdgcn_readlane(lane_expert, u);
   const int G = a.d / 64, C = a.d / 8;
-  const int li = lane % TPR, slot = lane / TPR;
-  const uint32_t wbytes = (uint32_t)a.f * C * 4, sbytes = (uint32_t)a.f * G * 2;
-  const auto gw = buffer_rsrc(a.gate.w + e * a.gate.stride_w, wbytes);
-  const auto gs = buffer_rsrc(a.gate.s + e * a.gate.stride_sb, sbytes);
-  const auto gb = buffer_rsrc(a.gate.b + e * a.gate.stride_sb, sbytes);
-  const auto uw = buffer_rsrc(a.up.w + e * a.up.stride_w, wbytes);
-  const auto us = buffer_rsrc(a.up.s + e * a.up.stride_sb, sbytes);
-  const auto ub = buffer_rsrc(a.up.b + e * a.up.stride_sb, sbytes);
+  const uint32_t wbytes = live ? (uint32_t)(kJ * C * 4) : 0u;
+  const uint32_t sbytes = live ? (uint32_t)(kJ * G * 2) : 0u;
+  const int64_t wr = (int64_t)j0 * C, sr = (int64_t)j0 * G;
+  const auto gw = buffer_rsrc(a.gate.w + e * a.gate.stride_w + wr, wbytes);
+  const auto gs = buffer_rsrc(a.gate.s + e * a.gate.stride_sb + sr, sbytes);
+  const auto gb = buffer_rsrc(a.gate.b + e * a.gate.stride_sb + sr, sbytes);
+  const auto uw = buffer_rsrc(a.up.w + e * a.up.stride_w + wr, wbytes);
+  const auto us = buffer_rsrc(a.up.s + e * a.up.stride_sb + sr, sbytes);
+  const auto ub = buffer_rsrc(a.up.b + e * a.up.stride_sb + sr, sbytes);
 #pragma unroll
   for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
-    const int rs = k * kRps + slot;                 // < kGuRows: kRps divides it
-    const bool is_up = rs >= kJ;
-    const uint32_t row = j0 + (rs % kJ);
-    const uint32_t wo = live ? (row * C + li * 8) * 4 : kBufferDead;
-    const uint32_t so = live ? (row * G + li) * 2 : kBufferDead;
-    buf.w[k][0] = buf_load4_nt(is_up ? uw : gw, wo);
-    buf.w[k][1] = buf_load4_nt(is_up ? uw : gw, wo + 16);
-    buf.s[k] = buf_load_u16(is_up ? us : gs, so);
-    buf.b[k] = buf_load_u16(is_up ? ub : gb, so);
+    const bool is_up = k * kRps >= kJ;             // rows k kRps ..: gate rows, then up rows
+    buf.w[k][0] = buf_load4_nt(is_up ? uw : gw, lo.w[k]);
+    buf.w[k][1] = buf_load4_nt(is_up ? uw : gw, lo.w[k] + 16);
+    buf.s[k] = buf_load_u16(is_up ? us : gs, lo.s[k]);
+    buf.b[k] = buf_load_u16(is_up ? ub : gb, lo.s[k]);
   }
   // keep every load of the item here: left to itself the scheduler sinks the
   // scale/bias loads to their first use, after the next item's loads, which
@@ -360,35 +384,33 @@ struct RouteKeep {
 
 template <int NTOK>
 __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& r, DecMeta& m,
-                                           RouteKeep& keep) {
+                                           RouteKeep& keep, TopkScratch* tks) {
   __shared__ int s_e[kMaxDecPairs];
   __shared__ float s_w[kMaxDecPairs];
-  __shared__ TopkScratch tks[2];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int E = a.E, K = a.K, P = a.B * a.K;
   if (NTOK == 1) {
     // one token: its K experts are distinct, so the union is the selected set
-    // in ascending expert order (as wave_topk_sel leaves it) and union slot q
-    // holds the one pair of that expert, the pair of its rank
+    // in ascending expert order and union slot q holds the one pair of that
+    // expert, the pair of its rank.  The items need only the set, so the
+    // ranks (route_rank) are left until the first items' loads are out.
     if (wave == 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = lane + 64 * j;
         keep.v[j] = e < E ? r.logits[e] : -FLT_MAX;
       }
-      keep.t = E <= 128 ? wave_topk_sel<2>(keep.v, E, K, &tks[0])
-                        : wave_topk_sel<4>(keep.v, E, K, &tks[0]);
-      if (lane < K) {
-        m.experts[lane] = keep.t.se;
-        m.offsets[lane] = lane;
-        m.pairs[lane] = keep.t.srank;
-        m.pos[keep.t.srank] = lane;
+      uint32_t key[4];
+      if (E <= 128) {
+        topk_keys<2>(keep.v, E, key);
+        topk_compact<2>(keep.v, key, topk_threshold<2>(key, K), K, tks, m.experts);
+      } else {
+        topk_keys<4>(keep.v, E, key);
+        topk_compact<4>(keep.v, key, topk_threshold<4>(key, K), K, tks, m.experts);
       }
-      if (lane == 0) {
-        m.n_union = K;
-        m.offsets[K] = K;
-      }
+      if (lane <= K) m.offsets[lane] = lane;
+      if (lane == 0) m.n_union = K;
     }
     __syncthreads();
     return;
@@ -464,6 +486,18 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
   __syncthreads();
 }
 
+// One token's ranks (wave 0, after route_meta<1> and its topk_compact):
+// the pair of each union slot, for the h flush, and what block 0 writes at
+// the kernel's end.
+__device__ __forceinline__ void route_rank(int K, DecMeta& m, RouteKeep& keep, TopkScratch* tks) {
+  const int lane = __lane_id();
+  keep.t = topk_rank(K, tks);
+  if (lane < K) {
+    m.pairs[lane] = keep.t.srank;
+    m.pos[keep.t.srank] = lane;
+  }
+}
+
 // grid: one 4-wave block per compute unit (at most one wave per item).  Wave
 // w takes items w, w + W, w + 2W, ...; the next item's loads go out before
 // the current one is computed, so each wave streams its share with one item
@@ -471,18 +505,28 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
 template <int NTOK, int TPR, bool kRoute>
 __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeRoute r) {
   __shared__ DecMeta m;
+  __shared__ TopkScratch tks[2];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  // one routed token: the block's pairs are ranked by wave 0 once its first
+  // items are in flight, and published to the flush by a barrier
+  constexpr bool kLateRank = kRoute && NTOK == 1;
   RouteKeep keep;
   if (kRoute)
-    route_meta<NTOK>(a, r, m, keep);
+    route_meta<NTOK>(a, r, m, keep, tks);
   else
     load_meta(a, m);
   const int nU = uniform(m.n_union);
   const int n_items = nU * (a.f / kJ);
   const int W = gridDim.x * kDecWaves;
   const int wid = blockIdx.x * kDecWaves + wave;
-  if (wid >= n_items) return;                     // no barrier follows
+  if (wid >= n_items) {
+    // no items; with kLateRank the wave still joins the barrier before the
+    // flush (a block's wave 0 has the lowest wid, so it has items whenever
+    // any wave of the block has)
+    if (kLateRank) __syncthreads();
+    return;
+  }
   // this lane's group of every token's prepped activations, loaded first:
   // they are few and cached, and the weight loads queue behind them
   const int G = a.d / 64, li = lane % TPR;
@@ -506,23 +550,26 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   // waits for it (and so for every load before it) before reusing its data
   // registers.  The grid gives every wave at most kGuMaxItems items.
   __shared__ uint16_t hst[kDecWaves][kGuMaxItems][kJ * NTOK];
+  const GuLane<TPR> lo = gu_lane<TPR>(a, lane);
   GuBuf<TPR> b[kGuDepth];
 #pragma unroll
   for (int s = 0; s < kGuDepth - 1; ++s)
-    gu_load<TPR>(a, lane_expert, wid + s * W, n_items, lane, b[s]);
+    gu_load<TPR>(a, lane_expert, wid + s * W, n_items, lo, b[s]);
   for (int i = wid, loc = 0;; i += kGuDepth * W) {
 #pragma unroll
     for (int s = 0; s < kGuDepth; ++s, ++loc) {
       const int it = i + s * W;
       if (it >= n_items) goto flush;
-      gu_load<TPR>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, lane,
+      gu_load<TPR>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, lo,
                    b[(s + kGuDepth - 1) % kGuDepth]);
+      if (kLateRank && wave == 0 && loc == 0) route_rank(a.K, m, keep, tks);
       gu_compute<NTOK, TPR>(a, m, it, lane, b[s], xr, xs, hst[wave][loc]);
     }
   }
 flush:
+  if (kLateRank) __syncthreads();                 // wave 0's ranks (m.pairs)
   {
-    // the wave's own LDS rows: no barrier, the wave's LDS accesses are ordered
+    // the wave's own LDS rows: the wave's LDS accesses are ordered
     const int n_mine = (n_items - wid + W - 1) / W;
     const int per = a.f / kJ;
     for (int q = lane; q < n_mine * kJ * NTOK; q += 64) {
