@@ -211,7 +211,7 @@ __device__ __forceinline__ int wave_min_i(int v) {
 
 // Per-wave LDS scratch of wave_topk: the K selected entries in expert order.
 constexpr int kTopkMax = 16;
-struct TopkScratch {
+struct alignas(16) TopkScratch {
   uint32_t key[kTopkMax];
   int e[kTopkMax];
   float v[kTopkMax];
@@ -379,12 +379,23 @@ __device__ __forceinline__ TopkSel topk_rank(int K, TopkScratch* sc) {
   const uint32_t qk = sc->key[ql];
   const int qe = sc->e[ql];
   const float qv = sc->v[ql];
+  // all K entries by 16-byte broadcast reads issued together (entries past K
+  // are stale and masked), then a branch-free count
+  uint4 k4[kTopkMax / 4], e4[kTopkMax / 4];
+#pragma unroll
+  for (int i = 0; i < kTopkMax / 4; ++i) {
+    k4[i] = reinterpret_cast<const uint4*>(sc->key)[i];
+    e4[i] = reinterpret_cast<const uint4*>(sc->e)[i];
+  }
   int rank = 0;
 #pragma unroll
   for (int r = 0; r < kTopkMax; ++r) {
-    const uint32_t kr = sc->key[r];               // past K: stale, masked below
-    const int er = sc->e[r];
-    rank += (r < K && (kr > qk || (kr == qk && er < qe))) ? 1 : 0;
+    const uint4& kq = k4[r / 4];
+    const uint4& eq = e4[r / 4];
+    const uint32_t kr = (r % 4 == 0) ? kq.x : (r % 4 == 1) ? kq.y : (r % 4 == 2) ? kq.z : kq.w;
+    const int er = (int)((r % 4 == 0) ? eq.x : (r % 4 == 1) ? eq.y : (r % 4 == 2) ? eq.z : eq.w);
+    const int before = (int)(kr > qk) | ((int)(kr == qk) & (int)(er < qe));
+    rank += (r < K) ? before : 0;
   }
   asm volatile("" ::: "memory");                  // the scratch may be reused after this
   const int dst = mine ? rank : lane;             // a permutation of the lanes
