@@ -486,16 +486,14 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
   __syncthreads();
 }
 
-// One token's ranks (wave 0, after route_meta<1> and its topk_compact):
-// the pair of each union slot, for the h flush, and what block 0 writes at
-// the kernel's end.
-__device__ __forceinline__ void route_rank(int K, DecMeta& m, RouteKeep& keep, TopkScratch* tks) {
-  const int lane = __lane_id();
+// One token's ranks, from the selection route_meta<1> left in the scratch:
+// every wave ranks for itself (the pair of each union slot, for its own h
+// flush, into its own LDS row), so that no barrier is needed; block 0's wave
+// 0 also keeps what it writes at the kernel's end.
+__device__ __forceinline__ void route_rank(int K, int* slot_pair, RouteKeep& keep,
+                                           TopkScratch* tks) {
   keep.t = topk_rank(K, tks);
-  if (lane < K) {
-    m.pairs[lane] = keep.t.srank;
-    m.pos[keep.t.srank] = lane;
-  }
+  if (__lane_id() < K) slot_pair[__lane_id()] = keep.t.srank;
 }
 
 // grid: one 4-wave block per compute unit (at most one wave per item).  Wave
@@ -508,9 +506,10 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   __shared__ TopkScratch tks[2];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  // one routed token: the block's pairs are ranked by wave 0 once its first
-  // items are in flight, and published to the flush by a barrier
+  // one routed token: each wave ranks the selected experts once its first
+  // items are in flight (route_rank)
   constexpr bool kLateRank = kRoute && NTOK == 1;
+  __shared__ int slot_pair[kDecWaves][kMaxDecPairs];
   RouteKeep keep;
   if (kRoute)
     route_meta<NTOK>(a, r, m, keep, tks);
@@ -520,13 +519,7 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   const int n_items = nU * (a.f / kJ);
   const int W = gridDim.x * kDecWaves;
   const int wid = blockIdx.x * kDecWaves + wave;
-  if (wid >= n_items) {
-    // no items; with kLateRank the wave still joins the barrier before the
-    // flush (a block's wave 0 has the lowest wid, so it has items whenever
-    // any wave of the block has)
-    if (kLateRank) __syncthreads();
-    return;
-  }
+  if (wid >= n_items) return;                     // no barrier follows
   // this lane's group of every token's prepped activations, loaded first:
   // they are few and cached, and the weight loads queue behind them
   const int G = a.d / 64, li = lane % TPR;
@@ -562,12 +555,11 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
       if (it >= n_items) goto flush;
       gu_load<TPR>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, lo,
                    b[(s + kGuDepth - 1) % kGuDepth]);
-      if (kLateRank && wave == 0 && loc == 0) route_rank(a.K, m, keep, tks);
+      if (kLateRank && loc == 0) route_rank(a.K, slot_pair[wave], keep, tks);
       gu_compute<NTOK, TPR>(a, m, it, lane, b[s], xr, xs, hst[wave][loc]);
     }
   }
 flush:
-  if (kLateRank) __syncthreads();                 // wave 0's ranks (m.pairs)
   {
     // the wave's own LDS rows: the wave's LDS accesses are ordered
     const int n_mine = (n_items - wid + W - 1) / W;
@@ -580,7 +572,7 @@ flush:
       const int j = (item - u * per) * kJ + jj;
       const int pb = m.offsets[u];
       if (k < m.offsets[u + 1] - pb) {
-        const int p = m.pairs[pb + k];
+        const int p = kLateRank ? slot_pair[wave][u] : m.pairs[pb + k];
         a.hp[(int64_t)p * a.f + prepped_pos(j)] = hst[wave][loc][rr];
       }
     }
