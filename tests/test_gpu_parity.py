@@ -146,6 +146,11 @@ FWD_CASES = [
     (small_config("dec_b2_e8", 2048, 8, 8, 512, 2), 2, False),          # every expert, E < B*K
     (small_config("gemv_b1", 4096, 64, 8, 1536, 1), 1, False),
     (small_config("gemv_k16", 2048, 64, 16, 512, 1), 1, True),
+    # the decode down kernel gives lane L words 4L..4L+3 of a row: f/32 lanes
+    (small_config("dec_b1_f2048", 2048, 16, 4, 2048, 1), 1, True),     # all 64 lanes
+    (small_config("dec_b2_f1024", 4096, 32, 8, 1024, 2), 2, False),    # 32 lanes
+    (small_config("dec_b1_f64", 2048, 8, 2, 64, 1), 1, True),          # 2 lanes, one group
+    (small_config("b1_f2560", 2048, 16, 4, 2560, 1), 1, True),         # past 64 lanes: MFMA path
 ]
 
 
@@ -175,6 +180,7 @@ def test_forward_parity_injected_routing(smoe, cfg, B, with_res):
                                    (small_config("l1", 1024, 64, 8, 256, 1), 1),
                                    (small_config("l_dec1", 4096, 32, 8, 256, 1), 1),
                                    (small_config("l_dec2", 2048, 64, 8, 512, 2), 2),
+                                   (small_config("l_dec1_f2048", 2048, 32, 8, 2048, 1), 1),
                                    (small_config("l_dec2_nonorm", 2048, 40, 6, 192, 2, norm=False), 2)],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_layer_parity(smoe, cfg, B):
