@@ -373,6 +373,11 @@ SMOE_API int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers,
     if (rc != SMOE_OK) return rc;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // Decode-sized layers (B <= 2) leave the norm of their output to the next
+  // layer's router, which forms the same factor as smoe_rmsnorm (the same
+  // summation order), routes the normalised rows and writes them to h: one
+  // launch fewer per layer, bit-identical results.
+  bool norm_pending = false;                      // tmp holds the raw output, h is stale
   for (int l = 0; l < n_layers; ++l) {
     smoe::RouteArgs r;
     smoe::FfnArgs a;
@@ -380,10 +385,19 @@ SMOE_API int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers,
     if (n_union != nullptr) u.n_union = n_union + l;
     layer_setup(desc, router_w[l], experts + l, h, B, h, tmp, nullptr, topk_idx + l * per_layer,
                 topk_w + l * per_layer, &u, ws, ws_bytes, &r, &a);
+    if (norm_pending) {
+      r.x = tmp;
+      r.norm_out = h;
+      r.norm_eps = eps;
+    }
     hipError_t err = launch_layer(r, a, s);
-    if (err == hipSuccess) err = smoe::launch_rmsnorm(tmp, B, desc->d_model, eps, h, s);
+    norm_pending = smoe::gemv_path_ok(a) && B <= 2;
+    if (err == hipSuccess && !norm_pending)
+      err = smoe::launch_rmsnorm(tmp, B, desc->d_model, eps, h, s);
     if (err != hipSuccess) return SMOE_EHIP;
   }
+  if (norm_pending && smoe::launch_rmsnorm(tmp, B, desc->d_model, eps, h, s) != hipSuccess)
+    return SMOE_EHIP;
   return SMOE_OK;
 }
 

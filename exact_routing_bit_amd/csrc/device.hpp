@@ -192,6 +192,43 @@ __device__ __forceinline__ float segment_sum(float v, int width) {
   return (__lane_id() < 32) ? lo : hi;
 }
 
+// Root-mean-square normalisation of one row of d floats (d % 4 == 0, d <=
+// 8192): inv = 1 / sqrt(mean(row^2) + eps), formed by a block of 256 threads
+// in one fixed order: thread i adds the squares of float4s i, i + 256, ...
+// as an fma chain (all of its loads issued first; the slots past the row
+// add fma(0, 0, s) = s), each wave's threads are summed by wave_sum, and the
+// four wave sums are added in order.  Every thread of the block must call
+// it; `part` is 4 floats of LDS; the result is the same in every thread.
+__device__ __forceinline__ float sumsq4(float ss, const float4& q) {
+  ss = __builtin_fmaf(q.x, q.x, ss);
+  ss = __builtin_fmaf(q.y, q.y, ss);
+  ss = __builtin_fmaf(q.z, q.z, ss);
+  return __builtin_fmaf(q.w, q.w, ss);
+}
+constexpr int kRowInvMaxPerThread = 8;            // 8192 / 4 / 256
+__device__ __forceinline__ float block_row_inv(const float* row, int d, float eps, float* part) {
+  const float4* r4 = reinterpret_cast<const float4*>(row);
+  const int n4 = d / 4, tid = threadIdx.x;
+  float4 q[kRowInvMaxPerThread];
+#pragma unroll
+  for (int j = 0; j < kRowInvMaxPerThread; ++j) {
+    const int i = tid + 256 * j;
+    q[j] = r4[i < n4 ? i : 0];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < kRowInvMaxPerThread; ++j) {
+    const bool in = tid + 256 * j < n4;
+    ss = sumsq4(ss, in ? q[j] : make_float4(0.f, 0.f, 0.f, 0.f));
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  __syncthreads();                                // part may be reused after this
+  return 1.0f / sqrtf(tot / (float)d + eps);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<kDppXor1>(v));
   v = fmaxf(v, dpp<kDppXor2>(v));

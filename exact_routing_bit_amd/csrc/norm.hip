@@ -11,24 +11,17 @@ namespace {
 
 constexpr int kNormThreads = 256;
 
-// One block per row: fp32 sum of squares (per-thread partials, then wave and
-// block sums in a fixed order), then the scaling.  out may alias v.
+// One block per row: the factor by block_row_inv (the order the router also
+// follows when it normalises a row itself), then the scaling.  out may alias
+// v.
 __global__ __launch_bounds__(kNormThreads) void k_rmsnorm(const float* v, int d, float eps,
                                                           float* out) {
+  static_assert(kNormThreads == 256, "block_row_inv's summation order");
   __shared__ float part[kNormThreads / 64];
   const int t = blockIdx.x;
   const float4* row = reinterpret_cast<const float4*>(v + (int64_t)t * d);
   const int n4 = d / 4;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < n4; i += kNormThreads) {
-    const float4 q = row[i];
-    ss += q.x * q.x + q.y * q.y + q.z * q.z + q.w * q.w;
-  }
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
-  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  const float inv = block_row_inv(v + (int64_t)t * d, d, eps, part);
   float4* dst = reinterpret_cast<float4*>(out + (int64_t)t * d);
   for (int i = threadIdx.x; i < n4; i += kNormThreads) {
     const float4 q = row[i];

@@ -22,6 +22,7 @@ namespace smoe {
 namespace {
 
 constexpr int kRouteThreads = 256;              // 4 waves: 4 experts per block
+static_assert(kRouteThreads == 256, "block_row_inv needs blocks of 256 threads");
 constexpr int kTokensPerWave = 2;
 constexpr int kTailThreads = 1024;              // stand-alone top-k / union block
 constexpr int kTopkThreads = 256;               // top-k grid: one token per wave
@@ -29,13 +30,24 @@ constexpr int kMaxTicketBlocks = 64;            // larger grids hand the tail to
 
 // Prepped activations of one (token, 64-input group): 8 chunks + group sums.
 // All 16 loads are issued before the first store (a store between them would
-// keep the compiler from hoisting the next loads above it).
-__device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, float2* xs) {
+// keep the compiler from hoisting the next loads above it).  With norm_out,
+// the group is first scaled by inv (the token's RMSNorm factor) and the
+// scaled values are also written to norm_out.
+__device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, float2* xs,
+                           float* norm_out, float inv) {
   const float4* src = reinterpret_cast<const float4*>(x + (int64_t)t * d + g * 64);
   uint4* dst = reinterpret_cast<uint4*>(xp + (int64_t)t * d + g * 64);
   float4 v4[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) v4[c] = src[c];
+  if (norm_out != nullptr) {
+    float4* hn = reinterpret_cast<float4*>(norm_out + (int64_t)t * d + g * 64);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      v4[c] = make_float4(v4[c].x * inv, v4[c].y * inv, v4[c].z * inv, v4[c].w * inv);
+      hn[c] = v4[c];
+    }
+  }
   float X = 0.f, S = 0.f;
   uint4 out[8];
 #pragma unroll
@@ -159,57 +171,112 @@ __device__ __forceinline__ void route_tail(const RouteArgs& a, bool do_topk, boo
   build_union(a, us);
 }
 
+// Gate values of expert e for input chunk c0 .. c0 + 4095 (one wave): lane l
+// holds inputs c0 + 8 l + 512 m .. + 7, m < 8 (zeros past d).
+template <bool kBf16>
+__device__ __forceinline__ void gate_chunk(const RouteArgs& a, int e, int c0, float (&wv)[8][8]) {
+  const int lane = __lane_id();
+  const int d = a.d;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int i = c0 + lane * 8 + 512 * m;
+    const bool ok = i < d;
+    const int64_t at = (int64_t)e * d + (ok ? i : 0);
+    if (kBf16) {
+      const uint4 raw = *reinterpret_cast<const uint4*>((const uint16_t*)a.router_w + at);
+      const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        wv[m][2 * z] = ok ? __uint_as_float(r4[z] << 16) : 0.f;
+        wv[m][2 * z + 1] = ok ? __uint_as_float(r4[z] & 0xFFFF0000u) : 0.f;
+      }
+    } else {
+      const float4* wp = reinterpret_cast<const float4*>((const float*)a.router_w + at);
+      const float4 lo = wp[0], hi = wp[1];
+      const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int z = 0; z < 8; ++z) wv[m][z] = ok ? v8[z] : 0.f;
+    }
+  }
+}
+
+// acc[j] += this lane's share of chunk c0 of sum_i Wr[e, i] x[t0 + j, i];
+// kScaled: the inputs are x * inv[j] (the tokens' RMSNorm factors), rounded
+// as smoe_rmsnorm rounds them.
+template <bool kScaled>
+__device__ __forceinline__ void dot_chunk(const RouteArgs& a, int t0, int nt, int c0,
+                                          const float (&wv)[8][8],
+                                          const float (&inv)[kTokensPerWave],
+                                          float (&acc)[kTokensPerWave]) {
+  const int lane = __lane_id();
+  const int d = a.d;
+#pragma unroll
+  for (int j = 0; j < kTokensPerWave; ++j) {
+    const int t = t0 + min(j, nt - 1);
+    float part = 0.f;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int i = c0 + lane * 8 + 512 * m;
+      const float4* xp4 = reinterpret_cast<const float4*>(a.x + (int64_t)t * d + (i < d ? i : 0));
+      float4 lo = xp4[0], hi = xp4[1];
+      if (kScaled) {
+        const float s = inv[j];
+        lo = make_float4(lo.x * s, lo.y * s, lo.z * s, lo.w * s);
+        hi = make_float4(hi.x * s, hi.y * s, hi.z * s, hi.w * s);
+      }
+      part += wv[m][0] * lo.x + wv[m][1] * lo.y + wv[m][2] * lo.z + wv[m][3] * lo.w +
+              wv[m][4] * hi.x + wv[m][5] * hi.y + wv[m][6] * hi.z + wv[m][7] * hi.w;
+    }
+    acc[j] += part;
+  }
+}
+
 // Logits of expert e for tokens t0, t0+1 (one wave).  Lanes stride the input
 // 8 elements at a time; within each 4096-element chunk every gate and input
 // load is issued before the products.
 template <bool kBf16>
 __device__ void logits_wave(const RouteArgs& a, int e, int t0, int nt) {
-  const int lane = __lane_id();
-  const int d = a.d;
+  const float inv[kTokensPerWave] = {1.f, 1.f};
   float acc[kTokensPerWave] = {};
-  for (int c0 = 0; c0 < d; c0 += 4096) {
+  for (int c0 = 0; c0 < a.d; c0 += 4096) {
     float wv[8][8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int i = c0 + lane * 8 + 512 * m;
-      const bool ok = i < d;
-      const int64_t at = (int64_t)e * d + (ok ? i : 0);
-      if (kBf16) {
-        const uint4 raw = *reinterpret_cast<const uint4*>((const uint16_t*)a.router_w + at);
-        const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          wv[m][2 * z] = ok ? __uint_as_float(r4[z] << 16) : 0.f;
-          wv[m][2 * z + 1] = ok ? __uint_as_float(r4[z] & 0xFFFF0000u) : 0.f;
-        }
-      } else {
-        const float4* wp = reinterpret_cast<const float4*>((const float*)a.router_w + at);
-        const float4 lo = wp[0], hi = wp[1];
-        const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-        for (int z = 0; z < 8; ++z) wv[m][z] = ok ? v8[z] : 0.f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kTokensPerWave; ++j) {
-      const int t = t0 + min(j, nt - 1);
-      float part = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int i = c0 + lane * 8 + 512 * m;
-        const float4* xp4 =
-            reinterpret_cast<const float4*>(a.x + (int64_t)t * d + (i < d ? i : 0));
-        const float4 lo = xp4[0], hi = xp4[1];
-        part += wv[m][0] * lo.x + wv[m][1] * lo.y + wv[m][2] * lo.z + wv[m][3] * lo.w +
-                wv[m][4] * hi.x + wv[m][5] * hi.y + wv[m][6] * hi.z + wv[m][7] * hi.w;
-      }
-      acc[j] += part;
-    }
+    gate_chunk<kBf16>(a, e, c0, wv);
+    dot_chunk<false>(a, t0, nt, c0, wv, inv, acc);
   }
 #pragma unroll
   for (int j = 0; j < kTokensPerWave; ++j) {
     const float tot = wave_sum(acc[j]);
-    if (lane == 0 && j < nt) a.logits[(int64_t)(t0 + j) * a.E + e] = tot;
+    if (__lane_id() == 0 && j < nt) a.logits[(int64_t)(t0 + j) * a.E + e] = tot;
+  }
+}
+
+// As logits_wave for a whole block (wave w: expert e0 + w) on the RMSNorm of
+// x (a.norm_out set; B <= kTokensPerWave, one grid row): each wave's first
+// gate chunk is requested, then the block forms the tokens' factors
+// (block_row_inv, as smoe_rmsnorm does), then the products.
+template <bool kBf16>
+__device__ void logits_block_normed(const RouteArgs& a, int e0, float* part) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e = e0 + wave;
+  const bool has_e = e < a.E;
+  const int nt = a.B;
+  float wv[8][8];
+  gate_chunk<kBf16>(a, has_e ? e : 0, 0, wv);
+  float inv[kTokensPerWave] = {1.f, 1.f};
+#pragma unroll
+  for (int j = 0; j < kTokensPerWave; ++j)
+    if (j < nt) inv[j] = block_row_inv(a.x + (int64_t)j * a.d, a.d, a.norm_eps, part);
+  if (!has_e) return;
+  float acc[kTokensPerWave] = {};
+  dot_chunk<true>(a, 0, nt, 0, wv, inv, acc);
+  for (int c0 = 4096; c0 < a.d; c0 += 4096) {
+    gate_chunk<kBf16>(a, e, c0, wv);
+    dot_chunk<true>(a, 0, nt, c0, wv, inv, acc);
+  }
+#pragma unroll
+  for (int j = 0; j < kTokensPerWave; ++j) {
+    const float tot = wave_sum(acc[j]);
+    if (__lane_id() == 0 && j < nt) a.logits[(int64_t)j * a.E + e] = tot;
   }
 }
 
@@ -221,16 +288,33 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
   // blocks [0, E/4) compute logits (4 experts each, kTokensPerWave tokens per
   // grid row); the blocks after them prep the activations, one (token, group)
   // unit per thread, in grid row 0, alongside the logits
+  __shared__ float part[kRouteThreads / 64];
   const int n_logit_blocks = (a.E + 3) / 4;
   if ((int)blockIdx.x < n_logit_blocks) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int e = blockIdx.x * (kRouteThreads / 64) + wave;
-    const int t0 = blockIdx.y * kTokensPerWave;
-    if (e < a.E) logits_wave<kBf16>(a, e, t0, min(kTokensPerWave, a.B - t0));
+    const int e0 = blockIdx.x * (kRouteThreads / 64);
+    if (a.norm_out != nullptr) {
+      logits_block_normed<kBf16>(a, e0, part);
+    } else {
+      const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int e = e0 + wave;
+      const int t0 = blockIdx.y * kTokensPerWave;
+      if (e < a.E) logits_wave<kBf16>(a, e, t0, min(kTokensPerWave, a.B - t0));
+    }
   } else if (a.xp != nullptr && blockIdx.y == 0) {
+    // with a.norm_out (B <= kTokensPerWave) the block forms the tokens'
+    // RMSNorm factors first (block_row_inv), then preps the scaled rows
+    float inv[kTokensPerWave] = {1.f, 1.f};
+    if (a.norm_out != nullptr) {
+#pragma unroll
+      for (int j = 0; j < kTokensPerWave; ++j)
+        if (j < a.B) inv[j] = block_row_inv(a.x + (int64_t)j * a.d, a.d, a.norm_eps, part);
+    }
     const int G = a.d / 64;
     const int u = (blockIdx.x - n_logit_blocks) * kRouteThreads + threadIdx.x;
-    if (u < a.B * G) prep_group(a.x, a.d, u / G, u % G, a.xp, a.xs);
+    if (u < a.B * G) {
+      const int t = u / G;
+      prep_group(a.x, a.d, t, u % G, a.xp, a.xs, a.norm_out, t == 0 ? inv[0] : inv[1]);
+    }
   }
   if (!do_tail) return;
   // last block: every other block's logits are visible after its release and our acquire
@@ -310,7 +394,7 @@ __global__ __launch_bounds__(256) void k_prep(const float* x, int B, int d, uint
                                               float2* xs) {
   const int G = d / 64;
   const int u = blockIdx.x * blockDim.x + threadIdx.x;
-  if (u < B * G) prep_group(x, d, u / G, u % G, xp, xs);
+  if (u < B * G) prep_group(x, d, u / G, u % G, xp, xs, nullptr, 1.f);
 }
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {

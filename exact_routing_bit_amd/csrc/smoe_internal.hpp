@@ -90,6 +90,10 @@ struct RouteArgs {
   int32_t* expert_offsets;
   int32_t* pair_list;
   int32_t* pair_pos;
+  // when non-null, x is a previous layer's raw output: the router routes
+  // RMSNorm(x) (eps norm_eps) and writes it here (B <= 2, logits + prep only)
+  float* norm_out;
+  float norm_eps;
 };
 
 struct FfnArgs {

@@ -228,6 +228,10 @@ int smoe_rmsnorm(const float* v, int32_t B, int32_t d, float eps, float* out, vo
  * ws: one workspace sized for (desc, B), shared by the layers.
  * All layers are validated before the first launch: on an error nothing is
  * launched and h is unchanged.  n_layers == 0 or B == 0 is a no-op.
+ * The results are bit-identical to that loop of smoe_moe_layer and
+ * smoe_rmsnorm calls; for decode-sized batches the norm of a layer's output
+ * is formed inside the next layer's router (the same summation order), so
+ * the stack launches one kernel fewer per layer.
  * Async on stream; eps > 0. */
 int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers, const void* const* router_w,
                        const smoe_experts* experts, float* h, int32_t B, float eps, float* tmp,
