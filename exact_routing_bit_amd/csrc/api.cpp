@@ -104,6 +104,8 @@ smoe::FfnArgs ffn_args(const smoe_layer_desc* L, const smoe_experts* ex, const s
   a.hp = ws_at<uint16_t>(ws, lay.hp);
   a.hs = ws_at<float2>(ws, lay.hs);
   a.y = ws_at<float>(ws, lay.y);
+  a.dec_meta = ws_at<int32_t>(ws, lay.meta);
+  a.dec_meta_valid = 0;
   a.status = ws_at<uint32_t>(ws, lay.status);
   return a;
 }
@@ -269,6 +271,7 @@ smoe::DecodeRoute decode_route(const smoe::RouteArgs& r) {
   d.expert_offsets = r.expert_offsets;
   d.pair_list = r.pair_list;
   d.pair_pos = r.pair_pos;
+  d.dec_meta = nullptr;
   return d;
 }
 
@@ -281,9 +284,14 @@ hipError_t launch_decode_logits(const smoe::RouteArgs& r, hipStream_t s,
 hipError_t launch_layer(const smoe::RouteArgs& r, const smoe::FfnArgs& a, hipStream_t s) {
   hipError_t err;
   if (smoe::gemv_path_ok(a)) {
+    // the routed gate_up kernel also packs the routing metadata for down
+    smoe::DecodeRoute dr = decode_route(r);
+    dr.dec_meta = a.dec_meta;
+    smoe::FfnArgs ad = a;
+    ad.dec_meta_valid = 1;
     err = launch_decode_logits(r, s);
-    if (err == hipSuccess) err = smoe::launch_gate_up_routed(a, decode_route(r), s);
-    if (err == hipSuccess) err = smoe::launch_down(a, s);
+    if (err == hipSuccess) err = smoe::launch_gate_up_routed(a, dr, s);
+    if (err == hipSuccess) err = smoe::launch_down(ad, s);
     return err;
   }
   err = smoe::launch_router(r, false, true, true, s);

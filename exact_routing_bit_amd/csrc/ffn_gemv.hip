@@ -83,7 +83,10 @@ __device__ __forceinline__ float lane_row_dot(const uint4 (&w)[GPL][2], const fl
   return part;
 }
 
-// Routing metadata of the call (at most 16 pairs), staged once in LDS.
+// Routing metadata of the call (at most 16 pairs), staged once in LDS.  The
+// routed gate_up kernel also writes it, in this layout, to FfnArgs::dec_meta,
+// so that the down kernel reads it with one load per thread instead of
+// gathering it from six arrays.
 struct DecMeta {
   int n_union;
   int experts[kMaxDecPairs];
@@ -92,6 +95,9 @@ struct DecMeta {
   int pos[kMaxDecPairs];      // pair_pos
   float w[kMaxDecPairs];      // topk_w
 };
+constexpr int kDecMetaWords = sizeof(DecMeta) / 4;
+static_assert(sizeof(DecMeta) == 4 * (5 * kMaxDecPairs + 2) && sizeof(DecMeta) <= 512,
+              "DecMeta is the packed layout of FfnArgs::dec_meta");
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -484,6 +490,9 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
     }
   }
   __syncthreads();
+  // block 0: the packed copy for the down kernel
+  if (blockIdx.x == 0 && r.dec_meta != nullptr && threadIdx.x < kDecMetaWords)
+    r.dec_meta[threadIdx.x] = reinterpret_cast<const int*>(&m)[threadIdx.x];
 }
 
 // One token's ranks, from the selection route_meta<1> left in the scratch:
@@ -594,6 +603,21 @@ flush:
       *r.n_union = K;
       r.expert_offsets[K] = K;
     }
+    if (r.dec_meta != nullptr) {
+      // the same, packed as DecMeta for the down kernel
+      DecMeta* pm = reinterpret_cast<DecMeta*>(r.dec_meta);
+      if (lane < K) {
+        pm->experts[lane] = keep.t.se;
+        pm->offsets[lane] = lane;
+        pm->pairs[lane] = keep.t.srank;
+        pm->pos[keep.t.srank] = lane;
+        pm->w[lane] = w;
+      }
+      if (lane == 0) {
+        pm->n_union = K;
+        pm->offsets[K] = K;
+      }
+    }
   }
 }
 
@@ -612,7 +636,12 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   if (a.residual != nullptr && threadIdx.x < a.B * kDnRows)
     res_pref = a.residual[(int64_t)(threadIdx.x / kDnRows) * a.d + blockIdx.x * kDnRows +
                           threadIdx.x % kDnRows];
-  load_meta(a, m);
+  if (a.dec_meta_valid) {
+    if (threadIdx.x < kDecMetaWords) reinterpret_cast<int*>(&m)[threadIdx.x] = a.dec_meta[threadIdx.x];
+    __syncthreads();
+  } else {
+    load_meta(a, m);
+  }
   const int nU = uniform(m.n_union);
   const int C = a.f / 8, G = a.f / 64, NL = C / 4;
   const bool lane_live = lane < NL;

@@ -38,6 +38,7 @@ struct WsLayout {
   size_t hp;       // [P, f] f16 prepped h
   size_t hs;       // [P, f/64, 2] float2 half-group sums of hp
   size_t y;        // [P, d] f32 per-pair expert outputs
+  size_t meta;     // 512 B: the decode kernels' packed routing metadata
   size_t total;
 };
 
@@ -59,6 +60,7 @@ inline WsLayout ws_layout(const smoe_layer_desc& L, int B) {
   w.hp = take(P * L.ffn_dim * 2);
   w.hs = take(P * (L.ffn_dim / 64) * 2 * 8);
   w.y = take(P * L.d_model * 4);
+  w.meta = take(512);
   w.total = off;
   return w;
 }
@@ -113,6 +115,10 @@ struct FfnArgs {
   float2* hs;
   float* y;
   uint32_t* status;  // workspace status area: status bits, tickets, sync counters
+  // decode kernels: the call's routing metadata in one packed block (written
+  // by the routed gate_up kernel; read by the down kernel when dec_meta_valid)
+  int32_t* dec_meta;
+  int dec_meta_valid;
 };
 
 // Routing done inside the decode gate_up kernel (smoe_moe_layer with B <= 2):
@@ -128,6 +134,7 @@ struct DecodeRoute {
   int32_t* expert_offsets;
   int32_t* pair_list;
   int32_t* pair_pos;
+  int32_t* dec_meta;       // packed copy of the routing metadata (block 0 writes it)
 };
 
 // ------------------------------------------------------------- launchers
