@@ -124,13 +124,6 @@ __device__ __forceinline__ void issue_rest(const Sources& S, char* slot, int k, 
     dma4_to_lds(align4(S.b + gB), sb + 768);
   }
 }
-template <bool kGateUp, bool kFastSB>
-__device__ __forceinline__ void issue_stage(const Sources& S, char* slot, int k, int G, int wave,
-                                            int lane) {
-  issue_words<kGateUp>(S, slot, k, G, wave, lane);
-  issue_rest<kGateUp, kFastSB>(S, slot, k, G, wave, lane);
-}
-
 // The uint4 that lane src/4 holds in v.
 __device__ __forceinline__ uint4 bpermute4(int src, const uint4& v) {
   return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)v.x),
@@ -353,10 +346,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
           wait_vmcnt<copies_of_rest<kFastSB>()>();                                                \
         else                                                                                      \
           wait_vmcnt<copies_of_stage<kFastSB>()>();                                               \
-        barrier_no_wait();           /* ... and every wave's; slot k-1 is free */                 \
+        /* this wave's words of stage k+2 go to its own part of slot k-1, which */               \
+        /* only it reads (its compute of k-1 is done): no need to wait for the others */         \
         if (k + 2 < nst)                                                                          \
-          issue_stage<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave,       \
-                                        lane);                                                    \
+          issue_words<kGateUp>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave, lane);        \
+        barrier_no_wait();           /* every wave's copies of k landed; slot k-1 is free */      \
+        if (k + 2 < nst)                                                                          \
+          issue_rest<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave,        \
+                                       lane);                                                     \
         if (kFastSB && kk == 0) {                                                                 \
           const int j = k / kSuper;                  /* groups 8j .. 8j+7: piece j */             \
           const int src = (col * 4 + (j & 3)) * 4;   /* lane holding this row's piece j */        \
