@@ -42,6 +42,13 @@ __device__ __forceinline__ uint4 buf_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
+// 2 bytes, nontemporal (a streamed scale or bias)
+__device__ __forceinline__ uint32_t buf_load_u16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 2);
+}
+__device__ __forceinline__ uint32_t ld_stream_u16(const uint16_t* p) {
+  return __builtin_nontemporal_load(p);
+}
 
 // Direct global -> LDS copies (no VGPRs held while in flight).  Each active
 // lane copies n bytes from its own source address to lds_base + n * lane;

@@ -166,8 +166,8 @@ __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int i
     const bool is_up = k * kRps >= kJ;             // rows k kRps ..: gate rows, then up rows
     buf.w[k][0] = buf_load4_nt(is_up ? uw : gw, lo.w[k]);
     buf.w[k][1] = buf_load4_nt(is_up ? uw : gw, lo.w[k] + 16);
-    buf.s[k] = buf_load_u16(is_up ? us : gs, lo.s[k]);
-    buf.b[k] = buf_load_u16(is_up ? ub : gb, lo.s[k]);
+    buf.s[k] = buf_load_u16_nt(is_up ? us : gs, lo.s[k]);
+    buf.b[k] = buf_load_u16_nt(is_up ? ub : gb, lo.s[k]);
   }
   // keep every load of the item here: left to itself the scheduler sinks the
   // scale/bias loads to their first use, after the next item's loads, which
@@ -259,7 +259,8 @@ __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, in
   const int64_t sb = e * a.down.stride_sb + (int64_t)r0 * G + (L >> 1);
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
-    const uint32_t sv = a.down.s[sb + (int64_t)r * G], bv = a.down.b[sb + (int64_t)r * G];
+    const uint32_t sv = ld_stream_u16(a.down.s + sb + (int64_t)r * G);
+    const uint32_t bv = ld_stream_u16(a.down.b + sb + (int64_t)r * G);
     it.s[r] = lane_live ? sv : 0u;
     it.b[r] = lane_live ? bv : 0u;
   }
