@@ -33,6 +33,7 @@ def lib():
         vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         L.oracle_router_logits.argtypes = [vp, i32, vp, i32, i32, i32, vp]
         L.oracle_topk_softmax.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        L.oracle_rank.argtypes = [vp, i32, i32, i32, vp]
         L.oracle_build_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.oracle_build_union.restype = i32
         L.oracle_dequant.argtypes = [vp, vp, vp, i32, i32, vp]
@@ -80,6 +81,16 @@ def topk_softmax(logits: np.ndarray, K: int, norm: bool = True):
     w = np.empty((B, K), np.float32)
     lib().oracle_topk_softmax(pl, B, E, K, int(norm), idx.ctypes.data, w.ctypes.data)
     return idx, w
+
+
+def rank(logits: np.ndarray, R: int) -> np.ndarray:
+    """The R highest-ranked experts of each token in rank order (logit
+    descending, index ascending): [B, R] int32."""
+    logits, pl = _c(logits, np.float32)
+    B, E = logits.shape
+    out = np.empty((B, R), np.int32)
+    lib().oracle_rank(pl, B, E, R, out.ctypes.data)
+    return out
 
 
 def route(Wr, x, K, norm=True):

@@ -129,6 +129,21 @@ void oracle_topk_softmax(const float* logits, int B, int E, int K, int norm, int
   }
 }
 
+// The R highest-ranked experts of each token, in rank order: larger logit
+// first, equal logits by lower index ("Data Flow", the routing step: ranked
+// top-(8+spec), ranks 8 and up queued for speculative prefetch; "Surface
+// Scout": the current token's lower gate ranks).  The first K equal
+// oracle_topk_softmax's indices.
+void oracle_rank(const float* logits, int B, int E, int R, int32_t* ranked) {
+  std::vector<int> order(E);
+  for (int t = 0; t < B; ++t) {
+    const float* l = logits + static_cast<int64_t>(t) * E;
+    for (int e = 0; e < E; ++e) order[e] = e;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return l[a] > l[b]; });
+    for (int k = 0; k < R; ++k) ranked[static_cast<int64_t>(t) * R + k] = order[k];
+  }
+}
+
 int oracle_build_union(const int32_t* idx, int B, int K, int E, int32_t* union_experts,
                        int32_t* offsets, int32_t* pair_list, int32_t* pair_pos) {
   const int P = B * K;

@@ -48,6 +48,8 @@ void oracle_router_logits(const void* Wr, int wr_is_bf16, const float* x, int B,
  * softmax p; w[t,k] = p[idx] / sum_k' p[idx_k'] when norm != 0, else p[idx]. */
 void oracle_topk_softmax(const float* logits, int B, int E, int K, int norm, int32_t* idx,
                          float* w);
+// The R highest-ranked experts per token, rank order (ranked [B, R]).
+void oracle_rank(const float* logits, int B, int E, int R, int32_t* ranked);
 
 /* Expert union and per-expert pair lists ([LMP] "The Inversion": dedupe the
  * chunk's experts, apply each union expert to every routed token).

@@ -107,6 +107,27 @@ def test_topk_all_experts_is_full_softmax():
         assert sorted(idx[t]) == list(range(16))
 
 
+def test_rank_hand_worked_and_definition():
+    """Ranked output ("Data Flow": ranked top-(8+spec)): by hand on ties, then
+    the definition by brute force on tie-heavy rows (integer logits): the
+    expert at rank k is beaten, by a larger logit or an equal one at a lower
+    index, by exactly k experts; the first K are the top-K indices."""
+    got = oracle.rank(np.array([[1, 3, 3, 2], [0, 0, 0, 0], [-1, 5, -1, 5]], np.float32), 4)
+    assert got.tolist() == [[1, 2, 3, 0], [0, 1, 2, 3], [1, 3, 0, 2]]
+    rng = np.random.default_rng(7)
+    lg = rng.integers(-3, 4, size=(40, 24)).astype(np.float32)
+    R = 12
+    ranked = oracle.rank(lg, R)
+    for t in range(lg.shape[0]):
+        l = lg[t]
+        assert len(set(ranked[t])) == R
+        for k, r in enumerate(ranked[t]):
+            beats = sum(1 for j in range(24) if l[j] > l[r] or (l[j] == l[r] and j < r))
+            assert beats == k
+    idx, _ = oracle.topk_softmax(lg, 5, True)
+    assert np.array_equal(ranked[:, :5], idx)
+
+
 # --------------------------------------------------------------- union
 def brute_union(idx, E):
     flat = idx.reshape(-1)
