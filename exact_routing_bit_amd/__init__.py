@@ -29,7 +29,8 @@ MAX_BATCH = 64
 
 SMOE_STAGE_ROUTE, SMOE_STAGE_GATE_UP, SMOE_STAGE_DOWN, SMOE_STAGE_COMBINE = 0, 1, 2, 3
 
-EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_build_union",
+EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_route_ranked",
+            "smoe_build_union",
             "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_rmsnorm",
             "smoe_stack_forward", "smoe_read_status", "smoe_strerror")
 
@@ -72,6 +73,7 @@ def _load():
     L.smoe_workspace_size.restype = sz
     L.smoe_workspace_init.argtypes = [vp, sz, vp]
     L.smoe_route.argtypes = [dp, vp, vp, i32, vp, vp, vp, u32, vp, sz, vp]
+    L.smoe_route_ranked.argtypes = [dp, vp, vp, i32, vp, i32, vp, vp, vp, u32, vp, sz, vp]
     L.smoe_build_union.argtypes = [dp, vp, i32, ctypes.POINTER(Union), vp, sz, vp]
     L.smoe_moe_forward.argtypes = [dp, ctypes.POINTER(Experts), vp, vp, vp, ctypes.POINTER(Union),
                                    i32, vp, vp, vp, sz, vp]
@@ -183,6 +185,20 @@ def route(desc, router_w, x, topk_idx, topk_w, ws, logits=None, logits_in=False,
                           _ptr(topk_idx, torch.int32, "topk_idx"),
                           _ptr(topk_w, torch.float32, "topk_w"), flags,
                           _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)), "smoe_route")
+
+
+def route_ranked(desc, router_w, x, spec, ranked_idx, topk_idx, topk_w, ws, logits=None,
+                 logits_in=False, stream=None):
+    B = logits.shape[0] if logits_in else x.shape[0]
+    flags = SMOE_ROUTE_LOGITS_IN if logits_in else 0
+    _check(lib.smoe_route_ranked(ctypes.byref(desc), _ptr(router_w, None, "router_w"),
+                                 _ptr(x, torch.float32, "x"), B,
+                                 _ptr(logits, torch.float32, "logits"), int(spec),
+                                 _ptr(ranked_idx, torch.int32, "ranked_idx"),
+                                 _ptr(topk_idx, torch.int32, "topk_idx"),
+                                 _ptr(topk_w, torch.float32, "topk_w"), flags,
+                                 _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+           "smoe_route_ranked")
 
 
 def build_union(desc, topk_idx, un: UnionBuffers, ws, stream=None):

@@ -159,6 +159,47 @@ SMOE_API int smoe_route(const smoe_layer_desc* desc, const void* router_w, const
   return hip_rc(smoe::launch_router(a, logits_in, true, false, static_cast<hipStream_t>(stream)));
 }
 
+SMOE_API int smoe_route_ranked(const smoe_layer_desc* desc, const void* router_w,
+                               const float* x, int32_t B, float* logits, int32_t spec,
+                               int32_t* ranked_idx, int32_t* topk_idx, float* topk_w,
+                               uint32_t flags, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_desc(desc);
+  if (rc == SMOE_OK) rc = check_batch(B);
+  if (rc != SMOE_OK) return rc;
+  if ((flags & ~SMOE_ROUTE_LOGITS_IN) != 0) return SMOE_EINVAL;
+  if (spec < 0 || desc->top_k + spec > SMOE_MAX_TOPK || desc->top_k + spec > desc->num_experts)
+    return SMOE_EUNSUPPORTED;
+  if (B == 0) return SMOE_OK;
+  const bool logits_in = (flags & SMOE_ROUTE_LOGITS_IN) != 0;
+  if (topk_idx == nullptr || topk_w == nullptr || ranked_idx == nullptr) return SMOE_EINVAL;
+  if (logits_in && logits == nullptr) return SMOE_EINVAL;
+  if (!logits_in) {
+    if (router_w == nullptr || x == nullptr || !aligned(router_w, 16) || !aligned(x, 16))
+      return SMOE_EINVAL;
+  }
+  rc = check_ws(desc, B, ws, ws_bytes);
+  if (rc != SMOE_OK) return rc;
+  const WsLayout lay = smoe::ws_layout(*desc, B);
+  smoe::RouteArgs a{};
+  a.router_w = router_w;
+  a.router_bf16 = desc->router_dtype == SMOE_BF16;
+  a.x = x;
+  a.B = B;
+  a.d = desc->d_model;
+  a.E = desc->num_experts;
+  a.K = desc->top_k;
+  a.norm = desc->norm_topk_prob;
+  a.logits = logits ? logits : ws_at<float>(ws, lay.logits);
+  a.topk_idx = topk_idx;
+  a.topk_w = topk_w;
+  a.status = ws_at<uint32_t>(ws, lay.status);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (!logits_in) err = smoe::launch_router(a, false, false, false, s);   // logits only
+  if (err == hipSuccess) err = smoe::launch_topk_ranked(a, desc->top_k + spec, ranked_idx, s);
+  return hip_rc(err);
+}
+
 SMOE_API int smoe_build_union(const smoe_layer_desc* desc, const int32_t* topk_idx, int32_t B,
                               const smoe_union* un, void* ws, size_t ws_bytes, void* stream) {
   int rc = check_desc(desc);

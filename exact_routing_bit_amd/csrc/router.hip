@@ -383,6 +383,36 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_
   build_union(a, &us);
 }
 
+// Ranked routing ("Data Flow", the routing step: ranked top-(8+spec), the
+// ranks past K queued as speculative prefetch; "Surface Scout": the current
+// token's lower gate ranks): one token per wave, the top R = K + spec by
+// (logit descending, index ascending); lanes k < K also write the top-K
+// index and weight.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_ranked(RouteArgs a, int R,
+                                                             int32_t* ranked) {
+  __shared__ TopkScratch sc[kTopkThreads / 64];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kTopkThreads / 64) + wave;
+  if (t >= a.B) return;                            // whole wave
+  const int E = a.E, K = a.K;
+  float v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
+  }
+  float my_v;
+  int my_e;
+  wave_topk(v, E, R, my_v, my_e, &sc[wave]);
+  const float w = topk_weight(v, E, K, a.norm != 0, my_v);   // lanes < K only
+  if (lane < K) {
+    a.topk_idx[(int64_t)t * K + lane] = my_e;
+    a.topk_w[(int64_t)t * K + lane] = w;
+  }
+  if (lane < R) ranked[(int64_t)t * R + lane] = my_e;
+}
+
 // Top-k only (logits given) and/or union only (indices given): one block.
 __global__ __launch_bounds__(kTailThreads) void k_topk_union(RouteArgs a, int do_topk,
                                                              int do_union) {
@@ -403,6 +433,12 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
 }
 
 }  // namespace
+
+hipError_t launch_topk_ranked(const RouteArgs& a, int R, int32_t* ranked, hipStream_t s) {
+  const int blocks = (a.B + kTopkThreads / 64 - 1) / (kTopkThreads / 64);
+  hipLaunchKernelGGL(k_topk_ranked, dim3(blocks), dim3(kTopkThreads), 0, s, a, R, ranked);
+  return hipGetLastError();
+}
 
 hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
                          hipStream_t s, const LaunchTiming* t) {

@@ -157,6 +157,10 @@ struct LaunchTiming {
 // All return hipSuccess or the launch error.
 hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
                          hipStream_t s, const LaunchTiming* t = nullptr);
+// Top R = K + spec of every token from a.logits (one token per wave): the
+// top K indices and weights to a.topk_idx / a.topk_w, all R indices in rank
+// order to ranked [B, R].
+hipError_t launch_topk_ranked(const RouteArgs& a, int R, int32_t* ranked, hipStream_t s);
 hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);

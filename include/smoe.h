@@ -145,6 +145,20 @@ int smoe_route(const smoe_layer_desc* desc, const void* router_w, const float* x
                float* logits, int32_t* topk_idx, float* topk_w, uint32_t flags, void* ws,
                size_t ws_bytes, void* stream);
 
+/* Ranked routing: smoe_route, plus each token's R = top_k + spec
+ * highest-ranked experts in rank order ([DF], the routing step: ranked
+ * top-(8+spec), ranks 8 and up queued as speculative prefetch for the next
+ * token; [SC]: prefetch of the current token's lower gate ranks, --spec N).
+ * ranked_idx: [B, R] int32, rank order by (logit descending, index
+ * ascending); ranked_idx[t, :top_k] equals topk_idx[t, :].  The weights
+ * cover the top_k only.  0 <= spec and R <= min(SMOE_MAX_TOPK, E), else
+ * SMOE_EUNSUPPORTED; the other arguments and errors as smoe_route.
+ * B == 0 is a no-op. */
+int smoe_route_ranked(const smoe_layer_desc* desc, const void* router_w, const float* x,
+                      int32_t B, float* logits, int32_t spec, int32_t* ranked_idx,
+                      int32_t* topk_idx, float* topk_w, uint32_t flags, void* ws, size_t ws_bytes,
+                      void* stream);
+
 /* Builds the union and the pair lists from topk_idx [B, top_k] on the
  * device, with no host synchronisation ([LMP] "dedupe -> expert UNION").
  * Ids outside [0, E) set SMOE_STATUS_BAD_EXPERT and their pairs are left

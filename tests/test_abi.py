@@ -106,6 +106,30 @@ def test_route_argument_errors(smoe):
              None) == smoe.SMOE_EINVAL                                  # misaligned workspace
 
 
+def test_route_ranked_argument_errors(smoe):
+    d = desc_of(smoe)                                   # top_k 8 of 128
+    f = ctypes.c_void_p(4096)
+    r = smoe.lib.smoe_route_ranked
+    big = 1 << 30
+
+    def call(B=1, spec=4, ranked=f, idx=f, flags=0, gate=f, ws=f, n=big, desc=d):
+        return r(ctypes.byref(desc), gate, f, B, None, spec, ranked, idx, f, flags, ws, n, None)
+
+    assert call(spec=-1) == smoe.SMOE_EUNSUPPORTED
+    assert call(spec=9) == smoe.SMOE_EUNSUPPORTED      # 8 + 9 > 16 ranks
+    assert call(spec=8, desc=desc_of(smoe, num_experts=12)) == smoe.SMOE_EUNSUPPORTED   # > E
+    assert call(B=-1) == smoe.SMOE_EINVAL
+    assert call(B=65) == smoe.SMOE_EUNSUPPORTED
+    assert call(B=0, ranked=None) == smoe.SMOE_OK       # nothing to do
+    assert call(ranked=None) == smoe.SMOE_EINVAL
+    assert call(idx=None) == smoe.SMOE_EINVAL
+    assert call(gate=None) == smoe.SMOE_EINVAL
+    assert call(flags=0x10) == smoe.SMOE_EINVAL
+    assert call(flags=smoe.SMOE_ROUTE_LOGITS_IN) == smoe.SMOE_EINVAL   # needs logits
+    assert call(B=8, n=1024) == smoe.SMOE_EWORKSPACE
+    assert call(ws=ctypes.c_void_p(4096 + 16)) == smoe.SMOE_EINVAL
+
+
 def test_forward_argument_errors(smoe):
     d = desc_of(smoe)
     f = 4096

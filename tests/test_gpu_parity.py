@@ -105,6 +105,61 @@ def test_topk_ties_lower_index_wins(smoe):
     assert np.allclose(down(w), w_ref, rtol=1e-6)
 
 
+RANKED_CASES = [(configs.DECODE, 1, 4), (configs.DECODE, 1, 8), (configs.DECODE, 37, 2),
+                (configs.FUSED_B64, 64, 4), (small_config("k16r", 256, 16, 16, 64, 5, bf16=False), 5, 0),
+                (small_config("nonorm_r", 512, 40, 6, 64, 9, norm=False), 9, 10)]
+
+
+@pytest.mark.parametrize("cfg,B,spec", RANKED_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_route_ranked_parity(smoe, cfg, B, spec):
+    desc = desc_for(smoe, cfg)
+    K, R = cfg.top_k, cfg.top_k + spec
+    Wr = synth.router(cfg.seed, 0, cfg.num_experts, cfg.d_model, cfg.router_sigma, cfg.router_bf16)
+    x = synth.hidden(cfg.seed, 0, 12, B, cfg.d_model)
+    lg_ref = oracle.route(Wr, x, K, cfg.norm_topk_prob)[0]
+    ws = new_ws(smoe, desc, B)
+    lg = torch.zeros(B, cfg.num_experts, dtype=torch.float32, device=dev())
+    ranked = torch.full((B, R), -7, dtype=torch.int32, device=dev())
+    idx = torch.zeros(B, K, dtype=torch.int32, device=dev())
+    w = torch.zeros(B, K, dtype=torch.float32, device=dev())
+    smoe.route_ranked(desc, up(Wr), up(x), spec, ranked, idx, w, ws, logits=lg)
+    lg_g = down(lg)
+    # on the logits it computed: the ranking is the oracle's, the first K
+    # ranks are the top-k, and the weights are smoe_route's
+    assert np.array_equal(down(ranked), oracle.rank(lg_g, R))
+    assert np.array_equal(down(ranked)[:, :K], down(idx))
+    idx_own, w_own = oracle.topk_softmax(lg_g, K, cfg.norm_topk_prob)
+    assert np.array_equal(down(idx), idx_own)
+    assert np.allclose(down(w), w_own, rtol=1e-6, atol=1e-7)
+    idx2 = torch.zeros_like(idx)
+    w2 = torch.zeros_like(w)
+    smoe.route(desc, None, None, idx2, w2, ws, logits=lg, logits_in=True)
+    assert torch.equal(idx2, idx) and torch.equal(w2, w)
+    # fed the oracle's logits: bit-exact ranking
+    smoe.route_ranked(desc, None, None, spec, ranked, idx, w, ws, logits=up(lg_ref), logits_in=True)
+    assert np.array_equal(down(ranked), oracle.rank(lg_ref, R))
+
+
+def test_route_ranked_ties_and_all_experts(smoe):
+    cfg = small_config("rties", 64, 12, 4, 64, 3)
+    desc = desc_for(smoe, cfg)
+    lg = np.zeros((3, 12), np.float32)
+    lg[0] = 1.0                                    # all tied: index order
+    lg[1, [11, 2, 7]] = 3.0                        # a tied top above a flat floor
+    lg[2] = np.arange(12, dtype=np.float32) % 4    # repeated values
+    R = 12                                         # every expert ranked
+    ws = new_ws(smoe, desc, 3)
+    ranked = torch.zeros(3, R, dtype=torch.int32, device=dev())
+    idx = torch.zeros(3, 4, dtype=torch.int32, device=dev())
+    w = torch.zeros(3, 4, dtype=torch.float32, device=dev())
+    smoe.route_ranked(desc, None, None, R - 4, ranked, idx, w, ws, logits=up(lg), logits_in=True)
+    got = down(ranked)
+    assert list(got[0]) == list(range(12))
+    assert list(got[1][:4]) == [2, 7, 11, 0]
+    assert np.array_equal(got, oracle.rank(lg, R))
+    assert np.array_equal(got[:, :4], down(idx))
+
+
 # ---------------------------------------------------------------------- union
 @pytest.mark.parametrize("B,K,E,mode", [(1, 8, 128, "rand"), (8, 4, 16, "rand"),
                                         (64, 8, 128, "rand"), (37, 8, 256, "rand"),
