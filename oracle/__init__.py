@@ -43,6 +43,8 @@ def lib():
             fn.argtypes = [qp, qp, qp, i32, i32, i32, vp, i32, i32, vp, vp, vp, vp, vp]
             fn.restype = i32
         L.oracle_rmsnorm.argtypes = [vp, i32, i32, f32, vp]
+        L.oracle_shared_ffn.argtypes = [qp, qp, qp, i32, i32, vp, i32, vp]
+        L.oracle_combine_shared.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
         L.oracle_num_threads.restype = i32
         L.oracle_set_num_threads.argtypes = [i32]
         _lib = L
@@ -151,10 +153,48 @@ def _qmat(triple):
     return q, (w, s, b)
 
 
-def moe(gate, up, down, x, idx, w, residual=None, layer_major=False, return_pairs=False):
+def shared_ffn(gate, up, down, x):
+    """Shared-expert FFN on every token: gate/up/down are (w, s, b) triples
+    of one expert (a leading axis of 1, [1, fs, d/8] etc.); x [B, d] ->
+    shared_out [B, d]."""
+    qg, keep_g = _qmat(gate)
+    qu, keep_u = _qmat(up)
+    qd, keep_d = _qmat(down)
+    fs, d = keep_g[0].shape[1], keep_g[0].shape[2] * 8
+    x, px = _c(x, np.float32)
+    out = np.empty((x.shape[0], d), np.float32)
+    lib().oracle_shared_ffn(ctypes.byref(qg), ctypes.byref(qu), ctypes.byref(qd), d, fs, px,
+                            x.shape[0], out.ctypes.data)
+    return out
+
+
+def combine_shared(y_pairs, w, shared_out, residual=None):
+    """out = residual + (shared_out + routed_out), routed_out the k-ascending
+    weighted sum of the pairs' y ([B*K, d]) with w [B, K]."""
+    w, pw = _c(w, np.float32)
+    B, K = w.shape
+    y_pairs, py = _c(y_pairs, np.float32)
+    shared_out, ps = _c(shared_out, np.float32)
+    d = shared_out.shape[1]
+    pr = 0
+    if residual is not None:
+        residual, pr = _c(residual, np.float32)
+    out = np.empty((B, d), np.float32)
+    lib().oracle_combine_shared(py, pw, ps, pr or None, B, K, d, out.ctypes.data)
+    return out
+
+
+def moe(gate, up, down, x, idx, w, residual=None, layer_major=False, return_pairs=False,
+        shared=None):
     """One layer: gate/up/down are (w, s, b) triples with a leading expert
     axis ([E, f, d/8] etc.); x [B, d]; idx, w [B, K].  Returns out [B, d]
-    (and y per pair [B*K, d] when ``return_pairs``)."""
+    (and y per pair [B*K, d] when ``return_pairs``).  ``shared``: an optional
+    (gate, up, down) of the shared expert (see shared_ffn), added as
+    out = residual + (shared_out + routed_out)."""
+    if shared is not None:
+        _, yp = moe(gate, up, down, x, idx, w, layer_major=layer_major, return_pairs=True)
+        out = combine_shared(yp, w, shared_ffn(*shared, x), residual)
+        return (out, yp) if return_pairs else out
     qg, keep_g = _qmat(gate)
     qu, keep_u = _qmat(up)
     qd, keep_d = _qmat(down)

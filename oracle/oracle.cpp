@@ -247,6 +247,33 @@ int oracle_moe_layer_major(const oracle_qmat* gate, const oracle_qmat* up, const
   return 0;
 }
 
+void oracle_shared_ffn(const oracle_qmat* gate, const oracle_qmat* up, const oracle_qmat* down,
+                       int d, int fs, const float* x, int B, float* shared_out) {
+  DenseExpert ex;
+  dequant_expert(gate, up, down, d, fs, 0, &ex);
+  for (int t = 0; t < B; ++t)
+    oracle_expert_ffn(ex.Wg.data(), ex.Wu.data(), ex.Wd.data(), x + static_cast<int64_t>(t) * d, d,
+                      fs, nullptr, nullptr, nullptr, shared_out + static_cast<int64_t>(t) * d);
+}
+
+void oracle_combine_shared(const float* y_pairs, const float* w, const float* shared_out,
+                           const float* residual, int B, int K, int d, float* out) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < B; ++t) {
+    for (int r = 0; r < d; ++r) {
+      float routed = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        const float term = w[t * K + k] * y_pairs[(static_cast<int64_t>(t) * K + k) * d + r];
+        routed = routed + term;
+      }
+      const int64_t o = static_cast<int64_t>(t) * d + r;
+      const float both = shared_out[o] + routed;
+      const float res = residual ? residual[o] : 0.0f;
+      out[o] = res + both;
+    }
+  }
+}
+
 void oracle_rmsnorm(const float* v, int B, int d, float eps, float* out) {
   for (int t = 0; t < B; ++t) {
     const float* row = v + static_cast<int64_t>(t) * d;

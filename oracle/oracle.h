@@ -88,6 +88,21 @@ int oracle_moe_layer_major(const oracle_qmat* gate, const oracle_qmat* up, const
                            int d, int f, int E, const float* x, int B, int K, const int32_t* idx,
                            const float* w, const float* residual, float* out, float* y_pairs);
 
+/* Shared-expert FFN ([DF] layer flow: the shared expert FFN beside the routed
+ * experts, giving shared_out; [SC] weight inventory: the shared expert of
+ * architectures that have one): one always-active SwiGLU expert of width fs
+ * on every token, shared_out[t] = Wd_s (silu(Wg_s x_t) * Wu_s x_t).  gate/up
+ * hold one [fs, d] matrix, down one [d, fs] (expert 0 of each qmat). */
+void oracle_shared_ffn(const oracle_qmat* gate, const oracle_qmat* up, const oracle_qmat* down,
+                       int d, int fs, const float* x, int B, float* shared_out);
+
+/* Combine with a shared expert ([DF] "residual += shared_out + routed_out"):
+ * routed_out[t] = sum over k ascending of w[t,k] y[t*K+k] (formed first), then
+ * out[t] = residual[t] + (shared_out[t] + routed_out[t]).  residual may be
+ * NULL (zero). */
+void oracle_combine_shared(const float* y_pairs, const float* w, const float* shared_out,
+                           const float* residual, int B, int K, int d, float* out);
+
 /* RMSNorm with unit gain: out = v / sqrt(mean(v^2) + eps), fp32, sum ascending. */
 void oracle_rmsnorm(const float* v, int B, int d, float eps, float* out);
 

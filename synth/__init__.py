@@ -29,6 +29,9 @@ T_UP = 4
 T_DOWN = 5
 T_DECODE = 6
 T_RESIDUAL = 7
+T_SHARED_GATE = 8
+T_SHARED_UP = 9
+T_SHARED_DOWN = 10
 
 RMS_EPS = 1e-6
 
@@ -160,6 +163,21 @@ def make_layer(cfg: "LayerConfig", layer: int = 0, experts=None):
             w[e0:e0 + n], s[e0:e0 + n], b[e0:e0 + n] = ww, ss, bb
             i = j + 1
         out[name] = (w, s, b)
+    if cfg.fused:
+        out["gate_up"] = fuse_gate_up(out["gate"], out["up"])
+    if cfg.shared_ffn_dim:
+        out["shared"] = make_shared(cfg, layer)
+    return out
+
+
+def make_shared(cfg: "LayerConfig", layer: int = 0) -> dict:
+    """The shared expert of a layer: 'gate', 'up' ([1, fs, d/8] words etc.)
+    and 'down' ([1, d, fs/8]) triples, plus 'gate_up' for fused configs."""
+    d, fs, seed = cfg.d_model, cfg.shared_ffn_dim, cfg.seed
+    out = {}
+    for name, tensor, rows, cols in (("gate", T_SHARED_GATE, fs, d), ("up", T_SHARED_UP, fs, d),
+                                     ("down", T_SHARED_DOWN, d, fs)):
+        out[name] = quant_experts(seed, layer, tensor, 0, 1, rows, cols, cfg.expert_sigma)
     if cfg.fused:
         out["gate_up"] = fuse_gate_up(out["gate"], out["up"])
     return out

@@ -28,6 +28,7 @@ class LayerConfig:
     expert_sigma: float = 0.02
     seed: int = 0
     num_layers: int = 1
+    shared_ffn_dim: int = 0       # 0: no shared expert
 
     @property
     def router_sigma(self) -> float:
@@ -61,7 +62,15 @@ FUSED_B64 = dataclasses.replace(FUSED_B1, name="fused_d2048_e256_k8_f512_b64", b
 # Stacked routed-expert path: 94 layers of the decode shape.
 STACK = dataclasses.replace(DECODE, name="stack94_d4096_e128_k8_f1536", num_layers=94)
 
-ALL = {c.name: c for c in (TINY, DECODE, PREFILL, FUSED_B1, FUSED_B64, STACK)}
+# The decode layer with a shared expert twice the routed width (an always-active
+# expert beside the routed ones, as in architectures that have one).
+DECODE_SHARED = dataclasses.replace(DECODE, name="d4096_e128_k8_f1536_s3072_b1",
+                                    shared_ffn_dim=3072)
+PREFILL_SHARED = dataclasses.replace(DECODE_SHARED, name="d4096_e128_k8_f1536_s3072_b64",
+                                     batch=64)
+
+ALL = {c.name: c for c in (TINY, DECODE, PREFILL, FUSED_B1, FUSED_B64, STACK, DECODE_SHARED,
+                           PREFILL_SHARED)}
 
 
 def expected_union(E: int, K: int, B: int) -> float:

@@ -275,6 +275,89 @@ def test_combine_order_and_residual():
         assert np.array_equal(out[t], acc)
 
 
+# -------------------------------------------------------- shared expert
+def _shared_cfg(fs, fused=False):
+    return configs.LayerConfig("sh", 256, 12, 3, 128, 5, router_bf16=True, fused=fused,
+                               shared_ffn_dim=fs)
+
+
+def test_shared_ffn_matches_dense_fp64_brute_force():
+    """shared_out = Wd_s (silu(Wg_s x) * Wu_s x) on every token, against the
+    dequantised weights in fp64; a width unlike the routed one (192 vs 128)
+    and a gate/up swap as the negative control."""
+    cfg = _shared_cfg(192)
+    S = synth.make_shared(cfg)
+    x = synth.hidden(cfg.seed, 0, 3, cfg.batch, cfg.d_model)
+    got = oracle.shared_ffn(S["gate"], S["up"], S["down"], x)
+
+    def deq(t):
+        w, s, b = (a[0] for a in t)
+        q = unpack(w).astype(np.float64)
+        return q * np.repeat(bf16_to_f32(s), 64, -1) + np.repeat(bf16_to_f32(b), 64, -1)
+
+    Wg, Wu, Wd = deq(S["gate"]), deq(S["up"]), deq(S["down"])
+    assert Wg.shape == (192, 256) and Wd.shape == (256, 192)
+    x64 = x.astype(np.float64)
+
+    def ffn(A, Bm):
+        g, u = x64 @ A.T, x64 @ Bm.T
+        return (g / (1 + np.exp(-g)) * u) @ Wd.T
+
+    ref = ffn(Wg, Wu)
+    assert rel_l2(got, ref) < 1e-5
+    assert rel_l2(ffn(Wu, Wg), ref) > 0.3
+
+
+def test_shared_with_zero_weights_is_the_routed_layer():
+    cfg = _shared_cfg(128)
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 0, cfg.batch, cfg.d_model)
+    res = synth.hidden(cfg.seed, 0, 9, cfg.batch, cfg.d_model, tensor=synth.T_RESIDUAL)
+    _, idx, w = oracle.route(L["router"], x, cfg.top_k)
+    zero = {k: tuple(np.zeros_like(a) for a in L["shared"][k]) for k in ("gate", "up", "down")}
+    plain = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res)
+    with_zero = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res,
+                           shared=(zero["gate"], zero["up"], zero["down"]))
+    assert np.array_equal(plain.view(np.uint32), with_zero.view(np.uint32))
+    live = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res,
+                      shared=(L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"]))
+    assert rel_l2(live - res, plain - res) > 0.1
+
+
+def test_shared_copy_of_a_routed_expert_doubles_its_output():
+    """With top-1 routing (weight exactly 1) to expert e and a shared expert
+    holding e's weights, shared_out equals e's y bit for bit and
+    out = residual + 2 y."""
+    cfg = configs.LayerConfig("sh1", 256, 12, 1, 128, 4, router_bf16=True, shared_ffn_dim=128)
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 1, cfg.batch, cfg.d_model)
+    res = synth.hidden(cfg.seed, 0, 2, cfg.batch, cfg.d_model, tensor=synth.T_RESIDUAL)
+    e = 7
+    idx = np.full((cfg.batch, 1), e, np.int32)
+    w = np.ones((cfg.batch, 1), np.float32)
+    copy = tuple(tuple(a[e:e + 1] for a in L[k]) for k in ("gate", "up", "down"))
+    out, yp = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res,
+                         return_pairs=True, shared=copy)
+    assert np.array_equal(oracle.shared_ffn(*copy, x).view(np.uint32), yp.view(np.uint32))
+    assert np.array_equal(out.view(np.uint32), (res + 2 * yp).view(np.uint32))
+
+
+def test_shared_combine_order():
+    """out = residual + (shared_out + routed_out), routed_out formed first:
+    with residual 1, shared 2^24 and routed -2^24 only this order gives 1
+    ((1 + 2^24) rounds to 2^24 in fp32)."""
+    big = np.float32(2.0**24)
+    y = np.array([[-big / 2], [-big / 2]], np.float32).reshape(2, 1)   # [B*K, d], K = 2
+    w = np.array([[1.0, 1.0]], np.float32)
+    out = oracle.combine_shared(y, w, np.array([[big]], np.float32),
+                                np.array([[1.0]], np.float32))
+    assert out[0, 0] == 1.0
+    assert np.float32(np.float32(1.0) + big) + np.float32(-big) == 0.0   # the other order
+    # no residual: shared + routed
+    out0 = oracle.combine_shared(y, w, np.array([[3.0]], np.float32))
+    assert out0[0, 0] == np.float32(3.0) + np.float32(-big)
+
+
 def test_rmsnorm_closed_form():
     v = np.full((2, 64), 3.0, np.float32)
     v[1] = -2.0
