@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--stack", action="store_true",
                    help="run only the stacked harness (94 layers: prompt chunks, then decode)")
     p.add_argument("--no-stack", action="store_true", help="leave the stacked harness out")
+    p.add_argument("--shared", action="store_true",
+                   help="only the layer with a shared expert (decode and prefill), beside the "
+                        "same layer without one")
     p.add_argument("--stack-layers", type=int, default=94)
     p.add_argument("--stack-prompt", type=int, default=512)
     p.add_argument("--stack-decode", type=int, default=128)
@@ -64,12 +67,11 @@ class Stack:
         import synth.gpu as sg
         self.cfg, self.smoe = cfg, smoe
         self.desc = smoe.make_desc(cfg.d_model, cfg.ffn_dim, cfg.num_experts, cfg.top_k,
-                                   cfg.norm_topk_prob, cfg.router_bf16)
+                                   cfg.norm_topk_prob, cfg.router_bf16, cfg.shared_ffn_dim)
         self.layers = []
         for l in range(n_layers):
             W = sg.make_layer(cfg, layer=l)
-            ex = smoe.Experts(smoe.qmat(*W["gate"]), smoe.qmat(*W["up"]), smoe.qmat(*W["down"]))
-            self.layers.append((W, ex))
+            self.layers.append((W, smoe.experts_of(self.desc, W)))
         dev = torch.device("cuda:0")
         self.ws = torch.zeros(smoe.workspace_size(self.desc, max_batch), dtype=torch.uint8,
                               device=dev)
@@ -150,6 +152,51 @@ def union_sizes(stack, xs, steps):
         sizes.append(stack.un.n_union.clone())
     torch.cuda.synchronize()
     return [int(t.item()) for t in sizes]
+
+
+def shared_bench(smoe, args):
+    """The decode and prefill layer with a shared expert (fs = 3072 beside the
+    routed experts), and the same layer without one in the same run: the
+    shared expert's bytes are read once per call for every token."""
+    import torch
+    from synth import configs
+    res = {}
+    for name, cfg in (("shared", configs.DECODE_SHARED), ("plain", configs.DECODE)):
+        st = Stack(smoe, cfg, args.layers, max_batch=64)
+        xs1 = x_pool(cfg, 1, 257)
+        t1 = time_layer(st, xs1, args.steps, args.warmup) / args.steps
+        u1 = sum(union_sizes(st, xs1, 256)) / 256
+        xs64 = x_pool(cfg, 64, 17)
+        t64 = time_layer(st, xs64, args.prefill_steps, 5) / args.prefill_steps
+        u64 = sum(union_sizes(st, xs64, args.prefill_steps)) / args.prefill_steps
+        res[name] = (t1, u1, t64, u64)
+        del st
+        torch.cuda.empty_cache()
+    cfg = configs.DECODE_SHARED
+    eb = cfg.expert_bytes()
+    sb = 3 * (cfg.shared_ffn_dim * cfg.d_model // 2 + 2 * 2 * cfg.shared_ffn_dim * cfg.d_model // 64)
+    t1, u1, t64, u64 = res["shared"]
+    p1, _, p64, _ = res["plain"]
+    g1 = (u1 * eb + sb) / t1 / 1e9
+    g64 = (u64 * eb + sb) / t64 / 1e9
+    return {
+        "metric": "layer with a shared expert: decode tokens/s (B=1)", "value": round(1 / t1, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(t1 * 1e3, 5), "higher_is_better": True, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: the routed layer (d=4096, 128 experts, top-8, ffn "
+                               "1536) plus a shared expert of width 3072 on every token, 4-bit g64",
+                   "shared_expert_bytes": sb, "effective_bytes_per_step": int(u1 * eb + sb)},
+        "effective_gbps": round(g1, 1), "hbm_frac": round(g1 / HBM_PEAK_GBPS, 4),
+        "plain_layer_us": round(p1 * 1e6, 3), "shared_cost_us": round((t1 - p1) * 1e6, 3),
+        "shared_bytes_time_at_peak_us": round(sb / HBM_PEAK_GBPS / 1e3, 3),
+        "secondary": {"workload": f"{configs.PREFILL_SHARED.name}: the same, 64-token chunk",
+                      "tokens_per_s": round(64 / t64, 1), "ms_per_step": round(t64 * 1e3, 5),
+                      "mean_union": u64, "effective_gbps": round(g64, 1),
+                      "hbm_frac": round(g64 / HBM_PEAK_GBPS, 4),
+                      "plain_layer_us": round(p64 * 1e6, 3),
+                      "shared_cost_us": round((t64 - p64) * 1e6, 3)},
+    }
 
 
 def cpu_baseline(cfg, seconds):
@@ -315,7 +362,7 @@ def stack_harness(smoe, n_layers, prompt, steps):
 # copy of COPY_BYTES.  The summary records a hash of the kernel's sources;
 # once they change, the figure is stale and `traffic` is reported as null.
 COPY_BYTES = 1 << 30
-ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64, true>"
+ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64, true, false>"
 ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/device.hpp",
                     "exact_routing_bit_amd/csrc/smoe_internal.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_up_gemv_decode_b1_traffic.txt")
@@ -418,6 +465,9 @@ def main():
     import exact_routing_bit_amd as smoe
     from synth import configs
     torch.cuda.set_device(0)
+    if args.shared:
+        print(json.dumps(shared_bench(smoe, args)), flush=True)
+        return
     if args.stack:
         r = stack_harness(smoe, args.stack_layers, args.stack_prompt, args.stack_decode)
         print(json.dumps({"metric": "stacked routed path: decode tokens/s (B=1 through every "

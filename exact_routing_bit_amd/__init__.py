@@ -45,7 +45,7 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("ffn_dim", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("norm_topk_prob", ctypes.c_int32),
-                ("router_dtype", ctypes.c_int32)]
+                ("router_dtype", ctypes.c_int32), ("shared_ffn_dim", ctypes.c_int32)]
 
 
 class QMat(ctypes.Structure):
@@ -54,7 +54,8 @@ class QMat(ctypes.Structure):
 
 
 class Experts(ctypes.Structure):
-    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat)]
+    _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat),
+                ("shared_gate", QMat), ("shared_up", QMat), ("shared_down", QMat)]
 
 
 class Union(ctypes.Structure):
@@ -125,9 +126,10 @@ def _ptr(t, dtype=None, name="tensor"):
     return t.data_ptr()
 
 
-def make_desc(d_model, ffn_dim, num_experts, top_k, norm_topk_prob=True, router_bf16=True):
+def make_desc(d_model, ffn_dim, num_experts, top_k, norm_topk_prob=True, router_bf16=True,
+              shared_ffn_dim=0):
     return LayerDesc(d_model, ffn_dim, num_experts, top_k, 64, int(bool(norm_topk_prob)),
-                     SMOE_BF16 if router_bf16 else SMOE_F32)
+                     SMOE_BF16 if router_bf16 else SMOE_F32, int(shared_ffn_dim))
 
 
 def workspace_size(desc: LayerDesc, max_batch: int) -> int:
@@ -153,6 +155,24 @@ def qmat(w: torch.Tensor, s: torch.Tensor, b: torch.Tensor, expert_stride_w=None
         if t.dim() == 3 and (t.stride(2) != 1 or t.stride(1) != t.shape[2]):
             raise ValueError(f"{nm}: rows must be contiguous")
     return QMat(w.data_ptr(), s.data_ptr(), b.data_ptr(), sw, ssb)
+
+
+def _gate_up(weights: dict, prefix: str, f: int):
+    if prefix + "gate_up" in weights:
+        gw, gs, gb = weights[prefix + "gate_up"]
+        return (qmat(gw[:, :f], gs[:, :f], gb[:, :f], gw.stride(0), gs.stride(0)),
+                qmat(gw[:, f:], gs[:, f:], gb[:, f:], gw.stride(0), gs.stride(0)))
+    return qmat(*weights[prefix + "gate"]), qmat(*weights[prefix + "up"])
+
+
+def experts_of(desc: LayerDesc, weights: dict) -> Experts:
+    """The Experts descriptor of a layer's weight dict (see Layer)."""
+    gate, up = _gate_up(weights, "", desc.ffn_dim)
+    ex = Experts(gate, up, qmat(*weights["down"]))
+    if desc.shared_ffn_dim > 0:
+        ex.shared_gate, ex.shared_up = _gate_up(weights, "shared_", desc.shared_ffn_dim)
+        ex.shared_down = qmat(*weights["shared_down"])
+    return ex
 
 
 @dataclass
@@ -310,7 +330,9 @@ class Layer:
 
     ``weights`` maps 'router' and 'gate'/'up'/'down' (each a (w, s, b) triple
     of CUDA tensors with a leading expert axis) or 'gate_up' (fused, gate rows
-    on top) + 'down'.
+    on top) + 'down'; with a shared expert (desc.shared_ffn_dim > 0) also
+    'shared_gate'/'shared_up' or 'shared_gate_up', and 'shared_down' (a
+    leading axis of 1).
     """
 
     def __init__(self, desc: LayerDesc, weights: dict, max_batch: int = MAX_BATCH,
@@ -318,16 +340,7 @@ class Layer:
         self.desc = desc
         self.w = weights
         self.router_w = weights["router"]
-        f, d = desc.ffn_dim, desc.d_model
-        if "gate_up" in weights:
-            gw, gs, gb = weights["gate_up"]
-            gate = qmat(gw[:, :f], gs[:, :f], gb[:, :f], gw.stride(0), gs.stride(0))
-            up = qmat(gw[:, f:], gs[:, f:], gb[:, f:], gw.stride(0), gs.stride(0))
-        else:
-            gate = qmat(*weights["gate"])
-            up = qmat(*weights["up"])
-        down = qmat(*weights["down"])
-        self.experts = Experts(gate, up, down)
+        self.experts = experts_of(desc, weights)
         self.max_batch = max_batch
         nbytes = workspace_size(desc, max_batch)
         if nbytes == 0:

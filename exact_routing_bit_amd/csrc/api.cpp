@@ -30,6 +30,9 @@ int check_desc(const smoe_layer_desc* L) {
     return SMOE_EUNSUPPORTED;
   if (L->norm_topk_prob != 0 && L->norm_topk_prob != 1) return SMOE_EINVAL;
   if (L->router_dtype != SMOE_F32 && L->router_dtype != SMOE_BF16) return SMOE_EUNSUPPORTED;
+  if (L->shared_ffn_dim != 0 &&
+      (L->shared_ffn_dim < 64 || L->shared_ffn_dim > kMaxDim || L->shared_ffn_dim % 64 != 0))
+    return SMOE_EUNSUPPORTED;
   return SMOE_OK;
 }
 
@@ -67,6 +70,13 @@ int check_experts(const smoe_layer_desc* L, const smoe_experts* ex) {
   int rc = check_qmat(ex->gate, L->ffn_dim, L->d_model);
   if (rc == SMOE_OK) rc = check_qmat(ex->up, L->ffn_dim, L->d_model);
   if (rc == SMOE_OK) rc = check_qmat(ex->down, L->d_model, L->ffn_dim);
+  if (rc == SMOE_OK && L->shared_ffn_dim > 0) {
+    for (const smoe_qmat* m : {&ex->shared_gate, &ex->shared_up, &ex->shared_down}) {
+      if (m->w == nullptr || m->s == nullptr || m->b == nullptr || !aligned(m->w, 16) ||
+          !aligned(m->s, 2) || !aligned(m->b, 2))
+        return SMOE_EINVAL;
+    }
+  }
   return rc;
 }
 
@@ -78,6 +88,8 @@ T* ws_at(void* ws, size_t off) {
 smoe::QMat to_q(const smoe_qmat& m) {
   return smoe::QMat{m.w, m.s, m.b, m.expert_stride_w, m.expert_stride_sb};
 }
+// A single matrix (the shared expert): expert 0 only, so the strides are unused.
+smoe::QMat to_q1(const smoe_qmat& m) { return smoe::QMat{m.w, m.s, m.b, 0, 0}; }
 
 smoe::FfnArgs ffn_args(const smoe_layer_desc* L, const smoe_experts* ex, const smoe_union* un,
                        const float* topk_w, int32_t B, const float* residual, float* out, void* ws,
@@ -107,6 +119,15 @@ smoe::FfnArgs ffn_args(const smoe_layer_desc* L, const smoe_experts* ex, const s
   a.dec_meta = ws_at<int32_t>(ws, lay.meta);
   a.dec_meta_valid = 0;
   a.status = ws_at<uint32_t>(ws, lay.status);
+  a.fs = L->shared_ffn_dim;
+  if (a.fs > 0) {
+    a.sgate = to_q1(ex->shared_gate);
+    a.sup = to_q1(ex->shared_up);
+    a.sdown = to_q1(ex->shared_down);
+    a.shp = ws_at<uint16_t>(ws, lay.shp);
+    a.shs = ws_at<float2>(ws, lay.shs);
+    a.sy = ws_at<float>(ws, lay.sy);
+  }
   return a;
 }
 

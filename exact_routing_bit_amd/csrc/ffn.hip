@@ -4,7 +4,9 @@
 // ffn_gemv.hip, whose down pass also combines.  Prefill chunks take the MFMA
 // kernels of ffn_mfma.hip, which write y per pair, and k_combine below forms
 // out[t] = residual[t] + sum_k w[t,k] y[t*K+k] in rank order ("Data Flow":
-// "gather GPU outputs x routing weights -> routed_out", "residual += ...").
+// "gather GPU outputs x routing weights -> routed_out", "residual += ..."),
+// plus the shared expert's output when the layer has one:
+// residual + (shared_out + routed_out).
 // No float atomics: every output element has exactly one writer.
 #include "device.hpp"
 #include "smoe_internal.hpp"
@@ -12,7 +14,8 @@
 namespace smoe {
 namespace {
 
-// out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k ascending.
+// out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k ascending;
+// with a shared expert, residual + (sy[t, r] + that sum).
 __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;   // one float4 of out
   const int per_row = a.d / 4;
@@ -35,6 +38,8 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
   }
   const float4 res = a.residual ? reinterpret_cast<const float4*>(a.residual + (int64_t)t * a.d)[r4]
                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4 shv = a.fs > 0 ? reinterpret_cast<const float4*>(a.sy + (int64_t)t * a.d)[r4]
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
   // k ascending, fp32, then the residual
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -45,6 +50,12 @@ __global__ __launch_bounds__(256) void k_combine(FfnArgs a) {
       acc.z += w[k] * y[k].z;
       acc.w += w[k] * y[k].w;
     }
+  }
+  if (a.fs > 0) {                                 // shared_out + routed_out
+    acc.x = shv.x + acc.x;
+    acc.y = shv.y + acc.y;
+    acc.z = shv.z + acc.z;
+    acc.w = shv.w + acc.w;
   }
   if (a.residual) {
     acc.x = res.x + acc.x;

@@ -20,6 +20,13 @@
 // Both kernels stage the call's routing metadata (at most 16 pairs) in LDS
 // first, so no dependent global load sits inside their loops.
 //
+// A shared expert ("Data Flow": the shared expert FFN beside the routed ones)
+// rides along as more items of the same launches: gate_up items past the
+// routed ones cover its rows (every token a pair), and down items past the
+// union slots cover its rows in equal chunks of up to 2048 inputs (a lane's
+// four words of each chunk), whose partial sums the combine adds up first:
+// out = residual + (shared_out + routed_out).
+//
 // Lane layouts.  gate_up: a row's d/64 groups (64 inputs each) over TPR =
 // d/64 lanes (32 or 64), one group a lane, 64/TPR rows per wave instruction.
 // down: lane L owns words 4L .. 4L+3 (32 inputs) of every row and the
@@ -50,6 +57,7 @@ constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU (one row block 
 constexpr int kDnThreads = 512;       // down: 8 waves a block, one item each at d = 4096
 constexpr int kDnWaves = kDnThreads / 64;
 constexpr int kDnMaxF = 2048;         // down: f/32 <= 64 lanes of 4 words a row
+constexpr int kMaxShChunks = 8192 / kDnMaxF;   // shared expert down chunks (fs <= 8192)
 
 // Prepped position (half index within the row) of column c.
 __device__ __forceinline__ int prepped_pos(int c) {
@@ -139,15 +147,47 @@ __device__ __forceinline__ GuLane<TPR> gu_lane(const FfnArgs& a, int lane) {
 // compiler has no reason to wait for the previous item's loads first.  An
 // item past the end gets empty resources: its loads return zeros and touch
 // no memory.
-template <int TPR>
+// Expert e's matrix of a projection, or the shared expert's one (sh).
+struct QPtr {
+  const uint32_t* w;
+  const uint16_t* s;
+  const uint16_t* b;
+};
+__device__ __forceinline__ QPtr expert_mat(const QMat& m, const QMat& shared, bool sh, int e) {
+  return sh ? QPtr{shared.w, shared.s, shared.b}
+            : QPtr{m.w + e * m.stride_w, m.s + e * m.stride_sb, m.b + e * m.stride_sb};
+}
+// The same as mask arithmetic on both addresses (sh uniform): inside the ring
+// loop a branch around the multiplies would need a vector register for its
+// condition, and the compiler then waits for the loads in flight first.
+template <class T>
+__device__ __forceinline__ const T* pick(bool sh, const T* if_sh, const T* if_not) {
+  const uint64_t m = 0 - (uint64_t)sh;
+  const uint64_t a = reinterpret_cast<uint64_t>(if_sh), b = reinterpret_cast<uint64_t>(if_not);
+  return reinterpret_cast<const T*>(b ^ ((a ^ b) & m));
+}
+__device__ __forceinline__ QPtr expert_mat_nb(const QMat& m, const QMat& shared, bool sh, int e) {
+  return QPtr{pick(sh, shared.w, m.w + e * m.stride_w), pick(sh, shared.s, m.s + e * m.stride_sb),
+              pick(sh, shared.b, m.b + e * m.stride_sb)};
+}
+
+// Items 0 .. nR-1 are routed (union slot, j0); items from nR on cover the
+// shared expert's rows, j0 = 2 (item - nR).  kShared: the layer has a shared
+// expert (a separate instance: the extra pointers would otherwise crowd the
+// scalar registers of the routed-only loop).
+template <int TPR, bool kShared>
 __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int item, int n_items,
-                                        const GuLane<TPR>& lo, GuBuf<TPR>& buf) {
+                                        int nR, const GuLane<TPR>& lo, GuBuf<TPR>& buf) {
   constexpr int kRps = 64 / TPR;
   const int per = a.f / kJ;
   const bool live = item < n_items;
   const int itc = live ? item : n_items - 1;
-  const int u = uniform(itc / per);
-  const int j0 = (itc - u * per) * kJ;
+  const bool sh = kShared && itc >= nR;
+  // kShared: no branches in here (see pick); a shared item's u is a valid
+  // slot whose expert goes unused
+  const int u = kShared ? uniform((int)((unsigned)max(min(itc, nR - 1), 0) / (unsigned)per))
+                        : uniform(itc / per);
+  const int j0 = (sh ? itc - nR : itc - u * per) * kJ;
   // union slot u's expert, from lane u of a register (no LDS read, so no
   // temporary register is written while the ring's loads are in flight)
   const int e = __builtin_amdgcn_readlane(lane_expert, u);
@@ -155,12 +195,13 @@ __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int i
   const uint32_t wbytes = live ? (uint32_t)(kJ * C * 4) : 0u;
   const uint32_t sbytes = live ? (uint32_t)(kJ * G * 2) : 0u;
   const int64_t wr = (int64_t)j0 * C, sr = (int64_t)j0 * G;
-  const auto gw = buffer_rsrc(a.gate.w + e * a.gate.stride_w + wr, wbytes);
-  const auto gs = buffer_rsrc(a.gate.s + e * a.gate.stride_sb + sr, sbytes);
-  const auto gb = buffer_rsrc(a.gate.b + e * a.gate.stride_sb + sr, sbytes);
-  const auto uw = buffer_rsrc(a.up.w + e * a.up.stride_w + wr, wbytes);
-  const auto us = buffer_rsrc(a.up.s + e * a.up.stride_sb + sr, sbytes);
-  const auto ub = buffer_rsrc(a.up.b + e * a.up.stride_sb + sr, sbytes);
+  const QPtr g = expert_mat_nb(a.gate, a.sgate, sh, e), up = expert_mat_nb(a.up, a.sup, sh, e);
+  const auto gw = buffer_rsrc(g.w + wr, wbytes);
+  const auto gs = buffer_rsrc(g.s + sr, sbytes);
+  const auto gb = buffer_rsrc(g.b + sr, sbytes);
+  const auto uw = buffer_rsrc(up.w + wr, wbytes);
+  const auto us = buffer_rsrc(up.s + sr, sbytes);
+  const auto ub = buffer_rsrc(up.b + sr, sbytes);
 #pragma unroll
   for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
     const bool is_up = k * kRps >= kJ;             // rows k kRps ..: gate rows, then up rows
@@ -179,16 +220,18 @@ __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int i
 // the wave's LDS row st: st[jj * NTOK + q] = h of row j0 + jj for the union
 // expert's q-th pair (q < its pair count).  xr/xs: the lane's group of the
 // prepped activations of token t (t < NTOK).
-template <int NTOK, int TPR>
-__device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, int item, int lane,
-                                           const GuBuf<TPR>& buf, const uint4 (&xr)[NTOK][8],
-                                           const float2 (&xs)[NTOK], uint16_t* st) {
+template <int NTOK, int TPR, bool kShared>
+__device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, int item, int nR,
+                                           int lane, const GuBuf<TPR>& buf,
+                                           const uint4 (&xr)[NTOK][8], const float2 (&xs)[NTOK],
+                                           uint16_t* st) {
   constexpr int kRps = 64 / TPR;
   const int per = a.f / kJ;
-  const int u = uniform(item / per);
-  const int j0 = (item - u * per) * kJ;
-  const int pb = uniform(m.offsets[u]);
-  const int ne = uniform(m.offsets[u + 1]) - pb;   // 1 .. NTOK
+  const bool sh = kShared && item >= nR;          // a shared-expert item: pair q = token q
+  const int u = sh ? 0 : uniform(item / per);
+  const int j0 = (sh ? item - nR : item - u * per) * kJ;
+  const int pb = sh ? 0 : uniform(m.offsets[u]);
+  const int ne = sh ? a.B : uniform(m.offsets[u + 1]) - pb;   // 1 .. NTOK
   const int li = lane % TPR, slot = lane / TPR;
   // r[k][t]: row (k*kRps + slot) against token t
   float r[GuBuf<TPR>::kSteps][NTOK];
@@ -211,7 +254,7 @@ __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, i
 #pragma unroll
       for (int q = 0; q < NTOK; ++q) {
         if (q >= ne) break;
-        const int t = NTOK == 1 ? 0 : uniform(m.pairs[pb + q]) / a.K;
+        const int t = NTOK == 1 ? 0 : (sh ? q : uniform(m.pairs[pb + q]) / a.K);
         const float g = (NTOK == 1 || t == 0) ? r[kg][0] : r[kg][NTOK - 1];
         const float up = (NTOK == 1 || t == 0) ? r[ku][0] : r[ku][NTOK - 1];
         const float h = silu_mul(g, up);
@@ -234,33 +277,50 @@ struct DnItem {
   uint4 h[NTOK][4];
 };
 
-// Issue the loads of item (union slot u, rows r0 .. r0+7): h of the slot's
-// pairs first (the compute needs it first), then the rows' words, scales and
-// biases.  No branch: dead pair slots repeat the last live pair.
-template <int NTOK>
-__device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, int u, int r0, int L,
-                                          bool lane_live, int C, int G, DnItem<NTOK>& it) {
-  // an empty union (every routed id invalid) has no items; an invalid id in a
-  // live slot cannot occur, but would read expert 0
-  const int e0 = uniform(m.experts[u]);
+// Issue the loads of item (slot u, rows r0 .. r0+7): h of the slot's pairs
+// first (the compute needs it first), then the rows' words, scales and
+// biases.  Slots u < nU are the union's experts; slot nU + c is chunk c of
+// the shared expert (words c*chw .. of its rows, which are fs/8 words long;
+// pair q = token q).  Lane L < NL owns words 4L .. 4L+3 of the row (of the chunk);
+// lanes from NL on repeat lane NL-1's addresses with zero scale and bias.
+// No branch: dead pair slots repeat the last live pair.  Returns in ne the
+// slot's pair count and in ys[q] the ylds row of its q-th pair.
+template <int NTOK, bool kShared>
+__device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, int u, int nU, int chw,
+                                          int r0, int lane, DnItem<NTOK>& it, int& ne,
+                                          int (&ys)[NTOK]) {
+  const bool sh = kShared && u >= nU;
+  const int c = u - nU;
+  const int Cr = sh ? a.fs / 8 : a.f / 8, Gr = Cr / 8;    // words and groups of a row
+  const int cw = sh ? c * chw : 0;                       // the chunk's first word
+  const int NL = (sh ? min(chw, Cr - cw) : Cr) / 4;
+  const bool lane_live = lane < NL;
+  const int L = lane_live ? lane : NL - 1;
+  // an empty union (every routed id invalid) has no routed items; an invalid
+  // id in a live slot cannot occur, but would read expert 0
+  const int e0 = sh ? 0 : uniform(m.experts[u]);
   const int e = (unsigned)e0 < (unsigned)a.E ? e0 : 0;
-  const int pb = uniform(m.offsets[u]), ne = uniform(m.offsets[u + 1]) - pb;
-  // h of pair p: C chunks of 8 prepped halves; chunk c goes with word c of a row
-  const uint4* hsrc = reinterpret_cast<const uint4*>(a.hp);
+  const int pb = sh ? 0 : uniform(m.offsets[u]);
+  ne = sh ? a.B : uniform(m.offsets[u + 1]) - pb;
+  // h of pair p: Cr chunks of 8 prepped halves; chunk i goes with word i of a row
+  const uint4* hsrc = reinterpret_cast<const uint4*>(sh ? a.shp : a.hp);
 #pragma unroll
   for (int q = 0; q < NTOK; ++q) {
-    const int p = uniform(m.pairs[pb + max(min(q, ne - 1), 0)]);
+    const int qq = max(min(q, ne - 1), 0);
+    const int p = sh ? qq : uniform(m.pairs[pb + qq]);
+    ys[q] = sh ? kMaxDecPairs + 2 * c + qq : p;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) it.h[q][k] = hsrc[(int64_t)p * C + L * 4 + k];
+    for (int k = 0; k < 4; ++k) it.h[q][k] = hsrc[(int64_t)p * Cr + cw + L * 4 + k];
   }
-  const uint32_t* wr = a.down.w + e * a.down.stride_w + (int64_t)r0 * C + L * 4;
+  const QPtr dn = expert_mat(a.down, a.sdown, sh, e);
+  const uint32_t* wr = dn.w + (int64_t)r0 * Cr + cw + L * 4;
 #pragma unroll
-  for (int r = 0; r < kDnRows; ++r) it.w[r] = ld_stream4(wr + (int64_t)r * C);
-  const int64_t sb = e * a.down.stride_sb + (int64_t)r0 * G + (L >> 1);
+  for (int r = 0; r < kDnRows; ++r) it.w[r] = ld_stream4(wr + (int64_t)r * Cr);
+  const int64_t sb = (int64_t)r0 * Gr + cw / 8 + (L >> 1);
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
-    const uint32_t sv = ld_stream_u16(a.down.s + sb + (int64_t)r * G);
-    const uint32_t bv = ld_stream_u16(a.down.b + sb + (int64_t)r * G);
+    const uint32_t sv = ld_stream_u16(dn.s + sb + (int64_t)r * Gr);
+    const uint32_t bv = ld_stream_u16(dn.b + sb + (int64_t)r * Gr);
     it.s[r] = lane_live ? sv : 0u;
     it.b[r] = lane_live ? bv : 0u;
   }
@@ -310,11 +370,10 @@ __device__ __forceinline__ float rows8_wave_sum(const float (&v)[8]) {
 }
 
 // One item: the group sums of its pairs' h slices, the eight row dots, the
-// wave sums, and the rows' outputs into ylds[pair][row] (live pairs only).
+// wave sums, and the rows' outputs into ylds[ys[q]][row] (live pairs only).
 template <int NTOK>
-__device__ __forceinline__ void down_compute(const FfnArgs& a, const DecMeta& m, int u, int lane,
+__device__ __forceinline__ void down_compute(int ne, const int (&ys)[NTOK], int lane,
                                              const DnItem<NTOK>& it, float* ylds) {
-  const int pb = uniform(m.offsets[u]), ne = uniform(m.offsets[u + 1]) - pb;
   float sc[kDnRows], bi[kDnRows];
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
@@ -351,10 +410,7 @@ __device__ __forceinline__ void down_compute(const FfnArgs& a, const DecMeta& m,
       part[r] = sc[r] * (acc - S1024) + bi[r] * X;
     }
     const float y = rows8_wave_sum(part);
-    if (q < ne && (lane & 7) == 0) {
-      const int p = uniform(m.pairs[pb + q]);
-      ylds[p * kDnRows + (lane >> 3)] = y;
-    }
+    if (q < ne && (lane & 7) == 0) ylds[ys[q] * kDnRows + (lane >> 3)] = y;
   }
 }
 
@@ -510,7 +566,7 @@ __device__ __forceinline__ void route_rank(int K, int* slot_pair, RouteKeep& kee
 // w takes items w, w + W, w + 2W, ...; the next item's loads go out before
 // the current one is computed, so each wave streams its share with one item
 // in flight while it computes.
-template <int NTOK, int TPR, bool kRoute>
+template <int NTOK, int TPR, bool kRoute, bool kShared>
 __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeRoute r) {
   __shared__ DecMeta m;
   __shared__ TopkScratch tks[2];
@@ -526,7 +582,8 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   else
     load_meta(a, m);
   const int nU = uniform(m.n_union);
-  const int n_items = nU * (a.f / kJ);
+  const int nR = nU * (a.f / kJ);                 // routed items; then the shared expert's
+  const int n_items = nR + (kShared ? a.fs / kJ : 0);
   const int W = gridDim.x * kDecWaves;
   const int wid = blockIdx.x * kDecWaves + wave;
   if (wid >= n_items) return;                     // no barrier follows
@@ -557,16 +614,16 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   GuBuf<TPR> b[kGuDepth];
 #pragma unroll
   for (int s = 0; s < kGuDepth - 1; ++s)
-    gu_load<TPR>(a, lane_expert, wid + s * W, n_items, lo, b[s]);
+    gu_load<TPR, kShared>(a, lane_expert, wid + s * W, n_items, nR, lo, b[s]);
   for (int i = wid, loc = 0;; i += kGuDepth * W) {
 #pragma unroll
     for (int s = 0; s < kGuDepth; ++s, ++loc) {
       const int it = i + s * W;
       if (it >= n_items) goto flush;
-      gu_load<TPR>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, lo,
+      gu_load<TPR, kShared>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, nR, lo,
                    b[(s + kGuDepth - 1) % kGuDepth]);
       if (kLateRank && loc == 0) route_rank(a.K, slot_pair[wave], keep, tks);
-      gu_compute<NTOK, TPR>(a, m, it, lane, b[s], xr, xs, hst[wave][loc]);
+      gu_compute<NTOK, TPR, kShared>(a, m, it, nR, lane, b[s], xr, xs, hst[wave][loc]);
     }
   }
 flush:
@@ -578,6 +635,11 @@ flush:
       const int loc = q / (kJ * NTOK), rr = q % (kJ * NTOK);
       const int jj = rr / NTOK, k = rr % NTOK;
       const int item = wid + loc * W;
+      if (kShared && item >= nR) {                // shared expert: pair k = token k
+        const int j = (item - nR) * kJ + jj;
+        if (k < a.B) a.shp[(int64_t)k * a.fs + prepped_pos(j)] = hst[wave][loc][rr];
+        continue;
+      }
       const int u = item / per;
       const int j = (item - u * per) * kJ + jj;
       const int pb = m.offsets[u];
@@ -626,10 +688,10 @@ flush:
 // block b takes row blocks b, b + grid, ... of 8 output rows x all union
 // experts, one (union slot, row block) item per wave, and ends each row block
 // with the weighted combine of its rows in rank order.
-template <int NTOK>
+template <int NTOK, bool kShared>
 __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   __shared__ DecMeta m;
-  __shared__ float ylds[kMaxDecPairs * kDnRows];
+  __shared__ float ylds[(kMaxDecPairs + 2 * kMaxShChunks) * kDnRows];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   // the first row block's residual, fetched before anything waits
@@ -644,21 +706,25 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
     load_meta(a, m);
   }
   const int nU = uniform(m.n_union);
-  const int C = a.f / 8, G = a.f / 64, NL = C / 4;
-  const bool lane_live = lane < NL;
-  const int L = lane_live ? lane : NL - 1;
+  // the shared expert's rows in nCh chunks of equal width (chw words, whole
+  // groups, the last one shorter when fs does not divide), each at most 2048
+  // inputs and one item, so that its items weigh about as much as each other
+  const int nCh = kShared ? (a.fs + kDnMaxF - 1) / kDnMaxF : 0;
+  const int chw = kShared ? ((a.fs / 8 + nCh - 1) / nCh + 7) / 8 * 8 : 0;
   const int n_rb = a.d / kDnRows;
   const int K = a.K;
   for (int rb = blockIdx.x; rb < n_rb; rb += gridDim.x) {
     const int r0 = rb * kDnRows;
-    for (int u = wave; u < nU; u += kDnWaves) {
+    for (int u = wave; u < nU + nCh; u += kDnWaves) {
       DnItem<NTOK> it;
-      down_load<NTOK>(a, m, u, r0, L, lane_live, C, G, it);
-      down_compute<NTOK>(a, m, u, lane, it, ylds);
+      int ne, ys[NTOK];
+      down_load<NTOK, kShared>(a, m, u, nU, chw, r0, lane, it, ne, ys);
+      down_compute<NTOK>(ne, ys, lane, it, ylds);
     }
     __syncthreads();
     // combine: out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k
-    // ascending; a batch of eight pairs' values is read before it is summed
+    // ascending (with a shared expert: residual + (shared + that sum)); a
+    // batch of eight pairs' values is read before it is summed
     if (threadIdx.x < a.B * kDnRows) {
       const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
       float acc = 0.f;
@@ -675,6 +741,12 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           if (k0 + j < K && pv[j] >= 0) acc += wv[j] * yv[j];
+      }
+      if (kShared) {
+        // shared_out (its chunks in order) + routed_out
+        float shv = 0.f;
+        for (int c = 0; c < nCh; ++c) shv += ylds[(kMaxDecPairs + 2 * c + t) * kDnRows + rr];
+        acc = shv + acc;
       }
       const int64_t o = (int64_t)t * a.d + r0 + rr;
       const float res = rb == (int)blockIdx.x ? res_pref : (a.residual ? a.residual[o] : 0.f);
@@ -704,7 +776,7 @@ template <int NTOK, int TPR, bool kRoute>
 hipError_t launch_gate_up_gemv(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
                                const LaunchTiming* t) {
   const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
-  const int items = max_union * (a.f / kJ);
+  const int items = max_union * (a.f / kJ) + a.fs / kJ;
   const int ncu = cu_count();
   if (ncu <= 0) return hipErrorInvalidDevice;
   // one block per CU, but enough blocks that no wave has more than
@@ -712,7 +784,12 @@ hipError_t launch_gate_up_gemv(const FfnArgs& a, const DecodeRoute& r, hipStream
   const int per_block = kDecWaves * kGuMaxItems;
   const int grid = std::max(std::min((items + kDecWaves - 1) / kDecWaves, ncu * kGuBlocksPerCU),
                             (items + per_block - 1) / per_block);
-  SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, kRoute>), dim3(grid), dim3(kDecThreads), 0, s, a, r);
+  if (a.fs > 0)
+    SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, kRoute, true>), dim3(grid), dim3(kDecThreads), 0, s,
+                a, r);
+  else
+    SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, kRoute, false>), dim3(grid), dim3(kDecThreads), 0, s,
+                a, r);
   return hipGetLastError();
 }
 
@@ -731,7 +808,10 @@ hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming*
   const int ncu = cu_count();
   if (ncu <= 0) return hipErrorInvalidDevice;
   const int grid = std::min(a.d / kDnRows, ncu * kDnBlocksPerCU);
-  SMOE_LAUNCH(t, k_down_combine_gemv<NTOK>, dim3(grid), dim3(kDnThreads), 0, s, a);
+  if (a.fs > 0)
+    SMOE_LAUNCH(t, (k_down_combine_gemv<NTOK, true>), dim3(grid), dim3(kDnThreads), 0, s, a);
+  else
+    SMOE_LAUNCH(t, (k_down_combine_gemv<NTOK, false>), dim3(grid), dim3(kDnThreads), 0, s, a);
   return hipGetLastError();
 }
 

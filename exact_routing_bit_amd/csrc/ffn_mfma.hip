@@ -210,18 +210,39 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   constexpr int kSlot = slot_bytes(kFastSB);
   __shared__ __align__(16) char ring[kRing * kSlot];
   __shared__ int lpair_w[kWaves][kPairTile];       // each wave's copy of the tile's pair ids
-  const int u = blockIdx.y;
+  // The grid is one row of blocks per 16-token tile of the shared expert (if
+  // the layer has one: every token is one of its pairs, pair q = token q),
+  // then one row per union slot, laid out one after another along x: bx is
+  // the block within its row (kWaves units each), tile or u its row.  The
+  // shared rows go first, as their blocks serve the most pairs.
+  const int units_r = kGateUp ? a.f / 32 : a.d / 64;
+  const int units_s = kGateUp ? a.fs / 32 : a.d / 64;
+  const int gx_r = (units_r + kWaves - 1) / kWaves, gx_s = (units_s + kWaves - 1) / kWaves;
+  const int n_sh = a.fs > 0 ? (a.B + kPairTile - 1) / kPairTile : 0;
+  const int b_lin = blockIdx.x;
+  const bool sh = b_lin < n_sh * gx_s;
+  const int b_r = b_lin - n_sh * gx_s;
+  const int u = sh ? -1 : b_r / gx_r;
+  const int tile = sh ? b_lin / gx_s : 0;
+  const int bx = sh ? b_lin - tile * gx_s : b_r - u * gx_r;
+  const int ul = sh ? 0 : u;
   // the union's size and this slot's expert and offsets in one round trip (slot
   // u < the largest union is always inside the union arrays)
   const int nU = *a.n_union;
-  const int e_ld = a.union_experts[u];
-  const int pb_ld = a.expert_offsets[u];
-  const int pe_ld = a.expert_offsets[u + 1];
-  if (u >= nU) return;
-  const int e = e_ld;
-  const int pb = pb_ld;
-  const int ne = pe_ld - pb;                       // >= 1
-  const int K = kGateUp ? a.d : a.f;
+  const int e_ld = a.union_experts[ul];
+  const int pb_ld = a.expert_offsets[ul];
+  const int pe_ld = a.expert_offsets[ul + 1];
+  if (!sh && u >= nU) return;
+  const int e = sh ? 0 : e_ld;
+  const int pb = sh ? 0 : pb_ld;
+  const int ne = sh ? a.B : pe_ld - pb;            // >= 1
+  const int F = sh ? a.fs : a.f;                   // the expert's width
+  const int Kt = sh ? 1 : a.K;                     // pair q serves token q / Kt
+  const QMat qg = sh ? a.sgate : a.gate, qu = sh ? a.sup : a.up, qd = sh ? a.sdown : a.down;
+  uint16_t* const hp = sh ? a.shp : a.hp;
+  float2* const hs = sh ? a.shs : a.hs;
+  float* const yout = sh ? a.sy : a.y;
+  const int K = kGateUp ? a.d : F;
   const int G = K / 64, C = K / 8;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -229,9 +250,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
 
   // this wave's unit; waves past the last unit run along on a copy of the
   // last one (they take part in the shared copies and barriers) and write nothing
-  const int units = kGateUp ? a.f / 32 : a.d / 64;
-  const bool has_unit = (int)blockIdx.x * kWaves + wave < units;
-  const int unit = min((int)blockIdx.x * kWaves + wave, units - 1);
+  const int units = sh ? units_s : units_r;
+  const bool has_unit = bx * kWaves + wave < units;
+  const int unit = min(bx * kWaves + wave, units - 1);
   int rows0[kTiles];
 #pragma unroll
   for (int T = 0; T < kTiles; ++T) rows0[T] = kGateUp ? unit * 32 + (T & 1) * 16 : unit * 64 + T * 16;
@@ -239,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   Sources S;
 #pragma unroll
   for (int T = 0; T < kTiles; ++T) {
-    const QMat& m = kGateUp ? (T < 2 ? a.gate : a.up) : a.down;   // T is a constant here
+    const QMat& m = kGateUp ? (T < 2 ? qg : qu) : qd;   // T is a constant here
     S.w[T] = m.w + e * m.stride_w + (int64_t)(rows0[T] + (lane & 15)) * C + ((lane >> 4) & 1) * 4;
   }
   {
@@ -248,12 +269,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     const int T = kFastSB ? lane >> 4 : lane & 3;
     const int r = kFastSB ? lane & 15 : lane >> 2;
     const bool up = kGateUp && T >= 2;
-    const uint16_t* s0 = kGateUp ? a.gate.s : a.down.s;
-    const uint16_t* b0 = kGateUp ? a.gate.b : a.down.b;
-    const int64_t st0 = kGateUp ? a.gate.stride_sb : a.down.stride_sb;
-    const uint16_t* sp = up ? a.up.s : s0;
-    const uint16_t* bp = up ? a.up.b : b0;
-    const int64_t stride = up ? a.up.stride_sb : st0;
+    const uint16_t* s0 = kGateUp ? qg.s : qd.s;
+    const uint16_t* b0 = kGateUp ? qg.b : qd.b;
+    const int64_t st0 = kGateUp ? qg.stride_sb : qd.stride_sb;
+    const uint16_t* sp = up ? qu.s : s0;
+    const uint16_t* bp = up ? qu.b : b0;
+    const int64_t stride = up ? qu.stride_sb : st0;
     const int row = (kGateUp ? unit * 32 + (T & 1) * 16 : unit * 64 + T * 16) + r;
     S.s = sp + e * stride + (int64_t)row * G;
     S.b = bp + e * stride + (int64_t)row * G;
@@ -262,7 +283,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   if (!kFastSB) {
 #pragma unroll
     for (int T = 0; T < kTiles; ++T) {
-      const QMat& m = kGateUp ? (T < 2 ? a.gate : a.up) : a.down;
+      const QMat& m = kGateUp ? (T < 2 ? qg : qu) : qd;
       const int64_t first = e * m.stride_sb + (int64_t)(rows0[T] + col) * G;
       parity |= (uint32_t)((reinterpret_cast<uintptr_t>(m.s + first) >> 1) & 1) << T;
       parity |= (uint32_t)((reinterpret_cast<uintptr_t>(m.b + first) >> 1) & 1) << (4 + T);
@@ -278,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     const int P = G / 8;                           // <= 8 pieces a row (G <= 64)
 #pragma unroll
     for (int T = 0; T < kTiles; ++T) {
-      const QMat& m = kGateUp ? (T < 2 ? a.gate : a.up) : a.down;
+      const QMat& m = kGateUp ? (T < 2 ? qg : qu) : qd;
       const int64_t row = rows0[T] + (lane >> 2);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -301,13 +322,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
       }
   }
 
-  for (int m0 = 0; m0 < ne; m0 += kPairTile) {
+  // a union slot's pairs in 16-pair tiles; a shared-expert block does one tile
+  const int m_first = sh ? tile * kPairTile : 0;
+  const int m_end = sh ? m_first + 1 : ne;
+  for (int m0 = m_first; m0 < m_end; m0 += kPairTile) {
     __syncthreads();                               // the previous tile is done with the ring
     int* lpair = lpair_w[wave];
     // the tile's pair ids (copied like the rest, so that no compiler-counted
     // load sits behind the copies), then the first two stages' words, which
     // need only the expert; the wait covers the ids alone
-    if (lane < kPairTile) dma4_to_lds(a.pair_list + pb + min(m0 + lane, ne - 1), lpair);
+    if (lane < kPairTile) {
+      if (sh)
+        lpair[lane] = min(m0 + lane, ne - 1);      // the shared expert's pairs are the tokens
+      else
+        dma4_to_lds(a.pair_list + pb + min(m0 + lane, ne - 1), lpair);
+    }
     issue_words<kGateUp>(S, ring, 0, G, wave, lane);
     if (nst > 1) {
       issue_words<kGateUp>(S, ring + kSlot, 1, G, wave, lane);
@@ -319,12 +348,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
       const int q = lpair[lane & 15];
       const int word = 4 * (wave & 1) + (lane >> 4);
       if (kGateUp) {
-        const int t = q / a.K;
+        const int t = q / Kt;
         S.act = reinterpret_cast<const uint4*>(a.xp + (int64_t)t * a.d) + word;
         S.sums = reinterpret_cast<const float*>(a.xs) + (int64_t)t * G * 2 + (wave & 1);
       } else {
-        S.act = reinterpret_cast<const uint4*>(a.hp + (int64_t)q * a.f) + word;
-        S.sums = reinterpret_cast<const float*>(a.hs) + (int64_t)q * G * 4 + (wave & 1) * 2 +
+        S.act = reinterpret_cast<const uint4*>(hp + (int64_t)q * F) + word;
+        S.sums = reinterpret_cast<const float*>(hs) + (int64_t)q * G * 4 + (wave & 1) * 2 +
                  ((lane >> 4) & 1);
       }
     }
@@ -391,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
           X[i] += (j & 1) ? stf * 16.0f : stf;
           if (m < ne) {
             const int n = j & 7;
-            a.hp[(int64_t)lpair[m - m0] * a.f + (j & ~7) + 2 * (n & 3) + (n >> 2)] = f16_bits(stv);
+            hp[(int64_t)lpair[m - m0] * F + (j & ~7) + 2 * (n & 3) + (n >> 2)] = f16_bits(stv);
           }
         }
       }
@@ -402,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
         const int m = m0 + 4 * lg + i;
         if (col == 0 && m < ne) {
           const int j0 = unit * 32;
-          a.hs[((int64_t)lpair[m - m0] * (a.f / 64) + j0 / 64) * 2 + (j0 % 64) / 32] =
+          hs[((int64_t)lpair[m - m0] * (F / 64) + j0 / 64) * 2 + (j0 % 64) / 32] =
               make_float2(Xt, 1024.0f * St);
         }
       }
@@ -412,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = m0 + 4 * lg + i;
-          if (m < ne) a.y[(int64_t)lpair[m - m0] * a.d + rows0[T] + col] = acc[T][i];
+          if (m < ne) yout[(int64_t)lpair[m - m0] * a.d + rows0[T] + col] = acc[T][i];
         }
     }
   }
@@ -428,16 +457,23 @@ bool fast_sb_ok(const QMat& m, int G) {
 
 hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {
   const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
-  const int units = gate_up ? a.f / 32 : a.d / 64;
-  const dim3 grid((units + kWaves - 1) / kWaves, max_union);
+  const bool shared = a.fs > 0;
+  // a row of blocks per 16-token tile of the shared expert, then one per union
+  // slot (see the kernel), along x
+  const int n_sh = shared ? (a.B + kPairTile - 1) / kPairTile : 0;
+  const int units_r = gate_up ? a.f / 32 : a.d / 64;
+  const int units_s = gate_up ? a.fs / 32 : a.d / 64;
+  const int gx_r = (units_r + kWaves - 1) / kWaves, gx_s = (units_s + kWaves - 1) / kWaves;
+  const dim3 grid(n_sh * gx_s + max_union * gx_r);
   if (gate_up) {
-    const bool fast = fast_sb_ok(a.gate, a.d / 64) && fast_sb_ok(a.up, a.d / 64);
+    const bool fast = fast_sb_ok(a.gate, a.d / 64) && fast_sb_ok(a.up, a.d / 64) &&
+                      (!shared || (fast_sb_ok(a.sgate, a.d / 64) && fast_sb_ok(a.sup, a.d / 64)));
     if (fast)
       SMOE_LAUNCH(t, (k_ffn_mfma<true, true>), grid, dim3(kThreads), 0, s, a);
     else
       SMOE_LAUNCH(t, (k_ffn_mfma<true, false>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (fast_sb_ok(a.down, a.f / 64))
+    if (fast_sb_ok(a.down, a.f / 64) && (!shared || fast_sb_ok(a.sdown, a.fs / 64)))
       SMOE_LAUNCH(t, (k_ffn_mfma<false, true>), grid, dim3(kThreads), 0, s, a);
     else
       SMOE_LAUNCH(t, (k_ffn_mfma<false, false>), grid, dim3(kThreads), 0, s, a);

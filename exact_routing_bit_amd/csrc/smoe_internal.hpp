@@ -39,6 +39,9 @@ struct WsLayout {
   size_t hs;       // [P, f/64, 2] float2 half-group sums of hp
   size_t y;        // [P, d] f32 per-pair expert outputs
   size_t meta;     // 512 B: the decode kernels' packed routing metadata
+  size_t shp;      // [B, fs] f16 prepped h of the shared expert
+  size_t shs;      // [B, fs/64, 2] float2 half-group sums of shp
+  size_t sy;       // [B, d] f32 shared expert output (prefill path)
   size_t total;
 };
 
@@ -61,6 +64,10 @@ inline WsLayout ws_layout(const smoe_layer_desc& L, int B) {
   w.hs = take(P * (L.ffn_dim / 64) * 2 * 8);
   w.y = take(P * L.d_model * 4);
   w.meta = take(512);
+  const size_t fs = L.shared_ffn_dim > 0 ? (size_t)L.shared_ffn_dim : 0;
+  w.shp = take((size_t)B * fs * 2);
+  w.shs = take((size_t)B * (fs / 64) * 2 * 8);
+  w.sy = take(fs ? (size_t)B * L.d_model * 4 : 0);
   w.total = off;
   return w;
 }
@@ -119,6 +126,14 @@ struct FfnArgs {
   // by the routed gate_up kernel; read by the down kernel when dec_meta_valid)
   int32_t* dec_meta;
   int dec_meta_valid;
+  // the shared expert (fs > 0): one matrix each (expert 0, strides unused),
+  // applied to every token; its h in shp/shs like hp/hs with token t as the
+  // pair, its output in sy (prefill path; the decode path combines in-kernel)
+  QMat sgate, sup, sdown;
+  int fs;
+  uint16_t* shp;
+  float2* shs;
+  float* sy;
 };
 
 // Routing done inside the decode gate_up kernel (smoe_moe_layer with B <= 2):

@@ -67,7 +67,8 @@ extern "C" {
 /* ----------------------------------------------------------- descriptors */
 /* Supported: d_model and ffn_dim multiples of 64 in [64, 8192];
  * 1 <= num_experts <= 256; 1 <= top_k <= min(num_experts, 16);
- * group_size == 64; router_dtype SMOE_F32 or SMOE_BF16. */
+ * group_size == 64; router_dtype SMOE_F32 or SMOE_BF16;
+ * shared_ffn_dim 0 or a multiple of 64 in [64, 8192]. */
 typedef struct smoe_layer_desc {
   int32_t d_model;
   int32_t ffn_dim;
@@ -76,6 +77,11 @@ typedef struct smoe_layer_desc {
   int32_t group_size;     /* must be 64 */
   int32_t norm_topk_prob; /* 1: top-k weights renormalised to sum 1; 0: raw softmax */
   int32_t router_dtype;   /* SMOE_F32 or SMOE_BF16 */
+  /* Width of the layer's shared expert, 0 for none ([DF] layer flow: a
+   * shared expert FFN beside the routed ones, giving shared_out; [SC] model
+   * config, shared expert width, 0 = none).  With one, every layer call
+   * adds it:  out = residual + (shared_out + routed_out). */
+  int32_t shared_ffn_dim;
 } smoe_layer_desc;
 
 /* One quantised projection of every expert ([SSD] "Quantized Layout"):
@@ -102,6 +108,14 @@ typedef struct smoe_experts {
   smoe_qmat gate;
   smoe_qmat up;
   smoe_qmat down;
+  /* The shared expert, read only when desc->shared_ffn_dim = fs > 0 ([SC]
+   * weight inventory: the shared expert of architectures that have one):
+   * one always-active SwiGLU expert applied to every token, in the same
+   * format with a single matrix each (expert strides ignored): gate and up
+   * [fs, d_model], down [d_model, fs]; fused as above with ffn_dim -> fs. */
+  smoe_qmat shared_gate;
+  smoe_qmat shared_up;
+  smoe_qmat shared_down;
 } smoe_experts;
 
 /* The layer-major inversion ([LMP] "The Inversion"), all int32 device arrays:

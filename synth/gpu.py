@@ -10,7 +10,8 @@ import os
 
 import torch
 
-from . import T_DOWN, T_GATE, T_HIDDEN, T_ROUTER, T_UP, RMS_EPS
+from . import (T_DOWN, T_GATE, T_HIDDEN, T_ROUTER, T_SHARED_DOWN, T_SHARED_GATE, T_SHARED_UP,
+               T_UP, RMS_EPS)
 from .configs import LayerConfig
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -100,4 +101,23 @@ def make_layer(cfg: LayerConfig, layer: int = 0, device="cuda") -> dict:
     dn = _alloc(E, d, f, device)
     quant_experts_into(*dn, seed, layer, T_DOWN, 0, sig)
     out["down"] = dn
+    fs = cfg.shared_ffn_dim
+    if fs:
+        # the shared expert: 'shared_gate_up' (fused configs) or 'shared_gate' and
+        # 'shared_up', and 'shared_down', each with a leading axis of 1
+        if cfg.fused:
+            gu = _alloc(1, 2 * fs, d, device)
+            quant_experts_into(gu[0][:, :fs], gu[1][:, :fs], gu[2][:, :fs], seed, layer,
+                               T_SHARED_GATE, 0, sig)
+            quant_experts_into(gu[0][:, fs:], gu[1][:, fs:], gu[2][:, fs:], seed, layer,
+                               T_SHARED_UP, 0, sig)
+            out["shared_gate_up"] = gu
+        else:
+            for name, tensor in (("shared_gate", T_SHARED_GATE), ("shared_up", T_SHARED_UP)):
+                t = _alloc(1, fs, d, device)
+                quant_experts_into(*t, seed, layer, tensor, 0, sig)
+                out[name] = t
+        sd = _alloc(1, d, fs, device)
+        quant_experts_into(*sd, seed, layer, T_SHARED_DOWN, 0, sig)
+        out["shared_down"] = sd
     return out

@@ -39,7 +39,7 @@ def rel_l2(a, ref) -> float:
 
 def desc_for(smoe, cfg):
     return smoe.make_desc(cfg.d_model, cfg.ffn_dim, cfg.num_experts, cfg.top_k,
-                          cfg.norm_topk_prob, cfg.router_bf16)
+                          cfg.norm_topk_prob, cfg.router_bf16, cfg.shared_ffn_dim)
 
 
 def device_weights(L: dict) -> dict:
@@ -49,12 +49,17 @@ def device_weights(L: dict) -> dict:
             W[k] = tuple(up(a) for a in L[k])
     if "gate_up" in W:
         del W["gate"], W["up"]
+    if "shared" in L:
+        S = L["shared"]
+        keys = ("gate_up", "down") if "gate_up" in S else ("gate", "up", "down")
+        for k in keys:
+            W["shared_" + k] = tuple(up(a) for a in S[k])
     return W
 
 
-def small_config(name, d, E, K, f, B, bf16=True, fused=False, norm=True):
+def small_config(name, d, E, K, f, B, bf16=True, fused=False, norm=True, shared=0):
     return configs.LayerConfig(name, d, E, K, f, B, router_bf16=bf16, fused=fused,
-                               norm_topk_prob=norm)
+                               norm_topk_prob=norm, shared_ffn_dim=shared)
 
 
 def near_tie(logits_row: np.ndarray, K: int) -> bool:
@@ -69,4 +74,8 @@ def near_tie(logits_row: np.ndarray, K: int) -> bool:
 def oracle_layer(L, x, cfg, residual=None, idx=None, w=None):
     if idx is None:
         _, idx, w = oracle.route(L["router"], x, cfg.top_k, cfg.norm_topk_prob)
-    return oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=residual), idx, w
+    shared = None
+    if "shared" in L:
+        shared = (L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"])
+    return oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=residual,
+                      shared=shared), idx, w

@@ -160,6 +160,27 @@ def test_forward_argument_errors(smoe):
     assert call(B=-3) == smoe.SMOE_EINVAL
 
 
+def test_shared_expert_arguments(smoe):
+    for fs in (-64, 32, 100, 8256):
+        d = desc_of(smoe, shared_ffn_dim=fs)
+        assert smoe.workspace_size(d, 8) == 0
+    d0, d1 = desc_of(smoe), desc_of(smoe, shared_ffn_dim=3072)
+    # the shared expert's h (f16 + group sums) and output rows per token
+    grow = smoe.workspace_size(d1, 64) - smoe.workspace_size(d0, 64)
+    assert grow >= 64 * (3072 * 2 + 3072 // 64 * 16 + 4096 * 4)
+    f = 4096
+    q = smoe.QMat(f, f, f, 1536 * 512, 1536 * 64)
+    qd = smoe.QMat(f, f, f, 4096 * 192, 4096 * 24)
+    un = smoe.Union(f, f, f, f, f)
+    fw = smoe.lib.smoe_moe_forward
+    sq = smoe.QMat(f, f, f, 0, 0)                      # one matrix: strides unused
+    for ex in (smoe.Experts(q, q, qd),                 # shared matrices missing
+               smoe.Experts(q, q, qd, sq, sq, smoe.QMat(f + 4, f, f, 0, 0)),   # misaligned
+               smoe.Experts(q, q, qd, sq, smoe.QMat(f, None, f, 0, 0), sq)):
+        assert fw(ctypes.byref(d1), ctypes.byref(ex), f, f, f, ctypes.byref(un), 8, None, f, f,
+                  1 << 30, None) == smoe.SMOE_EINVAL
+
+
 def test_stage_argument_errors(smoe):
     d = desc_of(smoe)
     f = 4096

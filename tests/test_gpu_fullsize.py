@@ -36,7 +36,9 @@ def gpu_layer(smoe, cfg, layer_id):
 
 
 @pytest.mark.parametrize("cfg,sample", [(configs.DECODE, [0]), (configs.PREFILL, [0, 17, 42, 63]),
-                                        (configs.FUSED_B1, [0]), (configs.FUSED_B64, [3, 31, 60])],
+                                        (configs.FUSED_B1, [0]), (configs.FUSED_B64, [3, 31, 60]),
+                                        (configs.DECODE_SHARED, [0]),
+                                        (configs.PREFILL_SHARED, [0, 29, 63])],
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_full_size_layer(smoe, cfg, sample):
     layer_id = 5
@@ -63,7 +65,14 @@ def test_full_size_layer(smoe, cfg, sample):
         for a, b in zip(W[key], Lc[key]):
             assert np.array_equal(down(a[e]).view(b.dtype), b[e])
     xs = x[sample]
-    ref = oracle.moe(Lc["gate"], Lc["up"], Lc["down"], xs, idx[sample], wts[sample])
+    shared = None
+    if cfg.shared_ffn_dim:
+        S = Lc["shared"]
+        for a, b in zip(W["shared_gate"], S["gate"]):
+            assert np.array_equal(down(a).view(b.dtype), b)
+        shared = (S["gate"], S["up"], S["down"])
+    ref = oracle.moe(Lc["gate"], Lc["up"], Lc["down"], xs, idx[sample], wts[sample],
+                     shared=shared)
     err = rel_l2(out[sample], ref)
     assert err <= TOL, err
     # the GPU weights for the sampled tokens match the oracle's to 1e-6

@@ -44,6 +44,15 @@ def test_gpu_generator_matches_cpu_generator():
     for k in ("gate_up", "down"):
         for a, b in zip(Lg[k], Lc[k]):
             assert np.array_equal(down(a).view(b.dtype), b), k
+    # the shared expert's tensors, fused and split
+    for fused in (True, False):
+        cs = small_config("gen_s", 512, 6, 2, 192, 4, fused=fused, shared=320)
+        Sc = synth.make_shared(cs, layer=2)
+        Sg = sg.make_layer(cs, layer=2)
+        keys = ("gate_up", "down") if fused else ("gate", "up", "down")
+        for k in keys:
+            for a, b in zip(Sg["shared_" + k], Sc[k]):
+                assert np.array_equal(down(a).view(b.dtype), b), k
     xg = sg.hidden(0, 0, 5, 7, 512)
     assert np.array_equal(down(xg).view(np.uint32), synth.hidden(0, 0, 5, 7, 512).view(np.uint32))
 
@@ -206,6 +215,10 @@ FWD_CASES = [
     (small_config("dec_b2_f1024", 4096, 32, 8, 1024, 2), 2, False),    # 32 lanes
     (small_config("dec_b1_f64", 2048, 8, 2, 64, 1), 1, True),          # 2 lanes, one group
     (small_config("b1_f2560", 2048, 16, 4, 2560, 1), 1, True),         # past 64 lanes: MFMA path
+    # with a shared expert
+    (small_config("s_fwd_dec2", 2048, 32, 8, 512, 2, shared=2560), 2, True),
+    (small_config("s_fwd_odd", 512, 24, 6, 192, 13, shared=320), 13, True),   # 5 groups
+    (small_config("s_fwd_b3", 2048, 16, 2, 128, 3, bf16=False, shared=128), 3, False),
 ]
 
 
@@ -215,7 +228,7 @@ def test_forward_parity_injected_routing(smoe, cfg, B, with_res):
     x = synth.hidden(cfg.seed, 0, 1, B, cfg.d_model)
     res = synth.hidden(cfg.seed, 0, 2, B, cfg.d_model, tensor=synth.T_RESIDUAL) if with_res else None
     _, idx, w = oracle.route(L["router"], x, cfg.top_k, cfg.norm_topk_prob)
-    ref = oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, residual=res)
+    ref = oracle_layer(L, x, cfg, residual=res, idx=idx, w=w)[0]
     desc = desc_for(smoe, cfg)
     layer = smoe.Layer(desc, device_weights(L), max_batch=B, device=dev())
     smoe.build_union(desc, up(idx), layer.union, layer.ws)
@@ -231,12 +244,28 @@ def test_forward_parity_injected_routing(smoe, cfg, B, with_res):
     assert err <= 1.5e-3, f"precision regression: {err}"
 
 
+# Layers with a shared expert: decode kernels (B <= 2; its down rows in one to
+# four chunks of up to 2048 inputs, the last one partial) and prefill MFMA
+# kernels (its own grid row; wider and narrower than the routed experts, the
+# register and the LDS scale/bias variants), fused and split layouts.
+SHARED_CASES = [
+    (small_config("s_dec1_fs3072", 4096, 32, 8, 256, 1, shared=3072), 1),
+    (small_config("s_dec2_fused", 2048, 64, 8, 512, 2, fused=True, shared=1024), 2),
+    (small_config("s_dec1_fs8192", 2048, 16, 4, 256, 1, shared=8192), 1),
+    (small_config("s_dec1_d1024", 1024, 16, 4, 128, 1, shared=192), 1),
+    (small_config("s_pref64", 1024, 64, 8, 256, 64, shared=512), 64),
+    (small_config("s_pref37_narrow", 1024, 32, 4, 512, 37, fused=True, shared=256), 37),
+    (small_config("s_pref5_fs6144", 1024, 16, 2, 128, 5, shared=6144), 5),
+]
+
+
 @pytest.mark.parametrize("cfg,B", [(configs.TINY, 8), (small_config("l", 1024, 64, 8, 256, 64), 64),
                                    (small_config("l1", 1024, 64, 8, 256, 1), 1),
                                    (small_config("l_dec1", 4096, 32, 8, 256, 1), 1),
                                    (small_config("l_dec2", 2048, 64, 8, 512, 2), 2),
                                    (small_config("l_dec1_f2048", 2048, 32, 8, 2048, 1), 1),
-                                   (small_config("l_dec2_nonorm", 2048, 40, 6, 192, 2, norm=False), 2)],
+                                   (small_config("l_dec2_nonorm", 2048, 40, 6, 192, 2, norm=False), 2)]
+                         + SHARED_CASES,
                          ids=lambda v: getattr(v, "name", str(v)))
 def test_layer_parity(smoe, cfg, B):
     L = synth.make_layer(cfg)
@@ -266,6 +295,29 @@ def test_layer_parity(smoe, cfg, B):
     assert np.array_equal(down(un.expert_offsets)[:n + 1], off)
     assert np.array_equal(down(un.pair_list)[:B * cfg.top_k], pl)
     assert np.array_equal(down(un.pair_pos)[:B * cfg.top_k], pp)
+
+
+@pytest.mark.parametrize("cfg,B", [SHARED_CASES[0], SHARED_CASES[1], SHARED_CASES[4],
+                                   SHARED_CASES[6]], ids=lambda v: getattr(v, "name", str(v)))
+def test_shared_zero_weights_leave_the_routed_layer(smoe, cfg, B):
+    """A shared expert whose weights are all zero changes no bit of the
+    layer: residual + (0 + routed_out) = residual + routed_out."""
+    import dataclasses
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 4, B, cfg.d_model)
+    res = synth.hidden(cfg.seed, 0, 5, B, cfg.d_model, tensor=synth.T_RESIDUAL)
+    plain_cfg = dataclasses.replace(cfg, shared_ffn_dim=0)
+    Lp = {k: v for k, v in L.items() if k != "shared"}
+    plain = smoe.Layer(desc_for(smoe, plain_cfg), device_weights(Lp), max_batch=B, device=dev())
+    Lz = dict(L)
+    Lz["shared"] = {k: tuple(np.zeros_like(a) for a in v) for k, v in L["shared"].items()}
+    zero = smoe.Layer(desc_for(smoe, cfg), device_weights(Lz), max_batch=B, device=dev())
+    live = smoe.Layer(desc_for(smoe, cfg), device_weights(L), max_batch=B, device=dev())
+    a = down(plain.forward(up(x), residual=up(res)))
+    b = down(zero.forward(up(x), residual=up(res)))
+    c = down(live.forward(up(x), residual=up(res)))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert rel_l2(c - res, a - res) > 0.1
 
 
 def test_deterministic_bitwise(smoe):
