@@ -438,6 +438,29 @@ def test_decode_all_experts_bad_gives_residual(smoe, B):
     assert np.array_equal(down(out), res)
 
 
+@pytest.mark.parametrize("B", [1, 2, 3])
+def test_all_experts_bad_leaves_the_shared_expert(smoe, B):
+    """Every routed id invalid with a shared expert: the union is empty and the
+    output is residual + shared_out (decode kernels for B <= 2, MFMA rows for B = 3)."""
+    cfg = small_config("allbad_s", 2048, 16, 4, 512, B, shared=1536)
+    L = synth.make_layer(cfg)
+    x = synth.hidden(0, 0, 7, B, 2048)
+    res = synth.hidden(0, 0, 8, B, 2048, tensor=synth.T_RESIDUAL)
+    idx = np.full((B, 4), 77, np.int32)
+    w = np.full((B, 4), 0.25, np.float32)
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=B, device=dev())
+    smoe.build_union(desc, up(idx), layer.union, layer.ws)
+    assert int(down(layer.union.n_union)[0]) == 0
+    out = torch.empty(B, 2048, dtype=torch.float32, device=dev())
+    smoe.moe_forward(desc, layer.experts, up(x), up(idx), up(w), layer.union, out, layer.ws,
+                     residual=up(res))
+    assert smoe.read_status(layer.ws) & smoe.SMOE_STATUS_BAD_EXPERT
+    S = L["shared"]
+    ref = oracle.shared_ffn(S["gate"], S["up"], S["down"], x)
+    assert rel_l2(down(out) - res, ref) <= TOL
+
+
 def test_empty_batch_is_noop(smoe):
     cfg = configs.TINY
     L = synth.make_layer(cfg)

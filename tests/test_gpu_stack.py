@@ -66,8 +66,7 @@ class GpuStack:
         self.smoe, self.cfg, self.B = smoe, cfg, B
         self.desc = desc_for(smoe, cfg)
         self.W = layers_w
-        self.ex = [smoe.Experts(smoe.qmat(*W["gate"]), smoe.qmat(*W["up"]), smoe.qmat(*W["down"]))
-                   for W in layers_w]
+        self.ex = [smoe.experts_of(self.desc, W) for W in layers_w]
         self.args = smoe.StackArgs([W["router"] for W in layers_w], self.ex)
         self.ws = torch.zeros(smoe.workspace_size(self.desc, B), dtype=torch.uint8, device=dev())
         smoe.workspace_init(self.ws)
@@ -116,16 +115,22 @@ def check_layer_vs_oracle(L, cfg, x, s_gpu, idx_gpu, w_gpu, tokens=None):
         if not np.array_equal(idx_g[i], idx_ref[i]):
             assert near_tie(lg[i], cfg.top_k), f"token {tokens[i]}: routing differs"
             idx_ref, w_ref = idx_g, w_gpu[tokens]          # inject the GPU's routing
-    moe_ref = oracle.moe(L["gate"], L["up"], L["down"], xs, idx_ref, w_ref)
+    shared = None
+    if "shared" in L:
+        shared = (L["shared"]["gate"], L["shared"]["up"], L["shared"]["down"])
+    moe_ref = oracle.moe(L["gate"], L["up"], L["down"], xs, idx_ref, w_ref, shared=shared)
     moe_gpu = s_gpu[tokens].astype(np.float64) - xs.astype(np.float64)
     assert rel_l2(moe_gpu, moe_ref) <= TOL
 
 
 # d = 2048 with B <= 2 takes the decode kernels, where each layer after the
-# first normalises its input inside its router
-@pytest.mark.parametrize("d,B", [(1024, 1), (1024, 2), (1024, 5), (1024, 64), (2048, 1), (2048, 2)])
-def test_stack_equals_chain_and_oracle(smoe, d, B):
-    cfg = small_config("stack", d, 32, 8, 256, B)
+# first normalises its input inside its router; the last cases have a shared
+# expert in every layer
+@pytest.mark.parametrize("d,B,shared", [(1024, 1, 0), (1024, 2, 0), (1024, 5, 0), (1024, 64, 0),
+                                        (2048, 1, 0), (2048, 2, 0), (2048, 1, 2560),
+                                        (1024, 5, 320)])
+def test_stack_equals_chain_and_oracle(smoe, d, B, shared):
+    cfg = small_config("stack", d, 32, 8, 256, B, shared=shared)
     n_layers = 3
     Ls = [synth.make_layer(cfg, layer=l) for l in range(n_layers)]
     st = GpuStack(smoe, cfg, n_layers, B, [device_weights(L) for L in Ls])
