@@ -266,6 +266,49 @@ def stack_stats(idx_pre, nu_pre, idx_dec, E):
     }
 
 
+def stack_graph_decode(smoe, desc, args, cfg, n_layers, steps, h_out, idx_out, tmp, un, ws):
+    """The decode steps again with each token's whole stack captured once in a
+    HIP graph and replayed (the token's input copied into the graph's static
+    buffer first).  Every replay's output and routing must equal the stream
+    launches' bits for the same input (h_out, idx_out: the eager results)."""
+    import torch
+
+    import synth.gpu as sg
+    d, K = cfg.d_model, cfg.top_k
+    dev = torch.device("cuda:0")
+    ins = [sg.hidden(cfg.seed, 0, 6000 + n, 1, d) for n in range(min(steps, 16))]
+    hg = torch.zeros(1, d, dtype=torch.float32, device=dev)
+    idx_g = torch.zeros(n_layers, 1, K, dtype=torch.int32, device=dev)
+    w_g = torch.zeros(n_layers, 1, K, dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        hg.copy_(ins[0])
+        smoe.stack_forward(desc, args, hg, tmp[:1], idx_g, w_g, un, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        smoe.stack_forward(desc, args, hg, tmp[:1], idx_g, w_g, un, ws)
+    torch.cuda.synchronize()
+    equal = True
+    for n in range(len(ins)):
+        hg.copy_(ins[n])
+        g.replay()
+        torch.cuda.synchronize()
+        equal = equal and torch.equal(hg, h_out[n]) and torch.equal(idx_g, idx_out[n])
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for n in range(steps):
+        hg.copy_(ins[n % len(ins)])
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    t = ev[0].elapsed_time(ev[1]) / steps
+    return {"decode_graph_ms_per_token": round(t, 4), "decode_graph_tokens_per_s": round(1e3 / t, 2),
+            "decode_graph_replays_equal_stream_bits": bool(equal)}
+
+
 def stack_harness(smoe, n_layers, prompt, steps):
     """The stacked routed-expert path: n_layers layers of the decode shape
     resident in HBM; a prompt of `prompt` tokens in chunks of 64, layer-major
@@ -328,6 +371,7 @@ def stack_harness(smoe, n_layers, prompt, steps):
         raise RuntimeError("the stack reported a bad expert id")
     pre_s = ev[0].elapsed_time(ev[1]) / 1e3
     dec_s = ev[1].elapsed_time(ev[2]) / 1e3
+    graph = stack_graph_decode(smoe, desc, args, cfg, n_layers, steps, h_dec, idx_dec, tmp, un, ws)
     st = stack_stats(idx_pre.cpu().numpy(), nu_pre.cpu().numpy(), idx_dec.cpu().numpy(), E)
     if not np.all(nu_dec.cpu().numpy() == K):
         raise RuntimeError("a decode step's union is not its K experts")
@@ -349,6 +393,7 @@ def stack_harness(smoe, n_layers, prompt, steps):
         "decode_hbm_frac": round(dec_bytes / dec_s / 1e9 / HBM_PEAK_GBPS, 4),
         "outputs_finite": finite,
     }
+    out.update(graph)
     out.update(st)
     del Ws, ex, args
     torch.cuda.empty_cache()

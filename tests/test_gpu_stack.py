@@ -152,6 +152,47 @@ def test_stack_equals_chain_and_oracle(smoe, d, B, shared):
         assert np.all(np.abs(nxt - ref) <= norm_tol(cfg.d_model) * np.abs(ref) + 1e-30)
 
 
+@pytest.mark.parametrize("d,B,shared", [(2048, 1, 0), (1024, 5, 0), (2048, 2, 1024)])
+def test_stack_graph_replays_match_eager(smoe, d, B, shared):
+    """smoe_stack_forward captured once in a HIP graph: every replay, with the
+    program's own eager calls and synchronisations between replays, gives the
+    eager call's bits for the same input (output, routing, union sizes)."""
+    cfg = small_config("stack_g", d, 32, 8, 256, B, shared=shared)
+    n_layers = 3
+    Ls = [synth.make_layer(cfg, layer=l) for l in range(n_layers)]
+    st = GpuStack(smoe, cfg, n_layers, B, [device_weights(L) for L in Ls])
+    inputs = [up(synth.hidden(cfg.seed, 0, 3000 + i, B, d)) for i in range(3)]
+    refs = []
+    for x in inputs:
+        h = st.forward(x.clone())
+        torch.cuda.synchronize()
+        refs.append((down(h).copy(), down(st.idx).copy(), down(st.w).copy(), down(st.nu).copy()))
+    hg = torch.zeros(B, d, dtype=torch.float32, device=dev())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        hg.copy_(inputs[0])
+        st.forward(hg)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.forward(hg)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, x in enumerate(inputs):
+            hg.copy_(x)
+            g.replay()
+            torch.cuda.synchronize()
+            h_ref, idx_ref, w_ref, nu_ref = refs[i]
+            assert np.array_equal(down(hg).view(np.uint32), h_ref.view(np.uint32)), (rep, i)
+            assert np.array_equal(down(st.idx), idx_ref)
+            assert np.array_equal(down(st.w).view(np.uint32), w_ref.view(np.uint32))
+            assert np.array_equal(down(st.nu), nu_ref)
+            st.forward(inputs[(i + 1) % 3].clone())       # eager work between replays
+            torch.cuda.synchronize()
+
+
 def test_stack_bad_layer_leaves_h_unchanged(smoe):
     cfg = small_config("stack_bad", 1024, 32, 8, 256, 1)
     Ls = [synth.make_layer(cfg, layer=l) for l in range(2)]
