@@ -32,7 +32,8 @@ SMOE_STAGE_ROUTE, SMOE_STAGE_GATE_UP, SMOE_STAGE_DOWN, SMOE_STAGE_COMBINE = 0, 1
 EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_route_ranked",
             "smoe_build_union",
             "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_rmsnorm",
-            "smoe_stack_forward", "smoe_read_status", "smoe_strerror")
+            "smoe_stack_forward", "smoe_read_status", "smoe_strerror",
+            "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage")
 
 
 class SmoeError(RuntimeError):
@@ -56,6 +57,13 @@ class QMat(ctypes.Structure):
 class Experts(ctypes.Structure):
     _fields_ = [("gate", QMat), ("up", QMat), ("down", QMat),
                 ("shared_gate", QMat), ("shared_up", QMat), ("shared_down", QMat)]
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("rope_theta", ctypes.c_double), ("ctx", ctypes.c_int64),
+                ("d_model", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("reserved", ctypes.c_int32)]
 
 
 class Union(ctypes.Structure):
@@ -89,8 +97,14 @@ def _load():
     L.smoe_read_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.smoe_strerror.argtypes = [ctypes.c_int]
     L.smoe_strerror.restype = ctypes.c_char_p
+    ap, i64 = ctypes.POINTER(AttnDesc), ctypes.c_int64
+    L.smoe_attn_workspace_size.argtypes = [ap, i32]
+    L.smoe_attn_workspace_size.restype = sz
+    L.smoe_attn_forward.argtypes = [ap, vp, vp, vp, i32, i64, vp, vp, vp, vp, sz, vp]
+    L.smoe_attn_forward_stage.argtypes = [ctypes.c_int, ap, vp, vp, vp, i32, i64, vp, vp, vp, vp,
+                                          sz, vp, vp, vp]
     for name in EXPORTED:
-        if name != "smoe_workspace_size" and name != "smoe_strerror":
+        if name not in ("smoe_workspace_size", "smoe_strerror", "smoe_attn_workspace_size"):
             getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -316,6 +330,41 @@ def stack_forward(desc, stack: StackArgs, h, tmp, topk_idx, topk_w, un: UnionBuf
                                   _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
            "smoe_stack_forward")
     return h
+
+
+def make_attn_desc(d_model, num_heads, num_kv_heads, ctx, rope_theta=1.0e6, eps=1e-6,
+                   head_dim=128) -> AttnDesc:
+    return AttnDesc(float(rope_theta), int(ctx), d_model, num_heads, num_kv_heads, head_dim,
+                    float(eps), 0)
+
+
+def attn_workspace_size(desc: AttnDesc, max_batch: int) -> int:
+    return int(lib.smoe_attn_workspace_size(ctypes.byref(desc), max_batch))
+
+
+def _attn_args(desc, wqkv, wo, x, pos0, k_cache, v_cache, out, ws):
+    return (ctypes.byref(desc), _ptr(wqkv, None, "wqkv"), _ptr(wo, None, "wo"),
+            _ptr(x, torch.float32, "x"), x.shape[0], int(pos0), _ptr(k_cache, None, "k_cache"),
+            _ptr(v_cache, None, "v_cache"), _ptr(out, torch.float32, "out"),
+            _ptr(ws, torch.uint8, "ws"), ws.numel())
+
+
+def attn_forward(desc, wqkv, wo, x, pos0, k_cache, v_cache, out, ws, stream=None):
+    """out = x + attention block of x (B tokens at positions pos0 ..); the
+    K/V rings (bf16 bits, [Hkv, ctx, 128]) are updated in place."""
+    _check(lib.smoe_attn_forward(*_attn_args(desc, wqkv, wo, x, pos0, k_cache, v_cache, out, ws),
+                                 _stream(stream)), "smoe_attn_forward")
+    return out
+
+
+def attn_forward_stage(stage, desc, wqkv, wo, x, pos0, k_cache, v_cache, out, ws, stream=None,
+                       events=None):
+    ev0 = ev1 = None
+    if events is not None:
+        ev0, ev1 = (ctypes.c_void_p(e.cuda_event) for e in events)
+    _check(lib.smoe_attn_forward_stage(stage, *_attn_args(desc, wqkv, wo, x, pos0, k_cache,
+                                                          v_cache, out, ws),
+                                       _stream(stream), ev0, ev1), "smoe_attn_forward_stage")
 
 
 def read_status(ws, stream=None) -> int:

@@ -471,6 +471,94 @@ SMOE_API int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers,
   return SMOE_OK;
 }
 
+namespace {
+
+int check_attn(const smoe_attn_desc* D) {
+  if (D == nullptr) return SMOE_EINVAL;
+  if (!(D->rope_theta > 0.0) || !(D->eps > 0.0f) || D->reserved != 0) return SMOE_EINVAL;
+  if (!smoe::attn_shape_ok(D->d_model, D->num_heads, D->num_kv_heads, D->head_dim))
+    return SMOE_EUNSUPPORTED;
+  if (D->ctx < 1 || D->ctx > (int64_t)1 << 24) return SMOE_EUNSUPPORTED;
+  return SMOE_OK;
+}
+
+int attn_setup(const smoe_attn_desc* D, const uint16_t* wqkv, const uint16_t* wo, const float* x,
+               int32_t B, int64_t pos0, uint16_t* k_cache, uint16_t* v_cache, float* out,
+               void* ws, size_t ws_bytes, smoe::AttnArgs* a) {
+  int rc = check_attn(D);
+  if (rc == SMOE_OK) rc = check_batch(B);
+  if (rc != SMOE_OK) return rc;
+  if (B > D->ctx) return SMOE_EUNSUPPORTED;
+  if (pos0 < 0) return SMOE_EINVAL;
+  if (B == 0) return SMOE_OK;
+  for (const void* p : {(const void*)wqkv, (const void*)wo, (const void*)x, (const void*)out,
+                        (const void*)k_cache, (const void*)v_cache})
+    if (p == nullptr || !aligned(p, 16)) return SMOE_EINVAL;
+  if (ws == nullptr || !aligned(ws, 256)) return SMOE_EINVAL;
+  const smoe::AttnWsLayout lay = smoe::attn_ws_layout(*D, B);
+  if (ws_bytes < lay.total) return SMOE_EWORKSPACE;
+  *a = smoe::AttnArgs{};
+  a->x = x;
+  a->out = out;
+  a->wqkv = wqkv;
+  a->wo = wo;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->B = B;
+  a->d = D->d_model;
+  a->H = D->num_heads;
+  a->Hkv = D->num_kv_heads;
+  a->qkv_rows = (D->num_heads + 2 * D->num_kv_heads) * smoe::kAttnHeadDim;
+  a->pos0 = pos0;
+  a->ctx = D->ctx;
+  const int64_t p_last = pos0 + B - 1;
+  const int64_t window = p_last + 1 < D->ctx ? p_last + 1 : D->ctx;
+  a->nsplit = (int)((window + smoe::kAttnSplit - 1) / smoe::kAttnSplit);
+  a->theta = D->rope_theta;
+  a->eps = D->eps;
+  a->xb = ws_at<uint16_t>(ws, lay.xb);
+  a->qkv = ws_at<float>(ws, lay.qkv);
+  a->q = ws_at<float>(ws, lay.q);
+  a->part_o = ws_at<float>(ws, lay.part_o);
+  a->part_ml = ws_at<float>(ws, lay.part_ml);
+  a->ob = ws_at<uint16_t>(ws, lay.ob);
+  return SMOE_OK;
+}
+
+}  // namespace
+
+SMOE_API size_t smoe_attn_workspace_size(const smoe_attn_desc* desc, int32_t max_batch) {
+  if (check_attn(desc) != SMOE_OK || max_batch < 1 || max_batch > SMOE_MAX_BATCH) return 0;
+  return smoe::attn_ws_layout(*desc, max_batch).total;
+}
+
+SMOE_API int smoe_attn_forward(const smoe_attn_desc* desc, const uint16_t* wqkv,
+                               const uint16_t* wo, const float* x, int32_t B, int64_t pos0,
+                               uint16_t* k_cache, uint16_t* v_cache, float* out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  smoe::AttnArgs a;
+  const int rc = attn_setup(desc, wqkv, wo, x, B, pos0, k_cache, v_cache, out, ws, ws_bytes, &a);
+  if (rc != SMOE_OK || B == 0) return rc;
+  return hip_rc(smoe::launch_attn(a, static_cast<hipStream_t>(stream)));
+}
+
+SMOE_API int smoe_attn_forward_stage(int stage, const smoe_attn_desc* desc, const uint16_t* wqkv,
+                                     const uint16_t* wo, const float* x, int32_t B, int64_t pos0,
+                                     uint16_t* k_cache, uint16_t* v_cache, float* out, void* ws,
+                                     size_t ws_bytes, void* stream, void* start_event,
+                                     void* stop_event) {
+  if (stage < 0 || stage > 2) return SMOE_EINVAL;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return SMOE_EINVAL;
+  smoe::AttnArgs a;
+  const int rc = attn_setup(desc, wqkv, wo, x, B, pos0, k_cache, v_cache, out, ws, ws_bytes, &a);
+  if (rc != SMOE_OK || B == 0) return rc;
+  smoe::LaunchTiming timing;
+  timing.start = static_cast<hipEvent_t>(start_event);
+  timing.stop = static_cast<hipEvent_t>(stop_event);
+  return hip_rc(smoe::launch_attn(a, static_cast<hipStream_t>(stream), stage,
+                                  start_event != nullptr ? &timing : nullptr));
+}
+
 SMOE_API int smoe_read_status(const void* ws, size_t ws_bytes, void* stream,
                               uint32_t* status_out) {
   if (ws == nullptr || ws_bytes < 256 || status_out == nullptr) return SMOE_EINVAL;

@@ -152,6 +152,63 @@ struct DecodeRoute {
   int32_t* dec_meta;       // packed copy of the routing metadata (block 0 writes it)
 };
 
+// ------------------------------------------------------- attention block
+constexpr int kAttnHeadDim = 128;   // head dimension
+constexpr int kAttnMaxGroup = 16;   // query heads per key/value head
+constexpr int kAttnSplit = 256;     // cached positions per attention block
+
+// Workspace of the attention block for up to B tokens ([DF] layer loop).
+struct AttnWsLayout {
+  size_t xb;       // [B, d] bf16: the normed input
+  size_t qkv;      // [B, (H + 2 Hkv) hd] f32
+  size_t q;        // [B, H, hd] f32 after QK-norm and RoPE
+  size_t part_o;   // [B, Hkv, nsplit, 16, hd] f32
+  size_t part_ml;  // [B, Hkv, nsplit, 16] (max, sum) pairs
+  size_t ob;       // [B, H hd] bf16: the attention output
+  size_t total;
+};
+
+inline int attn_nsplit_max(int64_t ctx) { return (int)((ctx + kAttnSplit - 1) / kAttnSplit); }
+
+inline AttnWsLayout attn_ws_layout(const smoe_attn_desc& D, int B) {
+  AttnWsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const size_t hd = kAttnHeadDim, H = D.num_heads, G = D.num_kv_heads;
+  const size_t ns = (size_t)attn_nsplit_max(D.ctx);
+  w.xb = take((size_t)B * D.d_model * 2);
+  w.qkv = take((size_t)B * (H + 2 * G) * hd * 4);
+  w.q = take((size_t)B * H * hd * 4);
+  w.part_o = take((size_t)B * G * ns * kAttnMaxGroup * hd * 4);
+  w.part_ml = take((size_t)B * G * ns * kAttnMaxGroup * 8);
+  w.ob = take((size_t)B * H * hd * 2);
+  w.total = off;
+  return w;
+}
+
+struct AttnArgs {
+  const float* x;          // [B, d] input hidden states (also the residual)
+  float* out;              // [B, d]
+  const uint16_t* wqkv;    // [(H + 2 Hkv) hd, d] bf16
+  const uint16_t* wo;      // [d, H hd] bf16
+  uint16_t* k_cache;       // [Hkv, ctx, hd] bf16
+  uint16_t* v_cache;
+  int B, d, H, Hkv, qkv_rows, nsplit;
+  int64_t pos0, ctx;
+  double theta;
+  float eps;
+  uint16_t* xb;
+  float* qkv;
+  float* q;
+  float* part_o;
+  float* part_ml;
+  uint16_t* ob;
+};
+
 // ------------------------------------------------------------- launchers
 // Optional timing events for a stage's main kernel: when `start` is set the
 // kernel is launched with hipExtLaunchKernelGGL, which submits the events
@@ -191,6 +248,11 @@ hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up,
 // kernel then only computes logits and the prepped activations
 hipError_t launch_gate_up_routed(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
                                  const LaunchTiming* t = nullptr);
+// attention block: stage -1 = all, 0 = norm + QKV, 1 = prep + attention +
+// merge, 2 = O projection + residual (t times that stage's main kernel)
+bool attn_shape_ok(int d, int H, int Hkv, int hd);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage = -1,
+                       const LaunchTiming* t = nullptr);
 // prefill-chunk MFMA kernels
 hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up,
                            const LaunchTiming* t = nullptr);

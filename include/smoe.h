@@ -229,6 +229,61 @@ int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* rou
                          float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
                          void* stream, void* start_event, void* stop_event);
 
+/* ----------------------------------------------------- attention block */
+/* The attention block around the routed layer ([DF] layer loop: RMS norm,
+ * Q/K/V projections as bf16 matrix-vector products, per-head QK-RMSNorm,
+ * RoPE, K/V append into the layer's KV ring, causal GQA attention, O
+ * projection, residual; [LMP] "Choreography Per Chunk" steps 1-4; [SC] the
+ * model config and "KV-Cache").  For B tokens at positions pos0 .. pos0+B-1:
+ *   xn = bf16(RMSNorm(x))                      unit gain, eps, fp32;
+ *   [q; k; v] = Wqkv xn                        fp32 accumulation;
+ *   q_h, k_g <- RMSNorm (unit gain, eps) of each head, then RoPE at the
+ *     token's position p: pair (i, i + hd/2) rotated by p * rope_theta^(-2i/hd);
+ *   K[g, p mod ctx] = bf16(k_g), V[g, p mod ctx] = bf16(v_g)   (all B first);
+ *   o_h = softmax_j(q_h . K[g, j] / sqrt(hd)) V[g, j], g = h / (H / Hkv),
+ *     over the cached positions j <= p that the ring holds after the call
+ *     (p_last - ctx + 1 .. p_last);
+ *   out = x + Wo bf16(o).
+ * Supported: head_dim 128; H % Hkv == 0 with H / Hkv <= 16; d_model and
+ * num_heads * 128 each one of 512, 1024, 2048, 4096, 8192; ctx >= 1 and
+ * B <= min(ctx, 64); else SMOE_EUNSUPPORTED. */
+typedef struct smoe_attn_desc {
+  double rope_theta;      /* e.g. 1e6; > 0 */
+  int64_t ctx;            /* KV ring slots per layer */
+  int32_t d_model;
+  int32_t num_heads;      /* query heads H */
+  int32_t num_kv_heads;   /* key/value heads Hkv */
+  int32_t head_dim;       /* must be 128 */
+  float eps;              /* RMS norm epsilon, > 0 */
+  int32_t reserved;       /* 0 */
+} smoe_attn_desc;
+
+/* Bytes of device workspace for calls of up to max_batch (1..64) tokens; 0
+ * when the descriptor is unsupported.  Host only. */
+size_t smoe_attn_workspace_size(const smoe_attn_desc* desc, int32_t max_batch);
+
+/* One call of the block (a decode step, B <= 2, or B tokens of a chunk):
+ *   wqkv  [(H + 2 Hkv) 128, d_model] bf16 bits, rows of q, then k, then v;
+ *   wo    [d_model, H 128] bf16 bits;
+ *   x     [B, d_model] f32; out [B, d_model] f32 (out may be x);
+ *   k_cache, v_cache  [Hkv, ctx, 128] bf16 bits, updated in place; slots not
+ *         written by this call must hold the K/V of the positions the ring
+ *         covers (pos0 - ctx + B .. pos0 - 1, where >= 0).
+ * Pointers are device pointers, 16-byte aligned; pos0 >= 0.  Errors as
+ * smoe_route; B == 0 is a no-op. */
+int smoe_attn_forward(const smoe_attn_desc* desc, const uint16_t* wqkv, const uint16_t* wo,
+                      const float* x, int32_t B, int64_t pos0, uint16_t* k_cache,
+                      uint16_t* v_cache, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Diagnostic: one stage of smoe_attn_forward (0: norm + QKV projection;
+ * 1: QK-norm, RoPE, K/V append, attention; 2: O projection + residual), for
+ * per-kernel timing; the event pair (hipEvent_t, both or neither) brackets
+ * that stage's main kernel. */
+int smoe_attn_forward_stage(int stage, const smoe_attn_desc* desc, const uint16_t* wqkv,
+                            const uint16_t* wo, const float* x, int32_t B, int64_t pos0,
+                            uint16_t* k_cache, uint16_t* v_cache, float* out, void* ws,
+                            size_t ws_bytes, void* stream, void* start_event, void* stop_event);
+
 /* ----------------------------------------------------- between layers */
 /* The norm between stacked layers, h <- RMSNorm(h + MoE(h)): run
  * smoe_moe_layer with residual = h, then this on its output.  The backbone

@@ -32,6 +32,10 @@ T_RESIDUAL = 7
 T_SHARED_GATE = 8
 T_SHARED_UP = 9
 T_SHARED_DOWN = 10
+T_ATTN_QKV = 11
+T_ATTN_O = 12
+T_K_CACHE = 13
+T_V_CACHE = 14
 
 RMS_EPS = 1e-6
 
@@ -97,6 +101,14 @@ def router(seed, layer, E, d, sigma, bf16: bool) -> np.ndarray:
     """[E, d] router gate: fp32, or bf16 bit patterns (uint16) when ``bf16``."""
     out = np.empty((E, d), np.uint16 if bf16 else np.float32)
     lib().synth_router(seed, layer, T_ROUTER, E, d, sigma, int(bf16), _ptr(out))
+    return out
+
+
+def bf16_matrix(seed, layer, tensor, rows, cols, sigma) -> np.ndarray:
+    """[rows, cols] bf16 bit patterns (uint16) of sigma * N(0, 1), round to
+    nearest even: the attention projections and the prior KV-ring contents."""
+    out = np.empty((rows, cols), np.uint16)
+    lib().synth_router(seed, layer, tensor, rows, cols, sigma, 1, _ptr(out))
     return out
 
 

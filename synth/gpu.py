@@ -70,6 +70,13 @@ def normals(seed, layer, tensor, stream_id, start, n, sigma=1.0, device="cuda"):
     return out
 
 
+def bf16_matrix(seed, layer, tensor, rows, cols, sigma, device="cuda"):
+    """The same bits as synth.bf16_matrix, as an int16 tensor on the device."""
+    out = torch.empty(rows, cols, dtype=torch.int16, device=device)
+    _ok(lib().synth_gpu_router(seed, layer, tensor, rows, cols, sigma, 1, out.data_ptr(), _s()))
+    return out
+
+
 def router(seed, layer, E, d, sigma, bf16, device="cuda"):
     out = torch.empty(E, d, dtype=torch.int16 if bf16 else torch.float32, device=device)
     _ok(lib().synth_gpu_router(seed, layer, T_ROUTER, E, d, sigma, int(bf16), out.data_ptr(), _s()))

@@ -181,6 +181,41 @@ def test_shared_expert_arguments(smoe):
                   1 << 30, None) == smoe.SMOE_EINVAL
 
 
+def test_attention_arguments(smoe):
+    ok = dict(d_model=4096, num_heads=64, num_kv_heads=4, ctx=4096)
+    assert smoe.attn_workspace_size(smoe.make_attn_desc(**ok), 1) > 0
+    for kw, code in ((dict(head_dim=64), -2), (dict(num_heads=48), -2),          # 48*128 not 2^k*512
+                     (dict(num_heads=64, num_kv_heads=3), -2), (dict(num_kv_heads=2), -2),
+                     (dict(d_model=3072), -2), (dict(d_model=16384), -2), (dict(ctx=0), -2),
+                     (dict(eps=0.0), -1), (dict(rope_theta=-1.0), -1)):
+        d = smoe.make_attn_desc(**dict(ok, **kw))
+        assert smoe.attn_workspace_size(d, 1) == 0, kw
+    desc = smoe.make_attn_desc(**ok)
+    f = ctypes.c_void_p(4096)
+    big = 1 << 30
+    fw = smoe.lib.smoe_attn_forward
+
+    def call(B=1, pos0=0, w=f, out=f, ws=f, n=big, d=desc):
+        return fw(ctypes.byref(d), w, f, f, B, pos0, f, f, out, ws, n, None)
+
+    assert call(B=-1) == smoe.SMOE_EINVAL
+    assert call(B=65) == smoe.SMOE_EUNSUPPORTED
+    small = smoe.make_attn_desc(**dict(ok, ctx=4))
+    assert call(B=5, d=small) == smoe.SMOE_EUNSUPPORTED        # more tokens than ring slots
+    assert call(pos0=-1) == smoe.SMOE_EINVAL
+    assert call(B=0, w=None, out=None) == smoe.SMOE_OK         # nothing to do
+    assert call(w=None) == smoe.SMOE_EINVAL
+    assert call(out=ctypes.c_void_p(4096 + 8)) == smoe.SMOE_EINVAL
+    assert call(ws=ctypes.c_void_p(4096 + 16)) == smoe.SMOE_EINVAL
+    assert call(n=1024) == smoe.SMOE_EWORKSPACE
+    bad = smoe.make_attn_desc(**ok)
+    bad.reserved = 1
+    assert call(d=bad) == smoe.SMOE_EINVAL
+    st = smoe.lib.smoe_attn_forward_stage
+    assert st(3, ctypes.byref(desc), f, f, f, 1, 0, f, f, f, f, big, None, None, None) == smoe.SMOE_EINVAL
+    assert st(0, ctypes.byref(desc), f, f, f, 1, 0, f, f, f, f, big, None, f, None) == smoe.SMOE_EINVAL
+
+
 def test_stage_argument_errors(smoe):
     d = desc_of(smoe)
     f = 4096
