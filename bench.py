@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--stack", action="store_true",
                    help="run only the stacked harness (94 layers: prompt chunks, then decode)")
     p.add_argument("--no-stack", action="store_true", help="leave the stacked harness out")
+    p.add_argument("--attention", action="store_true",
+                   help="only the attention block around the layer (decode and 64-token chunks)")
     p.add_argument("--shared", action="store_true",
                    help="only the layer with a shared expert (decode and prefill), beside the "
                         "same layer without one")
@@ -196,6 +198,120 @@ def shared_bench(smoe, args):
                       "hbm_frac": round(g64 / HBM_PEAK_GBPS, 4),
                       "plain_layer_us": round(p64 * 1e6, 3),
                       "shared_cost_us": round((t64 - p64) * 1e6, 3)},
+    }
+
+
+def _blas_threads():
+    """Threads numpy's BLAS uses (the attention oracle's matrix products)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:
+        return os.cpu_count() or 1
+
+
+ATTN_SHAPE = dict(d_model=4096, num_heads=64, num_kv_heads=4, ctx=4096, rope_theta=1.0e6)
+
+
+def attention_bench(smoe, args):
+    """The attention block around the layer (d 4096, 64 query and 4 key/value
+    heads of 128, a 4096-slot bf16 KV ring, RoPE theta 1e6): decode steps at
+    B = 1 with the ring full (each step appends and wraps), over 16 distinct
+    layers resident in HBM; then 64-token chunks.  Weights bf16 N(0, 0.02),
+    prior ring contents N(0, 1), hidden states RMS-normalised N(0, 1)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import synth.gpu as sg
+    from oracle import attention as A
+    sh = ATTN_SHAPE
+    d, H, G, ctx = sh["d_model"], sh["num_heads"], sh["num_kv_heads"], sh["ctx"]
+    hd = 128
+    rows = (H + 2 * G) * hd
+    desc = smoe.make_attn_desc(d, H, G, ctx, rope_theta=sh["rope_theta"])
+    nl = args.layers
+    layers = []
+    for l in range(nl):
+        wqkv = sg.bf16_matrix(0, l, synth.T_ATTN_QKV, rows, d, 0.02)
+        wo = sg.bf16_matrix(0, l, synth.T_ATTN_O, d, H * hd, 0.02)
+        kc = sg.bf16_matrix(0, l, synth.T_K_CACHE, G * ctx, hd, 1.0)
+        vc = sg.bf16_matrix(0, l, synth.T_V_CACHE, G * ctx, hd, 1.0)
+        layers.append((wqkv, wo, kc, vc))
+    dev = torch.device("cuda:0")
+    ws = torch.zeros(smoe.attn_workspace_size(desc, 64), dtype=torch.uint8, device=dev)
+    xs1 = [sg.hidden(0, 0, 3000 + i, 1, d) for i in range(64)]
+    out = torch.empty(64, d, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i, B, xs, pos):
+        wqkv, wo, kc, vc = layers[i % nl]
+        smoe.attn_forward(desc, wqkv, wo, xs[i % len(xs)], pos, kc, vc, out[:B], ws)
+
+    def timed(fn, n, warm):
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    pos_base = ctx - 1                     # the ring is full from the first step on
+    t1 = timed(lambda i: step(i, 1, xs1, pos_base + i // nl), args.steps, args.warmup)
+    # the QKV projection alone, back to back (HIP events on its launch stream)
+    def qkv_only(i):
+        wqkv, wo, kc, vc = layers[i % nl]
+        smoe.attn_forward_stage(0, desc, wqkv, wo, xs1[i % 64], pos_base, kc, vc, out[:1], ws)
+
+    tq = timed(qkv_only, min(args.steps, 2000), 20)
+    qkv_bytes = rows * d * 2
+    kv_bytes = 2 * G * ctx * hd * 2
+    step_bytes = qkv_bytes + d * H * hd * 2 + kv_bytes
+    xs64 = [sg.hidden(0, 0, 4000 + i, 64, d) for i in range(4)]
+    t64 = timed(lambda i: step(i, 64, xs64, pos_base + 64 * (i // nl + 1)),
+                max(4, args.prefill_steps // 10), 2)
+    # the oracle (as it stands) on one decode step of layer 0, from CPU-generated inputs
+    cfg = A.AttnConfig(d_model=d, num_heads=H, num_kv_heads=G, ctx=ctx, rope_theta=sh["rope_theta"])
+    Wq = synth.bf16_matrix(0, 0, synth.T_ATTN_QKV, rows, d, 0.02)
+    Wo_ = synth.bf16_matrix(0, 0, synth.T_ATTN_O, d, H * hd, 0.02)
+    kc64 = A.bf16_bits_to_f64(synth.bf16_matrix(0, 0, synth.T_K_CACHE, G * ctx, hd, 1.0)).reshape(G, ctx, hd)
+    vc64 = A.bf16_bits_to_f64(synth.bf16_matrix(0, 0, synth.T_V_CACHE, G * ctx, hd, 1.0)).reshape(G, ctx, hd)
+    x0 = synth.hidden(0, 0, 3000, 1, d)
+    n_cpu, t0 = 0, time.perf_counter()
+    while True:
+        A.attention_block(cfg, Wq, Wo_, x0, pos_base + n_cpu, kc64, vc64)
+        n_cpu += 1
+        if time.perf_counter() - t0 > min(args.cpu_seconds, 10.0) or n_cpu >= 20:
+            break
+    cpu_s = (time.perf_counter() - t0) / n_cpu
+    del layers
+    torch.cuda.empty_cache()
+    return {
+        "metric": "attention block: decode tokens/s (B=1, full 4096-slot KV ring)",
+        "value": round(1.0 / t1, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t1 * 1e3, 5), "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "attn_d4096_h64_kv4_hd128_ctx4096: RMS norm, bf16 QKV projection, "
+                               "QK-norm, RoPE (theta 1e6), K/V append, causal GQA attention over the "
+                               "full ring, bf16 O projection + residual; B=1 decode",
+                   "layers_rotated": nl, "effective_bytes_per_step": step_bytes},
+        "effective_gbps": round(step_bytes / t1 / 1e9, 1),
+        "hbm_frac": round(step_bytes / t1 / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_bf16<1, 8> (QKV projection)",
+                     "achieved": round(qkv_bytes / tq / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(qkv_bytes / tq / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "bytes_per_launch": qkv_bytes,
+                     "mean_launch_us": round(tq * 1e6, 3)},
+        "secondary": {"workload": "the same block on 64-token chunks (two tokens per "
+                                  "matrix-vector pass; not yet a batched projection)",
+                      "tokens_per_s": round(64 / t64, 1), "ms_per_step": round(t64 * 1e3, 4)},
+        "cpu_baseline": {"value": round(1.0 / cpu_s, 3), "unit": "tokens/s", "cores": _blas_threads(),
+                         "kind": "oracle",
+                         "sample": f"{n_cpu} decode steps of layer 0 at a full ring, numpy float64"},
     }
 
 
@@ -512,6 +628,9 @@ def main():
     torch.cuda.set_device(0)
     if args.shared:
         print(json.dumps(shared_bench(smoe, args)), flush=True)
+        return
+    if args.attention:
+        print(json.dumps(attention_bench(smoe, args)), flush=True)
         return
     if args.stack:
         r = stack_harness(smoe, args.stack_layers, args.stack_prompt, args.stack_decode)

@@ -516,9 +516,7 @@ int attn_setup(const smoe_attn_desc* D, const uint16_t* wqkv, const uint16_t* wo
   a->nsplit = (int)((window + smoe::kAttnSplit - 1) / smoe::kAttnSplit);
   a->theta = D->rope_theta;
   a->eps = D->eps;
-  a->xb = ws_at<uint16_t>(ws, lay.xb);
   a->qkv = ws_at<float>(ws, lay.qkv);
-  a->q = ws_at<float>(ws, lay.q);
   a->part_o = ws_at<float>(ws, lay.part_o);
   a->part_ml = ws_at<float>(ws, lay.part_ml);
   a->ob = ws_at<uint16_t>(ws, lay.ob);

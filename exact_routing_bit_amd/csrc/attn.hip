@@ -4,25 +4,24 @@
 // ring -> causal GQA attention -> O projection -> residual; "Surface Scout",
 // the model config and "KV-Cache").
 //
-// Five kernels per call of B tokens at positions pos0 .. pos0+B-1:
-//  k_attn_in      RMS norm of each token (block_row_inv, unit gain), rounded
-//                 to bf16: the projection's input;
-//  k_gemv_bf16    out[t, r] (+)= sum_c W[r, c] x[t, c] for bf16 W [R, C] and
-//                 bf16 x, fp32 accumulation (v_dot2_f32_bf16): the QKV
-//                 projection, and later the O projection with the residual;
-//                 one 4-wave block per CU, each wave streaming 16-byte pieces
-//                 of its rows through a two-item ring of raw buffer loads
-//                 (constant per-lane offsets, the rows' place in scalar
-//                 registers), x of the tokens in LDS;
-//  k_attn_prep    per (token, head vector): QK-norm and RoPE of q and k (the
-//                 angle pos * theta^(-2i/hd) in fp64, the rotate-half pairs
-//                 (i, i + 64) in one lane), q kept in fp32, k and v rounded
-//                 to bf16 into ring slot pos mod ctx;
-//  k_attn_decode  per (256-position split, key/value head, token): the split's
-//                 scores for the head's 16 query heads, their max and
+// Four launches per call of B tokens at positions pos0 .. pos0+B-1:
+//  k_gemv_bf16    QKV projection: out[t, r] = sum_c W[r, c] x[t, c] for bf16
+//                 W [R, C] and bf16 x, fp32 accumulation (v_dot2_f32_bf16),
+//                 x = bf16(RMSNorm(x)) formed by each block into LDS (unit
+//                 gain); one 4-wave block per CU, each wave streaming 16-byte
+//                 pieces of its rows through a two-item ring of range-checked
+//                 buffer loads (constant per-lane offsets), row sums staged
+//                 in LDS and written after the loop;
+//  k_attn_decode  per (256-position split, key/value head, token): appends
+//                 the call's K/V that fall in the split (QK-norm and RoPE of
+//                 k, the angle pos * theta^(-2i/hd) in fp64, the rotate-half
+//                 pair (i, i + 64) in one lane; bf16 into ring slot pos mod
+//                 ctx), forms its query heads the same way, stages the
+//                 split's V in LDS and computes the scores, their max and
 //                 exponent sum, and the exponent-weighted sum of V;
 //  k_attn_merge   per (query head, token): the splits combined in order,
-//                 rounded to bf16 (the O projection's input).
+//                 rounded to bf16 (the O projection's input);
+//  k_gemv_bf16    O projection plus the residual.
 #include <algorithm>
 
 #include "device.hpp"
@@ -48,22 +47,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// ------------------------------------------------------------- k_attn_in
-__global__ __launch_bounds__(kAttnThreads) void k_attn_in(const float* x, int d, float eps,
-                                                          uint16_t* xb) {
-  __shared__ float part[kAttnThreads / 64];
-  const int t = blockIdx.x;
-  const float* row = x + (int64_t)t * d;
-  const float inv = block_row_inv(row, d, eps, part);
-  const float4* r4 = reinterpret_cast<const float4*>(row);
-  uint2* o2 = reinterpret_cast<uint2*>(xb + (int64_t)t * d);
-  for (int i = threadIdx.x; i < d / 4; i += kAttnThreads) {
-    const float4 v = r4[i];
-    o2[i] = make_uint2(bf16_rne(v.x * inv) | (bf16_rne(v.y * inv) << 16),
-                       bf16_rne(v.z * inv) | (bf16_rne(v.w * inv) << 16));
-  }
-}
 
 // ----------------------------------------------------------- k_gemv_bf16
 // Lane l reads the 8 values at columns 512 m + 8 l (m < C/512) of each row.
@@ -136,15 +119,34 @@ __device__ __forceinline__ void gemv_compute(const uint4 (*xs)[kChunks * 64], in
 
 constexpr int kGemvMaxItems = 16;     // items per wave (their sums staged in LDS)
 
-// out[t, r] = (residual[t, r] +) sum_c Wm[r, c] x[t, c], t < NTOK, C = 512 kChunks.
+// out[t, r] = (residual[t, r] +) sum_c Wm[r, c] x[t, c], t < NTOK, C = 512 kChunks,
+// with x the bf16 rows given, or (xf set) bf16(RMSNorm(xf[t])) formed by every
+// block for itself (block_row_inv, unit gain).
 template <int NTOK, int kChunks>
 __global__ __launch_bounds__(kAttnThreads) void k_gemv_bf16(const uint16_t* Wm, int R,
-                                                            const uint16_t* x,
-                                                            const float* residual, float* out) {
+                                                            const uint16_t* x, const float* xf,
+                                                            float eps, const float* residual,
+                                                            float* out) {
   constexpr int C = kChunks * 512;
   __shared__ uint4 xs[NTOK][C / 8];
-  for (int i = threadIdx.x; i < NTOK * (C / 8); i += kAttnThreads)
-    xs[i / (C / 8)][i % (C / 8)] = reinterpret_cast<const uint4*>(x)[i];
+  __shared__ float part[kAttnThreads / 64];
+  if (xf != nullptr) {
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) {
+      const float* row = xf + (int64_t)t * C;
+      const float inv = block_row_inv(row, C, eps, part);
+      const float4* r4 = reinterpret_cast<const float4*>(row);
+      uint2* x2 = reinterpret_cast<uint2*>(xs[t]);
+      for (int i = threadIdx.x; i < C / 4; i += kAttnThreads) {
+        const float4 v = r4[i];
+        x2[i] = make_uint2(bf16_rne(v.x * inv) | (bf16_rne(v.y * inv) << 16),
+                           bf16_rne(v.z * inv) | (bf16_rne(v.w * inv) << 16));
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < NTOK * (C / 8); i += kAttnThreads)
+      xs[i / (C / 8)][i % (C / 8)] = reinterpret_cast<const uint4*>(x)[i];
+  }
   __syncthreads();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -179,169 +181,198 @@ __global__ __launch_bounds__(kAttnThreads) void k_gemv_bf16(const uint16_t* Wm, 
   }
 }
 
-// ------------------------------------------------------------ k_attn_prep
-// One wave per (head vector, token): vectors 0 .. H-1 are q, then Hkv k, then
-// Hkv v.  Lane l holds elements l and l + 64, the pair RoPE rotates together.
-__global__ __launch_bounds__(kAttnThreads) void k_attn_prep(AttnArgs a) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+// ------------------------------------------------------------- attention
+// QK-norm (unit gain) and RoPE at position pos of one head vector held as
+// (x0, x1) = elements (lane, lane + 64): the rotate-half pair of one lane.
+__device__ __forceinline__ void qk_norm_rope(float& x0, float& x1, int64_t pos, double theta,
+                                             float eps) {
   const int lane = threadIdx.x & 63;
-  const int H = a.H, G = a.Hkv;
-  const int vec = blockIdx.x * (kAttnThreads / 64) + wave;
-  if (vec >= H + 2 * G) return;
-  const int t = blockIdx.y;
-  const int64_t pos = a.pos0 + t;
-  const float* src = a.qkv + (int64_t)t * a.qkv_rows + (int64_t)vec * kHd;
-  float x0 = src[lane], x1 = src[lane + 64];
-  const bool is_v = vec >= H + G;
-  if (!is_v) {
-    // QK-norm (unit gain), then RoPE at the token's absolute position
-    const float ss = wave_sum(x0 * x0 + x1 * x1);
-    const float inv = 1.0f / sqrtf(ss / (float)kHd + a.eps);
-    x0 *= inv;
-    x1 *= inv;
-    const double ang = (double)pos * pow(a.theta, -2.0 * (double)lane / (double)kHd);
-    const float c = (float)cos(ang), s = (float)sin(ang);
-    const float r0 = x0 * c - x1 * s, r1 = x1 * c + x0 * s;
-    x0 = r0;
-    x1 = r1;
-  }
-  if (vec < H) {
-    float* q = a.q + ((int64_t)t * H + vec) * kHd;
-    q[lane] = x0;
-    q[lane + 64] = x1;
-  } else {
-    const bool is_k = !is_v;
-    const int g = is_k ? vec - H : vec - H - G;
-    uint16_t* cache = is_k ? a.k_cache : a.v_cache;
-    const int64_t slot = pos % a.ctx;
-    uint16_t* dst = cache + ((int64_t)g * a.ctx + slot) * kHd;
-    dst[lane] = (uint16_t)bf16_rne(x0);
-    dst[lane + 64] = (uint16_t)bf16_rne(x1);
-  }
+  const float ss = wave_sum(x0 * x0 + x1 * x1);
+  const float inv = 1.0f / sqrtf(ss / (float)kHd + eps);
+  x0 *= inv;
+  x1 *= inv;
+  const double ang = (double)pos * pow(theta, -2.0 * (double)lane / (double)kHd);
+  const float c = (float)cos(ang), s = (float)sin(ang);
+  const float r0 = x0 * c - x1 * s, r1 = x1 * c + x0 * s;
+  x0 = r0;
+  x1 = r1;
 }
 
-// ---------------------------------------------------------- k_attn_decode
-// Block (split s, key/value head g, token t): the split's positions are
-// start .. start + n - 1 with start = lo + 256 s (lo: the first position the
-// ring holds) and n clipped to the token's own position.  Writes, per query
-// head of the group, m = the max score, l = sum exp(score - m) and
-// o = sum exp(score - m) v (unnormalised); an empty split writes l = 0.
+// Block (split s, key/value head g, token t).  The split's positions are
+// start .. start + 255 with start = lo + 256 s (lo: the first position the
+// ring holds after the call); token t reads n of them, up to its own.
+//  1. The call's K/V that fall in the split are formed (k: QK-norm + RoPE;
+//     v as is) and appended, by every token's block of the split alike (the
+//     same bits), so that each block reads what it wrote after its barrier.
+//  2. The group's G query heads of token t: QK-norm + RoPE, scaled by
+//     1/sqrt(hd), into LDS.
+//  3. V of the split into LDS (all loads issued first, in flight during 4).
+//  4. Scores: thread j takes position start + j against every head; then per
+//     head the max m, p = exp(score - m) and l = sum p.
+//  5. o = sum_j p_j v_j per head.  Writes (m, l) and o; an empty split
+//     writes l = 0.
 __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   __shared__ float qs[kMaxGroup][kHd];
   __shared__ float ps[kMaxGroup][kSplit];
-  __shared__ float red[kMaxGroup][kAttnThreads / 64];
+  __shared__ uint4 vl[kSplit][kHd / 8];
+  __shared__ uint4 kl[kSplit][kHd / 8 + 1];        // padded rows: conflict-free chunk reads
   const int s = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = a.H / a.Hkv;                       // query heads of this group
+  const int G = a.H / a.Hkv;
   const int64_t pos = a.pos0 + t;
   const int64_t p_last = a.pos0 + a.B - 1;
   const int64_t lo = p_last - a.ctx + 1 > 0 ? p_last - a.ctx + 1 : 0;
   const int64_t start = lo + (int64_t)s * kSplit;
+  // 1. the call's K/V in this split
+  const int64_t a_lo = start > a.pos0 ? start : a.pos0;
+  const int64_t a_hi = start + kSplit - 1 < p_last ? start + kSplit - 1 : p_last;
+  for (int64_t p = a_lo + wave; p <= a_hi; p += kAttnThreads / 64) {
+    const float* src = a.qkv + (p - a.pos0) * a.qkv_rows;
+    const float* ks = src + (int64_t)(a.H + g) * kHd;
+    const float* vsrc = src + (int64_t)(a.H + a.Hkv + g) * kHd;
+    float k0 = ks[lane], k1 = ks[lane + 64];
+    const float v0 = vsrc[lane], v1 = vsrc[lane + 64];
+    qk_norm_rope(k0, k1, p, a.theta, a.eps);
+    const int64_t row = ((int64_t)g * a.ctx + p % a.ctx) * kHd;
+    a.k_cache[row + lane] = (uint16_t)bf16_rne(k0);
+    a.k_cache[row + lane + 64] = (uint16_t)bf16_rne(k1);
+    a.v_cache[row + lane] = (uint16_t)bf16_rne(v0);
+    a.v_cache[row + lane + 64] = (uint16_t)bf16_rne(v1);
+  }
+  // 2. the group's queries (rows G .. 15 zero: the loops below run over all
+  //    16 rows without a branch on G, whose LDS reads would each wait)
+  const float scale = 1.0f / sqrtf((float)kHd);
+  for (int i = G * kHd + tid; i < kMaxGroup * kHd; i += kAttnThreads) qs[i / kHd][i % kHd] = 0.f;
+  for (int h = wave; h < G; h += kAttnThreads / 64) {
+    const float* qsrc = a.qkv + (int64_t)t * a.qkv_rows + (int64_t)(g * G + h) * kHd;
+    float q0 = qsrc[lane], q1 = qsrc[lane + 64];
+    qk_norm_rope(q0, q1, pos, a.theta, a.eps);
+    qs[h][lane] = q0 * scale;
+    qs[h][lane + 64] = q1 * scale;
+  }
   const int64_t avail = pos + 1 - start;
   const int n = avail <= 0 ? 0 : (avail >= kSplit ? kSplit : (int)avail);
   const int64_t base = (((int64_t)t * a.Hkv + g) * a.nsplit + s) * kMaxGroup;
   float* po = a.part_o + base * kHd;
   float2* pml = reinterpret_cast<float2*>(a.part_ml) + base;
-  if (n == 0) {                                    // whole block
+  if (n == 0) {                                    // whole block; its appends are done
     if (tid < kMaxGroup) pml[tid] = make_float2(0.f, 0.f);
     return;
   }
-  // the group's queries, scaled by 1/sqrt(hd)
-  const float scale = 1.0f / sqrtf((float)kHd);
-  for (int i = tid; i < G * kHd; i += kAttnThreads)
-    qs[i / kHd][i % kHd] = a.q[((int64_t)t * a.H + (int64_t)g * G + i / kHd) * kHd + i % kHd] * scale;
-  __syncthreads();
+  __syncthreads();                                 // appends and queries visible to the block
   const int64_t slot0 = start % a.ctx;
-  // scores: thread j takes position start + j
-  const bool live = tid < n;
-  int64_t slot = slot0 + (live ? tid : 0);
-  if (slot >= a.ctx) slot -= a.ctx;
-  const uint4* krow = reinterpret_cast<const uint4*>(a.k_cache + ((int64_t)g * a.ctx + slot) * kHd);
-  float sc[kMaxGroup];
+  // 3. K and V of the split into LDS: thread i copies 16-byte piece i % 16 of
+  //    row i / 16 (i = tid + 256 k) of each, every load issued first
+  {
+    constexpr int kPieces = kSplit * (kHd / 8) / kAttnThreads;
+    const uint4* kbase = reinterpret_cast<const uint4*>(a.k_cache + (int64_t)g * a.ctx * kHd);
+    const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache + (int64_t)g * a.ctx * kHd);
+    uint4 kr[kPieces], vr[kPieces];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) sc[h] = 0.f;
-#pragma unroll 4
+    for (int k = 0; k < kPieces; ++k) {
+      const int i = tid + kAttnThreads * k, j = i >> 4, c = i & 15;
+      int64_t sl = slot0 + (j < n ? j : 0);
+      if (sl >= a.ctx) sl -= a.ctx;
+      kr[k] = kbase[sl * (kHd / 8) + c];
+      vr[k] = vbase[sl * (kHd / 8) + c];
+    }
+#pragma unroll
+    for (int k = 0; k < kPieces; ++k) {
+      const int i = tid + kAttnThreads * k;
+      kl[i >> 4][i & 15] = kr[k];
+      vl[i >> 4][i & 15] = vr[k];
+    }
+  }
+  __syncthreads();
+  // 4. wave w takes query heads 4w .. 4w+3 (rows G .. 15 of qs are zero) over
+  //    all the split's positions, lane l positions l + 64 m (m < 4): four
+  //    positions share each read of a query chunk, one 16-byte key chunk at a time
+  const int hb = 4 * wave;
+  float sc[4][4];                                  // [position m][head hh]
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) sc[m][hh] = 0.f;
+#pragma unroll 2
   for (int c = 0; c < kHd / 8; ++c) {
-    const uint4 kv = krow[c];
-    const float kf[8] = {bf16_lo(kv.x), bf16_hi(kv.x), bf16_lo(kv.y), bf16_hi(kv.y),
-                         bf16_lo(kv.z), bf16_hi(kv.z), bf16_lo(kv.w), bf16_hi(kv.w)};
+    float kf[4][8];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < G) {
-        const float4 qa = *reinterpret_cast<const float4*>(&qs[h][c * 8]);
-        const float4 qb = *reinterpret_cast<const float4*>(&qs[h][c * 8 + 4]);
-        float acc = sc[h];
-        acc = __builtin_fmaf(qa.x, kf[0], acc);
-        acc = __builtin_fmaf(qa.y, kf[1], acc);
-        acc = __builtin_fmaf(qa.z, kf[2], acc);
-        acc = __builtin_fmaf(qa.w, kf[3], acc);
-        acc = __builtin_fmaf(qb.x, kf[4], acc);
-        acc = __builtin_fmaf(qb.y, kf[5], acc);
-        acc = __builtin_fmaf(qb.z, kf[6], acc);
-        acc = __builtin_fmaf(qb.w, kf[7], acc);
-        sc[h] = acc;
+    for (int m = 0; m < 4; ++m) {
+      const uint4 kv = kl[lane + 64 * m][c];
+      kf[m][0] = bf16_lo(kv.x); kf[m][1] = bf16_hi(kv.x);
+      kf[m][2] = bf16_lo(kv.y); kf[m][3] = bf16_hi(kv.y);
+      kf[m][4] = bf16_lo(kv.z); kf[m][5] = bf16_hi(kv.z);
+      kf[m][6] = bf16_lo(kv.w); kf[m][7] = bf16_hi(kv.w);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const float4 qa = *reinterpret_cast<const float4*>(&qs[hb + hh][c * 8]);
+      const float4 qb = *reinterpret_cast<const float4*>(&qs[hb + hh][c * 8 + 4]);
+      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float x = sc[m][hh];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x = __builtin_fmaf(qv[e], kf[m][e], x);
+        sc[m][hh] = x;
       }
     }
   }
-  // per head: the split's max, the exponents and their sum
+  // per head (all within the wave): m over the split, p = exp(score - m)
+  // (0 past n) into the wave's own rows of ps, l = sum p
+  float mh[4], lh[4];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h < G) {
-      const float m = wave_max(live ? sc[h] : -FLT_MAX);
-      if (lane == 0) red[h][wave] = m;
+  for (int hh = 0; hh < 4; ++hh) {
+    float mx = -FLT_MAX;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) mx = fmaxf(mx, lane + 64 * m < n ? sc[m][hh] : -FLT_MAX);
+    mh[hh] = wave_max(mx);
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float p = lane + 64 * m < n ? expf(sc[m][hh] - mh[hh]) : 0.f;
+      ps[hb + hh][lane + 64 * m] = p;
+      acc += p;
     }
+    lh[hh] = wave_sum(acc);
   }
-  __syncthreads();
-  float mh[kMaxGroup];
+  // 5. o[h][d] = sum_j p[h][j] v[j][d] for the wave's heads, lane: dims 2 lane,
+  //    2 lane + 1; four positions a step (p past n is 0, rows past n finite);
+  //    the wave reads only the rows of ps it wrote
+  float o0[4], o1[4];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h)
-    mh[h] = h < G ? fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3])) : 0.f;
-  __syncthreads();                                 // red is reused below
+  for (int hh = 0; hh < 4; ++hh) o0[hh] = o1[hh] = 0.f;
+  const int n4 = (n + 3) & ~3;
+#pragma unroll 2
+  for (int j = 0; j < n4; j += 4) {
+    float v0[4], v1[4];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h < G) {
-      const float p = live ? expf(sc[h] - mh[h]) : 0.f;
-      ps[h][tid] = p;
-      const float ws = wave_sum(p);
-      if (lane == 0) red[h][wave] = ws;
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t vv = reinterpret_cast<const uint32_t*>(vl[j + u])[lane];
+      v0[u] = bf16_lo(vv);
+      v1[u] = bf16_hi(vv);
     }
-  }
-  __syncthreads();
-  // o[h][d] = sum_j p[h][j] v[j][d]: thread (dims 2 d2, 2 d2 + 1; heads wave, wave + 4, ...)
-  const int d2 = lane;
-  float o0[kMaxGroup / 4], o1[kMaxGroup / 4];
 #pragma unroll
-  for (int k = 0; k < kMaxGroup / 4; ++k) o0[k] = o1[k] = 0.f;
-  const uint32_t* vbase = reinterpret_cast<const uint32_t*>(a.v_cache + (int64_t)g * a.ctx * kHd);
-  int64_t vs = slot0;
-  for (int j = 0; j < n; ++j) {
-    const uint32_t vv = vbase[vs * (kHd / 2) + d2];
-    const float v0 = bf16_lo(vv), v1 = bf16_hi(vv);
+    for (int hh = 0; hh < 4; ++hh) {
+      const float4 p4 = *reinterpret_cast<const float4*>(&ps[hb + hh][j]);
+      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-    for (int k = 0; k < kMaxGroup / 4; ++k) {
-      const int h = wave + 4 * k;
-      if (h < G) {
-        const float p = ps[h][j];
-        o0[k] = __builtin_fmaf(p, v0, o0[k]);
-        o1[k] = __builtin_fmaf(p, v1, o1[k]);
+      for (int u = 0; u < 4; ++u) {
+        o0[hh] = __builtin_fmaf(pv[u], v0[u], o0[hh]);
+        o1[hh] = __builtin_fmaf(pv[u], v1[u], o1[hh]);
       }
     }
-    vs = vs + 1 == a.ctx ? 0 : vs + 1;
   }
 #pragma unroll
-  for (int k = 0; k < kMaxGroup / 4; ++k) {
-    const int h = wave + 4 * k;
+  for (int hh = 0; hh < 4; ++hh) {
+    const int h = hb + hh;
     if (h < G) {
       float* oh = po + (int64_t)h * kHd;
-      oh[2 * d2] = o0[k];
-      oh[2 * d2 + 1] = o1[k];
+      oh[2 * lane] = o0[hh];
+      oh[2 * lane + 1] = o1[hh];
+      if (lane == 0) pml[h] = make_float2(mh[hh], lh[hh]);
     }
-  }
-  if (tid < G) {
-    const int h = tid;
-    const float l = ((red[h][0] + red[h][1]) + red[h][2]) + red[h][3];
-    pml[h] = make_float2(mh[h], l);
   }
 }
 
@@ -352,20 +383,24 @@ __global__ __launch_bounds__(kHd) void k_attn_merge(AttnArgs a) {
   const int G = a.H / a.Hkv, g = h / G, hh = h % G;
   const int64_t base = (((int64_t)t * a.Hkv + g) * a.nsplit) * kMaxGroup + hh;
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
-  float M = -FLT_MAX;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const float2 ml = pml[base + (int64_t)s * kMaxGroup];
-    if (ml.y > 0.f) M = fmaxf(M, ml.x);
-  }
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < a.nsplit; ++s) {
-    const int64_t at = base + (int64_t)s * kMaxGroup;
+  // one pass, the running max rescaling what came before; no branch, so that
+  // the loads of a group of splits go out together (an empty split, l = 0,
+  // has an unwritten o, which the selects keep out)
+  float M = -FLT_MAX, num = 0.f, den = 0.f;
+  for (int s0 = 0; s0 < a.nsplit; s0 += 16) {       // groups of 16, indices clamped
+#pragma unroll
+   for (int u = 0; u < 16; ++u) {
+    const int s = s0 + u;
+    const int64_t at = base + (int64_t)(s < a.nsplit ? s : a.nsplit - 1) * kMaxGroup;
     const float2 ml = pml[at];
-    if (ml.y > 0.f) {
-      const float w = expf(ml.x - M);
-      num = __builtin_fmaf(w, a.part_o[at * kHd + d], num);
-      den = __builtin_fmaf(w, ml.y, den);
-    }
+    const float o = a.part_o[at * kHd + d];
+    const bool has = s < a.nsplit && ml.y > 0.f;
+    const float Mn = has ? fmaxf(M, ml.x) : M;
+    const float r = expf(M - Mn), w = has ? expf(ml.x - Mn) : 0.f;
+    num = __builtin_fmaf(w, has ? o : 0.f, num * r);
+    den = __builtin_fmaf(w, has ? ml.y : 0.f, den * r);
+    M = Mn;
+   }
   }
   a.ob[(int64_t)t * a.H * kHd + (int64_t)h * kHd + d] = (uint16_t)bf16_rne(num / den);
 }
@@ -384,8 +419,8 @@ int cu_count_attn() {
 }
 
 template <int NTOK, int kChunks>
-hipError_t launch_gemv_c(const uint16_t* Wm, int R, const uint16_t* x, const float* residual,
-                         float* out, hipStream_t s, const LaunchTiming* t) {
+hipError_t launch_gemv_c(const uint16_t* Wm, int R, const uint16_t* x, const float* xf, float eps,
+                         const float* residual, float* out, hipStream_t s, const LaunchTiming* t) {
   const int ncu = cu_count_attn();
   if (ncu <= 0) return hipErrorInvalidDevice;
   const int items = (R + GemvItem<kChunks>::kRows - 1) / GemvItem<kChunks>::kRows;
@@ -393,33 +428,36 @@ hipError_t launch_gemv_c(const uint16_t* Wm, int R, const uint16_t* x, const flo
   const int grid = std::max(std::min((items + 3) / 4, ncu),
                             (items + 4 * kGemvMaxItems - 1) / (4 * kGemvMaxItems));
   SMOE_LAUNCH(t, (k_gemv_bf16<NTOK, kChunks>), dim3(grid), dim3(kAttnThreads), 0, s, Wm, R, x,
-              residual, out);
+              xf, eps, residual, out);
   return hipGetLastError();
 }
 
 template <int NTOK>
-hipError_t launch_gemv_n(const uint16_t* Wm, int R, int C, const uint16_t* x,
-                         const float* residual, float* out, hipStream_t s, const LaunchTiming* t) {
+hipError_t launch_gemv_n(const uint16_t* Wm, int R, int C, const uint16_t* x, const float* xf,
+                         float eps, const float* residual, float* out, hipStream_t s,
+                         const LaunchTiming* t) {
   switch (C / 512) {
-    case 1: return launch_gemv_c<NTOK, 1>(Wm, R, x, residual, out, s, t);
-    case 2: return launch_gemv_c<NTOK, 2>(Wm, R, x, residual, out, s, t);
-    case 4: return launch_gemv_c<NTOK, 4>(Wm, R, x, residual, out, s, t);
-    case 8: return launch_gemv_c<NTOK, 8>(Wm, R, x, residual, out, s, t);
-    case 16: return launch_gemv_c<NTOK, 16>(Wm, R, x, residual, out, s, t);
+    case 1: return launch_gemv_c<NTOK, 1>(Wm, R, x, xf, eps, residual, out, s, t);
+    case 2: return launch_gemv_c<NTOK, 2>(Wm, R, x, xf, eps, residual, out, s, t);
+    case 4: return launch_gemv_c<NTOK, 4>(Wm, R, x, xf, eps, residual, out, s, t);
+    case 8: return launch_gemv_c<NTOK, 8>(Wm, R, x, xf, eps, residual, out, s, t);
+    case 16: return launch_gemv_c<NTOK, 16>(Wm, R, x, xf, eps, residual, out, s, t);
     default: return hipErrorInvalidValue;
   }
 }
 
-// out[t] = (residual[t] +) W x[t] for B tokens, two at a time.
-hipError_t launch_gemv_bf16(const uint16_t* Wm, int R, int C, const uint16_t* x, int B,
-                            const float* residual, float* out, hipStream_t s,
+// out[t] = (residual[t] +) W x[t] for B tokens, two at a time; x is either
+// bf16 rows or (xf) fp32 rows to normalise first.
+hipError_t launch_gemv_bf16(const uint16_t* Wm, int R, int C, const uint16_t* x, const float* xf,
+                            float eps, int B, const float* residual, float* out, hipStream_t s,
                             const LaunchTiming* t = nullptr) {
   for (int t0 = 0; t0 < B; t0 += 2) {
-    const uint16_t* xt = x + (int64_t)t0 * C;
+    const uint16_t* xt = x ? x + (int64_t)t0 * C : nullptr;
+    const float* xft = xf ? xf + (int64_t)t0 * C : nullptr;
     const float* rt = residual ? residual + (int64_t)t0 * R : nullptr;
     float* ot = out + (int64_t)t0 * R;
-    const hipError_t err = B - t0 >= 2 ? launch_gemv_n<2>(Wm, R, C, xt, rt, ot, s, t)
-                                       : launch_gemv_n<1>(Wm, R, C, xt, rt, ot, s, t);
+    const hipError_t err = B - t0 >= 2 ? launch_gemv_n<2>(Wm, R, C, xt, xft, eps, rt, ot, s, t)
+                                       : launch_gemv_n<1>(Wm, R, C, xt, xft, eps, rt, ot, s, t);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -438,17 +476,11 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage, const Launch
   hipError_t err = hipSuccess;
   const int rows = a.qkv_rows;
   if (stage < 0 || stage == 0) {
-    hipLaunchKernelGGL(k_attn_in, dim3(a.B), dim3(kAttnThreads), 0, s, a.x, a.d, a.eps, a.xb);
-    err = hipGetLastError();
-    if (err == hipSuccess)
-      err = launch_gemv_bf16(a.wqkv, rows, a.d, a.xb, a.B, nullptr, a.qkv, s, stage == 0 ? t : nullptr);
+    err = launch_gemv_bf16(a.wqkv, rows, a.d, nullptr, a.x, a.eps, a.B, nullptr, a.qkv, s,
+                           stage == 0 ? t : nullptr);
     if (err != hipSuccess) return err;
   }
   if (stage < 0 || stage == 1) {
-    const dim3 gp((a.H + 2 * a.Hkv + 3) / 4, a.B);
-    hipLaunchKernelGGL(k_attn_prep, gp, dim3(kAttnThreads), 0, s, a);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
     SMOE_LAUNCH(stage == 1 ? t : nullptr, k_attn_decode, dim3(a.nsplit, a.Hkv, a.B),
                 dim3(kAttnThreads), 0, s, a);
     err = hipGetLastError();
@@ -458,7 +490,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage, const Launch
     if (err != hipSuccess) return err;
   }
   if (stage < 0 || stage == 2)
-    err = launch_gemv_bf16(a.wo, a.d, a.H * kHd, a.ob, a.B, a.x, a.out, s, stage == 2 ? t : nullptr);
+    err = launch_gemv_bf16(a.wo, a.d, a.H * kHd, a.ob, nullptr, 0.f, a.B, a.x, a.out, s,
+                           stage == 2 ? t : nullptr);
   return err;
 }
 

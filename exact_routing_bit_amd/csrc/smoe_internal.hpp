@@ -159,9 +159,7 @@ constexpr int kAttnSplit = 256;     // cached positions per attention block
 
 // Workspace of the attention block for up to B tokens ([DF] layer loop).
 struct AttnWsLayout {
-  size_t xb;       // [B, d] bf16: the normed input
   size_t qkv;      // [B, (H + 2 Hkv) hd] f32
-  size_t q;        // [B, H, hd] f32 after QK-norm and RoPE
   size_t part_o;   // [B, Hkv, nsplit, 16, hd] f32
   size_t part_ml;  // [B, Hkv, nsplit, 16] (max, sum) pairs
   size_t ob;       // [B, H hd] bf16: the attention output
@@ -180,9 +178,7 @@ inline AttnWsLayout attn_ws_layout(const smoe_attn_desc& D, int B) {
   };
   const size_t hd = kAttnHeadDim, H = D.num_heads, G = D.num_kv_heads;
   const size_t ns = (size_t)attn_nsplit_max(D.ctx);
-  w.xb = take((size_t)B * D.d_model * 2);
   w.qkv = take((size_t)B * (H + 2 * G) * hd * 4);
-  w.q = take((size_t)B * H * hd * 4);
   w.part_o = take((size_t)B * G * ns * kAttnMaxGroup * hd * 4);
   w.part_ml = take((size_t)B * G * ns * kAttnMaxGroup * 8);
   w.ob = take((size_t)B * H * hd * 2);
@@ -201,9 +197,7 @@ struct AttnArgs {
   int64_t pos0, ctx;
   double theta;
   float eps;
-  uint16_t* xb;
   float* qkv;
-  float* q;
   float* part_o;
   float* part_ml;
   uint16_t* ob;
