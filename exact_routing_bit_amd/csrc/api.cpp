@@ -478,7 +478,7 @@ int check_attn(const smoe_attn_desc* D) {
   if (!(D->rope_theta > 0.0) || !(D->eps > 0.0f) || D->reserved != 0) return SMOE_EINVAL;
   if (!smoe::attn_shape_ok(D->d_model, D->num_heads, D->num_kv_heads, D->head_dim))
     return SMOE_EUNSUPPORTED;
-  if (D->ctx < 1 || D->ctx > (int64_t)1 << 24) return SMOE_EUNSUPPORTED;
+  if (D->ctx < 1 || D->ctx > (int64_t)1 << 22) return SMOE_EUNSUPPORTED;
   return SMOE_OK;
 }
 

@@ -46,6 +46,30 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi): two bf16 products carry
+// x to about 2^-16 relative.  Eight values in, both halves packed.
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], uint4& hi, uint4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = bf16_rne(x[e]);
+    l[e] = bf16_rne(x[e] - __uint_as_float(h[e] << 16));
+  }
+  hi = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+  lo = make_uint4(l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16));
+}
+__device__ __forceinline__ floatx4 mfma_bf16(const uint4& a, const uint4& b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float segment_max16(float v) {
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppMirror>(v));
+}
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ----------------------------------------------------------- k_gemv_bf16
@@ -212,10 +236,15 @@ __device__ __forceinline__ void qk_norm_rope(float& x0, float& x1, int64_t pos, 
 //  5. o = sum_j p_j v_j per head.  Writes (m, l) and o; an empty split
 //     writes l = 0.
 __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
-  __shared__ float qs[kMaxGroup][kHd];
-  __shared__ float ps[kMaxGroup][kSplit];
-  __shared__ uint4 vl[kSplit][kHd / 8];
-  __shared__ uint4 kl[kSplit][kHd / 8 + 1];        // padded rows: conflict-free chunk reads
+  // LDS: p (rows padded: the A-operand reads of 16 rows hit distinct banks),
+  // whose first 8 KB first hold the scaled queries; K row-major and V
+  // transposed (padded rows), the MFMA operands' 16-byte pieces
+  __shared__ float ps[kMaxGroup][kSplit + 4];
+  __shared__ uint4 kl[kSplit][kHd / 8 + 1];
+  __shared__ uint16_t vt[kHd][kSplit + 8];
+  __shared__ float red[kMaxGroup][kAttnThreads / 64];
+  __shared__ float redl[kMaxGroup][kAttnThreads / 64];
+  float (*qs)[kHd] = reinterpret_cast<float (*)[kHd]>(&ps[0][0]);
   const int s = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -262,117 +291,123 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   }
   __syncthreads();                                 // appends and queries visible to the block
   const int64_t slot0 = start % a.ctx;
-  // 3. K and V of the split into LDS: thread i copies 16-byte piece i % 16 of
-  //    row i / 16 (i = tid + 256 k) of each, every load issued first
+  const int col = lane & 15, lg = lane >> 4;
+  // 3. K (row-major) and V (transposed) of the split into LDS: thread i copies
+  //    16-byte piece i % 16 of row i / 16 (i = tid + 256 k), every load issued
+  //    first; the query operands (hi, lo) come out of LDS meanwhile: lane
+  //    (head col, dims 32 s + 8 lg .. +7)
+  constexpr int kPieces = kSplit * (kHd / 8) / kAttnThreads;
+  uint4 qh[kHd / 32], ql[kHd / 32];
   {
-    constexpr int kPieces = kSplit * (kHd / 8) / kAttnThreads;
-    const uint4* kbase = reinterpret_cast<const uint4*>(a.k_cache + (int64_t)g * a.ctx * kHd);
-    const uint4* vbase = reinterpret_cast<const uint4*>(a.v_cache + (int64_t)g * a.ctx * kHd);
+    // thread tid: chunk c = tid % 16 of rows tid / 16 + 16 k; one 32-bit byte
+    // offset per row serves K and V (ring of this head: ctx * 256 bytes)
+    const uint32_t ring_bytes = (uint32_t)(a.ctx * kHd * 2);
+    const auto krs = buffer_rsrc(a.k_cache + (int64_t)g * a.ctx * kHd, ring_bytes);
+    const auto vrs = buffer_rsrc(a.v_cache + (int64_t)g * a.ctx * kHd, ring_bytes);
     uint4 kr[kPieces], vr[kPieces];
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
-      const int i = tid + kAttnThreads * k, j = i >> 4, c = i & 15;
+      const int j = (tid >> 4) + 16 * k;
       int64_t sl = slot0 + (j < n ? j : 0);
       if (sl >= a.ctx) sl -= a.ctx;
-      kr[k] = kbase[sl * (kHd / 8) + c];
-      vr[k] = vbase[sl * (kHd / 8) + c];
+      const uint32_t off = (uint32_t)(sl * (kHd * 2) + (tid & 15) * 16);
+      kr[k] = buf_load4_nt(krs, off);
+      vr[k] = buf_load4_nt(vrs, off);
+    }
+#pragma unroll
+    for (int st = 0; st < kHd / 32; ++st) {
+      const float4 xa = *reinterpret_cast<const float4*>(&qs[col][32 * st + 8 * lg]);
+      const float4 xb = *reinterpret_cast<const float4*>(&qs[col][32 * st + 8 * lg + 4]);
+      const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+      split_bf16x8(x, qh[st], ql[st]);
     }
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
-      const int i = tid + kAttnThreads * k;
-      kl[i >> 4][i & 15] = kr[k];
-      vl[i >> 4][i & 15] = vr[k];
+      const int i = tid + kAttnThreads * k, j = i >> 4, c = i & 15;
+      kl[j][c] = kr[k];
+      const uint32_t w[4] = {vr[k].x, vr[k].y, vr[k].z, vr[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt[8 * c + 2 * e][j] = (uint16_t)(w[e] & 0xFFFFu);
+        vt[8 * c + 2 * e + 1][j] = (uint16_t)(w[e] >> 16);
+      }
     }
+  }
+  __syncthreads();                                 // K, V in LDS; the queries are read
+  // 4. scores S[head][position] = q . k (q pre-scaled): wave w, positions
+  //    64 w + 16 T + col; D[i] = S[4 lg + i][that position]
+  floatx4 sc[4];
+#pragma unroll
+  for (int T = 0; T < 4; ++T) {
+    sc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
+    const int j = 64 * wave + 16 * T + col;
+#pragma unroll
+    for (int st = 0; st < kHd / 32; ++st) {
+      const uint4 b = kl[j][4 * st + lg];
+      sc[T] = mfma_bf16(qh[st], b, sc[T]);
+      sc[T] = mfma_bf16(ql[st], b, sc[T]);
+    }
+  }
+  // 5. per head: max over the split, p = exp(score - max) (0 past n), sum of p
+  float mx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float m = -FLT_MAX;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) m = fmaxf(m, 64 * wave + 16 * T + col < n ? sc[T][i] : -FLT_MAX);
+    mx[i] = segment_max16(m);
+    if (col == 0) red[4 * lg + i][wave] = mx[i];
   }
   __syncthreads();
-  // 4. wave w takes query heads 4w .. 4w+3 (rows G .. 15 of qs are zero) over
-  //    all the split's positions, lane l positions l + 64 m (m < 4): four
-  //    positions share each read of a query chunk, one 16-byte key chunk at a time
-  const int hb = 4 * wave;
-  float sc[4][4];                                  // [position m][head hh]
+  float mh[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) sc[m][hh] = 0.f;
-#pragma unroll 2
-  for (int c = 0; c < kHd / 8; ++c) {
-    float kf[4][8];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint4 kv = kl[lane + 64 * m][c];
-      kf[m][0] = bf16_lo(kv.x); kf[m][1] = bf16_hi(kv.x);
-      kf[m][2] = bf16_lo(kv.y); kf[m][3] = bf16_hi(kv.y);
-      kf[m][4] = bf16_lo(kv.z); kf[m][5] = bf16_hi(kv.z);
-      kf[m][6] = bf16_lo(kv.w); kf[m][7] = bf16_hi(kv.w);
-    }
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const float4 qa = *reinterpret_cast<const float4*>(&qs[hb + hh][c * 8]);
-      const float4 qb = *reinterpret_cast<const float4*>(&qs[hb + hh][c * 8 + 4]);
-      const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        float x = sc[m][hh];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x = __builtin_fmaf(qv[e], kf[m][e], x);
-        sc[m][hh] = x;
-      }
-    }
-  }
-  // per head (all within the wave): m over the split, p = exp(score - m)
-  // (0 past n) into the wave's own rows of ps, l = sum p
-  float mh[4], lh[4];
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {
-    float mx = -FLT_MAX;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) mx = fmaxf(mx, lane + 64 * m < n ? sc[m][hh] : -FLT_MAX);
-    mh[hh] = wave_max(mx);
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * lg + i;
+    mh[i] = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
     float acc = 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float p = lane + 64 * m < n ? expf(sc[m][hh] - mh[hh]) : 0.f;
-      ps[hb + hh][lane + 64 * m] = p;
+    for (int T = 0; T < 4; ++T) {
+      const int j = 64 * wave + 16 * T + col;
+      const float p = j < n ? expf(sc[T][i] - mh[i]) : 0.f;
+      ps[h][j] = p;
       acc += p;
     }
-    lh[hh] = wave_sum(acc);
+    acc = segment_sum16(acc, 16);
+    if (col == 0) redl[h][wave] = acc;
   }
-  // 5. o[h][d] = sum_j p[h][j] v[j][d] for the wave's heads, lane: dims 2 lane,
-  //    2 lane + 1; four positions a step (p past n is 0, rows past n finite);
-  //    the wave reads only the rows of ps it wrote
-  float o0[4], o1[4];
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) o0[hh] = o1[hh] = 0.f;
-  const int n4 = (n + 3) & ~3;
+  __syncthreads();
+  // 6. O[head][dim] = sum_j p[head][j] v[j][dim]: wave w, dims 16 dt + col for
+  //    dt = 2 w, 2 w + 1; A = p (hi, lo) of (head col, positions 32 s + 8 lg ..)
+  floatx4 oc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll 2
-  for (int j = 0; j < n4; j += 4) {
-    float v0[4], v1[4];
+  for (int st = 0; st < kSplit / 32; ++st) {
+    const float4 pa = *reinterpret_cast<const float4*>(&ps[col][32 * st + 8 * lg]);
+    const float4 pb = *reinterpret_cast<const float4*>(&ps[col][32 * st + 8 * lg + 4]);
+    const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    uint4 ph, pl;
+    split_bf16x8(pv, ph, pl);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t vv = reinterpret_cast<const uint32_t*>(vl[j + u])[lane];
-      v0[u] = bf16_lo(vv);
-      v1[u] = bf16_hi(vv);
-    }
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      const float4 p4 = *reinterpret_cast<const float4*>(&ps[hb + hh][j]);
-      const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        o0[hh] = __builtin_fmaf(pv[u], v0[u], o0[hh]);
-        o1[hh] = __builtin_fmaf(pv[u], v1[u], o1[hh]);
-      }
+    for (int u = 0; u < 2; ++u) {
+      const int dt = 2 * wave + u;
+      const uint4 b = *reinterpret_cast<const uint4*>(&vt[16 * dt + col][32 * st + 8 * lg]);
+      oc[u] = mfma_bf16(ph, b, oc[u]);
+      oc[u] = mfma_bf16(pl, b, oc[u]);
     }
   }
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {
-    const int h = hb + hh;
-    if (h < G) {
-      float* oh = po + (int64_t)h * kHd;
-      oh[2 * lane] = o0[hh];
-      oh[2 * lane + 1] = o1[hh];
-      if (lane == 0) pml[h] = make_float2(mh[hh], lh[hh]);
+  for (int u = 0; u < 2; ++u) {
+    const int d = 16 * (2 * wave + u) + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * lg + i;
+      if (h < G) po[(int64_t)h * kHd + d] = oc[u][i];
     }
+  }
+  if (tid < G) {
+    const int h = tid;
+    const float m = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
+    const float l = ((redl[h][0] + redl[h][1]) + redl[h][2]) + redl[h][3];
+    pml[h] = make_float2(m, l);
   }
 }
 

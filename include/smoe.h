@@ -245,8 +245,8 @@ int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* rou
  *     (p_last - ctx + 1 .. p_last);
  *   out = x + Wo bf16(o).
  * Supported: head_dim 128; H % Hkv == 0 with H / Hkv <= 16; d_model and
- * num_heads * 128 each one of 512, 1024, 2048, 4096, 8192; ctx >= 1 and
- * B <= min(ctx, 64); else SMOE_EUNSUPPORTED. */
+ * num_heads * 128 each one of 512, 1024, 2048, 4096, 8192; 1 <= ctx <= 2^22
+ * and B <= min(ctx, 64); else SMOE_EUNSUPPORTED. */
 typedef struct smoe_attn_desc {
   double rope_theta;      /* e.g. 1e6; > 0 */
   int64_t ctx;            /* KV ring slots per layer */
