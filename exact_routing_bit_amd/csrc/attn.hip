@@ -206,18 +206,21 @@ __global__ __launch_bounds__(kAttnThreads) void k_gemv_bf16(const uint16_t* Wm, 
 }
 
 // ------------------------------------------------------------- attention
-// QK-norm (unit gain) and RoPE at position pos of one head vector held as
-// (x0, x1) = elements (lane, lane + 64): the rotate-half pair of one lane.
-__device__ __forceinline__ void qk_norm_rope(float& x0, float& x1, int64_t pos, double theta,
-                                             float eps) {
+// RoPE's cos and sin for this lane's pair (lane, lane + 64) at position pos:
+// angle pos * theta^(-2 lane / hd), in fp64 (the same for every head).
+__device__ __forceinline__ float2 rope_cs(int64_t pos, double theta) {
   const int lane = threadIdx.x & 63;
+  const double ang = (double)pos * pow(theta, -2.0 * (double)lane / (double)kHd);
+  return make_float2((float)cos(ang), (float)sin(ang));
+}
+// QK-norm (unit gain), then the rotation by cs, of one head vector held as
+// (x0, x1) = elements (lane, lane + 64): the rotate-half pair of one lane.
+__device__ __forceinline__ void qk_norm_rope(float& x0, float& x1, float2 cs, float eps) {
   const float ss = wave_sum(x0 * x0 + x1 * x1);
   const float inv = 1.0f / sqrtf(ss / (float)kHd + eps);
   x0 *= inv;
   x1 *= inv;
-  const double ang = (double)pos * pow(theta, -2.0 * (double)lane / (double)kHd);
-  const float c = (float)cos(ang), s = (float)sin(ang);
-  const float r0 = x0 * c - x1 * s, r1 = x1 * c + x0 * s;
+  const float r0 = x0 * cs.x - x1 * cs.y, r1 = x1 * cs.x + x0 * cs.y;
   x0 = r0;
   x1 = r1;
 }
@@ -262,7 +265,7 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
     const float* vsrc = src + (int64_t)(a.H + a.Hkv + g) * kHd;
     float k0 = ks[lane], k1 = ks[lane + 64];
     const float v0 = vsrc[lane], v1 = vsrc[lane + 64];
-    qk_norm_rope(k0, k1, p, a.theta, a.eps);
+    qk_norm_rope(k0, k1, rope_cs(p, a.theta), a.eps);
     const int64_t row = ((int64_t)g * a.ctx + p % a.ctx) * kHd;
     a.k_cache[row + lane] = (uint16_t)bf16_rne(k0);
     a.k_cache[row + lane + 64] = (uint16_t)bf16_rne(k1);
@@ -273,10 +276,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   //    16 rows without a branch on G, whose LDS reads would each wait)
   const float scale = 1.0f / sqrtf((float)kHd);
   for (int i = G * kHd + tid; i < kMaxGroup * kHd; i += kAttnThreads) qs[i / kHd][i % kHd] = 0.f;
+  const float2 cs = rope_cs(pos, a.theta);          // the token's rotation, once
   for (int h = wave; h < G; h += kAttnThreads / 64) {
     const float* qsrc = a.qkv + (int64_t)t * a.qkv_rows + (int64_t)(g * G + h) * kHd;
     float q0 = qsrc[lane], q1 = qsrc[lane + 64];
-    qk_norm_rope(q0, q1, pos, a.theta, a.eps);
+    qk_norm_rope(q0, q1, cs, a.eps);
     qs[h][lane] = q0 * scale;
     qs[h][lane + 64] = q1 * scale;
   }
