@@ -520,6 +520,8 @@ int attn_setup(const smoe_attn_desc* D, const uint16_t* wqkv, const uint16_t* wo
   a->part_o = ws_at<float>(ws, lay.part_o);
   a->part_ml = ws_at<float>(ws, lay.part_ml);
   a->ob = ws_at<uint16_t>(ws, lay.ob);
+  a->xb = B >= smoe::kAttnProjMinBatch ? ws_at<uint16_t>(ws, lay.xb) : nullptr;
+  a->ppart = B >= smoe::kAttnProjMinBatch ? ws_at<float>(ws, lay.ppart) : nullptr;
   return SMOE_OK;
 }
 

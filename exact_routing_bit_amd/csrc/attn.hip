@@ -22,6 +22,10 @@
 //  k_attn_merge   per (query head, token): the splits combined in order,
 //                 rounded to bf16 (the O projection's input);
 //  k_gemv_bf16    O projection plus the residual.
+// Chunks of kAttnProjMinBatch tokens or more run each projection as one pass
+// over the weights instead: k_rms_bf16 (the normed input as bf16 rows, QKV
+// only), k_proj_mfma (bf16 MFMA tiles over 512-input slices) and
+// k_proj_reduce (the slices' sums in order, plus the residual).
 #include <algorithm>
 
 #include "device.hpp"
@@ -70,7 +74,6 @@ __device__ __forceinline__ float segment_max16(float v) {
   v = fmaxf(v, dpp<kDppHalfMirror>(v));
   return fmaxf(v, dpp<kDppMirror>(v));
 }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ----------------------------------------------------------- k_gemv_bf16
 // Lane l reads the 8 values at columns 512 m + 8 l (m < C/512) of each row.
@@ -204,6 +207,110 @@ __global__ __launch_bounds__(kAttnThreads) void k_gemv_bf16(const uint16_t* Wm, 
     }
   }
 }
+
+// ------------------------------------------------------ batched projections
+// Chunks of kAttnProjMinBatch .. 64 tokens take one pass over the weights for
+// all of their tokens, on the MFMA units, with the inputs split into slices of
+// kAttnProjK and the slices' partial sums added in a fixed order afterwards.
+constexpr int kProjRows = 64;                 // weight rows per block, 16 per wave
+constexpr int kProjK = kAttnProjK;            // inputs per block
+constexpr int kProjLdsRow = kProjK / 8 + 1;   // uint4 per staged token row (16 B padding)
+constexpr int kProjOutRow = kProjRows + 4;    // floats per token row of the result tile
+
+// xb[t] = bf16(RMSNorm(x[t])), unit gain (the arithmetic of k_gemv_bf16's
+// fused norm); one block per token.
+__global__ __launch_bounds__(kAttnThreads) void k_rms_bf16(const float* x, int C, float eps,
+                                                           uint16_t* xb) {
+  __shared__ float part[kAttnThreads / 64];
+  const float* row = x + (int64_t)blockIdx.x * C;
+  const float inv = block_row_inv(row, C, eps, part);
+  const float4* r4 = reinterpret_cast<const float4*>(row);
+  uint2* o2 = reinterpret_cast<uint2*>(xb + (int64_t)blockIdx.x * C);
+  for (int i = threadIdx.x; i < C / 4; i += kAttnThreads) {
+    const float4 v = r4[i];
+    o2[i] = make_uint2(bf16_rne(v.x * inv) | (bf16_rne(v.y * inv) << 16),
+                       bf16_rne(v.z * inv) | (bf16_rne(v.w * inv) << 16));
+  }
+}
+
+// Block (row block rb, input slice ks), NT = ceil(B / 16):
+//   part[ks, t, r] = sum_{c in slice ks} W[r, c] xb[t, c],  t < B, r in rb's 64 rows.
+// The tokens' slice is staged in LDS (token rows past B read zeros).  Wave w
+// streams rows 64 rb + 16 w .. + 15: lane (m = lane % 16, q = lane / 16)
+// holds inputs 32 s + 8 q .. + 7 of row m for s = 0..15, the A operand of
+// v_mfma_f32_16x16x32_bf16 (m = row, n = token, k = input), all 16 loads
+// issued at once.  The 64 x 16 NT result goes through LDS, so that each
+// token's 64 partial sums leave as one 256-byte run.  R must be a multiple of
+// 64 and C of kProjK.
+template <int NT>
+__global__ __launch_bounds__(kAttnThreads) void k_proj_mfma(const uint16_t* W, int R, int C,
+                                                            const uint16_t* xb, int B,
+                                                            float* part) {
+  static_assert(NT * 16 * kProjOutRow * 4 <= NT * 16 * kProjLdsRow * 16, "result tile fits");
+  __shared__ uint4 xs[NT * 16][kProjLdsRow];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = blockIdx.x, ks = blockIdx.y, k0 = ks * kProjK;
+  const auto rw = buffer_rsrc(W, (uint32_t)((size_t)R * C * 2));
+  const uint32_t wo =
+      (uint32_t)(((size_t)(rb * kProjRows + wave * 16 + (lane & 15)) * C + k0 + 8 * (lane >> 4)) * 2);
+  uint4 a[kProjK / 32];
+#pragma unroll
+  for (int s = 0; s < kProjK / 32; ++s) a[s] = buf_load4_nt(rw, wo + 64 * s);
+  // the tokens' slice: thread (row i / 64 of each group of 4, piece tid % 64)
+  const auto rx = buffer_rsrc(xb, (uint32_t)((size_t)B * C * 2));
+#pragma unroll
+  for (int i = 0; i < NT * 4; ++i) {
+    const int t = 4 * i + (tid >> 6);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+        rx, (int)(((size_t)t * C + k0 + 8 * lane) * 2), 0, 0);
+    xs[t][lane] = make_uint4(v.x, v.y, v.z, v.w);
+  }
+  __syncthreads();
+  floatx4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const int n = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < kProjK / 32; ++s)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(a[s], xs[nt * 16 + n][4 * s + q], acc[nt]);
+  __syncthreads();                                 // xs is reused for the result tile
+  float(*ot)[kProjOutRow] = reinterpret_cast<float(*)[kProjOutRow]>(&xs[0][0]);
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ot[nt * 16 + n][wave * 16 + 4 * q + i] = acc[nt][i];
+  __syncthreads();
+  for (int e = tid; e < B * (kProjRows / 4); e += kAttnThreads) {
+    const int t = e / (kProjRows / 4), c4 = e % (kProjRows / 4);
+    const float4 v = make_float4(ot[t][4 * c4], ot[t][4 * c4 + 1], ot[t][4 * c4 + 2], ot[t][4 * c4 + 3]);
+    reinterpret_cast<float4*>(part + ((int64_t)ks * B + t) * R + rb * kProjRows)[c4] = v;
+  }
+}
+
+// out[t, r] = (residual[t, r] +) (part[0, t, r] + part[1, t, r] + ...), the
+// slices in order; one float4 per thread.
+__global__ __launch_bounds__(kAttnThreads) void k_proj_reduce(const float* part, int S, int n4,
+                                                              const float* residual, float* out) {
+  const int i = blockIdx.x * kAttnThreads + threadIdx.x;
+  if (i >= n4) return;
+  const float4* p4 = reinterpret_cast<const float4*>(part);
+  float4 v = p4[i];
+  for (int s = 1; s < S; ++s) {
+    const float4 w = p4[(int64_t)s * n4 + i];
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  if (residual != nullptr) {
+    const float4 r = reinterpret_cast<const float4*>(residual)[i];
+    v = make_float4(r.x + v.x, r.y + v.y, r.z + v.z, r.w + v.w);
+  }
+  reinterpret_cast<float4*>(out)[i] = v;
+}
+
 
 // ------------------------------------------------------------- attention
 // RoPE's cos and sin for this lane's pair (lane, lane + 64) at position pos:
@@ -485,6 +592,27 @@ hipError_t launch_gemv_n(const uint16_t* Wm, int R, int C, const uint16_t* x, co
   }
 }
 
+// out = (residual +) W xb for B >= kAttnProjMinBatch tokens of bf16 rows xb:
+// the slices' partial sums, then their ordered sum.
+hipError_t launch_proj(const uint16_t* Wm, int R, int C, const uint16_t* xb, int B,
+                       const float* residual, float* out, float* part, hipStream_t s,
+                       const LaunchTiming* t) {
+  if (R % kProjRows != 0 || C % kProjK != 0 || B < 1 || B > 64) return hipErrorInvalidValue;
+  const dim3 grid(R / kProjRows, C / kProjK);
+  switch ((B + 15) / 16) {
+    case 1: SMOE_LAUNCH(t, k_proj_mfma<1>, grid, dim3(kAttnThreads), 0, s, Wm, R, C, xb, B, part); break;
+    case 2: SMOE_LAUNCH(t, k_proj_mfma<2>, grid, dim3(kAttnThreads), 0, s, Wm, R, C, xb, B, part); break;
+    case 3: SMOE_LAUNCH(t, k_proj_mfma<3>, grid, dim3(kAttnThreads), 0, s, Wm, R, C, xb, B, part); break;
+    default: SMOE_LAUNCH(t, k_proj_mfma<4>, grid, dim3(kAttnThreads), 0, s, Wm, R, C, xb, B, part); break;
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n4 = B * R / 4;
+  hipLaunchKernelGGL(k_proj_reduce, dim3((n4 + kAttnThreads - 1) / kAttnThreads),
+                     dim3(kAttnThreads), 0, s, part, C / kProjK, n4, residual, out);
+  return hipGetLastError();
+}
+
 // out[t] = (residual[t] +) W x[t] for B tokens, two at a time; x is either
 // bf16 rows or (xf) fp32 rows to normalise first.
 hipError_t launch_gemv_bf16(const uint16_t* Wm, int R, int C, const uint16_t* x, const float* xf,
@@ -514,9 +642,19 @@ bool attn_shape_ok(int d, int H, int Hkv, int hd) {
 hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage, const LaunchTiming* t) {
   hipError_t err = hipSuccess;
   const int rows = a.qkv_rows;
+  const bool batched = a.B >= kAttnProjMinBatch;
+  if (batched && (a.xb == nullptr || a.ppart == nullptr)) return hipErrorInvalidValue;
   if (stage < 0 || stage == 0) {
-    err = launch_gemv_bf16(a.wqkv, rows, a.d, nullptr, a.x, a.eps, a.B, nullptr, a.qkv, s,
-                           stage == 0 ? t : nullptr);
+    if (batched) {
+      hipLaunchKernelGGL(k_rms_bf16, dim3(a.B), dim3(kAttnThreads), 0, s, a.x, a.d, a.eps, a.xb);
+      err = hipGetLastError();
+      if (err == hipSuccess)
+        err = launch_proj(a.wqkv, rows, a.d, a.xb, a.B, nullptr, a.qkv, a.ppart, s,
+                          stage == 0 ? t : nullptr);
+    } else {
+      err = launch_gemv_bf16(a.wqkv, rows, a.d, nullptr, a.x, a.eps, a.B, nullptr, a.qkv, s,
+                             stage == 0 ? t : nullptr);
+    }
     if (err != hipSuccess) return err;
   }
   if (stage < 0 || stage == 1) {
@@ -529,8 +667,10 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage, const Launch
     if (err != hipSuccess) return err;
   }
   if (stage < 0 || stage == 2)
-    err = launch_gemv_bf16(a.wo, a.d, a.H * kHd, a.ob, nullptr, 0.f, a.B, a.x, a.out, s,
-                           stage == 2 ? t : nullptr);
+    err = batched ? launch_proj(a.wo, a.d, a.H * kHd, a.ob, a.B, a.x, a.out, a.ppart, s,
+                                stage == 2 ? t : nullptr)
+                  : launch_gemv_bf16(a.wo, a.d, a.H * kHd, a.ob, nullptr, 0.f, a.B, a.x, a.out,
+                                     s, stage == 2 ? t : nullptr);
   return err;
 }
 

@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/smoe.h"
 
 namespace smoe {
@@ -156,6 +158,8 @@ struct DecodeRoute {
 constexpr int kAttnHeadDim = 128;   // head dimension
 constexpr int kAttnMaxGroup = 16;   // query heads per key/value head
 constexpr int kAttnSplit = 256;     // cached positions per attention block
+constexpr int kAttnProjMinBatch = 3;  // chunks of this many tokens or more: batched projections
+constexpr int kAttnProjK = 512;       // inputs per block of a batched projection (the K split)
 
 // Workspace of the attention block for up to B tokens ([DF] layer loop).
 struct AttnWsLayout {
@@ -163,6 +167,8 @@ struct AttnWsLayout {
   size_t part_o;   // [B, Hkv, nsplit, 16, hd] f32
   size_t part_ml;  // [B, Hkv, nsplit, 16] (max, sum) pairs
   size_t ob;       // [B, H hd] bf16: the attention output
+  size_t xb;       // [B, d] bf16: the normed input (batched projections only)
+  size_t ppart;    // [K splits, B, rows] f32: partial sums (batched projections only)
   size_t total;
 };
 
@@ -182,6 +188,11 @@ inline AttnWsLayout attn_ws_layout(const smoe_attn_desc& D, int B) {
   w.part_o = take((size_t)B * G * ns * kAttnMaxGroup * hd * 4);
   w.part_ml = take((size_t)B * G * ns * kAttnMaxGroup * 8);
   w.ob = take((size_t)B * H * hd * 2);
+  if (B >= kAttnProjMinBatch) {
+    const size_t d = (size_t)D.d_model, qkv_rows = (H + 2 * G) * hd;
+    w.xb = take((size_t)B * d * 2);
+    w.ppart = take((size_t)B * std::max(d / kAttnProjK * qkv_rows, H * hd / kAttnProjK * d) * 4);
+  }
   w.total = off;
   return w;
 }
@@ -201,6 +212,8 @@ struct AttnArgs {
   float* part_o;
   float* part_ml;
   uint16_t* ob;
+  uint16_t* xb;            // batched projections only
+  float* ppart;
 };
 
 // ------------------------------------------------------------- launchers

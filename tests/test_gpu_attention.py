@@ -4,8 +4,13 @@ the CPU oracle (oracle/attention.py) on the same seeded inputs.
 Bars: the block's contribution out - x within relative L2 3e-3 of the
 oracle's; the K/V entries the call appends within one bf16 step of the
 oracle's (the GPU rounds its fp32 values, the oracle its fp64 ones) plus
-1e-5 of their RMS, most of them equal; every other ring slot unchanged, bit
-for bit.
+2e-3 of their RMS, more than 95% of them equal; every other ring slot
+unchanged, bit for bit.  The absolute term is the effect of one projection
+input that the GPU's fp32 input norm and the oracle's fp64 one round to
+neighbouring bf16 values: one step of |x| <= 4 against a weight |w| <= 0.08
+moves an entry by up to 0.08 * 4 * 2^-8 = 1.3e-3, against an RMS of 0.64
+(V) or 1 (K).  Such inputs are rare (about one in 40 tokens here), so
+chunks of many tokens meet them.
 """
 import numpy as np
 import pytest
@@ -63,10 +68,10 @@ def check(cfg, B, pos0, x, ref, got, before, after, ref_cache):
         assert np.array_equal(a[:, keep], b[:, keep])           # untouched slots
         got_v = A.bf16_bits_to_f64(a[:, written])
         want = r[:, written]
-        # one bf16 step of the value, plus the fp32 pipeline's absolute error,
-        # which dominates for entries near zero
+        # one bf16 step of the value, plus the effect of one input rounded to
+        # the neighbouring bf16 value, which dominates for entries near zero
         rms = np.sqrt(np.mean(want * want))
-        assert np.all(np.abs(got_v - want) <= 2.0**-7 * np.abs(want) + 1e-5 * rms)
+        assert np.all(np.abs(got_v - want) <= 2.0**-7 * np.abs(want) + 2e-3 * rms)
         assert np.mean(got_v == want) > 0.95
     return err
 
@@ -84,6 +89,11 @@ CASES = [
     (ODD_CTX, 1, 299),    # full ring of 300: two splits, the second partial
     (ODD_CTX, 2, 1000),   # wrapped, the window crossing the ring's end
     (GROUP16, 1, 700),    # 16 query heads per key/value head
+    # chunks of 3 or more tokens take the batched projections (MFMA tiles of
+    # 16 tokens over 512-input slices, the slices summed in order)
+    (GROUP16, 3, 10),     # the smallest batched chunk; 4 input slices
+    (GROUP16, 17, 500),   # two token tiles, the second holding one token
+    (ODD_CTX, 40, 280),   # three token tiles, the chunk crossing the ring's end
 ]
 
 
@@ -98,16 +108,18 @@ def test_attention_block_parity(smoe, cfg, B, pos0):
 FULL = A.AttnConfig(d_model=4096, num_heads=64, num_kv_heads=4, ctx=4096)
 
 
-@pytest.mark.parametrize("B,pos0", [(1, 4095), (2, 5000)])
+@pytest.mark.parametrize("B,pos0", [(1, 4095), (2, 5000), (64, 4032)])
 def test_attention_block_full_size(smoe, B, pos0):
     """The decode shape (d 4096, 64 query heads, 4 key/value heads, a 4096-slot
-    ring), with the ring full and with it wrapped."""
+    ring), with the ring full and with it wrapped, and a 64-token chunk that
+    ends at the ring's last slot."""
     x, ref, got, before, after, ref_cache, _ = run_both(smoe, FULL, B, pos0)
     check(FULL, B, pos0, x, ref, got, before, after, ref_cache)
 
 
-def test_stages_equal_the_whole_call(smoe):
-    cfg, B, pos0 = SMALL, 2, 50
+@pytest.mark.parametrize("cfg,B", [(SMALL, 2), (GROUP16, 5)], ids=["gemv_b2", "batched_b5"])
+def test_stages_equal_the_whole_call(smoe, cfg, B):
+    pos0 = 50
     Wqkv, Wo, Kc, Vc = make_inputs(cfg, 3)
     x = up(synth.hidden(3, 0, 9, B, cfg.d_model))
     desc = smoe.make_attn_desc(cfg.d_model, cfg.num_heads, cfg.num_kv_heads, cfg.ctx,
@@ -128,8 +140,9 @@ def test_stages_equal_the_whole_call(smoe):
         assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
 
 
-def test_in_place_and_empty(smoe):
-    cfg, B, pos0 = SMALL, 1, 9
+@pytest.mark.parametrize("B", [1, 4])
+def test_in_place_and_empty(smoe, B):
+    cfg, pos0 = SMALL, 9
     x, ref, got, *_ = run_both(smoe, cfg, B, pos0, seed=4)
     Wqkv, Wo, Kc, Vc = make_inputs(cfg, 4)
     desc = smoe.make_attn_desc(cfg.d_model, cfg.num_heads, cfg.num_kv_heads, cfg.ctx,
