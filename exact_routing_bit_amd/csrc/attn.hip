@@ -332,19 +332,36 @@ __device__ __forceinline__ void qk_norm_rope(float& x0, float& x1, float2 cs, fl
   x1 = r1;
 }
 
-// Block (split s, key/value head g, token t).  The split's positions are
-// start .. start + 255 with start = lo + 256 s (lo: the first position the
-// ring holds after the call); token t reads n of them, up to its own.
+// The query operands of one MFMA score tile: lane (head col, dims
+// 32 st + 8 lg .. + 7) as bf16 high and low parts.
+__device__ __forceinline__ void query_operands(const float (*qs)[kHd], int col, int lg,
+                                               uint4 (&qh)[kHd / 32], uint4 (&ql)[kHd / 32]) {
+#pragma unroll
+  for (int st = 0; st < kHd / 32; ++st) {
+    const float4 xa = *reinterpret_cast<const float4*>(&qs[col][32 * st + 8 * lg]);
+    const float4 xb = *reinterpret_cast<const float4*>(&qs[col][32 * st + 8 * lg + 4]);
+    const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+    split_bf16x8(x, qh[st], ql[st]);
+  }
+}
+
+// Block (split s, key/value head g, tokens t0 .. t1 - 1: a group of a.tgroup
+// tokens of the call).  The split's positions are start .. start + 255 with
+// start = lo + 256 s (lo: the first position the ring holds after the call);
+// token t reads n_t of them, up to its own.
 //  1. The call's K/V that fall in the split are formed (k: QK-norm + RoPE;
-//     v as is) and appended, by every token's block of the split alike (the
+//     v as is) and appended, by every group's block of the split alike (the
 //     same bits), so that each block reads what it wrote after its barrier.
-//  2. The group's G query heads of token t: QK-norm + RoPE, scaled by
-//     1/sqrt(hd), into LDS.
-//  3. V of the split into LDS (all loads issued first, in flight during 4).
-//  4. Scores: thread j takes position start + j against every head; then per
-//     head the max m, p = exp(score - m) and l = sum p.
-//  5. o = sum_j p_j v_j per head.  Writes (m, l) and o; an empty split
-//     writes l = 0.
+//  2. The first token's G query heads: QK-norm + RoPE, scaled by 1/sqrt(hd),
+//     into LDS.
+//  3. K and V of the split into LDS, as many positions as the group's last
+//     token reads (every load issued first; the query operands are formed
+//     meanwhile).
+//  4. Per token, scores as 16 x 16 MFMA tiles (query heads x positions); per
+//     head the max m, p = exp(score - m) (0 past n_t) and l = sum p.
+//  5. o = sum_j p_j v_j per head, as MFMA tiles.  Writes (m, l) and o; a split
+//     that the token does not reach writes l = 0.  Then the next token's
+//     queries (2) and again from 4, against the same staged K and V.
 __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   // LDS: p (rows padded: the A-operand reads of 16 rows hit distinct banks),
   // whose first 8 KB first hold the scaled queries; K row-major and V
@@ -355,11 +372,11 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   __shared__ float red[kMaxGroup][kAttnThreads / 64];
   __shared__ float redl[kMaxGroup][kAttnThreads / 64];
   float (*qs)[kHd] = reinterpret_cast<float (*)[kHd]>(&ps[0][0]);
-  const int s = blockIdx.x, g = blockIdx.y, t = blockIdx.z;
+  const int s = blockIdx.x, g = blockIdx.y;
+  const int t0 = blockIdx.z * a.tgroup, t1 = min(a.B, t0 + a.tgroup);   // the block's tokens
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = a.H / a.Hkv;
-  const int64_t pos = a.pos0 + t;
   const int64_t p_last = a.pos0 + a.B - 1;
   const int64_t lo = p_last - a.ctx + 1 > 0 ? p_last - a.ctx + 1 : 0;
   const int64_t start = lo + (int64_t)s * kSplit;
@@ -379,27 +396,34 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
     a.v_cache[row + lane] = (uint16_t)bf16_rne(v0);
     a.v_cache[row + lane + 64] = (uint16_t)bf16_rne(v1);
   }
-  // 2. the group's queries (rows G .. 15 zero: the loops below run over all
-  //    16 rows without a branch on G, whose LDS reads would each wait)
+  // 2. the first token's queries (rows G .. 15 zero: the loops below run over
+  //    all 16 rows without a branch on G, whose LDS reads would each wait)
   const float scale = 1.0f / sqrtf((float)kHd);
-  for (int i = G * kHd + tid; i < kMaxGroup * kHd; i += kAttnThreads) qs[i / kHd][i % kHd] = 0.f;
-  const float2 cs = rope_cs(pos, a.theta);          // the token's rotation, once
-  for (int h = wave; h < G; h += kAttnThreads / 64) {
-    const float* qsrc = a.qkv + (int64_t)t * a.qkv_rows + (int64_t)(g * G + h) * kHd;
-    float q0 = qsrc[lane], q1 = qsrc[lane + 64];
-    qk_norm_rope(q0, q1, cs, a.eps);
-    qs[h][lane] = q0 * scale;
-    qs[h][lane + 64] = q1 * scale;
-  }
-  const int64_t avail = pos + 1 - start;
-  const int n = avail <= 0 ? 0 : (avail >= kSplit ? kSplit : (int)avail);
-  const int64_t base = (((int64_t)t * a.Hkv + g) * a.nsplit + s) * kMaxGroup;
-  float* po = a.part_o + base * kHd;
-  float2* pml = reinterpret_cast<float2*>(a.part_ml) + base;
-  if (n == 0) {                                    // whole block; its appends are done
-    if (tid < kMaxGroup) pml[tid] = make_float2(0.f, 0.f);
+  auto form_queries = [&](int t) {
+    for (int i = G * kHd + tid; i < kMaxGroup * kHd; i += kAttnThreads) qs[i / kHd][i % kHd] = 0.f;
+    const float2 cs = rope_cs(a.pos0 + t, a.theta);   // the token's rotation, once
+    for (int h = wave; h < G; h += kAttnThreads / 64) {
+      const float* qsrc = a.qkv + (int64_t)t * a.qkv_rows + (int64_t)(g * G + h) * kHd;
+      float q0 = qsrc[lane], q1 = qsrc[lane + 64];
+      qk_norm_rope(q0, q1, cs, a.eps);
+      qs[h][lane] = q0 * scale;
+      qs[h][lane + 64] = q1 * scale;
+    }
+  };
+  // positions of the split that token t reads (non-decreasing in t)
+  auto n_of = [&](int t) {
+    const int64_t avail = a.pos0 + t + 1 - start;
+    return avail <= 0 ? 0 : (avail >= kSplit ? kSplit : (int)avail);
+  };
+  auto part_base = [&](int t) { return (((int64_t)t * a.Hkv + g) * a.nsplit + s) * kMaxGroup; };
+  const int n_last = n_of(t1 - 1);
+  if (n_last == 0) {                               // whole block; its appends are done
+    if (tid < kMaxGroup)
+      for (int t = t0; t < t1; ++t)
+        reinterpret_cast<float2*>(a.part_ml)[part_base(t) + tid] = make_float2(0.f, 0.f);
     return;
   }
+  form_queries(t0);
   __syncthreads();                                 // appends and queries visible to the block
   const int64_t slot0 = start % a.ctx;
   const int col = lane & 15, lg = lane >> 4;
@@ -419,19 +443,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
       const int j = (tid >> 4) + 16 * k;
-      int64_t sl = slot0 + (j < n ? j : 0);
+      int64_t sl = slot0 + (j < n_last ? j : 0);
       if (sl >= a.ctx) sl -= a.ctx;
       const uint32_t off = (uint32_t)(sl * (kHd * 2) + (tid & 15) * 16);
       kr[k] = buf_load4_nt(krs, off);
       vr[k] = buf_load4_nt(vrs, off);
     }
-#pragma unroll
-    for (int st = 0; st < kHd / 32; ++st) {
-      const float4 xa = *reinterpret_cast<const float4*>(&qs[col][32 * st + 8 * lg]);
-      const float4 xb = *reinterpret_cast<const float4*>(&qs[col][32 * st + 8 * lg + 4]);
-      const float x[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
-      split_bf16x8(x, qh[st], ql[st]);
-    }
+    query_operands(qs, col, lg, qh, ql);
 #pragma unroll
     for (int k = 0; k < kPieces; ++k) {
       const int i = tid + kAttnThreads * k, j = i >> 4, c = i & 15;
@@ -445,80 +463,95 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
     }
   }
   __syncthreads();                                 // K, V in LDS; the queries are read
-  // 4. scores S[head][position] = q . k (q pre-scaled): wave w, positions
-  //    64 w + 16 T + col; D[i] = S[4 lg + i][that position]
-  floatx4 sc[4];
-#pragma unroll
-  for (int T = 0; T < 4; ++T) {
-    sc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
-    const int j = 64 * wave + 16 * T + col;
-#pragma unroll
-    for (int st = 0; st < kHd / 32; ++st) {
-      const uint4 b = kl[j][4 * st + lg];
-      sc[T] = mfma_bf16(qh[st], b, sc[T]);
-      sc[T] = mfma_bf16(ql[st], b, sc[T]);
+  // 4.-6. per token of the group, against the staged K and V
+  for (int t = t0;;) {
+    const int n = n_of(t);
+    float* po = a.part_o + part_base(t) * kHd;
+    float2* pml = reinterpret_cast<float2*>(a.part_ml) + part_base(t);
+    if (n == 0) {                                  // uniform over the block
+      if (tid < kMaxGroup) pml[tid] = make_float2(0.f, 0.f);
+    } else {
+      // 4. scores S[head][position] = q . k (q pre-scaled): wave w, positions
+      //    64 w + 16 T + col; D[i] = S[4 lg + i][that position]
+      floatx4 sc[4];
+    #pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        sc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int j = 64 * wave + 16 * T + col;
+    #pragma unroll
+        for (int st = 0; st < kHd / 32; ++st) {
+          const uint4 b = kl[j][4 * st + lg];
+          sc[T] = mfma_bf16(qh[st], b, sc[T]);
+          sc[T] = mfma_bf16(ql[st], b, sc[T]);
+        }
+      }
+      // 5. per head: max over the split, p = exp(score - max) (0 past n), sum of p
+      float mx[4];
+    #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float m = -FLT_MAX;
+    #pragma unroll
+        for (int T = 0; T < 4; ++T) m = fmaxf(m, 64 * wave + 16 * T + col < n ? sc[T][i] : -FLT_MAX);
+        mx[i] = segment_max16(m);
+        if (col == 0) red[4 * lg + i][wave] = mx[i];
+      }
+      __syncthreads();
+      float mh[4];
+    #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 4 * lg + i;
+        mh[i] = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
+        float acc = 0.f;
+    #pragma unroll
+        for (int T = 0; T < 4; ++T) {
+          const int j = 64 * wave + 16 * T + col;
+          const float p = j < n ? expf(sc[T][i] - mh[i]) : 0.f;
+          ps[h][j] = p;
+          acc += p;
+        }
+        acc = segment_sum16(acc, 16);
+        if (col == 0) redl[h][wave] = acc;
+      }
+      __syncthreads();
+      // 6. O[head][dim] = sum_j p[head][j] v[j][dim]: wave w, dims 16 dt + col for
+      //    dt = 2 w, 2 w + 1; A = p (hi, lo) of (head col, positions 32 s + 8 lg ..)
+      floatx4 oc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    #pragma unroll 2
+      for (int st = 0; st < kSplit / 32; ++st) {
+        const float4 pa = *reinterpret_cast<const float4*>(&ps[col][32 * st + 8 * lg]);
+        const float4 pb = *reinterpret_cast<const float4*>(&ps[col][32 * st + 8 * lg + 4]);
+        const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        uint4 ph, pl;
+        split_bf16x8(pv, ph, pl);
+    #pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int dt = 2 * wave + u;
+          const uint4 b = *reinterpret_cast<const uint4*>(&vt[16 * dt + col][32 * st + 8 * lg]);
+          oc[u] = mfma_bf16(ph, b, oc[u]);
+          oc[u] = mfma_bf16(pl, b, oc[u]);
+        }
+      }
+    #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int d = 16 * (2 * wave + u) + col;
+    #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = 4 * lg + i;
+          if (h < G) po[(int64_t)h * kHd + d] = oc[u][i];
+        }
+      }
+      if (tid < G) {
+        const int h = tid;
+        const float m = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
+        const float l = ((redl[h][0] + redl[h][1]) + redl[h][2]) + redl[h][3];
+        pml[h] = make_float2(m, l);
+      }
     }
-  }
-  // 5. per head: max over the split, p = exp(score - max) (0 past n), sum of p
-  float mx[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float m = -FLT_MAX;
-#pragma unroll
-    for (int T = 0; T < 4; ++T) m = fmaxf(m, 64 * wave + 16 * T + col < n ? sc[T][i] : -FLT_MAX);
-    mx[i] = segment_max16(m);
-    if (col == 0) red[4 * lg + i][wave] = mx[i];
-  }
-  __syncthreads();
-  float mh[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * lg + i;
-    mh[i] = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
-    float acc = 0.f;
-#pragma unroll
-    for (int T = 0; T < 4; ++T) {
-      const int j = 64 * wave + 16 * T + col;
-      const float p = j < n ? expf(sc[T][i] - mh[i]) : 0.f;
-      ps[h][j] = p;
-      acc += p;
-    }
-    acc = segment_sum16(acc, 16);
-    if (col == 0) redl[h][wave] = acc;
-  }
-  __syncthreads();
-  // 6. O[head][dim] = sum_j p[head][j] v[j][dim]: wave w, dims 16 dt + col for
-  //    dt = 2 w, 2 w + 1; A = p (hi, lo) of (head col, positions 32 s + 8 lg ..)
-  floatx4 oc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll 2
-  for (int st = 0; st < kSplit / 32; ++st) {
-    const float4 pa = *reinterpret_cast<const float4*>(&ps[col][32 * st + 8 * lg]);
-    const float4 pb = *reinterpret_cast<const float4*>(&ps[col][32 * st + 8 * lg + 4]);
-    const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
-    uint4 ph, pl;
-    split_bf16x8(pv, ph, pl);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int dt = 2 * wave + u;
-      const uint4 b = *reinterpret_cast<const uint4*>(&vt[16 * dt + col][32 * st + 8 * lg]);
-      oc[u] = mfma_bf16(ph, b, oc[u]);
-      oc[u] = mfma_bf16(pl, b, oc[u]);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int d = 16 * (2 * wave + u) + col;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * lg + i;
-      if (h < G) po[(int64_t)h * kHd + d] = oc[u][i];
-    }
-  }
-  if (tid < G) {
-    const int h = tid;
-    const float m = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
-    const float l = ((redl[h][0] + redl[h][1]) + redl[h][2]) + redl[h][3];
-    pml[h] = make_float2(m, l);
+    if (++t >= t1) break;
+    __syncthreads();                               // p, red, redl read; qs may be rewritten
+    form_queries(t);
+    __syncthreads();
+    query_operands(qs, col, lg, qh, ql);
   }
 }
 
@@ -658,8 +691,16 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage, const Launch
     if (err != hipSuccess) return err;
   }
   if (stage < 0 || stage == 1) {
-    SMOE_LAUNCH(stage == 1 ? t : nullptr, k_attn_decode, dim3(a.nsplit, a.Hkv, a.B),
-                dim3(kAttnThreads), 0, s, a);
+    // token groups: about two blocks per CU, one token a block for decode
+    const int ncu = cu_count_attn();
+    if (ncu <= 0) return hipErrorInvalidDevice;
+    const int heads_splits = a.nsplit * a.Hkv;
+    const int ngroups = std::max(1, std::min(a.B, (2 * ncu + heads_splits - 1) / heads_splits));
+    AttnArgs b = a;
+    b.tgroup = (a.B + ngroups - 1) / ngroups;
+    SMOE_LAUNCH(stage == 1 ? t : nullptr, k_attn_decode,
+                dim3(a.nsplit, a.Hkv, (a.B + b.tgroup - 1) / b.tgroup), dim3(kAttnThreads), 0, s,
+                b);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.B), dim3(kHd), 0, s, a);

@@ -205,6 +205,7 @@ struct AttnArgs {
   uint16_t* k_cache;       // [Hkv, ctx, hd] bf16
   uint16_t* v_cache;
   int B, d, H, Hkv, qkv_rows, nsplit;
+  int tgroup;              // tokens per attention block (set by the launcher)
   int64_t pos0, ctx;
   double theta;
   float eps;
