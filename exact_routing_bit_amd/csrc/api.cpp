@@ -522,6 +522,7 @@ int attn_setup(const smoe_attn_desc* D, const uint16_t* wqkv, const uint16_t* wo
   a->ob = ws_at<uint16_t>(ws, lay.ob);
   a->xb = B >= smoe::kAttnProjMinBatch ? ws_at<uint16_t>(ws, lay.xb) : nullptr;
   a->ppart = B >= smoe::kAttnProjMinBatch ? ws_at<float>(ws, lay.ppart) : nullptr;
+  a->rope = B >= smoe::kAttnProjMinBatch ? ws_at<float2>(ws, lay.rope) : nullptr;
   return SMOE_OK;
 }
 

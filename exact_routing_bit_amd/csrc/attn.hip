@@ -208,6 +208,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_gemv_bf16(const uint16_t* Wm, 
   }
 }
 
+// RoPE's cos and sin for this lane's pair (lane, lane + 64) at position pos:
+// angle pos * theta^(-2 lane / hd), in fp64 (the same for every head).
+__device__ __forceinline__ float2 rope_cs(int64_t pos, double theta) {
+  const int lane = threadIdx.x & 63;
+  const double ang = (double)pos * pow(theta, -2.0 * (double)lane / (double)kHd);
+  return make_float2((float)cos(ang), (float)sin(ang));
+}
 // ------------------------------------------------------ batched projections
 // Chunks of kAttnProjMinBatch .. 64 tokens take one pass over the weights for
 // all of their tokens, on the MFMA units, with the inputs split into slices of
@@ -218,10 +225,14 @@ constexpr int kProjLdsRow = kProjK / 8 + 1;   // uint4 per staged token row (16 
 constexpr int kProjOutRow = kProjRows + 4;    // floats per token row of the result tile
 
 // xb[t] = bf16(RMSNorm(x[t])), unit gain (the arithmetic of k_gemv_bf16's
-// fused norm); one block per token.
+// fused norm), and rope[t] = RoPE's (cos, sin) of position pos0 + t for each
+// pair, formed as the attention kernel forms them; one block per token.
 __global__ __launch_bounds__(kAttnThreads) void k_rms_bf16(const float* x, int C, float eps,
-                                                           uint16_t* xb) {
+                                                           uint16_t* xb, int64_t pos0,
+                                                           double theta, float2* rope) {
   __shared__ float part[kAttnThreads / 64];
+  if (threadIdx.x < kHd / 2)
+    rope[(int64_t)blockIdx.x * (kHd / 2) + threadIdx.x] = rope_cs(pos0 + blockIdx.x, theta);
   const float* row = x + (int64_t)blockIdx.x * C;
   const float inv = block_row_inv(row, C, eps, part);
   const float4* r4 = reinterpret_cast<const float4*>(row);
@@ -313,13 +324,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_proj_reduce(const float* part,
 
 
 // ------------------------------------------------------------- attention
-// RoPE's cos and sin for this lane's pair (lane, lane + 64) at position pos:
-// angle pos * theta^(-2 lane / hd), in fp64 (the same for every head).
-__device__ __forceinline__ float2 rope_cs(int64_t pos, double theta) {
-  const int lane = threadIdx.x & 63;
-  const double ang = (double)pos * pow(theta, -2.0 * (double)lane / (double)kHd);
-  return make_float2((float)cos(ang), (float)sin(ang));
-}
 // QK-norm (unit gain), then the rotation by cs, of one head vector held as
 // (x0, x1) = elements (lane, lane + 64): the rotate-half pair of one lane.
 __device__ __forceinline__ void qk_norm_rope(float& x0, float& x1, float2 cs, float eps) {
@@ -362,6 +366,9 @@ __device__ __forceinline__ void query_operands(const float (*qs)[kHd], int col, 
 //  5. o = sum_j p_j v_j per head, as MFMA tiles.  Writes (m, l) and o; a split
 //     that the token does not reach writes l = 0.  Then the next token's
 //     queries (2) and again from 4, against the same staged K and V.
+// kTable: RoPE's (cos, sin) come from a.rope (chunks) rather than being formed
+// here (decode).
+template <bool kTable>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   // LDS: p (rows padded: the A-operand reads of 16 rows hit distinct banks),
   // whose first 8 KB first hold the scaled queries; K row-major and V
@@ -389,7 +396,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
     const float* vsrc = src + (int64_t)(a.H + a.Hkv + g) * kHd;
     float k0 = ks[lane], k1 = ks[lane + 64];
     const float v0 = vsrc[lane], v1 = vsrc[lane + 64];
-    qk_norm_rope(k0, k1, rope_cs(p, a.theta), a.eps);
+    const float2 cs = kTable ? a.rope[(p - a.pos0) * (kHd / 2) + lane] : rope_cs(p, a.theta);
+    qk_norm_rope(k0, k1, cs, a.eps);
     const int64_t row = ((int64_t)g * a.ctx + p % a.ctx) * kHd;
     a.k_cache[row + lane] = (uint16_t)bf16_rne(k0);
     a.k_cache[row + lane + 64] = (uint16_t)bf16_rne(k1);
@@ -401,7 +409,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   const float scale = 1.0f / sqrtf((float)kHd);
   auto form_queries = [&](int t) {
     for (int i = G * kHd + tid; i < kMaxGroup * kHd; i += kAttnThreads) qs[i / kHd][i % kHd] = 0.f;
-    const float2 cs = rope_cs(a.pos0 + t, a.theta);   // the token's rotation, once
+    const float2 cs = kTable ? a.rope[(int64_t)t * (kHd / 2) + lane]
+                             : rope_cs(a.pos0 + t, a.theta);   // once per token
     for (int h = wave; h < G; h += kAttnThreads / 64) {
       const float* qsrc = a.qkv + (int64_t)t * a.qkv_rows + (int64_t)(g * G + h) * kHd;
       float q0 = qsrc[lane], q1 = qsrc[lane + 64];
@@ -676,10 +685,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage, const Launch
   hipError_t err = hipSuccess;
   const int rows = a.qkv_rows;
   const bool batched = a.B >= kAttnProjMinBatch;
-  if (batched && (a.xb == nullptr || a.ppart == nullptr)) return hipErrorInvalidValue;
+  if (batched && (a.xb == nullptr || a.ppart == nullptr || a.rope == nullptr))
+    return hipErrorInvalidValue;
   if (stage < 0 || stage == 0) {
     if (batched) {
-      hipLaunchKernelGGL(k_rms_bf16, dim3(a.B), dim3(kAttnThreads), 0, s, a.x, a.d, a.eps, a.xb);
+      hipLaunchKernelGGL(k_rms_bf16, dim3(a.B), dim3(kAttnThreads), 0, s, a.x, a.d, a.eps, a.xb,
+                         a.pos0, a.theta, a.rope);
       err = hipGetLastError();
       if (err == hipSuccess)
         err = launch_proj(a.wqkv, rows, a.d, a.xb, a.B, nullptr, a.qkv, a.ppart, s,
@@ -691,16 +702,20 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t s, int stage, const Launch
     if (err != hipSuccess) return err;
   }
   if (stage < 0 || stage == 1) {
-    // token groups: about two blocks per CU, one token a block for decode
+    // token groups: about one block per CU (each block stages its split's
+    // K and V once, which costs more than the CUs' idle tails of larger
+    // groups); one token a block for decode
     const int ncu = cu_count_attn();
     if (ncu <= 0) return hipErrorInvalidDevice;
     const int heads_splits = a.nsplit * a.Hkv;
-    const int ngroups = std::max(1, std::min(a.B, (2 * ncu + heads_splits - 1) / heads_splits));
+    const int ngroups = std::max(1, std::min(a.B, (ncu + heads_splits - 1) / heads_splits));
     AttnArgs b = a;
     b.tgroup = (a.B + ngroups - 1) / ngroups;
-    SMOE_LAUNCH(stage == 1 ? t : nullptr, k_attn_decode,
-                dim3(a.nsplit, a.Hkv, (a.B + b.tgroup - 1) / b.tgroup), dim3(kAttnThreads), 0, s,
-                b);
+    const dim3 grid(a.nsplit, a.Hkv, (a.B + b.tgroup - 1) / b.tgroup);
+    if (batched)
+      SMOE_LAUNCH(stage == 1 ? t : nullptr, k_attn_decode<true>, grid, dim3(kAttnThreads), 0, s, b);
+    else
+      SMOE_LAUNCH(stage == 1 ? t : nullptr, k_attn_decode<false>, grid, dim3(kAttnThreads), 0, s, b);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_attn_merge, dim3(a.H, a.B), dim3(kHd), 0, s, a);

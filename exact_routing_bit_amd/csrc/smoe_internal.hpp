@@ -169,6 +169,7 @@ struct AttnWsLayout {
   size_t ob;       // [B, H hd] bf16: the attention output
   size_t xb;       // [B, d] bf16: the normed input (batched projections only)
   size_t ppart;    // [K splits, B, rows] f32: partial sums (batched projections only)
+  size_t rope;     // [B, hd / 2] (cos, sin) of the tokens' positions (batched path only)
   size_t total;
 };
 
@@ -192,6 +193,7 @@ inline AttnWsLayout attn_ws_layout(const smoe_attn_desc& D, int B) {
     const size_t d = (size_t)D.d_model, qkv_rows = (H + 2 * G) * hd;
     w.xb = take((size_t)B * d * 2);
     w.ppart = take((size_t)B * std::max(d / kAttnProjK * qkv_rows, H * hd / kAttnProjK * d) * 4);
+    w.rope = take((size_t)B * (hd / 2) * 8);
   }
   w.total = off;
   return w;
@@ -215,6 +217,7 @@ struct AttnArgs {
   uint16_t* ob;
   uint16_t* xb;            // batched projections only
   float* ppart;
+  float2* rope;            // batched path only: (cos, sin) per token and pair
 };
 
 // ------------------------------------------------------------- launchers

@@ -108,11 +108,12 @@ def test_attention_block_parity(smoe, cfg, B, pos0):
 FULL = A.AttnConfig(d_model=4096, num_heads=64, num_kv_heads=4, ctx=4096)
 
 
-@pytest.mark.parametrize("B,pos0", [(1, 4095), (2, 5000), (64, 4032)])
+@pytest.mark.parametrize("B,pos0", [(1, 4095), (2, 5000), (64, 4032), (64, 3040)])
 def test_attention_block_full_size(smoe, B, pos0):
     """The decode shape (d 4096, 64 query heads, 4 key/value heads, a 4096-slot
-    ring), with the ring full and with it wrapped, and a 64-token chunk that
-    ends at the ring's last slot."""
+    ring), with the ring full and with it wrapped; a 64-token chunk that ends
+    at the ring's last slot; and one that crosses a 256-position split, so that
+    the early tokens of a token group do not reach the last split."""
     x, ref, got, before, after, ref_cache, _ = run_both(smoe, FULL, B, pos0)
     check(FULL, B, pos0, x, ref, got, before, after, ref_cache)
 
