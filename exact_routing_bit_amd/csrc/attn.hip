@@ -475,6 +475,20 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
   // 4.-6. per token of the group, against the staged K and V
   for (int t = t0;;) {
     const int n = n_of(t);
+    // chunks: the next token's query rows are requested now and used after
+    // this token (head wave + 4 i of the group, clamped; a fixed count, so
+    // that no load sits behind a branch)
+    float nq[kMaxGroup / 4][2];
+    if constexpr (kTable) {
+      const int tn = t + 1 < t1 ? t + 1 : t;
+#pragma unroll
+      for (int i = 0; i < kMaxGroup / 4; ++i) {
+        const int h = min(wave + 4 * i, G - 1);
+        const float* qsrc = a.qkv + (int64_t)tn * a.qkv_rows + (int64_t)(g * G + h) * kHd;
+        nq[i][0] = qsrc[lane];
+        nq[i][1] = qsrc[lane + 64];
+      }
+    }
     float* po = a.part_o + part_base(t) * kHd;
     float2* pml = reinterpret_cast<float2*>(a.part_ml) + part_base(t);
     if (n == 0) {                                  // uniform over the block
@@ -558,7 +572,22 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_decode(AttnArgs a) {
     }
     if (++t >= t1) break;
     __syncthreads();                               // p, red, redl read; qs may be rewritten
-    form_queries(t);
+    if constexpr (kTable) {
+      for (int i = G * kHd + tid; i < kMaxGroup * kHd; i += kAttnThreads) qs[i / kHd][i % kHd] = 0.f;
+      const float2 cs = a.rope[(int64_t)t * (kHd / 2) + lane];
+#pragma unroll
+      for (int i = 0; i < kMaxGroup / 4; ++i) {
+        const int h = wave + 4 * i;
+        if (h < G) {
+          float q0 = nq[i][0], q1 = nq[i][1];
+          qk_norm_rope(q0, q1, cs, a.eps);
+          qs[h][lane] = q0 * scale;
+          qs[h][lane + 64] = q1 * scale;
+        }
+      }
+    } else {
+      form_queries(t);
+    }
     __syncthreads();
     query_operands(qs, col, lg, qh, ql);
   }
