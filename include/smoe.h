@@ -259,10 +259,15 @@ typedef struct smoe_attn_desc {
 } smoe_attn_desc;
 
 /* Bytes of device workspace for calls of up to max_batch (1..64) tokens; 0
- * when the descriptor is unsupported.  Host only. */
+ * when the descriptor is unsupported.  Host only.  From 3 tokens on it also
+ * holds the batched projections' bf16 inputs and fp32 partial sums (one set
+ * per 512-input slice: at d_model 4096 with 64 + 2 x 4 heads, about 19 MB for
+ * 64 tokens). */
 size_t smoe_attn_workspace_size(const smoe_attn_desc* desc, int32_t max_batch);
 
-/* One call of the block (a decode step, B <= 2, or B tokens of a chunk):
+/* One call of the block (a decode step, B <= 2, which runs matrix-vector
+ * projections, or a chunk of B = 3..64 tokens, whose projections read each
+ * weight matrix once for all of its tokens):
  *   wqkv  [(H + 2 Hkv) 128, d_model] bf16 bits, rows of q, then k, then v;
  *   wo    [d_model, H 128] bf16 bits;
  *   x     [B, d_model] f32; out [B, d_model] f32 (out may be x);
