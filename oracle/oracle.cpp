@@ -280,8 +280,9 @@ void oracle_rmsnorm(const float* v, int B, int d, float eps, float* out) {
     float ss = 0.0f;
     for (int i = 0; i < d; ++i) ss = ss + row[i] * row[i];
     const float mean = ss / static_cast<float>(d);
-    const float inv = 1.0f / std::sqrt(mean + eps);
-    for (int i = 0; i < d; ++i) out[static_cast<int64_t>(t) * d + i] = row[i] * inv;
+    // the definition as written: each element divided by the root
+    const float root = std::sqrt(mean + eps);
+    for (int i = 0; i < d; ++i) out[static_cast<int64_t>(t) * d + i] = row[i] / root;
   }
 }
 

@@ -364,3 +364,42 @@ def test_rmsnorm_closed_form():
     out = oracle.rmsnorm(v, eps=1e-6)
     assert np.allclose(out[0], 3.0 / math.sqrt(9 + 1e-6), rtol=1e-7)
     assert np.allclose(out[1], -2.0 / math.sqrt(4 + 1e-6), rtol=1e-7)
+
+
+def test_rmsnorm_epsilon_is_inside_the_root():
+    """Rows whose mean square is comparable to eps, where eps moves the
+    result by tens of percent: a dropped, misplaced or mis-scaled eps fails.
+    Closed forms: a constant row c gives c / sqrt(c^2 + eps); mean square =
+    eps exactly gives 1/sqrt(2) of the eps-free value; a zero row gives 0."""
+    eps = 1e-6
+    c = np.float32(1e-3)
+    v = np.zeros((4, 256), np.float32)
+    v[0] = c                                             # mean square 1e-6 = eps
+    v[1, ::2], v[1, 1::2] = 2e-3, -2e-3                  # mean square 4e-6
+    v[2] = 3e-4                                          # eps dominates
+    out = oracle.rmsnorm(v, eps=eps)
+    exp0 = float(c) / math.sqrt(float(c) ** 2 + eps)
+    assert abs(exp0 - 1 / math.sqrt(2)) < 1e-6
+    assert np.allclose(out[0], exp0, rtol=2e-6)
+    assert np.allclose(out[1, ::2], 2e-3 / math.sqrt(4e-6 + eps), rtol=2e-6)
+    assert np.allclose(out[1, 1::2], -2e-3 / math.sqrt(4e-6 + eps), rtol=2e-6)
+    assert np.allclose(out[2], 3e-4 / math.sqrt(9e-8 + eps), rtol=2e-6)
+    assert np.array_equal(out[3], np.zeros(256, np.float32))
+    # eps is used as given: another value gives the other closed form
+    out2 = oracle.rmsnorm(v[:1], eps=3e-6)
+    assert np.allclose(out2[0], float(c) / math.sqrt(float(c) ** 2 + 3e-6), rtol=2e-6)
+    # without eps the constant row would be exactly 1; with it, well below
+    assert np.all(out[0] < 0.71)
+
+
+def test_rmsnorm_random_rows_fp64():
+    """Random rows of several scales against the fp64 definition
+    x / sqrt(mean(x^2) + eps), within fp32 summation rounding."""
+    rng = np.random.default_rng(17)
+    d = 1024
+    v = (rng.standard_normal((5, d)) * np.array([1e-4, 1e-3, 1.0, 30.0, 1e3])[:, None]).astype(
+        np.float32)
+    out = oracle.rmsnorm(v, eps=1e-6)
+    v64 = v.astype(np.float64)
+    ref = v64 / np.sqrt((v64 ** 2).mean(axis=1, keepdims=True) + 1e-6)
+    assert np.all(np.abs(out - ref) <= (0.5 * d + 4) * 2.0 ** -24 * np.abs(ref) + 1e-30)
