@@ -113,6 +113,7 @@ smoe::FfnArgs ffn_args(const smoe_layer_desc* L, const smoe_experts* ex, const s
   a.out = out;
   a.xp = ws_at<uint16_t>(ws, lay.xp);
   a.xs = ws_at<float2>(ws, lay.xs);
+  a.xa = ws_at<float>(ws, lay.xa);
   a.hp = ws_at<uint16_t>(ws, lay.hp);
   a.hs = ws_at<float2>(ws, lay.hs);
   a.y = ws_at<float>(ws, lay.y);
@@ -266,7 +267,7 @@ SMOE_API int smoe_moe_forward(const smoe_layer_desc* desc, const smoe_experts* e
   hipStream_t s = static_cast<hipStream_t>(stream);
   smoe::FfnArgs a = ffn_args(desc, experts, un, topk_w, B, residual, out, ws, lay);
   hipError_t err = smoe::launch_prep(x, B, desc->d_model, ws_at<uint16_t>(ws, lay.xp),
-                                     ws_at<float2>(ws, lay.xs), s);
+                                     ws_at<float2>(ws, lay.xs), ws_at<float>(ws, lay.xa), s);
   if (err != hipSuccess) return SMOE_EHIP;
   return hip_rc(smoe::launch_ffn(a, s));
 }
@@ -306,6 +307,7 @@ int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_ex
   r->status = ws_at<uint32_t>(ws, lay.status);
   r->xp = ws_at<uint16_t>(ws, lay.xp);
   r->xs = ws_at<float2>(ws, lay.xs);
+  r->xa = ws_at<float>(ws, lay.xa);
   r->n_union = un->n_union;
   r->union_experts = un->union_experts;
   r->expert_offsets = un->expert_offsets;

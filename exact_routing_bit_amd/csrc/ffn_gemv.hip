@@ -224,7 +224,7 @@ template <int NTOK, int TPR, bool kShared>
 __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, int item, int nR,
                                            int lane, const GuBuf<TPR>& buf,
                                            const uint4 (&xr)[NTOK][8], const float2 (&xs)[NTOK],
-                                           uint16_t* st) {
+                                           const float (&xa)[NTOK], uint16_t* st) {
   constexpr int kRps = 64 / TPR;
   const int per = a.f / kJ;
   const bool sh = kShared && item >= nR;          // a shared-expert item: pair q = token q
@@ -255,9 +255,13 @@ __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, i
       for (int q = 0; q < NTOK; ++q) {
         if (q >= ne) break;
         const int t = NTOK == 1 ? 0 : (sh ? q : uniform(m.pairs[pb + q]) / a.K);
-        const float g = (NTOK == 1 || t == 0) ? r[kg][0] : r[kg][NTOK - 1];
-        const float up = (NTOK == 1 || t == 0) ? r[ku][0] : r[ku][NTOK - 1];
-        const float h = silu_mul(g, up);
+        const int ti = (NTOK == 1 || t == 0) ? 0 : NTOK - 1;
+        // the sums were taken over a_t x: 1/a_t (exact) gives g and u, and h
+        // is stored as a_t^2 h
+        const float at = xa[ti], ia = 1.0f / at;
+        const float g = r[kg][ti] * ia;
+        const float up = r[ku][ti] * ia;
+        const float h = silu_mul(g, up) * (at * at);
         const half_t hv = (j & 1) ? (half_t)((float)(half_t)h * 0.0625f) : (half_t)h;
         if (li == 0) st[jj * NTOK + q] = f16_bits(hv);
       }
@@ -287,8 +291,8 @@ struct DnItem {
 // slot's pair count and in ys[q] the ylds row of its q-th pair.
 template <int NTOK, bool kShared>
 __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, int u, int nU, int chw,
-                                          int r0, int lane, DnItem<NTOK>& it, int& ne,
-                                          int (&ys)[NTOK]) {
+                                          int r0, int lane, const float (&ib)[2], DnItem<NTOK>& it,
+                                          int& ne, int (&ys)[NTOK], float (&ysc)[NTOK]) {
   const bool sh = kShared && u >= nU;
   const int c = u - nU;
   const int Cr = sh ? a.fs / 8 : a.f / 8, Gr = Cr / 8;    // words and groups of a row
@@ -309,6 +313,7 @@ __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, in
     const int qq = max(min(q, ne - 1), 0);
     const int p = sh ? qq : uniform(m.pairs[pb + qq]);
     ys[q] = sh ? kMaxDecPairs + 2 * c + qq : p;
+    ysc[q] = (sh ? qq : p / a.K) == 0 ? ib[0] : ib[1];   // 1/a_t^2 of the pair's token
 #pragma unroll
     for (int k = 0; k < 4; ++k) it.h[q][k] = hsrc[(int64_t)p * Cr + cw + L * 4 + k];
   }
@@ -372,8 +377,8 @@ __device__ __forceinline__ float rows8_wave_sum(const float (&v)[8]) {
 // One item: the group sums of its pairs' h slices, the eight row dots, the
 // wave sums, and the rows' outputs into ylds[ys[q]][row] (live pairs only).
 template <int NTOK>
-__device__ __forceinline__ void down_compute(int ne, const int (&ys)[NTOK], int lane,
-                                             const DnItem<NTOK>& it, float* ylds) {
+__device__ __forceinline__ void down_compute(int ne, const int (&ys)[NTOK], const float (&ysc)[NTOK],
+                                             int lane, const DnItem<NTOK>& it, float* ylds) {
   float sc[kDnRows], bi[kDnRows];
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
@@ -409,7 +414,8 @@ __device__ __forceinline__ void down_compute(int ne, const int (&ys)[NTOK], int 
       acc = dot_word(it.w[r].w, it.h[q][3], acc);
       part[r] = sc[r] * (acc - S1024) + bi[r] * X;
     }
-    const float y = rows8_wave_sum(part);
+    // h held a_t^2 h: 1/a_t^2 (exact) gives the row outputs
+    const float y = rows8_wave_sum(part) * ysc[q];
     if (q < ne && (lane & 7) == 0) ylds[ys[q] * kDnRows + (lane >> 3)] = y;
   }
 }
@@ -592,6 +598,7 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   const int G = a.d / 64, li = lane % TPR;
   uint4 xr[NTOK][8];
   float2 xs[NTOK];
+  float xa[NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
     const int tt = min(t, a.B - 1);
@@ -599,6 +606,7 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
 #pragma unroll
     for (int q = 0; q < 8; ++q) xr[t][q] = src[q];
     xs[t] = a.xs[(int64_t)tt * G + li];
+    xa[t] = a.xa[tt];
   }
   // a ring of kGuDepth items: item i computes while the next kGuDepth - 1
   // items of this wave (i + W, i + 2W, ...) are in flight.  Loads past the
@@ -623,7 +631,7 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
       gu_load<TPR, kShared>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, nR, lo,
                    b[(s + kGuDepth - 1) % kGuDepth]);
       if (kLateRank && loc == 0) route_rank(a.K, slot_pair[wave], keep, tks);
-      gu_compute<NTOK, TPR, kShared>(a, m, it, nR, lane, b[s], xr, xs, hst[wave][loc]);
+      gu_compute<NTOK, TPR, kShared>(a, m, it, nR, lane, b[s], xr, xs, xa, hst[wave][loc]);
     }
   }
 flush:
@@ -713,13 +721,21 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   const int chw = kShared ? ((a.fs / 8 + nCh - 1) / nCh + 7) / 8 * 8 : 0;
   const int n_rb = a.d / kDnRows;
   const int K = a.K;
+  // 1/a_t^2 of the (at most two) tokens
+  float ib[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float at = a.xa[min(t, a.B - 1)];
+    ib[t] = 1.0f / (at * at);
+  }
   for (int rb = blockIdx.x; rb < n_rb; rb += gridDim.x) {
     const int r0 = rb * kDnRows;
     for (int u = wave; u < nU + nCh; u += kDnWaves) {
       DnItem<NTOK> it;
       int ne, ys[NTOK];
-      down_load<NTOK, kShared>(a, m, u, nU, chw, r0, lane, it, ne, ys);
-      down_compute<NTOK>(ne, ys, lane, it, ylds);
+      float ysc[NTOK];
+      down_load<NTOK, kShared>(a, m, u, nU, chw, r0, lane, ib, it, ne, ys, ysc);
+      down_compute<NTOK>(ne, ys, ysc, lane, it, ylds);
     }
     __syncthreads();
     // combine: out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k

@@ -344,6 +344,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     } else {
       wait_vmcnt<kTiles>();
     }
+    // the token scale a_t of the pairs this lane's accumulators hold (pair
+    // slots 4 lg + i), used in the epilogue only
+    float tsc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tsc[i] = a.xa[lpair[4 * lg + i] / Kt];
     {
       const int q = lpair[lane & 15];
       const int word = 4 * (wave & 1) + (lane >> 4);
@@ -412,7 +417,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = m0 + 4 * lg + i;
-          const float h = silu_mul(acc[Th][i], acc[Th + 2][i]);
+          // the sums were taken over a_t x: 1/a_t (exact) gives g and u, and
+          // h is stored as a_t^2 h
+          const float at = tsc[i], ia = 1.0f / at;
+          const float h = silu_mul(acc[Th][i] * ia, acc[Th + 2][i] * ia) * (at * at);
           const half_t xi = (half_t)h;
           const half_t stv = (j & 1) ? (half_t)((float)xi * 0.0625f) : xi;
           const float stf = (float)stv;
@@ -436,12 +444,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
         }
       }
     } else {
+      // h held a_t^2 h: 1/a_t^2 (exact) gives the outputs
+      float ib[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ib[i] = 1.0f / (tsc[i] * tsc[i]);
 #pragma unroll
       for (int T = 0; T < kTiles; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = m0 + 4 * lg + i;
-          if (m < ne) yout[(int64_t)lpair[m - m0] * a.d + rows0[T] + col] = acc[T][i];
+          if (m < ne) yout[(int64_t)lpair[m - m0] * a.d + rows0[T] + col] = acc[T][i] * ib[i];
         }
     }
   }

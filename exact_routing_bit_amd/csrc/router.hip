@@ -28,37 +28,67 @@ constexpr int kTailThreads = 1024;              // stand-alone top-k / union blo
 constexpr int kTopkThreads = 256;               // top-k grid: one token per wave
 constexpr int kMaxTicketBlocks = 64;            // larger grids hand the tail to its own kernel
 
-// Prepped activations of one (token, 64-input group): 8 chunks + group sums.
-// All 16 loads are issued before the first store (a store between them would
-// keep the compiler from hoisting the next loads above it).  With norm_out,
-// the group is first scaled by inv (the token's RMSNorm factor) and the
-// scaled values are also written to norm_out.
-__device__ void prep_group(const float* x, int d, int t, int g, uint16_t* xp, float2* xs,
-                           float* norm_out, float inv) {
-  const float4* src = reinterpret_cast<const float4*>(x + (int64_t)t * d + g * 64);
-  uint4* dst = reinterpret_cast<uint4*>(xp + (int64_t)t * d + g * 64);
+// Prepped activations of two tokens per 256-thread block: thread j handles
+// group j % 128 (64 inputs) of token 2 * blk + j / 128, i.e. the first two
+// waves token 0 and the last two token 1 (d <= 8192, so G = d/64 <= 128).
+// Every thread of the block must call it (it has block barriers).
+//   1. the group's 64 inputs are loaded (with norm_out: scaled by inv[j/128],
+//      the token's RMSNorm factor, and written to norm_out);
+//   2. the token's largest magnitude m gives a_t = 2^-floor(log2 m), clamped
+//      to 2^-30 .. 2^30 (1 for a zero row), so that max |a_t x| is in [1, 2);
+//   3. a_t * x goes to the prepped fp16 layout with its group sums, and a_t
+//      to xa[t].
+// All 16 loads of a thread are issued before its first store.
+__device__ __forceinline__ float token_scale(float mx) {
+  if (!(mx > 0.0f)) return 1.0f;
+  const int e = min(max(ilogbf(mx), -30), 30);
+  return __builtin_ldexpf(1.0f, -e);
+}
+__device__ void prep_two_tokens(const float* x, int B, int d, int blk, uint16_t* xp, float2* xs,
+                                float* xa, float* norm_out, const float (&inv)[2], float* red) {
+  const int tid = threadIdx.x, j = tid >> 7, g = tid & 127;
+  const int G = d / 64;
+  const int t = 2 * blk + j;
+  const bool live = t < B && g < G;
+  const int tt = live ? t : 0, gg = live ? g : 0;
+  const float4* src = reinterpret_cast<const float4*>(x + (int64_t)tt * d + gg * 64);
   float4 v4[16];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) v4[c] = src[c];
+  for (int c = 0; c < 16; ++c) v4[c] = live ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
   if (norm_out != nullptr) {
-    float4* hn = reinterpret_cast<float4*>(norm_out + (int64_t)t * d + g * 64);
+    const float sc = inv[j];
+    float4* hn = reinterpret_cast<float4*>(norm_out + (int64_t)tt * d + gg * 64);
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      v4[c] = make_float4(v4[c].x * inv, v4[c].y * inv, v4[c].z * inv, v4[c].w * inv);
-      hn[c] = v4[c];
+      v4[c] = make_float4(v4[c].x * sc, v4[c].y * sc, v4[c].z * sc, v4[c].w * sc);
+      if (live) hn[c] = v4[c];
     }
   }
+  float mx = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c)
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v4[c].x), fabsf(v4[c].y)), fmaxf(fabsf(v4[c].z), fabsf(v4[c].w))));
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  const float a = token_scale(fmaxf(red[2 * j], red[2 * j + 1]));
+  __syncthreads();                                // red may be reused after this
+  if (!live) return;
+  uint16_t* dst16 = xp + (int64_t)t * d + g * 64;
+  uint4* dst = reinterpret_cast<uint4*>(dst16);
   float X = 0.f, S = 0.f;
   uint4 out[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const float4 lo = v4[2 * c], hi = v4[2 * c + 1];
-    const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const float v[8] = {lo.x * a, lo.y * a, lo.z * a, lo.w * a, hi.x * a, hi.y * a, hi.z * a,
+                        hi.w * a};
     out[c] = prep_chunk(v, &X, &S);
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) dst[c] = out[c];
-  xs[(int64_t)t * (d / 64) + g] = make_float2(X, 1024.0f * S);
+  xs[(int64_t)t * G + g] = make_float2(X, 1024.0f * S);
+  if (g == 0) xa[t] = a;
 }
 
 // Top-k of one token's E <= 256 logits by one full wave; writes indices and
@@ -301,20 +331,17 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
       if (e < a.E) logits_wave<kBf16>(a, e, t0, min(kTokensPerWave, a.B - t0));
     }
   } else if (a.xp != nullptr && blockIdx.y == 0) {
-    // with a.norm_out (B <= kTokensPerWave) the block forms the tokens'
-    // RMSNorm factors first (block_row_inv), then preps the scaled rows
+    // two tokens per prep block; with a.norm_out (B <= kTokensPerWave, one
+    // prep block) the block forms the tokens' RMSNorm factors first
+    // (block_row_inv), then preps the scaled rows
     float inv[kTokensPerWave] = {1.f, 1.f};
     if (a.norm_out != nullptr) {
 #pragma unroll
       for (int j = 0; j < kTokensPerWave; ++j)
         if (j < a.B) inv[j] = block_row_inv(a.x + (int64_t)j * a.d, a.d, a.norm_eps, part);
     }
-    const int G = a.d / 64;
-    const int u = (blockIdx.x - n_logit_blocks) * kRouteThreads + threadIdx.x;
-    if (u < a.B * G) {
-      const int t = u / G;
-      prep_group(a.x, a.d, t, u % G, a.xp, a.xs, a.norm_out, t == 0 ? inv[0] : inv[1]);
-    }
+    prep_two_tokens(a.x, a.B, a.d, blockIdx.x - n_logit_blocks, a.xp, a.xs, a.xa, a.norm_out,
+                    inv, part);
   }
   if (!do_tail) return;
   // last block: every other block's logits are visible after its release and our acquire
@@ -421,10 +448,10 @@ __global__ __launch_bounds__(kTailThreads) void k_topk_union(RouteArgs a, int do
 }
 
 __global__ __launch_bounds__(256) void k_prep(const float* x, int B, int d, uint16_t* xp,
-                                              float2* xs) {
-  const int G = d / 64;
-  const int u = blockIdx.x * blockDim.x + threadIdx.x;
-  if (u < B * G) prep_group(x, d, u / G, u % G, xp, xs, nullptr, 1.f);
+                                              float2* xs, float* xa) {
+  __shared__ float red[4];
+  const float inv[2] = {1.f, 1.f};
+  prep_two_tokens(x, B, d, blockIdx.x, xp, xs, xa, nullptr, inv, red);
 }
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
@@ -447,7 +474,7 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
   bool tail_done = false;
   if (!logits_in) {
     // logits (+ activation prep); small grids finish top-k/union in their last block
-    const int prep_blocks = a.xp != nullptr ? (a.B * (a.d / 64) + kRouteThreads - 1) / kRouteThreads : 0;
+    const int prep_blocks = a.xp != nullptr ? (a.B + 1) / 2 : 0;   // two tokens a block
     const dim3 grid((a.E + 3) / 4 + prep_blocks, (a.B + kTokensPerWave - 1) / kTokensPerWave);
     const bool fused = (do_topk || do_union) && (int)(grid.x * grid.y) <= kMaxTicketBlocks;
     uint32_t* ticket = a.status + 1;
@@ -472,9 +499,9 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
   return hipSuccess;
 }
 
-hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, hipStream_t s) {
-  const int units = B * (d / 64);
-  hipLaunchKernelGGL(k_prep, dim3((units + 255) / 256), dim3(256), 0, s, x, B, d, xp, xs);
+hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, float* xa,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(k_prep, dim3((B + 1) / 2), dim3(256), 0, s, x, B, d, xp, xs, xa);
   return hipGetLastError();
 }
 

@@ -13,6 +13,13 @@
 //                      stored halves (float2 per group).
 //   h (gate/up output) is stored in the same prepped layout, with its group
 //                      sums as two 32-column partials per group.
+//   token scales       xa [B] f32: a power of two a_t per token.  The prepped
+//                      activations hold a_t * x (a_t brings the row's largest
+//                      magnitude into [1, 2)), and h of a pair of token t is stored as
+//                      a_t^2 * h, so that neither leaves the fp16 range when
+//                      the hidden states or the weights are far from O(1).
+//                      Dot products over them are rescaled by 1/a_t (gate,
+//                      up) and 1/a_t^2 (down) in fp32, which is exact.
 #pragma once
 
 #include <hip/hip_ext.h>
@@ -37,6 +44,7 @@ struct WsLayout {
   size_t logits;   // [B, E] f32
   size_t xp;       // [B, d] f16 prepped activations
   size_t xs;       // [B, d/64] float2 group sums of xp
+  size_t xa;       // [B] f32 token scales (powers of two)
   size_t hp;       // [P, f] f16 prepped h
   size_t hs;       // [P, f/64, 2] float2 half-group sums of hp
   size_t y;        // [P, d] f32 per-pair expert outputs
@@ -62,6 +70,7 @@ inline WsLayout ws_layout(const smoe_layer_desc& L, int B) {
   w.logits = take((size_t)B * L.num_experts * 4);
   w.xp = take((size_t)B * L.d_model * 2);
   w.xs = take((size_t)B * (L.d_model / 64) * 8);
+  w.xa = take((size_t)B * 4);
   w.hp = take(P * L.ffn_dim * 2);
   w.hs = take(P * (L.ffn_dim / 64) * 2 * 8);
   w.y = take(P * L.d_model * 4);
@@ -95,6 +104,7 @@ struct RouteArgs {
   // prepped activations (written by the router kernel when non-null)
   uint16_t* xp;
   float2* xs;
+  float* xa;
   // union outputs (built after top-k when non-null)
   int32_t* n_union;
   int32_t* union_experts;
@@ -120,6 +130,7 @@ struct FfnArgs {
   float* out;
   const uint16_t* xp;
   const float2* xs;
+  const float* xa;     // token scales a_t (see the layouts above)
   uint16_t* hp;
   float2* hs;
   float* y;
@@ -244,7 +255,8 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
 // top K indices and weights to a.topk_idx / a.topk_w, all R indices in rank
 // order to ranked [B, R].
 hipError_t launch_topk_ranked(const RouteArgs& a, int R, int32_t* ranked, hipStream_t s);
-hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, hipStream_t s);
+hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, float* xa,
+                       hipStream_t s);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 hipError_t launch_gate_up(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);
 hipError_t launch_down(const FfnArgs& a, hipStream_t s, const LaunchTiming* t = nullptr);

@@ -34,6 +34,8 @@ def lib():
         L.oracle_router_logits.argtypes = [vp, i32, vp, i32, i32, i32, vp]
         L.oracle_topk_softmax.argtypes = [vp, i32, i32, i32, i32, vp, vp]
         L.oracle_rank.argtypes = [vp, i32, i32, i32, vp]
+        L.oracle_weights_of.argtypes = [vp, i32, i32, i32, i32, vp, vp]
+        L.oracle_weights_of.restype = i32
         L.oracle_build_union.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.oracle_build_union.restype = i32
         L.oracle_dequant.argtypes = [vp, vp, vp, i32, i32, vp]
@@ -93,6 +95,19 @@ def rank(logits: np.ndarray, R: int) -> np.ndarray:
     out = np.empty((B, R), np.int32)
     lib().oracle_rank(pl, B, E, R, out.ctypes.data)
     return out
+
+
+def weights_of(logits: np.ndarray, idx: np.ndarray, norm: bool = True) -> np.ndarray:
+    """Routing weights [B, K] of the given expert sets idx [B, K] from the
+    logits' full softmax (renormalised over the set when norm)."""
+    logits, pl = _c(logits, np.float32)
+    idx, pi = _c(idx, np.int32)
+    B, E = logits.shape
+    K = idx.shape[1]
+    w = np.empty((B, K), np.float32)
+    if lib().oracle_weights_of(pl, B, E, K, int(norm), pi, w.ctypes.data) != 0:
+        raise ValueError("expert id out of range")
+    return w
 
 
 def route(Wr, x, K, norm=True):

@@ -129,6 +129,37 @@ void oracle_topk_softmax(const float* logits, int B, int E, int K, int norm, int
   }
 }
 
+// Routing weights of a given set of K experts per token (idx, rank order as
+// given), from the same full softmax as oracle_topk_softmax: p over all E,
+// then p of the set divided by its sum (norm) or p itself.  For the top-k set
+// this is exactly oracle_topk_softmax's weights; tests use it where two
+// correct routings differ at a near-tie and the weights of the other set are
+// needed.  Ids outside [0, E) give -1.
+int oracle_weights_of(const float* logits, int B, int E, int K, int norm, const int32_t* idx,
+                      float* w) {
+  std::vector<float> p(E);
+  for (int t = 0; t < B; ++t) {
+    const float* l = logits + static_cast<int64_t>(t) * E;
+    for (int k = 0; k < K; ++k)
+      if (idx[t * K + k] < 0 || idx[t * K + k] >= E) return -1;
+    float m = l[0];
+    for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+    float Z = 0.0f;
+    for (int e = 0; e < E; ++e) {
+      p[e] = std::exp(l[e] - m);
+      Z = Z + p[e];
+    }
+    for (int e = 0; e < E; ++e) p[e] = p[e] / Z;
+    float S = 0.0f;
+    for (int k = 0; k < K; ++k) S = S + p[idx[t * K + k]];
+    for (int k = 0; k < K; ++k) {
+      const float pk = p[idx[t * K + k]];
+      w[t * K + k] = norm ? pk / S : pk;
+    }
+  }
+  return 0;
+}
+
 // The R highest-ranked experts of each token, in rank order: larger logit
 // first, equal logits by lower index ("Data Flow", the routing step: ranked
 // top-(8+spec), ranks 8 and up queued for speculative prefetch; "Surface

@@ -51,6 +51,13 @@ void oracle_topk_softmax(const float* logits, int B, int E, int K, int norm, int
 // The R highest-ranked experts per token, rank order (ranked [B, R]).
 void oracle_rank(const float* logits, int B, int E, int R, int32_t* ranked);
 
+/* Routing weights of a given K-expert set per token (rank order as given),
+ * from the full softmax of the logits: p_e / sum over the set (norm) or p_e.
+ * For the top-k set it equals oracle_topk_softmax's weights.  Returns -1 on
+ * an id outside [0, E), else 0. */
+int oracle_weights_of(const float* logits, int B, int E, int K, int norm, const int32_t* idx,
+                      float* w);
+
 /* Expert union and per-expert pair lists ([LMP] "The Inversion": dedupe the
  * chunk's experts, apply each union expert to every routed token).
  * Pair p = t*K + k.  Returns n_union; union_experts ascending;

@@ -37,6 +37,30 @@ def rel_l2(a, ref) -> float:
     return float(np.linalg.norm(a - ref) / np.linalg.norm(ref))
 
 
+def token_errors(out, ref, residual=None):
+    """Relative L2 error of the whole [B, d] output and of each token's row
+    (fp64).  With a residual, both sides have it subtracted first, so the
+    error is measured on what the layer adds."""
+    a = np.asarray(out, np.float64)
+    r = np.asarray(ref, np.float64)
+    if residual is not None:
+        a = a - residual
+        r = r - residual
+    whole = float(np.linalg.norm(a - r) / np.linalg.norm(r))
+    per = np.linalg.norm(a - r, axis=-1) / np.linalg.norm(r, axis=-1)
+    return whole, per
+
+
+def assert_layer_close(out, ref, tol, residual=None, what=""):
+    """The layer bar: relative L2 <= tol over the whole output AND for every
+    token's row (one bad row or lane cannot hide in a large batch)."""
+    whole, per = token_errors(out, ref, residual)
+    worst = int(np.argmax(per))
+    assert whole <= tol, f"{what} whole-output rel L2 {whole:.3e} > {tol}"
+    assert per[worst] <= tol, f"{what} token {worst}: rel L2 {per[worst]:.3e} > {tol}"
+    return whole, float(per[worst])
+
+
 def desc_for(smoe, cfg):
     return smoe.make_desc(cfg.d_model, cfg.ffn_dim, cfg.num_experts, cfg.top_k,
                           cfg.norm_topk_prob, cfg.router_bf16, cfg.shared_ffn_dim)

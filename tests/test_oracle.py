@@ -107,6 +107,32 @@ def test_topk_all_experts_is_full_softmax():
         assert sorted(idx[t]) == list(range(16))
 
 
+def test_weights_of_a_given_set():
+    """Weights of an arbitrary K-expert set: scipy's fp64 softmax restricted
+    to the set (renormalised or not); for the top-k set, bit for bit the
+    top-k weights; a permuted set permutes them; a bad id is rejected."""
+    rng = np.random.default_rng(3)
+    lg = (rng.standard_normal((20, 48)) * 2).astype(np.float32)
+    sets = np.stack([rng.choice(48, 6, replace=False) for _ in range(20)]).astype(np.int32)
+    for norm in (True, False):
+        w = oracle.weights_of(lg, sets, norm)
+        for t in range(20):
+            p = softmax(lg[t].astype(np.float64))[sets[t]]
+            ref = p / p.sum() if norm else p
+            assert np.allclose(w[t], ref, rtol=2e-6, atol=0)
+        idx, wt = oracle.topk_softmax(lg, 6, norm)
+        assert np.array_equal(oracle.weights_of(lg, idx, norm).view(np.uint32), wt.view(np.uint32))
+        # a permuted set permutes the weights (the set's sum is then added in
+        # another order: equal up to its rounding)
+        perm = sets[:, ::-1].copy()
+        assert np.allclose(oracle.weights_of(lg, perm, norm), w[:, ::-1], rtol=1e-6, atol=0)
+    assert np.allclose(oracle.weights_of(lg, sets, True).sum(axis=1), 1.0, atol=1e-6)
+    bad = sets.copy()
+    bad[4, 2] = 48
+    with pytest.raises(ValueError):
+        oracle.weights_of(lg, bad)
+
+
 def test_rank_hand_worked_and_definition():
     """Ranked output ("Data Flow": ranked top-(8+spec)): by hand on ties, then
     the definition by brute force on tie-heavy rows (integer logits): the
