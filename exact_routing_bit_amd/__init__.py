@@ -33,7 +33,8 @@ EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_ro
             "smoe_build_union",
             "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_rmsnorm",
             "smoe_stack_forward", "smoe_read_status", "smoe_strerror",
-            "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage")
+            "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage",
+            "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes")
 
 
 class SmoeError(RuntimeError):
@@ -88,6 +89,10 @@ def _load():
                                    i32, vp, vp, vp, sz, vp]
     L.smoe_moe_layer.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp, vp,
                                  ctypes.POINTER(Union), vp, sz, vp]
+    L.smoe_moe_layer_noalloc.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp,
+                                         vp, ctypes.POINTER(Union), vp]
+    L.smoe_noalloc_scratch_bytes.argtypes = []
+    L.smoe_noalloc_scratch_bytes.restype = sz
     L.smoe_moe_layer_stage.argtypes = [ctypes.c_int, dp, vp, ctypes.POINTER(Experts), vp, i32, vp,
                                        vp, vp, vp, vp, ctypes.POINTER(Union), vp, sz, vp, vp, vp]
     L.smoe_rmsnorm.argtypes = [vp, i32, i32, ctypes.c_float, vp, vp]
@@ -104,7 +109,8 @@ def _load():
     L.smoe_attn_forward_stage.argtypes = [ctypes.c_int, ap, vp, vp, vp, i32, i64, vp, vp, vp, vp,
                                           sz, vp, vp, vp]
     for name in EXPORTED:
-        if name not in ("smoe_workspace_size", "smoe_strerror", "smoe_attn_workspace_size"):
+        if name not in ("smoe_workspace_size", "smoe_strerror", "smoe_attn_workspace_size",
+                        "smoe_noalloc_scratch_bytes"):
             getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -265,6 +271,26 @@ def moe_layer(desc, router_w, experts: Experts, x, out, topk_idx, topk_w, un: Un
                               _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu),
                               _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
            "smoe_moe_layer")
+
+
+def moe_layer_noalloc(desc, router_w, experts: Experts, x, out, topk_idx, topk_w,
+                      un: UnionBuffers, residual=None, logits=None, stream=None):
+    """moe_layer with the library's own device scratch: no workspace argument
+    and no allocation (see smoe_moe_layer_noalloc in include/smoe.h)."""
+    cu = un.c()
+    _check(lib.smoe_moe_layer_noalloc(ctypes.byref(desc), _ptr(router_w, None, "router_w"),
+                                      ctypes.byref(experts), _ptr(x, torch.float32, "x"),
+                                      x.shape[0], _ptr(residual, torch.float32, "residual"),
+                                      _ptr(out, torch.float32, "out"),
+                                      _ptr(logits, torch.float32, "logits"),
+                                      _ptr(topk_idx, torch.int32, "topk_idx"),
+                                      _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu),
+                                      _stream(stream)),
+           "smoe_moe_layer_noalloc")
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib.smoe_noalloc_scratch_bytes())
 
 
 def moe_layer_stage(stage, desc, router_w, experts: Experts, x, out, topk_idx, topk_w,

@@ -272,9 +272,10 @@ SMOE_API int smoe_moe_forward(const smoe_layer_desc* desc, const smoe_experts* e
   return hip_rc(smoe::launch_ffn(a, s));
 }
 
-namespace {
+namespace smoe {
 
-// Validation and argument set-up shared by smoe_moe_layer and its stages.
+// Validation and argument set-up shared by smoe_moe_layer, its stages and
+// the no-allocation variant.
 int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_experts* experts,
                 const float* x, int32_t B, const float* residual, float* out, float* logits,
                 int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
@@ -317,7 +318,7 @@ int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_ex
   return SMOE_OK;
 }
 
-}  // namespace
+}  // namespace smoe
 
 namespace {
 
@@ -344,6 +345,10 @@ hipError_t launch_decode_logits(const smoe::RouteArgs& r, hipStream_t s,
   return smoe::launch_router(r, false, false, false, s, t);   // logits + activation prep
 }
 
+}  // namespace
+
+namespace smoe {
+
 // The kernels of one whole layer, in stream order.
 hipError_t launch_layer(const smoe::RouteArgs& r, const smoe::FfnArgs& a, hipStream_t s) {
   hipError_t err;
@@ -363,7 +368,10 @@ hipError_t launch_layer(const smoe::RouteArgs& r, const smoe::FfnArgs& a, hipStr
   return err;
 }
 
-}  // namespace
+}  // namespace smoe
+
+using smoe::launch_layer;
+using smoe::layer_setup;
 
 SMOE_API int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w,
                             const smoe_experts* experts, const float* x, int32_t B,

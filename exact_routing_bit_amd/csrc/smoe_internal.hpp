@@ -248,6 +248,15 @@ struct LaunchTiming {
       hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                       \
   } while (0)
 
+// Host-side validation and set-up of one layer call (api.cpp): fills r and a
+// for workspace ws; SMOE_OK or the SMOE_E* error.  Launches nothing.
+int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_experts* experts,
+                const float* x, int32_t B, const float* residual, float* out, float* logits,
+                int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
+                RouteArgs* r, FfnArgs* a);
+// The kernels of one whole layer call set up by layer_setup, in stream order.
+hipError_t launch_layer(const RouteArgs& r, const FfnArgs& a, hipStream_t s);
+
 // All return hipSuccess or the launch error.
 hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
                          hipStream_t s, const LaunchTiming* t = nullptr);

@@ -26,8 +26,9 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronise, except smoe_read_status.
  *   - The caller owns every buffer: weights, activations, outputs, union
- *     lists and the workspace.  The library allocates nothing, keeps no
- *     state between calls and never frees caller memory.
+ *     lists and the workspace.  The library allocates nothing and never
+ *     frees caller memory; apart from the device scratch array of
+ *     smoe_moe_layer_noalloc (below), it keeps no state between calls.
  *   - Return 0 on success or a negative SMOE_E* code.  Every argument check
  *     happens before anything is launched, so a failed call has no effect.
  *   - Pair p = t*top_k + k is token t's rank-k expert.
@@ -204,6 +205,32 @@ int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w, const smoe
                    const float* x, int32_t B, const float* residual, float* out, float* logits,
                    int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws,
                    size_t ws_bytes, void* stream);
+
+/* smoe_moe_layer without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  The
+ * arguments and results are those of smoe_moe_layer with ws/ws_bytes left
+ * out; the kernels are the same, so the outputs are bit for bit those of
+ * smoe_moe_layer on the same inputs.
+ * The scratch (status word, logits, prepped activations, h, per-pair
+ * outputs) is a device array of the library's own, smoe_noalloc_scratch_bytes()
+ * = 16 MiB, which every GPU the library runs on holds until the process
+ * ends; its address is taken on a device's first call, which also clears
+ * its status area with a kernel on `stream`.  A call needing more scratch
+ * than that (smoe_workspace_size(desc, B) > 16 MiB: e.g. d_model 8192 with
+ * ffn_dim 8192 at 64 tokens) returns SMOE_EWORKSPACE and launches nothing.
+ * Every call on one GPU shares that GPU's array and it keeps the last call's
+ * contents: calls that may overlap on one GPU (two streams, or host threads
+ * without ordering) race; calls ordered on one stream do not.  Invalid
+ * expert ids are skipped as in smoe_moe_layer; their status bit is not
+ * reported by this entry point.  Other errors as smoe_moe_layer. */
+int smoe_moe_layer_noalloc(const smoe_layer_desc* desc, const void* router_w,
+                           const smoe_experts* experts, const float* x, int32_t B,
+                           const float* residual, float* out, float* logits, int32_t* topk_idx,
+                           float* topk_w, const smoe_union* un, void* stream);
+
+/* Bytes of the device scratch smoe_moe_layer_noalloc uses (host only). */
+size_t smoe_noalloc_scratch_bytes(void);
 
 /* Diagnostic: enqueue one stage of smoe_moe_layer, so that a caller can time
  * each one.  Same arguments as smoe_moe_layer, plus two optional hipEvent_t
