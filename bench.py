@@ -4,17 +4,26 @@ SwiGLU experts -> combine) on one MI355X.
 A step is one call of the whole layer (router gate matvec, softmax/top-k,
 union and pair lists, gate_up, down, combine) on one fresh batch.  Steps
 rotate over a stack of distinct layers resident in HBM (16 by default) so
-that the weights stream from HBM, not from the 256 MB Infinity Cache.
+that the weights stream from HBM, not from the 256 MB Infinity Cache.  Each
+call's arguments are marshalled once; before anything is timed, every
+rotated layer runs at both batch sizes and then for 0.3 s more (clocks and
+caches in their steady state whatever --steps and --warmup are).
 
 Prints one JSON line:
   value       tokens/s of the decode layer (d=4096, 128 experts, top-8,
               ffn 1536, B=1), whole job, inputs resident in HBM;
   effective_gbps / hbm_frac   bytes of the distinct routed experts per step
               (packed words + bf16 scales + biases) / step time, vs 8 TB/s;
-  secondary   the same layer as a 64-token prefill chunk;
   roofline    the dominant kernel (gate_up) timed with HIP events on its
-              launch stream: algorithmic bytes per launch / mean duration;
-  cpu_baseline  the CPU oracle on a bounded sample of the decode workload.
+              launch stream over a fixed 1000 back-to-back launches:
+              algorithmic bytes per launch / mean duration;
+  kernels_back_to_back   the same for the down kernel;
+  secondary   the same layer as a 64-token prefill chunk, and the 256-expert
+              fused layer (d=2048, ffn 512) at B=1 and B=64, each with its
+              FFN kernels' rates;
+  calibration a plain streaming read of 4 GiB (smoe_stream_read);
+  stack       the 94-layer stacked harness;
+  cpu_baseline  the CPU oracle on bounded samples of the same workload.
 """
 from __future__ import annotations
 
@@ -38,9 +47,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--prefill-steps", type=int, default=200)
     p.add_argument("--layers", type=int, default=16, help="distinct layers rotated through")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-fused", action="store_true",
+                   help="leave out the 256-expert fused layer (B=1 and B=64)")
     p.add_argument("--stack", action="store_true",
                    help="run only the stacked harness (94 layers: prompt chunks, then decode)")
     p.add_argument("--no-stack", action="store_true", help="leave the stacked harness out")
@@ -61,7 +72,8 @@ def parse():
 
 
 class Stack:
-    """n distinct layers of one shape in device memory plus shared buffers."""
+    """n distinct layers of one shape in device memory plus shared buffers.
+    Calls are marshalled once per (layer, input) and then repeated."""
 
     def __init__(self, smoe, cfg, n_layers, max_batch):
         import torch
@@ -82,19 +94,26 @@ class Stack:
         self.idx = torch.zeros(max_batch, cfg.top_k, dtype=torch.int32, device=dev)
         self.w = torch.zeros(max_batch, cfg.top_k, dtype=torch.float32, device=dev)
         self.out = torch.zeros(max_batch, cfg.d_model, dtype=torch.float32, device=dev)
+        self._calls = {}
         torch.cuda.synchronize()
 
-    def call(self, l, x):
-        W, ex = self.layers[l]
-        B = x.shape[0]
-        self.smoe.moe_layer(self.desc, W["router"], ex, x, self.out[:B], self.idx[:B],
-                            self.w[:B], self.un, self.ws)
+    def prepared(self, l, x, stage=None):
+        key = (l, x.data_ptr(), x.shape[0], stage)
+        c = self._calls.get(key)
+        if c is None:
+            W, ex = self.layers[l]
+            B = x.shape[0]
+            c = self.smoe.prepare_moe_layer(self.desc, W["router"], ex, x, self.out[:B],
+                                            self.idx[:B], self.w[:B], self.un, self.ws,
+                                            stage=stage)
+            self._calls[key] = c
+        return c
 
-    def stage(self, st, l, x, events=None):
-        W, ex = self.layers[l]
-        B = x.shape[0]
-        self.smoe.moe_layer_stage(st, self.desc, W["router"], ex, x, self.out[:B], self.idx[:B],
-                                  self.w[:B], self.un, self.ws, events=events)
+    def call(self, l, x):
+        self.prepared(l, x)()
+
+    def stage(self, st, l, x):
+        self.prepared(l, x, st)()
 
 
 def x_pool(cfg, B, n):
@@ -102,43 +121,69 @@ def x_pool(cfg, B, n):
     return [sg.hidden(cfg.seed, 0, 1000 + i, B, cfg.d_model) for i in range(n)]
 
 
-def time_layer(stack, xs, steps, warmup):
-    """Seconds for `steps` whole-layer calls, rotating layers and inputs."""
+def warm_pass(stack, pools, seconds=0.3):
+    """Untimed: every rotated layer with every batch size, then more layer
+    calls until `seconds` have passed, so that clocks and caches are in their
+    steady state before anything is timed, whatever --steps and --warmup are."""
     import torch
     nl = len(stack.layers)
+    for xs in pools:
+        for l in range(nl):
+            stack.call(l, xs[l % len(xs)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(32):
+            xs = pools[i % len(pools)]
+            stack.call(i % nl, xs[i % len(xs)])
+            i += 1
+        torch.cuda.synchronize()
+
+
+def time_layer(stack, xs, steps, warmup):
+    """Seconds for `steps` whole-layer calls, rotating layers and inputs, timed
+    with events between two synchronisations after `warmup` untimed calls."""
+    import torch
+    nl = len(stack.layers)
+    calls = [stack.prepared(s % nl, xs[s % len(xs)]) for s in range(max(steps, warmup))]
     for s in range(warmup):
-        stack.call(s % nl, xs[s % len(xs)])
+        calls[s]()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for s in range(steps):
-        stack.call(s % nl, xs[s % len(xs)])
+        calls[s]()
     t1.record()
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / 1e3
 
 
-def time_gate_up(stack, xs, launches):
-    """Mean gate_up kernel duration (s): HIP events on the launch stream around
-    `launches` back-to-back gate_up launches over the rotating layers, all
-    with the logits (|U| = 8 experts at B = 1) of one routed token; at B = 1
-    the kernel also ranks them and builds the union.  Events
-    around each single launch would add the runtime's marker overhead
-    (about 3 us) to every sample; back to back, only the dispatch gaps
-    between consecutive kernels remain."""
+ROOFLINE_LAUNCHES = 1000
+
+
+def time_stage(stack, xs, stage, launches=ROOFLINE_LAUNCHES):
+    """Mean duration (s) of one stage's kernel: HIP events on its launch stream
+    around `launches` back-to-back launches over the rotating layers, all with
+    the routing of one input (the route stage runs once first, so every
+    launch sees that input's union).  A fixed count, independent of --steps.
+    Events around each single launch would add the runtime's marker overhead
+    (a few microseconds) to every sample; back to back, consecutive kernels
+    overlap one's tail with the next one's start instead."""
     import torch
     smoe = stack.smoe
     nl = len(stack.layers)
     stack.stage(smoe.SMOE_STAGE_ROUTE, 0, xs[0])
-    for i in range(20):
-        stack.stage(smoe.SMOE_STAGE_GATE_UP, i % nl, xs[0])
+    calls = [stack.prepared(i % nl, xs[0], stage) for i in range(nl)]
+    for i in range(50):
+        calls[i % nl]()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(launches):
-        stack.stage(smoe.SMOE_STAGE_GATE_UP, i % nl, xs[0])
+        calls[i % nl]()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / launches / 1e3
@@ -154,6 +199,80 @@ def union_sizes(stack, xs, steps):
         sizes.append(stack.un.n_union.clone())
     torch.cuda.synchronize()
     return [int(t.item()) for t in sizes]
+
+
+def gate_up_bytes(cfg):
+    """Packed words + scales + biases of one expert's gate and up projections."""
+    d, f = cfg.d_model, cfg.ffn_dim
+    return 2 * (f * d // 2 + 2 * 2 * f * d // 64)
+
+
+def down_bytes(cfg):
+    d, f = cfg.d_model, cfg.ffn_dim
+    return d * f // 2 + 2 * 2 * d * f // 64
+
+
+def layer_entry(stack, cfg, xs, steps, warmup, kernels=True):
+    """One workload's figures: step time, tokens/s, effective expert GB/s and
+    its fraction of the HBM peak, and (kernels) each FFN kernel's mean
+    duration back to back with its algorithmic bytes and rate."""
+    B = cfg.batch
+    t = time_layer(stack, xs, steps, warmup)
+    sz = union_sizes(stack, xs, min(steps, 256))
+    u = sum(sz) / len(sz)
+    step = t / steps
+    eb = cfg.expert_bytes()
+    gbps = u * eb / step / 1e9
+    e = {"workload": cfg.name, "batch": B, "steps": steps, "ms_per_step": round(step * 1e3, 5),
+         "tokens_per_s": round(B / step, 1), "mean_union": u,
+         "effective_bytes_per_step": int(u * eb), "effective_gbps": round(gbps, 1),
+         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    if kernels:
+        smoe = stack.smoe
+        u0 = union_sizes(stack, xs[:1], 1)[0]
+        ks = {}
+        for name, st, nbytes in (("gate_up", smoe.SMOE_STAGE_GATE_UP, gate_up_bytes(cfg)),
+                                 ("down", smoe.SMOE_STAGE_DOWN, down_bytes(cfg))):
+            ts = time_stage(stack, xs, st)
+            b = u0 * nbytes
+            ks[name] = {"mean_launch_us": round(ts * 1e6, 3), "bytes_per_launch": int(b),
+                        "gbps": round(b / ts / 1e9, 1), "frac": round(b / ts / 1e9 / HBM_PEAK_GBPS, 4)}
+        e["kernels_back_to_back"] = ks
+    return e
+
+
+STREAM_BYTES = 4 << 30
+
+
+def stream_read_calibration(smoe):
+    """Read bandwidth of a plain stream of 16-byte nontemporal loads over a
+    4 GiB buffer (smoe_stream_read, far larger than the 256 MB memory-side
+    cache), for several workgroup counts: the rate this part reaches on a
+    pure stream, context for the kernels' fractions of the 8 TB/s peak."""
+    import torch
+    dev = torch.device("cuda:0")
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.ones(STREAM_BYTES // 4, dtype=torch.int32, device=dev)
+    out = {}
+    for per_cu in (2, 4, 8):
+        sink = torch.zeros(ncu * per_cu, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            smoe.stream_read(buf, sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 10
+        e0.record()
+        for _ in range(n):
+            smoe.stream_read(buf, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / n
+        out[f"{per_cu}_blocks_per_cu"] = round(STREAM_BYTES / t / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    best = max(out.values())
+    return {"kernel": "k_stream_read (smoe_stream_read)", "bytes": STREAM_BYTES,
+            "gbps_by_grid": out, "best_gbps": best, "best_frac": round(best / HBM_PEAK_GBPS, 4)}
 
 
 def shared_bench(smoe, args):
@@ -315,35 +434,81 @@ def attention_bench(smoe, args):
     }
 
 
-def cpu_baseline(cfg, seconds):
-    """The oracle (as it stands) on a bounded sample of the decode workload:
-    route + layer-major MoE of single tokens through layer 0, repeated until
-    `seconds` of CPU time have elapsed.  Weight generation is not timed."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def host_layer(W):
+    """Host copies of one device layer's input bytes (router, gate, up, down)
+    for the oracle: the generator's bytes, the same as the CPU generator's."""
+    import numpy as np
+    import torch
+
+    def h(t):
+        return tuple(t_.cpu().numpy().view(np.uint32 if t_.dtype == torch.int32 else np.uint16)
+                     for t_ in t)
+    return {"router": W["router"].cpu().numpy().view(np.uint16), "gate": h(W["gate"]),
+            "up": h(W["up"]), "down": h(W["down"])}
+
+
+def cpu_baseline(cfg, L, seconds):
+    """The oracle (as it stands) on bounded samples of the same workload, on
+    the host cores: exact routing plus the layer-major FFN of layer 0
+    (L: host copies of its weights), timed with perf_counter.
+      * decode tokens (B = 1) on every core OpenMP gives it, for ~seconds/2;
+      * the same on one core, for ~seconds/4;
+      * one 64-token prefill chunk on every core (all of its ~126 union
+        experts).  Weight copies to the host are not timed."""
     import numpy as np
 
     import oracle
     import synth
-    Wr = synth.router(cfg.seed, 0, cfg.num_experts, cfg.d_model, cfg.router_sigma, cfg.router_bf16)
-    tokens = [synth.hidden(cfg.seed, 0, 1000 + i, 1, cfg.d_model) for i in range(4)]
-    routed = set()
-    for x in tokens:
-        _, idx, _ = oracle.route(Wr, x, cfg.top_k, cfg.norm_topk_prob)
-        routed.update(int(e) for e in idx.reshape(-1))
-    L = synth.make_layer(cfg, layer=0, experts=sorted(routed))
-    done = 0
+    from synth import configs
+    tokens = [synth.hidden(cfg.seed, 0, 1000 + i, 1, cfg.d_model) for i in range(8)]
+
+    def decode_rate(budget):
+        done, t0 = 0, time.perf_counter()
+        while True:
+            x = tokens[done % len(tokens)]
+            _, idx, w = oracle.route(L["router"], x, cfg.top_k, cfg.norm_topk_prob)
+            oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, layer_major=True)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return done / el, done, el
+
+    all_cores = oracle.num_threads()
+    v_all, n_all, el_all = decode_rate(seconds / 2)
+    oracle.set_num_threads(1)
+    try:
+        v_one, n_one, el_one = decode_rate(seconds / 4)
+    finally:
+        oracle.set_num_threads(all_cores)
+    pre = configs.PREFILL
+    x64 = synth.hidden(pre.seed, 0, 1000, pre.batch, pre.d_model)
     t0 = time.perf_counter()
-    while True:
-        x = tokens[done % len(tokens)]
-        _, idx, w = oracle.route(Wr, x, cfg.top_k, cfg.norm_topk_prob)
-        oracle.moe(L["gate"], L["up"], L["down"], x, idx, w, layer_major=True)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": done * cfg.batch / el, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{done} single-token decode calls of layer 0 ({len(tokens)} distinct tokens, "
-                      f"{len(routed)} experts generated beforehand), {el:.1f} s"}
+    _, idx, w = oracle.route(L["router"], x64, pre.top_k, pre.norm_topk_prob)
+    oracle.moe(L["gate"], L["up"], L["down"], x64, idx, w, layer_major=True)
+    el64 = time.perf_counter() - t0
+    return {"value": round(v_all, 3), "unit": "tokens/s", "cores": all_cores, "kind": "oracle",
+            "sample": f"{n_all} single-token decode calls of layer 0 of the decode layer "
+                      f"(routing + layer-major FFN), {el_all:.1f} s on {all_cores} threads",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "single_core": {"value": round(v_one, 3), "unit": "tokens/s", "cores": 1,
+                            "sample": f"{n_one} decode calls, {el_one:.1f} s"},
+            "prefill_chunk_b64": {"value": round(pre.batch / el64, 2), "unit": "tokens/s",
+                                  "cores": all_cores,
+                                  "sample": f"one 64-token chunk of layer 0 "
+                                            f"({len(np.unique(idx))} union experts), "
+                                            f"{el64:.1f} s"}}
 
 
 # ------------------------------------------------------------------ stack
@@ -641,56 +806,57 @@ def main():
                           "config": {"workload": r.pop("workload")}, "stack": r}), flush=True)
         return
 
-    dec = configs.DECODE
+    # the decode layer (B = 1) and its 64-token prefill chunk over 16 rotated layers
+    dec, pre = configs.DECODE, configs.PREFILL
     stack = Stack(smoe, dec, args.layers, max_batch=64)
     xs1 = x_pool(dec, 1, 257)
-    t = time_layer(stack, xs1, args.steps, args.warmup)
-    eb = dec.expert_bytes()
-    sizes1 = union_sizes(stack, xs1, min(args.steps, 512))
-    u1 = sum(sizes1) / len(sizes1)
-    step_s = t / args.steps
-    gbps = u1 * eb / step_s / 1e9
-    # roofline: gate_up (two thirds of the expert bytes) timed on its own
-    gu_s = time_gate_up(stack, xs1, min(args.steps, 2000))
-    gu_bytes = u1 * (2 * dec.ffn_dim * dec.d_model // 2 + 2 * 2 * 2 * dec.ffn_dim * dec.d_model // 64)
-    gu_gbps = gu_bytes / gu_s / 1e9
-
+    xs64 = x_pool(pre, 64, 17)
+    warm_pass(stack, [xs1, xs64])
+    main_e = layer_entry(stack, dec, xs1, args.steps, args.warmup)
+    gu = main_e["kernels_back_to_back"]["gate_up"]
+    step_s = main_e["ms_per_step"] / 1e3
     result = {
-        "metric": METRIC, "value": round(dec.batch * args.steps / t, 1), "unit": "tokens/s",
+        "metric": METRIC, "value": main_e["tokens_per_s"], "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "ms_per_step": main_e["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": f"{dec.name}: one routed MoE layer, d=4096, 128 experts, top-8 "
                                "norm_topk_prob, ffn 1536, 4-bit g64 experts, B=1 decode",
-                   "layers_rotated": args.layers, "mean_union": u1,
-                   "effective_bytes_per_step": int(u1 * eb)},
-        "effective_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                   "layers_rotated": args.layers, "mean_union": main_e["mean_union"],
+                   "effective_bytes_per_step": main_e["effective_bytes_per_step"],
+                   "warm_pass": "every rotated layer at B=1 and B=64, then 0.3 s of layer calls"},
+        "effective_gbps": main_e["effective_gbps"], "hbm_frac": main_e["hbm_frac"],
         "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL,
-                     "achieved": round(gu_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gu_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_per_launch(),
-                     "bytes_per_launch": int(gu_bytes), "mean_launch_us": round(gu_s * 1e6, 3)},
+                     "achieved": gu["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gu["frac"], "traffic": traffic_per_launch(),
+                     "bytes_per_launch": gu["bytes_per_launch"],
+                     "mean_launch_us": gu["mean_launch_us"], "launches": ROOFLINE_LAUNCHES},
+        "kernels_back_to_back": main_e["kernels_back_to_back"],
     }
+    sec = {}
     if not args.no_prefill:
-        pre = configs.PREFILL
-        xs64 = x_pool(pre, 64, 17)
-        tp = time_layer(stack, xs64, args.prefill_steps, 5)
-        sz = union_sizes(stack, xs64, args.prefill_steps)
-        up_ = sum(sz) / len(sz)
-        sp = tp / args.prefill_steps
-        g64 = up_ * eb / sp / 1e9
-        result["secondary"] = {"workload": f"{pre.name}: same layer, 64-token prefill chunk",
-                               "tokens_per_s": round(64 * args.prefill_steps / tp, 1),
-                               "ms_per_step": round(sp * 1e3, 5), "mean_union": up_,
-                               "effective_gbps": round(g64, 1),
-                               "hbm_frac": round(g64 / HBM_PEAK_GBPS, 4),
-                               "steps": args.prefill_steps}
+        sec["prefill_b64"] = layer_entry(stack, pre, xs64, args.prefill_steps, 5)
+    L0 = None if args.no_cpu else host_layer(stack.layers[0][0])
     del stack
     torch.cuda.empty_cache()
+    if not args.no_fused:
+        f1, f64 = configs.FUSED_B1, configs.FUSED_B64
+        fst = Stack(smoe, f1, args.layers, max_batch=64)
+        xf1, xf64 = x_pool(f1, 1, 257), x_pool(f64, 64, 17)
+        warm_pass(fst, [xf1, xf64])
+        sec["fused_b1"] = layer_entry(fst, f1, xf1, max(args.steps, 200), args.warmup)
+        if not args.no_prefill:
+            sec["fused_b64"] = layer_entry(fst, f64, xf64, args.prefill_steps, 5)
+        del fst
+        torch.cuda.empty_cache()
+    if sec:
+        result["secondary"] = sec
+    result["calibration"] = stream_read_calibration(smoe)
     if not args.no_stack:
         result["stack"] = stack_harness(smoe, args.stack_layers, args.stack_prompt,
                                         args.stack_decode)
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(dec, args.cpu_seconds)
+    if L0 is not None:
+        result["cpu_baseline"] = cpu_baseline(dec, L0, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -34,7 +34,7 @@ EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_ro
             "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_rmsnorm",
             "smoe_stack_forward", "smoe_read_status", "smoe_strerror",
             "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage",
-            "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes")
+            "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes", "smoe_stream_read")
 
 
 class SmoeError(RuntimeError):
@@ -91,6 +91,7 @@ def _load():
                                  ctypes.POINTER(Union), vp, sz, vp]
     L.smoe_moe_layer_noalloc.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp,
                                          vp, ctypes.POINTER(Union), vp]
+    L.smoe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     L.smoe_noalloc_scratch_bytes.argtypes = []
     L.smoe_noalloc_scratch_bytes.restype = sz
     L.smoe_moe_layer_stage.argtypes = [ctypes.c_int, dp, vp, ctypes.POINTER(Experts), vp, i32, vp,
@@ -273,6 +274,45 @@ def moe_layer(desc, router_w, experts: Experts, x, out, topk_idx, topk_w, un: Un
            "smoe_moe_layer")
 
 
+class PreparedCall:
+    """A library call whose arguments are marshalled once (pointers, the
+    descriptor structs, the stream), for loops that repeat the same call on
+    the same buffers: calling it is one ctypes call.  The tensors and structs
+    it points to are kept alive by the object."""
+
+    def __init__(self, fn, what, args, keep):
+        self._fn, self._what, self._args, self._keep = fn, what, args, keep
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != SMOE_OK:
+            raise SmoeError(rc, self._what)
+
+
+def prepare_moe_layer(desc, router_w, experts: Experts, x, out, topk_idx, topk_w,
+                      un: UnionBuffers, ws, residual=None, logits=None, stream=None,
+                      stage=None, events=None) -> PreparedCall:
+    """moe_layer (or, with ``stage``, moe_layer_stage) with its arguments
+    marshalled once."""
+    cu = un.c()
+    vp = ctypes.c_void_p
+    common = (vp(_ptr(x, torch.float32, "x")), x.shape[0],
+              vp(_ptr(residual, torch.float32, "residual")), vp(_ptr(out, torch.float32, "out")),
+              vp(_ptr(logits, torch.float32, "logits")),
+              vp(_ptr(topk_idx, torch.int32, "topk_idx")),
+              vp(_ptr(topk_w, torch.float32, "topk_w")), ctypes.byref(cu),
+              vp(_ptr(ws, torch.uint8, "ws")), ws.numel(), vp(_stream(stream)))
+    keep = (desc, experts, router_w, x, out, topk_idx, topk_w, un, ws, residual, logits, cu)
+    head = (ctypes.byref(desc), vp(_ptr(router_w, None, "router_w")), ctypes.byref(experts))
+    if stage is None:
+        return PreparedCall(lib.smoe_moe_layer, "smoe_moe_layer", head + common, keep)
+    ev = (None, None)
+    if events is not None:
+        ev = tuple(vp(e.cuda_event) for e in events)
+    return PreparedCall(lib.smoe_moe_layer_stage, "smoe_moe_layer_stage",
+                        (int(stage),) + head + common + ev, keep + (events,))
+
+
 def moe_layer_noalloc(desc, router_w, experts: Experts, x, out, topk_idx, topk_w,
                       un: UnionBuffers, residual=None, logits=None, stream=None):
     """moe_layer with the library's own device scratch: no workspace argument
@@ -287,6 +327,14 @@ def moe_layer_noalloc(desc, router_w, experts: Experts, x, out, topk_idx, topk_w
                                       _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu),
                                       _stream(stream)),
            "smoe_moe_layer_noalloc")
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes=None, stream=None):
+    """Diagnostic streaming read of a device buffer (see smoe_stream_read):
+    sink is an int32 tensor with one entry per workgroup."""
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    _check(lib.smoe_stream_read(_ptr(buf, None, "buf"), n, _ptr(sink, torch.int32, "sink"),
+                                sink.numel(), _stream(stream)), "smoe_stream_read")
 
 
 def noalloc_scratch_bytes() -> int:

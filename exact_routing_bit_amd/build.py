@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 SOURCES = ["api.cpp", "router.hip", "ffn.hip", "ffn_gemv.hip", "ffn_mfma.hip", "norm.hip",
-           "attn.hip", "noalloc.hip"]
+           "attn.hip", "noalloc.hip", "diag.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
          "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 LIB = os.path.join(HERE, "libsmoe.so")

@@ -353,6 +353,15 @@ int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers, const void
                        int32_t* topk_idx, float* topk_w, int32_t* n_union, const smoe_union* un,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------- calibration */
+/* Diagnostic: a plain streaming read of `bytes` (a multiple of 16) at `src`
+ * (16-byte aligned) by `blocks` workgroups of 256 threads with 16-byte
+ * nontemporal loads; block b writes the xor of what it read to sink[b]
+ * (sink: `blocks` uint32, device).  Measures the read bandwidth the part
+ * reaches on a pure stream, against which the layer's kernels are judged.
+ * Async on stream; SMOE_EINVAL on bad arguments, 1 <= blocks <= 2^20. */
+int smoe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+
 /* ------------------------------------------------------------ utilities */
 /* Synchronises `stream`, then copies the workspace status bits into
  * *status_out (host).  For tests and diagnostics, not for the hot path. */
