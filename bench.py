@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-fused", action="store_true",
                    help="leave out the 256-expert fused layer (B=1 and B=64)")
+    p.add_argument("--workloads", default="decode,prefill,fused_b1,fused_b64",
+                   help="comma list of decode, prefill, fused_b1, fused_b64 (the value line "
+                        "needs decode; the others go to secondary)")
     p.add_argument("--stack", action="store_true",
                    help="run only the stacked harness (94 layers: prompt chunks, then decode)")
     p.add_argument("--no-stack", action="store_true", help="leave the stacked harness out")
@@ -65,9 +68,14 @@ def parse():
     p.add_argument("--stack-decode", type=int, default=128)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a device-to-device copy of COPY_BYTES (for the counter scale)")
-    p.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
-                                                            "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                   help="write the traffic summary from rocprofv3 --pmc counter CSVs and exit")
+    p.add_argument("--summarize-counters", nargs="+",
+                   metavar="OUT LABEL COPY_FETCH_CSV COPY_WRITE_CSV CSV",
+                   help="write a per-kernel summary of rocprofv3 --pmc counter CSVs (any "
+                        "counters; FETCH_SIZE/WRITE_SIZE scaled by the copy calibration) to OUT "
+                        "and exit")
+    p.add_argument("--trace-csv", default=None,
+                   help="with --summarize-counters: the kernel_stats.csv of the same command, "
+                        "for kernel durations (MFMA rates)")
     return p.parse_args()
 
 
@@ -689,7 +697,8 @@ def stack_harness(smoe, n_layers, prompt, steps):
 # once they change, the figure is stale and `traffic` is reported as null.
 COPY_BYTES = 1 << 30
 ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64, true, false>"
-ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/device.hpp",
+ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/ffn_mfma.hip",
+                    "exact_routing_bit_amd/csrc/router.hip", "exact_routing_bit_amd/csrc/device.hpp",
                     "exact_routing_bit_amd/csrc/smoe_internal.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_up_gemv_decode_b1_traffic.txt")
 
@@ -714,51 +723,115 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": COPY_BYTES, "repeats": 3}), flush=True)
 
 
-def _counter_rows(path, counter):
+def _counter_rows(path, counter=None):
+    """(kernel, grid size, counter, value) of every dispatch row of a
+    rocprofv3 --pmc CSV (one counter, or all)."""
     import csv
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            if r.get("Counter_Name") == counter:
-                yield r["Kernel_Name"], float(r["Counter_Value"])
+            if counter is None or r.get("Counter_Name") == counter:
+                yield (r["Kernel_Name"], int(r.get("Grid_Size") or 0), r["Counter_Name"],
+                       float(r["Counter_Value"]), r.get("Dispatch_Id"))
 
 
-def summarize_counters(fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
-    def per_dispatch(path, counter, match):
-        vals = [v for k, v in _counter_rows(path, counter) if match(k)]
-        if not vals:
-            raise SystemExit(f"no {counter} rows for the kernel in {path}")
-        return sum(vals) / len(vals), len(vals)
+def short_kernel(name):
+    import re
+    n = name.replace("smoe::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+    n = re.sub(r"^void ", "", n)
+    i = n.find("(")
+    j = n.find(">")
+    # keep template arguments, drop the parameter list
+    if i >= 0 and (j < 0 or i < n.find("<") or j < i):
+        n = n[:i]
+    elif i >= 0:
+        k = n.find("(", j)
+        n = n[:k] if k >= 0 else n
+    return n.strip()
 
-    is_gu = lambda k: ROOFLINE_KERNEL in k
-    is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
-    f_kib, nf = per_dispatch(fetch_csv, "FETCH_SIZE", is_gu)
-    w_kib, nw = per_dispatch(write_csv, "WRITE_SIZE", is_gu)
-    cf = [v for k, v in _counter_rows(copy_fetch_csv, "FETCH_SIZE") if is_copy(k)]
-    cw = [v for k, v in _counter_rows(copy_write_csv, "WRITE_SIZE") if is_copy(k)]
-    if not cf or not cw:
-        raise SystemExit("no copy-kernel rows in the calibration CSVs")
-    # the copy's largest dispatch is the 1 GiB copy itself
-    cf_kib, cw_kib = max(cf), max(cw)
-    f_scale = COPY_BYTES / (cf_kib * 1024.0)
-    w_scale = COPY_BYTES / (cw_kib * 1024.0)
-    traffic = f_kib * 1024.0 * f_scale + w_kib * 1024.0 * w_scale
-    lines = [
-        f"# HBM traffic per launch of {ROOFLINE_KERNEL} on the decode layer (B=1)",
-        "# from rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (two passes) over",
-        "#   python3 bench.py --no-cpu --no-stack --no-prefill --steps 200 --warmup 10",
-        "# scaled by the same counters for a 1 GiB device copy:",
-        "#   python3 bench.py --copy-calibration",
-        f"kernel: {ROOFLINE_KERNEL}",
-        f"kernel_sources_sha256: {sources_sha()}",
-        f"fetch_kib_per_dispatch: {f_kib:.1f}  (mean of {nf} dispatches)",
-        f"write_kib_per_dispatch: {w_kib:.1f}  (mean of {nw} dispatches)",
-        f"copy_fetch_kib: {cf_kib:.1f}  (copy of {COPY_BYTES} bytes; scale {f_scale:.4f})",
-        f"copy_write_kib: {cw_kib:.1f}  (scale {w_scale:.4f})",
-        f"traffic_bytes_per_launch: {traffic:.0f}",
-    ]
-    with open(TRAFFIC_FILE, "w") as fh:
+
+def _copy_scale(path, counter):
+    vals = [v for k, _, c, v, _ in _counter_rows(path, counter) if "copyBuffer" in k or
+            "copy" in k.lower()]
+    if not vals:
+        raise SystemExit(f"no copy-kernel rows for {counter} in {path}")
+    return COPY_BYTES / (max(vals) * 1024.0), max(vals)
+
+
+def summarize_counters(out, label, copy_fetch_csv, copy_write_csv, *csvs, trace_csv=None):
+    """Per (kernel, grid size): the mean of every collected counter per
+    dispatch.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are turned into
+    HBM bytes with the scale that makes the same counter read a 1 GiB device
+    copy as 1 GiB.  With the kernel_stats.csv of the same command, MFMA
+    counters become rates: MOPS_F16 x 512 flops over the kernel's mean
+    duration, and MFMA busy cycles over GUI-active cycles x 1024 SIMDs."""
+    import csv
+    from collections import defaultdict
+    f_scale, cf = _copy_scale(copy_fetch_csv, "FETCH_SIZE")
+    w_scale, cw = _copy_scale(copy_write_csv, "WRITE_SIZE")
+    acc = defaultdict(lambda: defaultdict(list))
+    for path in csvs:
+        for k, g, c, v, _ in _counter_rows(path):
+            acc[(short_kernel(k), g)][c].append(v)
+    dur = {}
+    if trace_csv:
+        with open(trace_csv) as fh:
+            for r in csv.DictReader(fh):
+                dur[short_kernel(r["Name"])] = float(r["AverageNs"]) / 1e3
+    rows = []
+    for (k, g), cs in sorted(acc.items(), key=lambda kv: kv[0]):
+        if "copyBuffer" in k or k.startswith("at::") or k.startswith("k_quant") or k in (
+                "k_hidden", "k_router", "k_fill_u32"):
+            continue
+        r = {"kernel": k, "grid": g, "dispatches": max(len(v) for v in cs.values())}
+        for c, vals in cs.items():
+            r[c] = sum(vals) / len(vals)
+        if "FETCH_SIZE" in r:
+            r["hbm_read_bytes"] = r["FETCH_SIZE"] * 1024.0 * f_scale
+        if "WRITE_SIZE" in r:
+            r["hbm_write_bytes"] = r["WRITE_SIZE"] * 1024.0 * w_scale
+        if "SQ_INSTS_VALU_MFMA_MOPS_F16" in r and k in dur:
+            r["mfma_f16_tflops"] = r["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512 / (dur[k] * 1e-6) / 1e12
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in r and r.get("GRBM_GUI_ACTIVE"):
+            r["mfma_busy_pct"] = 100.0 * r["SQ_VALU_MFMA_BUSY_CYCLES"] / (r["GRBM_GUI_ACTIVE"] * 1024)
+        if "SQ_LDS_BANK_CONFLICT" in r and r.get("SQ_LDS_IDX_ACTIVE"):
+            r["lds_conflict_per_active"] = r["SQ_LDS_BANK_CONFLICT"] / r["SQ_LDS_IDX_ACTIVE"]
+        rows.append(r)
+    cols = ["hbm_read_bytes", "hbm_write_bytes", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+            "SQ_INSTS_VALU_MFMA_MOPS_F16", "mfma_f16_tflops", "mfma_busy_pct", "SQ_INSTS_LDS",
+            "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "lds_conflict_per_active",
+            "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
+            "GRBM_GUI_ACTIVE"]
+    lines = [f"# rocprofv3 --pmc counters per dispatch: {label}",
+             "# passes (one rocprofv3 run each, the same command):",
+             *[f"#   {p}" for p in csvs],
+             f"# FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}: the same counters "
+             f"read {cf:.0f} / {cw:.0f} KiB for a {COPY_BYTES}-byte device copy "
+             "(python3 bench.py --copy-calibration)",
+             f"# kernel sources sha256: {sources_sha()}", ""]
+    for r in rows:
+        lines.append(f"kernel: {r['kernel']}  grid: {r['grid']}  dispatches: {r['dispatches']}")
+        for c in cols:
+            if c in r:
+                v = r[c]
+                lines.append(f"  {c}: {v:.4g}" if isinstance(v, float) else f"  {c}: {v}")
+    with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+    # the roofline kernel's traffic line (read by traffic_per_launch)
+    for r in rows:
+        if r["kernel"] == ROOFLINE_KERNEL and "hbm_read_bytes" in r and "hbm_write_bytes" in r:
+            t = r["hbm_read_bytes"] + r["hbm_write_bytes"]
+            tl = [f"# HBM traffic per launch of {ROOFLINE_KERNEL} on the decode layer (B=1)",
+                  f"# from {out}",
+                  f"kernel: {ROOFLINE_KERNEL}",
+                  f"kernel_sources_sha256: {sources_sha()}",
+                  f"fetch_kib_per_dispatch: {r['FETCH_SIZE']:.1f}",
+                  f"write_kib_per_dispatch: {r['WRITE_SIZE']:.1f}",
+                  f"copy_fetch_kib: {cf:.1f}  (scale {f_scale:.4f})",
+                  f"copy_write_kib: {cw:.1f}  (scale {w_scale:.4f})",
+                  f"traffic_bytes_per_launch: {t:.0f}"]
+            with open(TRAFFIC_FILE, "w") as fh:
+                fh.write("\n".join(tl) + "\n")
 
 
 def traffic_per_launch():
@@ -777,7 +850,9 @@ def traffic_per_launch():
 def main():
     args = parse()
     if args.summarize_counters:
-        summarize_counters(*args.summarize_counters)
+        if len(args.summarize_counters) < 5:
+            raise SystemExit("--summarize-counters OUT LABEL COPY_FETCH_CSV COPY_WRITE_CSV CSV...")
+        summarize_counters(*args.summarize_counters, trace_csv=args.trace_csv)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -806,53 +881,62 @@ def main():
                           "config": {"workload": r.pop("workload")}, "stack": r}), flush=True)
         return
 
+    wl = set(w.strip() for w in args.workloads.split(",") if w.strip())
+    if args.no_prefill:
+        wl -= {"prefill", "fused_b64"}
+    if args.no_fused:
+        wl -= {"fused_b1", "fused_b64"}
     # the decode layer (B = 1) and its 64-token prefill chunk over 16 rotated layers
     dec, pre = configs.DECODE, configs.PREFILL
-    stack = Stack(smoe, dec, args.layers, max_batch=64)
-    xs1 = x_pool(dec, 1, 257)
-    xs64 = x_pool(pre, 64, 17)
-    warm_pass(stack, [xs1, xs64])
-    main_e = layer_entry(stack, dec, xs1, args.steps, args.warmup)
-    gu = main_e["kernels_back_to_back"]["gate_up"]
-    step_s = main_e["ms_per_step"] / 1e3
-    result = {
-        "metric": METRIC, "value": main_e["tokens_per_s"], "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": main_e["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": f"{dec.name}: one routed MoE layer, d=4096, 128 experts, top-8 "
-                               "norm_topk_prob, ffn 1536, 4-bit g64 experts, B=1 decode",
-                   "layers_rotated": args.layers, "mean_union": main_e["mean_union"],
-                   "effective_bytes_per_step": main_e["effective_bytes_per_step"],
-                   "warm_pass": "every rotated layer at B=1 and B=64, then 0.3 s of layer calls"},
-        "effective_gbps": main_e["effective_gbps"], "hbm_frac": main_e["hbm_frac"],
-        "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL,
-                     "achieved": gu["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gu["frac"], "traffic": traffic_per_launch(),
-                     "bytes_per_launch": gu["bytes_per_launch"],
-                     "mean_launch_us": gu["mean_launch_us"], "launches": ROOFLINE_LAUNCHES},
-        "kernels_back_to_back": main_e["kernels_back_to_back"],
-    }
-    sec = {}
-    if not args.no_prefill:
+    result, sec, L0 = {}, {}, None
+    if "decode" in wl or "prefill" in wl:
+        stack = Stack(smoe, dec, args.layers, max_batch=64)
+        xs1 = x_pool(dec, 1, 257)
+        xs64 = x_pool(pre, 64, 17)
+        warm_pass(stack, [xs1, xs64])
+    if "decode" in wl:
+        main_e = layer_entry(stack, dec, xs1, args.steps, args.warmup)
+        gu = main_e["kernels_back_to_back"]["gate_up"]
+        result = {
+            "metric": METRIC, "value": main_e["tokens_per_s"], "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": main_e["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": f"{dec.name}: one routed MoE layer, d=4096, 128 experts, top-8 "
+                                   "norm_topk_prob, ffn 1536, 4-bit g64 experts, B=1 decode",
+                       "layers_rotated": args.layers, "mean_union": main_e["mean_union"],
+                       "effective_bytes_per_step": main_e["effective_bytes_per_step"],
+                       "warm_pass": "every rotated layer at B=1 and B=64, then 0.3 s of layer calls"},
+            "effective_gbps": main_e["effective_gbps"], "hbm_frac": main_e["hbm_frac"],
+            "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL,
+                         "achieved": gu["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": gu["frac"], "traffic": traffic_per_launch(),
+                         "bytes_per_launch": gu["bytes_per_launch"],
+                         "mean_launch_us": gu["mean_launch_us"], "launches": ROOFLINE_LAUNCHES},
+            "kernels_back_to_back": main_e["kernels_back_to_back"],
+        }
+    if "prefill" in wl:
         sec["prefill_b64"] = layer_entry(stack, pre, xs64, args.prefill_steps, 5)
-    L0 = None if args.no_cpu else host_layer(stack.layers[0][0])
-    del stack
-    torch.cuda.empty_cache()
-    if not args.no_fused:
+    if "decode" in wl or "prefill" in wl:
+        if not args.no_cpu and "decode" in wl:
+            L0 = host_layer(stack.layers[0][0])
+        del stack
+        torch.cuda.empty_cache()
+    if "fused_b1" in wl or "fused_b64" in wl:
         f1, f64 = configs.FUSED_B1, configs.FUSED_B64
         fst = Stack(smoe, f1, args.layers, max_batch=64)
         xf1, xf64 = x_pool(f1, 1, 257), x_pool(f64, 64, 17)
         warm_pass(fst, [xf1, xf64])
-        sec["fused_b1"] = layer_entry(fst, f1, xf1, max(args.steps, 200), args.warmup)
-        if not args.no_prefill:
+        if "fused_b1" in wl:
+            sec["fused_b1"] = layer_entry(fst, f1, xf1, max(args.steps, 200), args.warmup)
+        if "fused_b64" in wl:
             sec["fused_b64"] = layer_entry(fst, f64, xf64, args.prefill_steps, 5)
         del fst
         torch.cuda.empty_cache()
     if sec:
         result["secondary"] = sec
     result["calibration"] = stream_read_calibration(smoe)
-    if not args.no_stack:
+    if not args.no_stack and "decode" in wl:
         result["stack"] = stack_harness(smoe, args.stack_layers, args.stack_prompt,
                                         args.stack_decode)
     if L0 is not None:

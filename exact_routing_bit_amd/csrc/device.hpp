@@ -69,6 +69,13 @@ __device__ __forceinline__ void dma16_to_lds(const void* src, void* lds_base) {
                "s"(lds_addr(lds_base))
                : "memory", "m0");
 }
+// The same with the nontemporal hint: for the last read of a line, which may
+// then leave the cache first (the line's other half was read before).
+__device__ __forceinline__ void dma16_to_lds_nt(const void* src, void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src),
+               "s"(lds_addr(lds_base))
+               : "memory", "m0");
+}
 __device__ __forceinline__ void dma4_to_lds(const void* src, void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src),
                "s"(lds_addr(lds_base))

@@ -773,21 +773,6 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
 }
 
 
-// Compute units of the current device, cached per device (an attribute
-// lookup, not state of any call).
-int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return 0;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int NTOK, int TPR, bool kRoute>
 hipError_t launch_gate_up_gemv(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
                                const LaunchTiming* t) {
@@ -832,6 +817,21 @@ hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming*
 }
 
 }  // namespace
+
+// Compute units of the current device, cached per device (an attribute
+// lookup, not state of any call).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 
 // The decode path applies to B <= 2 tokens (B*K <= 16) with d = 2048 or 4096
 // (one gate_up group per lane, 32 or 64 lanes a row) and f <= 2048 (a down

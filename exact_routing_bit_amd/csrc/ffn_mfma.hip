@@ -93,14 +93,27 @@ __device__ __forceinline__ const void* align4(const uint16_t* p) {
 // Copies of stage k (groups gA = 2k and gB = min(2k+1, G-1)) into `slot`:
 // the packed words (issue_words, kTiles copies) and the rest (issue_rest:
 // activations, sums and, without kFastSB, the scale/bias dwords).
+// Stage k copies bytes 64k .. 64k+63 of every row: with rows that start on a
+// 128-byte line (line_aligned), an even stage reads the first half of its
+// lines and the next (odd) stage the second half, which is then the line's
+// last use: that copy carries the nontemporal hint, so that the streamed
+// weights leave the L2 first and the activations that every workgroup of an
+// expert re-reads stay in it.
 template <bool kGateUp>
 __device__ __forceinline__ void issue_words(const Sources& S, char* slot, int k, int G, int wave,
-                                            int lane) {
+                                            int lane, bool line_aligned) {
   const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
   // packed words: lanes 0-31 copy group gA, lanes 32-63 group gB
   const int gw = (lane >> 5) ? gB : gA;
+  if (line_aligned && (k & 1)) {
 #pragma unroll
-  for (int T = 0; T < kTiles; ++T) dma16_to_lds(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
+    for (int T = 0; T < kTiles; ++T)
+      dma16_to_lds_nt(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
+  } else {
+#pragma unroll
+    for (int T = 0; T < kTiles; ++T)
+      dma16_to_lds(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
+  }
 }
 template <bool kGateUp, bool kFastSB>
 __device__ __forceinline__ void issue_rest(const Sources& S, char* slot, int k, int G, int wave,
@@ -290,6 +303,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     }
   }
   const int nst = (G + kGps - 1) / kGps;
+  // rows of C words start on 128-byte lines when every expert's matrix does
+  bool line_aligned = (C * 4) % 128 == 0;
+#pragma unroll
+  for (int T = 0; T < kTiles; ++T) {
+    const QMat& m = kGateUp ? (T < 2 ? qg : qu) : qd;
+    line_aligned = line_aligned && (reinterpret_cast<uintptr_t>(m.w + e * m.stride_w) & 127) == 0;
+  }
   // kFastSB: this wave's scales and biases for the whole K loop, read once as
   // contiguous runs (lane l: row rows0[T] + l/4, 16-byte piece 4h + l%4 of the
   // row's G/8), not as 16-byte pieces of 64 rows per four stages; each group
@@ -337,9 +357,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
       else
         dma4_to_lds(a.pair_list + pb + min(m0 + lane, ne - 1), lpair);
     }
-    issue_words<kGateUp>(S, ring, 0, G, wave, lane);
+    issue_words<kGateUp>(S, ring, 0, G, wave, lane, line_aligned);
     if (nst > 1) {
-      issue_words<kGateUp>(S, ring + kSlot, 1, G, wave, lane);
+      issue_words<kGateUp>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
       wait_vmcnt<2 * kTiles>();
     } else {
       wait_vmcnt<kTiles>();
@@ -383,7 +403,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
         /* this wave's words of stage k+2 go to its own part of slot k-1, which */               \
         /* only it reads (its compute of k-1 is done): no need to wait for the others */         \
         if (k + 2 < nst)                                                                          \
-          issue_words<kGateUp>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave, lane);        \
+          issue_words<kGateUp>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave, lane,         \
+                               line_aligned);                                                     \
         barrier_no_wait();           /* every wave's copies of k landed; slot k-1 is free */      \
         if (k + 2 < nst)                                                                          \
           issue_rest<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave,        \

@@ -257,6 +257,9 @@ int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_ex
 // The kernels of one whole layer call set up by layer_setup, in stream order.
 hipError_t launch_layer(const RouteArgs& r, const FfnArgs& a, hipStream_t s);
 
+// Compute units of the current device (0 when the query fails).
+int cu_count();
+
 // All return hipSuccess or the launch error.
 hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool do_union,
                          hipStream_t s, const LaunchTiming* t = nullptr);
