@@ -19,7 +19,9 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsmoe.so")
+# SMOE_LIBRARY may name another build of the same library (the sanitizer
+# build of build_sanitized.py); by default the in-tree libsmoe.so
+LIB_PATH = os.environ.get("SMOE_LIBRARY") or os.path.join(_HERE, "libsmoe.so")
 
 SMOE_OK, SMOE_EINVAL, SMOE_EUNSUPPORTED, SMOE_EWORKSPACE, SMOE_EHIP = 0, -1, -2, -3, -4
 SMOE_F32, SMOE_BF16 = 0, 1

@@ -344,28 +344,30 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
                     inv, part);
   }
   if (!do_tail) return;
-  // last block: every other block's logits are visible after its release and our acquire
+  // The last block to finish reads every block's logits.  Each wave releases
+  // its own stores at device (agent) scope before the block counts itself in
+  // with an acquire-release ticket; the last block acquires at the same scope
+  // before it reads.  The XCDs' L2 caches are not coherent with each other,
+  // so a release by one thread would not cover the stores of another wave.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
     const uint32_t n = gridDim.x * gridDim.y;
-    const uint32_t t = atomicAdd(ticket, 1u);
+    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     is_last = (t == n - 1);
-    if (is_last) {
-      __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __threadfence();
-    }
+    // the next launch is ordered after this one by the kernel boundary
+    if (is_last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   route_tail(a, true, a.n_union != nullptr, &us);
 }
 
 // Top-k with the logits given, one token per wave over a grid, and then (do_union)
-// the union by the last block to finish.  The top-k indices are stored and,
-// in the last block, loaded with agent-scope accesses, which are coherent
-// across the XCDs' L2s; the last block is found with an integer ticket
-// (status[2]) that it resets for the next call.
+// the union by the last block to finish, found with an integer ticket
+// (status[2]) that it resets for the next call; the indices reach it through
+// device-scope release (every wave) and acquire (the last block).
 __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_union,
                                                            uint32_t* ticket) {
   __shared__ UnionSmem us;
@@ -386,26 +388,28 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_
     wave_topk(v, E, K, my_v, my_e, &us.topk[wave]);
     const float w = topk_weight(v, E, K, a.norm != 0, my_v);
     if (lane < K) {
-      __hip_atomic_store(&a.topk_idx[t * K + lane], my_e, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      a.topk_idx[t * K + lane] = my_e;
       a.topk_w[t * K + lane] = w;
     }
   }
   if (!do_union) return;
-  __builtin_amdgcn_s_waitcnt(0);                   // this wave's stores are complete
+  // the last block to finish builds the union from every token's indices:
+  // each wave releases its stores at device scope, the block counts itself
+  // in with an acquire-release ticket, the last block acquires before reading
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t n = gridDim.x;
-    const uint32_t tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED,
+    const uint32_t tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL,
                                                __HIP_MEMORY_SCOPE_AGENT);
     is_last = (tk == n - 1);
     if (is_last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const int P = a.B * K;
-  for (int p = threadIdx.x; p < P; p += blockDim.x)
-    us.idx[p] = __hip_atomic_load(&a.topk_idx[p], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int p = threadIdx.x; p < P; p += blockDim.x) us.idx[p] = a.topk_idx[p];
   __syncthreads();
   build_union(a, &us);
 }

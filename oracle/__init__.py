@@ -26,7 +26,8 @@ class QMat(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        path = os.path.join(_HERE, "liboracle.so")
+        # ORACLE_LIBRARY may name the sanitizer build (build_sanitized.py)
+        path = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
         L = ctypes.CDLL(path)

@@ -11,7 +11,7 @@ HEADER = os.path.join(ROOT, "include", "smoe.h")
 
 
 def _lib_path():
-    return os.path.join(ROOT, "exact_routing_bit_amd", "libsmoe.so")
+    return os.environ.get("SMOE_LIBRARY") or os.path.join(ROOT, "exact_routing_bit_amd", "libsmoe.so")
 
 
 @pytest.fixture(scope="module")
