@@ -696,7 +696,7 @@ def stack_harness(smoe, n_layers, prompt, steps):
 # copy of COPY_BYTES.  The summary records a hash of the kernel's sources;
 # once they change, the figure is stale and `traffic` is reported as null.
 COPY_BYTES = 1 << 30
-ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64, true, false>"
+ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64, 1, true, false>"
 ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/ffn_mfma.hip",
                     "exact_routing_bit_amd/csrc/router.hip", "exact_routing_bit_amd/csrc/device.hpp",
                     "exact_routing_bit_amd/csrc/smoe_internal.hpp"]

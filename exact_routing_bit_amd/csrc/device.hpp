@@ -20,6 +20,9 @@ __device__ __forceinline__ uint4 ld_stream4(const uint32_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+__device__ __forceinline__ uint32_t ld_stream1(const uint32_t* p) {
+  return __builtin_nontemporal_load(p);
+}
 __device__ __forceinline__ uint2 ld_stream2(const uint32_t* p) {
   const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   return make_uint2(v.x, v.y);

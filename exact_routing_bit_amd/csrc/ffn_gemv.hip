@@ -23,16 +23,17 @@
 // A shared expert ("Data Flow": the shared expert FFN beside the routed ones)
 // rides along as more items of the same launches: gate_up items past the
 // routed ones cover its rows (every token a pair), and down items past the
-// union slots cover its rows in equal chunks of up to 2048 inputs (a lane's
-// four words of each chunk), whose partial sums the combine adds up first:
-// out = residual + (shared_out + routed_out).
+// routed ones cover its rows in chunks, whose partial sums the combine adds
+// up first: out = residual + (shared_out + routed_out).
 //
-// Lane layouts.  gate_up: a row's d/64 groups (64 inputs each) over TPR =
-// d/64 lanes (32 or 64), one group a lane, 64/TPR rows per wave instruction.
-// down: lane L owns words 4L .. 4L+3 (32 inputs) of every row and the
-// matching slice of h, so that a lane reads its h once per item and uses it
-// for all 8 rows; the row sums then come from one transpose-reduce over the
-// wave.
+// Lane layouts.  gate_up: a row's d/64 groups (64 inputs each) over TPR = 32
+// or 64 lanes, one or two groups a lane (lanes past the row's end idle), so
+// any d that is a multiple of 64 up to 8192.  down: lane L owns NW = 1, 2 or
+// 4 consecutive words of every row (of a chunk of at most 64 NW words) and
+// the matching slice of h, so that a lane reads its h once per item and uses
+// it for all 8 rows; the row sums then come from one transpose-reduce over
+// the wave.  Rows longer than 256 words split into equal chunks (one item
+// each), whose partial sums the combine adds in chunk order.
 #include <algorithm>
 
 #include "device.hpp"
@@ -43,8 +44,11 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kJ = 2;                 // gate_up item: j0, j0+1
-constexpr int kGuRows = 2 * kJ;       // gate rows then up rows
+// gate_up item: kJ consecutive j, gate rows then up rows; two j at one
+// 64-input group per lane, one j at two groups per lane (d > 4096), so that
+// an item is 8 KB of weights at d = 4096 and at d = 8192 alike
+template <int GPL>
+constexpr int kItemJ = 2 / GPL;
 constexpr int kDnRows = 8;            // down: output rows per block item
 constexpr int kMaxDecPairs = 16;      // B * K <= 16 on this path
 // gate_up: one 4-wave block per compute unit, i.e. one streaming wave per SIMD:
@@ -56,8 +60,7 @@ constexpr int kGuMaxItems = 64;       // gate_up: items per wave (h staged in LD
 constexpr int kDnBlocksPerCU = 2;     // down: two blocks per CU (one row block each at d = 4096)
 constexpr int kDnThreads = 512;       // down: 8 waves a block, one item each at d = 4096
 constexpr int kDnWaves = kDnThreads / 64;
-constexpr int kDnMaxF = 2048;         // down: f/32 <= 64 lanes of 4 words a row
-constexpr int kMaxShChunks = 8192 / kDnMaxF;   // shared expert down chunks (fs <= 8192)
+constexpr int kMaxDecF = 8192;        // f and fs on this path
 
 // Prepped position (half index within the row) of column c.
 __device__ __forceinline__ int prepped_pos(int c) {
@@ -111,32 +114,39 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 
 // ------------------------------------------------------------ gate_up items
 // One item: union slot u, j0 = 2 * (item % (f/2)); rows (gate j0, gate j0+1,
-// up j0, up j0+1).  TPR lanes per row (one group each), 64/TPR rows per step.
-template <int TPR>
+// up j0, up j0+1).  TPR lanes per row, 64/TPR rows per step; lane li of a row
+// takes groups li + TPR gi (gi < GPL) of its 64-input groups.  A (lane, gi)
+// past the row's last group is dead: its loads read nothing (an offset past
+// every buffer) and return zero words, scale and bias, so it adds 0.
+template <int TPR, int GPL>
 struct GuBuf {
-  static constexpr int kSteps = kGuRows / (64 / TPR);
-  uint4 w[kSteps][2];
-  uint32_t s[kSteps], b[kSteps];
+  static constexpr int kSteps = 2 * kItemJ<GPL> / (64 / TPR);
+  uint4 w[kSteps][GPL][2];
+  uint32_t s[kSteps][GPL], b[kSteps][GPL];
 };
 
 // Per-lane byte offsets of a gate_up item's loads, the same for every item:
 // step k covers rows rs = k kRps + slot (gate j0 + rs, or up j0 + rs - kJ).
-template <int TPR>
+template <int TPR, int GPL>
 struct GuLane {
-  uint32_t w[GuBuf<TPR>::kSteps];   // packed words, first 16 bytes
-  uint32_t s[GuBuf<TPR>::kSteps];   // scale and bias (bf16)
+  uint32_t w[GuBuf<TPR, GPL>::kSteps][GPL];   // packed words, first 16 bytes
+  uint32_t s[GuBuf<TPR, GPL>::kSteps][GPL];   // scale and bias (bf16)
 };
-template <int TPR>
-__device__ __forceinline__ GuLane<TPR> gu_lane(const FfnArgs& a, int lane) {
-  constexpr int kRps = 64 / TPR;
+template <int TPR, int GPL>
+__device__ __forceinline__ GuLane<TPR, GPL> gu_lane(const FfnArgs& a, int lane) {
+  constexpr int kRps = 64 / TPR, kJ = kItemJ<GPL>;
   const int G = a.d / 64, C = a.d / 8;
   const int li = lane % TPR, slot = lane / TPR;
-  GuLane<TPR> o;
+  GuLane<TPR, GPL> o;
 #pragma unroll
-  for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
+  for (int k = 0; k < GuBuf<TPR, GPL>::kSteps; ++k) {
     const int r = (k * kRps + slot) % kJ;           // row within the item's kJ
-    o.w[k] = (uint32_t)(r * C + li * 8) * 4;
-    o.s[k] = (uint32_t)(r * G + li) * 2;
+#pragma unroll
+    for (int gi = 0; gi < GPL; ++gi) {
+      const int grp = li + TPR * gi;
+      o.w[k][gi] = grp < G ? (uint32_t)(r * C + grp * 8) * 4 : kBufferDead;
+      o.s[k][gi] = grp < G ? (uint32_t)(r * G + grp) * 2 : kBufferDead;
+    }
   }
   return o;
 }
@@ -175,10 +185,10 @@ __device__ __forceinline__ QPtr expert_mat_nb(const QMat& m, const QMat& shared,
 // shared expert's rows, j0 = 2 (item - nR).  kShared: the layer has a shared
 // expert (a separate instance: the extra pointers would otherwise crowd the
 // scalar registers of the routed-only loop).
-template <int TPR, bool kShared>
+template <int TPR, int GPL, bool kShared>
 __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int item, int n_items,
-                                        int nR, const GuLane<TPR>& lo, GuBuf<TPR>& buf) {
-  constexpr int kRps = 64 / TPR;
+                                        int nR, const GuLane<TPR, GPL>& lo, GuBuf<TPR, GPL>& buf) {
+  constexpr int kRps = 64 / TPR, kJ = kItemJ<GPL>;
   const int per = a.f / kJ;
   const bool live = item < n_items;
   const int itc = live ? item : n_items - 1;
@@ -203,12 +213,15 @@ __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int i
   const auto us = buffer_rsrc(up.s + sr, sbytes);
   const auto ub = buffer_rsrc(up.b + sr, sbytes);
 #pragma unroll
-  for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
+  for (int k = 0; k < GuBuf<TPR, GPL>::kSteps; ++k) {
     const bool is_up = k * kRps >= kJ;             // rows k kRps ..: gate rows, then up rows
-    buf.w[k][0] = buf_load4_nt(is_up ? uw : gw, lo.w[k]);
-    buf.w[k][1] = buf_load4_nt(is_up ? uw : gw, lo.w[k] + 16);
-    buf.s[k] = buf_load_u16_nt(is_up ? us : gs, lo.s[k]);
-    buf.b[k] = buf_load_u16_nt(is_up ? ub : gb, lo.s[k]);
+#pragma unroll
+    for (int gi = 0; gi < GPL; ++gi) {
+      buf.w[k][gi][0] = buf_load4_nt(is_up ? uw : gw, lo.w[k][gi]);
+      buf.w[k][gi][1] = buf_load4_nt(is_up ? uw : gw, lo.w[k][gi] + 16);
+      buf.s[k][gi] = buf_load_u16_nt(is_up ? us : gs, lo.s[k][gi]);
+      buf.b[k][gi] = buf_load_u16_nt(is_up ? ub : gb, lo.s[k][gi]);
+    }
   }
   // keep every load of the item here: left to itself the scheduler sinks the
   // scale/bias loads to their first use, after the next item's loads, which
@@ -220,12 +233,14 @@ __device__ __forceinline__ void gu_load(const FfnArgs& a, int lane_expert, int i
 // the wave's LDS row st: st[jj * NTOK + q] = h of row j0 + jj for the union
 // expert's q-th pair (q < its pair count).  xr/xs: the lane's group of the
 // prepped activations of token t (t < NTOK).
-template <int NTOK, int TPR, bool kShared>
+template <int NTOK, int TPR, int GPL, bool kShared>
 __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, int item, int nR,
-                                           int lane, const GuBuf<TPR>& buf,
-                                           const uint4 (&xr)[NTOK][8], const float2 (&xs)[NTOK],
+                                           int lane, const GuBuf<TPR, GPL>& buf,
+                                           const uint4 (&xr)[NTOK][GPL * 8],
+                                           const float2 (&xs)[NTOK][GPL],
                                            const float (&xa)[NTOK], uint16_t* st) {
-  constexpr int kRps = 64 / TPR;
+  constexpr int kRps = 64 / TPR, kJ = kItemJ<GPL>;
+  static_assert(kRps == 1 || kRps == kJ, "a step holds gate rows only or up rows only");
   const int per = a.f / kJ;
   const bool sh = kShared && item >= nR;          // a shared-expert item: pair q = token q
   const int u = sh ? 0 : uniform(item / per);
@@ -234,15 +249,18 @@ __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, i
   const int ne = sh ? a.B : uniform(m.offsets[u + 1]) - pb;   // 1 .. NTOK
   const int li = lane % TPR, slot = lane / TPR;
   // r[k][t]: row (k*kRps + slot) against token t
-  float r[GuBuf<TPR>::kSteps][NTOK];
+  float r[GuBuf<TPR, GPL>::kSteps][NTOK];
 #pragma unroll
-  for (int k = 0; k < GuBuf<TPR>::kSteps; ++k) {
-    const float sc[1] = {bf16_to_f32((uint16_t)buf.s[k])};
-    const float bi[1] = {bf16_to_f32((uint16_t)buf.b[k])};
-    const uint4 wk[1][2] = {{buf.w[k][0], buf.w[k][1]}};
+  for (int k = 0; k < GuBuf<TPR, GPL>::kSteps; ++k) {
+    float sc[GPL], bi[GPL];
+#pragma unroll
+    for (int gi = 0; gi < GPL; ++gi) {
+      sc[gi] = bf16_to_f32((uint16_t)buf.s[k][gi]);
+      bi[gi] = bf16_to_f32((uint16_t)buf.b[k][gi]);
+    }
 #pragma unroll
     for (int t = 0; t < NTOK; ++t)
-      r[k][t] = segment_sum(lane_row_dot<1>(wk, sc, bi, xr[t], &xs[t]), TPR);
+      r[k][t] = segment_sum(lane_row_dot<GPL>(buf.w[k], sc, bi, xr[t], xs[t]), TPR);
   }
   // gate row j0 + jj sits in step jj / kRps at slot jj % kRps, its up row in
   // step (kJ + jj) / kRps at the same slot (kRps is 1 or 2 = kJ)
@@ -270,34 +288,55 @@ __device__ __forceinline__ void gu_compute(const FfnArgs& a, const DecMeta& m, i
 }
 
 // ------------------------------------------------------------- down items
-// Lane layout of the down kernel: lane L < NL = f/32 owns words 4L .. 4L+3 of
-// every row (32 inputs, half of group L/2) and the matching four chunks of h,
-// read once per item and kept in registers for all kDnRows rows of the item.
-// Lanes from NL on repeat lane NL-1's addresses with zero scale and bias.
-template <int NTOK>
+// Lane layout of the down kernel: a row, or a chunk of it, of at most 64 NW
+// words spreads over the wave, lane L owning words NW L .. NW L + NW - 1
+// (8 NW inputs, inside group NW L / 8) and the matching NW chunks of h, read
+// once per item and kept in registers for all kDnRows rows of the item.  NW
+// is the smallest of 1, 2, 4 whose 64 NW words hold a routed row (f <= 2048);
+// past that, NW = 4 and the rows split into chunks.  Lanes past a chunk's
+// last word repeat the last live lane's addresses with zero scale and bias.
+template <int NTOK, int NW>
 struct DnItem {
-  uint4 w[kDnRows];
+  uint32_t w[kDnRows][NW];
   uint32_t s[kDnRows], b[kDnRows];
-  uint4 h[NTOK][4];
+  uint4 h[NTOK][NW];
 };
 
-// Issue the loads of item (slot u, rows r0 .. r0+7): h of the slot's pairs
-// first (the compute needs it first), then the rows' words, scales and
-// biases.  Slots u < nU are the union's experts; slot nU + c is chunk c of
-// the shared expert (words c*chw .. of its rows, which are fs/8 words long;
-// pair q = token q).  Lane L < NL owns words 4L .. 4L+3 of the row (of the chunk);
-// lanes from NL on repeat lane NL-1's addresses with zero scale and bias.
+// How the down rows split into chunks: routed rows (f/8 words) into nr
+// chunks of wr words, the shared expert's (fs/8 words) into ns chunks of ws
+// words; equal widths in whole groups (multiples of 8 words), the last chunk
+// shorter when the width does not divide, each at most 64 NW words.
+struct DnChunks {
+  int nr, wr, ns, ws;
+};
+__host__ __device__ inline void dn_split(int words, int nw, int& n, int& w) {
+  n = (words + 64 * nw - 1) / (64 * nw);
+  w = n == 0 ? 0 : ((words + n - 1) / n + 7) / 8 * 8;
+}
+constexpr int kMaxRtChunks = 4;       // routed rows: f <= 8192 at 256 words a chunk
+constexpr int kMaxShChunks = 16;      // shared rows: fs <= 8192 at 64 words a chunk
+constexpr int kShRow0 = kMaxDecPairs * kMaxRtChunks;   // first shared ylds row
+
+// Issue the loads of item `item` of a row block (rows r0 .. r0+7): items
+// below nU nr are routed, slot item / nr, chunk item % nr; the rest are the
+// shared expert's chunks (pair q = token q).  h of the slot's pairs first
+// (the compute needs it first), then the rows' words, scales and biases.
 // No branch: dead pair slots repeat the last live pair.  Returns in ne the
-// slot's pair count and in ys[q] the ylds row of its q-th pair.
-template <int NTOK, bool kShared>
-__device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, int u, int nU, int chw,
-                                          int r0, int lane, const float (&ib)[2], DnItem<NTOK>& it,
-                                          int& ne, int (&ys)[NTOK], float (&ysc)[NTOK]) {
-  const bool sh = kShared && u >= nU;
-  const int c = u - nU;
+// slot's pair count, in ys[q] the ylds row of its q-th pair (pair p, chunk
+// c: row p kMaxRtChunks + c; shared chunk c, token t: kShRow0 + 2 c + t) and
+// in ysc[q] 1/a_t^2 of that pair's token.
+template <int NTOK, int NW, bool kShared>
+__device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, int item, int nU,
+                                          const DnChunks& g, int r0, int lane,
+                                          const float (&ib)[2], DnItem<NTOK, NW>& it, int& ne,
+                                          int (&ys)[NTOK], float (&ysc)[NTOK]) {
+  const int nRI = nU * g.nr;
+  const bool sh = kShared && item >= nRI;
+  const int u = sh ? 0 : uniform(item / g.nr);
+  const int c = sh ? item - nRI : item - u * g.nr;
   const int Cr = sh ? a.fs / 8 : a.f / 8, Gr = Cr / 8;    // words and groups of a row
-  const int cw = sh ? c * chw : 0;                       // the chunk's first word
-  const int NL = (sh ? min(chw, Cr - cw) : Cr) / 4;
+  const int cw = c * (sh ? g.ws : g.wr);                 // the chunk's first word
+  const int NL = min(sh ? g.ws : g.wr, Cr - cw) / NW;
   const bool lane_live = lane < NL;
   const int L = lane_live ? lane : NL - 1;
   // an empty union (every routed id invalid) has no routed items; an invalid
@@ -312,16 +351,29 @@ __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, in
   for (int q = 0; q < NTOK; ++q) {
     const int qq = max(min(q, ne - 1), 0);
     const int p = sh ? qq : uniform(m.pairs[pb + qq]);
-    ys[q] = sh ? kMaxDecPairs + 2 * c + qq : p;
-    ysc[q] = (sh ? qq : p / a.K) == 0 ? ib[0] : ib[1];   // 1/a_t^2 of the pair's token
+    ys[q] = sh ? kShRow0 + 2 * c + qq : p * kMaxRtChunks + c;
+    // 1/a_t^2 of the pair's token (one token: always ib[0], which also keeps
+    // the pick from becoming an indexed private array)
+    ysc[q] = (NTOK == 1 || (sh ? qq : p / a.K) == 0) ? ib[0] : ib[1];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) it.h[q][k] = hsrc[(int64_t)p * Cr + cw + L * 4 + k];
+    for (int k = 0; k < NW; ++k) it.h[q][k] = hsrc[(int64_t)p * Cr + cw + L * NW + k];
   }
   const QPtr dn = expert_mat(a.down, a.sdown, sh, e);
-  const uint32_t* wr = dn.w + (int64_t)r0 * Cr + cw + L * 4;
+  const uint32_t* wr = dn.w + (int64_t)r0 * Cr + cw + L * NW;
 #pragma unroll
-  for (int r = 0; r < kDnRows; ++r) it.w[r] = ld_stream4(wr + (int64_t)r * Cr);
-  const int64_t sb = (int64_t)r0 * Gr + cw / 8 + (L >> 1);
+  for (int r = 0; r < kDnRows; ++r) {
+    const uint32_t* src = wr + (int64_t)r * Cr;
+    if constexpr (NW == 4) {
+      const uint4 v = ld_stream4(src);
+      it.w[r][0] = v.x, it.w[r][1] = v.y, it.w[r][2] = v.z, it.w[r][3] = v.w;
+    } else if constexpr (NW == 2) {
+      const uint2 v = ld_stream2(src);
+      it.w[r][0] = v.x, it.w[r][1] = v.y;
+    } else {
+      it.w[r][0] = ld_stream1(src);
+    }
+  }
+  const int64_t sb = (int64_t)r0 * Gr + cw / 8 + (L * NW) / 8;
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
     const uint32_t sv = ld_stream_u16(dn.s + sb + (int64_t)r * Gr);
@@ -376,9 +428,9 @@ __device__ __forceinline__ float rows8_wave_sum(const float (&v)[8]) {
 
 // One item: the group sums of its pairs' h slices, the eight row dots, the
 // wave sums, and the rows' outputs into ylds[ys[q]][row] (live pairs only).
-template <int NTOK>
+template <int NTOK, int NW>
 __device__ __forceinline__ void down_compute(int ne, const int (&ys)[NTOK], const float (&ysc)[NTOK],
-                                             int lane, const DnItem<NTOK>& it, float* ylds) {
+                                             int lane, const DnItem<NTOK, NW>& it, float* ylds) {
   float sc[kDnRows], bi[kDnRows];
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
@@ -394,7 +446,7 @@ __device__ __forceinline__ void down_compute(int ne, const int (&ys)[NTOK], cons
     // true values (the bias term)
     float S = 0.f, X = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NW; ++k) {
       const uint32_t hw[4] = {it.h[q][k].x, it.h[q][k].y, it.h[q][k].z, it.h[q][k].w};
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
@@ -408,10 +460,8 @@ __device__ __forceinline__ void down_compute(int ne, const int (&ys)[NTOK], cons
 #pragma unroll
     for (int r = 0; r < kDnRows; ++r) {
       float acc = 0.f;
-      acc = dot_word(it.w[r].x, it.h[q][0], acc);
-      acc = dot_word(it.w[r].y, it.h[q][1], acc);
-      acc = dot_word(it.w[r].z, it.h[q][2], acc);
-      acc = dot_word(it.w[r].w, it.h[q][3], acc);
+#pragma unroll
+      for (int k = 0; k < NW; ++k) acc = dot_word(it.w[r][k], it.h[q][k], acc);
       part[r] = sc[r] * (acc - S1024) + bi[r] * X;
     }
     // h held a_t^2 h: 1/a_t^2 (exact) gives the row outputs
@@ -572,8 +622,9 @@ __device__ __forceinline__ void route_rank(int K, int* slot_pair, RouteKeep& kee
 // w takes items w, w + W, w + 2W, ...; the next item's loads go out before
 // the current one is computed, so each wave streams its share with one item
 // in flight while it computes.
-template <int NTOK, int TPR, bool kRoute, bool kShared>
+template <int NTOK, int TPR, int GPL, bool kRoute, bool kShared>
 __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeRoute r) {
+  constexpr int kJ = kItemJ<GPL>;
   __shared__ DecMeta m;
   __shared__ TopkScratch tks[2];
   const int wave = uniform(threadIdx.x >> 6);
@@ -596,16 +647,21 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   // this lane's group of every token's prepped activations, loaded first:
   // they are few and cached, and the weight loads queue behind them
   const int G = a.d / 64, li = lane % TPR;
-  uint4 xr[NTOK][8];
-  float2 xs[NTOK];
+  uint4 xr[NTOK][GPL * 8];
+  float2 xs[NTOK][GPL];
   float xa[NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) {
     const int tt = min(t, a.B - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(a.xp + (int64_t)tt * a.d) + li * 8;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) xr[t][q] = src[q];
-    xs[t] = a.xs[(int64_t)tt * G + li];
+    for (int gi = 0; gi < GPL; ++gi) {
+      // a dead group (past the row) reads the last one: finite, weighted by 0
+      const int grp = min(li + TPR * gi, G - 1);
+      const uint4* src = reinterpret_cast<const uint4*>(a.xp + (int64_t)tt * a.d) + grp * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xr[t][gi * 8 + q] = src[q];
+      xs[t][gi] = a.xs[(int64_t)tt * G + grp];
+    }
     xa[t] = a.xa[tt];
   }
   // a ring of kGuDepth items: item i computes while the next kGuDepth - 1
@@ -618,20 +674,20 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   // waits for it (and so for every load before it) before reusing its data
   // registers.  The grid gives every wave at most kGuMaxItems items.
   __shared__ uint16_t hst[kDecWaves][kGuMaxItems][kJ * NTOK];
-  const GuLane<TPR> lo = gu_lane<TPR>(a, lane);
-  GuBuf<TPR> b[kGuDepth];
+  const GuLane<TPR, GPL> lo = gu_lane<TPR, GPL>(a, lane);
+  GuBuf<TPR, GPL> b[kGuDepth];
 #pragma unroll
   for (int s = 0; s < kGuDepth - 1; ++s)
-    gu_load<TPR, kShared>(a, lane_expert, wid + s * W, n_items, nR, lo, b[s]);
+    gu_load<TPR, GPL, kShared>(a, lane_expert, wid + s * W, n_items, nR, lo, b[s]);
   for (int i = wid, loc = 0;; i += kGuDepth * W) {
 #pragma unroll
     for (int s = 0; s < kGuDepth; ++s, ++loc) {
       const int it = i + s * W;
       if (it >= n_items) goto flush;
-      gu_load<TPR, kShared>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, nR, lo,
-                   b[(s + kGuDepth - 1) % kGuDepth]);
+      gu_load<TPR, GPL, kShared>(a, lane_expert, it + (kGuDepth - 1) * W, n_items, nR, lo,
+                                 b[(s + kGuDepth - 1) % kGuDepth]);
       if (kLateRank && loc == 0) route_rank(a.K, slot_pair[wave], keep, tks);
-      gu_compute<NTOK, TPR, kShared>(a, m, it, nR, lane, b[s], xr, xs, xa, hst[wave][loc]);
+      gu_compute<NTOK, TPR, GPL, kShared>(a, m, it, nR, lane, b[s], xr, xs, xa, hst[wave][loc]);
     }
   }
 flush:
@@ -696,10 +752,10 @@ flush:
 // block b takes row blocks b, b + grid, ... of 8 output rows x all union
 // experts, one (union slot, row block) item per wave, and ends each row block
 // with the weighted combine of its rows in rank order.
-template <int NTOK, bool kShared>
+template <int NTOK, int NW, bool kShared>
 __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   __shared__ DecMeta m;
-  __shared__ float ylds[(kMaxDecPairs + 2 * kMaxShChunks) * kDnRows];
+  __shared__ float ylds[(kShRow0 + 2 * kMaxShChunks) * kDnRows];
   const int wave = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   // the first row block's residual, fetched before anything waits
@@ -714,11 +770,13 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
     load_meta(a, m);
   }
   const int nU = uniform(m.n_union);
-  // the shared expert's rows in nCh chunks of equal width (chw words, whole
-  // groups, the last one shorter when fs does not divide), each at most 2048
-  // inputs and one item, so that its items weigh about as much as each other
-  const int nCh = kShared ? (a.fs + kDnMaxF - 1) / kDnMaxF : 0;
-  const int chw = kShared ? ((a.fs / 8 + nCh - 1) / nCh + 7) / 8 * 8 : 0;
+  // the rows' chunks (one item each), so that items weigh about as much as
+  // each other
+  DnChunks g;
+  dn_split(a.f / 8, NW, g.nr, g.wr);
+  g.ns = 0, g.ws = 0;
+  if (kShared) dn_split(a.fs / 8, NW, g.ns, g.ws);
+  const int n_items = nU * g.nr + g.ns;
   const int n_rb = a.d / kDnRows;
   const int K = a.K;
   // 1/a_t^2 of the (at most two) tokens
@@ -730,17 +788,18 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   }
   for (int rb = blockIdx.x; rb < n_rb; rb += gridDim.x) {
     const int r0 = rb * kDnRows;
-    for (int u = wave; u < nU + nCh; u += kDnWaves) {
-      DnItem<NTOK> it;
+    for (int u = wave; u < n_items; u += kDnWaves) {
+      DnItem<NTOK, NW> it;
       int ne, ys[NTOK];
       float ysc[NTOK];
-      down_load<NTOK, kShared>(a, m, u, nU, chw, r0, lane, ib, it, ne, ys, ysc);
-      down_compute<NTOK>(ne, ys, ysc, lane, it, ylds);
+      down_load<NTOK, NW, kShared>(a, m, u, nU, g, r0, lane, ib, it, ne, ys, ysc);
+      down_compute<NTOK, NW>(ne, ys, ysc, lane, it, ylds);
     }
     __syncthreads();
     // combine: out[t, r] = residual[t, r] + sum_k w[t, k] * y[t*K + k, r], k
-    // ascending (with a shared expert: residual + (shared + that sum)); a
-    // batch of eight pairs' values is read before it is summed
+    // ascending, each y the sum of its chunks in order (with a shared expert:
+    // residual + (shared + that sum)); a batch of eight pairs' values is read
+    // before it is summed
     if (threadIdx.x < a.B * kDnRows) {
       const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
       float acc = 0.f;
@@ -752,7 +811,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
           const int p = t * K + min(k0 + j, K - 1);
           pv[j] = m.pos[p];
           wv[j] = m.w[p];
-          yv[j] = ylds[p * kDnRows + rr];
+          const float* yp = ylds + p * kMaxRtChunks * kDnRows + rr;
+          yv[j] = yp[0];
+          for (int c = 1; c < g.nr; ++c) yv[j] += yp[c * kDnRows];
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -761,7 +822,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
       if (kShared) {
         // shared_out (its chunks in order) + routed_out
         float shv = 0.f;
-        for (int c = 0; c < nCh; ++c) shv += ylds[(kMaxDecPairs + 2 * c + t) * kDnRows + rr];
+        for (int c = 0; c < g.ns; ++c) shv += ylds[(kShRow0 + 2 * c + t) * kDnRows + rr];
         acc = shv + acc;
       }
       const int64_t o = (int64_t)t * a.d + r0 + rr;
@@ -773,9 +834,10 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
 }
 
 
-template <int NTOK, int TPR, bool kRoute>
+template <int NTOK, int TPR, int GPL, bool kRoute>
 hipError_t launch_gate_up_gemv(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
                                const LaunchTiming* t) {
+  constexpr int kJ = kItemJ<GPL>;
   const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
   const int items = max_union * (a.f / kJ) + a.fs / kJ;
   const int ncu = cu_count();
@@ -786,34 +848,49 @@ hipError_t launch_gate_up_gemv(const FfnArgs& a, const DecodeRoute& r, hipStream
   const int grid = std::max(std::min((items + kDecWaves - 1) / kDecWaves, ncu * kGuBlocksPerCU),
                             (items + per_block - 1) / per_block);
   if (a.fs > 0)
-    SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, kRoute, true>), dim3(grid), dim3(kDecThreads), 0, s,
-                a, r);
+    SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, GPL, kRoute, true>), dim3(grid), dim3(kDecThreads),
+                0, s, a, r);
   else
-    SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, kRoute, false>), dim3(grid), dim3(kDecThreads), 0, s,
-                a, r);
+    SMOE_LAUNCH(t, (k_gate_up_gemv<NTOK, TPR, GPL, kRoute, false>), dim3(grid), dim3(kDecThreads),
+                0, s, a, r);
   return hipGetLastError();
 }
 
+// Lanes per row and groups per lane for a row of d inputs (G = d/64 groups):
+// 32 lanes up to 32 groups, 64 lanes up to 64, then two groups a lane.
+template <int NTOK, bool kRoute>
+hipError_t launch_gate_up_ntok(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
+                               const LaunchTiming* t) {
+  const int G = a.d / 64;
+  if (G <= 32) return launch_gate_up_gemv<NTOK, 32, 1, kRoute>(a, r, s, t);
+  if (G <= 64) return launch_gate_up_gemv<NTOK, 64, 1, kRoute>(a, r, s, t);
+  return launch_gate_up_gemv<NTOK, 64, 2, kRoute>(a, r, s, t);
+}
 template <bool kRoute>
 hipError_t launch_gate_up_any(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,
                               const LaunchTiming* t) {
-  if (a.B == 1)
-    return a.d == 4096 ? launch_gate_up_gemv<1, 64, kRoute>(a, r, s, t)
-                       : launch_gate_up_gemv<1, 32, kRoute>(a, r, s, t);
-  return a.d == 4096 ? launch_gate_up_gemv<2, 64, kRoute>(a, r, s, t)
-                     : launch_gate_up_gemv<2, 32, kRoute>(a, r, s, t);
+  return a.B == 1 ? launch_gate_up_ntok<1, kRoute>(a, r, s, t)
+                  : launch_gate_up_ntok<2, kRoute>(a, r, s, t);
 }
 
-template <int NTOK>
-hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+// Words per lane: the fewest (1, 2, 4) whose 64-lane span holds a routed row.
+template <int NTOK, int NW>
+hipError_t launch_down_nw(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
   const int ncu = cu_count();
   if (ncu <= 0) return hipErrorInvalidDevice;
   const int grid = std::min(a.d / kDnRows, ncu * kDnBlocksPerCU);
   if (a.fs > 0)
-    SMOE_LAUNCH(t, (k_down_combine_gemv<NTOK, true>), dim3(grid), dim3(kDnThreads), 0, s, a);
+    SMOE_LAUNCH(t, (k_down_combine_gemv<NTOK, NW, true>), dim3(grid), dim3(kDnThreads), 0, s, a);
   else
-    SMOE_LAUNCH(t, (k_down_combine_gemv<NTOK, false>), dim3(grid), dim3(kDnThreads), 0, s, a);
+    SMOE_LAUNCH(t, (k_down_combine_gemv<NTOK, NW, false>), dim3(grid), dim3(kDnThreads), 0, s, a);
   return hipGetLastError();
+}
+template <int NTOK>
+hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming* t) {
+  const int words = a.f / 8;
+  if (words <= 64) return launch_down_nw<NTOK, 1>(a, s, t);
+  if (words <= 128) return launch_down_nw<NTOK, 2>(a, s, t);
+  return launch_down_nw<NTOK, 4>(a, s, t);
 }
 
 }  // namespace
@@ -833,13 +910,15 @@ int cu_count() {
   return cached[dev];
 }
 
-// The decode path applies to B <= 2 tokens (B*K <= 16) with d = 2048 or 4096
-// (one gate_up group per lane, 32 or 64 lanes a row) and f <= 2048 (a down
-// row's words spread over at most 64 lanes, four a lane).
+// The decode path applies to B <= 2 tokens (B*K <= 16), d a multiple of 64
+// up to 8192 (a gate_up row over 32 or 64 lanes, one or two groups a lane),
+// f and fs multiples of 64 up to 8192 (down rows in at most 4 routed and 16
+// shared chunks).
 bool gemv_path_ok(const FfnArgs& a) {
   if (a.B < 1 || a.B > 2 || a.B * a.K > kMaxDecPairs) return false;
-  if (a.d != 2048 && a.d != 4096) return false;
-  return a.f % 64 == 0 && a.f <= kDnMaxF && a.f % kJ == 0 && a.d % kDnRows == 0;
+  if (a.d < 64 || a.d > 8192 || a.d % 64 != 0) return false;
+  if (a.fs < 0 || a.fs > kMaxDecF || a.fs % 64 != 0) return false;
+  return a.f >= 64 && a.f <= kMaxDecF && a.f % 64 == 0;
 }
 
 hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {

@@ -242,7 +242,9 @@ size_t smoe_noalloc_scratch_bytes(void);
  * microseconds.  Enqueuing
  * SMOE_STAGE_ROUTE, _GATE_UP, _DOWN and _COMBINE in this order on one stream
  * launches exactly the kernels of one smoe_moe_layer call, in the same order.
- * For decode batches (B <= 2 on the matrix-vector path) the ROUTE stage only
+ * For decode batches (B <= 2 with B * top_k <= 16: the matrix-vector path,
+ * at every d_model, ffn_dim and shared_ffn_dim the descriptor allows) the
+ * ROUTE stage only
  * computes the logits; the ranking, weights, union and activation prep run
  * at the start of the GATE_UP stage's kernel, and COMBINE is part of DOWN.
  * SMOE_EINVAL when only one event is given. */

@@ -203,18 +203,32 @@ FWD_CASES = [
     (small_config("hot", 1024, 8, 4, 256, 64), 64, True),            # up to 4 token tiles
     (small_config("fused", 512, 32, 8, 128, 64, fused=True), 64, False),
     (small_config("wide", 2048, 16, 2, 128, 3, bf16=False), 3, True),
-    (small_config("mfma_b2", 1024, 32, 8, 1536, 2), 2, True),           # B=2 off the decode path
+    (small_config("mfma_b2", 1024, 32, 12, 1536, 2), 2, True),          # B*K > 16: off the decode path
     (small_config("dec_b2", 2048, 32, 8, 1536, 2), 2, True),            # decode kernel, 32 lanes/row
     (small_config("dec_b2_f512", 4096, 64, 8, 512, 2), 2, False),       # 1 down group per lane
     (small_config("dec_b1_f192", 2048, 16, 4, 192, 1), 1, True),        # 3 groups, 1 lane per row
     (small_config("dec_b2_e8", 2048, 8, 8, 512, 2), 2, False),          # every expert, E < B*K
     (small_config("gemv_b1", 4096, 64, 8, 1536, 1), 1, False),
     (small_config("gemv_k16", 2048, 64, 16, 512, 1), 1, True),
-    # the decode down kernel gives lane L words 4L..4L+3 of a row: f/32 lanes
-    (small_config("dec_b1_f2048", 2048, 16, 4, 2048, 1), 1, True),     # all 64 lanes
-    (small_config("dec_b2_f1024", 4096, 32, 8, 1024, 2), 2, False),    # 32 lanes
-    (small_config("dec_b1_f64", 2048, 8, 2, 64, 1), 1, True),          # 2 lanes, one group
-    (small_config("b1_f2560", 2048, 16, 4, 2560, 1), 1, True),         # past 64 lanes: MFMA path
+    # the decode down kernel gives lane L words NW L .. NW L + NW - 1 of a row
+    # (NW = 1, 2, 4: the fewest whose 64 lanes hold f/8 words), longer rows in
+    # equal chunks of at most 256 words
+    (small_config("dec_b1_f2048", 2048, 16, 4, 2048, 1), 1, True),     # NW 4, all 64 lanes
+    (small_config("dec_b2_f1024", 4096, 32, 8, 1024, 2), 2, False),    # NW 2, all 64 lanes
+    (small_config("dec_b1_f64", 2048, 8, 2, 64, 1), 1, True),          # NW 1, 8 lanes, one group
+    (small_config("dec_b2_f320", 640, 8, 2, 320, 2), 2, True),         # NW 1, 40 lanes; d = 10 groups
+    (small_config("dec_b1_f768", 3072, 16, 4, 768, 1), 1, False),      # NW 2, 48 lanes; 48 of 64 row lanes
+    (small_config("b1_f2560", 2048, 16, 4, 2560, 1), 1, True),         # 2 chunks of 160 words
+    (small_config("dec_b1_f2624", 2048, 16, 4, 2624, 1), 1, False),    # 2 chunks: 168 + 160 words
+    (small_config("dec_b2_f3072", 2048, 16, 4, 3072, 2), 2, True),     # 2 chunks of 192 words
+    (small_config("dec_b1_f8192", 1024, 8, 2, 8192, 1), 1, True),      # 4 chunks of 256 words
+    # the decode gate_up kernel: 32 lanes a row up to 32 groups, 64 up to 64,
+    # then two groups a lane (one j an item); lanes past the row idle
+    (small_config("dec_d512", 512, 16, 4, 256, 1), 1, True),           # 8 of 32 lanes
+    (small_config("dec_d1536", 1536, 32, 8, 1024, 2), 2, False),       # 24 of 32 lanes
+    (small_config("dec_d6144", 6144, 16, 8, 1536, 1), 1, True),        # 96 groups: 2 a lane, 32 idle
+    (small_config("dec_d8192_b2", 8192, 8, 4, 512, 2), 2, True),       # 128 groups: 2 a lane
+    (small_config("dec_d8192_b1", 8192, 8, 8, 2048, 1), 1, False),
     # with a shared expert
     (small_config("s_fwd_dec2", 2048, 32, 8, 512, 2, shared=2560), 2, True),
     (small_config("s_fwd_odd", 512, 24, 6, 192, 13, shared=320), 13, True),   # 5 groups
@@ -241,7 +255,7 @@ def test_forward_parity_injected_routing(smoe, cfg, B, with_res):
 
 
 # Layers with a shared expert: decode kernels (B <= 2; its down rows in one to
-# four chunks of up to 2048 inputs, the last one partial) and prefill MFMA
+# sixteen chunks of up to 64 NW words, the last one partial) and prefill MFMA
 # kernels (its own grid row; wider and narrower than the routed experts, the
 # register and the LDS scale/bias variants), fused and split layouts.
 SHARED_CASES = [
@@ -249,6 +263,8 @@ SHARED_CASES = [
     (small_config("s_dec2_fused", 2048, 64, 8, 512, 2, fused=True, shared=1024), 2),
     (small_config("s_dec1_fs8192", 2048, 16, 4, 256, 1, shared=8192), 1),
     (small_config("s_dec1_d1024", 1024, 16, 4, 128, 1, shared=192), 1),
+    (small_config("s_dec1_d8192", 8192, 8, 4, 1024, 1, shared=8192), 1),    # NW 2: 8 chunks
+    (small_config("s_dec2_d2560", 2560, 16, 4, 512, 2, shared=4608), 2),    # NW 1: 9 chunks
     (small_config("s_pref64", 1024, 64, 8, 256, 64, shared=512), 64),
     (small_config("s_pref37_narrow", 1024, 32, 4, 512, 37, fused=True, shared=256), 37),
     (small_config("s_pref5_fs6144", 1024, 16, 2, 128, 5, shared=6144), 5),
@@ -294,8 +310,8 @@ def test_layer_parity(smoe, cfg, B):
     assert np.array_equal(down(un.pair_pos)[:B * cfg.top_k], pp)
 
 
-@pytest.mark.parametrize("cfg,B", [SHARED_CASES[0], SHARED_CASES[1], SHARED_CASES[4],
-                                   SHARED_CASES[6]], ids=lambda v: getattr(v, "name", str(v)))
+@pytest.mark.parametrize("cfg,B", [SHARED_CASES[0], SHARED_CASES[1], SHARED_CASES[6],
+                                   SHARED_CASES[8]], ids=lambda v: getattr(v, "name", str(v)))
 def test_shared_zero_weights_leave_the_routed_layer(smoe, cfg, B):
     """A shared expert whose weights are all zero changes no bit of the
     layer: residual + (0 + routed_out) = residual + routed_out."""
