@@ -175,6 +175,7 @@ SMOE_API int smoe_route(const smoe_layer_desc* desc, const void* router_w, const
   a.K = desc->top_k;
   a.norm = desc->norm_topk_prob;
   a.logits = logits ? logits : ws_at<float>(ws, lay.logits);
+  a.lgp = ws_at<float>(ws, lay.lgp);
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.status = ws_at<uint32_t>(ws, lay.status);
@@ -212,6 +213,7 @@ SMOE_API int smoe_route_ranked(const smoe_layer_desc* desc, const void* router_w
   a.K = desc->top_k;
   a.norm = desc->norm_topk_prob;
   a.logits = logits ? logits : ws_at<float>(ws, lay.logits);
+  a.lgp = ws_at<float>(ws, lay.lgp);
   a.topk_idx = topk_idx;
   a.topk_w = topk_w;
   a.status = ws_at<uint32_t>(ws, lay.status);
@@ -303,6 +305,7 @@ int layer_setup(const smoe_layer_desc* desc, const void* router_w, const smoe_ex
   r->K = desc->top_k;
   r->norm = desc->norm_topk_prob;
   r->logits = logits ? logits : ws_at<float>(ws, lay.logits);
+  r->lgp = ws_at<float>(ws, lay.lgp);
   r->topk_idx = topk_idx;
   r->topk_w = topk_w;
   r->status = ws_at<uint32_t>(ws, lay.status);

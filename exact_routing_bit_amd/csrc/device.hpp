@@ -209,6 +209,48 @@ __device__ __forceinline__ float segment_sum(float v, int width) {
   return (__lane_id() < 32) ? lo : hi;
 }
 
+// v_permlane32_swap / v_permlane16_swap through inline assembly: with the
+// compiler's builtins, the second register of the swapped pair was dropped
+// (both sums read the first).  The s_nop pairs cover the VALU-write ->
+// permlane-read and permlane-write -> VALU-read hazards, which the compiler
+// does not see through an asm statement.
+__device__ __forceinline__ void permlane32_swap(float& x, float& y) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+__device__ __forceinline__ void permlane16_swap(float& x, float& y) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(x), "+v"(y));
+}
+
+// Sum over the wave of eight per-lane row partials v[0..7]: afterwards every
+// lane of 8L' .. 8L'+7 holds the total of row L' (= lane / 8).  Bit 5 of the
+// lane is folded by permlane32 swaps (lanes 32-63 of the first register
+// trade places with lanes 0-31 of the second, so lanes 0-31 keep rows 0-3 and
+// lanes 32-63 rows 4-7), bit 4 by permlane16 swaps (odd 16-lane rows of the
+// first with even rows of the second), bit 3 by a DPP exchange, and bits 0-2
+// by DPP adds: about 20 VALU operations for eight rows.
+__device__ __forceinline__ float rows8_wave_sum(const float (&v)[8]) {
+  float a4[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float x = v[j], y = v[j + 4];
+    permlane32_swap(x, y);
+    a4[j] = x + y;                                 // row j + 4 bit5
+  }
+  float c2[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    float x = a4[j], y = a4[j + 2];
+    permlane16_swap(x, y);
+    c2[j] = x + y;                                 // row j + 2 bit4 + 4 bit5
+  }
+  // lane bit 3 picks which of the two it keeps; the partner lane^8 sends the other
+  const bool b3 = (__lane_id() & 8) != 0;
+  const float keep = b3 ? c2[1] : c2[0];
+  const float send = b3 ? c2[0] : c2[1];
+  const float t = keep + dpp<kDppRowRor8>(send);
+  return segment_sum16(t, 8);
+}
+
 // Root-mean-square normalisation of one row of d floats (d % 4 == 0, d <=
 // 8192): inv = 1 / sqrt(mean(row^2) + eps), formed by a block of 256 threads
 // in one fixed order: thread i adds the squares of float4s i, i + 256, ...

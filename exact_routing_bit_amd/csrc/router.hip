@@ -1,16 +1,19 @@
 // router.hip - exact routing and the layer-major inversion on the device.
 //
-// One launch does the whole routing step ("Data Flow", serial step "EXACT
+// One launch (B <= 2) or two do the whole routing step ("Data Flow", serial step "EXACT
 // ROUTING: gate matvec on heavy_normed -> ranked top-k", "norm_topk_prob
 // weights"; "Layer-Major Batched Prefill", "The Inversion"):
-//   1. every block computes logits[t,e] = sum_i Wr[e,i] x[t,i] (fp32) for a
-//      tile of experts x tokens, and converts a share of x into the prepped
-//      fp16 activation layout the expert kernels read;
-//   2. the last block to finish (an integer ticket; grids stay <= 64 blocks so
-//      the tickets do not queue up) ranks every token's experts by (logit
-//      descending, index ascending), forms the softmax / norm_topk_prob
-//      weights, and builds the union of the batch's experts with the sorted
-//      per-expert pair lists, all from LDS.
+//   1. blocks compute logits[t,e] = sum_i Wr[e,i] x[t,i] (fp32) for a tile
+//      of experts x tokens (B <= 2: one expert and both tokens a wave; B >= 3:
+//      4 tokens x 16 experts x 1024 inputs a block, x staged in LDS), and
+//      further blocks convert x into the prepped fp16 activation layout the
+//      expert kernels read;
+//   2. the last blocks to finish (integer tickets) rank every token's experts
+//      by (logit descending, index ascending), form the softmax /
+//      norm_topk_prob weights, and build the union of the batch's experts with
+//      the sorted per-expert pair lists, all from LDS.  B <= 2 grids finish in
+//      one last block; B >= 3 grids hand their K-slice partial sums to a
+//      top-k grid (a token a wave), whose last block builds the union.
 // No host synchronisation; downstream grids read n_union on the device.
 #include <float.h>
 #include <limits.h>
@@ -364,11 +367,116 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
   route_tail(a, true, a.n_union != nullptr, &us);
 }
 
-// Top-k with the logits given, one token per wave over a grid, and then (do_union)
-// the union by the last block to finish, found with an integer ticket
-// (status[2]) that it resets for the next call; the indices reach it through
-// device-scope release (every wave) and acquire (the last block).
-__global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_union,
+// ------------------------------------------------ tiled logits (B >= 3)
+// The logits of a batch are a small matrix product, logits = x Wr^T, of
+// [B, d] fp32 by [E, d]; a grid that gave every wave one expert and two
+// tokens would read x from the caches once per expert.  Here a block owns a
+// tile of kTileTok tokens x kTileExp experts x kTileK inputs: the tokens'
+// slice of x is staged once in LDS and used by all 16 experts (each wave
+// streams four gate rows), and the K slices' partial sums go to a workspace
+// buffer, which k_topk_grid adds up in slice order.  No tickets here: a
+// device-scope release costs an L2 writeback, and hundreds of them (one per
+// block) cost far more than the kernel boundary that publishes the partials.
+constexpr int kTileTok = 4;
+constexpr int kTileExp = 16;                    // four experts a wave
+constexpr int kTileK = 1024;
+constexpr int kMaxSlices = 8;                   // d <= 8192
+static_assert(kMaxSlices * kTileK >= 8192, "K slices of the widest d");
+static_assert(kTileExp / 4 * kTileTok == 16, "two eight-row transpose-reduces per wave");
+
+// Gate values of expert e at inputs k0 + 256 m + 4 l .. + 3 (lane l, m < 4),
+// zeros past d or for e >= E.
+template <bool kBf16>
+__device__ __forceinline__ void gate_slice(const RouteArgs& a, int e, int k0, float4 (&w)[4]) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int i = k0 + 256 * m + 4 * lane;
+    const bool ok = e < a.E && i < a.d;
+    const int64_t at = ok ? (int64_t)e * a.d + i : 0;
+    if (kBf16) {
+      const uint2 raw = *reinterpret_cast<const uint2*>((const uint16_t*)a.router_w + at);
+      w[m] = ok ? make_float4(__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                              __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u))
+                : make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      const float4 v = *reinterpret_cast<const float4*>((const float*)a.router_w + at);
+      w[m] = ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+}
+
+// grid: (ceil(E/16) * ceil(d/1024) logit blocks + prep blocks, ceil(B/4) tile
+// rows).  Logit block (eb, ks) of tile row ty: experts 16 eb .., inputs
+// 1024 ks .., tokens 4 ty ..; partial sums to lgp[ks][t][e].
+template <bool kBf16>
+__global__ __launch_bounds__(kRouteThreads) void k_route_tiled(RouteArgs a) {
+  __shared__ float xt[kTileTok][kTileK];
+  __shared__ float part[kRouteThreads / 64];
+  const int n_ks = (a.d + kTileK - 1) / kTileK;
+  const int n_logit = ((a.E + kTileExp - 1) / kTileExp) * n_ks;
+  const int t0 = blockIdx.y * kTileTok;
+  if ((int)blockIdx.x >= n_logit) {
+    // activation prep, two tokens a block, in tile row 0
+    if (a.xp != nullptr && blockIdx.y == 0) {
+      const float inv[kTokensPerWave] = {1.f, 1.f};
+      prep_two_tokens(a.x, a.B, a.d, blockIdx.x - n_logit, a.xp, a.xs, a.xa, nullptr, inv,
+                      part);
+    }
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = __lane_id();
+  const int ew = (blockIdx.x / n_ks) * kTileExp + 4 * wave, ks = blockIdx.x % n_ks;
+  const int k0 = ks * kTileK;
+  // the wave's four gate rows first: they come from HBM, x from the caches
+  float4 w[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) gate_slice<kBf16>(a, ew + j, k0, w[j]);
+  // x[t0 .., k0 ..] -> LDS, zeros past the batch or past d
+#pragma unroll
+  for (int j = 0; j < kTileTok * kTileK / 4 / kRouteThreads; ++j) {
+    const int f4 = j * kRouteThreads + threadIdx.x;          // float4 index in the tile
+    const int t = f4 / (kTileK / 4), c = (f4 % (kTileK / 4)) * 4;
+    const bool ok = t0 + t < a.B && k0 + c < a.d;
+    const float4 v = ok ? *reinterpret_cast<const float4*>(a.x + (int64_t)(t0 + t) * a.d + k0 + c)
+                        : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&xt[t][c]) = v;
+  }
+  __syncthreads();
+  // acc[h][4 j + t]: expert ew + 2 h + j, token t0 + t
+  float acc[2][8] = {};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int t = 0; t < kTileTok; ++t) {
+      const float4 xv = *reinterpret_cast<const float4*>(&xt[t][256 * m + 4 * lane]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j / 2][4 * (j % 2) + t] += w[j][m].x * xv.x + w[j][m].y * xv.y + w[j][m].z * xv.z +
+                                       w[j][m].w * xv.w;
+    }
+  }
+  // two transpose-reduces: lanes 8 r .. 8 r + 7 get the totals of row r of each
+  const float s0 = rows8_wave_sum(acc[0]);
+  const float s1 = rows8_wave_sum(acc[1]);
+  const int r = lane >> 3, t = r % kTileTok, jj = r / kTileTok;
+  if ((lane & 7) == 0 && t0 + t < a.B) {
+    float* dst = a.lgp + ((int64_t)ks * a.B + t0 + t) * a.E;
+    if (ew + jj < a.E) dst[ew + jj] = s0;
+    if (ew + 2 + jj < a.E) dst[ew + 2 + jj] = s1;
+  }
+}
+
+// Top-k, one token per wave over a grid, and then (do_union) the union by
+// the last block to finish, found with an integer ticket (status[2]) that it
+// resets for the next call.  n_ks > 0: the logits are first formed from
+// k_route_tiled's K-slice partials (added in slice order) and written out;
+// else they are read as given.  The indices reach the last block through
+// the memory model at device scope: the block's barrier orders its waves'
+// stores before thread 0's acquire-release ticket increment (release is
+// cumulative), and the last block acquires before it reads.
+__global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int n_ks, int do_union,
                                                            uint32_t* ticket) {
   __shared__ UnionSmem us;
   __shared__ int is_last;
@@ -378,10 +486,29 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_
   const int E = a.E, K = a.K;
   if (t < a.B) {
     float v[4];
+    if (n_ks > 0) {
+      float p[4][kMaxSlices];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = e < E ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+#pragma unroll
+        for (int ks = 0; ks < kMaxSlices; ++ks)
+          p[j][ks] = (e < E && ks < n_ks) ? a.lgp[((int64_t)ks * a.B + t) * E + e] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        float sum = p[j][0];
+        for (int ks = 1; ks < n_ks; ++ks) sum += p[j][ks];
+        v[j] = e < E ? sum : -FLT_MAX;
+        if (e < E) a.logits[(int64_t)t * E + e] = sum;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = lane + 64 * j;
+        v[j] = e < E ? a.logits[(int64_t)t * E + e] : -FLT_MAX;
+      }
     }
     float my_v;
     int my_e;
@@ -393,16 +520,13 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_
     }
   }
   if (!do_union) return;
-  // the last block to finish builds the union from every token's indices:
-  // each wave releases its stores at device scope, the block counts itself
-  // in with an acquire-release ticket, the last block acquires before reading
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (threadIdx.x == 0) {
     const uint32_t n = gridDim.x;
     const uint32_t tk = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL,
                                                __HIP_MEMORY_SCOPE_AGENT);
     is_last = (tk == n - 1);
+    // the next launch is ordered after this one by the kernel boundary
     if (is_last) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
@@ -412,6 +536,17 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int do_
   for (int p = threadIdx.x; p < P; p += blockDim.x) us.idx[p] = a.topk_idx[p];
   __syncthreads();
   build_union(a, &us);
+}
+
+// Logits only from k_route_tiled's partials (no top-k): one token per wave.
+__global__ __launch_bounds__(kTopkThreads) void k_sum_slices(RouteArgs a, int n_ks) {
+  const int t = blockIdx.x * (kTopkThreads / 64) + (int)(threadIdx.x >> 6);
+  if (t >= a.B) return;
+  for (int e = threadIdx.x & 63; e < a.E; e += 64) {
+    float sum = a.lgp[(int64_t)t * a.E + e];
+    for (int ks = 1; ks < n_ks; ++ks) sum += a.lgp[((int64_t)ks * a.B + t) * a.E + e];
+    a.logits[(int64_t)t * a.E + e] = sum;
+  }
 }
 
 // Ranked routing ("Data Flow", the routing step: ranked top-(8+spec), the
@@ -476,6 +611,27 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
   RouteArgs r = a;
   if (!do_union) r.n_union = nullptr;
   bool tail_done = false;
+  if (!logits_in && a.B > kTokensPerWave && a.norm_out == nullptr) {
+    // tiles of 4 tokens x 16 experts x 1024 inputs (+ activation prep), then
+    // the slices' sums with the top-k and union (or the sums alone)
+    const int prep_blocks = a.xp != nullptr ? (a.B + 1) / 2 : 0;   // two tokens a block
+    const int n_ks = (a.d + kTileK - 1) / kTileK;
+    const int n_logit = ((a.E + kTileExp - 1) / kTileExp) * n_ks;
+    const dim3 grid(n_logit + prep_blocks, (a.B + kTileTok - 1) / kTileTok);
+    if (a.router_bf16)
+      SMOE_LAUNCH(t, k_route_tiled<true>, grid, dim3(kRouteThreads), 0, s, r);
+    else
+      SMOE_LAUNCH(t, k_route_tiled<false>, grid, dim3(kRouteThreads), 0, s, r);
+    const int blocks = (a.B + kTopkThreads / 64 - 1) / (kTopkThreads / 64);
+    if (do_topk)
+      hipLaunchKernelGGL(k_topk_grid, dim3(blocks), dim3(kTopkThreads), 0, s, r, n_ks,
+                         (int)do_union, a.status + 2);
+    else
+      hipLaunchKernelGGL(k_sum_slices, dim3(blocks), dim3(kTopkThreads), 0, s, r, n_ks);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess || do_topk || !do_union) return err;
+    logits_in = true;                               // only a stand-alone union is left
+  }
   if (!logits_in) {
     // logits (+ activation prep); small grids finish top-k/union in their last block
     const int prep_blocks = a.xp != nullptr ? (a.B + 1) / 2 : 0;   // two tokens a block
@@ -492,7 +648,7 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
   }
   if (!tail_done && do_topk) {
     const int blocks = (a.B + kTopkThreads / 64 - 1) / (kTopkThreads / 64);
-    hipLaunchKernelGGL(k_topk_grid, dim3(blocks), dim3(kTopkThreads), 0, s, r, (int)do_union,
+    hipLaunchKernelGGL(k_topk_grid, dim3(blocks), dim3(kTopkThreads), 0, s, r, 0, (int)do_union,
                        a.status + 2);
     return hipGetLastError();
   }
