@@ -45,45 +45,67 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTiles = 4;                          // 16-row tiles per wave (64 rows)
 constexpr int kPairTile = 16;                      // pairs per token tile (MFMA M)
+constexpr int kMaxTiles = kMaxBatch / kPairTile;   // token tiles of the widest pass (64 pairs)
 constexpr int kGps = 2;                            // groups per pipeline stage
-constexpr int kRing = 3;                           // stages resident in LDS
 constexpr int kSuper = 4;                          // stages per scale/bias handout (kFastSB)
+static_assert(kMaxTiles == 4, "a wide pass holds every pair of a 64-token chunk");
 
+// A pass streams one unit of weight rows once and applies it to NT token
+// tiles (16 NT pairs).  An expert with at most 16 pairs takes the narrow
+// pass (NT = 1, a ring of three stages); one with more (at most 64: every
+// token of the chunk) the wide pass (NT = 4, two stages), so that every
+// expert's bytes are read once per layer.
+//
 // One ring slot (one stage).  Layouts, 16-byte entries unless noted:
 //   W  [wave][tile][chunk 4][row 16]    chunk c = group c/2, words 4(c%2)..+3
-//   A  [word 16][pair 16]               prepped activations of one word
-//   XS [group 2][half 2][X|C][pair 16]               f32 (gate_up: half 0 only)
+//   A  [token tile NT][word 16][pair 16]   prepped activations of one word
+//   XS f32, gate_up: [group 2][X|C][token tile NT][pair 16]
+//           down:    [group 2][half 2][token tile NT][X|C][pair 16]
 //   SB [wave][s|b][group 2][col 16][tile 4]          u32, the aligned dword
 //                                        holding that row's bf16 s (or b)
 //                                        (only without kFastSB)
-// kFastSB keeps scales and biases in registers (see the kernel).
+// kFastSB keeps scales and biases in registers (see the pass).
 constexpr int kWBytes = kWaves * kTiles * 1024;
-constexpr int kABytes = 16 * kPairTile * 16;
-constexpr int kXSBytes = kGps * 2 * 2 * kPairTile * 4;
+constexpr int kABytes = 16 * kPairTile * 16;       // per token tile
+constexpr int kXSBytes = kGps * 2 * 2 * kPairTile * 4;   // per token tile
 constexpr int kSBSlotBytes = kWaves * 2 * kGps * 256;
 constexpr int kOffA = kWBytes;
-constexpr int kOffXS = kOffA + kABytes;
-constexpr int kOffSB = kOffXS + kXSBytes;
-constexpr int slot_bytes(bool fast_sb) { return kOffSB + (fast_sb ? 0 : kSBSlotBytes); }
-// copy instructions per wave and stage: words (one per tile), activations,
-// sums, and (without kFastSB) the scale/bias dwords
-
+template <int NT>
+constexpr int off_xs() { return kOffA + NT * kABytes; }
+template <int NT>
+constexpr int off_sb() { return off_xs<NT>() + NT * kXSBytes; }
+template <bool kFastSB, int NT>
+constexpr int slot_bytes() { return off_sb<NT>() + (kFastSB ? 0 : kSBSlotBytes); }
+// the narrow pass (fast scale/bias variant, three stages) and the wide pass
+// (scales and biases through the slots, two stages) share the LDS buffer
 template <bool kFastSB>
-constexpr int copies_of_rest() {
-  return 2 + (kFastSB ? 0 : 2 * kGps);
+constexpr int ring_bytes() {
+  return 3 * slot_bytes<kFastSB, 1>() > 2 * slot_bytes<false, kMaxTiles>()
+             ? 3 * slot_bytes<kFastSB, 1>()
+             : 2 * slot_bytes<false, kMaxTiles>();
 }
-template <bool kFastSB>
+
+// Copy instructions per wave and stage: words (one per tile), activations
+// (one per token tile), sums (gate_up: one; down: one per two token tiles)
+// and, without kFastSB, the scale/bias dwords.
+template <bool kGateUp, bool kFastSB, int NT>
+constexpr int copies_of_rest() {
+  return NT + (kGateUp ? 1 : (NT + 1) / 2) + (kFastSB ? 0 : 2 * kGps);
+}
+template <bool kGateUp, bool kFastSB, int NT>
 constexpr int copies_of_stage() {
-  return kTiles + copies_of_rest<kFastSB>();
+  return kTiles + copies_of_rest<kGateUp, kFastSB, NT>();
 }
 
 // Per-lane copy sources that stay fixed over the K loop.
+template <int NT>
 struct Sources {
   const uint32_t* w[kTiles];   // row (tile T, lane%16), chunk half (lane/16)%2
   const uint16_t* s;           // scales of this lane's copy row (group 0)
   const uint16_t* b;           // biases of the same row
-  const uint4* act;            // activation row of pair lane%16, word 4(wave%2) + lane/16
-  const float* sums;           // group sums of the same pair
+  const uint4* act[NT];        // token tile n: activation row of pair lane%16,
+                               // word 4(wave%2) + lane/16
+  const float* sums[(NT + 1) / 2];   // group sums (see issue_rest)
 };
 
 __device__ __forceinline__ const void* align4(const uint16_t* p) {
@@ -99,9 +121,9 @@ __device__ __forceinline__ const void* align4(const uint16_t* p) {
 // last use: that copy carries the nontemporal hint, so that the streamed
 // weights leave the L2 first and the activations that every workgroup of an
 // expert re-reads stay in it.
-template <bool kGateUp>
-__device__ __forceinline__ void issue_words(const Sources& S, char* slot, int k, int G, int wave,
-                                            int lane, bool line_aligned) {
+template <int NT>
+__device__ __forceinline__ void issue_words(const Sources<NT>& S, char* slot, int k, int G,
+                                            int wave, int lane, bool line_aligned) {
   const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
   // packed words: lanes 0-31 copy group gA, lanes 32-63 group gB
   const int gw = (lane >> 5) ? gB : gA;
@@ -115,22 +137,28 @@ __device__ __forceinline__ void issue_words(const Sources& S, char* slot, int k,
       dma16_to_lds(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
   }
 }
-template <bool kGateUp, bool kFastSB>
-__device__ __forceinline__ void issue_rest(const Sources& S, char* slot, int k, int G, int wave,
-                                           int lane) {
+template <bool kGateUp, bool kFastSB, int NT>
+__device__ __forceinline__ void issue_rest(const Sources<NT>& S, char* slot, int k, int G,
+                                           int wave, int lane) {
   const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
   // activations: waves 0,1 copy the words of group gA, waves 2,3 those of gB
   const int ga = wave < 2 ? gA : gB;
-  dma16_to_lds(S.act + ga * 8, slot + kOffA + wave * 1024);
-  // group sums: wave = 2 * group + (gate_up: X|C, down: half)
+#pragma unroll
+  for (int n = 0; n < NT; ++n)
+    dma16_to_lds(S.act[n] + ga * 8, slot + kOffA + n * kABytes + wave * 1024);
+  // group sums: wave = 2 * group + (gate_up: X|C, down: half); lane L covers
+  // token tile L/16 (gate_up) or, per copy c, tile 2c + L/32 with X|C (L/16)%2
   if (kGateUp) {
-    if (lane < 16) dma4_to_lds(S.sums + ga * 2, slot + kOffXS + wave * 64);
+    if (lane < 16 * NT) dma4_to_lds(S.sums[0] + ga * 2, slot + off_xs<NT>() + wave * NT * 64);
   } else {
-    if (lane < 32) dma4_to_lds(S.sums + ga * 4, slot + kOffXS + wave * 128);
+#pragma unroll
+    for (int c = 0; c < (NT + 1) / 2; ++c)
+      if (lane < 32 * min(2, NT - 2 * c))
+        dma4_to_lds(S.sums[c] + ga * 4, slot + off_xs<NT>() + wave * NT * 128 + c * 256);
   }
   if (!kFastSB) {
     // one dword a lane, the aligned one that holds the value
-    char* sb = slot + kOffSB + wave * (2 * kGps * 256);
+    char* sb = slot + off_sb<NT>() + wave * (2 * kGps * 256);
     dma4_to_lds(align4(S.s + gA), sb);
     dma4_to_lds(align4(S.s + gB), sb + 256);
     dma4_to_lds(align4(S.b + gA), sb + 512);
@@ -156,32 +184,19 @@ struct SBRegs {
   uint4 s[kTiles], b[kTiles];
 };
 
-// acc[T] += s (D - C) + b X over the two groups of stage k.
+// acc[T][n] += s (D - C) + b X over the two groups of stage k, token tile n.
 //   kFastSB: scales/biases from `regs` (groups 8j.. of the current four stages,
 //            kk = k % 4 static);
 //   else:    from the slot, with `parity` bit T (scales) and 4 + T (biases) =
 //            the u16 address parity of group 0 of this lane's row in tile T.
-template <bool kGateUp, bool kFastSB, int kk>
+// Each group's words are dequantised once and used for every token tile.
+template <bool kGateUp, bool kFastSB, int NT, int kk>
 __device__ __forceinline__ void compute_stage(const char* slot, int k, int G, int wave, int col,
                                               int lg, const SBRegs& regs, uint32_t parity,
-                                              floatx4 (&acc)[kTiles]) {
+                                              floatx4 (&acc)[kTiles][NT]) {
 #pragma unroll
   for (int gl = 0; gl < kGps; ++gl) {
     const bool live = kFastSB || 2 * k + gl < G;   // uniform; a clamped copy otherwise
-    const half8_t A0 =
-        *reinterpret_cast<const half8_t*>(slot + kOffA + ((gl * 8 + 2 * lg) * 16 + col) * 16);
-    const half8_t A1 =
-        *reinterpret_cast<const half8_t*>(slot + kOffA + ((gl * 8 + 2 * lg + 1) * 16 + col) * 16);
-    floatx4 X, Cs;
-    if (kGateUp) {
-      X = *reinterpret_cast<const floatx4*>(slot + kOffXS + (gl * 2 + 0) * 64 + 16 * lg);
-      Cs = *reinterpret_cast<const floatx4*>(slot + kOffXS + (gl * 2 + 1) * 64 + 16 * lg);
-    } else {
-      const char* xs = slot + kOffXS + gl * 256 + 16 * lg;
-      X = *reinterpret_cast<const floatx4*>(xs) + *reinterpret_cast<const floatx4*>(xs + 128);
-      Cs = *reinterpret_cast<const floatx4*>(xs + 64) + *reinterpret_cast<const floatx4*>(xs + 192);
-    }
-    const floatx4 seed = -Cs;
     uint32_t sw[kTiles], bw[kTiles];
     if (kFastSB) {
 #pragma unroll
@@ -192,7 +207,7 @@ __device__ __forceinline__ void compute_stage(const char* slot, int k, int G, in
         bw[T] = bv[kk];
       }
     } else {
-      const char* sb = slot + kOffSB + wave * (2 * kGps * 256) + gl * 256 + col * 16;
+      const char* sb = slot + off_sb<NT>() + wave * (2 * kGps * 256) + gl * 256 + col * 16;
       const uint4 s4 = *reinterpret_cast<const uint4*>(sb);
       const uint4 b4 = *reinterpret_cast<const uint4*>(sb + 512);
       sw[0] = s4.x; sw[1] = s4.y; sw[2] = s4.z; sw[3] = s4.w;
@@ -200,77 +215,101 @@ __device__ __forceinline__ void compute_stage(const char* slot, int k, int G, in
     }
     const char* wrow =
         slot + (wave * kTiles) * 1024 + ((2 * gl + (lg >> 1)) * 16 + col) * 16 + (lg & 1) * 8;
+    float sc[kTiles], bi[kTiles];
 #pragma unroll
     for (int T = 0; T < kTiles; ++T) {
-      const uint2 w2 = *reinterpret_cast<const uint2*>(wrow + T * 1024);
       const bool shi = kFastSB ? gl == 1 : (((parity >> T) & 1) ^ gl) != 0;
       const bool bhi = kFastSB ? gl == 1 : (((parity >> (4 + T)) & 1) ^ gl) != 0;
-      const float sc = live ? bf16_half(sw[T], shi) : 0.f;
-      const float bi = live ? bf16_half(bw[T], bhi) : 0.f;
-      floatx4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, word_operand(w2.x), seed, 0, 0, 0);
-      D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, word_operand(w2.y), D, 0, 0, 0);
+      sc[T] = live ? bf16_half(sw[T], shi) : 0.f;
+      bi[T] = live ? bf16_half(bw[T], bhi) : 0.f;
+    }
+    // one token tile: each row tile's words dequantised as they are used;
+    // several: dequantised once for all of them
+    half8_t w0[NT == 1 ? 1 : kTiles], w1[NT == 1 ? 1 : kTiles];
+    if (NT > 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[T][i] = __builtin_fmaf(sc, D[i], acc[T][i]);
-        acc[T][i] = __builtin_fmaf(bi, X[i], acc[T][i]);
+      for (int T = 0; T < kTiles; ++T) {
+        const uint2 w2 = *reinterpret_cast<const uint2*>(wrow + T * 1024);
+        w0[NT == 1 ? 0 : T] = word_operand(w2.x);
+        w1[NT == 1 ? 0 : T] = word_operand(w2.y);
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const char* an = slot + kOffA + n * kABytes;
+      const half8_t A0 = *reinterpret_cast<const half8_t*>(an + ((gl * 8 + 2 * lg) * 16 + col) * 16);
+      const half8_t A1 =
+          *reinterpret_cast<const half8_t*>(an + ((gl * 8 + 2 * lg + 1) * 16 + col) * 16);
+      floatx4 X, Cs;
+      if (kGateUp) {
+        const char* xs = slot + off_xs<NT>() + (gl * 2 * NT + n) * 64 + 16 * lg;
+        X = *reinterpret_cast<const floatx4*>(xs);
+        Cs = *reinterpret_cast<const floatx4*>(xs + NT * 64);
+      } else {
+        const char* xs = slot + off_xs<NT>() + (gl * 2 * NT + n) * 128 + 16 * lg;
+        const int hstep = NT * 128;                 // half 0 -> half 1
+        X = *reinterpret_cast<const floatx4*>(xs) + *reinterpret_cast<const floatx4*>(xs + hstep);
+        Cs = *reinterpret_cast<const floatx4*>(xs + 64) +
+             *reinterpret_cast<const floatx4*>(xs + hstep + 64);
+      }
+      const floatx4 seed = -Cs;
+#pragma unroll
+      for (int T = 0; T < kTiles; ++T) {
+        half8_t o0, o1;
+        if (NT == 1) {
+          const uint2 w2 = *reinterpret_cast<const uint2*>(wrow + T * 1024);
+          o0 = word_operand(w2.x);
+          o1 = word_operand(w2.y);
+        } else {
+          o0 = w0[NT == 1 ? 0 : T];
+          o1 = w1[NT == 1 ? 0 : T];
+        }
+        floatx4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, o0, seed, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, o1, D, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[T][n][i] = __builtin_fmaf(sc[T], D[i], acc[T][n][i]);
+          acc[T][n][i] = __builtin_fmaf(bi[T], X[i], acc[T][n][i]);
+        }
       }
     }
   }
 }
 
-template <bool kGateUp, bool kFastSB>
-__global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
-  constexpr int kSlot = slot_bytes(kFastSB);
-  __shared__ __align__(16) char ring[kRing * kSlot];
-  __shared__ int lpair_w[kWaves][kPairTile];       // each wave's copy of the tile's pair ids
-  // The grid is one row of blocks per 16-token tile of the shared expert (if
-  // the layer has one: every token is one of its pairs, pair q = token q),
-  // then one row per union slot, laid out one after another along x: bx is
-  // the block within its row (kWaves units each), tile or u its row.  The
-  // shared rows go first, as their blocks serve the most pairs.
-  const int units_r = kGateUp ? a.f / 32 : a.d / 64;
-  const int units_s = kGateUp ? a.fs / 32 : a.d / 64;
-  const int gx_r = (units_r + kWaves - 1) / kWaves, gx_s = (units_s + kWaves - 1) / kWaves;
-  const int n_sh = a.fs > 0 ? (a.B + kPairTile - 1) / kPairTile : 0;
-  const int b_lin = blockIdx.x;
-  const bool sh = b_lin < n_sh * gx_s;
-  const int b_r = b_lin - n_sh * gx_s;
-  const int u = sh ? -1 : b_r / gx_r;
-  const int tile = sh ? b_lin / gx_s : 0;
-  const int bx = sh ? b_lin - tile * gx_s : b_r - u * gx_r;
-  const int ul = sh ? 0 : u;
-  // the union's size and this slot's expert and offsets in one round trip (slot
-  // u < the largest union is always inside the union arrays)
-  const int nU = *a.n_union;
-  const int e_ld = a.union_experts[ul];
-  const int pb_ld = a.expert_offsets[ul];
-  const int pe_ld = a.expert_offsets[ul + 1];
-  if (!sh && u >= nU) return;
-  const int e = sh ? 0 : e_ld;
-  const int pb = sh ? 0 : pb_ld;
-  const int ne = sh ? a.B : pe_ld - pb;            // >= 1
-  const int F = sh ? a.fs : a.f;                   // the expert's width
-  const int Kt = sh ? 1 : a.K;                     // pair q serves token q / Kt
-  const QMat qg = sh ? a.sgate : a.gate, qu = sh ? a.sup : a.up, qd = sh ? a.sdown : a.down;
-  uint16_t* const hp = sh ? a.shp : a.hp;
-  float2* const hs = sh ? a.shs : a.hs;
-  float* const yout = sh ? a.sy : a.y;
-  const int K = kGateUp ? a.d : F;
+// What a workgroup's pass needs to know about its expert (or the shared one).
+struct PassCtx {
+  bool sh;                 // the shared expert (pair q = token q)
+  int e, pb, ne;           // expert, first pair in pair_list, pair count (>= 1)
+  int F, Kt;               // the expert's width; pair q serves token q / Kt
+  QMat qg, qu, qd;
+  uint16_t* hp;
+  float2* hs;
+  float* yout;
+  int unit;                // this wave's unit of rows
+  bool has_unit;           // false: a copy of the last unit, nothing written
+};
+
+// The whole pass of one wave's unit over the expert's K dimension for its
+// pairs, in passes of 16 NT pairs (one pass when NT = 4), kRingN stages in
+// the ring.
+template <bool kGateUp, bool kFastSB, int NT, int kRingN>
+__device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, char* ring,
+                                         int* lpair) {
+  constexpr int kSlot = slot_bytes<kFastSB, NT>();
+  static_assert(kRingN == 2 || kRingN == 3, "two or three stages in flight");
+  const int K = kGateUp ? a.d : c.F;
   const int G = K / 64, C = K / 8;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, lg = lane >> 4;
-
-  // this wave's unit; waves past the last unit run along on a copy of the
-  // last one (they take part in the shared copies and barriers) and write nothing
-  const int units = sh ? units_s : units_r;
-  const bool has_unit = bx * kWaves + wave < units;
-  const int unit = min(bx * kWaves + wave, units - 1);
+  const int e = c.e, ne = c.ne, F = c.F, Kt = c.Kt;
+  const QMat &qg = c.qg, &qu = c.qu, &qd = c.qd;
   int rows0[kTiles];
 #pragma unroll
-  for (int T = 0; T < kTiles; ++T) rows0[T] = kGateUp ? unit * 32 + (T & 1) * 16 : unit * 64 + T * 16;
+  for (int T = 0; T < kTiles; ++T)
+    rows0[T] = kGateUp ? c.unit * 32 + (T & 1) * 16 : c.unit * 64 + T * 16;
 
-  Sources S;
+  Sources<NT> S;
 #pragma unroll
   for (int T = 0; T < kTiles; ++T) {
     const QMat& m = kGateUp ? (T < 2 ? qg : qu) : qd;   // T is a constant here
@@ -288,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     const uint16_t* sp = up ? qu.s : s0;
     const uint16_t* bp = up ? qu.b : b0;
     const int64_t stride = up ? qu.stride_sb : st0;
-    const int row = (kGateUp ? unit * 32 + (T & 1) * 16 : unit * 64 + T * 16) + r;
+    const int row = (kGateUp ? c.unit * 32 + (T & 1) * 16 : c.unit * 64 + T * 16) + r;
     S.s = sp + e * stride + (int64_t)row * G;
     S.b = bp + e * stride + (int64_t)row * G;
   }
@@ -332,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
     }
     // wait for them here, before any copy is in flight: the compiler does not
     // count the copies (inline assembly), so its wait at their first use
-    // would otherwise be vmcnt(0) behind three stages of copies
+    // would otherwise be vmcnt(0) behind the stages of copies
 #pragma unroll
     for (int T = 0; T < kTiles; ++T)
 #pragma unroll
@@ -342,73 +381,86 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
       }
   }
 
-  // a union slot's pairs in 16-pair tiles; a shared-expert block does one tile
-  const int m_first = sh ? tile * kPairTile : 0;
-  const int m_end = sh ? m_first + 1 : ne;
-  for (int m0 = m_first; m0 < m_end; m0 += kPairTile) {
-    __syncthreads();                               // the previous tile is done with the ring
-    int* lpair = lpair_w[wave];
-    // the tile's pair ids (copied like the rest, so that no compiler-counted
-    // load sits behind the copies), then the first two stages' words, which
-    // need only the expert; the wait covers the ids alone
-    if (lane < kPairTile) {
-      if (sh)
+  for (int m0 = 0; m0 < ne; m0 += kPairTile * NT) {
+    __syncthreads();                               // the previous pass is done with the ring
+    // the pass's pair ids (copied like the rest, so that no compiler-counted
+    // load sits behind the copies; lane L: pair slot L of the 16 NT), then
+    // the first stages' words, which need only the expert; the wait covers
+    // the ids alone
+    if (lane < kPairTile * NT) {
+      if (c.sh)
         lpair[lane] = min(m0 + lane, ne - 1);      // the shared expert's pairs are the tokens
       else
-        dma4_to_lds(a.pair_list + pb + min(m0 + lane, ne - 1), lpair);
+        dma4_to_lds(a.pair_list + c.pb + min(m0 + lane, ne - 1), lpair);
     }
-    issue_words<kGateUp>(S, ring, 0, G, wave, lane, line_aligned);
-    if (nst > 1) {
-      issue_words<kGateUp>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
+    issue_words<NT>(S, ring, 0, G, wave, lane, line_aligned);
+    if (kRingN == 3 && nst > 1) {
+      issue_words<NT>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
       wait_vmcnt<2 * kTiles>();
     } else {
       wait_vmcnt<kTiles>();
     }
-    // the token scale a_t of the pairs this lane's accumulators hold (pair
-    // slots 4 lg + i), used in the epilogue only
-    float tsc[4];
+    // the token scales a_t of the pairs this lane's accumulators hold (pair
+    // slots 16 n + 4 lg + i), used in the epilogue only: one token tile reads
+    // them here, under the first copies; several read them in the epilogue
+    // (held across the K loop, 16 of them cost registers)
+    float tsc1[4];
+    if (NT == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tsc[i] = a.xa[lpair[4 * lg + i] / Kt];
+      for (int i = 0; i < 4; ++i) tsc1[i] = a.xa[lpair[4 * lg + i] / Kt];
+    }
     {
-      const int q = lpair[lane & 15];
       const int word = 4 * (wave & 1) + (lane >> 4);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const int q = lpair[16 * n + (lane & 15)];
+        S.act[n] = kGateUp ? reinterpret_cast<const uint4*>(a.xp + (int64_t)(q / Kt) * a.d) + word
+                           : reinterpret_cast<const uint4*>(c.hp + (int64_t)q * F) + word;
+      }
       if (kGateUp) {
-        const int t = q / Kt;
-        S.act = reinterpret_cast<const uint4*>(a.xp + (int64_t)t * a.d) + word;
-        S.sums = reinterpret_cast<const float*>(a.xs) + (int64_t)t * G * 2 + (wave & 1);
+        // lane L: pair slot L (token tile L/16), X or C by wave & 1
+        const int q = lpair[min(lane, kPairTile * NT - 1)];
+        S.sums[0] = reinterpret_cast<const float*>(a.xs) + (int64_t)(q / Kt) * G * 2 + (wave & 1);
       } else {
-        S.act = reinterpret_cast<const uint4*>(hp + (int64_t)q * F) + word;
-        S.sums = reinterpret_cast<const float*>(hs) + (int64_t)q * G * 4 + (wave & 1) * 2 +
-                 ((lane >> 4) & 1);
+        // copy cc, lane L: pair slot 32 cc + L%16 + 16 (L/32), X|C (L/16)%2,
+        // half wave & 1
+#pragma unroll
+        for (int cc = 0; cc < (NT + 1) / 2; ++cc) {
+          const int slotp = min(32 * cc + 16 * (lane >> 5) + (lane & 15), kPairTile * NT - 1);
+          const int q = lpair[slotp];
+          S.sums[cc] = reinterpret_cast<const float*>(c.hs) + (int64_t)q * G * 4 + (wave & 1) * 2 +
+                       ((lane >> 4) & 1);
+        }
       }
     }
-    floatx4 acc[kTiles];
+    floatx4 acc[kTiles][NT];
 #pragma unroll
-    for (int T = 0; T < kTiles; ++T) acc[T] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int T = 0; T < kTiles; ++T)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[T][n] = floatx4{0.f, 0.f, 0.f, 0.f};
     SBRegs regs;
 
-    issue_rest<kGateUp, kFastSB>(S, ring, 0, G, wave, lane);
-    if (nst > 1) issue_rest<kGateUp, kFastSB>(S, ring + kSlot, 1, G, wave, lane);
+    issue_rest<kGateUp, kFastSB, NT>(S, ring, 0, G, wave, lane);
+    if (kRingN == 3 && nst > 1) issue_rest<kGateUp, kFastSB, NT>(S, ring + kSlot, 1, G, wave, lane);
     // stages in fours so that the stage's place in its four is a constant
     for (int ks = 0; ks < nst; ks += kSuper) {
 #define SMOE_MFMA_STAGE(kk)                                                                       \
       if (ks + kk < nst) {                                                                        \
         const int k = ks + kk;                                                                    \
-        if (k + 1 >= nst)            /* this wave's copies of stage k landed: */                  \
+        if (kRingN == 2 || k + 1 >= nst)  /* this wave's copies of stage k landed: */             \
           wait_vmcnt<0>();                                                                        \
         else if (kk == 0 && ks == 0) /* stage 1's words went out before stage 0's rest */         \
-          wait_vmcnt<copies_of_rest<kFastSB>()>();                                                \
+          wait_vmcnt<copies_of_rest<kGateUp, kFastSB, NT>()>();                                   \
         else                                                                                      \
-          wait_vmcnt<copies_of_stage<kFastSB>()>();                                               \
-        /* this wave's words of stage k+2 go to its own part of slot k-1, which */               \
+          wait_vmcnt<copies_of_stage<kGateUp, kFastSB, NT>()>();                                  \
+        const int kn = k + kRingN - 1;  /* the stage whose copies go out now */                   \
+        /* this wave's words of stage kn go to its own part of slot k-1, which */                \
         /* only it reads (its compute of k-1 is done): no need to wait for the others */         \
-        if (k + 2 < nst)                                                                          \
-          issue_words<kGateUp>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave, lane,         \
-                               line_aligned);                                                     \
+        if (kn < nst)                                                                             \
+          issue_words<NT>(S, ring + (kn % kRingN) * kSlot, kn, G, wave, lane, line_aligned);      \
         barrier_no_wait();           /* every wave's copies of k landed; slot k-1 is free */      \
-        if (k + 2 < nst)                                                                          \
-          issue_rest<kGateUp, kFastSB>(S, ring + ((k + 2) % kRing) * kSlot, k + 2, G, wave,        \
-                                       lane);                                                     \
+        if (kn < nst)                                                                             \
+          issue_rest<kGateUp, kFastSB, NT>(S, ring + (kn % kRingN) * kSlot, kn, G, wave, lane);   \
         if (kFastSB && kk == 0) {                                                                 \
           const int j = k / kSuper;                  /* groups 8j .. 8j+7: piece j */             \
           const int src = (col * 4 + (j & 3)) * 4;   /* lane holding this row's piece j */        \
@@ -417,8 +469,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
             regs.b[T] = bpermute4(src, j < 4 ? sbb[T][0] : sbb[T][1]);                            \
           }                                                                                       \
         }                                                                                         \
-        compute_stage<kGateUp, kFastSB, kk>(ring + (k % kRing) * kSlot, k, G, wave, col, lg,      \
-                                            regs, parity, acc);                                   \
+        compute_stage<kGateUp, kFastSB, NT, kk>(ring + (k % kRingN) * kSlot, k, G, wave, col, lg, \
+                                                regs, parity, acc);                               \
       }
       SMOE_MFMA_STAGE(0)
       SMOE_MFMA_STAGE(1)
@@ -426,58 +478,116 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
       SMOE_MFMA_STAGE(3)
 #undef SMOE_MFMA_STAGE
     }
-    if (!has_unit) continue;
+    if (!c.has_unit) continue;
 
-    // epilogue: lane holds (pair slot m0 + 4 lg + i, row rows0[T] + col)
-    if (kGateUp) {
-      // h for columns j = unit*32 + Th*16 + col, from gate tile Th and up tile Th+2
-      float X[4] = {0.f, 0.f, 0.f, 0.f}, Sm[4] = {0.f, 0.f, 0.f, 0.f};
+    // epilogue: lane holds (pair slot m0 + 16 n + 4 lg + i, row rows0[T] + col)
 #pragma unroll
-      for (int Th = 0; Th < 2; ++Th) {
-        const int j = unit * 32 + Th * 16 + col;
+    for (int n = 0; n < NT; ++n) {
+      float tsc[4];                                  // a_t of the lane's pairs
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tsc[i] = NT == 1 ? tsc1[i] : a.xa[lpair[16 * n + 4 * lg + i] / Kt];
+      if (kGateUp) {
+        // h for columns j = unit*32 + Th*16 + col, from gate tile Th and up tile Th+2
+        float X[4] = {0.f, 0.f, 0.f, 0.f}, Sm[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int Th = 0; Th < 2; ++Th) {
+          const int j = c.unit * 32 + Th * 16 + col;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ms = 16 * n + 4 * lg + i;      // pair slot in the pass
+            // the sums were taken over a_t x: 1/a_t (exact) gives g and u, and
+            // h is stored as a_t^2 h
+            const float at = tsc[i], ia = 1.0f / at;
+            const float h = silu_mul(acc[Th][n][i] * ia, acc[Th + 2][n][i] * ia) * (at * at);
+            const half_t xi = (half_t)h;
+            const half_t stv = (j & 1) ? (half_t)((float)xi * 0.0625f) : xi;
+            const float stf = (float)stv;
+            Sm[i] += stf;
+            X[i] += (j & 1) ? stf * 16.0f : stf;
+            if (m0 + ms < ne) {
+              const int nn = j & 7;
+              c.hp[(int64_t)lpair[ms] * F + (j & ~7) + 2 * (nn & 3) + (nn >> 2)] = f16_bits(stv);
+            }
+          }
+        }
+        // sums over the unit's 32 columns: the 16 lanes of a row segment
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 4 * lg + i;
-          // the sums were taken over a_t x: 1/a_t (exact) gives g and u, and
-          // h is stored as a_t^2 h
-          const float at = tsc[i], ia = 1.0f / at;
-          const float h = silu_mul(acc[Th][i] * ia, acc[Th + 2][i] * ia) * (at * at);
-          const half_t xi = (half_t)h;
-          const half_t stv = (j & 1) ? (half_t)((float)xi * 0.0625f) : xi;
-          const float stf = (float)stv;
-          Sm[i] += stf;
-          X[i] += (j & 1) ? stf * 16.0f : stf;
-          if (m < ne) {
-            const int n = j & 7;
-            hp[(int64_t)lpair[m - m0] * F + (j & ~7) + 2 * (n & 3) + (n >> 2)] = f16_bits(stv);
+          const float Xt = segment_sum16(X[i], 16), St = segment_sum16(Sm[i], 16);
+          const int ms = 16 * n + 4 * lg + i;
+          if (col == 0 && m0 + ms < ne) {
+            const int j0 = c.unit * 32;
+            c.hs[((int64_t)lpair[ms] * (F / 64) + j0 / 64) * 2 + (j0 % 64) / 32] =
+                make_float2(Xt, 1024.0f * St);
+          }
+        }
+      } else {
+        // h held a_t^2 h: 1/a_t^2 (exact) gives the outputs
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ms = 16 * n + 4 * lg + i;
+          const float ib = 1.0f / (tsc[i] * tsc[i]);
+          if (m0 + ms < ne) {
+#pragma unroll
+            for (int T = 0; T < kTiles; ++T)
+              c.yout[(int64_t)lpair[ms] * a.d + rows0[T] + col] = acc[T][n][i] * ib;
           }
         }
       }
-      // sums over the unit's 32 columns: the 16 lanes of a row segment
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float Xt = segment_sum16(X[i], 16), St = segment_sum16(Sm[i], 16);
-        const int m = m0 + 4 * lg + i;
-        if (col == 0 && m < ne) {
-          const int j0 = unit * 32;
-          hs[((int64_t)lpair[m - m0] * (F / 64) + j0 / 64) * 2 + (j0 % 64) / 32] =
-              make_float2(Xt, 1024.0f * St);
-        }
-      }
-    } else {
-      // h held a_t^2 h: 1/a_t^2 (exact) gives the outputs
-      float ib[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ib[i] = 1.0f / (tsc[i] * tsc[i]);
-#pragma unroll
-      for (int T = 0; T < kTiles; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + 4 * lg + i;
-          if (m < ne) yout[(int64_t)lpair[m - m0] * a.d + rows0[T] + col] = acc[T][i] * ib[i];
-        }
     }
   }
+}
+
+template <bool kGateUp, bool kFastSB>
+__global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
+  __shared__ __align__(16) char ring[ring_bytes<kFastSB>()];
+  __shared__ int lpair_w[kWaves][kPairTile * kMaxTiles];   // each wave's copy of the pass's pair ids
+  // The grid is one row of blocks for the shared expert (if the layer has
+  // one: every token is one of its pairs, pair q = token q), then one row per
+  // union slot, laid out one after another along x: bx is the block within
+  // its row (kWaves units each), u its row.  The shared row goes first, as
+  // its blocks serve the most pairs.
+  const int units_r = kGateUp ? a.f / 32 : a.d / 64;
+  const int units_s = kGateUp ? a.fs / 32 : a.d / 64;
+  const int gx_r = (units_r + kWaves - 1) / kWaves, gx_s = (units_s + kWaves - 1) / kWaves;
+  const int n_sh = a.fs > 0 ? 1 : 0;
+  const int b_lin = blockIdx.x;
+  const bool sh = b_lin < n_sh * gx_s;
+  const int b_r = b_lin - n_sh * gx_s;
+  const int u = sh ? -1 : b_r / gx_r;
+  const int bx = sh ? b_lin : b_r - u * gx_r;
+  const int ul = sh ? 0 : u;
+  // the union's size and this slot's expert and offsets in one round trip (slot
+  // u < the largest union is always inside the union arrays)
+  const int nU = *a.n_union;
+  const int e_ld = a.union_experts[ul];
+  const int pb_ld = a.expert_offsets[ul];
+  const int pe_ld = a.expert_offsets[ul + 1];
+  if (!sh && u >= nU) return;
+  PassCtx c;
+  c.sh = sh;
+  c.e = sh ? 0 : e_ld;
+  c.pb = sh ? 0 : pb_ld;
+  c.ne = sh ? a.B : pe_ld - pb_ld;                 // 1 .. B <= 64
+  c.F = sh ? a.fs : a.f;
+  c.Kt = sh ? 1 : a.K;
+  c.qg = sh ? a.sgate : a.gate;
+  c.qu = sh ? a.sup : a.up;
+  c.qd = sh ? a.sdown : a.down;
+  c.hp = sh ? a.shp : a.hp;
+  c.hs = sh ? a.shs : a.hs;
+  c.yout = sh ? a.sy : a.y;
+  // this wave's unit; waves past the last unit run along on a copy of the
+  // last one (they take part in the shared copies and barriers) and write nothing
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int units = sh ? units_s : units_r;
+  c.has_unit = bx * kWaves + wave < units;
+  c.unit = min(bx * kWaves + wave, units - 1);
+  int* lpair = lpair_w[wave];
+  if (__builtin_amdgcn_readfirstlane(c.ne) > kPairTile)
+    ffn_pass<kGateUp, false, kMaxTiles, 2>(a, c, ring, lpair);
+  else
+    ffn_pass<kGateUp, kFastSB, 1, 3>(a, c, ring, lpair);
 }
 
 // 16-byte scale/bias copies need 8 | G, 8 | stride and 16-byte aligned bases
@@ -491,9 +601,9 @@ bool fast_sb_ok(const QMat& m, int G) {
 hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up, const LaunchTiming* t) {
   const int max_union = a.E < a.B * a.K ? a.E : a.B * a.K;
   const bool shared = a.fs > 0;
-  // a row of blocks per 16-token tile of the shared expert, then one per union
-  // slot (see the kernel), along x
-  const int n_sh = shared ? (a.B + kPairTile - 1) / kPairTile : 0;
+  // a row of blocks for the shared expert, then one per union slot (see the
+  // kernel), along x
+  const int n_sh = shared ? 1 : 0;
   const int units_r = gate_up ? a.f / 32 : a.d / 64;
   const int units_s = gate_up ? a.fs / 32 : a.d / 64;
   const int gx_r = (units_r + kWaves - 1) / kWaves, gx_s = (units_s + kWaves - 1) / kWaves;

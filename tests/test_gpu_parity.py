@@ -254,6 +254,54 @@ def test_forward_parity_injected_routing(smoe, cfg, B, with_res):
     assert err <= 1.5e-3, f"precision regression: {err}"
 
 
+# Skewed routing: an expert that serves more than 16 pairs takes the wide
+# pass, all of its pairs (up to the chunk's 64 tokens) against one stream of
+# its weights; the shared expert does too once B > 16.
+SKEW_CASES = [
+    (small_config("skew_all64", 1024, 32, 4, 256, 64), 64, "all"),      # 4 experts x 64 pairs
+    (small_config("skew_hot48_s", 2048, 64, 8, 512, 48, shared=256), 48, "hot"),
+    (small_config("skew_all17_fused", 1024, 16, 2, 192, 17, fused=True), 17, "all"),
+    (small_config("skew_hot64_nof", 512, 40, 6, 320, 64, bf16=False), 64, "hot"),
+]
+
+
+def skewed_routing(cfg, B, mode, seed=7):
+    """Expert ids and weights: "all" routes every token to the same K experts
+    (in a different order per token); "hot" puts expert 5 first for every
+    token and fills the rest at random.  Weights are random and sum to one."""
+    rng = np.random.default_rng(seed)
+    E, K = cfg.num_experts, cfg.top_k
+    idx = np.empty((B, K), np.int32)
+    for t in range(B):
+        if mode == "all":
+            idx[t] = rng.permutation(np.arange(K))
+        else:
+            others = rng.choice(np.setdiff1d(np.arange(E), [5]), K - 1, replace=False)
+            idx[t] = np.concatenate([[5], others])
+    w = rng.random((B, K)).astype(np.float32) + 0.05
+    w /= w.sum(axis=1, keepdims=True)
+    return idx, w.astype(np.float32)
+
+
+@pytest.mark.parametrize("cfg,B,mode", SKEW_CASES, ids=lambda v: getattr(v, "name", str(v)))
+def test_forward_parity_skewed_routing(smoe, cfg, B, mode):
+    L = synth.make_layer(cfg)
+    x = synth.hidden(cfg.seed, 0, 4, B, cfg.d_model)
+    res = synth.hidden(cfg.seed, 0, 5, B, cfg.d_model, tensor=synth.T_RESIDUAL)
+    idx, w = skewed_routing(cfg, B, mode)
+    ref = oracle_layer(L, x, cfg, residual=res, idx=idx, w=w)[0]
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=B, device=dev())
+    smoe.build_union(desc, up(idx), layer.union, layer.ws)
+    counts = np.diff(down(layer.union.expert_offsets)[:int(down(layer.union.n_union)[0]) + 1])
+    assert counts.max() > 16
+    out = torch.empty(B, cfg.d_model, dtype=torch.float32, device=dev())
+    smoe.moe_forward(desc, layer.experts, up(x), up(idx), up(w), layer.union, out, layer.ws,
+                     residual=up(res))
+    err, worst = assert_layer_close(down(out), ref, TOL, residual=res)
+    assert err <= 1.5e-3, f"precision regression: {err}"
+
+
 # Layers with a shared expert: decode kernels (B <= 2; its down rows in one to
 # sixteen chunks of up to 64 NW words, the last one partial) and prefill MFMA
 # kernels (its own grid row; wider and narrower than the routed experts, the
