@@ -141,20 +141,23 @@ template <bool kGateUp, bool kFastSB, int NT>
 __device__ __forceinline__ void issue_rest(const Sources<NT>& S, char* slot, int k, int G,
                                            int wave, int lane) {
   const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
-  // activations: waves 0,1 copy the words of group gA, waves 2,3 those of gB
-  const int ga = wave < 2 ? gA : gB;
+  // activations: waves 0,1 (mod 4) copy the words of group gA, waves 2,3
+  // those of gB (with more than four waves, the others copy the same bytes
+  // again, so that every wave issues the same copies)
+  const int wq = wave & 3;
+  const int ga = wq < 2 ? gA : gB;
 #pragma unroll
   for (int n = 0; n < NT; ++n)
-    dma16_to_lds(S.act[n] + ga * 8, slot + kOffA + n * kABytes + wave * 1024);
-  // group sums: wave = 2 * group + (gate_up: X|C, down: half); lane L covers
+    dma16_to_lds(S.act[n] + ga * 8, slot + kOffA + n * kABytes + wq * 1024);
+  // group sums: wq = 2 * group + (gate_up: X|C, down: half); lane L covers
   // token tile L/16 (gate_up) or, per copy c, tile 2c + L/32 with X|C (L/16)%2
   if (kGateUp) {
-    if (lane < 16 * NT) dma4_to_lds(S.sums[0] + ga * 2, slot + off_xs<NT>() + wave * NT * 64);
+    if (lane < 16 * NT) dma4_to_lds(S.sums[0] + ga * 2, slot + off_xs<NT>() + wq * NT * 64);
   } else {
 #pragma unroll
     for (int c = 0; c < (NT + 1) / 2; ++c)
       if (lane < 32 * min(2, NT - 2 * c))
-        dma4_to_lds(S.sums[c] + ga * 4, slot + off_xs<NT>() + wave * NT * 128 + c * 256);
+        dma4_to_lds(S.sums[c] + ga * 4, slot + off_xs<NT>() + wq * NT * 128 + c * 256);
   }
   if (!kFastSB) {
     // one dword a lane, the aligned one that holds the value
@@ -276,6 +279,24 @@ __device__ __forceinline__ void compute_stage(const char* slot, int k, int G, in
   }
 }
 
+// Waits until every copy of this wave for stage k has landed, allowing (some
+// of) the copies of the stages issued after it to stay in flight.  Issue
+// order: the words of stages 0 .. R-2, then their rest (the prologue), then
+// in stage j's iteration the words and rest of stage j + R - 1.  In the
+// steady state (k >= R-2, and R-2 later stages issued) exactly R-2 full
+// stages follow stage k's copies; before it (R = 3, k = 0) the next stage's
+// rest; at the end nothing.  Three cases only: more branches in the
+// unrolled stage loop made the compiler spill.
+template <int kRest, int kStage, int kRingN>
+__device__ __forceinline__ void wait_stage(int k, int nst) {
+  if (k >= kRingN - 2 && k + kRingN - 2 < nst)
+    wait_vmcnt<(kRingN - 2) * kStage>();
+  else if (k < kRingN - 2 && k + 1 < nst)
+    wait_vmcnt<kRest>();
+  else
+    wait_vmcnt<0>();
+}
+
 // What a workgroup's pass needs to know about its expert (or the shared one).
 struct PassCtx {
   bool sh;                 // the shared expert (pair q = token q)
@@ -296,7 +317,9 @@ template <bool kGateUp, bool kFastSB, int NT, int kRingN>
 __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, char* ring,
                                          int* lpair) {
   constexpr int kSlot = slot_bytes<kFastSB, NT>();
-  static_assert(kRingN == 2 || kRingN == 3, "two or three stages in flight");
+  constexpr int kRest = copies_of_rest<kGateUp, kFastSB, NT>();
+  constexpr int kStage = copies_of_stage<kGateUp, kFastSB, NT>();
+  static_assert(kRingN == 2 || kRingN == 3, "two or three stages in the ring");
   const int K = kGateUp ? a.d : c.F;
   const int G = K / 64, C = K / 8;
   const int lane = threadIdx.x & 63;
@@ -394,12 +417,10 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
         dma4_to_lds(a.pair_list + c.pb + min(m0 + lane, ne - 1), lpair);
     }
     issue_words<NT>(S, ring, 0, G, wave, lane, line_aligned);
-    if (kRingN == 3 && nst > 1) {
-      issue_words<NT>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
-      wait_vmcnt<2 * kTiles>();
-    } else {
-      wait_vmcnt<kTiles>();
-    }
+    if (kRingN >= 3 && nst > 1) issue_words<NT>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
+    // the pair ids landed (the words of the prologue stages behind them)
+    if (kRingN >= 3 && nst > 1) wait_vmcnt<2 * kTiles>();
+    else wait_vmcnt<kTiles>();
     // the token scales a_t of the pairs this lane's accumulators hold (pair
     // slots 16 n + 4 lg + i), used in the epilogue only: one token tile reads
     // them here, under the first copies; several read them in the epilogue
@@ -441,18 +462,13 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
     SBRegs regs;
 
     issue_rest<kGateUp, kFastSB, NT>(S, ring, 0, G, wave, lane);
-    if (kRingN == 3 && nst > 1) issue_rest<kGateUp, kFastSB, NT>(S, ring + kSlot, 1, G, wave, lane);
+    if (kRingN >= 3 && nst > 1) issue_rest<kGateUp, kFastSB, NT>(S, ring + kSlot, 1, G, wave, lane);
     // stages in fours so that the stage's place in its four is a constant
     for (int ks = 0; ks < nst; ks += kSuper) {
 #define SMOE_MFMA_STAGE(kk)                                                                       \
       if (ks + kk < nst) {                                                                        \
         const int k = ks + kk;                                                                    \
-        if (kRingN == 2 || k + 1 >= nst)  /* this wave's copies of stage k landed: */             \
-          wait_vmcnt<0>();                                                                        \
-        else if (kk == 0 && ks == 0) /* stage 1's words went out before stage 0's rest */         \
-          wait_vmcnt<copies_of_rest<kGateUp, kFastSB, NT>()>();                                   \
-        else                                                                                      \
-          wait_vmcnt<copies_of_stage<kGateUp, kFastSB, NT>()>();                                  \
+        wait_stage<kRest, kStage, kRingN>(k, nst);  /* this wave's copies of stage k landed */    \
         const int kn = k + kRingN - 1;  /* the stage whose copies go out now */                   \
         /* this wave's words of stage kn go to its own part of slot k-1, which */                \
         /* only it reads (its compute of k-1 is done): no need to wait for the others */         \
