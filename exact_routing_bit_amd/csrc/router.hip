@@ -371,26 +371,31 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
 // The logits of a batch are a small matrix product, logits = x Wr^T, of
 // [B, d] fp32 by [E, d]; a grid that gave every wave one expert and two
 // tokens would read x from the caches once per expert.  Here a block owns a
-// tile of kTileTok tokens x kTileExp experts x kTileK inputs: the tokens'
-// slice of x is staged once in LDS and used by all 16 experts (each wave
-// streams four gate rows), and the K slices' partial sums go to a workspace
-// buffer, which k_topk_grid adds up in slice order.  No tickets here: a
-// device-scope release costs an L2 writeback, and hundreds of them (one per
-// block) cost far more than the kernel boundary that publishes the partials.
+// tile of kTileTok tokens x kTileExp experts x one K slice of 256 kM inputs:
+// the tokens' slice of x is staged once in LDS and used by all 16 experts
+// (each wave streams four gate rows), and the slices' partial sums go to a
+// workspace buffer, which k_topk_grid adds up in slice order.  The slice is
+// the narrowest of 256, 512, 1024 inputs that cuts d into at most
+// kMaxSlices: short slices make short dependent chains (load, stage, sum)
+// spread over more blocks.  No tickets here: a device-scope release costs
+// an L2 writeback, and hundreds of them (one per block) cost far more than
+// the kernel boundary that publishes the partials.
 constexpr int kTileTok = 4;
 constexpr int kTileExp = 16;                    // four experts a wave
-constexpr int kTileK = 1024;
-constexpr int kMaxSlices = 8;                   // d <= 8192
-static_assert(kMaxSlices * kTileK >= 8192, "K slices of the widest d");
+constexpr int kMaxSlices = 8;
 static_assert(kTileExp / 4 * kTileTok == 16, "two eight-row transpose-reduces per wave");
 
-// Gate values of expert e at inputs k0 + 256 m + 4 l .. + 3 (lane l, m < 4),
+// 4-input pieces a lane takes per slice (slice = 256 kM inputs) for a row of d.
+inline int slice_pieces(int d) { return d <= 8 * 256 ? 1 : d <= 8 * 512 ? 2 : 4; }
+inline int n_slices(int d) { return (d + 256 * slice_pieces(d) - 1) / (256 * slice_pieces(d)); }
+
+// Gate values of expert e at inputs k0 + 256 m + 4 l .. + 3 (lane l, m < kM),
 // zeros past d or for e >= E.
-template <bool kBf16>
-__device__ __forceinline__ void gate_slice(const RouteArgs& a, int e, int k0, float4 (&w)[4]) {
+template <bool kBf16, int kM>
+__device__ __forceinline__ void gate_slice(const RouteArgs& a, int e, int k0, float4 (&w)[kM]) {
   const int lane = __lane_id();
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < kM; ++m) {
     const int i = k0 + 256 * m + 4 * lane;
     const bool ok = e < a.E && i < a.d;
     const int64_t at = ok ? (int64_t)e * a.d + i : 0;
@@ -406,14 +411,15 @@ __device__ __forceinline__ void gate_slice(const RouteArgs& a, int e, int k0, fl
   }
 }
 
-// grid: (ceil(E/16) * ceil(d/1024) logit blocks + prep blocks, ceil(B/4) tile
+// grid: (ceil(E/16) * n_slices logit blocks + prep blocks, ceil(B/4) tile
 // rows).  Logit block (eb, ks) of tile row ty: experts 16 eb .., inputs
-// 1024 ks .., tokens 4 ty ..; partial sums to lgp[ks][t][e].
-template <bool kBf16>
+// 256 kM ks .., tokens 4 ty ..; partial sums to lgp[ks][t][e].
+template <bool kBf16, int kM>
 __global__ __launch_bounds__(kRouteThreads) void k_route_tiled(RouteArgs a) {
-  __shared__ float xt[kTileTok][kTileK];
+  constexpr int kK = 256 * kM;                  // the slice
+  __shared__ float xt[kTileTok][kK];
   __shared__ float part[kRouteThreads / 64];
-  const int n_ks = (a.d + kTileK - 1) / kTileK;
+  const int n_ks = (a.d + kK - 1) / kK;
   const int n_logit = ((a.E + kTileExp - 1) / kTileExp) * n_ks;
   const int t0 = blockIdx.y * kTileTok;
   if ((int)blockIdx.x >= n_logit) {
@@ -428,16 +434,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_tiled(RouteArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
   const int ew = (blockIdx.x / n_ks) * kTileExp + 4 * wave, ks = blockIdx.x % n_ks;
-  const int k0 = ks * kTileK;
+  const int k0 = ks * kK;
   // the wave's four gate rows first: they come from HBM, x from the caches
-  float4 w[4][4];
+  float4 w[4][kM];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) gate_slice<kBf16>(a, ew + j, k0, w[j]);
+  for (int j = 0; j < 4; ++j) gate_slice<kBf16, kM>(a, ew + j, k0, w[j]);
   // x[t0 .., k0 ..] -> LDS, zeros past the batch or past d
 #pragma unroll
-  for (int j = 0; j < kTileTok * kTileK / 4 / kRouteThreads; ++j) {
+  for (int j = 0; j < kTileTok * kK / 4 / kRouteThreads; ++j) {
     const int f4 = j * kRouteThreads + threadIdx.x;          // float4 index in the tile
-    const int t = f4 / (kTileK / 4), c = (f4 % (kTileK / 4)) * 4;
+    const int t = f4 / (kK / 4), c = (f4 % (kK / 4)) * 4;
     const bool ok = t0 + t < a.B && k0 + c < a.d;
     const float4 v = ok ? *reinterpret_cast<const float4*>(a.x + (int64_t)(t0 + t) * a.d + k0 + c)
                         : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -447,7 +453,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_tiled(RouteArgs a) {
   // acc[h][4 j + t]: expert ew + 2 h + j, token t0 + t
   float acc[2][8] = {};
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < kM; ++m) {
 #pragma unroll
     for (int t = 0; t < kTileTok; ++t) {
       const float4 xv = *reinterpret_cast<const float4*>(&xt[t][256 * m + 4 * lane]);
@@ -487,6 +493,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int n_k
   if (t < a.B) {
     float v[4];
     if (n_ks > 0) {
+      // every slice's partials requested at once, then added in slice order
+      // (unrolled and predicated: a loop to n_ks would index the array at
+      // run time, which puts it in scratch memory)
       float p[4][kMaxSlices];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -499,7 +508,9 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_grid(RouteArgs a, int n_k
       for (int j = 0; j < 4; ++j) {
         const int e = lane + 64 * j;
         float sum = p[j][0];
-        for (int ks = 1; ks < n_ks; ++ks) sum += p[j][ks];
+#pragma unroll
+        for (int ks = 1; ks < kMaxSlices; ++ks)
+          if (ks < n_ks) sum += p[j][ks];
         v[j] = e < E ? sum : -FLT_MAX;
         if (e < E) a.logits[(int64_t)t * E + e] = sum;
       }
@@ -612,16 +623,24 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
   if (!do_union) r.n_union = nullptr;
   bool tail_done = false;
   if (!logits_in && a.B > kTokensPerWave && a.norm_out == nullptr) {
-    // tiles of 4 tokens x 16 experts x 1024 inputs (+ activation prep), then
+    // tiles of 4 tokens x 16 experts x one K slice (+ activation prep), then
     // the slices' sums with the top-k and union (or the sums alone)
     const int prep_blocks = a.xp != nullptr ? (a.B + 1) / 2 : 0;   // two tokens a block
-    const int n_ks = (a.d + kTileK - 1) / kTileK;
+    const int n_ks = n_slices(a.d);
     const int n_logit = ((a.E + kTileExp - 1) / kTileExp) * n_ks;
     const dim3 grid(n_logit + prep_blocks, (a.B + kTileTok - 1) / kTileTok);
-    if (a.router_bf16)
-      SMOE_LAUNCH(t, k_route_tiled<true>, grid, dim3(kRouteThreads), 0, s, r);
-    else
-      SMOE_LAUNCH(t, k_route_tiled<false>, grid, dim3(kRouteThreads), 0, s, r);
+    const int pieces = slice_pieces(a.d);
+#define SMOE_TILED(BF, M) SMOE_LAUNCH(t, (k_route_tiled<BF, M>), grid, dim3(kRouteThreads), 0, s, r)
+    if (a.router_bf16) {
+      if (pieces == 1) SMOE_TILED(true, 1);
+      else if (pieces == 2) SMOE_TILED(true, 2);
+      else SMOE_TILED(true, 4);
+    } else {
+      if (pieces == 1) SMOE_TILED(false, 1);
+      else if (pieces == 2) SMOE_TILED(false, 2);
+      else SMOE_TILED(false, 4);
+    }
+#undef SMOE_TILED
     const int blocks = (a.B + kTopkThreads / 64 - 1) / (kTopkThreads / 64);
     if (do_topk)
       hipLaunchKernelGGL(k_topk_grid, dim3(blocks), dim3(kTopkThreads), 0, s, r, n_ks,

@@ -42,7 +42,7 @@ constexpr int kMaxPairs = kMaxBatch * kMaxTopK;
 struct WsLayout {
   size_t status;   // uint32 status word (+ padding)
   size_t logits;   // [B, E] f32
-  size_t lgp;      // [ceil(d/1024), B, E] f32 K-slice partial logits (B >= 3)
+  size_t lgp;      // [<= 8 K slices, B, E] f32 partial logits (B >= 3)
   size_t xp;       // [B, d] f16 prepped activations
   size_t xs;       // [B, d/64] float2 group sums of xp
   size_t xa;       // [B] f32 token scales (powers of two)
@@ -69,7 +69,7 @@ inline WsLayout ws_layout(const smoe_layer_desc& L, int B) {
   };
   w.status = take(256);
   w.logits = take((size_t)B * L.num_experts * 4);
-  w.lgp = take((size_t)((L.d_model + 1023) / 1024) * B * L.num_experts * 4);
+  w.lgp = take((size_t)8 * B * L.num_experts * 4);   // at most 8 K slices
   w.xp = take((size_t)B * L.d_model * 2);
   w.xs = take((size_t)B * (L.d_model / 64) * 8);
   w.xa = take((size_t)B * 4);
