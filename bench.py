@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--stack-layers", type=int, default=94)
     p.add_argument("--stack-prompt", type=int, default=512)
     p.add_argument("--stack-decode", type=int, default=128)
+    p.add_argument("--no-calibration", action="store_true",
+                   help="leave out the stream-read and launch/barrier calibration (profiling "
+                        "passes)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a device-to-device copy of COPY_BYTES (for the counter scale)")
     p.add_argument("--summarize-counters", nargs="+",
@@ -281,6 +284,46 @@ def stream_read_calibration(smoe):
     best = max(out.values())
     return {"kernel": "k_stream_read (smoe_stream_read)", "bytes": STREAM_BYTES,
             "gbps_by_grid": out, "best_gbps": best, "best_frac": round(best / HBM_PEAK_GBPS, 4)}
+
+
+def sync_calibration(smoe):
+    """What a kernel boundary costs against its in-kernel alternative:
+      * launch_us: mean cost of one more launch in a stream of back-to-back
+        launches of an empty kernel (one workgroup per CU), HIP events around
+        1000 launches enqueued by one call;
+      * grid_barrier_us: one device-wide barrier of a cooperative grid of one
+        256-thread workgroup per CU (smoe_grid_barrier: one device-scope
+        release per workgroup, then acquire polls), from the kernel's own
+        s_memrealtime stamps: first start to last exit, and last arrival to
+        last exit (the polls' share), medians of 20."""
+    import numpy as np
+    import torch
+    dev = torch.device("cuda:0")
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    smoe.empty_launch(ncu, 100)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 1000
+    e0.record()
+    smoe.empty_launch(ncu, n)                        # enqueued from C, back to back
+    e1.record()
+    torch.cuda.synchronize()
+    launch_us = e0.elapsed_time(e1) * 1e3 / n
+    counter = torch.zeros(1, dtype=torch.int32, device=dev)
+    timed_out = torch.zeros(1, dtype=torch.int32, device=dev)
+    stamps = torch.zeros(3 * ncu, dtype=torch.int64, device=dev)
+    whole, polls = [], []
+    for rep in range(25):
+        counter.zero_()
+        smoe.grid_barrier(ncu, counter, stamps, timed_out)
+        st = stamps.view(ncu, 3).cpu().numpy().astype(np.int64)
+        if rep >= 5:
+            whole.append((st[:, 2].max() - st[:, 0].min()) * 0.01)
+            polls.append((st[:, 2].max() - st[:, 1].max()) * 0.01)
+    return {"launch_us": round(launch_us, 2), "workgroups": ncu,
+            "grid_barrier_us": round(float(np.median(whole)), 2),
+            "grid_barrier_polls_us": round(float(np.median(polls)), 2),
+            "grid_barrier_timed_out": bool(int(timed_out.cpu()[0]))}
 
 
 def shared_bench(smoe, args):
@@ -935,7 +978,9 @@ def main():
         torch.cuda.empty_cache()
     if sec:
         result["secondary"] = sec
-    result["calibration"] = stream_read_calibration(smoe)
+    if not args.no_calibration:
+        result["calibration"] = stream_read_calibration(smoe)
+        result["calibration"]["sync"] = sync_calibration(smoe)
     if not args.no_stack and "decode" in wl:
         result["stack"] = stack_harness(smoe, args.stack_layers, args.stack_prompt,
                                         args.stack_decode)

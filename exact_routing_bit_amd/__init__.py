@@ -36,7 +36,8 @@ EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_ro
             "smoe_moe_forward", "smoe_moe_layer", "smoe_moe_layer_stage", "smoe_rmsnorm",
             "smoe_stack_forward", "smoe_read_status", "smoe_strerror",
             "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage",
-            "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes", "smoe_stream_read")
+            "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes", "smoe_stream_read",
+            "smoe_empty_launch", "smoe_grid_barrier")
 
 
 class SmoeError(RuntimeError):
@@ -94,6 +95,8 @@ def _load():
     L.smoe_moe_layer_noalloc.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp,
                                          vp, ctypes.POINTER(Union), vp]
     L.smoe_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    L.smoe_empty_launch.argtypes = [i32, i32, vp]
+    L.smoe_grid_barrier.argtypes = [i32, vp, vp, vp, vp]
     L.smoe_noalloc_scratch_bytes.argtypes = []
     L.smoe_noalloc_scratch_bytes.restype = sz
     L.smoe_moe_layer_stage.argtypes = [ctypes.c_int, dp, vp, ctypes.POINTER(Experts), vp, i32, vp,
@@ -337,6 +340,24 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes=None, stream=None)
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     _check(lib.smoe_stream_read(_ptr(buf, None, "buf"), n, _ptr(sink, torch.int32, "sink"),
                                 sink.numel(), _stream(stream)), "smoe_stream_read")
+
+
+def empty_launch(blocks: int, count: int = 1, stream=None):
+    """Diagnostic: `count` back-to-back launches of a kernel that does nothing
+    (smoe_empty_launch)."""
+    _check(lib.smoe_empty_launch(int(blocks), int(count), _stream(stream)), "smoe_empty_launch")
+
+
+def grid_barrier(blocks: int, counter, stamps, timed_out, stream=None):
+    """Diagnostic device-wide barrier of a cooperative grid (smoe_grid_barrier):
+    counter int32 [1] cleared by the caller, stamps int64 [3 * blocks],
+    timed_out int32 [1]."""
+    if stamps.dtype != torch.int64 or stamps.numel() < 3 * int(blocks):
+        raise ValueError("grid_barrier: stamps must be int64 with 3 * blocks entries")
+    _check(lib.smoe_grid_barrier(int(blocks), _ptr(counter, torch.int32, "counter"),
+                                 _ptr(stamps, torch.int64, "stamps"),
+                                 _ptr(timed_out, torch.int32, "timed_out"), _stream(stream)),
+           "smoe_grid_barrier")
 
 
 def noalloc_scratch_bytes() -> int:

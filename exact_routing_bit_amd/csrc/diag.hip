@@ -1,6 +1,12 @@
-// diag.hip - smoe_stream_read: a plain streaming read of a device buffer, the
-// calibration that measurements of the layer's kernels are set against (the
-// read bandwidth this part reaches on a pure stream of 16-byte loads).
+// diag.hip - calibrations that measurements of the layer's kernels are set
+// against:
+//   smoe_stream_read: a plain streaming read of a device buffer (the read
+//     bandwidth this part reaches on a pure stream of 16-byte loads);
+//   smoe_empty_launch: a kernel that does nothing (the cost of one more
+//     launch in a stream of back-to-back kernels);
+//   smoe_grid_barrier: one device-wide barrier of a cooperative grid (the
+//     cost of the alternative to a launch boundary: every block releases its
+//     stores at device scope, counts itself in and waits for all the others).
 #include "device.hpp"
 #include "smoe_internal.hpp"
 
@@ -37,6 +43,35 @@ __global__ __launch_bounds__(kReadThreads) void k_stream_read(const uint4* src, 
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
 }
 
+__global__ void k_empty() {}
+
+constexpr int kSpinLimit = 1 << 22;   // bounded wait: about 0.1 s, then give up
+
+// Each block: its barrier, one acquire-release increment of *counter at
+// device scope by thread 0, then (thread 0) acquire loads until all blocks
+// have arrived or the spin limit is reached.  stamps[3 b ..]: s_memrealtime
+// (100 MHz) at the block's start, after its increment, after its wait.
+__global__ __launch_bounds__(256) void k_grid_barrier(uint32_t* counter, uint64_t* stamps,
+                                                      int32_t* timed_out) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    int it = 0;
+    while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x &&
+           it < kSpinLimit) {
+      __builtin_amdgcn_s_sleep(1);
+      ++it;
+    }
+    if (it >= kSpinLimit) __hip_atomic_store(timed_out, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t2 = __builtin_amdgcn_s_memrealtime();
+    stamps[3 * blockIdx.x + 0] = t0;
+    stamps[3 * blockIdx.x + 1] = t1;
+    stamps[3 * blockIdx.x + 2] = t2;
+  }
+}
+
 }  // namespace
 }  // namespace smoe
 
@@ -50,4 +85,23 @@ SMOE_API int smoe_stream_read(const void* src, size_t bytes, uint32_t* sink, int
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
                      (int64_t)(bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? SMOE_OK : SMOE_EHIP;
+}
+
+SMOE_API int smoe_empty_launch(int32_t blocks, int32_t count, void* stream) {
+  if (blocks < 1 || blocks > (1 << 20) || count < 0 || count > (1 << 20)) return SMOE_EINVAL;
+  for (int i = 0; i < count; ++i)
+    hipLaunchKernelGGL(smoe::k_empty, dim3(blocks), dim3(64), 0, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? SMOE_OK : SMOE_EHIP;
+}
+
+SMOE_API int smoe_grid_barrier(int32_t blocks, uint32_t* counter, uint64_t* stamps,
+                               int32_t* timed_out, void* stream) {
+  if (blocks < 1 || blocks > 4096 || counter == nullptr || stamps == nullptr ||
+      timed_out == nullptr)
+    return SMOE_EINVAL;
+  void* args[] = {&counter, &stamps, &timed_out};
+  const hipError_t err = hipLaunchCooperativeKernel(
+      reinterpret_cast<const void*>(smoe::k_grid_barrier), dim3(blocks), dim3(256), args, 0,
+      static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? SMOE_OK : SMOE_EHIP;
 }

@@ -364,6 +364,28 @@ int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers, const void
  * Async on stream; SMOE_EINVAL on bad arguments, 1 <= blocks <= 2^20. */
 int smoe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
+/* Diagnostic: `count` (0 .. 2^20) back-to-back launches, from this one
+ * call, of a kernel of `blocks` (1 .. 2^20) workgroups of 64 threads that
+ * does nothing; timed on the stream, the mean is the cost of one more
+ * kernel boundary on the device (the host enqueues faster than that).
+ * Async on stream; SMOE_EINVAL on bad counts, SMOE_EHIP when a launch
+ * fails. */
+int smoe_empty_launch(int32_t blocks, int32_t count, void* stream);
+
+/* Diagnostic: one device-wide barrier, the in-kernel alternative to a kernel
+ * boundary.  A cooperative grid of `blocks` (1 .. 4096) workgroups of 256
+ * threads, all resident at once (the runtime refuses the launch otherwise:
+ * SMOE_EHIP); each block passes its own barrier, thread 0 increments
+ * *counter (acquire-release, device scope: one release of the block's
+ * stores) and then polls it with acquire loads until all blocks have arrived
+ * or about 2^22 polls have passed, when it sets *timed_out = 1 and goes on,
+ * so the kernel always ends.  stamps (device, 3 * blocks uint64) receive per
+ * block the s_memrealtime count (100 MHz) at its start, after its increment
+ * and after its wait.  *counter must be 0 on entry (the caller clears it);
+ * it is left at `blocks`.  Async on stream; SMOE_EINVAL on bad arguments. */
+int smoe_grid_barrier(int32_t blocks, uint32_t* counter, uint64_t* stamps, int32_t* timed_out,
+                      void* stream);
+
 /* ------------------------------------------------------------ utilities */
 /* Synchronises `stream`, then copies the workspace status bits into
  * *status_out (host).  For tests and diagnostics, not for the hot path. */

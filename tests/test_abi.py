@@ -284,3 +284,22 @@ def test_strerror(smoe):
     for c in (0, -1, -2, -3, -4):
         assert smoe.strerror(c)
     assert "unknown" in smoe.strerror(-99)
+
+
+def test_diagnostics_reject_bad_arguments(smoe):
+    """The calibration entry points validate before launching anything."""
+    f = 4096
+    sr = smoe.lib.smoe_stream_read
+    assert sr(f, 64, f, 0, None) == smoe.SMOE_EINVAL           # no blocks
+    assert sr(f + 4, 64, f, 8, None) == smoe.SMOE_EINVAL       # unaligned source
+    assert sr(f, 60, f, 8, None) == smoe.SMOE_EINVAL           # not whole 16-byte words
+    assert sr(None, 64, f, 8, None) == smoe.SMOE_EINVAL
+    assert smoe.lib.smoe_empty_launch(0, 1, None) == smoe.SMOE_EINVAL
+    assert smoe.lib.smoe_empty_launch((1 << 20) + 1, 1, None) == smoe.SMOE_EINVAL
+    assert smoe.lib.smoe_empty_launch(8, -1, None) == smoe.SMOE_EINVAL
+    gb = smoe.lib.smoe_grid_barrier
+    assert gb(0, f, f, f, None) == smoe.SMOE_EINVAL
+    assert gb(4097, f, f, f, None) == smoe.SMOE_EINVAL
+    assert gb(8, None, f, f, None) == smoe.SMOE_EINVAL
+    assert gb(8, f, None, f, None) == smoe.SMOE_EINVAL
+    assert gb(8, f, f, None, None) == smoe.SMOE_EINVAL
