@@ -58,10 +58,16 @@ def test_gpu_generator_matches_cpu_generator():
 
 
 # -------------------------------------------------------------------- routing
+# B >= 3 routes through K-slice tiles of 256, 512 or 1024 inputs (at most
+# eight slices): d = 2048 and below take 256, 4096 takes 512, wider 1024;
+# ragged last slices at d = 640 and 6144
 ROUTE_CASES = [(configs.TINY, 8), (configs.TINY, 1), (configs.DECODE, 1), (configs.DECODE, 37),
                (configs.DECODE, 64), (configs.FUSED_B64, 64),
                (small_config("k16", 256, 16, 16, 64, 5, bf16=False), 5),
-               (small_config("nonorm", 512, 40, 6, 64, 9, norm=False), 9)]
+               (small_config("nonorm", 512, 40, 6, 64, 9, norm=False), 9),
+               (small_config("d640_e20", 640, 20, 4, 64, 6), 6),
+               (small_config("d6144_b3", 6144, 64, 8, 64, 3), 3),
+               (small_config("d8192_b64_f32", 8192, 48, 6, 64, 64, bf16=False), 64)]
 
 
 @pytest.mark.parametrize("cfg,B", ROUTE_CASES, ids=lambda v: getattr(v, "name", str(v)))
