@@ -641,7 +641,94 @@ def stack_graph_decode(smoe, desc, args, cfg, n_layers, steps, h_out, idx_out, t
             "decode_graph_replays_equal_stream_bits": bool(equal)}
 
 
-def stack_harness(smoe, n_layers, prompt, steps):
+def near_tie(row, K):
+    """True when a token's K-th and (K+1)-th oracle logits are within fp32
+    rounding noise, so that two correct implementations may pick either."""
+    import numpy as np
+    srt = np.sort(row.astype(np.float64))[::-1]
+    return K < len(srt) and (srt[K - 1] - srt[K]) <= 1e-5 * max(1.0, float(np.abs(srt).max()))
+
+
+def stack_oracle_points(smoe, desc, Ws, ex, cfg, n_layers, prompt, steps):
+    """The stack's share of the CPU baseline: the oracle on sampled (decode
+    step, layer) and (prompt chunk, layer) points, teacher-forced.  A point's
+    input is the GPU's own input to layer l (its stream's hidden state through
+    the stack's first l layers); layer l then runs alone on the GPU and in the
+    oracle, on host copies of the experts the point routes to (copies not
+    timed).  The oracle routes on its own logits; a token whose experts differ
+    from the GPU's must be at a near-tie, and takes the GPU's set with the
+    oracle's weights for it.  Per point: the oracle's seconds and the relative
+    L2 of MoE_l(x) over the point and over its worst token."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth.gpu as sg
+    E, K, d = cfg.num_experts, cfg.top_k, cfg.d_model
+    dev = torch.device("cuda:0")
+    ws = torch.zeros(smoe.workspace_size(desc, STACK_CHUNK), dtype=torch.uint8, device=dev)
+    smoe.workspace_init(ws)
+    un = smoe.UnionBuffers.alloc(E, STACK_CHUNK * K, dev)
+    layers = sorted({0, n_layers // 2, n_layers - 1})
+    points = [("decode", n, l) for n in sorted({0, steps - 1}) for l in layers]
+    points += [("prefill", 0, l) for l in sorted({0, n_layers - 1})]
+    out_points = []
+    for kind, n, l in points:
+        x = (sg.hidden(cfg.seed, 0, 6000 + n, 1, d) if kind == "decode"
+             else sg.hidden(cfg.seed, 0, 5000, prompt, d)[:STACK_CHUNK].clone())
+        B = x.shape[0]
+        i32 = dict(dtype=torch.int32, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        if l > 0:
+            args = smoe.StackArgs([W["router"] for W in Ws[:l]], ex[:l])
+            smoe.stack_forward(desc, args, x, torch.zeros(B, d, **f32), torch.zeros(l, B, K, **i32),
+                               torch.zeros(l, B, K, **f32), un, ws)
+        out = torch.empty(B, d, **f32)
+        idx_g = torch.zeros(B, K, **i32)
+        w_g = torch.zeros(B, K, **f32)
+        smoe.moe_layer(desc, Ws[l]["router"], ex[l], x, out, idx_g, w_g, un, ws)
+        torch.cuda.synchronize()
+        xh, outg, idxg = x.cpu().numpy(), out.cpu().numpy(), idx_g.cpu().numpy()
+        Wr = Ws[l]["router"].cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        lg_ref, idx_ref, w_ref = oracle.route(Wr, xh, K, cfg.norm_topk_prob)
+        t_route = time.perf_counter() - t0
+        flips = [t for t in range(B) if not np.array_equal(idxg[t], idx_ref[t])]
+        if any(not near_tie(lg_ref[t], K) for t in flips):
+            raise RuntimeError(f"stack point {kind} {n} layer {l}: routing differs off a near-tie")
+        idx_use, w_use = idx_ref.copy(), w_ref.copy()
+        for t in flips:
+            idx_use[t] = idxg[t]
+            w_use[t] = oracle.weights_of(lg_ref[t:t + 1], idxg[t:t + 1], cfg.norm_topk_prob)[0]
+        used = np.unique(idx_use)
+        sel = torch.from_numpy(used.astype(np.int64)).to(dev)
+
+        def host(mat):
+            return tuple(m.index_select(0, sel).cpu().numpy().view(
+                np.uint32 if m.dtype == torch.int32 else np.uint16) for m in mat)
+        gate, up, down = host(Ws[l]["gate"]), host(Ws[l]["up"]), host(Ws[l]["down"])
+        cidx = np.searchsorted(used, idx_use).astype(np.int32)
+        t1 = time.perf_counter()
+        ref = oracle.moe(gate, up, down, xh, cidx, w_use, layer_major=True)
+        t_ffn = time.perf_counter() - t1
+        diff = (outg.astype(np.float64) - ref.astype(np.float64))
+        ref64 = ref.astype(np.float64)
+        tok = np.linalg.norm(diff, axis=1) / np.maximum(np.linalg.norm(ref64, axis=1), 1e-30)
+        out_points.append({"point": f"{kind} {'step' if kind == 'decode' else 'chunk'} {n}, "
+                                    f"layer {l}", "tokens": B, "union": int(len(used)),
+                           "oracle_s": round(t_route + t_ffn, 3),
+                           "rel_l2": float(f"{np.linalg.norm(diff) / np.linalg.norm(ref64):.3e}"),
+                           "worst_token_rel_l2": float(f"{tok.max():.3e}"),
+                           "near_tie_flips": len(flips)})
+    del ws
+    torch.cuda.empty_cache()
+    return {"kind": "oracle", "cores": oracle.num_threads(),
+            "sample": "teacher-forced (step or chunk, layer) points of the 94-layer stack; "
+                      "MoE_l of the GPU's own input to layer l, oracle against GPU",
+            "points": out_points}
+
+
+def stack_harness(smoe, n_layers, prompt, steps, oracle_points=False):
     """The stacked routed-expert path: n_layers layers of the decode shape
     resident in HBM; a prompt of `prompt` tokens in chunks of 64, layer-major
     (each chunk through every layer before the next chunk), then `steps`
@@ -727,6 +814,9 @@ def stack_harness(smoe, n_layers, prompt, steps):
     }
     out.update(graph)
     out.update(st)
+    if oracle_points:
+        out["oracle_points"] = stack_oracle_points(smoe, desc, Ws, ex, cfg, n_layers, prompt,
+                                                   steps)
     del Ws, ex, args
     torch.cuda.empty_cache()
     return out
@@ -981,11 +1071,15 @@ def main():
     if not args.no_calibration:
         result["calibration"] = stream_read_calibration(smoe)
         result["calibration"]["sync"] = sync_calibration(smoe)
+    stack_points = None
     if not args.no_stack and "decode" in wl:
         result["stack"] = stack_harness(smoe, args.stack_layers, args.stack_prompt,
-                                        args.stack_decode)
+                                        args.stack_decode, oracle_points=not args.no_cpu)
+        stack_points = result["stack"].pop("oracle_points", None)
     if L0 is not None:
         result["cpu_baseline"] = cpu_baseline(dec, L0, args.cpu_seconds)
+        if stack_points is not None:
+            result["cpu_baseline"]["stack_points"] = stack_points
     print(json.dumps(result), flush=True)
 
 
