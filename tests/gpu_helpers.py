@@ -1,6 +1,9 @@
 """Helpers shared by the GPU tests: host<->device marshalling and comparisons.
-Oracle inputs always come from the CPU generator; GPU results are only ever
-compared, never fed to the oracle."""
+Oracle inputs come from the seeded generator: the CPU one, or host copies of
+the GPU one's bytes (the same bits, which the tests check).  The layer's GPU
+results are only ever compared, never fed to the oracle; the one exception is
+a token at a provable near-tie of its K-th and (K+1)-th logits, which is given
+the GPU's expert set (with the oracle's weights for that set)."""
 from __future__ import annotations
 
 import numpy as np
