@@ -49,7 +49,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
 }
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi): two bf16 products carry

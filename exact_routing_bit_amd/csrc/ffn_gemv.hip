@@ -320,7 +320,8 @@ constexpr int kShRow0 = kMaxDecPairs * kMaxRtChunks;   // first shared ylds row
 // Issue the loads of item `item` of a row block (rows r0 .. r0+7): items
 // below nU nr are routed, slot item / nr, chunk item % nr; the rest are the
 // shared expert's chunks (pair q = token q).  h of the slot's pairs first
-// (the compute needs it first), then the rows' words, scales and biases.
+// (the compute needs it first), then row by row the row's words, scale and
+// bias, so that each row's dot and epilogue wait for that row's loads only.
 // No branch: dead pair slots repeat the last live pair.  Returns in ne the
 // slot's pair count, in ys[q] the ylds row of its q-th pair (pair p, chunk
 // c: row p kMaxRtChunks + c; shared chunk c, token t: kShRow0 + 2 c + t) and
@@ -359,6 +360,7 @@ __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, in
     for (int k = 0; k < NW; ++k) it.h[q][k] = hsrc[(int64_t)p * Cr + cw + L * NW + k];
   }
   const QPtr dn = expert_mat(a.down, a.sdown, sh, e);
+  const int64_t sb = (int64_t)r0 * Gr + cw / 8 + (L * NW) / 8;
   const uint32_t* wr = dn.w + (int64_t)r0 * Cr + cw + L * NW;
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
@@ -372,10 +374,6 @@ __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, in
     } else {
       it.w[r][0] = ld_stream1(src);
     }
-  }
-  const int64_t sb = (int64_t)r0 * Gr + cw / 8 + (L * NW) / 8;
-#pragma unroll
-  for (int r = 0; r < kDnRows; ++r) {
     const uint32_t sv = ld_stream_u16(dn.s + sb + (int64_t)r * Gr);
     const uint32_t bv = ld_stream_u16(dn.b + sb + (int64_t)r * Gr);
     it.s[r] = lane_live ? sv : 0u;
@@ -573,7 +571,7 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
 __device__ __forceinline__ void route_rank(int K, int* slot_pair, RouteKeep& keep,
                                            TopkScratch* tks) {
   keep.t = topk_rank(K, tks);
-  if (__lane_id() < K) slot_pair[__lane_id()] = keep.t.srank;
+  if ((int)__lane_id() < K) slot_pair[__lane_id()] = keep.t.srank;
 }
 
 // grid: one 4-wave block per compute unit (at most one wave per item).  Wave
@@ -718,7 +716,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   const int lane = threadIdx.x & 63;
   // the first row block's residual, fetched before anything waits
   float res_pref = 0.f;
-  if (a.residual != nullptr && threadIdx.x < a.B * kDnRows)
+  if (a.residual != nullptr && (int)threadIdx.x < a.B * kDnRows)
     res_pref = a.residual[(int64_t)(threadIdx.x / kDnRows) * a.d + blockIdx.x * kDnRows +
                           threadIdx.x % kDnRows];
   if (a.dec_meta_valid) {
@@ -758,7 +756,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
     // ascending, each y the sum of its chunks in order (with a shared expert:
     // residual + (shared + that sum)); a batch of eight pairs' values is read
     // before it is summed
-    if (threadIdx.x < a.B * kDnRows) {
+    if ((int)threadIdx.x < a.B * kDnRows) {
       const int t = threadIdx.x / kDnRows, rr = threadIdx.x % kDnRows;
       float acc = 0.f;
       for (int k0 = 0; k0 < K; k0 += 8) {

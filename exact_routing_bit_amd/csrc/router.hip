@@ -4,10 +4,11 @@
 // ROUTING: gate matvec on heavy_normed -> ranked top-k", "norm_topk_prob
 // weights"; "Layer-Major Batched Prefill", "The Inversion"):
 //   1. blocks compute logits[t,e] = sum_i Wr[e,i] x[t,i] (fp32) for a tile
-//      of experts x tokens (B <= 2: one expert and both tokens a wave; B >= 3:
-//      4 tokens x 16 experts x 1024 inputs a block, x staged in LDS), and
-//      further blocks convert x into the prepped fp16 activation layout the
-//      expert kernels read;
+//      of experts x tokens (B <= 2: one expert and every token a block, its
+//      row split over the four waves; B >= 3: 4 tokens x 16 experts x one K
+//      slice of at most 1024 inputs a block, x staged in LDS), and further
+//      blocks (one a token) convert x into the prepped fp16 activation layout
+//      the expert kernels read;
 //   2. the last blocks to finish (integer tickets) rank every token's experts
 //      by (logit descending, index ascending), form the softmax /
 //      norm_topk_prob weights, and build the union of the batch's experts with
@@ -26,72 +27,93 @@ namespace {
 
 constexpr int kRouteThreads = 256;              // 4 waves: 4 experts per block
 static_assert(kRouteThreads == 256, "block_row_inv needs blocks of 256 threads");
-constexpr int kTokensPerWave = 2;
+constexpr int kMaxRouteTok = 2;            // k_route's batches; larger ones are tiled
 constexpr int kTailThreads = 1024;              // stand-alone top-k / union block
 constexpr int kTopkThreads = 256;               // top-k grid: one token per wave
 constexpr int kMaxTicketBlocks = 64;            // larger grids hand the tail to its own kernel
 
-// Prepped activations of two tokens per 256-thread block: thread j handles
-// group j % 128 (64 inputs) of token 2 * blk + j / 128, i.e. the first two
-// waves token 0 and the last two token 1 (d <= 8192, so G = d/64 <= 128).
-// Every thread of the block must call it (it has block barriers).
-//   1. the group's 64 inputs are loaded (with norm_out: scaled by inv[j/128],
-//      the token's RMSNorm factor, and written to norm_out);
-//   2. the token's largest magnitude m gives a_t = 2^-floor(log2 m), clamped
+// Prepped activations of one token per 256-thread block: thread j takes the
+// 16-input pieces j and j + 256 (d <= 8192), so that the four pieces of a
+// group of 64 inputs sit in four neighbouring lanes of one wave.  Every
+// thread of the block must call it (it has block barriers).
+//   1. the pieces are loaded (with norm_out: scaled by inv, the token's
+//      RMSNorm factor, and written to norm_out);
+//   2. the row's largest magnitude m gives a_t = 2^-floor(log2 m), clamped
 //      to 2^-30 .. 2^30 (1 for a zero row), so that max |a_t x| is in [1, 2);
-//   3. a_t * x goes to the prepped fp16 layout with its group sums, and a_t
-//      to xa[t].
-// All 16 loads of a thread are issued before its first store.
+//   3. a_t * x goes to the prepped fp16 layout; the group sums are each
+//      lane's piece sums added over the group's four lanes (the same order in
+//      all four), and a_t goes to xa[t].
+// All loads of a thread are issued before its first store.
+constexpr int kPrepPieces = 2;                  // 16-input pieces a thread: 8192 / 16 / 256
 __device__ __forceinline__ float token_scale(float mx) {
   if (!(mx > 0.0f)) return 1.0f;
   const int e = min(max(ilogbf(mx), -30), 30);
   return __builtin_ldexpf(1.0f, -e);
 }
-__device__ void prep_two_tokens(const float* x, int B, int d, int blk, uint16_t* xp, float2* xs,
-                                float* xa, float* norm_out, const float (&inv)[2], float* red) {
-  const int tid = threadIdx.x, j = tid >> 7, g = tid & 127;
-  const int G = d / 64;
-  const int t = 2 * blk + j;
-  const bool live = t < B && g < G;
-  const int tt = live ? t : 0, gg = live ? g : 0;
-  const float4* src = reinterpret_cast<const float4*>(x + (int64_t)tt * d + gg * 64);
-  float4 v4[16];
+__device__ void prep_token(const float* x, int d, int t, uint16_t* xp, float2* xs, float* xa,
+                           float* norm_out, float inv, float* red) {
+  const int tid = threadIdx.x;
+  const int np = d / 16;                        // pieces of the row, 4 a group
+  const int nr = np > 256 ? 2 : 1;              // uniform
+  float4 v4[kPrepPieces][4];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) v4[c] = live ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
-  if (norm_out != nullptr) {
-    const float sc = inv[j];
-    float4* hn = reinterpret_cast<float4*>(norm_out + (int64_t)tt * d + gg * 64);
+  for (int r = 0; r < kPrepPieces; ++r) {
+    if (r >= nr) break;
+    const int p = tid + 256 * r;
+    const bool live = p < np;
+    const float4* src = reinterpret_cast<const float4*>(x + (int64_t)t * d + (live ? p : 0) * 16);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      v4[c] = make_float4(v4[c].x * sc, v4[c].y * sc, v4[c].z * sc, v4[c].w * sc);
-      if (live) hn[c] = v4[c];
-    }
+    for (int c = 0; c < 4; ++c) v4[r][c] = live ? src[c] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float mx = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
-    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v4[c].x), fabsf(v4[c].y)), fmaxf(fabsf(v4[c].z), fabsf(v4[c].w))));
+  for (int r = 0; r < kPrepPieces; ++r) {
+    if (r >= nr) break;
+    const int p = tid + 256 * r;
+    if (norm_out != nullptr) {
+      float4* hn = reinterpret_cast<float4*>(norm_out + (int64_t)t * d + p * 16);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v4[r][c] = make_float4(v4[r][c].x * inv, v4[r][c].y * inv, v4[r][c].z * inv,
+                               v4[r][c].w * inv);
+        if (p < np) hn[c] = v4[r][c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v4[r][c].x), fabsf(v4[r][c].y)),
+                           fmaxf(fabsf(v4[r][c].z), fabsf(v4[r][c].w))));
+  }
   mx = wave_max(mx);
   if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  const float a = token_scale(fmaxf(red[2 * j], red[2 * j + 1]));
+  const float a = token_scale(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
   __syncthreads();                                // red may be reused after this
-  if (!live) return;
-  uint16_t* dst16 = xp + (int64_t)t * d + g * 64;
-  uint4* dst = reinterpret_cast<uint4*>(dst16);
-  float X = 0.f, S = 0.f;
-  uint4 out[8];
+  const int G = d / 64;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float4 lo = v4[2 * c], hi = v4[2 * c + 1];
-    const float v[8] = {lo.x * a, lo.y * a, lo.z * a, lo.w * a, hi.x * a, hi.y * a, hi.z * a,
-                        hi.w * a};
-    out[c] = prep_chunk(v, &X, &S);
+  for (int r = 0; r < kPrepPieces; ++r) {
+    if (r >= nr) break;
+    const int p = tid + 256 * r;
+    float X = 0.f, S = 0.f;
+    uint4 out[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const float4 lo = v4[r][2 * c], hi = v4[r][2 * c + 1];
+      const float v[8] = {lo.x * a, lo.y * a, lo.z * a, lo.w * a, hi.x * a, hi.y * a, hi.z * a,
+                          hi.w * a};
+      out[c] = prep_chunk(v, &X, &S);
+    }
+    // every lane takes part (dead pieces add zeros: a group is live or dead as a whole)
+    X = segment_sum16(X, 4);
+    S = segment_sum16(S, 4);
+    if (p < np) {
+      uint4* dst = reinterpret_cast<uint4*>(xp + (int64_t)t * d + p * 16);
+      dst[0] = out[0];
+      dst[1] = out[1];
+      if ((p & 3) == 0) xs[(int64_t)t * G + p / 4] = make_float2(X, 1024.0f * S);
+    }
   }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) dst[c] = out[c];
-  xs[(int64_t)t * G + g] = make_float2(X, 1024.0f * S);
-  if (g == 0) xa[t] = a;
+  if (tid == 0) xa[t] = a;
 }
 
 // Top-k of one token's E <= 256 logits by one full wave; writes indices and
@@ -204,147 +226,110 @@ __device__ __forceinline__ void route_tail(const RouteArgs& a, bool do_topk, boo
   build_union(a, us);
 }
 
-// Gate values of expert e for input chunk c0 .. c0 + 4095 (one wave): lane l
-// holds inputs c0 + 8 l + 512 m .. + 7, m < 8 (zeros past d).
-template <bool kBf16>
-__device__ __forceinline__ void gate_chunk(const RouteArgs& a, int e, int c0, float (&wv)[8][8]) {
+// Logits of expert e for the NT = B <= 2 tokens, one 256-thread block: the
+// row splits into pieces of 512 inputs, wave w taking pieces w, w + 4, ...
+// (kM of them; lane l takes inputs 512 P + 8 l .. + 7, zeros past d).  Each
+// wave's sums go to part[wave][t], and the block adds the four in wave
+// order.  With a.norm_out the inputs are x * inv_t (the tokens' RMSNorm
+// factors, from block_row_inv as smoe_rmsnorm forms them), rounded as
+// smoe_rmsnorm rounds them.  Every thread of the block must call it (it has
+// block barriers).  The gate rows are requested first (HBM), then the
+// factors are formed, then the inputs (caches) are read.
+template <bool kBf16, int NT, int kM>
+__device__ void logits_block(const RouteArgs& a, int e, float (*part)[NT]) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
   const int d = a.d;
+  int idx[kM];
+  bool ok[kM];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int i = c0 + lane * 8 + 512 * m;
-    const bool ok = i < d;
-    const int64_t at = (int64_t)e * d + (ok ? i : 0);
+  for (int m = 0; m < kM; ++m) {
+    idx[m] = 512 * (wave + 4 * m) + 8 * lane;
+    ok[m] = idx[m] < d;
+  }
+  float w[kM][8];
+#pragma unroll
+  for (int m = 0; m < kM; ++m) {
+    const int64_t at = (int64_t)e * d + (ok[m] ? idx[m] : 0);
     if (kBf16) {
       const uint4 raw = *reinterpret_cast<const uint4*>((const uint16_t*)a.router_w + at);
       const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
-        wv[m][2 * z] = ok ? __uint_as_float(r4[z] << 16) : 0.f;
-        wv[m][2 * z + 1] = ok ? __uint_as_float(r4[z] & 0xFFFF0000u) : 0.f;
+        w[m][2 * z] = ok[m] ? __uint_as_float(r4[z] << 16) : 0.f;
+        w[m][2 * z + 1] = ok[m] ? __uint_as_float(r4[z] & 0xFFFF0000u) : 0.f;
       }
     } else {
       const float4* wp = reinterpret_cast<const float4*>((const float*)a.router_w + at);
       const float4 lo = wp[0], hi = wp[1];
       const float v8[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
 #pragma unroll
-      for (int z = 0; z < 8; ++z) wv[m][z] = ok ? v8[z] : 0.f;
+      for (int z = 0; z < 8; ++z) w[m][z] = ok[m] ? v8[z] : 0.f;
     }
   }
-}
-
-// acc[j] += this lane's share of chunk c0 of sum_i Wr[e, i] x[t0 + j, i];
-// kScaled: the inputs are x * inv[j] (the tokens' RMSNorm factors), rounded
-// as smoe_rmsnorm rounds them.
-template <bool kScaled>
-__device__ __forceinline__ void dot_chunk(const RouteArgs& a, int t0, int nt, int c0,
-                                          const float (&wv)[8][8],
-                                          const float (&inv)[kTokensPerWave],
-                                          float (&acc)[kTokensPerWave]) {
-  const int lane = __lane_id();
-  const int d = a.d;
+  float inv[NT];
 #pragma unroll
-  for (int j = 0; j < kTokensPerWave; ++j) {
-    const int t = t0 + min(j, nt - 1);
-    float part = 0.f;
+  for (int t = 0; t < NT; ++t)
+    inv[t] = a.norm_out != nullptr ? block_row_inv(a.x + (int64_t)t * d, d, a.norm_eps, &part[0][0])
+                                   : 1.0f;
+  float acc[NT];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int i = c0 + lane * 8 + 512 * m;
-      const float4* xp4 = reinterpret_cast<const float4*>(a.x + (int64_t)t * d + (i < d ? i : 0));
-      float4 lo = xp4[0], hi = xp4[1];
-      if (kScaled) {
-        const float s = inv[j];
-        lo = make_float4(lo.x * s, lo.y * s, lo.z * s, lo.w * s);
-        hi = make_float4(hi.x * s, hi.y * s, hi.z * s, hi.w * s);
+  for (int t = 0; t < NT; ++t) {
+    float4 xv[kM][2];
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      const float4* xp4 = reinterpret_cast<const float4*>(a.x + (int64_t)t * d + (ok[m] ? idx[m] : 0));
+      xv[m][0] = xp4[0];
+      xv[m][1] = xp4[1];
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+      float v8[8] = {xv[m][0].x, xv[m][0].y, xv[m][0].z, xv[m][0].w,
+                     xv[m][1].x, xv[m][1].y, xv[m][1].z, xv[m][1].w};
+      if (a.norm_out != nullptr) {
+#pragma unroll
+        for (int z = 0; z < 8; ++z) v8[z] *= inv[t];
       }
-      part += wv[m][0] * lo.x + wv[m][1] * lo.y + wv[m][2] * lo.z + wv[m][3] * lo.w +
-              wv[m][4] * hi.x + wv[m][5] * hi.y + wv[m][6] * hi.z + wv[m][7] * hi.w;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) sum = fmaf(w[m][z], v8[z], sum);
     }
-    acc[j] += part;
+    acc[t] = wave_sum(sum);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) part[wave][t] = acc[t];
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < NT) {
+    const int t = threadIdx.x;
+    a.logits[(int64_t)t * a.E + e] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
   }
 }
 
-// Logits of expert e for tokens t0, t0+1 (one wave).  Lanes stride the input
-// 8 elements at a time; within each 4096-element chunk every gate and input
-// load is issued before the products.
-template <bool kBf16>
-__device__ void logits_wave(const RouteArgs& a, int e, int t0, int nt) {
-  const float inv[kTokensPerWave] = {1.f, 1.f};
-  float acc[kTokensPerWave] = {};
-  for (int c0 = 0; c0 < a.d; c0 += 4096) {
-    float wv[8][8];
-    gate_chunk<kBf16>(a, e, c0, wv);
-    dot_chunk<false>(a, t0, nt, c0, wv, inv, acc);
-  }
-#pragma unroll
-  for (int j = 0; j < kTokensPerWave; ++j) {
-    const float tot = wave_sum(acc[j]);
-    if (__lane_id() == 0 && j < nt) a.logits[(int64_t)(t0 + j) * a.E + e] = tot;
-  }
-}
+// Pieces of 512 inputs a wave for a row of d inputs.
+inline int route_pieces(int d) { return d <= 2048 ? 1 : d <= 4096 ? 2 : 4; }
 
-// As logits_wave for a whole block (wave w: expert e0 + w) on the RMSNorm of
-// x (a.norm_out set; B <= kTokensPerWave, one grid row): each wave's first
-// gate chunk is requested, then the block forms the tokens' factors
-// (block_row_inv, as smoe_rmsnorm does), then the products.
-template <bool kBf16>
-__device__ void logits_block_normed(const RouteArgs& a, int e0, float* part) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int e = e0 + wave;
-  const bool has_e = e < a.E;
-  const int nt = a.B;
-  float wv[8][8];
-  gate_chunk<kBf16>(a, has_e ? e : 0, 0, wv);
-  float inv[kTokensPerWave] = {1.f, 1.f};
-#pragma unroll
-  for (int j = 0; j < kTokensPerWave; ++j)
-    if (j < nt) inv[j] = block_row_inv(a.x + (int64_t)j * a.d, a.d, a.norm_eps, part);
-  if (!has_e) return;
-  float acc[kTokensPerWave] = {};
-  dot_chunk<true>(a, 0, nt, 0, wv, inv, acc);
-  for (int c0 = 4096; c0 < a.d; c0 += 4096) {
-    gate_chunk<kBf16>(a, e, c0, wv);
-    dot_chunk<true>(a, 0, nt, c0, wv, inv, acc);
-  }
-#pragma unroll
-  for (int j = 0; j < kTokensPerWave; ++j) {
-    const float tot = wave_sum(acc[j]);
-    if (__lane_id() == 0 && j < nt) a.logits[(int64_t)j * a.E + e] = tot;
-  }
-}
-
-template <bool kBf16>
+// B <= 2 tokens (NT = B), one grid row: blocks [0, B) prep a token's
+// activations (prep_token), blocks B .. B + E - 1 form the logits of one
+// expert each (logits_block).  do_tail: the last block to finish ranks and
+// builds the union.
+template <bool kBf16, int NT, int kM>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tail,
                                                          uint32_t* ticket) {
   __shared__ UnionSmem us;
   __shared__ int is_last;
-  // blocks [0, E/4) compute logits (4 experts each, kTokensPerWave tokens per
-  // grid row); the blocks after them prep the activations, one (token, group)
-  // unit per thread, in grid row 0, alongside the logits
-  __shared__ float part[kRouteThreads / 64];
-  const int n_logit_blocks = (a.E + 3) / 4;
-  if ((int)blockIdx.x < n_logit_blocks) {
-    const int e0 = blockIdx.x * (kRouteThreads / 64);
-    if (a.norm_out != nullptr) {
-      logits_block_normed<kBf16>(a, e0, part);
-    } else {
-      const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-      const int e = e0 + wave;
-      const int t0 = blockIdx.y * kTokensPerWave;
-      if (e < a.E) logits_wave<kBf16>(a, e, t0, min(kTokensPerWave, a.B - t0));
+  __shared__ float part[kRouteThreads / 64][NT];
+  if ((int)blockIdx.x < NT) {
+    if (a.xp != nullptr) {
+      const int t = blockIdx.x;
+      const float inv = a.norm_out != nullptr
+                            ? block_row_inv(a.x + (int64_t)t * a.d, a.d, a.norm_eps, &part[0][0])
+                            : 1.0f;
+      prep_token(a.x, a.d, t, a.xp, a.xs, a.xa, a.norm_out, inv, &part[0][0]);
     }
-  } else if (a.xp != nullptr && blockIdx.y == 0) {
-    // two tokens per prep block; with a.norm_out (B <= kTokensPerWave, one
-    // prep block) the block forms the tokens' RMSNorm factors first
-    // (block_row_inv), then preps the scaled rows
-    float inv[kTokensPerWave] = {1.f, 1.f};
-    if (a.norm_out != nullptr) {
-#pragma unroll
-      for (int j = 0; j < kTokensPerWave; ++j)
-        if (j < a.B) inv[j] = block_row_inv(a.x + (int64_t)j * a.d, a.d, a.norm_eps, part);
-    }
-    prep_two_tokens(a.x, a.B, a.d, blockIdx.x - n_logit_blocks, a.xp, a.xs, a.xa, a.norm_out,
-                    inv, part);
+  } else {
+    logits_block<kBf16, NT, kM>(a, blockIdx.x - NT, part);
   }
   if (!do_tail) return;
   // The last block to finish reads every block's logits.  Each wave releases
@@ -411,8 +396,9 @@ __device__ __forceinline__ void gate_slice(const RouteArgs& a, int e, int k0, fl
   }
 }
 
-// grid: (ceil(E/16) * n_slices logit blocks + prep blocks, ceil(B/4) tile
-// rows).  Logit block (eb, ks) of tile row ty: experts 16 eb .., inputs
+// grid (one-dimensional): the prep blocks (one a token, first, as they have
+// the longer chains), then ceil(B/4) tile rows of ceil(E/16) * n_slices logit
+// blocks.  Logit block (eb, ks) of tile row ty: experts 16 eb .., inputs
 // 256 kM ks .., tokens 4 ty ..; partial sums to lgp[ks][t][e].
 template <bool kBf16, int kM>
 __global__ __launch_bounds__(kRouteThreads) void k_route_tiled(RouteArgs a) {
@@ -421,19 +407,16 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_tiled(RouteArgs a) {
   __shared__ float part[kRouteThreads / 64];
   const int n_ks = (a.d + kK - 1) / kK;
   const int n_logit = ((a.E + kTileExp - 1) / kTileExp) * n_ks;
-  const int t0 = blockIdx.y * kTileTok;
-  if ((int)blockIdx.x >= n_logit) {
-    // activation prep, two tokens a block, in tile row 0
-    if (a.xp != nullptr && blockIdx.y == 0) {
-      const float inv[kTokensPerWave] = {1.f, 1.f};
-      prep_two_tokens(a.x, a.B, a.d, blockIdx.x - n_logit, a.xp, a.xs, a.xa, nullptr, inv,
-                      part);
-    }
+  const int n_prep = a.xp != nullptr ? a.B : 0;
+  if ((int)blockIdx.x < n_prep) {
+    prep_token(a.x, a.d, blockIdx.x, a.xp, a.xs, a.xa, nullptr, 1.0f, part);
     return;
   }
+  const int lb = blockIdx.x - n_prep;
+  const int t0 = (lb / n_logit) * kTileTok, bx = lb % n_logit;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = __lane_id();
-  const int ew = (blockIdx.x / n_ks) * kTileExp + 4 * wave, ks = blockIdx.x % n_ks;
+  const int ew = (bx / n_ks) * kTileExp + 4 * wave, ks = bx % n_ks;
   const int k0 = ks * kK;
   // the wave's four gate rows first: they come from HBM, x from the caches
   float4 w[4][kM];
@@ -597,11 +580,11 @@ __global__ __launch_bounds__(kTailThreads) void k_topk_union(RouteArgs a, int do
   route_tail(a, do_topk != 0, do_union != 0, &us);
 }
 
-__global__ __launch_bounds__(256) void k_prep(const float* x, int B, int d, uint16_t* xp,
-                                              float2* xs, float* xa) {
+// grid: one block per token
+__global__ __launch_bounds__(256) void k_prep(const float* x, int d, uint16_t* xp, float2* xs,
+                                              float* xa) {
   __shared__ float red[4];
-  const float inv[2] = {1.f, 1.f};
-  prep_two_tokens(x, B, d, blockIdx.x, xp, xs, xa, nullptr, inv, red);
+  prep_token(x, d, blockIdx.x, xp, xs, xa, nullptr, 1.0f, red);
 }
 
 __global__ void k_fill_u32(uint32_t* p, uint32_t v, int n) {
@@ -622,13 +605,14 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
   RouteArgs r = a;
   if (!do_union) r.n_union = nullptr;
   bool tail_done = false;
-  if (!logits_in && a.B > kTokensPerWave && a.norm_out == nullptr) {
+  if (!logits_in && a.B > kMaxRouteTok) {
     // tiles of 4 tokens x 16 experts x one K slice (+ activation prep), then
     // the slices' sums with the top-k and union (or the sums alone)
-    const int prep_blocks = a.xp != nullptr ? (a.B + 1) / 2 : 0;   // two tokens a block
+    if (a.norm_out != nullptr) return hipErrorInvalidValue;   // the norm is fused at B <= 2 only
+    const int prep_blocks = a.xp != nullptr ? a.B : 0;         // a token a block
     const int n_ks = n_slices(a.d);
     const int n_logit = ((a.E + kTileExp - 1) / kTileExp) * n_ks;
-    const dim3 grid(n_logit + prep_blocks, (a.B + kTileTok - 1) / kTileTok);
+    const dim3 grid(prep_blocks + n_logit * ((a.B + kTileTok - 1) / kTileTok));
     const int pieces = slice_pieces(a.d);
 #define SMOE_TILED(BF, M) SMOE_LAUNCH(t, (k_route_tiled<BF, M>), grid, dim3(kRouteThreads), 0, s, r)
     if (a.router_bf16) {
@@ -652,15 +636,30 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
     logits_in = true;                               // only a stand-alone union is left
   }
   if (!logits_in) {
-    // logits (+ activation prep); small grids finish top-k/union in their last block
-    const int prep_blocks = a.xp != nullptr ? (a.B + 1) / 2 : 0;   // two tokens a block
-    const dim3 grid((a.E + 3) / 4 + prep_blocks, (a.B + kTokensPerWave - 1) / kTokensPerWave);
-    const bool fused = (do_topk || do_union) && (int)(grid.x * grid.y) <= kMaxTicketBlocks;
+    // B <= 2: a block per token's prep (first, as they have the longer
+    // chains), then a block per expert's logits; small grids finish
+    // top-k/union in their last block
+    const dim3 grid(a.B + a.E);
+    const bool fused = (do_topk || do_union) && (int)grid.x <= kMaxTicketBlocks;
     uint32_t* ticket = a.status + 1;
-    if (a.router_bf16)
-      SMOE_LAUNCH(t, k_route<true>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
-    else
-      SMOE_LAUNCH(t, k_route<false>, grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket);
+    const int pieces = route_pieces(a.d);
+#define SMOE_ROUTE(BF, NT, M) \
+  SMOE_LAUNCH(t, (k_route<BF, NT, M>), grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket)
+#define SMOE_ROUTE_M(BF, NT)                  \
+  do {                                        \
+    if (pieces == 1) SMOE_ROUTE(BF, NT, 1);   \
+    else if (pieces == 2) SMOE_ROUTE(BF, NT, 2); \
+    else SMOE_ROUTE(BF, NT, 4);               \
+  } while (0)
+    if (a.router_bf16) {
+      if (a.B == 1) SMOE_ROUTE_M(true, 1);
+      else SMOE_ROUTE_M(true, 2);
+    } else {
+      if (a.B == 1) SMOE_ROUTE_M(false, 1);
+      else SMOE_ROUTE_M(false, 2);
+    }
+#undef SMOE_ROUTE_M
+#undef SMOE_ROUTE
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     tail_done = fused;
@@ -680,7 +679,7 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
 
 hipError_t launch_prep(const float* x, int B, int d, uint16_t* xp, float2* xs, float* xa,
                        hipStream_t s) {
-  hipLaunchKernelGGL(k_prep, dim3((B + 1) / 2), dim3(256), 0, s, x, B, d, xp, xs, xa);
+  hipLaunchKernelGGL(k_prep, dim3(B), dim3(256), 0, s, x, d, xp, xs, xa);
   return hipGetLastError();
 }
 
