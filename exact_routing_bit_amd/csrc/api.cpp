@@ -4,6 +4,7 @@
 // anything, then enqueues kernels on the caller's stream and returns without
 // synchronising (smoe_read_status excepted).
 #include <hip/hip_runtime.h>
+#include <algorithm>
 
 #include <cstdint>
 #include <cstring>

@@ -37,17 +37,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
   // dword 3 = 0x00020000: raw 32-bit data format, no swizzle (gfx9 family)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
-// 16 bytes, nontemporal (streamed once, see ld_stream4)
-__device__ __forceinline__ uint4 buf_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+// 16, 8 or 4 bytes, nontemporal (streamed once, see ld_stream4); soff is a
+// wave-uniform byte offset added in a scalar register
+__device__ __forceinline__ uint4 buf_load4_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff = 0) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, soff, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 buf_load2_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff = 0) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, soff, 2);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t buf_load1_nt(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, soff, 2);
+}
+// 16 bytes, cached (data that other workgroups read again)
+__device__ __forceinline__ uint4 buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff = 0) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint32_t buf_load_u16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 // 2 bytes, nontemporal (a streamed scale or bias)
-__device__ __forceinline__ uint32_t buf_load_u16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 2);
+__device__ __forceinline__ uint32_t buf_load_u16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                                    int soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, soff, 2);
 }
 __device__ __forceinline__ uint32_t ld_stream_u16(const uint16_t* p) {
   return __builtin_nontemporal_load(p);

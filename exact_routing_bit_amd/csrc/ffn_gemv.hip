@@ -338,8 +338,15 @@ __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, in
   const int Cr = sh ? a.fs / 8 : a.f / 8, Gr = Cr / 8;    // words and groups of a row
   const int cw = c * (sh ? g.ws : g.wr);                 // the chunk's first word
   const int NL = min(sh ? g.ws : g.wr, Cr - cw) / NW;
+  // Buffer loads: the rows' part of an offset is scalar (soffset), the lane's
+  // part a vector offset fixed for the item, so that issuing them takes no
+  // vector address arithmetic.  Lanes past the chunk's last word load past
+  // every resource, which returns zeros: their h sums, dots, scales and
+  // biases all vanish.
   const bool lane_live = lane < NL;
-  const int L = lane_live ? lane : NL - 1;
+  const uint32_t vw = lane_live ? (uint32_t)(cw + lane * NW) * 4u : kBufferDead;
+  const uint32_t vs = lane_live ? (uint32_t)(cw / 8 + (lane * NW) / 8) * 2u : kBufferDead;
+  const uint32_t vh = lane_live ? (uint32_t)(cw + lane * NW) * 16u : kBufferDead;
   // an empty union (every routed id invalid) has no routed items; an invalid
   // id in a live slot cannot occur, but would read expert 0
   const int e0 = sh ? 0 : uniform(m.experts[u]);
@@ -356,28 +363,29 @@ __device__ __forceinline__ void down_load(const FfnArgs& a, const DecMeta& m, in
     // 1/a_t^2 of the pair's token (one token: always ib[0], which also keeps
     // the pick from becoming an indexed private array)
     ysc[q] = (NTOK == 1 || (sh ? qq : p / a.K) == 0) ? ib[0] : ib[1];
+    const auto rh = buffer_rsrc(hsrc + (int64_t)p * Cr, (uint32_t)Cr * 16u);
 #pragma unroll
-    for (int k = 0; k < NW; ++k) it.h[q][k] = hsrc[(int64_t)p * Cr + cw + L * NW + k];
+    for (int k = 0; k < NW; ++k) it.h[q][k] = buf_load4(rh, vh + 16u * k);
   }
   const QPtr dn = expert_mat(a.down, a.sdown, sh, e);
-  const int64_t sb = (int64_t)r0 * Gr + cw / 8 + (L * NW) / 8;
-  const uint32_t* wr = dn.w + (int64_t)r0 * Cr + cw + L * NW;
+  const auto rw = buffer_rsrc(dn.w + (int64_t)r0 * Cr, (uint32_t)(kDnRows * Cr) * 4u);
+  const auto rs = buffer_rsrc(dn.s + (int64_t)r0 * Gr, (uint32_t)(kDnRows * Gr) * 2u);
+  const auto rb = buffer_rsrc(dn.b + (int64_t)r0 * Gr, (uint32_t)(kDnRows * Gr) * 2u);
 #pragma unroll
   for (int r = 0; r < kDnRows; ++r) {
-    const uint32_t* src = wr + (int64_t)r * Cr;
+    const int sow = r * Cr * 4, sos = r * Gr * 2;
     if constexpr (NW == 4) {
-      const uint4 v = ld_stream4(src);
+      const uint4 v = buf_load4_nt(rw, vw, sow);
       it.w[r][0] = v.x, it.w[r][1] = v.y, it.w[r][2] = v.z, it.w[r][3] = v.w;
     } else if constexpr (NW == 2) {
-      const uint2 v = ld_stream2(src);
+      const uint2 v = buf_load2_nt(rw, vw, sow);
       it.w[r][0] = v.x, it.w[r][1] = v.y;
     } else {
-      it.w[r][0] = ld_stream1(src);
+      it.w[r][0] = buf_load1_nt(rw, vw, sow);
     }
-    const uint32_t sv = ld_stream_u16(dn.s + sb + (int64_t)r * Gr);
-    const uint32_t bv = ld_stream_u16(dn.b + sb + (int64_t)r * Gr);
-    it.s[r] = lane_live ? sv : 0u;
-    it.b[r] = lane_live ? bv : 0u;
+    it.s[r] = buf_load_u16_nt(rs, vs, sos);
+    it.b[r] = buf_load_u16_nt(rb, vs, sos);
+    __builtin_amdgcn_sched_barrier(0);             // in row order, each row's three together
   }
   __builtin_amdgcn_sched_barrier(0);               // issue them here (see gu_load)
 }
@@ -785,7 +793,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
       const float res = rb == (int)blockIdx.x ? res_pref : (a.residual ? a.residual[o] : 0.f);
       a.out[o] = res + acc;
     }
-    __syncthreads();                               // ylds is free again
+    // ylds is free again for the block's next row block (the barrier would
+    // also wait for the stores above, so the last row block goes without)
+    if (rb + (int)gridDim.x < n_rb) __syncthreads();
   }
 }
 
