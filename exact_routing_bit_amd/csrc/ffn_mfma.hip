@@ -121,20 +121,22 @@ __device__ __forceinline__ const void* align4(const uint16_t* p) {
 // last use: that copy carries the nontemporal hint, so that the streamed
 // weights leave the L2 first and the activations that every workgroup of an
 // expert re-reads stay in it.
+// uoff: words from the pass's first unit of rows to the one being streamed.
 template <int NT>
 __device__ __forceinline__ void issue_words(const Sources<NT>& S, char* slot, int k, int G,
-                                            int wave, int lane, bool line_aligned) {
+                                            int wave, int lane, bool line_aligned,
+                                            int64_t uoff = 0) {
   const int gA = 2 * k, gB = min(2 * k + 1, G - 1);
   // packed words: lanes 0-31 copy group gA, lanes 32-63 group gB
   const int gw = (lane >> 5) ? gB : gA;
   if (line_aligned && (k & 1)) {
 #pragma unroll
     for (int T = 0; T < kTiles; ++T)
-      dma16_to_lds_nt(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
+      dma16_to_lds_nt(S.w[T] + uoff + gw * 8, slot + (wave * kTiles + T) * 1024);
   } else {
 #pragma unroll
     for (int T = 0; T < kTiles; ++T)
-      dma16_to_lds(S.w[T] + gw * 8, slot + (wave * kTiles + T) * 1024);
+      dma16_to_lds(S.w[T] + uoff + gw * 8, slot + (wave * kTiles + T) * 1024);
   }
 }
 template <bool kGateUp, bool kFastSB, int NT>
@@ -308,18 +310,26 @@ struct PassCtx {
   float* yout;
   int unit;                // this wave's unit of rows
   bool has_unit;           // false: a copy of the last unit, nothing written
+  int unit2;               // a second unit streamed right after the first (kU = 2)
+  bool has_unit2;
 };
 
 // The whole pass of one wave's unit over the expert's K dimension for its
 // pairs, in passes of 16 NT pairs (one pass when NT = 4), kRingN stages in
-// the ring.
-template <bool kGateUp, bool kFastSB, int NT, int kRingN>
+// the ring.  kU = 2 (the narrow down pass over at most 32 groups, a multiple
+// of eight): the wave streams a second unit (c.unit2) right behind the first
+// through the same ring, so that one fill and one drain serve both; the
+// first unit's accumulators are held until the end, and its scales and
+// biases take the register half that more than 32 groups would use.
+template <bool kGateUp, bool kFastSB, int NT, int kRingN, int kU = 1>
 __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, char* ring,
                                          int* lpair) {
   constexpr int kSlot = slot_bytes<kFastSB, NT>();
   constexpr int kRest = copies_of_rest<kGateUp, kFastSB, NT>();
   constexpr int kStage = copies_of_stage<kGateUp, kFastSB, NT>();
   static_assert(kRingN == 2 || kRingN == 3, "two or three stages in the ring");
+  static_assert(kU == 1 || (kU == 2 && !kGateUp && kFastSB && NT == 1),
+                "two units: the narrow down pass with scales in registers");
   const int K = kGateUp ? a.d : c.F;
   const int G = K / 64, C = K / 8;
   const int lane = threadIdx.x & 63;
@@ -365,6 +375,10 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
     }
   }
   const int nst = (G + kGps - 1) / kGps;
+  const int nstT = kU * nst;                       // stages of the whole pass
+  // the second unit: rows and words past the first (kU = 2)
+  const int rdu = kU == 2 ? (c.unit2 - c.unit) * 64 : 0;
+  const int64_t du = (int64_t)rdu * C;
   // rows of C words start on 128-byte lines when every expert's matrix does
   bool line_aligned = (C * 4) % 128 == 0;
 #pragma unroll
@@ -385,9 +399,10 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
       const int64_t row = rows0[T] + (lane >> 2);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int piece = 4 * h + (lane & 3);
+        // kU = 2 (P <= 4): half h holds unit h's pieces
+        const int piece = kU == 2 ? (lane & 3) : 4 * h + (lane & 3);
         const int pc = piece < P ? piece : 0;      // a valid address; the value is unused
-        const int64_t at = e * m.stride_sb + row * G + pc * 8;
+        const int64_t at = e * m.stride_sb + (row + (h == 1 ? rdu : 0)) * G + pc * 8;
         sbs[T][h] = *reinterpret_cast<const uint4*>(m.s + at);
         sbb[T][h] = *reinterpret_cast<const uint4*>(m.b + at);
       }
@@ -417,9 +432,9 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
         dma4_to_lds(a.pair_list + c.pb + min(m0 + lane, ne - 1), lpair);
     }
     issue_words<NT>(S, ring, 0, G, wave, lane, line_aligned);
-    if (kRingN >= 3 && nst > 1) issue_words<NT>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
+    if (kRingN >= 3 && nstT > 1) issue_words<NT>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
     // the pair ids landed (the words of the prologue stages behind them)
-    if (kRingN >= 3 && nst > 1) wait_vmcnt<2 * kTiles>();
+    if (kRingN >= 3 && nstT > 1) wait_vmcnt<2 * kTiles>();
     else wait_vmcnt<kTiles>();
     // the token scales a_t of the pairs this lane's accumulators hold (pair
     // slots 16 n + 4 lg + i), used in the epilogue only: one token tile reads
@@ -454,7 +469,7 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
         }
       }
     }
-    floatx4 acc[kTiles][NT];
+    floatx4 acc[kTiles][NT], acc1[kTiles][NT];     // acc1: the first unit's, when kU = 2
 #pragma unroll
     for (int T = 0; T < kTiles; ++T)
 #pragma unroll
@@ -462,31 +477,44 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
     SBRegs regs;
 
     issue_rest<kGateUp, kFastSB, NT>(S, ring, 0, G, wave, lane);
-    if (kRingN >= 3 && nst > 1) issue_rest<kGateUp, kFastSB, NT>(S, ring + kSlot, 1, G, wave, lane);
-    // stages in fours so that the stage's place in its four is a constant
-    for (int ks = 0; ks < nst; ks += kSuper) {
+    if (kRingN >= 3 && nstT > 1) issue_rest<kGateUp, kFastSB, NT>(S, ring + kSlot, 1, G, wave, lane);
+    // stages in fours so that the stage's place in its four is a constant (with
+    // two units, nst is a multiple of four: the place is the same in either)
+    for (int ks = 0; ks < nstT; ks += kSuper) {
 #define SMOE_MFMA_STAGE(kk)                                                                       \
-      if (ks + kk < nst) {                                                                        \
+      if (ks + kk < nstT) {                                                                       \
         const int k = ks + kk;                                                                    \
-        wait_stage<kRest, kStage, kRingN>(k, nst);  /* this wave's copies of stage k landed */    \
+        const int ui = (kU == 2 && k >= nst) ? 1 : 0;  /* unit of stage k, its stage kl */        \
+        const int kl = k - ui * nst;                                                              \
+        wait_stage<kRest, kStage, kRingN>(k, nstT);  /* this wave's copies of stage k landed */   \
         const int kn = k + kRingN - 1;  /* the stage whose copies go out now */                   \
+        const int un = (kU == 2 && kn >= nst) ? 1 : 0;                                            \
+        const int knl = kn - un * nst;                                                            \
         /* this wave's words of stage kn go to its own part of slot k-1, which */                \
         /* only it reads (its compute of k-1 is done): no need to wait for the others */         \
-        if (kn < nst)                                                                             \
-          issue_words<NT>(S, ring + (kn % kRingN) * kSlot, kn, G, wave, lane, line_aligned);      \
+        if (kn < nstT)                                                                            \
+          issue_words<NT>(S, ring + (kn % kRingN) * kSlot, knl, G, wave, lane, line_aligned,      \
+                          un * du);                                                               \
         barrier_no_wait();           /* every wave's copies of k landed; slot k-1 is free */      \
-        if (kn < nst)                                                                             \
-          issue_rest<kGateUp, kFastSB, NT>(S, ring + (kn % kRingN) * kSlot, kn, G, wave, lane);   \
+        if (kn < nstT)                                                                            \
+          issue_rest<kGateUp, kFastSB, NT>(S, ring + (kn % kRingN) * kSlot, knl, G, wave, lane);  \
         if (kFastSB && kk == 0) {                                                                 \
-          const int j = k / kSuper;                  /* groups 8j .. 8j+7: piece j */             \
+          const int j = kl / kSuper;                 /* groups 8j .. 8j+7: piece j */             \
           const int src = (col * 4 + (j & 3)) * 4;   /* lane holding this row's piece j */        \
+          const int hh = kU == 2 ? ui : (j < 4 ? 0 : 1);                                          \
           _Pragma("unroll") for (int T = 0; T < kTiles; ++T) {                                   \
-            regs.s[T] = bpermute4(src, j < 4 ? sbs[T][0] : sbs[T][1]);                            \
-            regs.b[T] = bpermute4(src, j < 4 ? sbb[T][0] : sbb[T][1]);                            \
+            regs.s[T] = bpermute4(src, hh == 0 ? sbs[T][0] : sbs[T][1]);                          \
+            regs.b[T] = bpermute4(src, hh == 0 ? sbb[T][0] : sbb[T][1]);                          \
           }                                                                                       \
         }                                                                                         \
-        compute_stage<kGateUp, kFastSB, NT, kk>(ring + (k % kRingN) * kSlot, k, G, wave, col, lg, \
-                                                regs, parity, acc);                               \
+        if (kU == 2 && k == nst) {   /* the second unit starts: hold the first's sums */          \
+          _Pragma("unroll") for (int T = 0; T < kTiles; ++T) {                                   \
+            acc1[T][0] = acc[T][0];                                                               \
+            acc[T][0] = floatx4{0.f, 0.f, 0.f, 0.f};                                              \
+          }                                                                                       \
+        }                                                                                         \
+        compute_stage<kGateUp, kFastSB, NT, kk>(ring + (k % kRingN) * kSlot, kl, G, wave, col,    \
+                                                lg, regs, parity, acc);                           \
       }
       SMOE_MFMA_STAGE(0)
       SMOE_MFMA_STAGE(1)
@@ -538,7 +566,8 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
           }
         }
       } else {
-        // h held a_t^2 h: 1/a_t^2 (exact) gives the outputs
+        // h held a_t^2 h: 1/a_t^2 (exact) gives the outputs (kU = 2: the
+        // first unit from its held sums, the second one rdu rows further)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ms = 16 * n + 4 * lg + i;
@@ -546,7 +575,13 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
           if (m0 + ms < ne) {
 #pragma unroll
             for (int T = 0; T < kTiles; ++T)
-              c.yout[(int64_t)lpair[ms] * a.d + rows0[T] + col] = acc[T][n][i] * ib;
+              c.yout[(int64_t)lpair[ms] * a.d + rows0[T] + col] =
+                  (kU == 2 ? acc1[T][n][i] : acc[T][n][i]) * ib;
+            if (kU == 2 && c.has_unit2) {
+#pragma unroll
+              for (int T = 0; T < kTiles; ++T)
+                c.yout[(int64_t)lpair[ms] * a.d + rows0[T] + rdu + col] = acc[T][n][i] * ib;
+            }
           }
         }
       }
@@ -554,7 +589,9 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
   }
 }
 
-template <bool kGateUp, bool kFastSB>
+// kU = 2 (down only): every wave takes two units, four apart, so that a
+// block covers 4 kU units.
+template <bool kGateUp, bool kFastSB, int kU>
 __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   __shared__ __align__(16) char ring[ring_bytes<kFastSB>()];
   __shared__ int lpair_w[kWaves][kPairTile * kMaxTiles];   // each wave's copy of the pass's pair ids
@@ -565,7 +602,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   // its blocks serve the most pairs.
   const int units_r = kGateUp ? a.f / 32 : a.d / 64;
   const int units_s = kGateUp ? a.fs / 32 : a.d / 64;
-  const int gx_r = (units_r + kWaves - 1) / kWaves, gx_s = (units_s + kWaves - 1) / kWaves;
+  constexpr int kUB = kWaves * kU;                // units a block
+  const int gx_r = (units_r + kUB - 1) / kUB, gx_s = (units_s + kUB - 1) / kUB;
   const int n_sh = a.fs > 0 ? 1 : 0;
   const int b_lin = blockIdx.x;
   const bool sh = b_lin < n_sh * gx_s;
@@ -597,13 +635,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_ffn_mfma(FfnArgs a) {
   // last one (they take part in the shared copies and barriers) and write nothing
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int units = sh ? units_s : units_r;
-  c.has_unit = bx * kWaves + wave < units;
-  c.unit = min(bx * kWaves + wave, units - 1);
+  c.has_unit = bx * kUB + wave < units;
+  c.unit = min(bx * kUB + wave, units - 1);
+  c.has_unit2 = kU == 2 && bx * kUB + kWaves + wave < units;
+  c.unit2 = kU == 2 ? min(bx * kUB + kWaves + wave, units - 1) : c.unit;
   int* lpair = lpair_w[wave];
-  if (__builtin_amdgcn_readfirstlane(c.ne) > kPairTile)
+  if (__builtin_amdgcn_readfirstlane(c.ne) > kPairTile) {
+    // the wide pass, unit by unit
     ffn_pass<kGateUp, false, kMaxTiles, 2>(a, c, ring, lpair);
-  else
-    ffn_pass<kGateUp, kFastSB, 1, 3>(a, c, ring, lpair);
+    if (kU == 2) {
+      PassCtx c2 = c;
+      c2.unit = c.unit2;
+      c2.has_unit = c.has_unit2;
+      ffn_pass<kGateUp, false, kMaxTiles, 2>(a, c2, ring, lpair);
+    }
+  } else {
+    ffn_pass<kGateUp, kFastSB, 1, 3, kU>(a, c, ring, lpair);
+  }
 }
 
 // 16-byte scale/bias copies need 8 | G, 8 | stride and 16-byte aligned bases
@@ -622,20 +670,28 @@ hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up, const 
   const int n_sh = shared ? 1 : 0;
   const int units_r = gate_up ? a.f / 32 : a.d / 64;
   const int units_s = gate_up ? a.fs / 32 : a.d / 64;
-  const int gx_r = (units_r + kWaves - 1) / kWaves, gx_s = (units_s + kWaves - 1) / kWaves;
+  // down with scales and biases in registers over 8, 16, 24 or 32 groups:
+  // two units a wave
+  auto two_units_ok = [](int K) { return K % 512 == 0 && K <= 2048; };
+  const bool fast_dn = !gate_up && fast_sb_ok(a.down, a.f / 64) && (!shared || fast_sb_ok(a.sdown, a.fs / 64));
+  const int kU = fast_dn && two_units_ok(a.f) && (!shared || two_units_ok(a.fs)) ? 2 : 1;
+  const int gx_r = (units_r + kWaves * kU - 1) / (kWaves * kU);
+  const int gx_s = (units_s + kWaves * kU - 1) / (kWaves * kU);
   const dim3 grid(n_sh * gx_s + max_union * gx_r);
   if (gate_up) {
     const bool fast = fast_sb_ok(a.gate, a.d / 64) && fast_sb_ok(a.up, a.d / 64) &&
                       (!shared || (fast_sb_ok(a.sgate, a.d / 64) && fast_sb_ok(a.sup, a.d / 64)));
     if (fast)
-      SMOE_LAUNCH(t, (k_ffn_mfma<true, true>), grid, dim3(kThreads), 0, s, a);
+      SMOE_LAUNCH(t, (k_ffn_mfma<true, true, 1>), grid, dim3(kThreads), 0, s, a);
     else
-      SMOE_LAUNCH(t, (k_ffn_mfma<true, false>), grid, dim3(kThreads), 0, s, a);
+      SMOE_LAUNCH(t, (k_ffn_mfma<true, false, 1>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if (fast_sb_ok(a.down, a.f / 64) && (!shared || fast_sb_ok(a.sdown, a.fs / 64)))
-      SMOE_LAUNCH(t, (k_ffn_mfma<false, true>), grid, dim3(kThreads), 0, s, a);
+    if (kU == 2)
+      SMOE_LAUNCH(t, (k_ffn_mfma<false, true, 2>), grid, dim3(kThreads), 0, s, a);
+    else if (fast_dn)
+      SMOE_LAUNCH(t, (k_ffn_mfma<false, true, 1>), grid, dim3(kThreads), 0, s, a);
     else
-      SMOE_LAUNCH(t, (k_ffn_mfma<false, false>), grid, dim3(kThreads), 0, s, a);
+      SMOE_LAUNCH(t, (k_ffn_mfma<false, false, 1>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -25,9 +25,9 @@
 namespace smoe {
 namespace {
 
-constexpr int kRouteThreads = 256;              // 4 waves: 4 experts per block
+constexpr int kRouteThreads = 256;              // 4 waves a block
 static_assert(kRouteThreads == 256, "block_row_inv needs blocks of 256 threads");
-constexpr int kMaxRouteTok = 2;            // k_route's batches; larger ones are tiled
+constexpr int kMaxRouteTok = 2;                 // k_route's batches; larger ones are tiled
 constexpr int kTailThreads = 1024;              // stand-alone top-k / union block
 constexpr int kTopkThreads = 256;               // top-k grid: one token per wave
 constexpr int kMaxTicketBlocks = 64;            // larger grids hand the tail to its own kernel

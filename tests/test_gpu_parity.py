@@ -235,6 +235,10 @@ FWD_CASES = [
     (small_config("dec_d6144", 6144, 16, 8, 1536, 1), 1, True),        # 96 groups: 2 a lane, 32 idle
     (small_config("dec_d8192_b2", 8192, 8, 4, 512, 2), 2, True),       # 128 groups: 2 a lane
     (small_config("dec_d8192_b1", 8192, 8, 8, 2048, 1), 1, False),
+    # down with f of 512 .. 2048 (a multiple of 512): two units a wave
+    (small_config("two_units_ragged", 640, 12, 4, 512, 13), 13, True),    # 10 units: second ones cut
+    (small_config("two_units_f2048", 1536, 16, 4, 2048, 9, bf16=False), 9, False),
+    (small_config("two_units_shared", 1024, 16, 4, 1024, 37, shared=2048), 37, True),
     # with a shared expert
     (small_config("s_fwd_dec2", 2048, 32, 8, 512, 2, shared=2560), 2, True),
     (small_config("s_fwd_odd", 512, 24, 6, 192, 13, shared=320), 13, True),   # 5 groups
@@ -268,6 +272,8 @@ SKEW_CASES = [
     (small_config("skew_hot48_s", 2048, 64, 8, 512, 48, shared=256), 48, "hot"),
     (small_config("skew_all17_fused", 1024, 16, 2, 192, 17, fused=True), 17, "all"),
     (small_config("skew_hot64_nof", 512, 40, 6, 320, 64, bf16=False), 64, "hot"),
+    # two units a wave (f = 1024): the wide pass runs unit by unit
+    (small_config("skew_hot64_two_units", 1536, 32, 4, 1024, 64, shared=512), 64, "hot"),
 ]
 
 
