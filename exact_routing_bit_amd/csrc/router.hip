@@ -143,18 +143,34 @@ struct UnionSmem {
   int32_t idx[kMaxPairs];
   int32_t hist[kMaxExperts];
   int32_t pos[kMaxExperts];
-  uint32_t mask[kMaxExperts * (kMaxPairs / 32)];
+  alignas(16) uint32_t mask[kMaxExperts * (kMaxPairs / 32)];   // rows of 16-byte pieces
+  alignas(16) uint16_t before[kMaxExperts * (kMaxPairs / 32)];  // the row's bits in earlier words
   TopkScratch topk[16];   // one per wave (blocks of up to 1024 threads)
 };
 
+// Inclusive prefix sum over the wave (lane order), by DPP: shifts of 1, 2,
+// 4, 8 within rows of 16, then row 0's total into row 1 and row 2's into row
+// 3, then row 1's into rows 2 and 3.  Lanes whose source lies outside the
+// row read 0.  Every lane of the wave must be active.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2, 3
+  return v;
+}
+
 // Union of the batch's experts and the per-expert pair lists, by one block
-// (any size that is a multiple of 64) from us->idx[0..P).
+// (a multiple of 64 threads, at least two waves) from us->idx[0..P).
 __device__ __forceinline__ void build_union(const RouteArgs& a, UnionSmem* us) {
   const int nthr = blockDim.x, tid = threadIdx.x;
   const int E = a.E, P = a.B * a.K;
-  const int W = (P + 31) / 32;
+  const int W = ((P + 31) / 32 + 3) & ~3;         // mask words an expert: whole 16-byte pieces
   for (int i = tid; i < E; i += nthr) us->hist[i] = 0;
-  for (int i = tid; i < E * W; i += nthr) us->mask[i] = 0u;
+  for (int i = tid; i < E * W / 4; i += nthr)
+    reinterpret_cast<uint4*>(us->mask)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   for (int p = tid; p < P; p += nthr) {
     const int e = us->idx[p];
@@ -167,6 +183,25 @@ __device__ __forceinline__ void build_union(const RouteArgs& a, UnionSmem* us) {
     }
   }
   __syncthreads();
+  // (blocks of at least two waves) the waves past the first count, for every
+  // expert row and mask word, the row's bits in the words before it, while
+  // the first wave scans the experts
+  for (int e = tid - 64; e >= 0 && e < E; e += nthr - 64) {
+    const uint4* m4 = reinterpret_cast<const uint4*>(us->mask + e * W);
+    uint16_t* b = us->before + e * W;
+    int run = 0;
+    for (int i = 0; i < W / 4; ++i) {
+      const uint4 v = m4[i];
+      b[4 * i] = (uint16_t)run;
+      run += __popc(v.x);
+      b[4 * i + 1] = (uint16_t)run;
+      run += __popc(v.y);
+      b[4 * i + 2] = (uint16_t)run;
+      run += __popc(v.z);
+      b[4 * i + 3] = (uint16_t)run;
+      run += __popc(v.w);
+    }
+  }
   if (tid < 64) {
     // exclusive scans of pair counts and of non-empty experts; lane l owns experts 4l..4l+3
     const int lane = tid;
@@ -178,11 +213,7 @@ __device__ __forceinline__ void build_union(const RouteArgs& a, UnionSmem* us) {
       cnt += c[j];
       nz += c[j] > 0;
     }
-    int inc_c = cnt, inc_nz = nz;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(inc_c, off, 64), onz = __shfl_up(inc_nz, off, 64);
-      if (lane >= off) { inc_c += oc; inc_nz += onz; }
-    }
+    const int inc_c = wave_scan_incl(cnt), inc_nz = wave_scan_incl(nz);
     int pos = inc_c - cnt, uid = inc_nz - nz;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -204,9 +235,10 @@ __device__ __forceinline__ void build_union(const RouteArgs& a, UnionSmem* us) {
   for (int p = tid; p < P; p += nthr) {
     const int e = us->idx[p];
     if (e < 0 || e >= E) continue;
-    const uint32_t* m = us->mask + e * W;
-    int rank = __popc(m[p >> 5] & ((1u << (p & 31)) - 1u));
-    for (int i = 0; i < (p >> 5); ++i) rank += __popc(m[i]);
+    // rank = the expert's pairs before p: its bits in the words before p's,
+    // then those below p in p's own word
+    const int at = e * W + (p >> 5);
+    const int rank = us->before[at] + __popc(us->mask[at] & ((1u << (p & 31)) - 1u));
     const int q = us->pos[e] + rank;
     a.pair_list[q] = p;
     a.pair_pos[p] = q;
