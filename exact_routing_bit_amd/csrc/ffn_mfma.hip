@@ -671,10 +671,13 @@ hipError_t launch_ffn_mfma(const FfnArgs& a, hipStream_t s, bool gate_up, const 
   const int units_r = gate_up ? a.f / 32 : a.d / 64;
   const int units_s = gate_up ? a.fs / 32 : a.d / 64;
   // down with scales and biases in registers over 8, 16, 24 or 32 groups:
-  // two units a wave
+  // two units a wave.  Not with a shared expert on its wide pass (more than
+  // 16 tokens): its blocks, which serve every token and take the longest,
+  // would run their two units one after the other.
   auto two_units_ok = [](int K) { return K % 512 == 0 && K <= 2048; };
   const bool fast_dn = !gate_up && fast_sb_ok(a.down, a.f / 64) && (!shared || fast_sb_ok(a.sdown, a.fs / 64));
-  const int kU = fast_dn && two_units_ok(a.f) && (!shared || two_units_ok(a.fs)) ? 2 : 1;
+  const int kU =
+      fast_dn && two_units_ok(a.f) && (!shared || (two_units_ok(a.fs) && a.B <= kPairTile)) ? 2 : 1;
   const int gx_r = (units_r + kWaves * kU - 1) / (kWaves * kU);
   const int gx_s = (units_s + kWaves * kU - 1) / (kWaves * kU);
   const dim3 grid(n_sh * gx_s + max_union * gx_r);

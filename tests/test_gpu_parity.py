@@ -238,7 +238,8 @@ FWD_CASES = [
     # down with f of 512 .. 2048 (a multiple of 512): two units a wave
     (small_config("two_units_ragged", 640, 12, 4, 512, 13), 13, True),    # 10 units: second ones cut
     (small_config("two_units_f2048", 1536, 16, 4, 2048, 9, bf16=False), 9, False),
-    (small_config("two_units_shared", 1024, 16, 4, 1024, 37, shared=2048), 37, True),
+    (small_config("two_units_shared", 1024, 16, 4, 1024, 13, shared=2048), 13, True),
+    (small_config("one_unit_shared_wide", 1024, 16, 4, 1024, 37, shared=2048), 37, True),
     # with a shared expert
     (small_config("s_fwd_dec2", 2048, 32, 8, 512, 2, shared=2560), 2, True),
     (small_config("s_fwd_odd", 512, 24, 6, 192, 13, shared=320), 13, True),   # 5 groups
@@ -273,7 +274,7 @@ SKEW_CASES = [
     (small_config("skew_all17_fused", 1024, 16, 2, 192, 17, fused=True), 17, "all"),
     (small_config("skew_hot64_nof", 512, 40, 6, 320, 64, bf16=False), 64, "hot"),
     # two units a wave (f = 1024): the wide pass runs unit by unit
-    (small_config("skew_hot64_two_units", 1536, 32, 4, 1024, 64, shared=512), 64, "hot"),
+    (small_config("skew_hot64_two_units", 1536, 32, 4, 1024, 64), 64, "hot"),
 ]
 
 
@@ -328,6 +329,8 @@ SHARED_CASES = [
     (small_config("s_pref64", 1024, 64, 8, 256, 64, shared=512), 64),
     (small_config("s_pref37_narrow", 1024, 32, 4, 512, 37, fused=True, shared=256), 37),
     (small_config("s_pref5_fs6144", 1024, 16, 2, 128, 5, shared=6144), 5),
+    # f = 1536 beside a shared expert on its wide pass: one unit a wave
+    (small_config("s_pref24_fs3072", 1024, 16, 4, 1536, 24, shared=3072), 24),
 ]
 
 
