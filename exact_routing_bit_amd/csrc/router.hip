@@ -148,6 +148,8 @@ struct UnionSmem {
   TopkScratch topk[16];   // one per wave (blocks of up to 1024 threads)
 };
 
+static_assert(sizeof(UnionSmem) <= 64 * 1024, "the router's tail takes it as dynamic LDS");
+
 // Inclusive prefix sum over the wave (lane order), by DPP: shifts of 1, 2,
 // 4, 8 within rows of 16, then row 0's total into row 1 and row 2's into row
 // 3, then row 1's into rows 2 and 3.  Lanes whose source lies outside the
@@ -345,11 +347,12 @@ inline int route_pieces(int d) { return d <= 2048 ? 1 : d <= 4096 ? 2 : 4; }
 // B <= 2 tokens (NT = B), one grid row: blocks [0, B) prep a token's
 // activations (prep_token), blocks B .. B + E - 1 form the logits of one
 // expert each (logits_block).  do_tail: the last block to finish ranks and
-// builds the union.
+// builds the union, in dynamic LDS of sizeof(UnionSmem) bytes that only such
+// launches ask for (the decode layer's router needs none).
 template <bool kBf16, int NT, int kM>
 __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tail,
                                                          uint32_t* ticket) {
-  __shared__ UnionSmem us;
+  extern __shared__ __align__(16) char route_dyn[];
   __shared__ int is_last;
   __shared__ float part[kRouteThreads / 64][NT];
   if ((int)blockIdx.x < NT) {
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(RouteArgs a, int do_tai
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  route_tail(a, true, a.n_union != nullptr, &us);
+  route_tail(a, true, a.n_union != nullptr, reinterpret_cast<UnionSmem*>(route_dyn));
 }
 
 // ------------------------------------------------ tiled logits (B >= 3)
@@ -675,8 +678,9 @@ hipError_t launch_router(const RouteArgs& a, bool logits_in, bool do_topk, bool 
     const bool fused = (do_topk || do_union) && (int)grid.x <= kMaxTicketBlocks;
     uint32_t* ticket = a.status + 1;
     const int pieces = route_pieces(a.d);
+    const size_t tail_lds = fused ? sizeof(UnionSmem) : 0;
 #define SMOE_ROUTE(BF, NT, M) \
-  SMOE_LAUNCH(t, (k_route<BF, NT, M>), grid, dim3(kRouteThreads), 0, s, r, (int)fused, ticket)
+  SMOE_LAUNCH(t, (k_route<BF, NT, M>), grid, dim3(kRouteThreads), tail_lds, s, r, (int)fused, ticket)
 #define SMOE_ROUTE_M(BF, NT)                  \
   do {                                        \
     if (pieces == 1) SMOE_ROUTE(BF, NT, 1);   \
