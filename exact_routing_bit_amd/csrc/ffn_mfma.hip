@@ -386,10 +386,28 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
     const QMat& m = kGateUp ? (T < 2 ? qg : qu) : qd;
     line_aligned = line_aligned && (reinterpret_cast<uintptr_t>(m.w + e * m.stride_w) & 127) == 0;
   }
-  // kFastSB: this wave's scales and biases for the whole K loop, read once as
-  // contiguous runs (lane l: row rows0[T] + l/4, 16-byte piece 4h + l%4 of the
-  // row's G/8), not as 16-byte pieces of 64 rows per four stages; each group
-  // of four stages hands every lane its rows' piece with ds_bpermute
+  // One pass: the narrow pass serves at most 16 pairs and the wide one at
+  // most 64, every token of a chunk (pass m0 = 0 of 16 NT pair slots).
+  constexpr int m0 = 0;
+  __syncthreads();                                 // a previous pass is done with the ring
+  // The start's three independent reads go out together instead of one after
+  // another: the pass's pair ids (copied like the rest, so that no
+  // compiler-counted load sits behind the copies; lane L: pair slot L of the
+  // 16 NT), the first stages' words (they need only the expert) and, with
+  // kFastSB, this wave's scales and biases for the whole K loop.  Those are
+  // read once as contiguous runs (lane l: row rows0[T] + l/4, 16-byte piece
+  // 4h + l%4 of the row's G/8), not as 16-byte pieces of 64 rows per four
+  // stages; each group of four stages hands every lane its rows' piece with
+  // ds_bpermute.  They are the last loads issued, so the compiler's wait for
+  // them (it counts only its own loads) also covers the copies before them.
+  if (lane < kPairTile * NT) {
+    if (c.sh)
+      lpair[lane] = min(m0 + lane, ne - 1);        // the shared expert's pairs are the tokens
+    else
+      dma4_to_lds(a.pair_list + c.pb + min(m0 + lane, ne - 1), lpair);
+  }
+  issue_words<NT>(S, ring, 0, G, wave, lane, line_aligned);
+  if (kRingN >= 3 && nstT > 1) issue_words<NT>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
   uint4 sbs[kTiles][2], sbb[kTiles][2];
   if (kFastSB) {
     const int P = G / 8;                           // <= 8 pieces a row (G <= 64)
@@ -407,9 +425,7 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
         sbb[T][h] = *reinterpret_cast<const uint4*>(m.b + at);
       }
     }
-    // wait for them here, before any copy is in flight: the compiler does not
-    // count the copies (inline assembly), so its wait at their first use
-    // would otherwise be vmcnt(0) behind the stages of copies
+    // wait for them here, while only these copies are in flight
 #pragma unroll
     for (int T = 0; T < kTiles; ++T)
 #pragma unroll
@@ -418,21 +434,7 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
         asm volatile("" ::"v"(sbb[T][h].x), "v"(sbb[T][h].y), "v"(sbb[T][h].z), "v"(sbb[T][h].w));
       }
   }
-
-  for (int m0 = 0; m0 < ne; m0 += kPairTile * NT) {
-    __syncthreads();                               // the previous pass is done with the ring
-    // the pass's pair ids (copied like the rest, so that no compiler-counted
-    // load sits behind the copies; lane L: pair slot L of the 16 NT), then
-    // the first stages' words, which need only the expert; the wait covers
-    // the ids alone
-    if (lane < kPairTile * NT) {
-      if (c.sh)
-        lpair[lane] = min(m0 + lane, ne - 1);      // the shared expert's pairs are the tokens
-      else
-        dma4_to_lds(a.pair_list + c.pb + min(m0 + lane, ne - 1), lpair);
-    }
-    issue_words<NT>(S, ring, 0, G, wave, lane, line_aligned);
-    if (kRingN >= 3 && nstT > 1) issue_words<NT>(S, ring + kSlot, 1, G, wave, lane, line_aligned);
+  {
     // the pair ids landed (the words of the prologue stages behind them)
     if (kRingN >= 3 && nstT > 1) wait_vmcnt<2 * kTiles>();
     else wait_vmcnt<kTiles>();
@@ -522,7 +524,7 @@ __device__ __forceinline__ void ffn_pass(const FfnArgs& a, const PassCtx& c, cha
       SMOE_MFMA_STAGE(3)
 #undef SMOE_MFMA_STAGE
     }
-    if (!c.has_unit) continue;
+    if (!c.has_unit) return;
 
     // epilogue: lane holds (pair slot m0 + 16 n + 4 lg + i, row rows0[T] + col)
 #pragma unroll

@@ -373,6 +373,63 @@ def test_layer_parity(smoe, cfg, B):
     assert np.array_equal(down(un.pair_pos)[:B * cfg.top_k], pp)
 
 
+def _bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("cfg,B,mode", [
+    # every token on the same 4 experts: 4 experts x 64 pairs (wide pass)
+    (small_config("lsk_all", 1024, 32, 4, 256, 64), 64, "all"),
+    # half the tokens on 8 hot experts (32+ pairs each), the rest spread
+    (small_config("lsk_half_s", 2048, 64, 8, 512, 64, shared=256), 64, "half"),
+    # the 256-expert fused layout with 2 hot experts at 48 tokens
+    (small_config("lsk_fused", 1024, 256, 8, 512, 48, fused=True), 48, "half"),
+], ids=lambda v: getattr(v, "name", str(v)))
+def test_layer_parity_skewed_router(smoe, cfg, B, mode):
+    """The whole layer (the GPU's own routing) with a router that sends many
+    tokens to a few experts: hot rows of the gate share a direction c that
+    the hot tokens' hidden states carry, so those experts serve 17..64 pairs
+    (the wide pass) while the rest serve few.  Checked against the oracle's
+    routing and layer, and the union outputs against the oracle's union."""
+    L = synth.make_layer(cfg)
+    d, E, K = cfg.d_model, cfg.num_experts, cfg.top_k
+    n_hot = K if mode == "all" else max(2, K // 4) if E > 64 else K
+    z = synth.hidden(cfg.seed, 0, 6, B, d).astype(np.float64)
+    c = synth.hidden(cfg.seed, 0, 7, 1, d)[0].astype(np.float64)
+    hot_tok = np.arange(B) if mode == "all" else np.arange(0, B, 2)
+    z[hot_tok] += 3.0 * c
+    x = (z / np.sqrt(np.mean(z * z, axis=1, keepdims=True) + 1e-6)).astype(np.float32)
+    rng = np.random.default_rng(11)
+    wr = rng.standard_normal((E, d)) / np.sqrt(d)
+    hot_exp = rng.choice(E, n_hot, replace=False)
+    wr[hot_exp] = 0.5 * c / np.sqrt(d) + rng.standard_normal((n_hot, d)) / np.sqrt(d)
+    L["router"] = _bf16_bits(wr)
+    ref, idx_ref, w_ref = oracle_layer(L, x, cfg)
+    lg_ref = oracle.router_logits(L["router"], x)
+    counts = np.bincount(idx_ref.ravel(), minlength=E)
+    assert counts.max() > 16, counts.max()            # some expert takes the wide pass
+    desc = desc_for(smoe, cfg)
+    layer = smoe.Layer(desc, device_weights(L), max_batch=B, device=dev())
+    out = down(layer.forward(up(x), want_logits=True))
+    idx = down(layer.topk_idx[:B])
+    bad = [t for t in range(B) if not np.array_equal(idx[t], idx_ref[t])]
+    for t in bad:
+        assert near_tie(lg_ref[t], K), f"routing differs for token {t}"
+    if bad:
+        w = oracle.weights_of(lg_ref, idx, cfg.norm_topk_prob)
+        ref, _, _ = oracle_layer(L, x, cfg, idx=idx, w=w)
+    assert_layer_close(out, ref, TOL)
+    n, ue, off, pl, pp = oracle.build_union(idx, E)
+    un = layer.union
+    assert int(down(un.n_union)[0]) == n
+    assert np.array_equal(down(un.union_experts)[:n], ue)
+    assert np.array_equal(down(un.expert_offsets)[:n + 1], off)
+    assert np.array_equal(down(un.pair_list)[:B * K], pl)
+    assert np.array_equal(down(un.pair_pos)[:B * K], pp)
+
+
 @pytest.mark.parametrize("cfg,B", [SHARED_CASES[0], SHARED_CASES[1], SHARED_CASES[6],
                                    SHARED_CASES[8]], ids=lambda v: getattr(v, "name", str(v)))
 def test_shared_zero_weights_leave_the_routed_layer(smoe, cfg, B):
