@@ -279,11 +279,36 @@ def stream_read_calibration(smoe):
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 1e3 / n
         out[f"{per_cu}_blocks_per_cu"] = round(STREAM_BYTES / t / 1e9, 1)
+    # the direct global -> LDS copy path of the prefill FFN kernels, on rows of
+    # the decode/prefill layer's gate_up (d = 4096: 2048 B) and down (f = 1536:
+    # 768 B) matrices, in the kernels' pattern and in memory order
+    dma = {}
+    for row_bytes in (2048, 768):
+        units = STREAM_BYTES // (64 * row_bytes)
+        nbytes = units * 64 * row_bytes
+        sink = torch.zeros((units + 3) // 4, dtype=torch.int32, device=dev)
+        r = {}
+        for mode, name in ((0, "ffn_pattern_gbps"), (1, "memory_order_gbps")):
+            for _ in range(3):
+                smoe.dma_read(buf, sink, row_bytes, mode, nbytes=nbytes)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            n = 10
+            e0.record()
+            for _ in range(n):
+                smoe.dma_read(buf, sink, row_bytes, mode, nbytes=nbytes)
+            e1.record()
+            torch.cuda.synchronize()
+            r[name] = round(nbytes / (e0.elapsed_time(e1) / 1e3 / n) / 1e9, 1)
+        dma[f"rows_{row_bytes}B"] = r
     del buf
     torch.cuda.empty_cache()
     best = max(out.values())
     return {"kernel": "k_stream_read (smoe_stream_read)", "bytes": STREAM_BYTES,
-            "gbps_by_grid": out, "best_gbps": best, "best_frac": round(best / HBM_PEAK_GBPS, 4)}
+            "gbps_by_grid": out, "best_gbps": best, "best_frac": round(best / HBM_PEAK_GBPS, 4),
+            "dma_read": {"kernel": "k_dma_read (smoe_dma_read): global -> LDS copies, three "
+                                   "4 KB stages a wave, two workgroups of four waves per CU",
+                         **dma}}
 
 
 def sync_calibration(smoe):

@@ -37,7 +37,7 @@ EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_ro
             "smoe_stack_forward", "smoe_read_status", "smoe_strerror",
             "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage",
             "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes", "smoe_stream_read",
-            "smoe_empty_launch", "smoe_grid_barrier")
+            "smoe_empty_launch", "smoe_grid_barrier", "smoe_dma_read")
 
 
 class SmoeError(RuntimeError):
@@ -96,6 +96,7 @@ def _load():
                                          vp, ctypes.POINTER(Union), vp]
     L.smoe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     L.smoe_empty_launch.argtypes = [i32, i32, vp]
+    L.smoe_dma_read.argtypes = [vp, sz, i32, i32, vp, i32, vp]
     L.smoe_grid_barrier.argtypes = [i32, vp, vp, vp, vp]
     L.smoe_noalloc_scratch_bytes.argtypes = []
     L.smoe_noalloc_scratch_bytes.restype = sz
@@ -340,6 +341,17 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes=None, stream=None)
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     _check(lib.smoe_stream_read(_ptr(buf, None, "buf"), n, _ptr(sink, torch.int32, "sink"),
                                 sink.numel(), _stream(stream)), "smoe_stream_read")
+
+
+def dma_read(buf: torch.Tensor, sink: torch.Tensor, row_bytes: int, mode: int, nbytes=None,
+             stream=None):
+    """Diagnostic stream of a device buffer through the direct global -> LDS
+    copy path (see smoe_dma_read): mode 0 the prefill FFN's pattern, 1 memory
+    order; sink is an int32 tensor of at least ceil(units / 4) entries."""
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    _check(lib.smoe_dma_read(_ptr(buf, None, "buf"), n, int(row_bytes), int(mode),
+                             _ptr(sink, torch.int32, "sink"), sink.numel(), _stream(stream)),
+           "smoe_dma_read")
 
 
 def empty_launch(blocks: int, count: int = 1, stream=None):

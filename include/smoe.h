@@ -364,6 +364,21 @@ int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers, const void
  * Async on stream; SMOE_EINVAL on bad arguments, 1 <= blocks <= 2^20. */
 int smoe_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
 
+/* Diagnostic: the direct global -> LDS copy path that the prefill FFN
+ * kernels stream their weights through ([LMP] "Choreography Per Chunk"
+ * step 6), with no arithmetic behind it.  `src` (16-byte aligned) is read as
+ * a [rows, row_bytes] matrix (row_bytes a multiple of 64 in 64 .. 65536;
+ * rows = bytes / row_bytes, whole 64-row units only); each wave streams one
+ * 64-row unit through a ring of three 4 KB stages in LDS, four waves a
+ * workgroup, two workgroups per compute unit.  mode 0: the FFN's pattern
+ * (stage k = bytes 64k .. 64k+63 of every row of the unit, 16-row tiles,
+ * the second half of each 128-byte line with the nontemporal hint); mode
+ * 1: the unit's bytes in memory order, 4 KB a stage.  Block b writes a xor
+ * of what it read to sink[b] (sink: sink_n uint32, device, at least
+ * ceil(units / 4)).  Async on stream; SMOE_EINVAL on bad arguments. */
+int smoe_dma_read(const void* src, size_t bytes, int32_t row_bytes, int32_t mode, uint32_t* sink,
+                  int32_t sink_n, void* stream);
+
 /* Diagnostic: `count` (0 .. 2^20) back-to-back launches, from this one
  * call, of a kernel of `blocks` (1 .. 2^20) workgroups of 64 threads that
  * does nothing; timed on the stream, the mean is the cost of one more

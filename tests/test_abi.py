@@ -297,6 +297,14 @@ def test_diagnostics_reject_bad_arguments(smoe):
     assert smoe.lib.smoe_empty_launch(0, 1, None) == smoe.SMOE_EINVAL
     assert smoe.lib.smoe_empty_launch((1 << 20) + 1, 1, None) == smoe.SMOE_EINVAL
     assert smoe.lib.smoe_empty_launch(8, -1, None) == smoe.SMOE_EINVAL
+    dr = smoe.lib.smoe_dma_read
+    assert dr(f, 1 << 20, 2048, 0, f, 1, None) == smoe.SMOE_EINVAL     # sink too small (2 blocks)
+    assert dr(f + 4, 1 << 20, 2048, 0, f, 64, None) == smoe.SMOE_EINVAL  # unaligned source
+    assert dr(f, 1 << 20, 2000, 0, f, 64, None) == smoe.SMOE_EINVAL     # row not whole 64 B
+    assert dr(f, 1 << 20, 2048, 2, f, 64, None) == smoe.SMOE_EINVAL     # no such mode
+    assert dr(None, 1 << 20, 2048, 0, f, 64, None) == smoe.SMOE_EINVAL
+    assert dr(f, 1 << 20, 2048, 1, None, 64, None) == smoe.SMOE_EINVAL
+    assert dr(f, 64 * 2048 - 1, 2048, 0, f, 1, None) == smoe.SMOE_OK    # no whole unit: nothing
     gb = smoe.lib.smoe_grid_barrier
     assert gb(0, f, f, f, None) == smoe.SMOE_EINVAL
     assert gb(4097, f, f, f, None) == smoe.SMOE_EINVAL
