@@ -40,6 +40,15 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "MoE-layer tokens/s and effective expert-weight GB/s (% HBM peak), B=1 and B=64"
 
 
+_T0 = time.time()
+
+
+def progress(msg):
+    """One line on stderr as each part of the run ends (the JSON line stays
+    the only thing on stdout)."""
+    print(f"bench: {msg} ({time.time() - _T0:.1f} s)", file=sys.stderr, flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -76,6 +85,12 @@ def parse():
                    help="write a per-kernel summary of rocprofv3 --pmc counter CSVs (any "
                         "counters; FETCH_SIZE/WRITE_SIZE scaled by the copy calibration) to OUT "
                         "and exit")
+    p.add_argument("--summarize-trace", nargs=4, metavar=("OUT", "LABEL", "COMMAND", "STATS_CSV"),
+                   help="write a rocprofv3 kernel_stats.csv as the per-kernel table in profiles/ "
+                        "(label and the command that made it in the header) and exit")
+    p.add_argument("--counter-command", default=None,
+                   help="with --summarize-counters: the command the rocprofv3 passes ran, for the "
+                        "summary's header")
     p.add_argument("--trace-csv", default=None,
                    help="with --summarize-counters: the kernel_stats.csv of the same command, "
                         "for kernel durations (MFMA rates)")
@@ -915,7 +930,8 @@ def _copy_scale(path, counter):
     return COPY_BYTES / (max(vals) * 1024.0), max(vals)
 
 
-def summarize_counters(out, label, copy_fetch_csv, copy_write_csv, *csvs, trace_csv=None):
+def summarize_counters(out, label, copy_fetch_csv, copy_write_csv, *csvs, trace_csv=None,
+                       command=None):
     """Per (kernel, grid size): the mean of every collected counter per
     dispatch.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are turned into
     HBM bytes with the scale that makes the same counter read a 1 GiB device
@@ -959,9 +975,24 @@ def summarize_counters(out, label, copy_fetch_csv, copy_write_csv, *csvs, trace_
             "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "lds_conflict_per_active",
             "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES",
             "GRBM_GUI_ACTIVE"]
+    if command:
+        passes = []
+        for i, pth in enumerate(csvs):
+            names = sorted({c for _, _, c, _, _ in _counter_rows(pth)})
+            passes.append(f"#   rocprofv3 --pmc {' '.join(names)} --output-format csv -d <out>/p{i} "
+                          f"-o p{i} -- {command}")
+        passes += [f"#   durations: rocprofv3 --kernel-trace --stats --output-format csv -d <out>/trace "
+                   f"-o t -- {command}",
+                   "#   copy scale: rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv "
+                   "... -- python3 bench.py --copy-calibration",
+                   "#   summary: python3 bench.py --summarize-counters <this file> <label> <copy fetch "
+                   "csv> <copy write csv> <pass csvs> --trace-csv <kernel_stats.csv> "
+                   "--counter-command '<command>'"]
+    else:
+        passes = [f"#   {p}" for p in csvs]
     lines = [f"# rocprofv3 --pmc counters per dispatch: {label}",
-             "# passes (one rocprofv3 run each, the same command):",
-             *[f"#   {p}" for p in csvs],
+             "# passes (one rocprofv3 run each, from /tmp, TMPDIR=/tmp):",
+             *passes,
              f"# FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}: the same counters "
              f"read {cf:.0f} / {cw:.0f} KiB for a {COPY_BYTES}-byte device copy "
              "(python3 bench.py --copy-calibration)",
@@ -1005,12 +1036,36 @@ def traffic_per_launch():
     return float(kv["traffic_bytes_per_launch"].split()[0])
 
 
+def summarize_trace(out, label, command, stats_csv):
+    """A kernel_stats.csv of rocprofv3 --kernel-trace --stats as a table of
+    per-kernel calls and durations (microseconds), longest total first."""
+    import csv
+    rows = []
+    with open(stats_csv) as fh:
+        for r in csv.DictReader(fh):
+            rows.append((short_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda t: -t[5])
+    lines = [f"# kernel trace: {label}", f"# command: {command}",
+             "# rocprofv3 --kernel-trace --stats (kernel_stats.csv), durations in microseconds", "",
+             f"{'kernel':70s} {'calls':>7s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'pct':>6s}"]
+    for k, c, a, lo, hi, pct in rows:
+        lines.append(f"{k[:70]:70s} {c:7d} {a:9.2f} {lo:9.2f} {hi:9.2f} {pct:6.2f}")
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.summarize_counters:
         if len(args.summarize_counters) < 5:
             raise SystemExit("--summarize-counters OUT LABEL COPY_FETCH_CSV COPY_WRITE_CSV CSV...")
-        summarize_counters(*args.summarize_counters, trace_csv=args.trace_csv)
+        summarize_counters(*args.summarize_counters, trace_csv=args.trace_csv,
+                           command=args.counter_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -1054,6 +1109,7 @@ def main():
         warm_pass(stack, [xs1, xs64])
     if "decode" in wl:
         main_e = layer_entry(stack, dec, xs1, args.steps, args.warmup)
+        progress("decode layer timed")
         gu = main_e["kernels_back_to_back"]["gate_up"]
         result = {
             "metric": METRIC, "value": main_e["tokens_per_s"], "unit": "tokens/s",
@@ -1075,6 +1131,7 @@ def main():
         }
     if "prefill" in wl:
         sec["prefill_b64"] = layer_entry(stack, pre, xs64, args.prefill_steps, 5)
+        progress("prefill chunk timed")
     if "decode" in wl or "prefill" in wl:
         if not args.no_cpu and "decode" in wl:
             L0 = host_layer(stack.layers[0][0])
@@ -1089,6 +1146,7 @@ def main():
             sec["fused_b1"] = layer_entry(fst, f1, xf1, max(args.steps, 200), args.warmup)
         if "fused_b64" in wl:
             sec["fused_b64"] = layer_entry(fst, f64, xf64, args.prefill_steps, 5)
+            progress("256-expert layer timed")
         del fst
         torch.cuda.empty_cache()
     if sec:
@@ -1096,11 +1154,13 @@ def main():
     if not args.no_calibration:
         result["calibration"] = stream_read_calibration(smoe)
         result["calibration"]["sync"] = sync_calibration(smoe)
+        progress("calibrations done")
     stack_points = None
     if not args.no_stack and "decode" in wl:
         result["stack"] = stack_harness(smoe, args.stack_layers, args.stack_prompt,
                                         args.stack_decode, oracle_points=not args.no_cpu)
         stack_points = result["stack"].pop("oracle_points", None)
+        progress("94-layer stack done")
     if L0 is not None:
         result["cpu_baseline"] = cpu_baseline(dec, L0, args.cpu_seconds)
         if stack_points is not None:
