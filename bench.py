@@ -123,15 +123,15 @@ class Stack:
         self._calls = {}
         torch.cuda.synchronize()
 
-    def prepared(self, l, x, stage=None):
-        key = (l, x.data_ptr(), x.shape[0], stage)
+    def prepared(self, l, x, stage=None, single=False):
+        key = (l, x.data_ptr(), x.shape[0], stage, single)
         c = self._calls.get(key)
         if c is None:
             W, ex = self.layers[l]
             B = x.shape[0]
             c = self.smoe.prepare_moe_layer(self.desc, W["router"], ex, x, self.out[:B],
                                             self.idx[:B], self.w[:B], self.un, self.ws,
-                                            stage=stage)
+                                            stage=stage, single=single)
             self._calls[key] = c
         return c
 
@@ -167,12 +167,14 @@ def warm_pass(stack, pools, seconds=0.3):
         torch.cuda.synchronize()
 
 
-def time_layer(stack, xs, steps, warmup):
+def time_layer(stack, xs, steps, warmup, single=False):
     """Seconds for `steps` whole-layer calls, rotating layers and inputs, timed
-    with events between two synchronisations after `warmup` untimed calls."""
+    with events between two synchronisations after `warmup` untimed calls
+    (single: the layer as one cooperative launch, smoe_moe_layer_single)."""
     import torch
     nl = len(stack.layers)
-    calls = [stack.prepared(s % nl, xs[s % len(xs)]) for s in range(max(steps, warmup))]
+    calls = [stack.prepared(s % nl, xs[s % len(xs)], single=single)
+             for s in range(max(steps, warmup))]
     for s in range(warmup):
         calls[s]()
     torch.cuda.synchronize()
@@ -1129,6 +1131,18 @@ def main():
                          "mean_launch_us": gu["mean_launch_us"], "launches": ROOFLINE_LAUNCHES},
             "kernels_back_to_back": main_e["kernels_back_to_back"],
         }
+        # the same layer as one cooperative launch (route, gate_up and down in
+        # one grid behind two device-wide barriers), beside the three launches
+        st = max(args.steps, 200)
+        t_single = time_layer(stack, xs1, st, args.warmup, single=True)
+        t_three = time_layer(stack, xs1, st, args.warmup)
+        sec["decode_single_launch"] = {
+            "workload": dec.name + ": the same layer, smoe_moe_layer_single", "steps": st,
+            "ms_per_step": round(t_single / st * 1e3, 5),
+            "tokens_per_s": round(st / t_single, 1),
+            "hbm_frac": round(dec.expert_bytes() * 8 / (t_single / st) / 1e9 / HBM_PEAK_GBPS, 4),
+            "three_launches_ms_per_step": round(t_three / st * 1e3, 5)}
+        progress("single-launch decode layer timed")
     if "prefill" in wl:
         sec["prefill_b64"] = layer_entry(stack, pre, xs64, args.prefill_steps, 5)
         progress("prefill chunk timed")

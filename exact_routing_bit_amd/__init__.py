@@ -37,7 +37,7 @@ EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_ro
             "smoe_stack_forward", "smoe_read_status", "smoe_strerror",
             "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage",
             "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes", "smoe_stream_read",
-            "smoe_empty_launch", "smoe_grid_barrier", "smoe_dma_read")
+            "smoe_empty_launch", "smoe_grid_barrier", "smoe_dma_read", "smoe_moe_layer_single")
 
 
 class SmoeError(RuntimeError):
@@ -92,6 +92,8 @@ def _load():
                                    i32, vp, vp, vp, sz, vp]
     L.smoe_moe_layer.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp, vp,
                                  ctypes.POINTER(Union), vp, sz, vp]
+    L.smoe_moe_layer_single.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp,
+                                        vp, ctypes.POINTER(Union), vp, sz, vp]
     L.smoe_moe_layer_noalloc.argtypes = [dp, vp, ctypes.POINTER(Experts), vp, i32, vp, vp, vp, vp,
                                          vp, ctypes.POINTER(Union), vp]
     L.smoe_stream_read.argtypes = [vp, sz, vp, i32, vp]
@@ -295,11 +297,27 @@ class PreparedCall:
             raise SmoeError(rc, self._what)
 
 
+def moe_layer_single(desc, router_w, experts: Experts, x, out, topk_idx, topk_w,
+                     un: UnionBuffers, ws, residual=None, logits=None, stream=None):
+    """moe_layer as one cooperative launch (see smoe_moe_layer_single: B = 1
+    decode layers only, SMOE_EUNSUPPORTED otherwise)."""
+    cu = un.c()
+    _check(lib.smoe_moe_layer_single(ctypes.byref(desc), _ptr(router_w, None, "router_w"),
+                                     ctypes.byref(experts), _ptr(x, torch.float32, "x"),
+                                     x.shape[0], _ptr(residual, torch.float32, "residual"),
+                                     _ptr(out, torch.float32, "out"),
+                                     _ptr(logits, torch.float32, "logits"),
+                                     _ptr(topk_idx, torch.int32, "topk_idx"),
+                                     _ptr(topk_w, torch.float32, "topk_w"), ctypes.byref(cu),
+                                     _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
+           "smoe_moe_layer_single")
+
+
 def prepare_moe_layer(desc, router_w, experts: Experts, x, out, topk_idx, topk_w,
                       un: UnionBuffers, ws, residual=None, logits=None, stream=None,
-                      stage=None, events=None) -> PreparedCall:
-    """moe_layer (or, with ``stage``, moe_layer_stage) with its arguments
-    marshalled once."""
+                      stage=None, events=None, single=False) -> PreparedCall:
+    """moe_layer (or, with ``stage``, moe_layer_stage; with ``single``,
+    moe_layer_single) with its arguments marshalled once."""
     cu = un.c()
     vp = ctypes.c_void_p
     common = (vp(_ptr(x, torch.float32, "x")), x.shape[0],
@@ -310,6 +328,9 @@ def prepare_moe_layer(desc, router_w, experts: Experts, x, out, topk_idx, topk_w
               vp(_ptr(ws, torch.uint8, "ws")), ws.numel(), vp(_stream(stream)))
     keep = (desc, experts, router_w, x, out, topk_idx, topk_w, un, ws, residual, logits, cu)
     head = (ctypes.byref(desc), vp(_ptr(router_w, None, "router_w")), ctypes.byref(experts))
+    if single:
+        return PreparedCall(lib.smoe_moe_layer_single, "smoe_moe_layer_single", head + common,
+                            keep)
     if stage is None:
         return PreparedCall(lib.smoe_moe_layer, "smoe_moe_layer", head + common, keep)
     ev = (None, None)

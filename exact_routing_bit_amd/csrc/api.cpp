@@ -390,6 +390,25 @@ SMOE_API int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w,
   return hip_rc(launch_layer(r, a, static_cast<hipStream_t>(stream)));
 }
 
+SMOE_API int smoe_moe_layer_single(const smoe_layer_desc* desc, const void* router_w,
+                                   const smoe_experts* experts, const float* x, int32_t B,
+                                   const float* residual, float* out, float* logits,
+                                   int32_t* topk_idx, float* topk_w, const smoe_union* un,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  smoe::RouteArgs r;
+  smoe::FfnArgs a;
+  const int rc = layer_setup(desc, router_w, experts, x, B, residual, out, logits, topk_idx,
+                             topk_w, un, ws, ws_bytes, &r, &a);
+  if (rc != SMOE_OK || B == 0) return rc;
+  if (!smoe::single_layer_ok(r, a)) return SMOE_EUNSUPPORTED;
+  // the same routing handoff as the three launches: block 0 of the gate_up
+  // pass packs the metadata that the down pass reads
+  smoe::DecodeRoute dr = decode_route(r);
+  dr.dec_meta = a.dec_meta;
+  a.dec_meta_valid = 1;
+  return hip_rc(smoe::launch_single_layer(r, a, dr, static_cast<hipStream_t>(stream)));
+}
+
 SMOE_API int smoe_moe_layer_stage(int stage, const smoe_layer_desc* desc, const void* router_w,
                                   const smoe_experts* experts, const float* x, int32_t B,
                                   const float* residual, float* out, float* logits,

@@ -37,6 +37,7 @@
 #include <algorithm>
 
 #include "device.hpp"
+#include "route_dev.hpp"
 #include "smoe_internal.hpp"
 
 namespace smoe {
@@ -467,7 +468,7 @@ struct RouteKeep {
 
 template <int NTOK>
 __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& r, DecMeta& m,
-                                           RouteKeep& keep, TopkScratch* tks) {
+                                           RouteKeep& keep, TopkScratch* tks, int blk) {
   __shared__ int s_e[kMaxDecPairs];
   __shared__ float s_w[kMaxDecPairs];
   const int wave = uniform(threadIdx.x >> 6);
@@ -549,7 +550,7 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
       m.n_union = nU;
       m.offsets[nU] = P;
     }
-    if (blockIdx.x == 0) {
+    if (blk == 0) {
       if (in) {
         r.topk_idx[lane] = e;
         r.topk_w[lane] = s_w[lane];
@@ -568,7 +569,7 @@ __device__ __forceinline__ void route_meta(const FfnArgs& a, const DecodeRoute& 
   }
   __syncthreads();
   // block 0: the packed copy for the down kernel
-  if (blockIdx.x == 0 && r.dec_meta != nullptr && threadIdx.x < kDecMetaWords)
+  if (blk == 0 && r.dec_meta != nullptr && threadIdx.x < kDecMetaWords)
     r.dec_meta[threadIdx.x] = reinterpret_cast<const int*>(&m)[threadIdx.x];
 }
 
@@ -586,8 +587,11 @@ __device__ __forceinline__ void route_rank(int K, int* slot_pair, RouteKeep& kee
 // w takes items w, w + W, w + 2W, ...; the next item's loads go out before
 // the current one is computed, so each wave streams its share with one item
 // in flight while it computes.
+// The gate_up pass of block blk of a grid of nblk 4-wave blocks (the kernel
+// below, or a phase of the single-launch layer).
 template <int NTOK, int TPR, int GPL, bool kRoute, bool kShared>
-__global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeRoute r) {
+__device__ __forceinline__ void gate_up_body(const FfnArgs& a, const DecodeRoute& r, int blk,
+                                             int nblk) {
   constexpr int kJ = kItemJ<GPL>;
   __shared__ DecMeta m;
   __shared__ TopkScratch tks[2];
@@ -599,14 +603,14 @@ __global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeR
   __shared__ int slot_pair[kDecWaves][kMaxDecPairs];
   RouteKeep keep;
   if (kRoute)
-    route_meta<NTOK>(a, r, m, keep, tks);
+    route_meta<NTOK>(a, r, m, keep, tks, blk);
   else
     load_meta(a, m);
   const int nU = uniform(m.n_union);
   const int nR = nU * (a.f / kJ);                 // routed items; then the shared expert's
   const int n_items = nR + (kShared ? a.fs / kJ : 0);
-  const int W = gridDim.x * kDecWaves;
-  const int wid = blockIdx.x * kDecWaves + wave;
+  const int W = nblk * kDecWaves;
+  const int wid = blk * kDecWaves + wave;
   if (wid >= n_items) return;                     // no barrier follows
   // this lane's group of every token's prepped activations, loaded first:
   // they are few and cached, and the weight loads queue behind them
@@ -677,7 +681,7 @@ flush:
       }
     }
   }
-  if (kRoute && NTOK == 1 && blockIdx.x == 0 && wave == 0) {
+  if (kRoute && NTOK == 1 && blk == 0 && wave == 0) {
     // the single token's routing outputs, as smoe_route and smoe_build_union
     // would write them (pair k = rank k; union slot q = the q-th expert)
     const int K = a.K;
@@ -712,12 +716,19 @@ flush:
   }
 }
 
+template <int NTOK, int TPR, int GPL, bool kRoute, bool kShared>
+__global__ __launch_bounds__(kDecThreads) void k_gate_up_gemv(FfnArgs a, DecodeRoute r) {
+  gate_up_body<NTOK, TPR, GPL, kRoute, kShared>(a, r, blockIdx.x, gridDim.x);
+}
+
 // grid: two 8-wave blocks per compute unit (at most one per row block);
 // block b takes row blocks b, b + grid, ... of 8 output rows x all union
 // experts, one (union slot, row block) item per wave, and ends each row block
-// with the weighted combine of its rows in rank order.
-template <int NTOK, int NW, bool kShared>
-__global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
+// with the weighted combine of its rows in rank order.  The down pass of
+// block blk of nblk blocks of kWaves waves (the kernel below, or a phase of
+// the single-launch layer).
+template <int NTOK, int NW, bool kShared, int kWaves>
+__device__ __forceinline__ void down_body(const FfnArgs& a, int blk, int nblk) {
   __shared__ DecMeta m;
   __shared__ float ylds[(kShRow0 + 2 * kMaxShChunks) * kDnRows];
   const int wave = uniform(threadIdx.x >> 6);
@@ -725,7 +736,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
   // the first row block's residual, fetched before anything waits
   float res_pref = 0.f;
   if (a.residual != nullptr && (int)threadIdx.x < a.B * kDnRows)
-    res_pref = a.residual[(int64_t)(threadIdx.x / kDnRows) * a.d + blockIdx.x * kDnRows +
+    res_pref = a.residual[(int64_t)(threadIdx.x / kDnRows) * a.d + blk * kDnRows +
                           threadIdx.x % kDnRows];
   if (a.dec_meta_valid) {
     if (threadIdx.x < kDecMetaWords) reinterpret_cast<int*>(&m)[threadIdx.x] = a.dec_meta[threadIdx.x];
@@ -750,9 +761,9 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
     const float at = a.xa[min(t, a.B - 1)];
     ib[t] = 1.0f / (at * at);
   }
-  for (int rb = blockIdx.x; rb < n_rb; rb += gridDim.x) {
+  for (int rb = blk; rb < n_rb; rb += nblk) {
     const int r0 = rb * kDnRows;
-    for (int u = wave; u < n_items; u += kDnWaves) {
+    for (int u = wave; u < n_items; u += kWaves) {
       DnItem<NTOK, NW> it;
       int ne, ys[NTOK];
       float ysc[NTOK];
@@ -790,13 +801,18 @@ __global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
         acc = shv + acc;
       }
       const int64_t o = (int64_t)t * a.d + r0 + rr;
-      const float res = rb == (int)blockIdx.x ? res_pref : (a.residual ? a.residual[o] : 0.f);
+      const float res = rb == blk ? res_pref : (a.residual ? a.residual[o] : 0.f);
       a.out[o] = res + acc;
     }
     // ylds is free again for the block's next row block (the barrier would
     // also wait for the stores above, so the last row block goes without)
-    if (rb + (int)gridDim.x < n_rb) __syncthreads();
+    if (rb + nblk < n_rb) __syncthreads();
   }
+}
+
+template <int NTOK, int NW, bool kShared>
+__global__ __launch_bounds__(kDnThreads) void k_down_combine_gemv(FfnArgs a) {
+  down_body<NTOK, NW, kShared, kDnWaves>(a, blockIdx.x, gridDim.x);
 }
 
 
@@ -859,7 +875,136 @@ hipError_t launch_down_gemv(const FfnArgs& a, hipStream_t s, const LaunchTiming*
   return launch_down_nw<NTOK, 4>(a, s, t);
 }
 
+// ------------------------------------------------ the single-launch layer
+// The decode layer (B = 1) as one cooperative grid ("Data Flow", serial step
+// trace: the routing, the experts and the combine of a step as one unit of
+// work): the router's per-block items (the token's activation prep, each
+// expert's gate matvec), a device-wide barrier, the gate_up pass (which ranks
+// the logits and builds the union first), a second barrier, and the down pass
+// with the combine, run by the same workgroups.  The barriers follow the
+// memory model at device scope: the block's barrier orders its waves' stores
+// before thread 0's acquire-release increment (a release is cumulative over
+// what happens before it, so one increment releases the whole block), thread
+// 0 waits for all blocks with relaxed loads and then acquires, and the
+// block's second barrier orders that acquire before every wave's next reads
+// (the caches it invalidates are the ones those waves read through).  One
+// release and one acquire a block: a fence in every wave made each barrier
+// several times slower.  A wait is bounded: past about
+// 2^22 polls it sets SMOE_STATUS_SYNC_TIMEOUT and goes on, so the grid always
+// drains.  Counters: status words kSingleBar .. +2 (two barriers, then an exit
+// ticket whose last holder clears all three for the next launch).
+constexpr int kSingleBar = 4;
+constexpr int kSingleSpin = 1 << 22;
+
+__device__ __forceinline__ void grid_sync(uint32_t* count, uint32_t nblk, uint32_t* status) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    int it = 0;
+    while (__hip_atomic_load(count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nblk) {
+      if (++it > kSingleSpin) {
+        __hip_atomic_fetch_or(status, (uint32_t)SMOE_STATUS_SYNC_TIMEOUT, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+template <int TPR, int NW, int kM>
+__global__ __launch_bounds__(kDecThreads) void k_layer_single(RouteArgs ra, FfnArgs a,
+                                                             DecodeRoute r) {
+  static_assert(kDecThreads == kRouteThreads, "the router's items need 4-wave blocks");
+  __shared__ float part[kRouteThreads / 64][1];
+  const int blk = blockIdx.x, nblk = gridDim.x;
+  uint32_t* bar = a.status + kSingleBar;
+  // 1. the token's prep and the E gate matvecs, one item a block at a time
+  for (int w = blk; w < 1 + ra.E; w += nblk) {
+    if (w == 0)
+      prep_token(ra.x, ra.d, 0, ra.xp, ra.xs, ra.xa, nullptr, 1.0f, &part[0][0]);
+    else
+      logits_block<true, 1, kM>(ra, w - 1, part);
+    __syncthreads();                               // part is the next item's
+  }
+  grid_sync(bar, nblk, a.status);
+  // 2. top-k, union and gate_up
+  gate_up_body<1, TPR, 1, true, false>(a, r, blk, nblk);
+  grid_sync(bar + 1, nblk, a.status);
+  // 3. down and the combine
+  down_body<1, NW, false, kDecWaves>(a, blk, nblk);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t t =
+        __hip_atomic_fetch_add(bar + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == (uint32_t)nblk - 1) {                 // every block is past both barriers
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        __hip_atomic_store(bar + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+template <int TPR, int NW, int kM>
+hipError_t launch_single_t(const RouteArgs& ra, const FfnArgs& a, const DecodeRoute& r, int grid,
+                           hipStream_t s) {
+  RouteArgs ra_ = ra;
+  FfnArgs a_ = a;
+  DecodeRoute r_ = r;
+  void* args[] = {&ra_, &a_, &r_};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_layer_single<TPR, NW, kM>),
+                                    dim3(grid), dim3(kDecThreads), args, 0, s);
+}
+
+template <int TPR, int NW, int kM>
+hipError_t single_fits(int grid, bool* ok) {
+  int per_cu = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, reinterpret_cast<const void*>(k_layer_single<TPR, NW, kM>), kDecThreads, 0);
+  *ok = e == hipSuccess && per_cu * cu_count() >= grid;
+  return e;
+}
+
 }  // namespace
+
+bool single_layer_ok(const RouteArgs& ra, const FfnArgs& a) {
+  return a.B == 1 && a.fs == 0 && ra.router_bf16 && ra.norm_out == nullptr && gemv_path_ok(a) &&
+         (a.d == 2048 || a.d == 4096) && a.E + 1 <= 4096;
+}
+
+hipError_t launch_single_layer(const RouteArgs& ra, const FfnArgs& a, const DecodeRoute& r,
+                               hipStream_t s) {
+  // the gate_up pass's grid (launch_gate_up_gemv): one block per CU, or more
+  // when a wave would hold more than kGuMaxItems items
+  const int max_union = a.E < a.K ? a.E : a.K;
+  const int items = max_union * (a.f / kItemJ<1>);
+  const int ncu = cu_count();
+  if (ncu <= 0) return hipErrorInvalidDevice;
+  const int per_block = kDecWaves * kGuMaxItems;
+  const int grid = std::max(std::min((items + kDecWaves - 1) / kDecWaves, ncu * kGuBlocksPerCU),
+                            (items + per_block - 1) / per_block);
+  const int words = a.f / 8;
+  const int nw = words <= 64 ? 1 : words <= 128 ? 2 : 4;
+  bool fits = false;
+#define SMOE_SINGLE(TPR, NW, M)                                        \
+  do {                                                                 \
+    const hipError_t e = single_fits<TPR, NW, M>(grid, &fits);          \
+    if (e != hipSuccess) return e;                                     \
+    if (!fits) return hipErrorCooperativeLaunchTooLarge;               \
+    return launch_single_t<TPR, NW, M>(ra, a, r, grid, s);             \
+  } while (0)
+  if (a.d == 2048) {
+    if (nw == 1) SMOE_SINGLE(32, 1, 1);
+    if (nw == 2) SMOE_SINGLE(32, 2, 1);
+    SMOE_SINGLE(32, 4, 1);
+  }
+  if (nw == 1) SMOE_SINGLE(64, 1, 2);
+  if (nw == 2) SMOE_SINGLE(64, 2, 2);
+  SMOE_SINGLE(64, 4, 2);
+#undef SMOE_SINGLE
+}
 
 // Compute units of the current device, cached per device (an attribute
 // lookup, not state of any call).

@@ -282,6 +282,11 @@ hipError_t launch_rmsnorm(const float* v, int B, int d, float eps, float* out, h
 bool gemv_path_ok(const FfnArgs& a);
 hipError_t launch_gemv(const FfnArgs& a, hipStream_t s, bool gate_up,
                        const LaunchTiming* t = nullptr);
+// The decode layer (B = 1, bf16 router, no shared expert, d of 2048 or 4096)
+// in one cooperative launch; single_layer_ok says whether a call qualifies.
+bool single_layer_ok(const RouteArgs& ra, const FfnArgs& a);
+hipError_t launch_single_layer(const RouteArgs& ra, const FfnArgs& a, const DecodeRoute& r,
+                               hipStream_t s);
 // gate_up with the routing tail (top-k, weights, union) folded in; the router
 // kernel then only computes logits and the prepped activations
 hipError_t launch_gate_up_routed(const FfnArgs& a, const DecodeRoute& r, hipStream_t s,

@@ -64,6 +64,7 @@ extern "C" {
 
 /* Device status bits, accumulated in the workspace until cleared. */
 #define SMOE_STATUS_BAD_EXPERT 0x1u /* an expert id outside [0, E) was given; its pair is skipped */
+#define SMOE_STATUS_SYNC_TIMEOUT 0x2u /* smoe_moe_layer_single: a device-wide barrier gave up waiting */
 
 /* ----------------------------------------------------------- descriptors */
 /* Supported: d_model and ffn_dim multiples of 64 in [64, 8192];
@@ -205,6 +206,29 @@ int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w, const smoe
                    const float* x, int32_t B, const float* residual, float* out, float* logits,
                    int32_t* topk_idx, float* topk_w, const smoe_union* un, void* ws,
                    size_t ws_bytes, void* stream);
+
+/* smoe_moe_layer as ONE cooperative launch ([DF] serial step trace: a
+ * step's routing, experts and combine submitted as one unit; [LMP]
+ * "Choreography Per Chunk" steps 5-6 at B = 1).  The same work in one grid
+ * of one workgroup per compute unit: the token's activation prep and every
+ * expert's gate matvec, a device-wide barrier, top-k + union + gate_up, a
+ * second barrier, down + the weighted combine.  The barriers release and
+ * acquire at device scope (every wave's stores); a wait that passes about
+ * 2^22 polls sets SMOE_STATUS_SYNC_TIMEOUT in the workspace status and goes
+ * on, so the launch always ends.  Results are bit for bit those of
+ * smoe_moe_layer on the same inputs.  Supported: B = 1, a bf16 router, no
+ * shared expert, d_model 2048 or 4096, the decode path's ffn_dim and top_k
+ * (top_k <= 16); else SMOE_EUNSUPPORTED (nothing launched).  The runtime
+ * refuses the launch (SMOE_EHIP) when the grid cannot be resident at once.
+ * Not for HIP graph capture: use smoe_moe_layer there.  On this part it is
+ * slower than smoe_moe_layer's three launches: a device-wide barrier costs
+ * several launch boundaries (the calibrations in bench.py measure both).
+ * Arguments, outputs and other errors as smoe_moe_layer. */
+int smoe_moe_layer_single(const smoe_layer_desc* desc, const void* router_w,
+                          const smoe_experts* experts, const float* x, int32_t B,
+                          const float* residual, float* out, float* logits, int32_t* topk_idx,
+                          float* topk_w, const smoe_union* un, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* smoe_moe_layer without a workspace argument and without any allocation,
  * for callers that cannot allocate device memory: code under HIP graph
