@@ -167,10 +167,17 @@ def warm_pass(stack, pools, seconds=0.3):
         torch.cuda.synchronize()
 
 
+HOLD_US = 200
+
+
 def time_layer(stack, xs, steps, warmup, single=False):
     """Seconds for `steps` whole-layer calls, rotating layers and inputs, timed
     with events between two synchronisations after `warmup` untimed calls
-    (single: the layer as one cooperative launch, smoe_moe_layer_single)."""
+    (single: the layer as one cooperative launch, smoe_moe_layer_single).
+    A device-side wait of HOLD_US queued before the first event keeps the GPU
+    busy while the host enqueues the first calls: without it the region
+    opens with the host's latency to its first launch (about 20 us, a
+    microsecond a step over 20 steps), which is not the layer's."""
     import torch
     nl = len(stack.layers)
     calls = [stack.prepared(s % nl, xs[s % len(xs)], single=single)
@@ -178,6 +185,7 @@ def time_layer(stack, xs, steps, warmup, single=False):
     for s in range(warmup):
         calls[s]()
     torch.cuda.synchronize()
+    stack.smoe.gpu_sleep(HOLD_US)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()

@@ -37,7 +37,8 @@ EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_ro
             "smoe_stack_forward", "smoe_read_status", "smoe_strerror",
             "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage",
             "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes", "smoe_stream_read",
-            "smoe_empty_launch", "smoe_grid_barrier", "smoe_dma_read", "smoe_moe_layer_single")
+            "smoe_empty_launch", "smoe_grid_barrier", "smoe_dma_read", "smoe_moe_layer_single",
+            "smoe_gpu_sleep")
 
 
 class SmoeError(RuntimeError):
@@ -98,6 +99,7 @@ def _load():
                                          vp, ctypes.POINTER(Union), vp]
     L.smoe_stream_read.argtypes = [vp, sz, vp, i32, vp]
     L.smoe_empty_launch.argtypes = [i32, i32, vp]
+    L.smoe_gpu_sleep.argtypes = [i32, vp]
     L.smoe_dma_read.argtypes = [vp, sz, i32, i32, vp, i32, vp]
     L.smoe_grid_barrier.argtypes = [i32, vp, vp, vp, vp]
     L.smoe_noalloc_scratch_bytes.argtypes = []
@@ -379,6 +381,12 @@ def empty_launch(blocks: int, count: int = 1, stream=None):
     """Diagnostic: `count` back-to-back launches of a kernel that does nothing
     (smoe_empty_launch)."""
     _check(lib.smoe_empty_launch(int(blocks), int(count), _stream(stream)), "smoe_empty_launch")
+
+
+def gpu_sleep(us: int, stream=None):
+    """Diagnostic: one wave that waits `us` microseconds on the device's clock
+    (smoe_gpu_sleep), queued ahead of a timed region."""
+    _check(lib.smoe_gpu_sleep(int(us), _stream(stream)), "smoe_gpu_sleep")
 
 
 def grid_barrier(blocks: int, counter, stamps, timed_out, stream=None):

@@ -9,6 +9,9 @@
 //     path reaches with no arithmetic behind it;
 //   smoe_empty_launch: a kernel that does nothing (the cost of one more
 //     launch in a stream of back-to-back kernels);
+//   smoe_gpu_sleep: one wave that waits a given time on the device's clock
+//     (queued ahead of a timed region, it lets the host enqueue the region's
+//     first launches before the device reaches them);
 //   smoe_grid_barrier: one device-wide barrier of a cooperative grid (the
 //     cost of the alternative to a launch boundary: every block releases its
 //     stores at device scope, counts itself in and waits for all the others).
@@ -106,6 +109,12 @@ __global__ __launch_bounds__(256, 2) void k_dma_read(const char* src, int64_t ro
 
 __global__ void k_empty() {}
 
+// Waits `ticks` of the 100 MHz s_memrealtime clock, then ends.
+__global__ __launch_bounds__(64) void k_sleep(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(16);
+}
+
 constexpr int kSpinLimit = 1 << 22;   // bounded wait: about 0.1 s, then give up
 
 // Each block: its barrier, one acquire-release increment of *counter at
@@ -172,6 +181,13 @@ SMOE_API int smoe_empty_launch(int32_t blocks, int32_t count, void* stream) {
   if (blocks < 1 || blocks > (1 << 20) || count < 0 || count > (1 << 20)) return SMOE_EINVAL;
   for (int i = 0; i < count; ++i)
     hipLaunchKernelGGL(smoe::k_empty, dim3(blocks), dim3(64), 0, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? SMOE_OK : SMOE_EHIP;
+}
+
+SMOE_API int smoe_gpu_sleep(int32_t us, void* stream) {
+  if (us < 0 || us > 100000) return SMOE_EINVAL;
+  hipLaunchKernelGGL(smoe::k_sleep, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     (uint64_t)us * 100u);
   return hipGetLastError() == hipSuccess ? SMOE_OK : SMOE_EHIP;
 }
 

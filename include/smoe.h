@@ -411,6 +411,14 @@ int smoe_dma_read(const void* src, size_t bytes, int32_t row_bytes, int32_t mode
  * fails. */
 int smoe_empty_launch(int32_t blocks, int32_t count, void* stream);
 
+/* Diagnostic: one wave that waits `us` (0 .. 100000) microseconds of the
+ * device's 100 MHz clock and ends.  Queued ahead of a timed region, it keeps
+ * the device busy while the host enqueues the region's first launches, so
+ * the region's time does not include the host's latency to its first kernel.
+ * Async on stream; SMOE_EINVAL on a bad duration, SMOE_EHIP when the launch
+ * fails. */
+int smoe_gpu_sleep(int32_t us, void* stream);
+
 /* Diagnostic: one device-wide barrier, the in-kernel alternative to a kernel
  * boundary.  A cooperative grid of `blocks` (1 .. 4096) workgroups of 256
  * threads, all resident at once (the runtime refuses the launch otherwise:

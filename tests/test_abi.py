@@ -297,6 +297,8 @@ def test_diagnostics_reject_bad_arguments(smoe):
     assert smoe.lib.smoe_empty_launch(0, 1, None) == smoe.SMOE_EINVAL
     assert smoe.lib.smoe_empty_launch((1 << 20) + 1, 1, None) == smoe.SMOE_EINVAL
     assert smoe.lib.smoe_empty_launch(8, -1, None) == smoe.SMOE_EINVAL
+    assert smoe.lib.smoe_gpu_sleep(-1, None) == smoe.SMOE_EINVAL
+    assert smoe.lib.smoe_gpu_sleep(100001, None) == smoe.SMOE_EINVAL
     dr = smoe.lib.smoe_dma_read
     assert dr(f, 1 << 20, 2048, 0, f, 1, None) == smoe.SMOE_EINVAL     # sink too small (2 blocks)
     assert dr(f + 4, 1 << 20, 2048, 0, f, 64, None) == smoe.SMOE_EINVAL  # unaligned source
