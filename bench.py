@@ -882,7 +882,8 @@ COPY_BYTES = 1 << 30
 ROOFLINE_KERNEL = "k_gate_up_gemv<1, 64, 1, true, false>"
 ROOFLINE_SOURCES = ["exact_routing_bit_amd/csrc/ffn_gemv.hip", "exact_routing_bit_amd/csrc/ffn_mfma.hip",
                     "exact_routing_bit_amd/csrc/router.hip", "exact_routing_bit_amd/csrc/device.hpp",
-                    "exact_routing_bit_amd/csrc/smoe_internal.hpp"]
+                    "exact_routing_bit_amd/csrc/smoe_internal.hpp",
+                    "exact_routing_bit_amd/csrc/route_dev.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gate_up_gemv_decode_b1_traffic.txt")
 
 
