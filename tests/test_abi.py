@@ -236,6 +236,34 @@ def test_stage_argument_errors(smoe):
     assert call(n=4096) == smoe.SMOE_EWORKSPACE
 
 
+def test_single_launch_argument_errors(smoe):
+    """smoe_moe_layer_single checks its arguments as smoe_moe_layer does, then
+    refuses the layers it has no single-launch kernel for (B != 1, an fp32
+    router, d outside 2048/4096, a shared expert), all before any launch."""
+    f = 4096
+    q = smoe.QMat(f, f, f, 1536 * 512, 1536 * 64)
+    qd = smoe.QMat(f, f, f, 4096 * 192, 4096 * 24)
+    sq = smoe.QMat(f, f, f, 0, 0)
+    ex = smoe.Experts(q, q, qd)
+    un = smoe.Union(f, f, f, f, f)
+    sl = smoe.lib.smoe_moe_layer_single
+
+    def call(d=None, B=1, x=f, n=1 << 30, e=ex):
+        d = desc_of(smoe) if d is None else d
+        return sl(ctypes.byref(d), f, ctypes.byref(e), x, B, None, f, f, f, f, ctypes.byref(un),
+                  f, n, None)
+
+    assert call(x=None) == smoe.SMOE_EINVAL
+    assert call(B=-1) == smoe.SMOE_EINVAL
+    assert call(n=4096) == smoe.SMOE_EWORKSPACE
+    assert call(B=0) == smoe.SMOE_OK                    # an empty batch launches nothing
+    assert call(B=2) == smoe.SMOE_EUNSUPPORTED
+    assert call(d=desc_of(smoe, router_bf16=False)) == smoe.SMOE_EUNSUPPORTED
+    assert call(d=desc_of(smoe, d_model=1024)) == smoe.SMOE_EUNSUPPORTED
+    assert call(d=desc_of(smoe, shared_ffn_dim=3072),
+                e=smoe.Experts(q, q, qd, sq, sq, sq)) == smoe.SMOE_EUNSUPPORTED
+
+
 def test_rmsnorm_argument_errors(smoe):
     f = ctypes.c_void_p(4096)
     rn = smoe.lib.smoe_rmsnorm
