@@ -614,6 +614,7 @@ def cpu_baseline(cfg, L, seconds):
 
 # ------------------------------------------------------------------ stack
 STACK_CHUNK = 64
+STACK_IN_FLIGHT = 4        # prompt chunks in flight in the stacked harness
 
 
 def stack_stats(idx_pre, nu_pre, idx_dec, E):
@@ -781,10 +782,14 @@ def stack_oracle_points(smoe, desc, Ws, ex, cfg, n_layers, prompt, steps):
 def stack_harness(smoe, n_layers, prompt, steps, oracle_points=False):
     """The stacked routed-expert path: n_layers layers of the decode shape
     resident in HBM; a prompt of `prompt` tokens in chunks of 64, layer-major
-    (each chunk through every layer before the next chunk), then `steps`
-    single-token decode steps through every layer; h <- RMSNorm(h + MoE(h))
-    between layers, attention left out.  Inputs: RMS-normalised N(0, 1)
-    rows, prompt from one seeded stream, decode step n from its own."""
+    (each chunk through every layer, its union streamed once per layer), then
+    `steps` single-token decode steps through every layer; h <- RMSNorm(h +
+    MoE(h)) between layers, attention left out.  The prompt runs with
+    STACK_IN_FLIGHT chunks at once (smoe_stack_forward_chunks: each chunk a
+    layer behind the previous one, on its own stream), and once more one chunk
+    at a time (smoe_stack_forward), which must give the same bits.  Inputs:
+    RMS-normalised N(0, 1) rows, prompt from one seeded stream, decode step n
+    from its own."""
     import numpy as np
     import torch
 
@@ -804,10 +809,16 @@ def stack_harness(smoe, n_layers, prompt, steps, oracle_points=False):
     args = smoe.StackArgs([W["router"] for W in Ws], ex)
     desc = smoe.make_desc(d, cfg.ffn_dim, E, K, cfg.norm_topk_prob, cfg.router_bf16)
     dev = torch.device("cuda:0")
-    ws = torch.zeros(smoe.workspace_size(desc, STACK_CHUNK), dtype=torch.uint8, device=dev)
-    smoe.workspace_init(ws)
-    un = smoe.UnionBuffers.alloc(E, STACK_CHUNK * K, dev)
-    tmp = torch.zeros(STACK_CHUNK, d, dtype=torch.float32, device=dev)
+    # one workspace, union and scratch per chunk in flight
+    wss = [torch.zeros(smoe.workspace_size(desc, STACK_CHUNK), dtype=torch.uint8, device=dev)
+           for _ in range(STACK_IN_FLIGHT)]
+    for w_ in wss:
+        smoe.workspace_init(w_)
+    uns = [smoe.UnionBuffers.alloc(E, STACK_CHUNK * K, dev) for _ in range(STACK_IN_FLIGHT)]
+    tmps = [torch.zeros(STACK_CHUNK, d, dtype=torch.float32, device=dev)
+            for _ in range(STACK_IN_FLIGHT)]
+    ws, un, tmp = wss[0], uns[0], tmps[0]
+    streams = [None] + [torch.cuda.Stream() for _ in range(STACK_IN_FLIGHT - 1)]
     i32 = dict(dtype=torch.int32, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
     idx_pre = torch.zeros(chunks, n_layers, STACK_CHUNK, K, **i32)
@@ -818,28 +829,50 @@ def stack_harness(smoe, n_layers, prompt, steps, oracle_points=False):
     nu_dec = torch.zeros(steps, n_layers, **i32)
     h_pre = sg.hidden(cfg.seed, 0, 5000, prompt, d)
     h_dec = [sg.hidden(cfg.seed, 0, 6000 + n, 1, d) for n in range(steps)]
-    # warm-up: one chunk and one decode step through the stack, on copies
+    def rows(h, c):
+        return h[c * STACK_CHUNK:(c + 1) * STACK_CHUNK]
+
+    # warm-up: one chunk, the chunks in flight and one decode step through the
+    # stack, on copies
     warm = h_pre[:STACK_CHUNK].clone()
     smoe.stack_forward(desc, args, warm, tmp, idx_pre[0], w_pre[0], un, ws, n_union=nu_pre[0])
+    warm = h_pre[:STACK_CHUNK * STACK_IN_FLIGHT].clone()
+    smoe.stack_forward_chunks(desc, args, [
+        dict(h=rows(warm, j), tmp=tmps[j], topk_idx=idx_pre[j], topk_w=w_pre[j],
+             n_union=nu_pre[j], un=uns[j], ws=wss[j], stream=streams[j])
+        for j in range(min(STACK_IN_FLIGHT, chunks))])
     warm = h_dec[0].clone()
     smoe.stack_forward(desc, args, warm, tmp[:1], idx_dec[0], w_dec[0], un, ws,
                        n_union=nu_dec[0])
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    h_one = h_pre.clone()                          # the prompt again, one chunk at a time
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     ev[0].record()
-    for c in range(chunks):
-        smoe.stack_forward(desc, args, h_pre[c * STACK_CHUNK:(c + 1) * STACK_CHUNK], tmp,
-                           idx_pre[c], w_pre[c], un, ws, n_union=nu_pre[c])
+    for c0 in range(0, chunks, STACK_IN_FLIGHT):
+        group = list(range(c0, min(c0 + STACK_IN_FLIGHT, chunks)))
+        smoe.stack_forward_chunks(desc, args, [
+            dict(h=rows(h_pre, c), tmp=tmps[j], topk_idx=idx_pre[c], topk_w=w_pre[c],
+                 n_union=nu_pre[c], un=uns[j], ws=wss[j], stream=streams[j])
+            for j, c in enumerate(group)])
     ev[1].record()
     for n in range(steps):
         smoe.stack_forward(desc, args, h_dec[n], tmp[:1], idx_dec[n], w_dec[n], un, ws,
                            n_union=nu_dec[n])
     ev[2].record()
+    ev[3].record()
+    for c in range(chunks):
+        smoe.stack_forward(desc, args, rows(h_one, c), tmp, idx_pre[c], w_pre[c], un, ws,
+                           n_union=nu_pre[c])
+    ev[4].record()
     torch.cuda.synchronize()
-    if smoe.read_status(ws) != 0:
+    if any(smoe.read_status(w_) != 0 for w_ in wss):
         raise RuntimeError("the stack reported a bad expert id")
     pre_s = ev[0].elapsed_time(ev[1]) / 1e3
     dec_s = ev[1].elapsed_time(ev[2]) / 1e3
+    one_s = ev[3].elapsed_time(ev[4]) / 1e3
+    in_flight_equal = bool(torch.equal(h_pre.view(torch.int32), h_one.view(torch.int32)))
+    if not in_flight_equal:
+        raise RuntimeError("chunks in flight differ from one chunk at a time")
     graph = stack_graph_decode(smoe, desc, args, cfg, n_layers, steps, h_dec, idx_dec, tmp, un, ws)
     st = stack_stats(idx_pre.cpu().numpy(), nu_pre.cpu().numpy(), idx_dec.cpu().numpy(), E)
     if not np.all(nu_dec.cpu().numpy() == K):
@@ -856,6 +889,9 @@ def stack_harness(smoe, n_layers, prompt, steps, oracle_points=False):
         "weight_generation_s": round(gen_s, 2),
         "prefill_s": round(pre_s, 5), "prefill_tokens_per_s": round(prompt / pre_s, 1),
         "prefill_effective_gbps": round(pre_bytes / pre_s / 1e9, 1),
+        "prefill_chunks_in_flight": STACK_IN_FLIGHT,
+        "prefill_one_chunk_at_a_time_s": round(one_s, 5),
+        "prefill_in_flight_equals_one_at_a_time": in_flight_equal,
         "decode_ms_per_token": round(dec_s / steps * 1e3, 4),
         "decode_tokens_per_s": round(steps / dec_s, 2),
         "decode_effective_gbps": round(dec_bytes / dec_s / 1e9, 1),

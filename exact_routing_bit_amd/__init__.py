@@ -38,7 +38,7 @@ EXPORTED = ("smoe_workspace_size", "smoe_workspace_init", "smoe_route", "smoe_ro
             "smoe_attn_workspace_size", "smoe_attn_forward", "smoe_attn_forward_stage",
             "smoe_moe_layer_noalloc", "smoe_noalloc_scratch_bytes", "smoe_stream_read",
             "smoe_empty_launch", "smoe_grid_barrier", "smoe_dma_read", "smoe_moe_layer_single",
-            "smoe_gpu_sleep")
+            "smoe_gpu_sleep", "smoe_stack_forward_chunks")
 
 
 class SmoeError(RuntimeError):
@@ -77,6 +77,16 @@ class Union(ctypes.Structure):
                 ("pair_pos", ctypes.c_void_p)]
 
 
+class StackChunk(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("B", ctypes.c_int32), ("tmp", ctypes.c_void_p),
+                ("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("n_union", ctypes.c_void_p), ("un", Union), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t), ("stream", ctypes.c_void_p)]
+
+
+MAX_STACK_CHUNKS = 8
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
@@ -110,6 +120,9 @@ def _load():
     L.smoe_stack_forward.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_void_p),
                                      ctypes.POINTER(Experts), vp, i32, ctypes.c_float, vp, vp, vp,
                                      vp, ctypes.POINTER(Union), vp, sz, vp]
+    L.smoe_stack_forward_chunks.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.POINTER(Experts), ctypes.c_float,
+                                            ctypes.POINTER(StackChunk), i32]
     L.smoe_read_status.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
     L.smoe_strerror.argtypes = [ctypes.c_int]
     L.smoe_strerror.restype = ctypes.c_char_p
@@ -468,6 +481,25 @@ def stack_forward(desc, stack: StackArgs, h, tmp, topk_idx, topk_w, un: UnionBuf
                                   _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(stream)),
            "smoe_stack_forward")
     return h
+
+
+def stack_forward_chunks(desc, stack: StackArgs, chunks, eps=1e-6):
+    """Several prompt chunks through the stack at once (smoe_stack_forward_chunks):
+    chunks is a list of dicts with h, tmp, topk_idx, topk_w, un (UnionBuffers),
+    ws, and optionally n_union and stream; each as for stack_forward, each with
+    buffers of its own.  Ordered on the first chunk's stream."""
+    arr = (StackChunk * max(len(chunks), 1))()
+    for i, c in enumerate(chunks):
+        h, ws = c["h"], c["ws"]
+        arr[i] = StackChunk(_ptr(h, torch.float32, "h"), h.shape[0],
+                            _ptr(c["tmp"], torch.float32, "tmp"),
+                            _ptr(c["topk_idx"], torch.int32, "topk_idx"),
+                            _ptr(c["topk_w"], torch.float32, "topk_w"),
+                            _ptr(c.get("n_union"), torch.int32, "n_union"), c["un"].c(),
+                            _ptr(ws, torch.uint8, "ws"), ws.numel(), _stream(c.get("stream")))
+    _check(lib.smoe_stack_forward_chunks(ctypes.byref(desc), stack.n, stack.router,
+                                         stack.experts, eps, arr, len(chunks)),
+           "smoe_stack_forward_chunks")
 
 
 def make_attn_desc(d_model, num_heads, num_kv_heads, ctx, rope_theta=1.0e6, eps=1e-6,

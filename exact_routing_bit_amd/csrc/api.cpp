@@ -450,44 +450,69 @@ SMOE_API int smoe_rmsnorm(const float* v, int32_t B, int32_t d, float eps, float
   return hip_rc(smoe::launch_rmsnorm(v, B, d, eps, out, static_cast<hipStream_t>(stream)));
 }
 
-SMOE_API int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers,
-                                const void* const* router_w, const smoe_experts* experts,
-                                float* h, int32_t B, float eps, float* tmp, int32_t* topk_idx,
-                                float* topk_w, int32_t* n_union, const smoe_union* un, void* ws,
-                                size_t ws_bytes, void* stream) {
-  if (n_layers < 0 || !(eps > 0.0f) || un == nullptr) return SMOE_EINVAL;
-  int rc = check_desc(desc);
-  if (rc == SMOE_OK) rc = check_batch(B);
-  if (rc != SMOE_OK) return rc;
-  if (n_layers == 0 || B == 0) return SMOE_OK;
-  if (router_w == nullptr || experts == nullptr || h == nullptr || tmp == nullptr || h == tmp ||
-      !aligned(h, 16) || !aligned(tmp, 16))
-    return SMOE_EINVAL;
-  const int64_t per_layer = (int64_t)B * desc->top_k;
-  // every layer is checked before the first launch, so a bad layer leaves h as it was
-  for (int l = 0; l < n_layers; ++l) {
-    smoe::RouteArgs r;
-    smoe::FfnArgs a;
-    smoe_union u = *un;
-    if (n_union != nullptr) u.n_union = n_union + l;
-    rc = layer_setup(desc, router_w[l], experts + l, h, B, h, tmp, nullptr,
-                     topk_idx ? topk_idx + l * per_layer : nullptr,
-                     topk_w ? topk_w + l * per_layer : nullptr, &u, ws, ws_bytes, &r, &a);
-    if (rc != SMOE_OK) return rc;
-  }
-  hipStream_t s = static_cast<hipStream_t>(stream);
+namespace {
+
+// One batch of tokens through a stack (smoe_stack_forward): its arguments,
+// checked once before anything is launched, and the state carried from one
+// layer to the next.
+struct StackRun {
+  const smoe_layer_desc* desc = nullptr;
+  int n_layers = 0;
+  const void* const* router_w = nullptr;
+  const smoe_experts* experts = nullptr;
+  float* h = nullptr;
+  int B = 0;
+  float eps = 0.0f;
+  float* tmp = nullptr;
+  int32_t* topk_idx = nullptr;
+  float* topk_w = nullptr;
+  int32_t* n_union = nullptr;
+  smoe_union un{};
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
   // Decode-sized layers (B <= 2) leave the norm of their output to the next
   // layer's router, which forms the same factor as smoe_rmsnorm (the same
   // summation order), routes the normalised rows and writes them to h: one
   // launch fewer per layer, bit-identical results.
   bool norm_pending = false;                      // tmp holds the raw output, h is stale
-  for (int l = 0; l < n_layers; ++l) {
+
+  int setup(int l, smoe::RouteArgs* r, smoe::FfnArgs* a) const {
+    const int64_t per_layer = (int64_t)B * desc->top_k;
+    smoe_union u = un;
+    if (n_union != nullptr) u.n_union = n_union + l;
+    return layer_setup(desc, router_w[l], experts + l, h, B, h, tmp, nullptr,
+                       topk_idx ? topk_idx + l * per_layer : nullptr,
+                       topk_w ? topk_w + l * per_layer : nullptr, &u, ws, ws_bytes, r, a);
+  }
+
+  // every check of smoe_stack_forward; SMOE_OK with nothing to do when
+  // n_layers or B is 0 (empty() then holds)
+  int check() const {
+    if (n_layers < 0 || !(eps > 0.0f)) return SMOE_EINVAL;
+    int rc = check_desc(desc);
+    if (rc == SMOE_OK) rc = check_batch(B);
+    if (rc != SMOE_OK) return rc;
+    if (empty()) return SMOE_OK;
+    if (router_w == nullptr || experts == nullptr || h == nullptr || tmp == nullptr || h == tmp ||
+        !aligned(h, 16) || !aligned(tmp, 16))
+      return SMOE_EINVAL;
+    // every layer is checked before the first launch, so a bad layer leaves h as it was
+    for (int l = 0; l < n_layers; ++l) {
+      smoe::RouteArgs r;
+      smoe::FfnArgs a;
+      rc = setup(l, &r, &a);
+      if (rc != SMOE_OK) return rc;
+    }
+    return SMOE_OK;
+  }
+
+  bool empty() const { return n_layers == 0 || B == 0; }
+
+  // layer l and its norm (or the norm left to layer l + 1's router)
+  hipError_t launch(int l, hipStream_t s) {
     smoe::RouteArgs r;
     smoe::FfnArgs a;
-    smoe_union u = *un;
-    if (n_union != nullptr) u.n_union = n_union + l;
-    layer_setup(desc, router_w[l], experts + l, h, B, h, tmp, nullptr, topk_idx + l * per_layer,
-                topk_w + l * per_layer, &u, ws, ws_bytes, &r, &a);
+    setup(l, &r, &a);
     if (norm_pending) {
       r.x = tmp;
       r.norm_out = h;
@@ -497,11 +522,137 @@ SMOE_API int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers,
     norm_pending = smoe::gemv_path_ok(a) && B <= 2;
     if (err == hipSuccess && !norm_pending)
       err = smoe::launch_rmsnorm(tmp, B, desc->d_model, eps, h, s);
-    if (err != hipSuccess) return SMOE_EHIP;
+    return err;
   }
-  if (norm_pending && smoe::launch_rmsnorm(tmp, B, desc->d_model, eps, h, s) != hipSuccess)
-    return SMOE_EHIP;
-  return SMOE_OK;
+
+  // the last layer's norm, when it was left to a next layer
+  hipError_t finish(hipStream_t s) {
+    if (!norm_pending) return hipSuccess;
+    norm_pending = false;
+    return smoe::launch_rmsnorm(tmp, B, desc->d_model, eps, h, s);
+  }
+};
+
+// The ordering events of smoe_stack_forward_chunks, kept per host thread and
+// device (created on first use, never destroyed; no device memory).
+hipError_t chunk_event(int slot, hipEvent_t* ev) {
+  constexpr int kDevs = 64;
+  thread_local hipEvent_t cache[kDevs][SMOE_MAX_STACK_CHUNKS + 1] = {};
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kDevs) return hipErrorInvalidDevice;
+  if (cache[dev][slot] == nullptr) {
+    err = hipEventCreateWithFlags(&cache[dev][slot], hipEventDisableTiming);
+    if (err != hipSuccess) {
+      cache[dev][slot] = nullptr;
+      return err;
+    }
+  }
+  *ev = cache[dev][slot];
+  return hipSuccess;
+}
+
+}  // namespace
+
+SMOE_API int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers,
+                                const void* const* router_w, const smoe_experts* experts,
+                                float* h, int32_t B, float eps, float* tmp, int32_t* topk_idx,
+                                float* topk_w, int32_t* n_union, const smoe_union* un, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (un == nullptr) return SMOE_EINVAL;
+  StackRun run;
+  run.desc = desc;
+  run.n_layers = n_layers;
+  run.router_w = router_w;
+  run.experts = experts;
+  run.h = h;
+  run.B = B;
+  run.eps = eps;
+  run.tmp = tmp;
+  run.topk_idx = topk_idx;
+  run.topk_w = topk_w;
+  run.n_union = n_union;
+  run.un = *un;
+  run.ws = ws;
+  run.ws_bytes = ws_bytes;
+  const int rc = run.check();
+  if (rc != SMOE_OK || run.empty()) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int l = 0; l < n_layers; ++l)
+    if (run.launch(l, s) != hipSuccess) return SMOE_EHIP;
+  return hip_rc(run.finish(s));
+}
+
+SMOE_API int smoe_stack_forward_chunks(const smoe_layer_desc* desc, int32_t n_layers,
+                                       const void* const* router_w, const smoe_experts* experts,
+                                       float eps, const smoe_stack_chunk* chunks,
+                                       int32_t n_chunks) {
+  if (chunks == nullptr || n_chunks < 1 || n_chunks > SMOE_MAX_STACK_CHUNKS) return SMOE_EINVAL;
+  StackRun run[SMOE_MAX_STACK_CHUNKS];
+  hipStream_t st[SMOE_MAX_STACK_CHUNKS];
+  int n = 0;                                       // chunks with work, in order
+  for (int i = 0; i < n_chunks; ++i) {
+    const smoe_stack_chunk& c = chunks[i];
+    StackRun& q = run[n];
+    q.desc = desc;
+    q.n_layers = n_layers;
+    q.router_w = router_w;
+    q.experts = experts;
+    q.h = c.h;
+    q.B = c.B;
+    q.eps = eps;
+    q.tmp = c.tmp;
+    q.topk_idx = c.topk_idx;
+    q.topk_w = c.topk_w;
+    q.n_union = c.n_union;
+    q.un = c.un;
+    q.ws = c.ws;
+    q.ws_bytes = c.ws_bytes;
+    const int rc = q.check();
+    if (rc != SMOE_OK) return rc;
+    // nothing a chunk writes may be another chunk's
+    for (int j = 0; j < n; ++j) {
+      const StackRun& o = run[j];
+      const void* mine[] = {q.h, q.tmp, q.topk_idx, q.topk_w, q.n_union, q.un.n_union,
+                            q.un.union_experts, q.un.expert_offsets, q.un.pair_list,
+                            q.un.pair_pos, q.ws};
+      const void* theirs[] = {o.h, o.tmp, o.topk_idx, o.topk_w, o.n_union, o.un.n_union,
+                              o.un.union_experts, o.un.expert_offsets, o.un.pair_list,
+                              o.un.pair_pos, o.ws};
+      for (const void* a : mine)
+        for (const void* b : theirs)
+          if (a != nullptr && a == b) return SMOE_EINVAL;
+    }
+    if (!q.empty()) st[n++] = static_cast<hipStream_t>(c.stream);
+  }
+  if (n == 0) return SMOE_OK;
+  hipEvent_t ev[SMOE_MAX_STACK_CHUNKS + 1];
+  for (int i = 0; i <= n; ++i)
+    if (chunk_event(i, &ev[i]) != hipSuccess) return SMOE_EHIP;
+  // fork: every stream after the work already queued on the first
+  hipError_t err = hipSuccess;
+  if (n > 1) err = hipEventRecord(ev[n], st[0]);
+  for (int i = 1; i < n && err == hipSuccess; ++i) err = hipStreamWaitEvent(st[i], ev[n], 0);
+  // Step t issues layer t - i of chunk i.  Chunks are issued last to first,
+  // so that chunk i waits on ev[i - 1] as recorded after chunk i - 1's same
+  // layer (one step earlier), before chunk i - 1 records it again.
+  for (int t = 0; t < n_layers + n - 1 && err == hipSuccess; ++t) {
+    for (int i = n - 1; i >= 0 && err == hipSuccess; --i) {
+      const int l = t - i;
+      if (l < 0 || l >= n_layers) continue;
+      if (i > 0) err = hipStreamWaitEvent(st[i], ev[i - 1], 0);
+      if (err == hipSuccess) err = run[i].launch(l, st[i]);
+      if (err == hipSuccess && i + 1 < n) err = hipEventRecord(ev[i], st[i]);
+    }
+  }
+  // join: the first stream after every chunk's last launch
+  for (int i = 0; i < n && err == hipSuccess; ++i) err = run[i].finish(st[i]);
+  for (int i = 1; i < n && err == hipSuccess; ++i) {
+    err = hipEventRecord(ev[i], st[i]);
+    if (err == hipSuccess) err = hipStreamWaitEvent(st[0], ev[i], 0);
+  }
+  return hip_rc(err);
 }
 
 namespace {

@@ -379,6 +379,48 @@ int smoe_stack_forward(const smoe_layer_desc* desc, int32_t n_layers, const void
                        int32_t* topk_idx, float* topk_w, int32_t* n_union, const smoe_union* un,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* One chunk of a prompt for smoe_stack_forward_chunks: the arguments of
+ * smoe_stack_forward that belong to one batch of tokens, with the same
+ * meaning and layout.  Every chunk has buffers of its own: h, tmp, the
+ * routing outputs, the union arrays and the workspace may not be shared
+ * between chunks.  stream: the chunk's own stream (chunks on one stream run
+ * one after another, still correctly). */
+typedef struct smoe_stack_chunk {
+  float* h;            /* [B, d] fp32, updated in place */
+  int32_t B;           /* 0 .. 64 tokens; 0 is skipped */
+  float* tmp;          /* [B, d] fp32 scratch, distinct from h */
+  int32_t* topk_idx;   /* [n_layers, B, top_k] int32 */
+  float* topk_w;       /* [n_layers, B, top_k] fp32 */
+  int32_t* n_union;    /* [n_layers] int32, or NULL */
+  smoe_union un;
+  void* ws;            /* workspace sized for (desc, B) */
+  size_t ws_bytes;
+  void* stream;
+} smoe_stack_chunk;
+
+#define SMOE_MAX_STACK_CHUNKS 8
+
+/* The chunks of a prompt through one stack, several in flight at once
+ * ([LMP] "Choreography Per Chunk": every chunk of up to 64 tokens goes
+ * through the layers in order, each layer's union streamed once for the
+ * chunk).  Chunk i runs on chunks[i].stream and starts its layer l when
+ * chunk i-1 has finished its own layer l, the order causal attention over
+ * the chunks would need; so while one chunk's FFN streams its experts, the
+ * next chunk's routing, combine and norm, which wait on latency rather than
+ * on HBM, run beside it.  Each chunk's outputs are bit-identical to
+ * smoe_stack_forward on that chunk alone.
+ * n_chunks: 1 .. SMOE_MAX_STACK_CHUNKS.  The call is ordered on
+ * chunks[0].stream like one launch: the other streams first wait for what
+ * is queued there, and it waits for all of them at the end.  Every chunk and
+ * layer is checked before the first launch (on an error nothing is launched):
+ * the errors of smoe_stack_forward, and SMOE_EINVAL when two chunks share h,
+ * tmp, a routing output, a union array or the workspace.  The library keeps
+ * SMOE_MAX_STACK_CHUNKS + 1 HIP events per host thread and device for the
+ * ordering, created on first use (no device memory).  Async. */
+int smoe_stack_forward_chunks(const smoe_layer_desc* desc, int32_t n_layers,
+                              const void* const* router_w, const smoe_experts* experts, float eps,
+                              const smoe_stack_chunk* chunks, int32_t n_chunks);
+
 /* ---------------------------------------------------------- calibration */
 /* Diagnostic: a plain streaming read of `bytes` (a multiple of 16) at `src`
  * (16-byte aligned) by `blocks` workgroups of 256 threads with 16-byte

@@ -308,6 +308,49 @@ def test_stack_argument_errors(smoe):
     assert call(n=0) == smoe.SMOE_OK and call(B=0) == smoe.SMOE_OK
 
 
+def test_stack_chunks_argument_errors(smoe):
+    """smoe_stack_forward_chunks checks every chunk and layer, and that no two
+    chunks share a buffer, before anything is launched."""
+    d = desc_of(smoe)
+    f = 4096
+    q = smoe.QMat(f, f, f, 1536 * 512, 1536 * 64)
+    qd = smoe.QMat(f, f, f, 4096 * 192, 4096 * 24)
+    good = smoe.Experts(q, q, qd)
+    bad = smoe.Experts(smoe.QMat(f, f, f, 1536 * 512 - 4, 1536 * 64), q, qd)
+    sc = smoe.lib.smoe_stack_forward_chunks
+    big = 1 << 30
+
+    def chunk(base, B=64, ws=None, nbytes=big):
+        # distinct 256-byte-aligned fake addresses per chunk (nothing is launched)
+        a = [base + 4096 * k for k in range(12)]
+        un = smoe.Union(a[5], a[6], a[7], a[8], a[9])
+        return smoe.StackChunk(a[0], B, a[1], a[2], a[3], a[4], un,
+                               a[10] if ws is None else ws, nbytes, None)
+
+    def call(chunks, n=3, experts=(good, good, good), eps=1e-6, count=None):
+        ra = (ctypes.c_void_p * 3)(f, f, f)
+        ea = (smoe.Experts * 3)(*experts)
+        arr = (smoe.StackChunk * max(len(chunks), 1))(*chunks)
+        return sc(ctypes.byref(d), n, ra, ea, eps, arr, len(chunks) if count is None else count)
+
+    c0, c1 = chunk(1 << 24), chunk(1 << 25)
+    assert call([c0, c1], count=0) == smoe.SMOE_EINVAL
+    assert call([c0] * 9, count=9) == smoe.SMOE_EINVAL
+    assert sc(ctypes.byref(d), 3, (ctypes.c_void_p * 3)(f, f, f), (smoe.Experts * 3)(good, good, good),
+              1e-6, None, 1) == smoe.SMOE_EINVAL
+    assert call([c0, c1], eps=0.0) == smoe.SMOE_EINVAL
+    assert call([c0, chunk(1 << 25, B=65)]) == smoe.SMOE_EUNSUPPORTED
+    assert call([c0, chunk(1 << 25, nbytes=4096)]) == smoe.SMOE_EWORKSPACE
+    assert call([c0, c1], experts=(good, good, bad)) == smoe.SMOE_EINVAL
+    # two chunks may not share a workspace, h or any other buffer
+    assert call([c0, chunk(1 << 25, ws=(1 << 24) + 4096 * 10)]) == smoe.SMOE_EINVAL
+    assert call([c0, chunk((1 << 24) + 4096 * 10)]) == smoe.SMOE_EINVAL   # c1.h == c0.ws
+    assert call([c0, c0]) == smoe.SMOE_EINVAL
+    # nothing to do
+    assert call([c0, c1], n=0) == smoe.SMOE_OK
+    assert call([chunk(1 << 24, B=0), chunk(1 << 25, B=0)]) == smoe.SMOE_OK
+
+
 def test_strerror(smoe):
     for c in (0, -1, -2, -3, -4):
         assert smoe.strerror(c)

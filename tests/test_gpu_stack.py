@@ -197,6 +197,52 @@ def test_stack_graph_replays_match_eager(smoe, d, B, shared):
             torch.cuda.synchronize()
 
 
+# several prompt chunks in flight on their own streams, each a layer behind
+# the previous one: every chunk's bits equal smoe_stack_forward on that chunk
+# alone (routing, union sizes and the output), on the MFMA path (chunks of
+# 5 and 64), the decode path (1 and 2 tokens: the norm inside the next
+# layer's router) and with a shared expert; an empty chunk is skipped
+@pytest.mark.parametrize("d,Bs,shared", [(1024, (64, 64, 5), 0), (2048, (2, 1), 0),
+                                         (1024, (5, 0, 64, 3), 320)])
+def test_stack_chunks_equal_one_chunk_at_a_time(smoe, d, Bs, shared):
+    cfg = small_config("stack_c", d, 32, 8, 256, max(Bs), shared=shared)
+    n_layers = 3
+    Ls = [synth.make_layer(cfg, layer=l) for l in range(n_layers)]
+    Wd = [device_weights(L) for L in Ls]
+    sts = [GpuStack(smoe, cfg, n_layers, max(B, 1), Wd) for B in Bs]
+    streams = [torch.cuda.current_stream()] + [torch.cuda.Stream() for _ in Bs[1:]]
+    for rep in range(2):                               # the ordering events are reused
+        h0 = [up(synth.hidden(cfg.seed, rep, 4000 + 7 * i, B, d)) if B else
+              torch.zeros(0, d, dtype=torch.float32, device=dev()) for i, B in enumerate(Bs)]
+        refs = []
+        for st, x, B in zip(sts, h0, Bs):
+            if B == 0:
+                refs.append(None)
+                continue
+            h = st.forward(x.clone())
+            torch.cuda.synchronize()
+            refs.append((down(h).copy(), down(st.idx).copy(), down(st.w).copy(), down(st.nu).copy()))
+            st.idx.fill_(-7)
+            st.w.fill_(-7.0)
+            st.nu.fill_(-7)
+        hs = [x.clone() for x in h0]
+        torch.cuda.synchronize()
+        # (views of each stack's own buffers; for B > 0 they are those buffers)
+        chunks = [dict(h=h, tmp=st.tmp[:h.shape[0]], topk_idx=st.idx[:, :h.shape[0]].contiguous(),
+                       topk_w=st.w[:, :h.shape[0]].contiguous(), n_union=st.nu, un=st.un,
+                       ws=st.ws, stream=s) for h, st, s in zip(hs, sts, streams)]
+        smoe.stack_forward_chunks(sts[0].desc, sts[0].args, chunks, eps=EPS)
+        torch.cuda.synchronize()
+        for i, (h, st, ref) in enumerate(zip(hs, sts, refs)):
+            if ref is None:
+                continue
+            assert np.array_equal(down(h).view(np.uint32), ref[0].view(np.uint32)), (rep, i)
+            assert np.array_equal(down(st.idx), ref[1]), (rep, i)
+            assert np.array_equal(down(st.w).view(np.uint32), ref[2].view(np.uint32)), (rep, i)
+            assert np.array_equal(down(st.nu), ref[3]), (rep, i)
+        assert all(smoe.read_status(st.ws) == 0 for st in sts)
+
+
 def test_stack_bad_layer_leaves_h_unchanged(smoe):
     cfg = small_config("stack_bad", 1024, 32, 8, 256, 1)
     Ls = [synth.make_layer(cfg, layer=l) for l in range(2)]
