@@ -890,6 +890,8 @@ def stack_harness(smoe, n_layers, prompt, steps, oracle_points=False):
         "prefill_s": round(pre_s, 5), "prefill_tokens_per_s": round(prompt / pre_s, 1),
         "prefill_effective_gbps": round(pre_bytes / pre_s / 1e9, 1),
         "prefill_chunks_in_flight": STACK_IN_FLIGHT,
+        "prefill_us_per_chunk_layer": round(pre_s / (chunks * n_layers) * 1e6, 1),
+        "prefill_one_chunk_at_a_time_us_per_chunk_layer": round(one_s / (chunks * n_layers) * 1e6, 1),
         "prefill_one_chunk_at_a_time_s": round(one_s, 5),
         "prefill_in_flight_equals_one_at_a_time": in_flight_equal,
         "decode_ms_per_token": round(dec_s / steps * 1e3, 4),
