@@ -212,8 +212,9 @@ int smoe_moe_layer(const smoe_layer_desc* desc, const void* router_w, const smoe
  * "Choreography Per Chunk" steps 5-6 at B = 1).  The same work in one grid
  * of one workgroup per compute unit: the token's activation prep and every
  * expert's gate matvec, a device-wide barrier, top-k + union + gate_up, a
- * second barrier, down + the weighted combine.  The barriers release and
- * acquire at device scope (every wave's stores); a wait that passes about
+ * second barrier, down + the weighted combine.  At each barrier every
+ * workgroup releases its waves' stores and acquires with one increment at
+ * device scope (after its own barrier); a wait that passes about
  * 2^22 polls sets SMOE_STATUS_SYNC_TIMEOUT in the workspace status and goes
  * on, so the launch always ends.  Results are bit for bit those of
  * smoe_moe_layer on the same inputs.  Supported: B = 1, a bf16 router, no
